@@ -1,0 +1,252 @@
+/*
+ * sm.h - C ABI of the MI355X (gfx950) Muon-family optimizer step library.
+ *
+ * One optimizer step of Sign-Muon, CacheMuon or LionMuon on a set of weight
+ * matrices, with M data-parallel workers simulated on one GPU as M gradient
+ * streams.  The steps are: momentum EMA, Frobenius normalisation,
+ * Newton-Schulz (NS) polar iteration or its Gram form with a cached left
+ * transform Q and an orthogonality-residual reuse check, entrywise sign,
+ * 1-bit packing, majority vote, and the weight update.
+ *
+ * Sources (cited below by short name):
+ *   [SignMuon-ja]  SignMuon technical summary, gist.science/ja/paper/2605.16311
+ *   [SignMuon-abs] SignMuon abstract, fugumt.com/fugumt/paper_check/2605.16311v1
+ *                  and hotpaper.ai/paper/2605.16311
+ *   [CacheMuon-ja] CacheMuon technical summary, gist.science/ja/paper/2606.16371
+ *   [LionMuon-pt]  LionMuon technical summary, gist.science/pt/paper/2605.19811
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is DEVICE memory, row-major, contiguous, owned by
+ *     the caller, and 16-byte aligned.  The library never allocates device
+ *     memory, never frees, and keeps no pointer after a call returns.
+ *     Scratch memory is passed in as `ws` (sized by the matching *_ws query).
+ *   - All GPU work is enqueued on the stream `s` (0 = null stream) and is
+ *     asynchronous; no call synchronises the stream or copies device data to
+ *     the host.
+ *   - Arguments are validated on the host before any HIP call; a bad
+ *     argument returns an SM_ERR_* code and enqueues nothing.  A failed
+ *     launch returns SM_ERR_HIP; sm_last_hip_error() then gives the HIP code.
+ *     No call aborts or throws across the ABI.
+ *   - Arithmetic is float32 (MFMA accumulation in float32).  bf16 values are
+ *     rounded from float32 with round-to-nearest-even.
+ *   - sign(x) = -1 if x < 0, else +1  (+0, -0 and NaN give +1).
+ *   - 1-bit layout: uint64 words, little-endian; bit j of word w holds entry
+ *     64*w + j of the row-major matrix in its original orientation; the bit
+ *     is 1 iff the entry is negative; unused tail bits are 0.
+ *   - Calls on different streams with disjoint buffers are independent.
+ */
+#ifndef SM_H
+#define SM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SM_OK = 0,
+  SM_ERR_ARG = 1,          /* null / misaligned / aliased pointer, bad scalar    */
+  SM_ERR_SHAPE = 2,        /* non-positive or too large dimension                */
+  SM_ERR_DTYPE = 3,        /* dtype not SM_F32 / SM_BF16                         */
+  SM_ERR_WORKSPACE = 4,    /* ws too small (query the *_ws call)                 */
+  SM_ERR_UNSUPPORTED = 5,  /* valid request outside what this build implements   */
+  SM_ERR_HIP = 6           /* a HIP runtime call or launch failed                */
+} sm_status;
+
+typedef enum { SM_F32 = 0, SM_BF16 = 1 } sm_dtype;
+
+/* Newton-Schulz parameters: iterations K and polynomial coefficients of
+ * X <- a X + b (X X^T) X + c (X X^T)^2 X, and the normalisation guard eps of
+ * X = Y / (||Y||_F + eps).  The pages print no coefficients; the cubic
+ * default is {5, 1.5f, -0.5f, 0.0f, 1e-7f}.  1 <= iters <= 64. */
+typedef struct {
+  int32_t iters;
+  float a, b, c;
+  float eps;
+} sm_ns_params;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* sm_status_string(int status);
+
+/* Last hipError_t returned by a HIP call inside the library (0 if none). */
+int sm_last_hip_error(void);
+
+/* Library ABI version (increments on any signature change). */
+int sm_version(void);
+
+/* ------------------------------------------------------------------------
+ * Direct Newton-Schulz polar factor.
+ * [SignMuon-ja] section 2, core mechanism 1 and algorithm flow step 1: each
+ * worker approximates the polar factor of its momentum by a Newton-Schulz
+ * iteration; [LionMuon-pt] problem statement: Muon steps with msign(G_hat).
+ *
+ * x, u : [batch][m][n] in dt.  u receives X_K.  x is read-only and must not
+ *        overlap u.  A tall problem (m > n) is iterated on its transpose
+ *        (Gram matrix n x n); x and u keep the original orientation.
+ * normalize : 1 -> iterate from x / (||x||_F + eps) per problem; 0 -> from x.
+ * ws   : scratch of at least sm_ns_polar_ws(...) bytes, 256-byte aligned.
+ * Errors: SM_ERR_ARG (null, misaligned, overlap, bad params), SM_ERR_SHAPE
+ *        (batch, m or n < 1, or m*n >= 2^31), SM_ERR_DTYPE, SM_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+sm_status sm_ns_polar_ws(int dt, int batch, int m, int n, size_t* ws_bytes);
+sm_status sm_ns_polar(const void* x, void* u, int dt, int batch, int m, int n,
+                      int normalize, const sm_ns_params* p, void* ws, size_t ws_bytes,
+                      hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * CacheMuon orthogonalisation: Gram Newton-Schulz with a cached left
+ * transform Q and a residual-based reuse trigger.
+ * [CacheMuon-ja] method, core mechanism items 1-3: a refresh runs the fresh
+ * Gram-NS solve, which returns the direction and the left transform Q; other
+ * steps apply the cached Q to the normalised momentum, D_hat = Q X, and keep
+ * it iff err = ||D_hat D_hat^T - I||_F / ||I||_F <= gamma, else refresh.
+ *
+ * With r = min(m,n) and X the wide orientation of x (x^T when m > n):
+ *   fresh: G_0 = X X^T, Q_0 = I; for k < K: P_k = aI + bG_k + cG_k^2,
+ *          Q_{k+1} = P_k Q_k, G_{k+1} = P_k G_k P_k; D = Q_K X.
+ * x, d  : [batch][m][n] in dt; d receives the direction in x's orientation.
+ * q     : [batch][r][r] float32, the cache (caller-owned, persistent state).
+ * cache_state : [batch][2] int32 = {has_cache, a_t} (persistent; zero it
+ *         before the first step).  a_t is the low 32 bits of t.
+ * err   : [batch] float32 out: the probed residual, or -1 if no candidate
+ *         was probed (no cache, or mode 1).
+ * refreshed : [batch] int32 out: 1 if a fresh solve ran, else 0.
+ * mode  : 0 trigger (reuse iff err <= gamma; NaN err refreshes),
+ *         1 force fresh every step, 2 force reuse whenever a cache exists.
+ * t     : step index (1-based) recorded as a_t on refresh.
+ * The accept/refresh decision is taken on the device; nothing is copied to
+ * the host.  Errors as for sm_ns_polar, plus SM_ERR_ARG for a bad mode.
+ * ---------------------------------------------------------------------- */
+sm_status sm_gram_ns_cached_ws(int dt, int batch, int m, int n, size_t* ws_bytes);
+sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_state,
+                            float* err, int32_t* refreshed, int dt, int batch, int m,
+                            int n, int normalize, const sm_ns_params* p, float gamma,
+                            int mode, int64_t t, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Entrywise sign and 1-bit pack.
+ * [SignMuon-ja] section 2, algorithm flow steps 2-3 (all-gather variant):
+ * workers keep only the entrywise sign of their direction, packed one bit
+ * per entry (32x fewer bytes than float32, [SignMuon-ja] communication
+ * efficiency).
+ * x    : [count] in dt.   bits : [ceil(count/64)] uint64 out.
+ * Errors: SM_ERR_ARG (null/misaligned), SM_ERR_SHAPE (count < 0),
+ *         SM_ERR_DTYPE.  count == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+sm_status sm_sign_pack(const void* x, int dt, int64_t count, uint64_t* bits, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Majority vote and update.
+ * [SignMuon-ja] section 2, core mechanism 3 and algorithm flow step 4: the
+ * workers' signs are summed as integers and thresholded by sign(); every
+ * worker then applies W <- W - eta * vote.
+ * bits : [M][words_stride] uint64, worker-major packed signs (what an
+ *        all-gather of the workers' 1-bit buffers delivers);
+ *        words_stride >= ceil(count/64).
+ * V_i  = sign(M - 2 * n_neg_i) in {-1, 0, +1} (0 only on ties, even M).
+ * w    : [count] in wdt, updated in place: W <- rnd_W(fp32(W) - fp32(lr)*V),
+ *        one float32 rounding, then RNE to bf16 for bf16 weights.
+ * vote_out : optional [count] int8 out (NULL to skip).
+ * Errors: SM_ERR_ARG (null/misaligned, words_stride too small, lr not
+ *         finite), SM_ERR_SHAPE (count < 0), SM_ERR_UNSUPPORTED (M < 1 or
+ *         M > 64), SM_ERR_DTYPE.
+ * ---------------------------------------------------------------------- */
+sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int64_t count,
+                         void* w, int wdt, float lr, int8_t* vote_out, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Whole optimizer step over a set of weight matrices.
+ *
+ * algo SM_SIGN_MUON  ([SignMuon-ja] section 2, algorithm flow steps 1-4):
+ *   per worker M <- beta1*M + (1-beta1)*G, D = NS(M/(||M||_F+eps)),
+ *   s = sign(D) packed to bits; V = majority vote; W <- W - lr*V.
+ * algo SM_CACHE_MUON ([CacheMuon-ja] core mechanism): as Sign-Muon but D
+ *   comes from the cached Gram-NS (q_cache, cache_state per matrix) with
+ *   reuse threshold gamma and cache_mode as in sm_gram_ns_cached; update
+ *   SM_UPDATE_POLAR (M must be 1) applies W <- W - lr*D, SM_UPDATE_VOTE
+ *   votes the signs of D.
+ * algo SM_LION_MUON  ([LionMuon-pt] core algorithm items 1-2):
+ *   G_hat = beta1*M + (1-beta1)*G, then M <- beta2*M + (1-beta2)*G.  If
+ *   period > 0 and t mod period == 0 the direction is NS(G_hat normalised)
+ *   (a Muon step), otherwise sign(G_hat) (a Lion step; period 0 = never
+ *   Muon).  Signs are voted over the M workers; with SM_UPDATE_POLAR and
+ *   M = 1 a Muon step applies W <- W - lr*D instead.
+ *
+ * sm_matrix: m, n > 0; w [m][n] in wdt; mom [M][m][n] in mdt (updated in
+ *   place); grad [M][m][n] in gdt (read-only); q_cache [M][r][r] float32 and
+ *   cache_state [M][2] int32 for SM_CACHE_MUON, else NULL.
+ * mdt is also the Newton-Schulz operand type (bf16 -> bf16 MFMA, f32 ->
+ *   f32 MFMA); accumulation is always float32.
+ * t: 1-based step index.  ws: at least sm_step_ws(...) bytes.
+ * diag: optional device float [nmat][M][2] out = {err, refreshed} per
+ *   (matrix, worker) for SM_CACHE_MUON (NULL to skip; ignored otherwise).
+ * Errors: SM_ERR_ARG, SM_ERR_SHAPE, SM_ERR_DTYPE, SM_ERR_WORKSPACE,
+ *   SM_ERR_UNSUPPORTED (M outside 1..64, POLAR with M != 1, SIGN_MUON with
+ *   POLAR), SM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+typedef enum { SM_SIGN_MUON = 0, SM_CACHE_MUON = 1, SM_LION_MUON = 2 } sm_algo;
+typedef enum { SM_UPDATE_VOTE = 0, SM_UPDATE_POLAR = 1 } sm_update;
+
+typedef struct {
+  int32_t m, n;
+  void* w;
+  void* mom;
+  const void* grad;
+  float* q_cache;
+  int32_t* cache_state;
+} sm_matrix;
+
+typedef struct {
+  int32_t algo;        /* sm_algo                                         */
+  int32_t update;      /* sm_update                                       */
+  int32_t M;           /* workers, 1..64                                  */
+  int32_t wdt, mdt, gdt;
+  float lr;
+  float beta1;         /* EMA beta (Sign/CacheMuon) or Lion beta1          */
+  float beta2;         /* Lion beta2 (LionMuon only)                       */
+  int32_t period;      /* LionMuon P, 0 = infinity                         */
+  sm_ns_params ns;
+  float gamma;         /* CacheMuon residual threshold                     */
+  int32_t cache_mode;  /* CacheMuon mode (0 trigger, 1 fresh, 2 reuse)     */
+} sm_config;
+
+sm_status sm_step_ws(const sm_config* c, const sm_matrix* mats, int nmat, size_t* ws_bytes);
+sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t,
+                  void* ws, size_t ws_bytes, float* diag, hipStream_t s);
+
+/* ------------------------------------------------------------------------
+ * Kernel-time accounting (for benchmarks; not part of the method).
+ * While enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events on its stream, tagged with its kind and its algorithmic work
+ * (flops for GEMMs, bytes for streaming kernels).  sm_profile_read waits for
+ * the recorded events and returns the totals for one kind.  Enabling
+ * creates an event pool (up to 65536 launches); reading or disabling never
+ * allocates.  Not thread-safe; meant for one benchmarking thread.
+ * ---------------------------------------------------------------------- */
+enum {
+  SM_K_EMA = 0,          /* momentum EMA (+ norm partials)         bytes  */
+  SM_K_NORM = 1,         /* sum-of-squares / scale finalize        bytes  */
+  SM_K_GEMM_GRAM = 2,    /* X X^T (NS and Gram-NS)                 flops  */
+  SM_K_GEMM_APPLY = 3,   /* a X + B X  /  Q X                      flops  */
+  SM_K_GEMM_RR = 4,      /* r x r products of Gram-NS / quintic    flops  */
+  SM_K_PROBE = 5,        /* residual D D^T - I                     flops  */
+  SM_K_SIGN_PACK = 6,    /* sign + 1-bit pack                      bytes  */
+  SM_K_VOTE_UPDATE = 7,  /* vote + W update                        bytes  */
+  SM_K_LION = 8,         /* fused Lion interpolation/EMA/sign/pack bytes  */
+  SM_K_POLAR_UPDATE = 9, /* W <- W - lr D                          bytes  */
+  SM_K_MISC = 10,        /* small finalize / copy kernels          bytes  */
+  SM_K_NUM_KINDS = 11
+};
+sm_status sm_profile_enable(int on);
+sm_status sm_profile_reset(void);
+sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double* work);
+const char* sm_kernel_kind_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SM_H */

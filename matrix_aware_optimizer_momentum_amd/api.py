@@ -1,0 +1,261 @@
+"""torch-tensor front end of libsm: same names as the C ABI, marshalling only.
+
+Tensors must be CUDA (HIP) tensors, contiguous, float32 or bfloat16 unless
+stated otherwise.  Work is enqueued on torch's current stream.  Non-OK
+status codes raise SmError.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _binding as B
+
+_DT = {torch.float32: B.F32, torch.bfloat16: B.BF16}
+_TORCH_DT = {B.F32: torch.float32, B.BF16: torch.bfloat16}
+
+
+@dataclass
+class NSParams:
+    iters: int = 5
+    a: float = 1.5
+    b: float = -0.5
+    c: float = 0.0
+    eps: float = 1e-7
+
+    def c_struct(self) -> B.NSParams:
+        return B.NSParams(self.iters, self.a, self.b, self.c, self.eps)
+
+
+@dataclass
+class StepConfig:
+    algo: int = B.SIGN_MUON
+    update: int = B.UPDATE_VOTE
+    M: int = 1
+    wdt: torch.dtype = torch.float32
+    mdt: torch.dtype = torch.float32
+    gdt: torch.dtype = torch.float32
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.99
+    period: int = 0
+    ns: NSParams = field(default_factory=NSParams)
+    gamma: float = 0.0
+    cache_mode: int = B.MODE_TRIGGER
+
+    def c_struct(self) -> B.Config:
+        return B.Config(self.algo, self.update, self.M, _DT[self.wdt], _DT[self.mdt],
+                        _DT[self.gdt], self.lr, self.beta1, self.beta2, self.period,
+                        self.ns.c_struct(), self.gamma, self.cache_mode)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"dtype {t.dtype} not supported (float32 / bfloat16)")
+    return _DT[t.dtype]
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _bmn(x: torch.Tensor):
+    if x.dim() == 2:
+        return 1, x.shape[0], x.shape[1]
+    if x.dim() == 3:
+        return x.shape[0], x.shape[1], x.shape[2]
+    raise ValueError("expected [m, n] or [batch, m, n]")
+
+
+# ------------------------------------------------------------------ sm_ns_polar
+
+def ns_polar_ws(dtype: torch.dtype, batch: int, m: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    B.check(B.lib().sm_ns_polar_ws(_DT[dtype], batch, m, n, ctypes.byref(out)), "sm_ns_polar_ws")
+    return out.value
+
+
+def ns_polar(x: torch.Tensor, out: Optional[torch.Tensor] = None, normalize: bool = True,
+             params: Optional[NSParams] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, "x")
+    batch, m, n = _bmn(x)
+    p = params or NSParams()
+    out = torch.empty_like(x) if out is None else out
+    _dev(out, "out")
+    ws = _ws(ns_polar_ws(x.dtype, batch, m, n), x.device, ws)
+    cp = p.c_struct()
+    code = B.lib().sm_ns_polar(x.data_ptr(), out.data_ptr(), _dt(x), batch, m, n,
+                               int(normalize), ctypes.byref(cp), ws.data_ptr(),
+                               ws.numel() * ws.element_size(), _stream())
+    B.check(code, "sm_ns_polar")
+    return out
+
+
+# ------------------------------------------------------------------ sm_gram_ns_cached
+
+def gram_ns_cached_ws(dtype: torch.dtype, batch: int, m: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    B.check(B.lib().sm_gram_ns_cached_ws(_DT[dtype], batch, m, n, ctypes.byref(out)),
+            "sm_gram_ns_cached_ws")
+    return out.value
+
+
+def gram_ns_cached(x: torch.Tensor, q: torch.Tensor, cache_state: torch.Tensor, t: int,
+                   gamma: float, mode: int = B.MODE_TRIGGER, normalize: bool = True,
+                   params: Optional[NSParams] = None, d: Optional[torch.Tensor] = None,
+                   err: Optional[torch.Tensor] = None, refreshed: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None):
+    """Returns (d, err, refreshed); q and cache_state are updated in place."""
+    _dev(x, "x")
+    batch, m, n = _bmn(x)
+    r = min(m, n)
+    if q.dtype != torch.float32 or q.numel() != batch * r * r:
+        raise ValueError("q must be float32 [batch, r, r]")
+    if cache_state.dtype != torch.int32 or cache_state.numel() != 2 * batch:
+        raise ValueError("cache_state must be int32 [batch, 2]")
+    _dev(q, "q"); _dev(cache_state, "cache_state")
+    p = params or NSParams()
+    d = torch.empty_like(x) if d is None else d
+    err = torch.empty(batch, dtype=torch.float32, device=x.device) if err is None else err
+    refreshed = (torch.empty(batch, dtype=torch.int32, device=x.device)
+                 if refreshed is None else refreshed)
+    ws = _ws(gram_ns_cached_ws(x.dtype, batch, m, n), x.device, ws)
+    cp = p.c_struct()
+    code = B.lib().sm_gram_ns_cached(x.data_ptr(), d.data_ptr(), q.data_ptr(),
+                                     cache_state.data_ptr(), err.data_ptr(),
+                                     refreshed.data_ptr(), _dt(x), batch, m, n, int(normalize),
+                                     ctypes.byref(cp), gamma, mode, t, ws.data_ptr(),
+                                     ws.numel() * ws.element_size(), _stream())
+    B.check(code, "sm_gram_ns_cached")
+    return d, err, refreshed
+
+
+# ------------------------------------------------------------------ sign / vote
+
+def sign_pack(x: torch.Tensor, bits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed signs as an int64 tensor holding the uint64 words."""
+    _dev(x, "x")
+    count = x.numel()
+    words = (count + 63) // 64
+    bits = torch.empty(max(words, 1), dtype=torch.int64, device=x.device) if bits is None else bits
+    code = B.lib().sm_sign_pack(x.data_ptr(), _dt(x), count, bits.data_ptr(), _stream())
+    B.check(code, "sm_sign_pack")
+    return bits
+
+
+def vote_update(bits: torch.Tensor, w: torch.Tensor, lr: float,
+                vote_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bits: int64 [M, words_stride]; w updated in place; returns w."""
+    _dev(bits, "bits"); _dev(w, "w")
+    if bits.dtype != torch.int64 or bits.dim() != 2:
+        raise ValueError("bits must be int64 [M, words_stride]")
+    M, stride = bits.shape
+    vp = 0
+    if vote_out is not None:
+        _dev(vote_out, "vote_out")
+        if vote_out.dtype != torch.int8 or vote_out.numel() != w.numel():
+            raise ValueError("vote_out must be int8 with w's element count")
+        vp = vote_out.data_ptr()
+    code = B.lib().sm_vote_update(bits.data_ptr(), M, stride, w.numel(), w.data_ptr(), _dt(w),
+                                  lr, vp, _stream())
+    B.check(code, "sm_vote_update")
+    return w
+
+
+# ------------------------------------------------------------------ sm_step
+
+@dataclass
+class MatrixBuffers:
+    """Caller-owned state of one weight matrix (all on the GPU)."""
+    w: torch.Tensor                       # [m, n]
+    mom: torch.Tensor                     # [M, m, n]
+    grad: torch.Tensor                    # [M, m, n]
+    q_cache: Optional[torch.Tensor] = None      # [M, r, r] float32 (CacheMuon)
+    cache_state: Optional[torch.Tensor] = None  # [M, 2] int32 (CacheMuon)
+
+    def c_struct(self) -> B.Matrix:
+        m, n = self.w.shape
+        return B.Matrix(m, n, self.w.data_ptr(), self.mom.data_ptr(), self.grad.data_ptr(),
+                        self.q_cache.data_ptr() if self.q_cache is not None else None,
+                        self.cache_state.data_ptr() if self.cache_state is not None else None)
+
+
+def _mats_array(mats: Sequence[MatrixBuffers]):
+    arr = (B.Matrix * len(mats))()
+    for i, mb in enumerate(mats):
+        arr[i] = mb.c_struct()
+    return arr
+
+
+def step_ws(cfg: StepConfig, mats: Sequence[MatrixBuffers]) -> int:
+    out = ctypes.c_size_t(0)
+    c = cfg.c_struct()
+    arr = _mats_array(mats)
+    B.check(B.lib().sm_step_ws(ctypes.byref(c), arr, len(mats), ctypes.byref(out)), "sm_step_ws")
+    return out.value
+
+
+class StepCall:
+    """A prepared sm_step call: marshalled structs and a workspace, reusable per step."""
+
+    def __init__(self, cfg: StepConfig, mats: Sequence[MatrixBuffers],
+                 ws: Optional[torch.Tensor] = None, diag: Optional[torch.Tensor] = None):
+        for mb in mats:
+            for name in ("w", "mom", "grad"):
+                _dev(getattr(mb, name), name)
+        self.cfg = cfg
+        self.mats = list(mats)
+        self._c = cfg.c_struct()
+        self._arr = _mats_array(self.mats)
+        nbytes = step_ws(cfg, self.mats)
+        self.ws = _ws(nbytes, self.mats[0].w.device, ws)
+        self.diag = diag
+
+    def __call__(self, t: int):
+        code = B.lib().sm_step(ctypes.byref(self._c), self._arr, len(self.mats), t,
+                               self.ws.data_ptr(), self.ws.numel() * self.ws.element_size(),
+                               self.diag.data_ptr() if self.diag is not None else None,
+                               _stream())
+        B.check(code, "sm_step")
+
+
+def step(cfg: StepConfig, mats: Sequence[MatrixBuffers], t: int,
+         ws: Optional[torch.Tensor] = None, diag: Optional[torch.Tensor] = None):
+    StepCall(cfg, mats, ws, diag)(t)
+
+
+# ------------------------------------------------------------------ kernel accounting
+
+def profile_enable(on: bool = True):
+    B.check(B.lib().sm_profile_enable(int(on)), "sm_profile_enable")
+
+
+def profile_reset():
+    B.check(B.lib().sm_profile_reset(), "sm_profile_reset")
+
+
+def profile_read(kind: str):
+    """(total_ms, launches, algorithmic work) for one kernel kind; waits on its events."""
+    k = B.KERNEL_KINDS.index(kind)
+    ms, n, work = ctypes.c_double(0), ctypes.c_int64(0), ctypes.c_double(0)
+    B.check(B.lib().sm_profile_read(k, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work)),
+            "sm_profile_read")
+    return ms.value, n.value, work.value

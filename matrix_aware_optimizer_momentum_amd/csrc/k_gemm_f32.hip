@@ -1,0 +1,16 @@
+// Instantiations of the batched MFMA GEMM: A operand float in HBM, MFMA input float.
+#include "k_gemm.hpp"
+
+namespace sm {
+
+sm_status launch_gemm_f32(const GemmArgs& g, int kind, hipStream_t s) {
+  using namespace gemm;
+  if (g.b.dt == F32) {
+    if (g.a.layout == KC && g.b.layout == KC) return launch_t<float, float, float, KC, KC>(g, kind, s);
+    if (g.a.layout == KC && g.b.layout == RC) return launch_t<float, float, float, KC, RC>(g, kind, s);
+    if (g.a.layout == RC && g.b.layout == RC) return launch_t<float, float, float, RC, RC>(g, kind, s);
+  }
+  return SM_ERR_UNSUPPORTED;
+}
+
+}  // namespace sm

@@ -1,0 +1,470 @@
+// Streaming (HBM-bound) kernels of the optimizer step: momentum EMA with
+// sum-of-squares partials, the fused Lion step, sign + 1-bit pack, majority
+// vote + update, the polar update, and the small per-problem finalize
+// kernels.  Every kernel reads and writes each element once with 16-byte
+// vector accesses where the problem size allows, and reduces in a fixed
+// order so results are run-to-run identical.
+//
+// Sources: SignMuon technical summary (gist.science/ja/paper/2605.16311),
+// CacheMuon technical summary (gist.science/ja/paper/2606.16371), LionMuon
+// technical summary (gist.science/pt/paper/2605.19811).
+#include "sm_internal.hpp"
+
+namespace sm {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = kThreads * 8;  // elements per block iteration
+
+template <typename T>
+__device__ __forceinline__ float round_to(float v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ float round_to<bf16_t>(float v) {
+  return bf2f(f2bf(v));
+}
+
+// Loads up to 8 elements starting at e0 (< count); missing ones read as 0.
+template <typename T>
+__device__ __forceinline__ void load8_tail(const T* p, int64_t e0, int64_t count, bool vec,
+                                           float* v) {
+  if (vec && e0 + 8 <= count) {
+    load8<T>(p + e0, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (e0 + e < count) ? Elem<T>::load(p + e0 + e) : 0.f;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8_tail(T* p, int64_t e0, int64_t count, bool vec,
+                                            const float* v) {
+  if (vec && e0 + 8 <= count) {
+    store8<T>(p + e0, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e0 + e < count) Elem<T>::store(p + e0 + e, v[e]);
+  }
+}
+
+// Fixed-order block sum: wave butterfly, then wave 0 adds the 4 wave sums.
+__device__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = 0.f;
+  if (threadIdx.x == 0) r = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
+// Byte of sign bits for 8 entries: bit e set iff v[e] < 0 (NaN, +-0 -> 0).
+__device__ __forceinline__ uint32_t neg_byte(const float* v, int64_t e0, int64_t count) {
+  uint32_t byte = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e0 + e < count && v[e] < 0.f) byte |= 1u << e;
+  return byte;
+}
+
+// Each thread leaves one byte (8 entries) in sbytes[tid]; threads 0..31 then
+// store the block's 2048 entries as 32 uint64 words (LSB-first).
+__device__ __forceinline__ void flush_bytes(uint8_t* sbytes, uint64_t* bits, int64_t word0,
+                                            int64_t words) {
+  __syncthreads();
+  if (threadIdx.x < kChunk / 64) {
+    int64_t wi = word0 + threadIdx.x;
+    if (wi < words) bits[wi] = reinterpret_cast<const uint64_t*>(sbytes)[threadIdx.x];
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ EMA
+
+template <typename TM, typename TG, typename TX>
+__global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad, int per,
+                                                         int64_t count, float beta, TX* x,
+                                                         float* partials, bool vec) {
+  __shared__ float red[4];
+  const int b = blockIdx.y;
+  TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
+  const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
+  TX* xo = x ? x + (int64_t)b * count : nullptr;
+  const float omb = 1.0f - beta;
+  float acc = 0.f;
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  for (int64_t ci = blockIdx.x; ci < nchunks; ci += gridDim.x) {
+    const int64_t e0 = ci * kChunk + (int64_t)threadIdx.x * 8;
+    if (e0 >= count) continue;
+    float mv[8], gv[8];
+    load8_tail<TM>(m, e0, count, vec, mv);
+    load8_tail<TG>(g, e0, count, vec, gv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = round_to<TM>(beta * mv[e] + omb * gv[e]);
+      mv[e] = v;
+      float xv = round_to<TX>(v);
+      gv[e] = xv;
+      if (e0 + e < count) acc += xv * xv;
+    }
+    store8_tail<TM>(m, e0, count, vec, mv);
+    if (xo) store8_tail<TX>(xo, e0, count, vec, gv);
+  }
+  float s = block_sum(acc, red);
+  if (threadIdx.x == 0 && partials) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
+}
+
+// LionMuon: ghat = b1*M + (1-b1)*G (direction), M <- b2*M + (1-b2)*G.
+template <typename TM, typename TG, typename TX>
+__global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int per,
+                                                   int64_t count, float b1, float b2, TX* x,
+                                                   float* partials, uint64_t* bits,
+                                                   int64_t words, bool vec) {
+  __shared__ float red[4];
+  __shared__ uint8_t sbytes[kThreads];
+  const int b = blockIdx.y;
+  TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
+  const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
+  TX* xo = x ? x + (int64_t)b * count : nullptr;
+  uint64_t* bo = bits ? bits + (int64_t)b * words : nullptr;
+  const float omb1 = 1.0f - b1, omb2 = 1.0f - b2;
+  float acc = 0.f;
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  for (int64_t ci = blockIdx.x; ci < nchunks; ci += gridDim.x) {
+    const int64_t e0 = ci * kChunk + (int64_t)threadIdx.x * 8;
+    uint32_t byte = 0;
+    if (e0 < count) {
+      float mv[8], gv[8], dv[8];
+      load8_tail<TM>(m, e0, count, vec, mv);
+      load8_tail<TG>(g, e0, count, vec, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dv[e] = b1 * mv[e] + omb1 * gv[e];
+        mv[e] = round_to<TM>(b2 * mv[e] + omb2 * gv[e]);
+      }
+      store8_tail<TM>(m, e0, count, vec, mv);
+      if (bo) {
+        byte = neg_byte(dv, e0, count);
+      } else if (xo) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dv[e] = round_to<TX>(dv[e]);
+          if (e0 + e < count) acc += dv[e] * dv[e];
+        }
+        store8_tail<TX>(xo, e0, count, vec, dv);
+      }
+    }
+    if (bo) {
+      sbytes[threadIdx.x] = (uint8_t)byte;
+      flush_bytes(sbytes, bo, ci * (kChunk / 64), words);
+    }
+  }
+  if (!bo) {
+    float s = block_sum(acc, red);
+    if (threadIdx.x == 0 && partials) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_sumsq(const T* x, int64_t count, float* partials,
+                                                    bool vec) {
+  __shared__ float red[4];
+  const int b = blockIdx.y;
+  const T* xp = x + (int64_t)b * count;
+  float acc = 0.f;
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  for (int64_t ci = blockIdx.x; ci < nchunks; ci += gridDim.x) {
+    const int64_t e0 = ci * kChunk + (int64_t)threadIdx.x * 8;
+    if (e0 >= count) continue;
+    float v[8];
+    load8_tail<T>(xp, e0, count, vec, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += v[e] * v[e];
+  }
+  float s = block_sum(acc, red);
+  if (threadIdx.x == 0) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
+}
+
+__global__ void k_scale_finalize(const float* partials, int nprob, float eps, float* scale) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nprob) return;
+  double s = 0.0;
+  for (int i = 0; i < kNormParts; ++i) s += (double)partials[(int64_t)b * kNormParts + i];
+  scale[b] = (float)(1.0 / (sqrt(s) + (double)eps));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_sign_pack(const T* x, int64_t count,
+                                                        uint64_t* bits, int64_t words,
+                                                        bool vec) {
+  __shared__ uint8_t sbytes[kThreads];
+  const int b = blockIdx.y;
+  const T* xp = x + (int64_t)b * count;
+  uint64_t* bo = bits + (int64_t)b * words;
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  for (int64_t ci = blockIdx.x; ci < nchunks; ci += gridDim.x) {
+    const int64_t e0 = ci * kChunk + (int64_t)threadIdx.x * 8;
+    uint32_t byte = 0;
+    if (e0 < count) {
+      float v[8];
+      load8_tail<T>(xp, e0, count, vec, v);
+      byte = neg_byte(v, e0, count);
+    }
+    sbytes[threadIdx.x] = (uint8_t)byte;
+    flush_bytes(sbytes, bo, ci * (kChunk / 64), words);
+  }
+}
+
+// Vote over M <= 64 workers for 8 entries per thread.  Each worker's byte of
+// sign bits is spread to one byte-wide counter per entry (a nibble times
+// 0x00204081 places bit i at bit 8i; the 4 partial products never overlap),
+// so one 32-bit add counts 4 entries at once; counts stay below 256.
+template <typename TW>
+__global__ __launch_bounds__(kThreads) void k_vote_update(const uint64_t* bits, int M,
+                                                          int64_t words_stride,
+                                                          int64_t mat_stride_words,
+                                                          int64_t count, PtrTbl w, float lr,
+                                                          int8_t* vote_out, bool vec) {
+  const int j = blockIdx.y;
+  const uint8_t* bb = reinterpret_cast<const uint8_t*>(bits + (int64_t)j * mat_stride_words);
+  const int64_t stride_bytes = words_stride * 8;
+  TW* wp = (TW*)w.p[j];
+  const int64_t nbytes = (count + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes;
+       i += (int64_t)gridDim.x * kThreads) {
+    uint32_t lo = 0, hi = 0;
+    for (int k = 0; k < M; ++k) {
+      const uint32_t byte = bb[(int64_t)k * stride_bytes + i];
+      lo += ((byte & 15u) * 0x00204081u) & 0x01010101u;
+      hi += ((byte >> 4) * 0x00204081u) & 0x01010101u;
+    }
+    const int64_t e0 = 8 * i;
+    float wv[8];
+    int vv[8];
+    load8_tail<TW>(wp, e0, count, vec, wv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int nneg = (int)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+      const int sum = M - 2 * nneg;
+      const int v = (sum > 0) - (sum < 0);
+      vv[e] = v;
+      wv[e] = wv[e] - lr * (float)v;  // lr*v is exact: one rounding
+    }
+    store8_tail<TW>(wp, e0, count, vec, wv);
+    if (vote_out) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e0 + e < count) vote_out[e0 + e] = (int8_t)vv[e];
+    }
+  }
+}
+
+template <typename TD, typename TW>
+__global__ __launch_bounds__(kThreads) void k_polar_update(const TD* d, int64_t count,
+                                                           PtrTbl w, float lr, bool vec) {
+  const int j = blockIdx.y;
+  const TD* dp = d + (int64_t)j * count;
+  TW* wp = (TW*)w.p[j];
+  const int64_t n8 = (count + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t e0 = 8 * i;
+    float wv[8], dv[8];
+    load8_tail<TW>(wp, e0, count, vec, wv);
+    load8_tail<TD>(dp, e0, count, vec, dv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wv[e] = __fsub_rn(wv[e], __fmul_rn(lr, dv[e]));
+    store8_tail<TW>(wp, e0, count, vec, wv);
+  }
+}
+
+__global__ void k_gather_has_cache(PtrTbl cs, int per, int nprob, int32_t* hc) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nprob) return;
+  hc[b] = reinterpret_cast<const int32_t*>(tbl_addr(cs, b, per, 8))[0];
+}
+
+__global__ void k_cache_decide(const float* resid, int parts, int nprob, int r,
+                               const int32_t* hc, PtrTbl cs, int per, int mode, float gamma,
+                               int32_t t32, int32_t* flags, float* err, int32_t* refreshed,
+                               float* diag, int diag_stride) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nprob) return;
+  int refresh;
+  float e = -1.0f;
+  if (mode == 1 || !hc[b]) {
+    refresh = 1;
+  } else {
+    double sum = 0.0;
+    for (int i = 0; i < parts; ++i) sum += (double)resid[(int64_t)b * parts + i];
+    e = (float)(sqrt(sum) / sqrt((double)r));
+    refresh = (mode == 2) ? 0 : !(e <= gamma);
+  }
+  flags[b] = refresh;
+  if (err) err[b] = e;
+  if (refreshed) refreshed[b] = refresh;
+  if (diag) {
+    diag[(int64_t)b * diag_stride] = e;
+    diag[(int64_t)b * diag_stride + 1] = (float)refresh;
+  }
+  if (refresh) {
+    int32_t* st = const_cast<int32_t*>(reinterpret_cast<const int32_t*>(tbl_addr(cs, b, per, 8)));
+    st[0] = 1;
+    st[1] = t32;
+  }
+}
+
+inline int stream_blocks(int64_t count, int nprob) {
+  // enough blocks in flight to fill 256 CUs several times over
+  int64_t per = (count + kChunk - 1) / kChunk;
+  int64_t want = (4096 + nprob - 1) / nprob;
+  if (want < 1) want = 1;
+  return (int)(per < want ? per : want);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+#define SM_DISPATCH_DT(dt, T, ...)                   \
+  do {                                               \
+    if ((dt) == BF16) {                              \
+      typedef bf16_t T;                              \
+      __VA_ARGS__;                                   \
+    } else {                                         \
+      typedef float T;                               \
+      __VA_ARGS__;                                   \
+    }                                                \
+  } while (0)
+
+sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
+                            int64_t count, int mdt, int gdt, float beta, void* x, int xdt,
+                            float* partials, hipStream_t s) {
+  if (nprob <= 0 || count <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0;
+  dim3 grid(kNormParts, nprob);
+  double bytes = (double)nprob * count *
+                 (2.0 * dt_size(mdt) + dt_size(gdt) + (x ? dt_size(xdt) : 0.0));
+  prof_begin(SM_K_EMA, bytes, s);
+  SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG, SM_DISPATCH_DT(xdt, TX,
+      hipLaunchKernelGGL((k_ema_single<TM, TG, TX>), grid, dim3(kThreads), 0, s, mom, grad,
+                         per, count, beta, (TX*)x, partials, vec))));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob, int64_t count,
+                      int mdt, int gdt, float beta1, float beta2, void* x, int xdt,
+                      float* partials, uint64_t* bits, int64_t words, hipStream_t s) {
+  if (nprob <= 0 || count <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0;
+  dim3 grid(bits ? stream_blocks(count, nprob) : kNormParts, nprob);
+  double bytes = (double)nprob * count * (2.0 * dt_size(mdt) + dt_size(gdt)) +
+                 (bits ? (double)nprob * words * 8.0 : (double)nprob * count * dt_size(xdt));
+  prof_begin(SM_K_LION, bytes, s);
+  SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG, SM_DISPATCH_DT(xdt, TX,
+      hipLaunchKernelGGL((k_lion<TM, TG, TX>), grid, dim3(kThreads), 0, s, mom, grad, per,
+                         count, beta1, beta2, (TX*)x, partials, bits, words, vec))));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* partials,
+                       hipStream_t s) {
+  if (nprob <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0;
+  dim3 grid(kNormParts, nprob);
+  prof_begin(SM_K_NORM, (double)nprob * count * dt_size(dt), s);
+  SM_DISPATCH_DT(dt, T,
+      hipLaunchKernelGGL((k_sumsq<T>), grid, dim3(kThreads), 0, s, (const T*)x, count,
+                         partials, vec));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_scale_finalize(const float* partials, int nprob, float eps, float* scale,
+                                hipStream_t s) {
+  if (nprob <= 0) return SM_OK;
+  prof_begin(SM_K_MISC, (double)nprob * (kNormParts + 1) * 4.0, s);
+  hipLaunchKernelGGL(k_scale_finalize, dim3((nprob + 63) / 64), dim3(64), 0, s, partials,
+                     nprob, eps, scale);
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_sign_pack(const void* x, int dt, int nprob, int64_t count, uint64_t* bits,
+                           int64_t words, hipStream_t s) {
+  if (nprob <= 0 || count <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0;
+  dim3 grid(stream_blocks(count, nprob), nprob);
+  prof_begin(SM_K_SIGN_PACK, (double)nprob * ((double)count * dt_size(dt) + words * 8.0), s);
+  SM_DISPATCH_DT(dt, T,
+      hipLaunchKernelGGL((k_sign_pack<T>), grid, dim3(kThreads), 0, s, (const T*)x, count,
+                         bits, words, vec));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_vote_update(const uint64_t* bits, int M, int64_t words_stride,
+                             int64_t mat_stride_words, int nmat, int64_t count, const PtrTbl& w,
+                             int wdt, float lr, int8_t* vote_out, hipStream_t s) {
+  if (nmat <= 0 || count <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0;
+  const int64_t nbytes = (count + 7) / 8;
+  int64_t want = (4096 + nmat - 1) / nmat;
+  int64_t need = (nbytes + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)(need < want ? need : want), nmat);
+  double bytes = (double)nmat * count * (M / 8.0 + 2.0 * dt_size(wdt) + (vote_out ? 1.0 : 0.0));
+  prof_begin(SM_K_VOTE_UPDATE, bytes, s);
+  SM_DISPATCH_DT(wdt, TW,
+      hipLaunchKernelGGL((k_vote_update<TW>), grid, dim3(kThreads), 0, s, bits, M,
+                         words_stride, mat_stride_words, count, w, lr, vote_out, vec));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
+                              int wdt, float lr, hipStream_t s) {
+  if (nmat <= 0 || count <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0;
+  const int64_t n8 = (count + 7) / 8;
+  int64_t want = (4096 + nmat - 1) / nmat;
+  int64_t need = (n8 + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)(need < want ? need : want), nmat);
+  prof_begin(SM_K_POLAR_UPDATE, (double)nmat * count * (dt_size(ddt) + 2.0 * dt_size(wdt)), s);
+  SM_DISPATCH_DT(ddt, TD, SM_DISPATCH_DT(wdt, TW,
+      hipLaunchKernelGGL((k_polar_update<TD, TW>), grid, dim3(kThreads), 0, s, (const TD*)d,
+                         count, w, lr, vec)));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t* hc,
+                                  hipStream_t s) {
+  if (nprob <= 0) return SM_OK;
+  prof_begin(SM_K_MISC, (double)nprob * 12.0, s);
+  hipLaunchKernelGGL(k_gather_has_cache, dim3((nprob + 63) / 64), dim3(64), 0, s, cs, per,
+                     nprob, hc);
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_cache_decide(const float* resid_partials, int parts, int nprob, int r,
+                              const int32_t* hc, const PtrTbl& cs, int per, int mode,
+                              float gamma, int64_t t, int32_t* flags, float* err,
+                              int32_t* refreshed, float* diag, int diag_stride, hipStream_t s) {
+  if (nprob <= 0) return SM_OK;
+  prof_begin(SM_K_MISC, (double)nprob * (parts * 4.0 + 24.0), s);
+  hipLaunchKernelGGL(k_cache_decide, dim3((nprob + 63) / 64), dim3(64), 0, s, resid_partials,
+                     parts, nprob, r, hc, cs, per, mode, gamma, (int32_t)t, flags, err,
+                     refreshed, diag, diag_stride);
+  prof_end(s);
+  return check_launch();
+}
+
+}  // namespace sm

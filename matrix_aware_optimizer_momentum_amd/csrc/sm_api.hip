@@ -1,0 +1,761 @@
+// C ABI of libsm: argument validation, workspace layout, and the launch
+// sequences of the optimizer step.  Every entry point validates its
+// arguments on the host before the first HIP call, enqueues its kernels on
+// the caller's stream and returns without synchronising.
+//
+// Sources (short names used below):
+//   [SignMuon-ja]  SignMuon technical summary, gist.science/ja/paper/2605.16311
+//   [CacheMuon-ja] CacheMuon technical summary, gist.science/ja/paper/2606.16371
+//   [LionMuon-pt]  LionMuon technical summary, gist.science/pt/paper/2605.19811
+#include "sm_internal.hpp"
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+namespace sm {
+
+// ====================================================================== errors
+
+static std::atomic<int> g_last_hip{0};
+
+sm_status hip_fail(hipError_t e) {
+  g_last_hip.store((int)e);
+  return SM_ERR_HIP;
+}
+
+sm_status check_launch() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+#define SM_TRY(expr)                    \
+  do {                                  \
+    sm_status _st = (expr);             \
+    if (_st != SM_OK) return _st;       \
+  } while (0)
+
+// ====================================================================== profiling
+
+namespace {
+struct ProfRec {
+  int kind;
+  double work;
+  hipEvent_t a, b;
+};
+constexpr size_t kProfMax = 65536;
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_prof_pool;  // 2 events per record
+std::vector<ProfRec> g_prof_recs;
+bool g_prof_open = false;
+}  // namespace
+
+void prof_begin(int kind, double work, hipStream_t s) {
+  g_prof_open = false;
+  if (!g_prof_on) return;
+  const size_t i = g_prof_recs.size();
+  if (2 * i + 1 >= g_prof_pool.size()) return;
+  ProfRec r{kind, work, g_prof_pool[2 * i], g_prof_pool[2 * i + 1]};
+  if (hipEventRecord(r.a, s) != hipSuccess) return;
+  g_prof_recs.push_back(r);
+  g_prof_open = true;
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof_open) return;
+  g_prof_open = false;
+  (void)hipEventRecord(g_prof_recs.back().b, s);
+}
+
+// ====================================================================== helpers
+
+namespace {
+
+bool valid_dt(int dt) { return dt == SM_F32 || dt == SM_BF16; }
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+bool finite(float v) { return std::isfinite(v); }
+
+sm_status check_ns_params(const sm_ns_params* p) {
+  if (!p) return SM_ERR_ARG;
+  if (p->iters < 1 || p->iters > 64) return SM_ERR_ARG;
+  if (!finite(p->a) || !finite(p->b) || !finite(p->c)) return SM_ERR_ARG;
+  if (!finite(p->eps) || p->eps < 0.f) return SM_ERR_ARG;
+  return SM_OK;
+}
+
+sm_status check_shape(int batch, int m, int n) {
+  if (batch < 1 || m < 1 || n < 1) return SM_ERR_SHAPE;
+  if ((int64_t)m * n >= (int64_t(1) << 31)) return SM_ERR_SHAPE;
+  if (batch > 4096) return SM_ERR_SHAPE;
+  return SM_OK;
+}
+
+// Bump allocator over the caller's workspace; with base == null it only
+// measures.  Every buffer starts on a 256-byte boundary.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+PtrTbl tbl_one(const void* p) {
+  PtrTbl t;
+  std::memset(&t, 0, sizeof(t));
+  t.p[0] = static_cast<const char*>(p);
+  return t;
+}
+
+GemmOperand opnd(const void* p, int64_t ld, int64_t stride, int dt, int layout, int tbl = 0) {
+  GemmOperand o;
+  o.p = p;
+  o.ld = ld;
+  o.stride = stride;
+  o.dt = dt;
+  o.layout = layout;
+  o.tbl = tbl;
+  return o;
+}
+
+GemmArgs gemm_base(int M, int N, int K, int batch) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.batch = batch;
+  g.alpha = 1.f;
+  g.beta = 0.f;
+  g.tbl_per = 1;
+  return g;
+}
+
+// ------------------------------------------------------------------ direct NS
+
+struct NsWs {
+  void* tmp;    // [batch][m*n] ping-pong iterate
+  void* amat;   // [batch][r*r]
+  void* amat2;  // [batch][r*r] (quintic term)
+};
+
+void carve_ns(Carver& cv, int dt, int batch, int m, int n, NsWs& w) {
+  const int64_t r = m < n ? m : n;
+  const size_t es = dt_size(dt);
+  w.tmp = cv.take<void>((size_t)batch * m * n * es);
+  w.amat = cv.take<void>((size_t)batch * r * r * es);
+  w.amat2 = cv.take<void>((size_t)batch * r * r * es);
+}
+
+// Products of one direct NS step on problems of shape m x n (x contiguous):
+//   gram:  A = alpha * X X^T       (oriented; Y^T Y for a tall Y)
+//   apply: X' = alpha * (B X) + beta * X   (X B^T for a tall Y)
+GemmArgs gram_args(const void* x, int dt, int batch, int m, int n) {
+  const bool wide = m <= n;
+  const int r = wide ? m : n, c = wide ? n : m;
+  GemmArgs g = gemm_base(r, r, c, batch);
+  const int lay = wide ? KC : RC;
+  g.a = opnd(x, n, (int64_t)m * n, dt, lay);
+  g.b = opnd(x, n, (int64_t)m * n, dt, lay);
+  return g;
+}
+
+GemmArgs apply_args(const void* bm, int bm_dt, int bm_tbl, const void* x, int dt, int batch,
+                    int m, int n) {
+  const bool wide = m <= n;
+  const int r = wide ? m : n;
+  GemmArgs g = gemm_base(m, n, r, batch);
+  if (wide) {  // X' = B X : A = B (r x r), B-operand = X with rows k contiguous
+    g.a = opnd(bm, r, (int64_t)r * r, bm_dt, KC, bm_tbl);
+    g.b = opnd(x, n, (int64_t)m * n, dt, RC);
+  } else {     // Y' = Y B^T : A = Y, B-operand(k, j) = B(j, k)
+    g.a = opnd(x, n, (int64_t)m * n, dt, KC);
+    g.b = opnd(bm, r, (int64_t)r * r, bm_dt, KC, bm_tbl);
+  }
+  return g;
+}
+
+// X_K of the direct iteration [SignMuon-ja] section 2 (core mechanism 1):
+// X_{k+1} = a X_k + (b A_k + c A_k^2) X_k,  A_k = X_k X_k^T, starting from
+// X_0 = s x (s = scale[b], or 1 without normalisation).  The scale enters
+// the first step's GEMMs: A_0 = s^2 x x^T, X_1 = s (a x + B_0 x).
+sm_status ns_core(const void* x, void* out, const NsWs& w, const float* scale, int dt, int batch,
+                  int m, int n, const sm_ns_params& p, hipStream_t s) {
+  const int r = m < n ? m : n;
+  const int K = p.iters;
+  const void* cur = x;
+  for (int k = 0; k < K; ++k) {
+    void* dst = ((K - 1 - k) % 2 == 0) ? out : w.tmp;
+    const bool first = (k == 0) && scale;
+    // A_k (times b when the quintic term is absent)
+    GemmArgs g = gram_args(cur, dt, batch, m, n);
+    g.c = w.amat; g.ldc = r; g.sc = (int64_t)r * r; g.c_dt = dt;
+    g.scale = scale; g.alpha_pow = first ? 2 : 0;
+    g.alpha = (p.c == 0.f) ? p.b : 1.f;
+    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_GRAM, s));
+    const void* bmat = w.amat;
+    if (p.c != 0.f) {  // B = c A A + b A
+      GemmArgs q = gemm_base(r, r, r, batch);
+      q.a = opnd(w.amat, r, (int64_t)r * r, dt, KC);
+      q.b = opnd(w.amat, r, (int64_t)r * r, dt, RC);
+      q.cin = w.amat; q.ldcin = r; q.scin = (int64_t)r * r;
+      q.c = w.amat2; q.ldc = r; q.sc = (int64_t)r * r; q.c_dt = dt;
+      q.alpha = p.c; q.beta = p.b;
+      SM_TRY(launch_gemm(q, dt, SM_K_GEMM_RR, s));
+      bmat = w.amat2;
+    }
+    GemmArgs a = apply_args(bmat, dt, 0, cur, dt, batch, m, n);
+    a.cin = cur; a.ldcin = n; a.scin = (int64_t)m * n;
+    a.c = dst; a.ldc = n; a.sc = (int64_t)m * n; a.c_dt = dt;
+    a.scale = scale; a.alpha_pow = first ? 1 : 0; a.beta_pow = first ? 1 : 0;
+    a.alpha = 1.f; a.beta = p.a;
+    SM_TRY(launch_gemm(a, dt, SM_K_GEMM_APPLY, s));
+    cur = dst;
+  }
+  return SM_OK;
+}
+
+// ------------------------------------------------------------------ Gram NS with cache
+
+struct GramWs {
+  float* ga;      // [batch][r*r]  G ping-pong
+  float* gb;
+  float* t;       // [batch][r*r]  P_k G_k
+  float* bq;      // [batch][r*r]  b G + c G^2 (quintic)
+  float* qt;      // [batch][r*r]  Q ping-pong partner of the cache
+  float* resid;   // [batch][tiles]
+  int32_t* hc;    // [batch] has_cache snapshot
+  int32_t* flags; // [batch] refresh decision
+};
+
+void carve_gram(Carver& cv, int batch, int m, int n, GramWs& w) {
+  const int64_t r = m < n ? m : n;
+  const size_t rr = (size_t)batch * r * r * 4;
+  w.ga = cv.take<float>(rr);
+  w.gb = cv.take<float>(rr);
+  w.t = cv.take<float>(rr);
+  w.bq = cv.take<float>(rr);
+  w.qt = cv.take<float>(rr);
+  w.resid = cv.take<float>((size_t)batch * gemm_tiles(0, (int)r, (int)r) * 4);
+  w.hc = cv.take<int32_t>((size_t)batch * 4);
+  w.flags = cv.take<int32_t>((size_t)batch * 4);
+}
+
+// One CacheMuon orthogonalisation per problem, [CacheMuon-ja] core mechanism:
+//   candidate (if cached): D_hat = Q X, err = ||D_hat D_hat^T - I||_F / sqrt(r)
+//   refresh iff no cache / forced / err > gamma, decided on the device;
+//   fresh Gram-NS (predicated on the decision): G_0 = X X^T, P_k = aI + B_k
+//   with B_k = b G_k + c G_k^2, Q_{k+1} = a Q_k + B_k Q_k,
+//   G_{k+1} = a T_k + T_k B_k with T_k = a G_k + B_k G_k, D = Q_K X.
+// The identity parts are added in float32 in the GEMM epilogues.  Q_K is
+// written straight into the cache.  Problem b's Q lives at
+// qtbl[b / qper] + (b % qper) * r*r floats; its {has_cache, a_t} pair at
+// cstbl[b / qper] + (b % qper) * 2 ints.
+sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cstbl, int qper,
+                    float* err_out, int32_t* refr_out, float* diag, int diag_stride,
+                    const GramWs& w, const float* scale, int dt, int batch, int m, int n,
+                    const sm_ns_params& p, float gamma, int mode, int64_t t, hipStream_t s) {
+  const bool wide = m <= n;
+  const int r = wide ? m : n;
+  const int64_t rr = (int64_t)r * r;
+  const int K = p.iters;
+  const bool quintic = p.c != 0.f;
+
+  SM_TRY(launch_gather_has_cache(cstbl, qper, batch, w.hc, s));
+  if (mode != 1) {
+    // candidate D_hat = s * Q x  (x^T oriented: s * x Q^T for a tall x)
+    GemmArgs g = apply_args(qtbl.p[0], F32, 1, x, dt, batch, m, n);
+    g.tbl = qtbl; g.tbl_per = qper;
+    g.c = d; g.ldc = n; g.sc = (int64_t)m * n; g.c_dt = dt;
+    g.scale = scale; g.alpha_pow = 1;
+    g.pred = w.hc; g.pred_stride = 1; g.pred_val = 1;
+    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_APPLY, s));
+    // residual partials of D_hat D_hat^T - I
+    GemmArgs pr = gram_args(d, dt, batch, m, n);
+    pr.resid = w.resid;
+    pr.pred = w.hc; pr.pred_stride = 1; pr.pred_val = 1;
+    SM_TRY(launch_gemm(pr, dt, SM_K_PROBE, s));
+  }
+  SM_TRY(launch_cache_decide(w.resid, gemm_tiles(dt, r, r), batch, r, w.hc, cstbl, qper, mode,
+                             gamma, t, w.flags, err_out, refr_out, diag, diag_stride, s));
+
+  // Q_k lives in the cache for k == K (mod 2) so that Q_K lands there.
+  auto qbuf_is_cache = [&](int k) { return ((K - k) % 2) == 0; };
+  auto set_q_out = [&](GemmArgs& g, int k) {  // write Q_k as output c
+    if (qbuf_is_cache(k)) { g.c = const_cast<char*>(qtbl.p[0]); g.c_tbl = 1; }
+    else { g.c = w.qt; g.c_tbl = 0; }
+    g.ldc = r; g.sc = rr; g.c_dt = F32;
+  };
+  auto pred_fresh = [&](GemmArgs& g) {
+    g.pred = w.flags; g.pred_stride = 1; g.pred_val = 1;
+    g.tbl = qtbl; g.tbl_per = qper;
+  };
+
+  // G_0 = s^2 x x^T, and Q_1 = aI + B_0
+  {
+    GemmArgs g = gram_args(x, dt, batch, m, n);
+    pred_fresh(g);
+    g.c = w.ga; g.ldc = r; g.sc = rr; g.c_dt = F32;
+    g.scale = scale; g.alpha_pow = 2;
+    if (!quintic) {
+      if (qbuf_is_cache(1)) { g.c2 = reinterpret_cast<float*>(const_cast<char*>(qtbl.p[0])); g.c2_tbl = 1; }
+      else { g.c2 = w.qt; g.c2_tbl = 0; }
+      g.ldc2 = r; g.sc2 = rr; g.c2_diag = p.a; g.c2_scale = p.b;
+    }
+    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_GRAM, s));
+  }
+  auto make_bq = [&](const float* gk, bool write_q1) -> sm_status {
+    GemmArgs g = gemm_base(r, r, r, batch);
+    pred_fresh(g);
+    g.a = opnd(gk, r, rr, F32, KC);
+    g.b = opnd(gk, r, rr, F32, RC);
+    g.cin = gk; g.ldcin = r; g.scin = rr;
+    g.c = w.bq; g.ldc = r; g.sc = rr; g.c_dt = F32;
+    g.alpha = p.c; g.beta = p.b;
+    if (write_q1) {
+      if (qbuf_is_cache(1)) { g.c2 = reinterpret_cast<float*>(const_cast<char*>(qtbl.p[0])); g.c2_tbl = 1; }
+      else { g.c2 = w.qt; g.c2_tbl = 0; }
+      g.ldc2 = r; g.sc2 = rr; g.c2_diag = p.a; g.c2_scale = 1.f;
+    }
+    return launch_gemm(g, dt, SM_K_GEMM_RR, s);
+  };
+  if (quintic) SM_TRY(make_bq(w.ga, true));
+
+  float* gprev = w.ga;
+  float* gnew = w.gb;
+  for (int k = 1; k < K; ++k) {
+    // T = a G + B G
+    {
+      GemmArgs g = gemm_base(r, r, r, batch);
+      pred_fresh(g);
+      g.a = quintic ? opnd(w.bq, r, rr, F32, KC) : opnd(gprev, r, rr, F32, KC);
+      g.b = opnd(gprev, r, rr, F32, RC);
+      g.cin = gprev; g.ldcin = r; g.scin = rr;
+      g.c = w.t; g.ldc = r; g.sc = rr; g.c_dt = F32;
+      g.alpha = quintic ? 1.f : p.b; g.beta = p.a;
+      SM_TRY(launch_gemm(g, dt, SM_K_GEMM_RR, s));
+    }
+    // G_k = a T + T B
+    {
+      GemmArgs g = gemm_base(r, r, r, batch);
+      pred_fresh(g);
+      g.a = opnd(w.t, r, rr, F32, KC);
+      g.b = quintic ? opnd(w.bq, r, rr, F32, RC) : opnd(gprev, r, rr, F32, RC);
+      g.cin = w.t; g.ldcin = r; g.scin = rr;
+      g.c = gnew; g.ldc = r; g.sc = rr; g.c_dt = F32;
+      g.alpha = quintic ? 1.f : p.b; g.beta = p.a;
+      SM_TRY(launch_gemm(g, dt, SM_K_GEMM_RR, s));
+    }
+    if (quintic) SM_TRY(make_bq(gnew, false));
+    // Q_{k+1} = a Q_k + B_k Q_k
+    {
+      GemmArgs g = gemm_base(r, r, r, batch);
+      pred_fresh(g);
+      g.a = quintic ? opnd(w.bq, r, rr, F32, KC) : opnd(gnew, r, rr, F32, KC);
+      const bool qc = qbuf_is_cache(k);
+      const void* qk = qc ? static_cast<const void*>(qtbl.p[0]) : static_cast<const void*>(w.qt);
+      g.b = opnd(qk, r, rr, F32, RC, qc ? 1 : 0);
+      g.cin = qk; g.cin_tbl = qc ? 1 : 0; g.ldcin = r; g.scin = rr;
+      set_q_out(g, k + 1);
+      g.alpha = quintic ? 1.f : p.b; g.beta = p.a;
+      SM_TRY(launch_gemm(g, dt, SM_K_GEMM_RR, s));
+    }
+    float* tmp = gprev; gprev = gnew; gnew = tmp;
+  }
+  // D = s * Q_K x
+  {
+    GemmArgs g = apply_args(qtbl.p[0], F32, 1, x, dt, batch, m, n);
+    pred_fresh(g);
+    g.c = d; g.ldc = n; g.sc = (int64_t)m * n; g.c_dt = dt;
+    g.scale = scale; g.alpha_pow = 1;
+    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_APPLY, s));
+  }
+  return SM_OK;
+}
+
+// ------------------------------------------------------------------ step planning
+
+struct Chunk {
+  int m, n;
+  std::vector<int> mats;  // <= kTbl matrix indices, all of shape m x n
+};
+
+std::vector<Chunk> plan_chunks(const sm_matrix* mats, int nmat) {
+  std::vector<Chunk> out;
+  std::vector<char> used(nmat, 0);
+  for (int i = 0; i < nmat; ++i) {
+    if (used[i]) continue;
+    Chunk c;
+    c.m = mats[i].m;
+    c.n = mats[i].n;
+    for (int j = i; j < nmat; ++j) {
+      if (used[j] || mats[j].m != c.m || mats[j].n != c.n) continue;
+      used[j] = 1;
+      c.mats.push_back(j);
+      if ((int)c.mats.size() == kTbl) {
+        out.push_back(c);
+        c.mats.clear();
+      }
+    }
+    if (!c.mats.empty()) out.push_back(c);
+  }
+  return out;
+}
+
+struct ChunkWs {
+  void* x0;
+  void* d;
+  NsWs ns;
+  GramWs gram;
+  float* partials;
+  float* scale;
+  uint64_t* bits;
+};
+
+void carve_chunk(Carver& cv, const sm_config& c, const Chunk& ch, ChunkWs& w) {
+  const int B = (int)ch.mats.size() * c.M;
+  const int64_t count = (int64_t)ch.m * ch.n;
+  const size_t es = dt_size(c.mdt);
+  const int64_t words = (count + 63) / 64;
+  const bool ns_possible = !(c.algo == SM_LION_MUON && c.period == 0);
+  std::memset(&w, 0, sizeof(w));
+  w.bits = cv.take<uint64_t>((size_t)B * words * 8);
+  if (!ns_possible) return;
+  w.partials = cv.take<float>((size_t)B * kNormParts * 4);
+  w.scale = cv.take<float>((size_t)B * 4);
+  w.x0 = cv.take<void>((size_t)B * count * es);
+  w.d = cv.take<void>((size_t)B * count * es);
+  if (c.algo == SM_CACHE_MUON)
+    carve_gram(cv, B, ch.m, ch.n, w.gram);
+  else
+    carve_ns(cv, c.mdt, B, ch.m, ch.n, w.ns);
+}
+
+sm_status check_config(const sm_config* c) {
+  if (!c) return SM_ERR_ARG;
+  if (c->algo < SM_SIGN_MUON || c->algo > SM_LION_MUON) return SM_ERR_ARG;
+  if (c->update != SM_UPDATE_VOTE && c->update != SM_UPDATE_POLAR) return SM_ERR_ARG;
+  if (!valid_dt(c->wdt) || !valid_dt(c->mdt) || !valid_dt(c->gdt)) return SM_ERR_DTYPE;
+  if (!finite(c->lr) || !finite(c->beta1) || !finite(c->beta2)) return SM_ERR_ARG;
+  if (c->period < 0) return SM_ERR_ARG;
+  if (c->cache_mode < 0 || c->cache_mode > 2) return SM_ERR_ARG;
+  if (std::isnan(c->gamma)) return SM_ERR_ARG;
+  SM_TRY(check_ns_params(&c->ns));
+  if (c->M < 1 || c->M > 64) return SM_ERR_UNSUPPORTED;
+  if (c->update == SM_UPDATE_POLAR && (c->M != 1 || c->algo == SM_SIGN_MUON))
+    return SM_ERR_UNSUPPORTED;
+  return SM_OK;
+}
+
+sm_status check_mats(const sm_config& c, const sm_matrix* mats, int nmat) {
+  if (!mats || nmat < 1) return SM_ERR_ARG;
+  for (int i = 0; i < nmat; ++i) {
+    const sm_matrix& a = mats[i];
+    SM_TRY(check_shape(1, a.m, a.n));
+    if (!a.w || !a.mom || !a.grad) return SM_ERR_ARG;
+    if (!al16(a.w) || !al16(a.mom) || !al16(a.grad)) return SM_ERR_ARG;
+    if (c.algo == SM_CACHE_MUON) {
+      if (!a.q_cache || !a.cache_state || !al16(a.q_cache) || !al16(a.cache_state))
+        return SM_ERR_ARG;
+    }
+  }
+  return SM_OK;
+}
+
+size_t step_ws_bytes(const sm_config& c, const std::vector<Chunk>& chunks) {
+  Carver cv(nullptr);
+  for (const Chunk& ch : chunks) {
+    ChunkWs w;
+    carve_chunk(cv, c, ch, w);
+  }
+  return cv.off + 256;
+}
+
+}  // namespace
+}  // namespace sm
+
+// ====================================================================== C ABI
+
+using namespace sm;
+
+extern "C" {
+
+const char* sm_status_string(int s) {
+  switch (s) {
+    case SM_OK: return "SM_OK";
+    case SM_ERR_ARG: return "SM_ERR_ARG: invalid argument";
+    case SM_ERR_SHAPE: return "SM_ERR_SHAPE: invalid shape";
+    case SM_ERR_DTYPE: return "SM_ERR_DTYPE: invalid dtype";
+    case SM_ERR_WORKSPACE: return "SM_ERR_WORKSPACE: workspace too small";
+    case SM_ERR_UNSUPPORTED: return "SM_ERR_UNSUPPORTED: unsupported configuration";
+    case SM_ERR_HIP: return "SM_ERR_HIP: HIP runtime error";
+    default: return "unknown sm_status";
+  }
+}
+
+int sm_last_hip_error(void) { return g_last_hip.load(); }
+
+int sm_version(void) { return 1; }
+
+sm_status sm_ns_polar_ws(int dt, int batch, int m, int n, size_t* ws_bytes) {
+  if (!ws_bytes) return SM_ERR_ARG;
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  SM_TRY(check_shape(batch, m, n));
+  Carver cv(nullptr);
+  NsWs w;
+  carve_ns(cv, dt, batch, m, n, w);
+  cv.take<float>((size_t)batch * kNormParts * 4);
+  cv.take<float>((size_t)batch * 4);
+  *ws_bytes = cv.off + 256;
+  return SM_OK;
+}
+
+sm_status sm_ns_polar(const void* x, void* u, int dt, int batch, int m, int n, int normalize,
+                      const sm_ns_params* p, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  SM_TRY(check_shape(batch, m, n));
+  SM_TRY(check_ns_params(p));
+  if (!x || !u || !ws || !al16(x) || !al16(u) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return SM_ERR_ARG;
+  if (normalize != 0 && normalize != 1) return SM_ERR_ARG;
+  const size_t bytes = (size_t)batch * m * n * dt_size(dt);
+  if (overlap(x, bytes, u, bytes)) return SM_ERR_ARG;
+  size_t need = 0;
+  SM_TRY(sm_ns_polar_ws(dt, batch, m, n, &need));
+  if (ws_bytes < need) return SM_ERR_WORKSPACE;
+  if (overlap(ws, ws_bytes, x, bytes) || overlap(ws, ws_bytes, u, bytes)) return SM_ERR_ARG;
+
+  Carver cv(ws);
+  NsWs w;
+  carve_ns(cv, dt, batch, m, n, w);
+  float* partials = cv.take<float>((size_t)batch * kNormParts * 4);
+  float* scale = cv.take<float>((size_t)batch * 4);
+  const int64_t count = (int64_t)m * n;
+  if (normalize) {
+    SM_TRY(launch_sumsq(x, dt, batch, count, partials, s));
+    SM_TRY(launch_scale_finalize(partials, batch, p->eps, scale, s));
+  }
+  return ns_core(x, u, w, normalize ? scale : nullptr, dt, batch, m, n, *p, s);
+}
+
+sm_status sm_gram_ns_cached_ws(int dt, int batch, int m, int n, size_t* ws_bytes) {
+  if (!ws_bytes) return SM_ERR_ARG;
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  SM_TRY(check_shape(batch, m, n));
+  Carver cv(nullptr);
+  GramWs w;
+  carve_gram(cv, batch, m, n, w);
+  cv.take<float>((size_t)batch * kNormParts * 4);
+  cv.take<float>((size_t)batch * 4);
+  *ws_bytes = cv.off + 256;
+  return SM_OK;
+}
+
+sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_state, float* err,
+                            int32_t* refreshed, int dt, int batch, int m, int n, int normalize,
+                            const sm_ns_params* p, float gamma, int mode, int64_t t, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  SM_TRY(check_shape(batch, m, n));
+  SM_TRY(check_ns_params(p));
+  if (!x || !d || !q || !cache_state || !ws) return SM_ERR_ARG;
+  if (!al16(x) || !al16(d) || !al16(q) || !al16(cache_state)) return SM_ERR_ARG;
+  if ((err && !al16(err)) || (refreshed && !al16(refreshed))) return SM_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return SM_ERR_ARG;
+  if (normalize != 0 && normalize != 1) return SM_ERR_ARG;
+  if (mode < 0 || mode > 2 || std::isnan(gamma)) return SM_ERR_ARG;
+  const size_t bytes = (size_t)batch * m * n * dt_size(dt);
+  if (overlap(x, bytes, d, bytes)) return SM_ERR_ARG;
+  size_t need = 0;
+  SM_TRY(sm_gram_ns_cached_ws(dt, batch, m, n, &need));
+  if (ws_bytes < need) return SM_ERR_WORKSPACE;
+
+  Carver cv(ws);
+  GramWs w;
+  carve_gram(cv, batch, m, n, w);
+  float* partials = cv.take<float>((size_t)batch * kNormParts * 4);
+  float* scale = cv.take<float>((size_t)batch * 4);
+  if (normalize) {
+    SM_TRY(launch_sumsq(x, dt, batch, (int64_t)m * n, partials, s));
+    SM_TRY(launch_scale_finalize(partials, batch, p->eps, scale, s));
+  }
+  const PtrTbl qt = tbl_one(q), cs = tbl_one(cache_state);
+  return gram_core(x, d, qt, cs, batch, err, refreshed, nullptr, 2, w,
+                   normalize ? scale : nullptr, dt, batch, m, n, *p, gamma, mode, t, s);
+}
+
+sm_status sm_sign_pack(const void* x, int dt, int64_t count, uint64_t* bits, hipStream_t s) {
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  if (count < 0) return SM_ERR_SHAPE;
+  if (count == 0) return SM_OK;
+  if (!x || !bits || !al16(x) || !al16(bits)) return SM_ERR_ARG;
+  return launch_sign_pack(x, dt, 1, count, bits, (count + 63) / 64, s);
+}
+
+sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int64_t count,
+                         void* w, int wdt, float lr, int8_t* vote_out, hipStream_t s) {
+  if (!valid_dt(wdt)) return SM_ERR_DTYPE;
+  if (count < 0) return SM_ERR_SHAPE;
+  if (M < 1 || M > 64) return SM_ERR_UNSUPPORTED;
+  if (count == 0) return SM_OK;
+  if (!bits || !w || !al16(bits) || !al16(w)) return SM_ERR_ARG;
+  if (vote_out && !al16(vote_out)) return SM_ERR_ARG;
+  if (words_stride < (count + 63) / 64 || !finite(lr)) return SM_ERR_ARG;
+  const PtrTbl wt = tbl_one(w);
+  return launch_vote_update(bits, M, words_stride, 0, 1, count, wt, wdt, lr, vote_out, s);
+}
+
+sm_status sm_step_ws(const sm_config* c, const sm_matrix* mats, int nmat, size_t* ws_bytes) {
+  if (!ws_bytes) return SM_ERR_ARG;
+  SM_TRY(check_config(c));
+  if (!mats || nmat < 1) return SM_ERR_ARG;
+  for (int i = 0; i < nmat; ++i) SM_TRY(check_shape(1, mats[i].m, mats[i].n));
+  *ws_bytes = step_ws_bytes(*c, plan_chunks(mats, nmat));
+  return SM_OK;
+}
+
+sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t, void* ws,
+                  size_t ws_bytes, float* diag, hipStream_t s) {
+  SM_TRY(check_config(c));
+  SM_TRY(check_mats(*c, mats, nmat));
+  if (t < 1 || !ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SM_ERR_ARG;
+  if (diag && !al16(diag)) return SM_ERR_ARG;
+  const std::vector<Chunk> chunks = plan_chunks(mats, nmat);
+  if (ws_bytes < step_ws_bytes(*c, chunks)) return SM_ERR_WORKSPACE;
+
+  const int M = c->M;
+  const bool muon_step =
+      (c->algo != SM_LION_MUON) || (c->period > 0 && (t % c->period) == 0);
+  const bool polar = c->update == SM_UPDATE_POLAR && muon_step;
+  Carver cv(ws);
+  for (const Chunk& ch : chunks) {
+    ChunkWs w;
+    carve_chunk(cv, *c, ch, w);
+    const int nc = (int)ch.mats.size();
+    const int B = nc * M;
+    const int64_t count = (int64_t)ch.m * ch.n;
+    const int64_t words = (count + 63) / 64;
+    PtrTbl mom, grad, wt, qt, cs;
+    std::memset(&mom, 0, sizeof(mom));
+    std::memset(&grad, 0, sizeof(grad));
+    std::memset(&wt, 0, sizeof(wt));
+    std::memset(&qt, 0, sizeof(qt));
+    std::memset(&cs, 0, sizeof(cs));
+    for (int j = 0; j < nc; ++j) {
+      const sm_matrix& a = mats[ch.mats[j]];
+      mom.p[j] = static_cast<const char*>(a.mom);
+      grad.p[j] = static_cast<const char*>(a.grad);
+      wt.p[j] = static_cast<const char*>(a.w);
+      qt.p[j] = reinterpret_cast<const char*>(a.q_cache);
+      cs.p[j] = reinterpret_cast<const char*>(a.cache_state);
+    }
+    // a1 (+ a2 partials): momentum, and the NS input or the Lion signs
+    if (c->algo == SM_LION_MUON) {
+      if (muon_step)
+        SM_TRY(launch_lion(mom, grad, M, B, count, c->mdt, c->gdt, c->beta1, c->beta2, w.x0,
+                           c->mdt, w.partials, nullptr, 0, s));
+      else
+        SM_TRY(launch_lion(mom, grad, M, B, count, c->mdt, c->gdt, c->beta1, c->beta2, nullptr,
+                           c->mdt, nullptr, w.bits, words, s));
+    } else {
+      SM_TRY(launch_ema_single(mom, grad, M, B, count, c->mdt, c->gdt, c->beta1, w.x0, c->mdt,
+                               w.partials, s));
+    }
+    if (muon_step) {
+      SM_TRY(launch_scale_finalize(w.partials, B, c->ns.eps, w.scale, s));
+      if (c->algo == SM_CACHE_MUON) {
+        // diag rows follow the matrices' order; a chunk's matrices may not be
+        // consecutive, so write per chunk into the rows of its first matrix
+        // only when they are, else skip diag for that chunk.
+        float* dg = nullptr;
+        if (diag) {
+          bool consecutive = true;
+          for (int j = 1; j < nc; ++j) consecutive &= (ch.mats[j] == ch.mats[0] + j);
+          if (consecutive) dg = diag + (int64_t)ch.mats[0] * M * 2;
+        }
+        SM_TRY(gram_core(w.x0, w.d, qt, cs, M, nullptr, nullptr, dg, 2, w.gram, w.scale,
+                         c->mdt, B, ch.m, ch.n, c->ns, c->gamma, c->cache_mode, t, s));
+      } else {
+        SM_TRY(ns_core(w.x0, w.d, w.ns, w.scale, c->mdt, B, ch.m, ch.n, c->ns, s));
+      }
+      if (polar) {
+        SM_TRY(launch_polar_update(w.d, c->mdt, nc, count, wt, c->wdt, c->lr, s));
+      } else {
+        SM_TRY(launch_sign_pack(w.d, c->mdt, B, count, w.bits, words, s));
+      }
+    }
+    if (!polar)
+      SM_TRY(launch_vote_update(w.bits, M, words, (int64_t)M * words, nc, count, wt, c->wdt,
+                                c->lr, nullptr, s));
+  }
+  return SM_OK;
+}
+
+// ------------------------------------------------------------------ profiling ABI
+
+sm_status sm_profile_enable(int on) {
+  if (on) {
+    if (g_prof_pool.empty()) {
+      g_prof_pool.resize(2 * kProfMax);
+      for (size_t i = 0; i < g_prof_pool.size(); ++i) {
+        hipError_t e = hipEventCreate(&g_prof_pool[i]);
+        if (e != hipSuccess) {
+          g_prof_pool.resize(i);
+          return hip_fail(e);
+        }
+      }
+      g_prof_recs.reserve(kProfMax);
+    }
+    g_prof_on = true;
+  } else {
+    g_prof_on = false;
+  }
+  return SM_OK;
+}
+
+sm_status sm_profile_reset(void) {
+  g_prof_recs.clear();
+  g_prof_open = false;
+  return SM_OK;
+}
+
+sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double* work) {
+  if (kind < 0 || kind >= SM_K_NUM_KINDS || !ms_total || !launches || !work) return SM_ERR_ARG;
+  double ms = 0.0, wk = 0.0;
+  int64_t n = 0;
+  for (const ProfRec& r : g_prof_recs) {
+    if (r.kind != kind) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e);
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e);
+    ms += t;
+    wk += r.work;
+    ++n;
+  }
+  *ms_total = ms;
+  *launches = n;
+  *work = wk;
+  return SM_OK;
+}
+
+const char* sm_kernel_kind_name(int kind) {
+  static const char* names[SM_K_NUM_KINDS] = {
+      "ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe",
+      "sign_pack", "vote_update", "lion", "polar_update", "misc"};
+  if (kind < 0 || kind >= SM_K_NUM_KINDS) return "unknown";
+  return names[kind];
+}
+
+}  // extern "C"

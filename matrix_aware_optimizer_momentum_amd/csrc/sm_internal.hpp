@@ -1,0 +1,208 @@
+// Internal declarations shared by the HIP translation units of libsm.
+// Device helpers, the operand descriptors of the batched MFMA GEMM, and the
+// host-side launchers that the C ABI layer (sm_api.hip) drives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/sm.h"
+
+namespace sm {
+
+// ---------------------------------------------------------------- types
+
+typedef uint16_t bf16_t;  // bfloat16 storage (upper half of an IEEE float32)
+
+enum Dt : int { F32 = SM_F32, BF16 = SM_BF16 };
+
+__host__ __device__ inline size_t dt_size(int dt) { return dt == BF16 ? 2 : 4; }
+
+// bfloat16 -> float32 is exact: the 16 stored bits are the float's top half.
+__device__ __forceinline__ float bf2f(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+// Written out so that it does not depend on which conversion instruction
+// the compiler picks.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
+    return (bf16_t)((u >> 16) | 0x0040u);
+  uint32_t lsb = (u >> 16) & 1u;
+  return (bf16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf2f(*p); }
+  __device__ __forceinline__ static void store(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Eight consecutive elements of a 16-byte-aligned array, as float32.
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v);
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+  uint4 a = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------- pointer tables
+
+// Up to kTbl matrices per launch; problem b of a launch is worker (b % per)
+// of matrix (b / per), at byte offset (b % per) * worker_stride_bytes.
+constexpr int kTbl = 64;
+struct PtrTbl {
+  const char* p[kTbl];
+};
+
+__device__ __forceinline__ const char* tbl_addr(const PtrTbl& t, int b, int per,
+                                                int64_t worker_stride_bytes) {
+  return t.p[b / per] + (int64_t)(b % per) * worker_stride_bytes;
+}
+
+// ---------------------------------------------------------------- launch accounting
+
+// Brackets every launch with events while profiling is enabled.
+void prof_begin(int kind, double work, hipStream_t s);
+void prof_end(hipStream_t s);
+
+// Records a failed HIP call and maps it to SM_ERR_HIP.
+sm_status hip_fail(hipError_t e);
+sm_status check_launch();
+
+// ---------------------------------------------------------------- streaming kernels
+
+// Number of partial sums per problem used by every sum-of-squares producer.
+constexpr int kNormParts = 32;
+
+// Single EMA  M <- beta*M + (1-beta)*G  over `nprob` problems (= matrices x
+// workers) of `count` elements.  Writes M, the NS input copy x (contiguous
+// [nprob][count] in xdt, may be null) and the per-problem sum-of-squares
+// partials of the stored x values ([nprob][kNormParts]).
+sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
+                            int64_t count, int mdt, int gdt, float beta, void* x, int xdt,
+                            float* partials, hipStream_t s);
+
+// LionMuon fused kernel.  ghat = beta1*M + (1-beta1)*G, M <- beta2*M +
+// (1-beta2)*G.  If bits != null (Lion step) the signs of ghat (float32) are
+// packed to bits[nprob][words]; otherwise ghat is stored to x in xdt with
+// sum-of-squares partials (Muon step input).
+sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob, int64_t count,
+                      int mdt, int gdt, float beta1, float beta2, void* x, int xdt,
+                      float* partials, uint64_t* bits, int64_t words, hipStream_t s);
+
+// Sum-of-squares partials of nprob contiguous problems.
+sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* partials,
+                       hipStream_t s);
+
+// scale[b] = 1 / (sqrt(sum_i partials[b][i]) + eps)
+sm_status launch_scale_finalize(const float* partials, int nprob, float eps, float* scale,
+                                hipStream_t s);
+
+// Sign + 1-bit pack of nprob contiguous problems of `count` elements into
+// bits (problem b at bits + b*words).
+sm_status launch_sign_pack(const void* x, int dt, int nprob, int64_t count, uint64_t* bits,
+                           int64_t words, hipStream_t s);
+
+// Vote + update of `nmat` matrices; matrix j reads bits + j*mat_stride_words
+// (worker k at + k*words_stride) and updates w.p[j].
+sm_status launch_vote_update(const uint64_t* bits, int M, int64_t words_stride,
+                             int64_t mat_stride_words, int nmat, int64_t count, const PtrTbl& w,
+                             int wdt, float lr, int8_t* vote_out, hipStream_t s);
+
+// W <- rnd(fp32(W) - fp32(lr*D)) for nmat matrices, D contiguous [nmat][count].
+sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
+                              int wdt, float lr, hipStream_t s);
+
+// has_cache flags of nprob problems: hc[b] = cache_state(b)[0], where problem
+// b's {has_cache, a_t} pair is at tbl_addr(cs, b, per, 8).
+sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t* hc,
+                                  hipStream_t s);
+
+// CacheMuon accept/refresh decision per problem (see sm_gram_ns_cached):
+// err from the residual partials, flags[b] = 1 to refresh, outputs err /
+// refreshed / diag (each optional), and {1, t} written to cache_state on a
+// refresh.
+sm_status launch_cache_decide(const float* resid_partials, int parts, int nprob, int r,
+                              const int32_t* hc, const PtrTbl& cs, int per, int mode,
+                              float gamma, int64_t t, int32_t* flags, float* err,
+                              int32_t* refreshed, float* diag, int diag_stride, hipStream_t s);
+
+// ---------------------------------------------------------------- batched MFMA GEMM
+
+enum Layout : int {
+  KC = 0,  // operand row i, column k at base + i*ld + k (k contiguous)
+  RC = 1   // at base + k*ld + i (row index contiguous)
+};
+
+struct GemmOperand {
+  const void* p;
+  int64_t ld;      // elements
+  int64_t stride;  // elements between problems
+  int dt;          // F32 / BF16 in memory
+  int layout;      // KC / RC
+  int tbl;         // 1: problem b lives at tbl.p[b / tbl_per] + (b % tbl_per) * stride
+};
+
+// C[b] (M x N) = alpha_b * A[b] B[b] + beta_b * Cin[b] + diag * I
+//   A[b] is M x K, B[b] is K x N (B's KC layout stores B^T row-major).
+//   alpha_b = alpha * scale[b]^alpha_pow, beta_b = beta * scale[b]^beta_pow.
+// Cin has C's dtype.  Optional outputs: C (c_dt), C2 (float32) =
+// c2_diag*I + c2_scale*value,
+// resid partials ([batch][tiles]) = sum over the tile of (value - I)^2.
+// Problems with pred && pred[b*pred_stride] != pred_val are skipped.
+struct GemmArgs {
+  GemmOperand a, b;
+  const void* cin; int64_t ldcin, scin; int cin_tbl;
+  void* c; int64_t ldc, sc; int c_dt; int c_tbl;
+  float* c2; int64_t ldc2, sc2; int c2_tbl;
+  float* resid;
+  const float* scale;
+  const int32_t* pred; int pred_stride; int32_t pred_val;
+  int M, N, K, batch;
+  float alpha; int alpha_pow;
+  float beta; int beta_pow;
+  float diag;
+  float c2_diag, c2_scale;
+  // Optional per-matrix base pointers for operands / outputs flagged `tbl`
+  // (CacheMuon's per-matrix Q caches); tbl_per problems per entry.
+  PtrTbl tbl;
+  int tbl_per;
+};
+
+// Tiles per problem that the GEMM launch uses for (M, N) (resid partials).
+int gemm_tiles(int mfma_dt, int M, int N);
+
+// Launch with MFMA operand type mfma_dt (BF16 -> bf16 MFMA, F32 -> fp32 MFMA).
+sm_status launch_gemm(const GemmArgs& g, int mfma_dt, int kind, hipStream_t s);
+
+}  // namespace sm

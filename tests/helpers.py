@@ -1,0 +1,44 @@
+"""Comparison helpers shared by the GPU parity tests (no method arithmetic)."""
+import numpy as np
+import torch
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    """GPU tensor -> float32 numpy holding exactly the stored values."""
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def words_np(bits: torch.Tensor) -> np.ndarray:
+    return bits.detach().cpu().numpy().view(np.uint64)
+
+
+def storage_bits(x: np.ndarray, dt: str) -> np.ndarray:
+    """Bit patterns of float32 values that are exact in the storage type."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.int64)
+    return (u >> 16) if dt == "bf16" else u
+
+
+def ordered(bits: np.ndarray, nbits: int) -> np.ndarray:
+    """Map IEEE bit patterns to integers ordered like the values."""
+    sign = bits >> (nbits - 1)
+    mag = bits & ((1 << (nbits - 1)) - 1)
+    return np.where(sign == 1, -mag, mag)
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray, dt: str) -> np.ndarray:
+    nb = 16 if dt == "bf16" else 32
+    return np.abs(ordered(storage_bits(a, dt), nb) - ordered(storage_bits(b, dt), nb))
+
+
+def rel_fro(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def tdt(dt: str):
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def to_gpu(x: np.ndarray, dt: str, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device).to(tdt(dt))

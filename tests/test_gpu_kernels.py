@@ -1,0 +1,239 @@
+"""GPU parity of the C-ABI entry points against the CPU oracle, stage by stage.
+
+Each entry point gets seeded inputs, and the oracle recomputes the same stage
+from exactly the values the GPU was given.  Sign, pack, vote and update must
+match bit for bit; Newton-Schulz and Gram factors must be within the relative
+Frobenius tolerance of their operand type (float32 1e-4, bfloat16 2e-2).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sm_oracle as O
+from tests.helpers import rel_fro, to_gpu, to_np, words_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _special(rng, n):
+    x = rng.standard_normal(n).astype(np.float32)
+    specials = np.array([0.0, -0.0, np.nan, -np.nan, np.inf, -np.inf, 1e-45, -1e-45,
+                         -1e-40, 3e38, -3e38], dtype=np.float32)
+    if n >= 4 * len(specials):
+        pos = rng.choice(n, size=len(specials), replace=False)
+        x[pos] = specials
+    return x
+
+
+# ------------------------------------------------------------------ sign + pack
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 2047, 2048, 2049, 100003, (1 << 20) + 7])
+def test_sign_pack_bit_exact(gpu_lib, dt, n):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(1000 + n)
+    x = _special(rng, n)
+    xt = to_gpu(x, dt)
+    bits = sm.sign_pack(xt)
+    torch.cuda.synchronize()
+    want = O.sign_pack(to_np(xt))
+    np.testing.assert_array_equal(words_np(bits)[: want.size], want)
+
+
+# ------------------------------------------------------------------ vote + update
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 64])
+@pytest.mark.parametrize("count", [1, 64, 1000, 4097, 65539])
+def test_vote_update_bit_exact(gpu_lib, wdt, M, count):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(M * 100003 + count)
+    words = (count + 63) // 64
+    stride = words + 3                       # a padded worker stride
+    signs = [rng.standard_normal(count).astype(np.float32) for _ in range(M)]
+    if M >= 4:                               # force exact ties on some entries
+        k = min(count, 50)
+        for j in range(M // 2):
+            signs[j][:k] = -1.0
+        for j in range(M // 2, 2 * (M // 2)):
+            signs[j][:k] = 1.0
+    packed = np.zeros((M, stride), dtype=np.uint64)
+    for k in range(M):
+        packed[k, :words] = O.sign_pack(signs[k])
+        packed[k, words:] = np.uint64(0xDEADBEEFDEADBEEF)   # padding must be ignored
+    w0 = (0.02 * rng.standard_normal(count)).astype(np.float32)
+    wt = to_gpu(w0, wdt)
+    w_before = to_np(wt)
+    bits = torch.from_numpy(packed.view(np.int64)).cuda()
+    vote = torch.empty(count, dtype=torch.int8, device="cuda")
+    sm.vote_update(bits, wt, 1e-3, vote_out=vote)
+    torch.cuda.synchronize()
+    want_v = O.vote_from_bits([packed[k, :words] for k in range(M)], count)
+    np.testing.assert_array_equal(vote.cpu().numpy(), want_v)
+    want_w = O.update_vote(w_before, want_v, 1e-3, O.F32 if wdt == "f32" else O.BF16)
+    np.testing.assert_array_equal(to_np(wt).view(np.uint32),
+                                  want_w.astype(np.float32).view(np.uint32))
+
+
+# ------------------------------------------------------------------ direct NS
+
+NS_CASES = [
+    # dt, batch, m, n, iters, (a, b, c)
+    ("f32", 1, 256, 256, 5, (1.5, -0.5, 0.0)),
+    ("f32", 3, 64, 147, 1, (1.5, -0.5, 0.0)),
+    ("f32", 2, 147, 64, 5, (1.5, -0.5, 0.0)),
+    ("f32", 2, 200, 300, 5, (1.5, -0.5, 0.0)),
+    ("f32", 1, 129, 130, 3, (1.5, -0.5, 0.0)),
+    ("f32", 4, 8, 8, 5, (1.5, -0.5, 0.0)),
+    ("f32", 2, 96, 160, 4, (1.8, -0.6, 0.04)),
+    ("f32", 1, 1, 5, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 768, 2304, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 3072, 768, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 3, 64, 576, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 250, 130, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 128, 384, 4, (1.8, -0.6, 0.04)),
+]
+
+
+@pytest.mark.parametrize("case", NS_CASES, ids=lambda c: f"{c[0]}-b{c[1]}-{c[2]}x{c[3]}-K{c[4]}")
+def test_ns_polar_matches_oracle(gpu_lib, case):
+    import matrix_aware_optimizer_momentum_amd as sm
+    dt, batch, m, n, iters, (a, b, c) = case
+    rng = np.random.default_rng(batch * 7919 + m * 31 + n)
+    x = (0.01 * rng.standard_normal((batch, m, n))).astype(np.float32)
+    xt = to_gpu(x, dt)
+    p = sm.NSParams(iters=iters, a=a, b=b, c=c)
+    u = sm.ns_polar(xt, normalize=True, params=p)
+    torch.cuda.synchronize()
+    xin = to_np(xt)
+    got = to_np(u)
+    op = O.NSParams(iters=iters, a=a, b=b, c=c)
+    for k in range(batch):
+        want = O.ns_polar(xin[k], op, normalize=True)
+        err = rel_fro(got[k], want)
+        assert err <= TOL[dt], (k, err)
+
+
+def test_ns_polar_without_normalisation(gpu_lib):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 40, 90)).astype(np.float32)
+    x /= np.linalg.norm(x, axis=(1, 2), keepdims=True) * 1.3
+    xt = to_gpu(x, "f32")
+    u = sm.ns_polar(xt, normalize=False, params=sm.NSParams(iters=5))
+    torch.cuda.synchronize()
+    for k in range(2):
+        want = O.ns_polar(x[k].astype(np.float64), O.NSParams(iters=5), normalize=False)
+        assert rel_fro(to_np(u)[k], want) <= 1e-4
+
+
+def test_ns_polar_zero_input_gives_zero(gpu_lib):
+    import matrix_aware_optimizer_momentum_amd as sm
+    xt = torch.zeros(2, 64, 96, device="cuda", dtype=torch.bfloat16)
+    u = sm.ns_polar(xt)
+    bits = sm.sign_pack(u)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(u.float()).item() == 0
+    assert torch.count_nonzero(bits).item() == 0          # all signs +1
+
+
+# ------------------------------------------------------------------ Gram NS with cache
+
+GRAM_CASES = [
+    ("f32", 2, 96, 160, (1.5, -0.5, 0.0)),
+    ("f32", 2, 160, 96, (1.5, -0.5, 0.0)),
+    ("f32", 1, 130, 129, (1.8, -0.6, 0.04)),
+    ("bf16", 2, 256, 640, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 640, 256, (1.5, -0.5, 0.0)),
+    ("bf16", 1, 200, 333, (1.8, -0.6, 0.04)),
+]
+
+
+def _oriented(y):
+    return (y.T, True) if y.shape[0] > y.shape[1] else (y, False)
+
+
+@pytest.mark.parametrize("case", GRAM_CASES, ids=lambda c: f"{c[0]}-b{c[1]}-{c[2]}x{c[3]}")
+def test_gram_ns_cached_stages(gpu_lib, case):
+    import matrix_aware_optimizer_momentum_amd as sm
+    dt, batch, m, n, (a, b, c) = case
+    r = min(m, n)
+    tol = TOL[dt]
+    rng = np.random.default_rng(m * n + batch)
+    p = sm.NSParams(iters=5, a=a, b=b, c=c)
+    op = O.NSParams(iters=5, a=a, b=b, c=c)
+    q = torch.zeros(batch, r, r, dtype=torch.float32, device="cuda")
+    cs = torch.zeros(batch, 2, dtype=torch.int32, device="cuda")
+    x = 0.01 * rng.standard_normal((batch, m, n)).astype(np.float32)
+
+    def run(xnp, t, gamma, mode):
+        xt = to_gpu(xnp, dt)
+        d, err, refr = sm.gram_ns_cached(xt, q, cs, t, gamma, mode=mode, params=p)
+        torch.cuda.synchronize()
+        return to_np(xt), to_np(d), err.cpu().numpy(), refr.cpu().numpy()
+
+    # step 1: no cache -> fresh solve
+    xin, d, err, refr = run(x, 1, 2.0, 0)
+    assert list(refr) == [1] * batch and np.all(err == -1.0)
+    assert cs.cpu().numpy().tolist() == [[1, 1]] * batch
+    qg = q.cpu().numpy().astype(np.float64)
+    for k in range(batch):
+        xo, tr = _oriented(O.frobenius_normalize(xin[k], op.eps))
+        dw, qw = O.gram_ns_fresh_oriented(xo, op)
+        assert rel_fro(d[k], dw.T if tr else dw) <= tol
+        assert rel_fro(qg[k], qw) <= tol
+
+    # step 2: forced reuse of the cached Q on a drifted input
+    x2 = x + 0.002 * rng.standard_normal(x.shape).astype(np.float32)
+    xin2, d2, err2, refr2 = run(x2, 2, -1.0, 2)
+    assert list(refr2) == [0] * batch
+    assert cs.cpu().numpy().tolist() == [[1, 1]] * batch
+    for k in range(batch):
+        xo, tr = _oriented(O.frobenius_normalize(xin2[k], op.eps))
+        cand = O.cache_reuse_oriented(qg[k], xo)
+        assert rel_fro(d2[k], cand.T if tr else cand) <= tol
+        # residual of the GPU's own candidate, brute force in float64
+        got_cand, _ = _oriented(d2[k].astype(np.float64))
+        assert abs(err2[k] - O.orth_residual(got_cand)) <= 1e-3 * O.orth_residual(got_cand)
+
+    # step 3: trigger with gamma = 0 refreshes (err > 0)
+    x3 = x2 + 0.002 * rng.standard_normal(x.shape).astype(np.float32)
+    xin3, d3, err3, refr3 = run(x3, 3, 0.0, 0)
+    assert list(refr3) == [1] * batch and np.all(err3 > 0)
+    assert cs.cpu().numpy().tolist() == [[1, 3]] * batch
+    for k in range(batch):
+        xo, tr = _oriented(O.frobenius_normalize(xin3[k], op.eps))
+        cand_err = O.orth_residual(O.cache_reuse_oriented(qg[k], xo))
+        assert abs(err3[k] - cand_err) <= max(tol, 1e-3) * cand_err
+        dw, _ = O.gram_ns_fresh_oriented(xo, op)
+        assert rel_fro(d3[k], dw.T if tr else dw) <= tol
+
+    # step 4: huge gamma accepts; step 5: forced fresh
+    _, _, err4, refr4 = run(x3, 4, 1e9, 0)
+    assert list(refr4) == [0] * batch and np.all(err4 >= 0)
+    assert cs.cpu().numpy().tolist() == [[1, 3]] * batch
+    _, _, err5, refr5 = run(x3, 5, 1e9, 1)
+    assert list(refr5) == [1] * batch and np.all(err5 == -1.0)
+    assert cs.cpu().numpy().tolist() == [[1, 5]] * batch
+
+
+def test_gram_reuse_on_identical_input_is_stable(gpu_lib):
+    """A constant input: the reused candidate equals the fresh direction."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((2, 64, 200)).astype(np.float32)
+    xt = to_gpu(x, "f32")
+    q = torch.zeros(2, 64, 64, device="cuda")
+    cs = torch.zeros(2, 2, dtype=torch.int32, device="cuda")
+    d1, _, _ = sm.gram_ns_cached(xt, q, cs, 1, 10.0)
+    d1 = d1.clone()
+    d2, err, refr = sm.gram_ns_cached(xt, q, cs, 2, 10.0)
+    torch.cuda.synchronize()
+    assert refr.cpu().tolist() == [0, 0]
+    assert rel_fro(to_np(d2), to_np(d1)) <= 1e-5
+    for k in range(2):
+        assert abs(err.cpu().numpy()[k] - O.orth_residual(to_np(d1)[k].astype(np.float64))) < 1e-4

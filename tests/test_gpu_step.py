@@ -1,0 +1,303 @@
+"""GPU parity of whole optimizer steps (sm_step).
+
+* Single steps from seeded states (weights, momentum, gradients and, for
+  CacheMuon, a cached Q written by the oracle) against the oracle's step on
+  the same inputs.  Momentum must agree to one unit in the last place of its
+  storage type.  The vote must agree everywhere except where some worker's
+  oracle direction is within the Newton-Schulz tolerance of zero (there the
+  sign is decided by rounding and both answers are valid).
+* Composition: sm_step equals, bit for bit, the chain of the individual entry
+  points (sm_ns_polar / sm_gram_ns_cached -> sm_sign_pack -> sm_vote_update)
+  run on the step's own momentum.
+* Full size: one GPT-2-small step (12 layers, M = 5, bf16) in the launch
+  configuration the benchmark times, checked on sampled matrices.
+"""
+import numpy as np
+import pytest
+import torch
+
+import matrix_aware_optimizer_momentum_amd as sm
+from matrix_aware_optimizer_momentum_amd import workloads as W
+from oracle import sm_oracle as O
+from tests.helpers import rel_fro, to_gpu, to_np, ulp_distance, words_np
+
+pytestmark = pytest.mark.gpu
+
+BAND = {"f32": 1e-3, "bf16": 0.1}     # |d| / rms(d) below which a sign is rounding-decided
+MISMATCH_MAX = {"f32": 1e-3, "bf16": 0.02}
+
+
+def _tdt(dt):
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def _cfg(wl: W.Workload, **kw) -> sm.StepConfig:
+    d = dict(algo=wl.algo, update=wl.update, M=wl.M, wdt=_tdt(wl.wdt), mdt=_tdt(wl.mdt),
+             gdt=_tdt(wl.gdt), lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, period=wl.period,
+             ns=sm.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c, wl.ns_eps), gamma=wl.gamma,
+             cache_mode=wl.cache_mode)
+    d.update(kw)
+    return sm.StepConfig(**d)
+
+
+def _ocfg(wl: W.Workload, cfg: sm.StepConfig) -> O.StepConfig:
+    return O.StepConfig(algo=cfg.algo, update=cfg.update, workers=cfg.M, wdt=wl.wdt, mdt=wl.mdt,
+                        lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, period=cfg.period,
+                        ns=O.NSParams(cfg.ns.iters, cfg.ns.a, cfg.ns.b, cfg.ns.c, cfg.ns.eps),
+                        gamma=cfg.gamma, cache_mode=cfg.cache_mode)
+
+
+class Seeded:
+    """Seeded state of a workload subset: storage-exact numpy copies + GPU tensors."""
+
+    def __init__(self, wl: W.Workload, shapes, mom_scale=0.01, seed_shift=0):
+        rng = np.random.default_rng(wl.seed + 777 + seed_shift)
+        self.shapes = list(shapes)
+        self.w = [W.as_storage(x, wl.wdt) for x in W.init_weights(wl, shapes)]
+        self.mom = [W.as_storage(mom_scale * wl.grad_std *
+                                 rng.standard_normal((wl.M, m, n)).astype(np.float32), wl.mdt)
+                    for m, n in shapes]
+        g = next(W.grad_stream(wl, shapes))
+        self.grad = [W.as_storage(x, wl.gdt) for x in g]
+        self.mats = []
+        for j, (m, n) in enumerate(shapes):
+            self.mats.append(sm.MatrixBuffers(
+                w=to_gpu(self.w[j], wl.wdt), mom=to_gpu(self.mom[j], wl.mdt),
+                grad=to_gpu(self.grad[j], wl.gdt)))
+
+
+def _vote_from_w(w_before, w_after, lr, wdt):
+    """The vote each entry's update implies (or 9 where v = -1, 0, 1 coincide)."""
+    cands = [O.update_vote(w_before, np.full(w_before.shape, v, np.int8), lr, wdt)
+             for v in (-1, 0, 1)]
+    hits = [c.astype(np.float32).view(np.uint32) == w_after.astype(np.float32).view(np.uint32)
+            for c in cands]
+    v = np.full(w_before.shape, 9, np.int8)
+    unique = (hits[0].astype(int) + hits[1] + hits[2]) == 1
+    for val, h in zip((-1, 0, 1), hits):
+        v[h & unique] = val
+    assert np.all(hits[0] | hits[1] | hits[2]), "update is not W - lr*v for any vote"
+    return v
+
+
+def _check_vote(v_gpu, v_or, dirs, dt, what):
+    known = v_gpu != 9
+    mism = known & (v_gpu != v_or)
+    margin = np.min(np.stack([np.abs(d) / np.sqrt(np.mean(d * d) + 1e-300) for d in dirs]),
+                    axis=0)
+    bad = mism & (margin >= BAND[dt])
+    assert not np.any(bad), f"{what}: {int(bad.sum())} vote mismatches outside the band"
+    assert mism.mean() <= MISMATCH_MAX[dt], f"{what}: mismatch fraction {mism.mean():.4f}"
+
+
+def _oracle_step(wl, cfg, st: Seeded, j, t, cache=None):
+    ms = O.MatrixState(w=st.w[j].astype(np.float64),
+                       mom=[st.mom[j][k].astype(np.float64) for k in range(cfg.M)],
+                       cache=cache or [])
+    out = O.step_matrix(ms, [st.grad[j][k] for k in range(cfg.M)], _ocfg(wl, cfg), t)
+    return ms, out
+
+
+def _check_step(wl, cfg, st, t, dtm):
+    call = sm.StepCall(cfg, st.mats)
+    call(t)
+    torch.cuda.synchronize()
+    for j, (m, n) in enumerate(st.shapes):
+        ms, out = _oracle_step(wl, cfg, st, j, t)
+        mb = st.mats[j]
+        for k in range(cfg.M):
+            ud = ulp_distance(to_np(mb.mom)[k], ms.mom[k].astype(np.float32), wl.mdt)
+            assert ud.max() <= 1, (j, k, int(ud.max()))
+        v_gpu = _vote_from_w(st.w[j], to_np(mb.w), cfg.lr, wl.wdt)
+        _check_vote(v_gpu, out["vote"], out["d"], dtm, f"matrix {j} {m}x{n}")
+
+
+# ------------------------------------------------------------------ Sign-Muon
+
+SIGN_CASES = [
+    (1, [(256, 256)]),
+    (3, [(64, 147), (256, 64), (128, 1152), (512, 4608)]),
+    (2, W.gpt2_block_shapes(768, 1)),
+]
+
+
+@pytest.mark.parametrize("idx,shapes", SIGN_CASES, ids=["c1", "c3-subset", "c2-one-layer"])
+def test_sign_muon_step_matches_oracle(gpu_lib, idx, shapes):
+    wl = W.WORKLOADS[idx]
+    st = Seeded(wl, shapes)
+    _check_step(wl, _cfg(wl), st, 3, wl.mdt)
+
+
+def _composition_sign_muon(cfg, st, t):
+    before_w = [mb.w.clone() for mb in st.mats]
+    call = sm.StepCall(cfg, st.mats)
+    call(t)
+    for j, mb in enumerate(st.mats):
+        u = sm.ns_polar(mb.mom, params=cfg.ns)
+        count = mb.w.numel()
+        words = (count + 63) // 64
+        bits = torch.empty(cfg.M, words, dtype=torch.int64, device="cuda")
+        for k in range(cfg.M):
+            sm.sign_pack(u[k], bits=bits[k])
+        w2 = before_w[j]
+        sm.vote_update(bits, w2, cfg.lr)
+        torch.cuda.synchronize()
+        assert torch.equal(w2.view(torch.int16) if w2.dtype == torch.bfloat16 else w2.view(torch.int32),
+                           mb.w.view(torch.int16) if mb.w.dtype == torch.bfloat16 else mb.w.view(torch.int32)), j
+
+
+@pytest.mark.parametrize("idx,shapes", SIGN_CASES, ids=["c1", "c3-subset", "c2-one-layer"])
+def test_sign_muon_step_equals_entry_point_chain(gpu_lib, idx, shapes):
+    wl = W.WORKLOADS[idx]
+    _composition_sign_muon(_cfg(wl), Seeded(wl, shapes), 2)
+
+
+def test_sign_muon_quintic_and_even_workers(gpu_lib):
+    wl = W.WORKLOADS[1].scaled(M=4)
+    cfg = _cfg(wl, ns=sm.NSParams(iters=4, a=1.8, b=-0.6, c=0.04))
+    _check_step(wl, cfg, Seeded(wl, [(96, 200), (200, 96)]), 1, "f32")
+    _composition_sign_muon(cfg, Seeded(wl, [(96, 200), (200, 96)], seed_shift=1), 1)
+
+
+# ------------------------------------------------------------------ CacheMuon
+
+def _cache_bufs(st, M):
+    for mb, (m, n) in zip(st.mats, st.shapes):
+        r = min(m, n)
+        mb.q_cache = torch.zeros(M, r, r, dtype=torch.float32, device="cuda")
+        mb.cache_state = torch.zeros(M, 2, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_cache_muon_step_equals_entry_point_chain(gpu_lib, dt):
+    wl = W.WORKLOADS[4].scaled(wdt=dt, mdt=dt, gdt=dt)
+    shapes = [(128, 384), (128, 128), (128, 512), (512, 128)]
+    st = Seeded(wl, shapes)
+    _cache_bufs(st, 1)
+    cfg = _cfg(wl)
+    ref_q = [None] * len(shapes)
+    for t, (gamma, mode) in enumerate([(2.0, 0), (-1.0, 2), (0.0, 0), (1e9, 0), (1e9, 1)], 1):
+        cfg.gamma, cfg.cache_mode = gamma, mode
+        w_before = [to_np(mb.w) for mb in st.mats]
+        q_before = [mb.q_cache.clone() for mb in st.mats]
+        cs_before = [mb.cache_state.clone() for mb in st.mats]
+        diag = torch.full((len(shapes), 1, 2), 7.0, device="cuda")
+        sm.StepCall(cfg, st.mats, diag=diag)(t)
+        for j, mb in enumerate(st.mats):
+            d, err, refr = sm.gram_ns_cached(mb.mom, q_before[j], cs_before[j], t, gamma,
+                                             mode=mode, params=cfg.ns)
+            torch.cuda.synchronize()
+            assert torch.equal(q_before[j], mb.q_cache), (t, j)
+            assert torch.equal(cs_before[j], mb.cache_state), (t, j)
+            assert diag[j, 0, 0].item() == err.item() and diag[j, 0, 1].item() == refr.item()
+            want = O.update_polar(w_before[j], to_np(d)[0], cfg.lr, wl.wdt)
+            np.testing.assert_array_equal(to_np(mb.w).view(np.uint32),
+                                          want.astype(np.float32).view(np.uint32))
+        # fresh solve on the first step, forced reuse on the second
+        if t == 1:
+            assert all(mb.cache_state.cpu().tolist() == [[1, 1]] for mb in st.mats)
+        if t == 2:
+            assert all(mb.cache_state.cpu().tolist() == [[1, 1]] for mb in st.mats)
+
+
+def test_cache_muon_reuse_step_with_oracle_written_cache(gpu_lib):
+    """A reuse step whose cached Q comes from the oracle's own fresh solve."""
+    wl = W.WORKLOADS[4].scaled(wdt="f32", mdt="f32", gdt="f32")
+    shapes = [(96, 256), (256, 96)]
+    st = Seeded(wl, shapes)
+    cfg = _cfg(wl, gamma=float("inf"))
+    rng = np.random.default_rng(4242)
+    caches = []
+    for mb, (m, n) in zip(st.mats, shapes):
+        x_prev = rng.standard_normal((m, n))
+        cst = O.CacheState()
+        O.cache_muon_direction(x_prev, cst, 1, O.NSParams())
+        caches.append(cst)
+        mb.q_cache = torch.from_numpy(cst.q.astype(np.float32)[None]).cuda()
+        mb.cache_state = torch.tensor([[1, 1]], dtype=torch.int32, device="cuda")
+    w_before = [to_np(mb.w) for mb in st.mats]
+    sm.StepCall(cfg, st.mats)(2)
+    torch.cuda.synchronize()
+    for j, mb in enumerate(st.mats):
+        cst = O.CacheState(True, 1, caches[j].q.astype(np.float32).astype(np.float64))
+        ms, out = _oracle_step(wl, cfg, st, j, 2, cache=[cst])
+        assert out["refreshed"] == [False]
+        assert mb.cache_state.cpu().tolist() == [[1, 1]]
+        d_or = out["d"][0]
+        # the GPU's step: W_after = rnd(W - lr * D); compare the implied directions
+        delta_gpu = (w_before[j].astype(np.float64) - to_np(mb.w)) / cfg.lr
+        assert rel_fro(delta_gpu, d_or) <= 1e-3
+
+
+# ------------------------------------------------------------------ LionMuon
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_lion_muon_lion_step_bit_exact(gpu_lib, dt):
+    wl = W.WORKLOADS[5].scaled(wdt=dt, mdt=dt, gdt=dt, M=3, period=2)
+    shapes = [(64, 200), (300, 70)]
+    st = Seeded(wl, shapes, mom_scale=1.0)
+    cfg = _cfg(wl)
+    sm.StepCall(cfg, st.mats)(1)            # t = 1, P = 2: a Lion step
+    torch.cuda.synchronize()
+    for j in range(len(shapes)):
+        ms, out = _oracle_step(wl, cfg, st, j, 1)
+        mb = st.mats[j]
+        for k in range(cfg.M):
+            assert ulp_distance(to_np(mb.mom)[k], ms.mom[k].astype(np.float32), dt).max() <= 1
+        np.testing.assert_array_equal(to_np(mb.w).view(np.uint32),
+                                      ms.w.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_lion_muon_muon_step_matches_oracle(gpu_lib, dt):
+    wl = W.WORKLOADS[5].scaled(wdt=dt, mdt=dt, gdt=dt, M=3, period=2)
+    st = Seeded(wl, [(64, 200), (300, 70)], mom_scale=1.0)
+    _check_step(wl, _cfg(wl), st, 2, dt)    # t = 2, P = 2: a Muon step
+
+
+def test_lion_muon_polar_single_worker(gpu_lib):
+    """P5's own LionMuon (no vote): Muon steps apply W - lr * D."""
+    wl = W.WORKLOADS[5].scaled(wdt="f32", mdt="f32", gdt="f32", M=1, period=1)
+    st = Seeded(wl, [(80, 120)], mom_scale=1.0)
+    cfg = _cfg(wl, update=sm.UPDATE_POLAR)
+    w_before = to_np(st.mats[0].w)
+    sm.StepCall(cfg, st.mats)(1)
+    torch.cuda.synchronize()
+    ms, out = _oracle_step(wl, cfg, st, 0, 1)
+    delta_gpu = (w_before.astype(np.float64) - to_np(st.mats[0].w)) / cfg.lr
+    assert rel_fro(delta_gpu, out["d"][0]) <= 1e-3
+
+
+# ------------------------------------------------------------------ full size (benchmark launch)
+
+def test_full_size_gpt2_small_step_sampled(gpu_lib):
+    """One full config-2 step (85M parameters, M = 5, bf16) as the benchmark runs it."""
+    wl = W.WORKLOADS[2]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    mats = []
+    for (m, n) in wl.shapes:
+        w = (0.02 * torch.randn(m, n, generator=gen, device="cuda")).to(torch.bfloat16)
+        mom = (1e-4 * torch.randn(wl.M, m, n, generator=gen, device="cuda")).to(torch.bfloat16)
+        g = (wl.grad_std * torch.randn(wl.M, m, n, generator=gen, device="cuda")).to(torch.bfloat16)
+        mats.append(sm.MatrixBuffers(w=w, mom=mom, grad=g))
+    sample = [0, 2, 3, 46]                    # qkv, fc, fc_out (tall), a last-layer fc
+    before = {j: (to_np(mats[j].w), to_np(mats[j].mom), to_np(mats[j].grad)) for j in sample}
+    w_all_before = [mb.w.clone() for mb in mats]
+    cfg = _cfg(wl)
+    sm.StepCall(cfg, mats)(5)
+    torch.cuda.synchronize()
+    # any size: with odd M every entry moves by exactly one rounded lr step
+    for j, mb in enumerate(mats):
+        changed = (mb.w.view(torch.int16) != w_all_before[j].view(torch.int16)).float().mean()
+        assert changed.item() > 0.99, j
+    for j in sample:
+        w0, m0, g0 = before[j]
+        ms = O.MatrixState(w=w0.astype(np.float64), mom=[m0[k].astype(np.float64)
+                                                        for k in range(wl.M)])
+        out = O.step_matrix(ms, [g0[k] for k in range(wl.M)], _ocfg(wl, cfg), 5)
+        for k in range(wl.M):
+            assert ulp_distance(to_np(mats[j].mom)[k], ms.mom[k].astype(np.float32),
+                                "bf16").max() <= 1
+        v_gpu = _vote_from_w(w0, to_np(mats[j].w), cfg.lr, "bf16")
+        _check_vote(v_gpu, out["vote"], out["d"], "bf16", f"full-size matrix {j}")
