@@ -1,0 +1,252 @@
+"""Benchmark of the Muon-family optimizer step on one MI355X.
+
+Default workload: the GPT-2-small layer set (12 layers x {768x2304, 768x768,
+768x3072, 3072x768}, 84,934,656 parameters), Sign-Muon with M = 5 simulated
+workers, bf16 momentum / Newton-Schulz operands with float32 accumulation,
+5 cubic NS iterations, 1-bit packed majority vote.  A step is one sm_step
+call: momentum EMA + norm, NS, sign + pack, vote + update for all 48
+matrices.  Inputs are synthetic and resident in HBM before timing starts.
+
+Prints one JSON line: steps/s (value), the roofline of the dominant kernel
+measured with HIP events on the step's stream over the timed region, and the
+CPU oracle timed on a bounded sample on this host.
+
+  python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+METRIC = "optimizer steps/s per layer set; NS TFLOP/s (MFMA %); vote+update GB/s (HBM %)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--gamma", type=float, default=None, help="CacheMuon threshold override")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def _tdt(dt):
+    import torch
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def build_state(wl, device="cuda"):
+    """Weights, momentum, gradients (and CacheMuon caches) generated on the GPU."""
+    import torch
+    import matrix_aware_optimizer_momentum_amd as sm
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.seed)
+    mats = []
+    for (m, n) in wl.shapes:
+        w = (0.02 * torch.randn(m, n, generator=gen, device=device)).to(_tdt(wl.wdt))
+        mom = torch.zeros(wl.M, m, n, device=device, dtype=_tdt(wl.mdt))
+        if wl.grad_kind == "student_t":
+            z = torch.randn(wl.M, m, n, generator=gen, device=device)
+            chi = torch.zeros_like(z)
+            for _ in range(3):
+                chi += torch.randn(wl.M, m, n, generator=gen, device=device) ** 2
+            g = wl.grad_std * z / torch.sqrt(chi / 3.0)
+            del z, chi
+        else:
+            g = wl.grad_std * torch.randn(wl.M, m, n, generator=gen, device=device)
+        mb = sm.MatrixBuffers(w=w, mom=mom, grad=g.to(_tdt(wl.gdt)))
+        del g
+        if wl.algo == sm.CACHE_MUON:
+            r = min(m, n)
+            mb.q_cache = torch.zeros(wl.M, r, r, device=device)
+            mb.cache_state = torch.zeros(wl.M, 2, dtype=torch.int32, device=device)
+        mats.append(mb)
+    return mats
+
+
+def step_config(wl, gamma=None):
+    import matrix_aware_optimizer_momentum_amd as sm
+    return sm.StepConfig(algo=wl.algo, update=wl.update, M=wl.M, wdt=_tdt(wl.wdt),
+                         mdt=_tdt(wl.mdt), gdt=_tdt(wl.gdt), lr=wl.lr, beta1=wl.beta1,
+                         beta2=wl.beta2, period=wl.period,
+                         ns=sm.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c, wl.ns_eps),
+                         gamma=wl.gamma if gamma is None else gamma, cache_mode=wl.cache_mode)
+
+
+def stream_bytes(wl, kind):
+    """Algorithmic bytes per step of one streaming kernel kind (whole layer set)."""
+    es = {"bf16": 2, "f32": 4}
+    n = wl.params
+    if kind == "ema":        # read G and M, write M and the NS input copy
+        return n * wl.M * (es[wl.gdt] + 2 * es[wl.mdt] + es[wl.mdt])
+    if kind == "sign_pack":  # read D, write 1 bit
+        return n * wl.M * (es[wl.mdt] + 1 / 8)
+    if kind == "vote_update":
+        return n * (wl.M / 8 + 2 * es[wl.wdt])
+    return 0.0
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle's step on a bounded sample of the layer set, on this host's cores."""
+    import numpy as np
+    from matrix_aware_optimizer_momentum_amd import workloads as W
+    from oracle import sm_oracle as O
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
+                      default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    ocfg = O.StepConfig(algo=wl.algo, update=wl.update, workers=wl.M, wdtype=wl.wdt,
+                        mdtype=wl.mdt, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
+                        period=wl.period, ns=O.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c,
+                                                        wl.ns_eps),
+                        gamma=wl.gamma, cache_mode=wl.cache_mode)
+    done_params = 0
+    elapsed = 0.0
+    nmat = 0
+    rng = np.random.default_rng(wl.seed)
+    for (m, n) in wl.shapes:
+        w = W.as_storage((0.02 * rng.standard_normal((m, n))).astype(np.float32), wl.wdt)
+        g = [W.as_storage((wl.grad_std * rng.standard_normal((m, n))).astype(np.float32), wl.gdt)
+             for _ in range(wl.M)]
+        st = O.MatrixState(w=w.astype(np.float64), mom=[np.zeros((m, n)) for _ in range(wl.M)])
+        t0 = time.perf_counter()
+        O.step_matrix(st, g, ocfg, 1)
+        elapsed += time.perf_counter() - t0
+        done_params += m * n
+        nmat += 1
+        if elapsed >= seconds:
+            break
+    scale = wl.params / done_params
+    sec_per_step = elapsed * scale
+    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{nmat} of {len(wl.shapes)} matrices ({done_params} of {wl.params} "
+                       f"parameters) x {wl.M} workers, one step, {elapsed:.1f} s; "
+                       f"{'extrapolated x%.2f to the whole layer set' % scale if scale > 1 else 'whole layer set'}"),
+            "seconds_per_step": sec_per_step}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "path is not part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import matrix_aware_optimizer_momentum_amd as sm
+    from matrix_aware_optimizer_momentum_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = W.WORKLOADS[args.config]
+    mats = build_state(wl)
+    cfg = step_config(wl, args.gamma)
+    call = sm.StepCall(cfg, mats)
+    torch.cuda.synchronize()
+
+    t = 1
+    for _ in range(args.warmup):
+        call(t)
+        t += 1
+    torch.cuda.synchronize()
+
+    sm.profile_enable(True)
+    sm.profile_reset()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call(t)
+        t += 1
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sm.profile_enable(False)
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1000.0 * wall / args.steps
+    value = args.steps / wall
+
+    kinds = {}
+    for kind in ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pack",
+                 "vote_update", "lion", "polar_update", "misc"]:
+        ms, n, work = sm.profile_read(kind)
+        if n:
+            kinds[kind] = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+                           "avg_launch_ms": ms / n, "work_per_launch": work / n,
+                           "flops" if kind.startswith(("gemm", "probe")) else "bytes": work / args.steps}
+    dom = max(kinds, key=lambda k: kinds[k]["ms_per_step"])
+    is_mfma = dom.startswith(("gemm", "probe"))
+    dk = kinds[dom]
+    if is_mfma:
+        achieved = dk["work_per_launch"] / (dk["avg_launch_ms"] * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[wl.mdt]
+        unit = "TFLOP/s"
+    else:
+        achieved = dk["work_per_launch"] / (dk["avg_launch_ms"] * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+        unit = "GB/s"
+    roofline = {"bound": "mfma" if is_mfma else "hbm", "kernel": dom, "achieved": achieved,
+                "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": None,
+                "avg_launch_ms": dk["avg_launch_ms"], "work_per_launch": dk["work_per_launch"]}
+
+    ns_ms = sum(kinds.get(k, {}).get("ms_per_step", 0.0) for k in ("gemm_gram", "gemm_apply",
+                                                                   "gemm_rr"))
+    ns_flops = sum(kinds.get(k, {}).get("flops", 0.0) for k in ("gemm_gram", "gemm_apply",
+                                                               "gemm_rr"))
+    extra = {}
+    if ns_ms > 0:
+        extra["ns_tflops"] = ns_flops / (ns_ms * 1e-3) / 1e12
+        extra["ns_mfma_frac"] = extra["ns_tflops"] / PEAK_TFLOPS[wl.mdt]
+        extra["ns_tflops_step"] = wl.ns_flops_per_step() / (ms_per_step * 1e-3) / 1e12
+    if "vote_update" in kinds:
+        vu = kinds["vote_update"]
+        extra["vote_update_gbs"] = vu["bytes"] / (vu["ms_per_step"] * 1e-3) / 1e9
+        extra["vote_update_hbm_frac"] = extra["vote_update_gbs"] / PEAK_HBM_GBS
+    if wl.algo == sm.CACHE_MUON:
+        refreshed = sum(int(mb.cache_state[:, 1].eq(t - 1).sum().item()) for mb in mats)
+        extra["last_step_refreshed_matrices"] = refreshed
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": gpu_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.mdt,
+        "data": "synthetic (seeded on-GPU Gaussian / AR(1) / Student-t gradients; no dataset)",
+        "config": {"workload": wl.name, "matrices": len(wl.shapes), "params": wl.params,
+                   "workers": wl.M, "ns_iters": wl.ns_iters, "algo": ["sign_muon", "cache_muon",
+                                                                       "lion_muon"][wl.algo],
+                   "weights": wl.wdt, "momentum": wl.mdt, "grads": wl.gdt},
+        "roofline": roofline,
+        **extra,
+        "kernels": kinds,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

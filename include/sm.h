@@ -17,7 +17,7 @@
  *
  * Conventions shared by every call
  *   - Every tensor pointer is DEVICE memory, row-major, contiguous, owned by
- *     the caller, and 16-byte aligned.  The library never allocates device
+ *     the caller, and 16-byte aligned unless a call states otherwise.  The library never allocates device
  *     memory, never frees, and keeps no pointer after a call returns.
  *     Scratch memory is passed in as `ws` (sized by the matching *_ws query).
  *   - All GPU work is enqueued on the stream `s` (0 = null stream) and is
@@ -132,7 +132,8 @@ sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_sta
  * workers keep only the entrywise sign of their direction, packed one bit
  * per entry (32x fewer bytes than float32, [SignMuon-ja] communication
  * efficiency).
- * x    : [count] in dt.   bits : [ceil(count/64)] uint64 out.
+ * x    : [count] in dt (element-aligned; 16-byte alignment takes the
+ *        vector path).   bits : [ceil(count/64)] uint64 out, 8-byte aligned.
  * Errors: SM_ERR_ARG (null/misaligned), SM_ERR_SHAPE (count < 0),
  *         SM_ERR_DTYPE.  count == 0 is a no-op.
  * ---------------------------------------------------------------------- */
@@ -143,13 +144,13 @@ sm_status sm_sign_pack(const void* x, int dt, int64_t count, uint64_t* bits, hip
  * [SignMuon-ja] section 2, core mechanism 3 and algorithm flow step 4: the
  * workers' signs are summed as integers and thresholded by sign(); every
  * worker then applies W <- W - eta * vote.
- * bits : [M][words_stride] uint64, worker-major packed signs (what an
- *        all-gather of the workers' 1-bit buffers delivers);
+ * bits : [M][words_stride] uint64 (8-byte aligned), worker-major packed
+ *        signs (what an all-gather of the workers' 1-bit buffers delivers);
  *        words_stride >= ceil(count/64).
  * V_i  = sign(M - 2 * n_neg_i) in {-1, 0, +1} (0 only on ties, even M).
  * w    : [count] in wdt, updated in place: W <- rnd_W(fp32(W) - fp32(lr)*V),
  *        one float32 rounding, then RNE to bf16 for bf16 weights.
- * vote_out : optional [count] int8 out (NULL to skip).
+ * vote_out : optional [count] int8 out (NULL to skip; any alignment).
  * Errors: SM_ERR_ARG (null/misaligned, words_stride too small, lr not
  *         finite), SM_ERR_SHAPE (count < 0), SM_ERR_UNSUPPORTED (M < 1 or
  *         M > 64), SM_ERR_DTYPE.

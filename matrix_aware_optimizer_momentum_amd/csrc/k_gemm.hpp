@@ -233,7 +233,9 @@ struct KArgs {
   int tiles_n, tiles;
 };
 
-template <typename TA, typename TB, typename TM, int LA, int LB>
+// ROLE (the SM_K_GEMM_* / SM_K_PROBE kind) changes no code; it gives each
+// role its own kernel symbol so per-kernel profiles attribute time by role.
+template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE>
 __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
   __shared__ __attribute__((aligned(16))) TM As[BM * LDK];
@@ -361,7 +363,20 @@ sm_status launch_t(const GemmArgs& g, int kind, hipStream_t s) {
   ka.tiles = tiles_m * ka.tiles_n;
   dim3 grid(ka.tiles, g.batch);
   prof_begin(kind, 2.0 * g.M * (double)g.N * g.K * g.batch, s);
-  hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB>), grid, dim3(NT), 0, s, ka);
+  switch (kind) {
+    case SM_K_GEMM_GRAM:
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_GRAM>), grid, dim3(NT), 0, s, ka);
+      break;
+    case SM_K_GEMM_APPLY:
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_APPLY>), grid, dim3(NT), 0, s, ka);
+      break;
+    case SM_K_PROBE:
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_PROBE>), grid, dim3(NT), 0, s, ka);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_RR>), grid, dim3(NT), 0, s, ka);
+      break;
+  }
   prof_end(s);
   return check_launch();
 }

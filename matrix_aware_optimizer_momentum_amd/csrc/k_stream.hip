@@ -50,6 +50,22 @@ __device__ __forceinline__ void store8_tail(T* p, int64_t e0, int64_t count, boo
   }
 }
 
+// beta*m + (1-beta)*g as one fixed float32 sequence: the product (1-beta)*g
+// is rounded, then fused with beta*m (one more rounding).  Fixing the order
+// keeps sign decisions on the result reproducible off the GPU.
+__device__ __forceinline__ float ema32(float beta, float m, float omb, float g) {
+  return __fmaf_rn(beta, m, __fmul_rn(omb, g));
+}
+
+// Sum-of-squares accumulation shared by every producer of norm partials, so
+// that the EMA kernel and the standalone reduction give identical bits:
+// entries beyond the problem are loaded as 0 and add exactly nothing.
+__device__ __forceinline__ float sumsq8(float acc, const float* v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __fmaf_rn(v[e], v[e], acc);
+  return acc;
+}
+
 // Fixed-order block sum: wave butterfly, then wave 0 adds the 4 wave sums.
 __device__ float block_sum(float v, float* red) {
 #pragma unroll
@@ -106,12 +122,11 @@ __global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad
     load8_tail<TG>(g, e0, count, vec, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = round_to<TM>(beta * mv[e] + omb * gv[e]);
+      float v = round_to<TM>(ema32(beta, mv[e], omb, gv[e]));
       mv[e] = v;
-      float xv = round_to<TX>(v);
-      gv[e] = xv;
-      if (e0 + e < count) acc += xv * xv;
+      gv[e] = round_to<TX>(v);  // 0 beyond the end: both inputs load as 0
     }
+    acc = sumsq8(acc, gv);
     store8_tail<TM>(m, e0, count, vec, mv);
     if (xo) store8_tail<TX>(xo, e0, count, vec, gv);
   }
@@ -144,18 +159,16 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
       load8_tail<TG>(g, e0, count, vec, gv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        dv[e] = b1 * mv[e] + omb1 * gv[e];
-        mv[e] = round_to<TM>(b2 * mv[e] + omb2 * gv[e]);
+        dv[e] = ema32(b1, mv[e], omb1, gv[e]);
+        mv[e] = round_to<TM>(ema32(b2, mv[e], omb2, gv[e]));
       }
       store8_tail<TM>(m, e0, count, vec, mv);
       if (bo) {
         byte = neg_byte(dv, e0, count);
       } else if (xo) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dv[e] = round_to<TX>(dv[e]);
-          if (e0 + e < count) acc += dv[e] * dv[e];
-        }
+        for (int e = 0; e < 8; ++e) dv[e] = round_to<TX>(dv[e]);
+        acc = sumsq8(acc, dv);
         store8_tail<TX>(xo, e0, count, vec, dv);
       }
     }
@@ -183,8 +196,7 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(const T* x, int64_t count, f
     if (e0 >= count) continue;
     float v[8];
     load8_tail<T>(xp, e0, count, vec, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += v[e] * v[e];
+    acc = sumsq8(acc, v);
   }
   float s = block_sum(acc, red);
   if (threadIdx.x == 0) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
@@ -400,7 +412,7 @@ sm_status launch_scale_finalize(const float* partials, int nprob, float eps, flo
 sm_status launch_sign_pack(const void* x, int dt, int nprob, int64_t count, uint64_t* bits,
                            int64_t words, hipStream_t s) {
   if (nprob <= 0 || count <= 0) return SM_OK;
-  const bool vec = (count % 8) == 0;
+  const bool vec = (count % 8) == 0 && (reinterpret_cast<uintptr_t>(x) % 16) == 0;
   dim3 grid(stream_blocks(count, nprob), nprob);
   prof_begin(SM_K_SIGN_PACK, (double)nprob * ((double)count * dt_size(dt) + words * 8.0), s);
   SM_DISPATCH_DT(dt, T,

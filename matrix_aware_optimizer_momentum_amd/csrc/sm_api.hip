@@ -598,7 +598,9 @@ sm_status sm_sign_pack(const void* x, int dt, int64_t count, uint64_t* bits, hip
   if (!valid_dt(dt)) return SM_ERR_DTYPE;
   if (count < 0) return SM_ERR_SHAPE;
   if (count == 0) return SM_OK;
-  if (!x || !bits || !al16(x) || !al16(bits)) return SM_ERR_ARG;
+  if (!x || !bits) return SM_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) % dt_size(dt)) || (reinterpret_cast<uintptr_t>(bits) & 7u))
+    return SM_ERR_ARG;
   return launch_sign_pack(x, dt, 1, count, bits, (count + 63) / 64, s);
 }
 
@@ -608,8 +610,7 @@ sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int6
   if (count < 0) return SM_ERR_SHAPE;
   if (M < 1 || M > 64) return SM_ERR_UNSUPPORTED;
   if (count == 0) return SM_OK;
-  if (!bits || !w || !al16(bits) || !al16(w)) return SM_ERR_ARG;
-  if (vote_out && !al16(vote_out)) return SM_ERR_ARG;
+  if (!bits || !w || !al16(w) || (reinterpret_cast<uintptr_t>(bits) & 7u)) return SM_ERR_ARG;
   if (words_stride < (count + 63) / 64 || !finite(lr)) return SM_ERR_ARG;
   const PtrTbl wt = tbl_one(w);
   return launch_vote_update(bits, M, words_stride, 0, 1, count, wt, wdt, lr, vote_out, s);

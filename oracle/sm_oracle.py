@@ -128,6 +128,23 @@ def lion_momentum(m_prev, g, beta2: float) -> np.ndarray:
     return beta2 * np.asarray(m_prev, np.float64) + (1.0 - beta2) * np.asarray(g, np.float64)
 
 
+def lion_sign_negative(m_prev, g, beta1: float) -> np.ndarray:
+    """Sign decision of the Lion direction, taken in float32 as the kernel takes it.
+
+    The sign is an integer decided by floating point, so it is decided in the
+    kernel's precision: with b = fp32(beta1) and c = fp32(1 - b), the kernel
+    evaluates b*m + rnd32(c*g) with one final rounding, whose sign is the
+    sign of the exact value computed here (b*m is exact in float64).  Entries
+    that are exactly 0 count as +1.
+    """
+    b = np.float32(beta1)
+    c = np.float32(np.float32(1.0) - b)
+    m32 = np.asarray(m_prev, dtype=np.float64).astype(np.float32)
+    g32 = np.asarray(g, dtype=np.float64).astype(np.float32)
+    cg = (c * g32).astype(np.float32).astype(np.float64)
+    return (np.float64(b) * m32.astype(np.float64) + cg) < 0
+
+
 # --------------------------------------------------------------------------
 # a2: Frobenius normalisation
 # --------------------------------------------------------------------------
@@ -471,13 +488,13 @@ def step_matrix(st: MatrixState, grads: Sequence[np.ndarray], cfg: StepConfig, t
     for k in range(mw):
         g = np.asarray(grads[k], np.float64)
         if cfg.algo == LION_MUON:
-            y = lion_interp(st.mom[k], g, cfg.beta1)
+            m_prev = st.mom[k]
+            y = lion_interp(m_prev, g, cfg.beta1)
             st.mom[k] = round_storage(lion_momentum(st.mom[k], g, cfg.beta2), cfg.mdtype)
             if not muon_step:
                 # Lion step: sign of the interpolation, decided in float32.
-                y32 = y.astype(np.float32)
-                out["d"][k] = y32.astype(np.float64)
-                out["bits"][k] = sign_pack(y32)
+                out["d"][k] = y
+                out["bits"][k] = pack_bits(lion_sign_negative(m_prev, g, cfg.beta1).reshape(-1))
                 continue
             y = round_storage(y, cfg.mdtype)
         else:

@@ -42,3 +42,33 @@ def tdt(dt: str):
 
 def to_gpu(x: np.ndarray, dt: str, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device).to(tdt(dt))
+
+
+def storage_ulp(x: np.ndarray, dt: str) -> np.ndarray:
+    """Spacing of the storage type at |x| (bf16: 8 significant bits)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    if dt == "f32":
+        return np.spacing(a.astype(np.float32)).astype(np.float64)
+    _, e = np.frexp(np.maximum(a, 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
+
+
+def assert_ema_close(gpu, want, m_prev, g, beta, dt, what=""):
+    """|gpu - want| <= 1 storage ulp + float32 rounding of the two EMA terms.
+
+    The kernel evaluates beta*m + (1-beta)*g in float32 and stores it in dt;
+    when the terms cancel, the float32 error is relative to the terms, not
+    to the (small) result.
+    """
+    gpu = np.asarray(gpu, np.float64)
+    want = np.asarray(want, np.float64)
+    terms = np.abs(beta * np.asarray(m_prev, np.float64)) + \
+        np.abs((1 - beta) * np.asarray(g, np.float64))
+    tol = storage_ulp(want, dt) + 2.0 ** -22 * terms
+    bad = np.abs(gpu - want) > tol
+    assert not np.any(bad), f"{what}: {int(bad.sum())} momentum entries off by more than the bound"
+
+
+def f32(v: float) -> float:
+    """A hyper-parameter as the float32 the C ABI receives."""
+    return float(np.float32(v))

@@ -128,9 +128,13 @@ def test_host_validation_rejects_before_any_gpu_call():
     assert lib.sm_vote_update(None, 0, 1, 64, None, B.F32, 1e-3, None, None) == 5
     assert lib.sm_vote_update(None, 65, 1, 64, None, B.F32, 1e-3, None, None) == 5
     assert lib.sm_vote_update(None, 3, 1, 64, None, 5, 1e-3, None, None) == 3
-    # misaligned pointer (never dereferenced: rejected on the host)
+    # misaligned pointers (never dereferenced: rejected on the host)
     assert lib.sm_sign_pack(ctypes.c_void_p(0x1001), B.F32, 10, ctypes.c_void_p(0x2000),
                             None) == 1
+    assert lib.sm_sign_pack(ctypes.c_void_p(0x1000), B.F32, 10, ctypes.c_void_p(0x2004),
+                            None) == 1
+    assert lib.sm_vote_update(ctypes.c_void_p(0x1000), 3, 1, 64, ctypes.c_void_p(0x2008),
+                              B.F32, 1e-3, None, None) == 1
     # words_stride too small for the count
     assert lib.sm_vote_update(ctypes.c_void_p(0x1000), 3, 1, 65, ctypes.c_void_p(0x2000),
                               B.F32, 1e-3, None, None) == 1

@@ -19,7 +19,7 @@ import torch
 import matrix_aware_optimizer_momentum_amd as sm
 from matrix_aware_optimizer_momentum_amd import workloads as W
 from oracle import sm_oracle as O
-from tests.helpers import rel_fro, to_gpu, to_np, ulp_distance, words_np
+from tests.helpers import assert_ema_close, f32, rel_fro, to_gpu, to_np, words_np
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,19 @@ def _cfg(wl: W.Workload, **kw) -> sm.StepConfig:
 
 
 def _ocfg(wl: W.Workload, cfg: sm.StepConfig) -> O.StepConfig:
-    return O.StepConfig(algo=cfg.algo, update=cfg.update, workers=cfg.M, wdt=wl.wdt, mdt=wl.mdt,
-                        lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, period=cfg.period,
-                        ns=O.NSParams(cfg.ns.iters, cfg.ns.a, cfg.ns.b, cfg.ns.c, cfg.ns.eps),
-                        gamma=cfg.gamma, cache_mode=cfg.cache_mode)
+    """The oracle's configuration, with every scalar as the float32 the ABI receives."""
+    return O.StepConfig(algo=cfg.algo, update=cfg.update, workers=cfg.M, wdtype=wl.wdt,
+                        mdtype=wl.mdt, lr=f32(cfg.lr), beta1=f32(cfg.beta1),
+                        beta2=f32(cfg.beta2), period=cfg.period,
+                        ns=O.NSParams(cfg.ns.iters, f32(cfg.ns.a), f32(cfg.ns.b), f32(cfg.ns.c),
+                                      f32(cfg.ns.eps)),
+                        gamma=f32(cfg.gamma), cache_mode=cfg.cache_mode)
+
+
+def _check_mom(wl, cfg, gpu_mom, ms, m_prev, g, what):
+    beta = f32(cfg.beta2 if cfg.algo == sm.LION_MUON else cfg.beta1)
+    for k in range(cfg.M):
+        assert_ema_close(gpu_mom[k], ms.mom[k], m_prev[k], g[k], beta, wl.mdt, f"{what} worker {k}")
 
 
 class Seeded:
@@ -105,9 +114,7 @@ def _check_step(wl, cfg, st, t, dtm):
     for j, (m, n) in enumerate(st.shapes):
         ms, out = _oracle_step(wl, cfg, st, j, t)
         mb = st.mats[j]
-        for k in range(cfg.M):
-            ud = ulp_distance(to_np(mb.mom)[k], ms.mom[k].astype(np.float32), wl.mdt)
-            assert ud.max() <= 1, (j, k, int(ud.max()))
+        _check_mom(wl, cfg, to_np(mb.mom), ms, st.mom[j], st.grad[j], f"matrix {j}")
         v_gpu = _vote_from_w(st.w[j], to_np(mb.w), cfg.lr, wl.wdt)
         _check_vote(v_gpu, out["vote"], out["d"], dtm, f"matrix {j} {m}x{n}")
 
@@ -211,7 +218,7 @@ def test_cache_muon_reuse_step_with_oracle_written_cache(gpu_lib):
     for mb, (m, n) in zip(st.mats, shapes):
         x_prev = rng.standard_normal((m, n))
         cst = O.CacheState()
-        O.cache_muon_direction(x_prev, cst, 1, O.NSParams())
+        O.cache_muon_direction(x_prev, cst, 1, O.NSParams(), gamma=1.0)
         caches.append(cst)
         mb.q_cache = torch.from_numpy(cst.q.astype(np.float32)[None]).cuda()
         mb.cache_state = torch.tensor([[1, 1]], dtype=torch.int32, device="cuda")
@@ -242,8 +249,7 @@ def test_lion_muon_lion_step_bit_exact(gpu_lib, dt):
     for j in range(len(shapes)):
         ms, out = _oracle_step(wl, cfg, st, j, 1)
         mb = st.mats[j]
-        for k in range(cfg.M):
-            assert ulp_distance(to_np(mb.mom)[k], ms.mom[k].astype(np.float32), dt).max() <= 1
+        _check_mom(wl, cfg, to_np(mb.mom), ms, st.mom[j], st.grad[j], f"matrix {j}")
         np.testing.assert_array_equal(to_np(mb.w).view(np.uint32),
                                       ms.w.astype(np.float32).view(np.uint32))
 
@@ -296,8 +302,6 @@ def test_full_size_gpt2_small_step_sampled(gpu_lib):
         ms = O.MatrixState(w=w0.astype(np.float64), mom=[m0[k].astype(np.float64)
                                                         for k in range(wl.M)])
         out = O.step_matrix(ms, [g0[k] for k in range(wl.M)], _ocfg(wl, cfg), 5)
-        for k in range(wl.M):
-            assert ulp_distance(to_np(mats[j].mom)[k], ms.mom[k].astype(np.float32),
-                                "bf16").max() <= 1
+        _check_mom(wl, cfg, to_np(mats[j].mom), ms, m0, g0, f"full-size matrix {j}")
         v_gpu = _vote_from_w(w0, to_np(mats[j].w), cfg.lr, "bf16")
         _check_vote(v_gpu, out["vote"], out["d"], "bf16", f"full-size matrix {j}")

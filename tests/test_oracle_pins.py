@@ -495,3 +495,41 @@ def test_cache_muon_trajectory_polar_mode():
         refreshed += out["refreshed"]
     assert refreshed == [True] + [False] * 5
     assert st.cache[0].a_t == 1
+
+
+# ---------------------------------------------------------------- Lion sign decision
+
+def test_lion_sign_decision_in_float32():
+    rng = np.random.default_rng(22)
+    m = rng.standard_normal(20000)
+    g = rng.standard_normal(20000)
+    b = float(np.float32(0.9))
+    exact = b * m.astype(np.float32).astype(np.float64) + \
+        (1 - b) * g.astype(np.float32).astype(np.float64)
+    clear = np.abs(exact) > 1e-5
+    got = O.lion_sign_negative(m, g, 0.9)
+    np.testing.assert_array_equal(got[clear], exact[clear] < 0)
+    # exact cancellation g = -9 m: with fp32(0.9) = 0.89999998 and
+    # fp32(1 - 0.89999998) = 0.10000002 the float32 value is
+    # 0.89999998 - rnd32(0.90000021) = -2.4e-7 < 0, while beta = 0.9 exactly
+    # would give 0 (sign +1).
+    assert O.lion_sign_negative(np.array([1.0]), np.array([-9.0]), 0.9)[0]
+    assert not O.lion_sign_negative(np.array([-1.0]), np.array([9.0]), 0.9)[0]
+    # beta = 0.5 is exact in float32: m = 1, g = -1 cancels to +0 -> +1
+    assert not O.lion_sign_negative(np.array([1.0]), np.array([-1.0]), 0.5)[0]
+
+
+def test_update_polar_matches_torch_float32_and_bf16():
+    rng = np.random.default_rng(23)
+    n = 5000
+    w32 = (0.02 * rng.standard_normal(n)).astype(np.float32)
+    d32 = (0.05 * rng.standard_normal(n)).astype(np.float32)
+    lr = 1e-3
+    tl = torch.tensor(lr, dtype=torch.float32)
+    want32 = (torch.from_numpy(w32) - tl * torch.from_numpy(d32)).numpy()
+    got32 = O.update_polar(w32, d32, lr, O.F32).astype(np.float32)
+    np.testing.assert_array_equal(got32.view(np.uint32), want32.view(np.uint32))
+    wbf = torch.from_numpy(w32).to(torch.bfloat16).to(torch.float32)
+    want_b = (wbf - tl * torch.from_numpy(d32)).to(torch.bfloat16).view(torch.int16).numpy()
+    got_b = O.update_polar(wbf.numpy(), d32, lr, O.BF16).astype(np.float32)
+    np.testing.assert_array_equal(O.bf16_bits_from_f32(got_b), want_b.view(np.uint16))
