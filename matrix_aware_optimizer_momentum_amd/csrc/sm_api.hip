@@ -147,14 +147,123 @@ struct NsWs {
   void* tmp;    // [batch][m*n] ping-pong iterate
   void* amat;   // [batch][r*r]
   void* amat2;  // [batch][r*r] (quintic term)
+  void* xt;     // [batch][n*m] transposed input      (bf16 NT path)
+  void* tmpt;   // [batch][n*m] transposed ping-pong  (bf16 NT path)
+  void* outt;   // [batch][n*m] transposed output partner (bf16 NT path)
 };
 
 void carve_ns(Carver& cv, int dt, int batch, int m, int n, NsWs& w) {
   const int64_t r = m < n ? m : n;
   const size_t es = dt_size(dt);
-  w.tmp = cv.take<void>((size_t)batch * m * n * es);
+  const size_t mn = (size_t)batch * m * n * es;
+  w.tmp = cv.take<void>(mn);
   w.amat = cv.take<void>((size_t)batch * r * r * es);
   w.amat2 = cv.take<void>((size_t)batch * r * r * es);
+  const bool nt = dt == BF16;
+  w.xt = nt ? cv.take<void>(mn) : nullptr;
+  w.tmpt = nt ? cv.take<void>(mn) : nullptr;
+  w.outt = nt ? cv.take<void>(mn) : nullptr;
+}
+
+// Whether every product of ns_core_nt meets the NT kernel's requirements
+// (alignment, leading dimensions, K a multiple of the unrolled k-step).
+bool ns_nt_ok(const void* x, const void* out, const NsWs& w, int batch, int m, int n) {
+  const bool wide = m <= n;
+  const int r = wide ? m : n, c = wide ? n : m;
+  const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
+  auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
+  auto mp = [](const void* q) { return const_cast<bf16_t*>(static_cast<const bf16_t*>(q)); };
+  NtLaunch gram;
+  std::memset(&gram, 0, sizeof(gram));
+  gram.a = bp(wide ? x : w.xt); gram.lda = c; gram.sa = mn;
+  gram.b = gram.a; gram.ldb = c; gram.sb = mn;
+  gram.c = mp(w.amat); gram.ldc = r; gram.sc = rr; gram.M = r; gram.N = r; gram.K = c;
+  gram.batch = batch;
+  NtLaunch ap;
+  std::memset(&ap, 0, sizeof(ap));
+  ap.a = bp(wide ? w.amat2 : x); ap.lda = wide ? r : n; ap.sa = wide ? rr : mn;
+  ap.b = bp(wide ? w.xt : w.amat); ap.ldb = r; ap.sb = wide ? mn : rr;
+  ap.cin = bp(x); ap.ldcin = n; ap.scin = mn;
+  ap.c = mp(out); ap.ldc = n; ap.sc = mn; ap.ct = mp(w.outt); ap.ldct = m; ap.sct = mn;
+  ap.M = m; ap.N = n; ap.K = r; ap.batch = batch;
+  NtLaunch tmp = ap;
+  tmp.c = mp(w.tmp); tmp.ct = mp(w.tmpt);
+  return gemm_nt_supported(gram) && gemm_nt_supported(ap) && gemm_nt_supported(tmp);
+}
+
+// Direct NS with the bf16 NT kernel: every product is A B^T with both
+// operands k-contiguous, because the iterate is kept in both orientations
+// (x and xt); each apply writes the next iterate and its transpose.
+// The caller checks ns_nt_ok first.
+sm_status ns_core_nt(const void* x, const void* xt, void* out, const NsWs& w,
+                     const float* scale, int batch, int m, int n, const sm_ns_params& p,
+                     hipStream_t s) {
+  const bool wide = m <= n;
+  const int r = wide ? m : n, c = wide ? n : m;
+  const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
+  const int K = p.iters;
+  auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
+  auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
+  const void* cur = x;
+  const void* curt = xt;
+  for (int k = 0; k < K; ++k) {
+    const bool last_out = ((K - 1 - k) % 2) == 0;
+    void* dst = last_out ? out : w.tmp;
+    void* dstt = last_out ? w.outt : w.tmpt;
+    const bool first = (k == 0) && scale;
+    NtLaunch g;
+    std::memset(&g, 0, sizeof(g));
+    // A = X X^T (wide) or Y^T Y (tall), symmetric
+    const void* gsrc = wide ? cur : curt;
+    g.a = bp(gsrc); g.lda = c; g.sa = mn;
+    g.b = bp(gsrc); g.ldb = c; g.sb = mn;
+    g.M = r; g.N = r; g.K = c; g.batch = batch; g.sym = true;
+    g.c = mp(w.amat); g.ldc = r; g.sc = rr;
+    g.scale = scale; g.alpha_pow = first ? 2 : 0;
+    g.alpha = (p.c == 0.f) ? p.b : 1.f;
+    SM_TRY(launch_gemm_nt(g, SM_K_GEMM_GRAM, s));
+    const void* bmat = w.amat;
+    if (p.c != 0.f) {  // B = c A A^T + b A  (A is symmetric)
+      NtLaunch q;
+      std::memset(&q, 0, sizeof(q));
+      q.a = bp(w.amat); q.lda = r; q.sa = rr;
+      q.b = bp(w.amat); q.ldb = r; q.sb = rr;
+      q.M = r; q.N = r; q.K = r; q.batch = batch; q.sym = true;
+      q.cin = bp(w.amat); q.ldcin = r; q.scin = rr;
+      q.c = mp(w.amat2); q.ldc = r; q.sc = rr;
+      q.alpha = p.c; q.beta = p.b;
+      SM_TRY(launch_gemm_nt(q, SM_K_GEMM_RR, s));
+      bmat = w.amat2;
+    }
+    // X' = a X + B X  (wide: A = B, B-operand = X^T) or Y' = a Y + Y B^T (tall)
+    NtLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    if (wide) {
+      a.a = bp(bmat); a.lda = r; a.sa = rr;
+      a.b = bp(curt); a.ldb = r; a.sb = mn;
+    } else {
+      a.a = bp(cur); a.lda = n; a.sa = mn;
+      a.b = bp(bmat); a.ldb = r; a.sb = rr;
+    }
+    a.M = m; a.N = n; a.K = r; a.batch = batch;
+    uint32_t abits;
+    std::memcpy(&abits, &p.a, 4);
+    if ((abits & 0xFFFFu) == 0u) {   // a is exact in bf16: fold a X into the MFMAs
+      a.ident = wide ? 1 : 2;
+      a.ident_bits = abits >> 16;
+    } else {                         // general a: add a X from the iterate in the epilogue
+      a.cin = bp(cur); a.ldcin = n; a.scin = mn;
+      a.beta = p.a; a.beta_pow = first ? 1 : 0;
+    }
+    a.c = mp(dst); a.ldc = n; a.sc = mn;
+    if (k + 1 < K) { a.ct = mp(dstt); a.ldct = m; a.sct = mn; }
+    a.scale = scale; a.alpha_pow = first ? 1 : 0;
+    a.alpha = 1.f;
+    SM_TRY(launch_gemm_nt(a, SM_K_GEMM_APPLY, s));
+    cur = dst;
+    curt = dstt;
+  }
+  return SM_OK;
 }
 
 // Products of one direct NS step on problems of shape m x n (x contiguous):
@@ -191,6 +300,10 @@ GemmArgs apply_args(const void* bm, int bm_dt, int bm_tbl, const void* x, int dt
 // the first step's GEMMs: A_0 = s^2 x x^T, X_1 = s (a x + B_0 x).
 sm_status ns_core(const void* x, void* out, const NsWs& w, const float* scale, int dt, int batch,
                   int m, int n, const sm_ns_params& p, hipStream_t s) {
+  if (dt == BF16 && w.xt && ns_nt_ok(x, out, w, batch, m, n)) {
+    SM_TRY(launch_transpose(x, w.xt, dt, batch, m, n, s));
+    return ns_core_nt(x, w.xt, out, w, scale, batch, m, n, p, s);
+  }
   const int r = m < n ? m : n;
   const int K = p.iters;
   const void* cur = x;

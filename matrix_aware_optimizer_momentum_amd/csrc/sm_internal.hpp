@@ -143,6 +143,10 @@ sm_status launch_vote_update(const uint64_t* bits, int M, int64_t words_stride,
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
                               int wdt, float lr, hipStream_t s);
 
+// xt[b] = x[b]^T for batch problems of m x n (row-major, contiguous).
+sm_status launch_transpose(const void* x, void* xt, int dt, int batch, int m, int n,
+                           hipStream_t s);
+
 // has_cache flags of nprob problems: hc[b] = cache_state(b)[0], where problem
 // b's {has_cache, a_t} pair is at tbl_addr(cs, b, per, 8).
 sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t* hc,
@@ -204,5 +208,32 @@ int gemm_tiles(int mfma_dt, int M, int N);
 
 // Launch with MFMA operand type mfma_dt (BF16 -> bf16 MFMA, F32 -> fp32 MFMA).
 sm_status launch_gemm(const GemmArgs& g, int mfma_dt, int kind, hipStream_t s);
+
+// ---------------------------------------------------------------- NT bf16 GEMM (NS hot path)
+
+// C[b] = alpha_b * A[b] B[b]^T + beta_b * Cin[b]; A: M x K, B: N x K, both
+// row-major bf16 with k contiguous; C (M x N) and optional C^T (N x M) bf16.
+// sym: A == B (C symmetric): only the lower tile triangle is computed and
+// mirrored.  alpha_b / beta_b as in GemmArgs.
+struct NtLaunch {
+  const bf16_t* a; int64_t lda, sa;
+  const bf16_t* b; int64_t ldb, sb;
+  const bf16_t* cin; int64_t ldcin, scin;
+  bf16_t* c; int64_t ldc, sc;
+  bf16_t* ct; int64_t ldct, sct;
+  const float* scale; int alpha_pow, beta_pow;
+  float alpha, beta;
+  int M, N, K, batch;
+  bool sym;
+  // Identity fold: 1 adds (a I) * B-operand part (C += a * B^T rows, the wide
+  // apply), 2 adds A-operand * (a I) (the tall apply); ident_bits = bf16(a),
+  // which must equal a exactly.
+  int ident;
+  uint32_t ident_bits;
+};
+
+// True when the operands satisfy the vector-load alignment of the NT kernel.
+bool gemm_nt_supported(const NtLaunch& L);
+sm_status launch_gemm_nt(const NtLaunch& L, int kind, hipStream_t s);
 
 }  // namespace sm

@@ -96,6 +96,19 @@ NS_CASES = [
     ("bf16", 3, 64, 576, 5, (1.5, -0.5, 0.0)),
     ("bf16", 2, 250, 130, 5, (1.5, -0.5, 0.0)),
     ("bf16", 2, 128, 384, 4, (1.8, -0.6, 0.04)),
+    # 256-tile kernel: partial tiles in every dimension, tall and wide
+    ("bf16", 2, 136, 520, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 520, 136, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 1, 264, 264, 3, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 256, 1024, 5, (1.8, -0.6, 0.04)),
+    ("bf16", 1, 1280, 1280, 5, (1.5, -0.5, 0.0)),
+    # 256-tile NT kernel with partial tiles (dimensions multiples of 128):
+    # identity fold (a = 1.5 exact in bf16) and the general a path (1.3)
+    ("bf16", 2, 384, 640, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 640, 384, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 3, 128, 1152, 3, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 384, 640, 5, (1.3, -0.3, 0.0)),
+    ("bf16", 2, 640, 384, 4, (1.3, -0.3, 0.0)),
 ]
 
 
