@@ -8,13 +8,17 @@
 //
 // Tile 256 x 256, 256 threads = 4 waves (2 x 2), each wave 128 x 128 as 4 x 4
 // blocks of v_mfma_f32_32x32x16_bf16 (256 float32 accumulators per lane).
-// Operands move HBM/L2 -> registers -> LDS in k-stages of 32 through a ring
-// of four 32 KB LDS stage buffers.  The global loads of stage k + 2 are issued
-// into one of two register slots before stage k is multiplied, and written to
-// LDS at the end of stage k + 1, so a load has two stages of MFMA work to
-// arrive; one barrier per stage.  The main loop is straight-line (loads
-// past the matrix edge are clamped to a valid address, see load_stage), so
-// the compiler's wait for a slot counts only the loads issued after it.
+// Operands move HBM/L2 -> LDS with gfx950 direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the instruction's LDS
+// base + 16 l), without passing through registers, into a ring of four 32 KB
+// k-stages (k = 32 each).  Step k multiplies stage k, issues the loads of
+// stage k + 3 into the buffer stage k - 1 left, and reads the fragments of
+// its own second k16 slice and of the first slice of stage k + 1 while its
+// MFMAs run (one memory instruction after each MFMA).  Before the step's
+// barrier each wave waits for its loads of stage k + 2 only, so the loads of
+// a stage have about two steps of MFMA work to arrive.  The barrier is a bare
+// s_barrier between compiler memory fences: the loads still in flight target
+// buffers nobody reads until a later barrier.
 //
 // LDS stage layout: A rows then B rows, 64 bytes per row, the four 16-byte k
 // chunks of row R stored at chunk position c ^ ((R >> 2) & 3).  Sixteen
@@ -65,45 +69,65 @@ struct NtArgs {
   int xcd_chunk;      // blocks per XCD after remapping (0: no remap)
 };
 
-// One k-stage of this thread: 4 rows of A and 4 of B (row t / 4 + 64 i,
-// 16-byte chunk t % 4).  Rows past the matrix are clamped to its last row
-// and k past K to its last chunk: an operand row outside the matrix only
-// feeds accumulator rows / columns that the epilogue never stores, and
-// chunks past K only occur in the prefetches beyond the last stage, which
-// are never multiplied.  The loads are therefore unconditional, which keeps
-// the loop free of branches.
-struct StageRegs {
-  uint4 a[4], b[4];
+// Direct-to-LDS loads of one k-stage: each wave fills 4 row groups of A and
+// 4 of B, 16 rows x 64 bytes (1 KB) per instruction.  Lane l of a group
+// covers row l / 4 and fetches the global k chunk that belongs at position
+// l % 4 of that row under the stage swizzle.  Rows past the matrix are
+// clamped to its last row and stages past K to the last stage: an operand row
+// outside the matrix only feeds accumulator rows / columns that the epilogue
+// never stores, and stages past K are prefetched but never multiplied.  The
+// loads are therefore unconditional.  Offsets are 32-bit byte offsets from
+// the problem's base (the launcher checks that they fit).
+struct DmaOffs {
+  uint32_t a[4], b[4];
 };
 
-__device__ __forceinline__ uint4 ld16(const bf16_t* __restrict__ base, int64_t ld, int row,
-                                      int rows, int k, int K) {
-  const int r = row < rows ? row : rows - 1;
-  const int kk = k < K ? k : K - 8;
-  return *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + kk);
-}
-
-__device__ __forceinline__ void load_stage(StageRegs& r, const bf16_t* __restrict__ A,
-                                           int64_t lda, int m0, int M,
-                                           const bf16_t* __restrict__ B, int64_t ldb, int n0,
-                                           int N, int k0, int K) {
-  const int row = threadIdx.x >> 2, kc = k0 + 8 * (threadIdx.x & 3);
+__device__ __forceinline__ DmaOffs dma_offsets(int64_t lda, int m0, int M, int64_t ldb, int n0,
+                                               int N) {
+  DmaOffs o;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane >> 2;
+  const int kc = 8 * ((lane & 3) ^ ((lane >> 4) & 3));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r.a[i] = ld16(A, lda, m0 + row + 64 * i, M, kc, K);
-    r.b[i] = ld16(B, ldb, n0 + row + 64 * i, N, kc, K);
+    const int grp = wave * 4 + i;
+    const int ra = m0 + grp * 16 + rl, rb = n0 + grp * 16 + rl;
+    o.a[i] = (uint32_t)(2 * ((ra < M ? ra : M - 1) * lda + kc));
+    o.b[i] = (uint32_t)(2 * ((rb < N ? rb : N - 1) * ldb + kc));
   }
+  return o;
 }
 
-__device__ __forceinline__ void store_stage(bf16_t* S, const StageRegs& r) {
-  const int row = threadIdx.x >> 2, c = threadIdx.x & 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = row + 64 * i;
-    const int off = R * BK + 8 * (c ^ ((R >> 2) & 3));
-    *reinterpret_cast<uint4*>(S + off) = r.a[i];
-    *reinterpret_cast<uint4*>(S + BOFF + off) = r.b[i];
-  }
+// Byte offset of k-stage k0: stages past K are clamped to the last one.
+__device__ __forceinline__ uint32_t stage_koff(int k0, int K) {
+  return 2u * (uint32_t)(k0 < K ? k0 : K - BK);
+}
+
+// Load q (0..3: A groups, 4..7: B groups) of this wave's share of a stage.
+__device__ __forceinline__ void dma_load(bf16_t* S, const char* A, const char* B,
+                                         const DmaOffs& o, uint32_t koff, int q) {
+  const int grp = (threadIdx.x >> 6) * 4 + (q & 3);
+  if (q < 4)
+    __builtin_amdgcn_global_load_lds(A + (o.a[q] + koff), S + grp * 16 * BK, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(B + (o.b[q - 4] + koff), S + BOFF + grp * 16 * BK, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt low
+// bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence (no wait for outstanding direct-
+// to-LDS loads); the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // 16-byte fragment of row R, k chunk c (0..3) of a stage operand.
@@ -127,40 +151,75 @@ __device__ __forceinline__ bf16x8 ident_frag(int half, uint32_t abits) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// One k-stage (two k16 slices) of this wave's 128 x 128 sub-tile.  IDM: 0
-// none; 1 adds (a I) times the B part for row block IB (wide apply); 2 adds
-// the A part times (a I) for column block IB (tall apply).
-template <int IDM, int IB>
-__device__ __forceinline__ void mma_stage(const bf16_t* S, int wm, int wn, f32x16 (&acc)[4][4],
-                                          uint32_t abits) {
+// The fragments of one k16 slice of this wave's 128 x 128 sub-tile.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const bf16_t* S, int wm, int wn, int s) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lk = lane >> 5;
-  bf16x8 af[2][4], bfg[2][4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int i = 0; i < 4; ++i) f.a[i] = frag(S, wm * 128 + i * 32 + lr, 2 * s + lk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[s][i] = frag(S, wm * 128 + i * 32 + lr, 2 * s + lk);
+  for (int j = 0; j < 4; ++j) f.b[j] = frag(S + BOFF, wn * 128 + j * 32 + lr, 2 * s + lk);
+}
+
+// One step of the main loop (stage k): the two k16 slices' MFMAs, each
+// followed by at most one memory instruction, in this order:
+//   slice 0 (f0): reads of this stage's slice-1 fragments into f1, then the
+//                 direct-to-LDS loads of stage k + 3 into buffer ld3;
+//   slice 1 (f1): reads of stage k + 1's slice-0 fragments into f0.
+// sched_barrier keeps the compiler from regrouping them (hoisting the reads
+// would need a second set of fragment registers).
+template <int IDM, int IB>
+__device__ __forceinline__ void nt_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                        const bf16_t* cur, const bf16_t* nxt, bf16_t* ld3,
+                                        const char* A, const char* B, const DmaOffs& o,
+                                        uint32_t koff3, int wm, int wn, bf16x8 id0,
+                                        bf16x8 id1) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bfg[s][j] = frag(S + BOFF, wn * 128 + j * 32 + lr, 2 * s + lk);
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
+    if (q < 4)
+      f1.a[q] = frag(cur, wm * 128 + q * 32 + lr, 2 + lk);
+    else if (q < 8)
+      f1.b[q - 4] = frag(cur + BOFF, wn * 128 + (q - 4) * 32 + lr, 2 + lk);
+    else
+      dma_load(ld3, A, B, o, koff3, q - 8);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (IDM == 1) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+    for (int j = 0; j < 4; ++j)
+      acc[IB][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id0, f0.b[j], acc[IB][j], 0, 0, 0);
+  } else if constexpr (IDM == 2) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
+      acc[i][IB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], id0, acc[i][IB], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfg[s][j], acc[i][j], 0, 0, 0);
-    if constexpr (IDM == 1) {
-      const bf16x8 id = ident_frag(s, abits);
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
+    if (q < 4)
+      f0.a[q] = frag(nxt, wm * 128 + q * 32 + lr, lk);
+    else if (q < 8)
+      f0.b[q - 4] = frag(nxt + BOFF, wn * 128 + (q - 4) * 32 + lr, lk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (IDM == 1) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[IB][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, bfg[s][j], acc[IB][j], 0, 0, 0);
-    } else if constexpr (IDM == 2) {
-      const bf16x8 id = ident_frag(s, abits);
+    for (int j = 0; j < 4; ++j)
+      acc[IB][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id1, f1.b[j], acc[IB][j], 0, 0, 0);
+  } else if constexpr (IDM == 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i][IB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], id, acc[i][IB], 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      acc[i][IB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], id1, acc[i][IB], 0, 0, 0);
   }
 }
 
@@ -275,36 +334,48 @@ void k_gemm_nt(NtArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Stage k sits in LDS buffer k % 4 while it is multiplied; its global
-  // loads were issued two stages earlier into register slot k % 2.  Step k:
-  // issue the loads of stage k + 2 into slot k % 2 (stage k left it for LDS
-  // one step ago), multiply stage k, write stage k + 1 from slot (k + 1) % 2
-  // into LDS buffer (k + 1) % 4 (last read at step k - 3), barrier.
-  const int nk = (g.K + BK - 1) / BK;
-  StageRegs r0, r1;
-  load_stage(r0, A, g.lda, m0, g.M, B, g.ldb, n0, g.N, 0, g.K);
-  load_stage(r1, A, g.lda, m0, g.M, B, g.ldb, n0, g.N, BK, g.K);
-  store_stage(S0, r0);
-  __syncthreads();
-#define SM_NT_STEP(KOFF, CUR, NXT, RK, RK1, IDM)                                         \
-  {                                                                                      \
-    const int k = kt + (KOFF);                                                           \
-    load_stage(RK, A, g.lda, m0, g.M, B, g.ldb, n0, g.N, (k + 2) * BK, g.K);             \
-    mma_stage<IDM, KOFF>(CUR, wm, wn, acc, g.ident_bits);                                \
-    store_stage(NXT, RK1);                                                               \
-    __syncthreads();                                                                     \
+  // Stage j sits in LDS buffer j % 4.  Step k: loads of stage k + 3 go into
+  // buffer (k + 3) % 4, whose stage k - 1 was last read in step k - 1; at
+  // the end of step k the wave waits for its loads of stage k + 2 (read from
+  // step k + 1 on), leaving the 8 loads of stage k + 3 in flight.
+  const int nk = g.K / BK;   // a multiple of 4 (the launcher requires K % 128 == 0)
+  const DmaOffs dof = dma_offsets(g.lda, m0, g.M, g.ldb, n0, g.N);
+  bf16x8 id0, id1;
+  if constexpr (IDM != 0) {
+    id0 = ident_frag(0, g.ident_bits);
+    id1 = ident_frag(1, g.ident_bits);
+  } else {
+    id0 = id1 = bf16x8{};
   }
-#define SM_NT_GROUP(IDM)                          \
-  SM_NT_STEP(0, S0, S1, r0, r1, IDM)              \
-  SM_NT_STEP(1, S1, S2, r1, r0, IDM)              \
-  SM_NT_STEP(2, S2, S3, r0, r1, IDM)              \
-  SM_NT_STEP(3, S3, S0, r1, r0, IDM)
-  // nk is a multiple of 4 (the launcher requires K % 128 == 0).  With the
-  // identity fold, the one group of four stages whose k range equals this
-  // wave's 128 output rows (wide) or columns (tall) adds a I: step s of that
-  // group covers block s.  The loop is peeled around that group so the
-  // accumulators follow a single code path; every wave still runs nk
-  // barriers.
+  const char* Ab = reinterpret_cast<const char*>(A);
+  const char* Bb = reinterpret_cast<const char*>(B);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_load(S0, Ab, Bb, dof, stage_koff(0, g.K), q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_load(S1, Ab, Bb, dof, stage_koff(BK, g.K), q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_load(S2, Ab, Bb, dof, stage_koff(2 * BK, g.K), q);
+  wait_vm<8>();            // stages 0 and 1 of this wave
+  barrier_nofence();
+  Frags f0, f1;
+  read_frags(f0, S0, wm, wn, 0);
+#define SM_NT_STEP(KOFF, CUR, NXT, L3, IDM)                                              \
+  {                                                                                    \
+    nt_step<IDM, KOFF>(acc, f0, f1, CUR, NXT, L3, Ab, Bb, dof,                         \
+                       stage_koff((kt + (KOFF) + 3) * BK, g.K), wm, wn, id0, id1);     \
+    wait_vm<8>();                                                                      \
+    barrier_nofence();                                                                 \
+  }
+#define SM_NT_GROUP(IDM)               \
+  SM_NT_STEP(0, S0, S1, S3, IDM)       \
+  SM_NT_STEP(1, S1, S2, S0, IDM)       \
+  SM_NT_STEP(2, S2, S3, S1, IDM)       \
+  SM_NT_STEP(3, S3, S0, S2, IDM)
+  // With the identity fold, the one group of four stages whose k range
+  // equals this wave's 128 output rows (wide) or columns (tall) adds a I:
+  // step s of that group covers block s.  The loop is peeled around that
+  // group so the accumulators follow a single code path; every wave still
+  // runs nk barriers.
   int kt = 0;
   if constexpr (IDM != 0) {
     const int id_kt = (IDM == 1 ? wr0 : wc0) / BK;   // a multiple of 4
@@ -321,6 +392,9 @@ void k_gemm_nt(NtArgs g) {
   }
 #undef SM_NT_GROUP
 #undef SM_NT_STEP
+  // the prefetches past the last stage must land before the buffers are reused
+  wait_vm<0>();
+  __syncthreads();
 
   // ---------------- epilogue (the stage buffers are free after the last barrier)
   float alpha = g.alpha, beta = g.beta;
@@ -425,6 +499,9 @@ bool gemm_nt_supported(const NtLaunch& L) {
   if (L.lda % 8 || L.ldb % 8 || L.sa % 8 || L.sb % 8 || L.ldc % 8 || L.sc % 8) return false;
   if (L.cin && (!al(L.cin) || L.ldcin % 8 || L.scin % 8)) return false;
   if (L.K % (4 * nt::BK)) return false;  // whole groups of four k-stages
+  // operand byte offsets within one problem must fit in 32 bits
+  if ((int64_t)L.M * L.lda >= (int64_t)1 << 31 || (int64_t)L.N * L.ldb >= (int64_t)1 << 31)
+    return false;   // (byte offsets below 2^32)
   if (L.ct && (!al(L.ct) || L.ldct % 8 || L.sct % 8)) return false;
   return true;
 }
@@ -453,7 +530,8 @@ sm_status launch_gemm_nt(const NtLaunch& L, int kind, hipStream_t s) {
   const int64_t blocks = (int64_t)g.tiles_per_prob * L.batch;
   // remap only when the grid splits evenly over the 8 XCDs
   g.xcd_chunk = (blocks % 8 == 0) ? (int)(blocks / 8) : 0;
-  const double flops = 2.0 * L.M * (double)L.N * L.K * L.batch;
+  // a symmetric product is credited with the half it needs (M N K), not 2 M N K
+  const double flops = (L.sym ? 1.0 : 2.0) * L.M * (double)L.N * L.K * L.batch;
   prof_begin(kind, flops, s);
   const dim3 grid((unsigned)blocks), block(NT);
   if (L.ident == 1)

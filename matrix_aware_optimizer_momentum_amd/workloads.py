@@ -82,14 +82,22 @@ class Workload:
         return sum(m * n for m, n in self.shapes)
 
     def ns_flops_per_step(self, muon_step: bool = True) -> float:
-        """Direct NS: 4 r^2 c per cubic iteration (+2 r^3 quintic) per problem."""
+        """Direct NS flops per step, counted as the kernels count them.
+
+        Per cubic iteration and problem the two products are 2 r^2 c each
+        (+2 r^3 for the quintic term).  The bf16 path computes the symmetric
+        Gram product X X^T (and A^2) as one triangle, so it is credited with
+        half of it: 3 r^2 c (+ r^3).  The f32 path computes full products.
+        """
         if not muon_step or self.algo == CACHE_MUON:
             return 0.0
+        sym = self.mdt == "bf16"
         tot = 0.0
         for m, n in self.shapes:
             r, c = min(m, n), max(m, n)
-            per = 4.0 * r * r * c + (2.0 * r ** 3 if self.ns_c != 0 else 0.0)
-            tot += per * self.ns_iters * self.M
+            gram = (1.0 if sym else 2.0) * r * r * c
+            quint = ((1.0 if sym else 2.0) * r ** 3) if self.ns_c != 0 else 0.0
+            tot += (gram + 2.0 * r * r * c + quint) * self.ns_iters * self.M
         return tot
 
     def scaled(self, layers_fraction: float = None, shapes=None, **kw) -> "Workload":
