@@ -1,0 +1,743 @@
+// Persistent grouped bf16 GEMM for the direct Newton-Schulz products.
+//
+// One launch computes every product of one kind (all Gram products X X^T,
+// or all applies B X, of one NS iteration) over several groups of batched
+// problems of different shapes: C = alpha_b * A B^T per problem, A M x K and
+// B N x K in the "operand" sense, fp32 accumulation, bf16 output.
+//
+// Operand storage.  An operand is either k-contiguous (KC: stored rows x K,
+// row-major) or k-major (KR: stored K x rows, row-major, i.e. its transpose
+// is what is multiplied).  With KR the NS iterate never has to exist in both
+// orientations: the wide apply reads X (m x n, contraction over m) as KR, the
+// tall Gram X^T X reads X as KR on both sides.  KR fragments come out of LDS
+// through the gfx950 transposing read ds_read_b64_tr_b16.
+//
+// Work split.  The grid is one workgroup per CU (or fewer), each walking the
+// flat list of 256 x 256 output tiles with stride gridDim; workgroups of one
+// XCD take consecutive tiles so that they share that XCD's L2.  Groups are
+// ordered by the caller (largest K first) so that concurrent tiles have
+// similar work.
+//
+// Pipeline.  256 threads = 4 waves (2 x 2), each wave 128 x 128 of the tile
+// as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Operands go HBM -> LDS with
+// direct-to-LDS loads (global_load_lds_dwordx4) into a ring of four 32 KB
+// k-stages (k = 32), four separate LDS arrays indexed statically (so that the
+// compiler can tell a pending load's target from the buffers being read).
+// Step k multiplies stage k, issues the loads of stage k + 3 (into the buffer
+// stage k - 1 left) and reads the fragments of its second k16 slice and of
+// the first slice of stage k + 1 while its MFMAs run; at its end each wave
+// waits for its own loads of stage k + 2 and the workgroup meets at a
+// fence-free barrier.  Every tile has a multiple of 4 stages, so stage k
+// always sits in buffer k % 4.  The stage sequence runs on across tile
+// boundaries: the next tile's first stages load during the current tile's
+// last steps and its epilogue.
+//
+// Epilogue: value = alpha_b * acc, rounded to bf16 with v_cvt_pk_bf16_f32 and
+// stored straight from registers (no LDS: the ring holds the next tile).
+// Row-major C: two rounds of quad DPP shuffles give each lane 1 row x 4
+// columns (8-byte stores).  A symmetric product (A == B) computes only tiles
+// with tm >= tn and stores each off-diagonal tile a second time, transposed,
+// as the mirror tile (8-byte stores of 4 consecutive rows of one column).
+//
+// Identity fold.  The apply X' = a X + B X gets a X from extra MFMAs in the
+// k-stages that cover the output's own rows (wide: (a I) X) or columns (tall:
+// X (a I)), against an a I fragment; a is split into up to two bf16 terms
+// a_hi + a_lo, whose products with bf16 data are exact in fp32.
+#include "sm_internal.hpp"
+
+namespace sm {
+namespace nsg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 32, NT = 256;
+constexpr int HALF = 256 * BK;   // bf16 elements of one operand in a stage (16 KB)
+constexpr int STG = 2 * HALF;    // a stage: A half, then B half (32 KB)
+
+// Kernel-side group descriptor (the launcher copies NsgGroup into it).
+struct Grp {
+  const bf16_t* a;
+  const bf16_t* b;
+  bf16_t* c;
+  const float* scale;
+  int64_t lda, sa, ldb, sb, ldc, sc;
+  int M, N, K, batch;
+  int combo;          // instantiation index within the kernel's role
+  int a_kr, b_kr;
+  int sym;
+  int ident;          // 0 none, 1 A side (wide apply), 2 B side (tall apply)
+  uint32_t id_hi, id_lo;   // bf16 bits of the identity terms
+  int alpha_pow;
+  float alpha;
+  int tiles_m, tiles_n, tiles_per_prob, tile_begin;
+};
+
+struct Args {
+  Grp g[kNsgMaxGroups];
+  int ngroups, total_tiles, xcd_chunk;
+};
+
+// ---------------------------------------------------------------- LDS layouts
+// KC half: 256 operand rows x 64 bytes; the 16-byte k chunk c of row R sits
+// at position c ^ ((R >> 2) & 3) (16 consecutive rows read at one chunk hit
+// 16 distinct 4-bank groups).
+// KR half: 32 k-rows x 512 bytes; the 16-byte column chunk c of k-row r sits
+// at position c ^ (4 (r & 3)) (the four k-rows a transposing read touches
+// land in four distinct 64-byte bank ranges).
+
+// ---------------------------------------------------------------- tile decode
+struct Tile {
+  int gi, prob, tm, tn;
+};
+
+__device__ __forceinline__ Tile decode_tile(const Args& A, int t) {
+  Tile r;
+  int gi = 0;
+#pragma unroll
+  for (int q = 1; q < kNsgMaxGroups; ++q)
+    if (q < A.ngroups && t >= A.g[q].tile_begin) gi = q;
+  const Grp& g = A.g[gi];
+  const int local = t - g.tile_begin;
+  r.gi = gi;
+  r.prob = local / g.tiles_per_prob;
+  const int u = local - r.prob * g.tiles_per_prob;
+  if (g.sym) {  // lower triangle, row-major: u = tm (tm + 1) / 2 + tn
+    int tm = (int)((sqrtf(8.f * u + 1.f) - 1.f) * 0.5f);
+    while ((tm + 1) * (tm + 2) / 2 <= u) ++tm;
+    while (tm * (tm + 1) / 2 > u) --tm;
+    r.tm = tm;
+    r.tn = u - tm * (tm + 1) / 2;
+  } else if (g.tiles_m <= 4) {  // few row tiles: consecutive tiles share B's rows
+    r.tn = u / g.tiles_m;
+    r.tm = u - r.tn * g.tiles_m;
+  } else {
+    r.tm = u / g.tiles_n;
+    r.tn = u - r.tm * g.tiles_n;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- DMA side
+// Load q of a wave lands at 1 KB * (4 wave + q) within the stage half:
+//  KC: operand rows row0 + 16 (4 wave + q) + lane / 4, k chunk of position
+//      lane % 4;
+//  KR: k-row 2 (4 wave + q) + lane / 32, column chunk of position lane % 32.
+// Operand rows past the matrix are clamped to its last row (KC) or last
+// column chunk (KR): they only feed outputs that are never stored.  The
+// per-lane byte offsets are for stage 0; stage k0 adds k0 * kstride bytes
+// (kstride = 2 for KC, 2 ld for KR).
+__device__ __forceinline__ void dma_offsets(uint32_t (&off)[4], int kr, int64_t ld, int row0,
+                                            int rows) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int slot = 4 * wave + q;
+    if (!kr) {
+      int row = row0 + 16 * slot + (lane >> 2);
+      row = row < rows ? row : rows - 1;
+      const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+      off[q] = (uint32_t)(2 * ((int64_t)row * ld + 8 * chunk));
+    } else {
+      const int krow = 2 * slot + (lane >> 5);
+      int col = row0 + 8 * ((lane & 31) ^ (4 * (krow & 3)));
+      col = col < rows ? col : rows - 8;
+      off[q] = (uint32_t)(2 * ((int64_t)krow * ld + col));
+    }
+  }
+}
+
+// Load position: one group of 4 stages of one tile, with the per-lane
+// offsets of that tile.
+struct LoadPos {
+  const char* abase;
+  const char* bbase;
+  uint32_t aoff[4], boff[4];
+  uint32_t akst, bkst;
+  int t;        // tile
+  int kg;       // group of 4 stages within the tile
+  int nkg;      // groups in the tile
+};
+
+__device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int t) {
+  const Tile tl = decode_tile(A, t);
+  const Grp& g = A.g[tl.gi];
+  L.abase = reinterpret_cast<const char*>(g.a + (int64_t)tl.prob * g.sa);
+  L.bbase = reinterpret_cast<const char*>(g.b + (int64_t)tl.prob * g.sb);
+  dma_offsets(L.aoff, g.a_kr, g.lda, tl.tm * 256, g.M);
+  dma_offsets(L.boff, g.b_kr, g.ldb, tl.tn * 256, g.N);
+  L.akst = g.a_kr ? (uint32_t)(2 * g.lda) : 2u;
+  L.bkst = g.b_kr ? (uint32_t)(2 * g.ldb) : 2u;
+  L.t = t;
+  L.kg = 0;
+  L.nkg = g.K / (4 * BK);
+}
+
+// The group after p: the next group of the same tile, else the first group of
+// the workgroup's next tile; past the last tile p itself (its stages are then
+// loaded again into buffers that are never multiplied).
+__device__ __forceinline__ void load_advance(LoadPos& p, const Args& A, int stride) {
+  if (p.kg + 1 < p.nkg) {
+    ++p.kg;
+  } else if (p.t + stride < A.total_tiles) {
+    load_tile_setup(p, A, p.t + stride);
+  }
+}
+
+// One direct-to-LDS load: each lane's 16 bytes at base + voff land at LDS
+// byte address m0 + 16 lane.  Issued from inline assembly so that the
+// compiler, which cannot tell which LDS bytes a pending load writes, does not
+// add a wait for all of them before every LDS read: the kernel's own
+// s_waitcnt vmcnt and barriers order the buffers (see the pipeline notes).
+// The instruction has no register result; M0 is set one wait state ahead.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t m0) {
+  // The operands are wave-uniform; readfirstlane makes them scalar registers.
+  // It returns int: each half goes through uint32_t so that the low half is
+  // zero-extended (a sign-extended low half would corrupt the high bits).
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t sm0 = (uint32_t)__builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(sm0)
+               : "memory", "m0");
+}
+
+// LDS byte address of a shared array.
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Load q (0..3: A, 4..7: B) of this wave's share of stage s (0..3) of the
+// group at L into the stage buffer at LDS byte address sbuf; wbase is this
+// wave's first slot (4 wave KB).
+__device__ __forceinline__ void dma_load(uint32_t sbuf, uint32_t wbase, const LoadPos& L, int s,
+                                         int q) {
+  const uint32_t k0 = (uint32_t)(L.kg * 4 * BK + s * BK);
+  if (q < 4)
+    dma16(L.abase, L.aoff[q] + k0 * L.akst, sbuf + wbase + 1024u * q);
+  else
+    dma16(L.bbase, L.boff[q - 4] + k0 * L.bkst, sbuf + 2u * HALF + wbase + 1024u * (q - 4));
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt low
+// bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A wave-uniform float loaded through the scalar unit (counted by lgkmcnt,
+// not vmcnt, so it does not wait for the loads in flight); the wait is in the
+// same statement.
+__device__ __forceinline__ float scalar_load(const float* p) {
+  float v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Workgroup barrier without a memory fence (no wait for outstanding direct-
+// to-LDS loads); the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------- fragments
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+// Per-lane LDS element offsets of the fragment reads of one operand half for
+// this wave's rows rbase.. (128 rows = 4 blocks of 32): KC uses one offset
+// per k16 slice (block i adds 32 rows = i * 32 * BK elements); KR uses one
+// per (block, read) pair (slice s adds 16 k-rows = s * 16 * 256 elements).
+struct FragOffs {
+  int kc[2];
+  int kr[4][2];
+};
+
+__device__ __forceinline__ void frag_offsets(FragOffs& f, int rbase) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int R = rbase + lr, c = 2 * s + lk;
+    f.kc[s] = R * BK + 8 * (c ^ ((R >> 2) & 3));
+  }
+  const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int krow = 8 * (g >> 1) + 4 * r + (j >> 2);
+      const int col = rbase + 32 * i + 16 * (g & 1) + 4 * (j & 3);
+      const int chunk = (col >> 3) ^ (4 * (krow & 3));
+      f.kr[i][r] = krow * 256 + 8 * chunk + (col & 7);
+    }
+}
+
+// Fragment of block i (32 operand rows), k16 slice s, of an operand half.
+template <int KR>
+__device__ __forceinline__ bf16x8 frag(const bf16_t* H, const FragOffs& f, int i, int s) {
+  if constexpr (!KR) {
+    return *reinterpret_cast<const bf16x8*>(H + f.kc[s] + i * 32 * BK);
+  } else {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const bf16_t* p0 = H + f.kr[i][0] + s * 16 * 256;
+    const bf16_t* p1 = H + f.kr[i][1] + s * 16 * 256;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(__attribute__((address_space(3))) void*)(p0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(__attribute__((address_space(3))) void*)(p1));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  }
+}
+
+// Identity fragment for k16 slice `half` of the 32-index block a stage of the
+// identity group covers: lane l supplies index l % 32 and k = 16 half +
+// 8 (l / 32) + e; the element is `bits` where they agree.
+__device__ __forceinline__ bf16x8 ident_frag(int half, uint32_t bits) {
+  const int lane = threadIdx.x & 63;
+  const int e = (lane & 31) - 16 * half - 8 * (lane >> 5);
+  uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
+  const uint32_t v = bits << (16 * (e & 1));
+  if (e >= 0 && e < 8) {
+    const int d = e >> 1;
+    w0 = d == 0 ? v : 0u; w1 = d == 1 ? v : 0u; w2 = d == 2 ? v : 0u; w3 = d == 3 ? v : 0u;
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+}
+
+// The identity terms of a tile: bf16 bit patterns of a_hi and a_lo.
+struct Ident {
+  uint32_t hi, lo;
+};
+
+#define SM_MFMA(A_, B_, C_) C_ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_, B_, C_, 0, 0, 0)
+
+// Identity MFMAs of slice s for block IB.
+template <int IDM, int IDT, int IB>
+__device__ __forceinline__ void ident_mma(f32x16 (&acc)[4][4], const Frags& f, const Ident& id,
+                                          int s) {
+  if constexpr (IDM == 1) {
+    const bf16x8 h = ident_frag(s, id.hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) SM_MFMA(h, f.b[j], acc[IB][j]);
+    if constexpr (IDT == 2) {
+      const bf16x8 l = ident_frag(s, id.lo);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) SM_MFMA(l, f.b[j], acc[IB][j]);
+    }
+  } else if constexpr (IDM == 2) {
+    const bf16x8 h = ident_frag(s, id.hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], h, acc[i][IB]);
+    if constexpr (IDT == 2) {
+      const bf16x8 l = ident_frag(s, id.lo);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], l, acc[i][IB]);
+    }
+  }
+}
+
+// One step of the main loop (stage k in buffer cur): the two k16 slices'
+// MFMAs, each followed by at most two memory instructions:
+//   slice 0 (f0): reads of this stage's slice-1 fragments into f1, then this
+//                 wave's direct-to-LDS loads of stage k + 3 (stage ls of the
+//                 group at L) into buffer ld3;
+//   slice 1 (f1): reads of stage k + 1's slice-0 fragments into f0.
+// sched_barrier keeps the compiler from regrouping them (hoisting the reads
+// would need a second set of fragment registers).  A KR fragment takes two
+// transposing reads.
+template <int AKR, int BKR, int IDM, int IDT, int IB>
+__device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                         const bf16_t* cur, const bf16_t* nxt, uint32_t ld3,
+                                         uint32_t wbase, const LoadPos& L, int ls,
+                                         const FragOffs& fa, const FragOffs& fb,
+                                         const Ident& id) {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 2, j = q & 3;
+    SM_MFMA(f0.a[i], f0.b[j], acc[i][j]);
+    if (q < 4) f1.a[q] = frag<AKR>(cur, fa, q, 1);
+    else if (q < 8) f1.b[q - 4] = frag<BKR>(cur + HALF, fb, q - 4, 1);
+    else dma_load(ld3, wbase, L, ls, q - 8);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  ident_mma<IDM, IDT, IB>(acc, f0, id, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 2, j = q & 3;
+    SM_MFMA(f1.a[i], f1.b[j], acc[i][j]);
+    if (q < 4) f0.a[q] = frag<AKR>(nxt, fa, q, 0);
+    else if (q < 8) f0.b[q - 4] = frag<BKR>(nxt + HALF, fb, q - 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  ident_mma<IDM, IDT, IB>(acc, f1, id, 1);
+}
+
+// The k loop of one tile: nk / 4 groups of 4 steps.  Step s of a group
+// multiplies the group's stage s (buffer S_s) and loads the stage 3 ahead:
+// for s = 0 the group's own stage 3, for s = 1..3 stages 0..2 of the next
+// group, possibly of the next tile.  The load position LP therefore moves on
+// between steps 0 and 1.  `lenient`: the tile follows an epilogue (see the
+// wait rule at the end of each step).
+template <int AKR, int BKR, int IDM, int IDT>
+__device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                         const bf16_t* S0, const bf16_t* S1, const bf16_t* S2,
+                                         const bf16_t* S3, const uint32_t (&la)[4],
+                                         uint32_t wbase, LoadPos& LP, const Args& A,
+                                         int stride, int nkg, int id_g, const FragOffs& fa,
+                                         const FragOffs& fb, const Ident& id, bool lenient) {
+  for (int kg = 0; kg < nkg; ++kg) {
+#define SM_NSG_STEP(S_, CUR, NXT, LD3, LS, IDM_)                                            \
+    {                                                                                       \
+      nsg_step<AKR, BKR, IDM_, IDT, S_>(acc, f0, f1, CUR, NXT, LD3, wbase, LP, LS, fa, fb,  \
+                                        id);                                                \
+      /* stage k + 2 must have landed: in steady state the 8 loads of stage k + 3  */       \
+      /* follow it; in a tile's first step an epilogue's >= 55 stores do as well.  */       \
+      if ((S_) == 0 && kg == 0 && lenient) wait_vm<63>(); else wait_vm<8>();                \
+      barrier_nofence();                                                                    \
+      if ((S_) == 0) load_advance(LP, A, stride);                                           \
+    }
+#define SM_NSG_GROUP(IDM_)                      \
+    SM_NSG_STEP(0, S0, S1, la[3], 3, IDM_)      \
+    SM_NSG_STEP(1, S1, S2, la[0], 0, IDM_)      \
+    SM_NSG_STEP(2, S2, S3, la[1], 1, IDM_)      \
+    SM_NSG_STEP(3, S3, S0, la[2], 2, IDM_)
+    if constexpr (IDM != 0) {
+      if (kg == id_g) {
+        SM_NSG_GROUP(IDM)
+        continue;
+      }
+    }
+    SM_NSG_GROUP(0)
+#undef SM_NSG_GROUP
+#undef SM_NSG_STEP
+  }
+}
+
+// ---------------------------------------------------------------- epilogue
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t cvt2(float x, float y) {
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Stores this wave's 128 x 128 sub-tile (origin wr0, wc0) of alpha * acc, and
+// its transpose into the mirror tile when `mirror`.  Returns with every
+// store issued (and, for a tile that is not entirely inside the matrix, the
+// wave's memory operations drained, so that the next steps' waits hold).
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc, int M,
+                                         int N, int wr0, int wc0, float alpha, bool mirror) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lq = (lane >> 5) * 4;
+  const bool interior = wr0 + 128 <= M && wc0 + 128 <= N;
+  const int cm = lane & 3;
+  const int rsel = ((cm & 1) << 1) | (cm >> 1);   // which of the 4 rows this lane ends with
+  const int colq = lr & ~3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
+        const uint32_t v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
+        const uint32_t v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
+        if (mirror) {   // C^T: the 4 rows are 4 consecutive elements of one row
+          const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
+          bf16_t* p = C + (int64_t)trow * ldc + tcol;
+          if (interior) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(v0, v1);
+          } else if (trow < N) {
+            const uint32_t w[2] = {v0, v1};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (tcol + e < M) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+        const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
+        const uint32_t mine = (cm & 1) ? v1 : v0;
+        const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
+        const uint32_t hi = (cm & 1) ? mine : recv;
+        const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
+        const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
+        const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
+        const uint32_t keep = (cm < 2) ? ra : rb;
+        const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
+        const int row = wr0 + i * 32 + q * 8 + lq + rsel;
+        const int col = wc0 + j * 32 + colq;
+        bf16_t* p = C + (int64_t)row * ldc + col;
+        if (interior) {
+          *reinterpret_cast<uint2*>(p) = out;
+        } else if (row < M) {
+          if (col + 4 <= N) {
+            *reinterpret_cast<uint2*>(p) = out;
+          } else {
+            const uint32_t w[2] = {out.x, out.y};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+  if (!interior) wait_vm<0>();
+}
+
+// ---------------------------------------------------------------- kernel
+// Combos per role (index = Grp::combo): operand layouts and identity mode.
+//   GRAM:  0 (KC, KC)        1 (KR, KR)
+//   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
+//          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
+//   RR:    0 (KC, KC, B-side id, 1 term)   1 (KC, KC, B-side id, 2 terms)
+template <int ROLE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_ns(Args args) {
+  __shared__ __attribute__((aligned(16))) bf16_t S0[STG];
+  __shared__ __attribute__((aligned(16))) bf16_t S1[STG];
+  __shared__ __attribute__((aligned(16))) bf16_t S2[STG];
+  __shared__ __attribute__((aligned(16))) bf16_t S3[STG];
+  const Args& A = args;   // read in place from the kernel argument segment
+  int vid = blockIdx.x;
+  if (A.xcd_chunk > 0) vid = (vid & 7) * A.xcd_chunk + (vid >> 3);
+  const int stride = gridDim.x;
+  int t = vid;
+  if (t >= A.total_tiles) return;
+
+  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  FragOffs fa, fb;
+  frag_offsets(fa, wm * 128);
+  frag_offsets(fb, wn * 128);
+
+  // LDS byte addresses of the stage buffers and of this wave's load slots
+  const uint32_t la[4] = {lds_addr(S0), lds_addr(S1), lds_addr(S2), lds_addr(S3)};
+  const uint32_t wbase = 4096u * (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+  // prologue: stages 0..2 of the first tile
+  LoadPos LP;
+  load_tile_setup(LP, A, t);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_load(la[0], wbase, LP, 0, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_load(la[1], wbase, LP, 1, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_load(la[2], wbase, LP, 2, q);
+  wait_vm<8>();   // stages 0 and 1 of this wave
+  barrier_nofence();
+  Frags f0, f1;
+  f0.a[0] = f0.a[1] = f0.a[2] = f0.a[3] = bf16x8{};
+  f0.b[0] = f0.b[1] = f0.b[2] = f0.b[3] = bf16x8{};
+  f1 = f0;
+
+  bool lenient = false;
+  for (;;) {
+    const Tile tc = decode_tile(A, t);
+    const Grp& g = A.g[tc.gi];
+    const int nkg = g.K / (4 * BK);
+    const int wr0 = tc.tm * 256 + wm * 128, wc0 = tc.tn * 256 + wn * 128;
+    // identity group of this wave: the 128 k-indices equal to its rows / columns
+    const int id_g = (g.ident == 1 ? wr0 : wc0) / (4 * BK);
+    Ident id;
+    id.hi = g.id_hi;
+    id.lo = g.id_lo;
+    // slice 0 of the tile's first stage (in S0; the previous tile's last step
+    // read it with that tile's layouts, so it is read again with this tile's)
+#define SM_NSG_F0(AKR_, BKR_)                                                 \
+    {                                                                         \
+      for (int i = 0; i < 4; ++i) f0.a[i] = frag<AKR_>(S0, fa, i, 0);         \
+      for (int i = 0; i < 4; ++i) f0.b[i] = frag<BKR_>(S0 + HALF, fb, i, 0);  \
+    }
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    if constexpr (ROLE == SM_K_GEMM_GRAM) {
+      if (g.combo == 0) {
+        SM_NSG_F0(0, 0)
+        run_tile<0, 0, 0, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      } else {
+        SM_NSG_F0(1, 1)
+        run_tile<1, 1, 0, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      }
+    } else if constexpr (ROLE == SM_K_GEMM_APPLY) {
+      if (g.combo == 0) {
+        SM_NSG_F0(0, 1)
+        run_tile<0, 1, 1, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      } else if (g.combo == 1) {
+        SM_NSG_F0(0, 0)
+        run_tile<0, 0, 2, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      } else if (g.combo == 2) {
+        SM_NSG_F0(0, 1)
+        run_tile<0, 1, 1, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      } else {
+        SM_NSG_F0(0, 0)
+        run_tile<0, 0, 2, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      }
+    } else {
+      if (g.combo == 0) {
+        SM_NSG_F0(0, 0)
+        run_tile<0, 0, 2, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      } else {
+        SM_NSG_F0(0, 0)
+        run_tile<0, 0, 2, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+      }
+    }
+#undef SM_NSG_F0
+    float alpha = g.alpha;
+    if (g.scale) {
+      const float sc = scalar_load(g.scale + tc.prob);
+      for (int p = 0; p < g.alpha_pow; ++p) alpha *= sc;
+    }
+    epilogue(acc, g.c + (int64_t)tc.prob * g.sc, g.ldc, g.M, g.N, wr0, wc0, alpha,
+             g.sym && tc.tm != tc.tn);
+    t += stride;
+    if (t >= A.total_tiles) break;
+    lenient = true;
+  }
+  wait_vm<0>();   // the loads past the last stage target this workgroup's LDS
+}
+
+}  // namespace nsg
+
+// ------------------------------------------------------------------ launcher
+
+namespace {
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+}  // namespace
+
+bool gemm_ns_supported(const NsgGroup& G) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (!al(G.a) || !al(G.b) || !al(G.c)) return false;
+  if (G.lda % 8 || G.ldb % 8 || G.sa % 8 || G.sb % 8 || G.ldc % 4 || G.sc % 4) return false;
+  if (G.M < 8 || G.N < 8 || G.K <= 0 || G.K % (4 * nsg::BK)) return false;
+  if (G.a_kr && G.M % 8) return false;
+  if (G.b_kr && G.N % 8) return false;
+  // operand byte offsets within one problem must fit in 32 bits
+  const int64_t ea = G.a_kr ? (int64_t)G.K * G.lda : (int64_t)G.M * G.lda;
+  const int64_t eb = G.b_kr ? (int64_t)G.K * G.ldb : (int64_t)G.N * G.ldb;
+  if (2 * ea >= ((int64_t)1 << 32) || 2 * eb >= ((int64_t)1 << 32)) return false;
+  if (G.sym && (G.M != G.N || G.a != G.b || G.a_kr != G.b_kr)) return false;
+  if (G.ident && G.ident_terms != 1 && G.ident_terms != 2) return false;
+  if (G.ident == 1 && G.K != G.M) return false;
+  if (G.ident == 2 && G.K != G.N) return false;
+  return true;
+}
+
+// Splits a into hi + lo with hi = bf16(a) and lo = bf16(a - hi); returns the
+// number of terms needed for the sum to equal a exactly (1 or 2), or 0 if
+// two are not enough.
+int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits) {
+  auto bf = [](float x) {
+    uint32_t u;
+    std::memcpy(&u, &x, 4);
+    const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return r >> 16;
+  };
+  auto fl = [](uint32_t b) {
+    const uint32_t u = b << 16;
+    float x;
+    std::memcpy(&x, &u, 4);
+    return x;
+  };
+  const uint32_t h = bf(a);
+  const float rem = a - fl(h);
+  const uint32_t l = bf(rem);
+  *hi_bits = h;
+  *lo_bits = l;
+  if (rem == 0.f) return 1;
+  return (fl(h) + fl(l) == a) ? 2 : 0;
+}
+
+sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s) {
+  using namespace nsg;
+  if (ngroups <= 0 || ngroups > kNsgMaxGroups) return SM_ERR_ARG;
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  int tiles = 0;
+  double flops = 0.0;
+  for (int q = 0; q < ngroups; ++q) {
+    const NsgGroup& G = groups[q];
+    Grp& g = a.g[q];
+    g.a = G.a; g.b = G.b; g.c = G.c; g.scale = G.scale;
+    g.lda = G.lda; g.sa = G.sa; g.ldb = G.ldb; g.sb = G.sb; g.ldc = G.ldc; g.sc = G.sc;
+    g.M = G.M; g.N = G.N; g.K = G.K; g.batch = G.batch;
+    g.a_kr = G.a_kr ? 1 : 0;
+    g.b_kr = G.b_kr ? 1 : 0;
+    g.sym = G.sym ? 1 : 0;
+    g.ident = G.ident;
+    g.id_hi = G.ident_hi;
+    g.id_lo = G.ident_terms == 2 ? G.ident_lo : 0u;
+    g.alpha_pow = G.alpha_pow;
+    g.alpha = G.alpha;
+    // the instantiation for this group's layouts and identity mode
+    int combo = -1;
+    const bool two = G.ident && G.ident_terms == 2;
+    if (kind == SM_K_GEMM_GRAM) {
+      if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
+      else if (!G.ident && g.a_kr && g.b_kr) combo = 1;
+    } else if (kind == SM_K_GEMM_APPLY) {
+      if (G.ident == 1 && !g.a_kr && g.b_kr) combo = two ? 2 : 0;
+      else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 1;
+    } else if (kind == SM_K_GEMM_RR) {
+      if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 1 : 0;
+    }
+    if (combo < 0) return SM_ERR_UNSUPPORTED;
+    g.combo = combo;
+    g.tiles_m = (G.M + 255) / 256;
+    g.tiles_n = (G.N + 255) / 256;
+    g.tiles_per_prob = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
+    g.tile_begin = tiles;
+    const int64_t gt = (int64_t)g.tiles_per_prob * G.batch;
+    if (gt <= 0) return SM_ERR_ARG;
+    if ((int64_t)tiles + gt > (int64_t)1 << 30) return SM_ERR_UNSUPPORTED;
+    tiles += (int)gt;
+    // a symmetric product is credited with the half it needs (M N K)
+    flops += (g.sym ? 1.0 : 2.0) * G.M * (double)G.N * G.K * G.batch;
+  }
+  a.ngroups = ngroups;
+  a.total_tiles = tiles;
+  const int grid = std::min(tiles, cu_count());
+  a.xcd_chunk = (grid % 8 == 0) ? grid / 8 : 0;
+  prof_begin(kind, flops, s);
+  if (kind == SM_K_GEMM_GRAM)
+    hipLaunchKernelGGL((k_gemm_ns<SM_K_GEMM_GRAM>), dim3(grid), dim3(NT), 0, s, a);
+  else if (kind == SM_K_GEMM_APPLY)
+    hipLaunchKernelGGL((k_gemm_ns<SM_K_GEMM_APPLY>), dim3(grid), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_ns<SM_K_GEMM_RR>), dim3(grid), dim3(NT), 0, s, a);
+  prof_end(s);
+  return check_launch();
+}
+
+}  // namespace sm

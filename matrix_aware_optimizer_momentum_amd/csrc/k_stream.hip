@@ -331,50 +331,6 @@ __global__ void k_cache_decide(const float* resid, int parts, int nprob, int r,
   }
 }
 
-// Batched transpose x[b] (m x n) -> xt[b] (n x m) through a 64 x 64 LDS
-// tile: 16-byte row loads, 8 strided LDS reads per 16-byte row store.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_transpose(const T* x, T* xt, int m, int n,
-                                                        int tiles_n) {
-  constexpr int TS = 64, VEC = 16 / sizeof(T), PITCH = TS + VEC;
-  __shared__ __attribute__((aligned(16))) T tile[TS * PITCH];
-  const int b = blockIdx.y;
-  const int tr = blockIdx.x / tiles_n, tc = blockIdx.x % tiles_n;
-  const int r0 = tr * TS, c0 = tc * TS;
-  const T* xp = x + (int64_t)b * m * n;
-  T* tp = xt + (int64_t)b * m * n;
-  const bool vec = (n % VEC) == 0 && (m % VEC) == 0;
-  constexpr int CPR = TS / VEC;            // vector chunks per tile row
-  for (int v = threadIdx.x; v < TS * CPR; v += kThreads) {
-    const int rr = v / CPR, cc = (v % CPR) * VEC;
-    const int r = r0 + rr, c = c0 + cc;
-    T* dst = tile + rr * PITCH + cc;
-    if (vec && r < m && c + VEC <= n) {
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(xp + (int64_t)r * n + c);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        dst[e] = (r < m && c + e < n) ? xp[(int64_t)r * n + c + e] : (T)0;
-    }
-  }
-  __syncthreads();
-  for (int v = threadIdx.x; v < TS * CPR; v += kThreads) {
-    const int oc_r = v / CPR, oc_c = (v % CPR) * VEC;   // output row (= input col), col
-    const int orow = c0 + oc_r, ocol = r0 + oc_c;
-    if (orow >= n) continue;
-    __attribute__((aligned(16))) T vals[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) vals[e] = tile[(oc_c + e) * PITCH + oc_r];
-    T* dst = tp + (int64_t)orow * m + ocol;
-    if (vec && ocol + VEC <= m) {
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        if (ocol + e < m) dst[e] = vals[e];
-    }
-  }
-}
 
 inline int stream_blocks(int64_t count, int nprob) {
   // enough blocks in flight to fill 256 CUs several times over
@@ -501,18 +457,6 @@ sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, c
   return check_launch();
 }
 
-sm_status launch_transpose(const void* x, void* xt, int dt, int batch, int m, int n,
-                            hipStream_t s) {
-  if (batch <= 0 || m <= 0 || n <= 0) return SM_OK;
-  const int tiles_m = (m + 63) / 64, tiles_n = (n + 63) / 64;
-  dim3 grid(tiles_m * tiles_n, batch);
-  prof_begin(SM_K_MISC, 2.0 * batch * (double)m * n * dt_size(dt), s);
-  SM_DISPATCH_DT(dt, T,
-      hipLaunchKernelGGL((k_transpose<T>), grid, dim3(kThreads), 0, s, (const T*)x, (T*)xt, m,
-                         n, tiles_n));
-  prof_end(s);
-  return check_launch();
-}
 
 sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t* hc,
                                   hipStream_t s) {

@@ -147,123 +147,126 @@ struct NsWs {
   void* tmp;    // [batch][m*n] ping-pong iterate
   void* amat;   // [batch][r*r]
   void* amat2;  // [batch][r*r] (quintic term)
-  void* xt;     // [batch][n*m] transposed input      (bf16 NT path)
-  void* tmpt;   // [batch][n*m] transposed ping-pong  (bf16 NT path)
-  void* outt;   // [batch][n*m] transposed output partner (bf16 NT path)
 };
 
 void carve_ns(Carver& cv, int dt, int batch, int m, int n, NsWs& w) {
   const int64_t r = m < n ? m : n;
   const size_t es = dt_size(dt);
-  const size_t mn = (size_t)batch * m * n * es;
-  w.tmp = cv.take<void>(mn);
+  w.tmp = cv.take<void>((size_t)batch * m * n * es);
   w.amat = cv.take<void>((size_t)batch * r * r * es);
   w.amat2 = cv.take<void>((size_t)batch * r * r * es);
-  const bool nt = dt == BF16;
-  w.xt = nt ? cv.take<void>(mn) : nullptr;
-  w.tmpt = nt ? cv.take<void>(mn) : nullptr;
-  w.outt = nt ? cv.take<void>(mn) : nullptr;
 }
 
-// Whether every product of ns_core_nt meets the NT kernel's requirements
-// (alignment, leading dimensions, K a multiple of the unrolled k-step).
-bool ns_nt_ok(const void* x, const void* out, const NsWs& w, int batch, int m, int n) {
-  const bool wide = m <= n;
-  const int r = wide ? m : n, c = wide ? n : m;
-  const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
-  auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
-  auto mp = [](const void* q) { return const_cast<bf16_t*>(static_cast<const bf16_t*>(q)); };
-  NtLaunch gram;
-  std::memset(&gram, 0, sizeof(gram));
-  gram.a = bp(wide ? x : w.xt); gram.lda = c; gram.sa = mn;
-  gram.b = gram.a; gram.ldb = c; gram.sb = mn;
-  gram.c = mp(w.amat); gram.ldc = r; gram.sc = rr; gram.M = r; gram.N = r; gram.K = c;
-  gram.batch = batch;
-  NtLaunch ap;
-  std::memset(&ap, 0, sizeof(ap));
-  ap.a = bp(wide ? w.amat2 : x); ap.lda = wide ? r : n; ap.sa = wide ? rr : mn;
-  ap.b = bp(wide ? w.xt : w.amat); ap.ldb = r; ap.sb = wide ? mn : rr;
-  ap.cin = bp(x); ap.ldcin = n; ap.scin = mn;
-  ap.c = mp(out); ap.ldc = n; ap.sc = mn; ap.ct = mp(w.outt); ap.ldct = m; ap.sct = mn;
-  ap.M = m; ap.N = n; ap.K = r; ap.batch = batch;
-  NtLaunch tmp = ap;
-  tmp.c = mp(w.tmp); tmp.ct = mp(w.tmpt);
-  return gemm_nt_supported(gram) && gemm_nt_supported(ap) && gemm_nt_supported(tmp);
-}
+// One batch of same-shaped direct-NS problems: x[batch][m][n] -> out.
+struct NsJob {
+  const void* x;
+  void* out;
+  NsWs w;
+  const float* scale;
+  int batch, m, n;
+};
 
-// Direct NS with the bf16 NT kernel: every product is A B^T with both
-// operands k-contiguous, because the iterate is kept in both orientations
-// (x and xt); each apply writes the next iterate and its transpose.
-// The caller checks ns_nt_ok first.
-sm_status ns_core_nt(const void* x, const void* xt, void* out, const NsWs& w,
-                     const float* scale, int batch, int m, int n, const sm_ns_params& p,
-                     hipStream_t s) {
-  const bool wide = m <= n;
-  const int r = wide ? m : n, c = wide ? n : m;
+// The grouped-kernel descriptors of one NS iteration of job j:
+//   gram:  A_k = alpha X X^T (wide: X KC on both sides) or X^T X (tall: X KR
+//          on both sides), symmetric, alpha = b (c = 0) or 1, times s^2 in
+//          the first iteration;
+//   rr:    B_k = c (A_k A_k + (b / c) A_k), the quintic term (c != 0);
+//   apply: X_{k+1} = (B_k + a I) X_k (wide: A = B_k, B operand = X_k as KR)
+//          or X_k (B_k + a I) (tall: A = X_k, B operand = B_k), times s in
+//          the first iteration.
+struct NsDesc {
+  NsgGroup gram, rr, apply;
+};
+
+bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, const sm_ns_params& p,
+             NsDesc& d) {
+  const bool wide = j.m <= j.n;
+  const int m = j.m, n = j.n, r = wide ? m : n;
   const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
-  const int K = p.iters;
   auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
   auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
-  const void* cur = x;
-  const void* curt = xt;
-  for (int k = 0; k < K; ++k) {
-    const bool last_out = ((K - 1 - k) % 2) == 0;
-    void* dst = last_out ? out : w.tmp;
-    void* dstt = last_out ? w.outt : w.tmpt;
-    const bool first = (k == 0) && scale;
-    NtLaunch g;
-    std::memset(&g, 0, sizeof(g));
-    // A = X X^T (wide) or Y^T Y (tall), symmetric
-    const void* gsrc = wide ? cur : curt;
-    g.a = bp(gsrc); g.lda = c; g.sa = mn;
-    g.b = bp(gsrc); g.ldb = c; g.sb = mn;
-    g.M = r; g.N = r; g.K = c; g.batch = batch; g.sym = true;
-    g.c = mp(w.amat); g.ldc = r; g.sc = rr;
-    g.scale = scale; g.alpha_pow = first ? 2 : 0;
-    g.alpha = (p.c == 0.f) ? p.b : 1.f;
-    SM_TRY(launch_gemm_nt(g, SM_K_GEMM_GRAM, s));
-    const void* bmat = w.amat;
-    if (p.c != 0.f) {  // B = c A A^T + b A  (A is symmetric)
-      NtLaunch q;
-      std::memset(&q, 0, sizeof(q));
-      q.a = bp(w.amat); q.lda = r; q.sa = rr;
-      q.b = bp(w.amat); q.ldb = r; q.sb = rr;
-      q.M = r; q.N = r; q.K = r; q.batch = batch; q.sym = true;
-      q.cin = bp(w.amat); q.ldcin = r; q.scin = rr;
-      q.c = mp(w.amat2); q.ldc = r; q.sc = rr;
-      q.alpha = p.c; q.beta = p.b;
-      SM_TRY(launch_gemm_nt(q, SM_K_GEMM_RR, s));
-      bmat = w.amat2;
-    }
-    // X' = a X + B X  (wide: A = B, B-operand = X^T) or Y' = a Y + Y B^T (tall)
-    NtLaunch a;
-    std::memset(&a, 0, sizeof(a));
-    if (wide) {
-      a.a = bp(bmat); a.lda = r; a.sa = rr;
-      a.b = bp(curt); a.ldb = r; a.sb = mn;
-    } else {
-      a.a = bp(cur); a.lda = n; a.sa = mn;
-      a.b = bp(bmat); a.ldb = r; a.sb = rr;
-    }
-    a.M = m; a.N = n; a.K = r; a.batch = batch;
-    uint32_t abits;
-    std::memcpy(&abits, &p.a, 4);
-    if ((abits & 0xFFFFu) == 0u) {   // a is exact in bf16: fold a X into the MFMAs
-      a.ident = wide ? 1 : 2;
-      a.ident_bits = abits >> 16;
-    } else {                         // general a: add a X from the iterate in the epilogue
-      a.cin = bp(cur); a.ldcin = n; a.scin = mn;
-      a.beta = p.a; a.beta_pow = first ? 1 : 0;
-    }
-    a.c = mp(dst); a.ldc = n; a.sc = mn;
-    if (k + 1 < K) { a.ct = mp(dstt); a.ldct = m; a.sct = mn; }
-    a.scale = scale; a.alpha_pow = first ? 1 : 0;
-    a.alpha = 1.f;
-    SM_TRY(launch_gemm_nt(a, SM_K_GEMM_APPLY, s));
-    cur = dst;
-    curt = dstt;
+  std::memset(&d, 0, sizeof(d));
+  NsgGroup& g = d.gram;
+  g.a = bp(cur); g.lda = n; g.sa = mn; g.a_kr = wide ? 0 : 1;
+  g.b = bp(cur); g.ldb = n; g.sb = mn; g.b_kr = wide ? 0 : 1;
+  g.c = mp(j.w.amat); g.ldc = r; g.sc = rr;
+  g.scale = j.scale; g.alpha_pow = first && j.scale ? 2 : 0;
+  g.alpha = (p.c == 0.f) ? p.b : 1.f;
+  g.M = r; g.N = r; g.K = wide ? n : m; g.batch = j.batch; g.sym = 1;
+  if (!gemm_ns_supported(g)) return false;
+  const void* bmat = j.w.amat;
+  if (p.c != 0.f) {
+    NsgGroup& q = d.rr;
+    q.a = bp(j.w.amat); q.lda = r; q.sa = rr;
+    q.b = bp(j.w.amat); q.ldb = r; q.sb = rr;
+    q.c = mp(j.w.amat2); q.ldc = r; q.sc = rr;
+    q.alpha = p.c;
+    q.M = r; q.N = r; q.K = r; q.batch = j.batch; q.sym = 1;
+    q.ident = 2;
+    q.ident_terms = ns_ident_split(p.b / p.c, &q.ident_hi, &q.ident_lo);
+    if (q.ident_terms == 0 || !gemm_ns_supported(q)) return false;
+    bmat = j.w.amat2;
+  }
+  NsgGroup& a = d.apply;
+  if (wide) {
+    a.a = bp(bmat); a.lda = r; a.sa = rr;
+    a.b = bp(cur); a.ldb = n; a.sb = mn; a.b_kr = 1;
+    a.ident = 1;
+  } else {
+    a.a = bp(cur); a.lda = n; a.sa = mn;
+    a.b = bp(bmat); a.ldb = r; a.sb = rr;
+    a.ident = 2;
+  }
+  a.c = mp(dst); a.ldc = n; a.sc = mn;
+  a.scale = j.scale; a.alpha_pow = first && j.scale ? 1 : 0; a.alpha = 1.f;
+  a.M = m; a.N = n; a.K = r; a.batch = j.batch;
+  a.ident_terms = ns_ident_split(p.a, &a.ident_hi, &a.ident_lo);
+  return a.ident_terms != 0 && gemm_ns_supported(a);
+}
+
+// Launches one product kind for all jobs, at most kNsgMaxGroups groups per
+// launch, groups ordered by decreasing K so that concurrent tiles carry
+// similar work.
+sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
+  std::stable_sort(gs.begin(), gs.end(),
+                   [](const NsgGroup& x, const NsgGroup& y) { return x.K > y.K; });
+  for (size_t i = 0; i < gs.size(); i += kNsgMaxGroups) {
+    const int ng = (int)std::min<size_t>(kNsgMaxGroups, gs.size() - i);
+    SM_TRY(launch_gemm_ns(gs.data() + i, ng, kind, s));
   }
   return SM_OK;
+}
+
+// Direct NS on bf16 jobs with the grouped kernel, all jobs' products of one
+// kind and iteration in one launch.  Returns SM_ERR_UNSUPPORTED (nothing
+// launched) if some job does not meet the kernel's requirements.
+sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipStream_t s) {
+  const int K = p.iters;
+  std::vector<NsDesc> d(jobs.size());
+  for (int k = 0; k < K; ++k) {
+    std::vector<NsgGroup> gram, rr, apply;
+    for (size_t i = 0; i < jobs.size(); ++i) {
+      const NsJob& j = jobs[i];
+      const void* cur = k == 0 ? j.x : (((K - k) % 2 == 0) ? j.out : j.w.tmp);
+      void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
+      if (!ns_desc(j, cur, dst, k == 0, p, d[i])) return SM_ERR_UNSUPPORTED;
+      gram.push_back(d[i].gram);
+      if (p.c != 0.f) rr.push_back(d[i].rr);
+      apply.push_back(d[i].apply);
+    }
+    SM_TRY(launch_ns_groups(gram, SM_K_GEMM_GRAM, s));
+    if (!rr.empty()) SM_TRY(launch_ns_groups(rr, SM_K_GEMM_RR, s));
+    SM_TRY(launch_ns_groups(apply, SM_K_GEMM_APPLY, s));
+  }
+  return SM_OK;
+}
+
+// Whether ns_grouped takes job j (checked for the first iteration's
+// pointers; later iterations use buffers of the same shapes and alignment).
+bool ns_grouped_ok(const NsJob& j, int dt, const sm_ns_params& p) {
+  if (dt != BF16) return false;
+  NsDesc d;
+  return ns_desc(j, j.x, j.out, true, p, d) && ns_desc(j, j.out, j.w.tmp, false, p, d);
 }
 
 // Products of one direct NS step on problems of shape m x n (x contiguous):
@@ -300,10 +303,8 @@ GemmArgs apply_args(const void* bm, int bm_dt, int bm_tbl, const void* x, int dt
 // the first step's GEMMs: A_0 = s^2 x x^T, X_1 = s (a x + B_0 x).
 sm_status ns_core(const void* x, void* out, const NsWs& w, const float* scale, int dt, int batch,
                   int m, int n, const sm_ns_params& p, hipStream_t s) {
-  if (dt == BF16 && w.xt && ns_nt_ok(x, out, w, batch, m, n)) {
-    SM_TRY(launch_transpose(x, w.xt, dt, batch, m, n, s));
-    return ns_core_nt(x, w.xt, out, w, scale, batch, m, n, p, s);
-  }
+  const NsJob job{x, out, w, scale, batch, m, n};
+  if (ns_grouped_ok(job, dt, p)) return ns_grouped(std::vector<NsJob>{job}, p, s);
   const int r = m < n ? m : n;
   const int K = p.iters;
   const void* cur = x;
@@ -751,42 +752,60 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
   const bool muon_step =
       (c->algo != SM_LION_MUON) || (c->period > 0 && (t % c->period) == 0);
   const bool polar = c->update == SM_UPDATE_POLAR && muon_step;
-  Carver cv(ws);
-  for (const Chunk& ch : chunks) {
+  // Tables of the chunks' per-matrix pointers.
+  struct ChunkRun {
     ChunkWs w;
-    carve_chunk(cv, *c, ch, w);
-    const int nc = (int)ch.mats.size();
-    const int B = nc * M;
-    const int64_t count = (int64_t)ch.m * ch.n;
-    const int64_t words = (count + 63) / 64;
     PtrTbl mom, grad, wt, qt, cs;
-    std::memset(&mom, 0, sizeof(mom));
-    std::memset(&grad, 0, sizeof(grad));
-    std::memset(&wt, 0, sizeof(wt));
-    std::memset(&qt, 0, sizeof(qt));
-    std::memset(&cs, 0, sizeof(cs));
-    for (int j = 0; j < nc; ++j) {
+    int nc, B;
+    int64_t count, words;
+  };
+  std::vector<ChunkRun> runs(chunks.size());
+  Carver cv(ws);
+  for (size_t ci = 0; ci < chunks.size(); ++ci) {
+    const Chunk& ch = chunks[ci];
+    ChunkRun& r = runs[ci];
+    carve_chunk(cv, *c, ch, r.w);
+    r.nc = (int)ch.mats.size();
+    r.B = r.nc * M;
+    r.count = (int64_t)ch.m * ch.n;
+    r.words = (r.count + 63) / 64;
+    std::memset(&r.mom, 0, sizeof(r.mom));
+    std::memset(&r.grad, 0, sizeof(r.grad));
+    std::memset(&r.wt, 0, sizeof(r.wt));
+    std::memset(&r.qt, 0, sizeof(r.qt));
+    std::memset(&r.cs, 0, sizeof(r.cs));
+    for (int j = 0; j < r.nc; ++j) {
       const sm_matrix& a = mats[ch.mats[j]];
-      mom.p[j] = static_cast<const char*>(a.mom);
-      grad.p[j] = static_cast<const char*>(a.grad);
-      wt.p[j] = static_cast<const char*>(a.w);
-      qt.p[j] = reinterpret_cast<const char*>(a.q_cache);
-      cs.p[j] = reinterpret_cast<const char*>(a.cache_state);
+      r.mom.p[j] = static_cast<const char*>(a.mom);
+      r.grad.p[j] = static_cast<const char*>(a.grad);
+      r.wt.p[j] = static_cast<const char*>(a.w);
+      r.qt.p[j] = reinterpret_cast<const char*>(a.q_cache);
+      r.cs.p[j] = reinterpret_cast<const char*>(a.cache_state);
     }
-    // a1 (+ a2 partials): momentum, and the NS input or the Lion signs
+  }
+  // a1 (+ a2 partials): momentum, and the NS input or the Lion signs
+  for (size_t ci = 0; ci < chunks.size(); ++ci) {
+    ChunkRun& r = runs[ci];
     if (c->algo == SM_LION_MUON) {
       if (muon_step)
-        SM_TRY(launch_lion(mom, grad, M, B, count, c->mdt, c->gdt, c->beta1, c->beta2, w.x0,
-                           c->mdt, w.partials, nullptr, 0, s));
+        SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
+                           r.w.x0, c->mdt, r.w.partials, nullptr, 0, s));
       else
-        SM_TRY(launch_lion(mom, grad, M, B, count, c->mdt, c->gdt, c->beta1, c->beta2, nullptr,
-                           c->mdt, nullptr, w.bits, words, s));
+        SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
+                           nullptr, c->mdt, nullptr, r.w.bits, r.words, s));
     } else {
-      SM_TRY(launch_ema_single(mom, grad, M, B, count, c->mdt, c->gdt, c->beta1, w.x0, c->mdt,
-                               w.partials, s));
+      SM_TRY(launch_ema_single(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, r.w.x0,
+                               c->mdt, r.w.partials, s));
     }
-    if (muon_step) {
-      SM_TRY(launch_scale_finalize(w.partials, B, c->ns.eps, w.scale, s));
+    if (muon_step) SM_TRY(launch_scale_finalize(r.w.partials, r.B, c->ns.eps, r.w.scale, s));
+  }
+  // a3-a5: the direction.  Direct NS runs all chunks the grouped kernel takes
+  // together (one launch per product kind and iteration).
+  if (muon_step) {
+    std::vector<NsJob> grouped;
+    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+      const Chunk& ch = chunks[ci];
+      ChunkRun& r = runs[ci];
       if (c->algo == SM_CACHE_MUON) {
         // diag rows follow the matrices' order; a chunk's matrices may not be
         // consecutive, so write per chunk into the rows of its first matrix
@@ -794,23 +813,34 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
         float* dg = nullptr;
         if (diag) {
           bool consecutive = true;
-          for (int j = 1; j < nc; ++j) consecutive &= (ch.mats[j] == ch.mats[0] + j);
+          for (int j = 1; j < r.nc; ++j) consecutive &= (ch.mats[j] == ch.mats[0] + j);
           if (consecutive) dg = diag + (int64_t)ch.mats[0] * M * 2;
         }
-        SM_TRY(gram_core(w.x0, w.d, qt, cs, M, nullptr, nullptr, dg, 2, w.gram, w.scale,
-                         c->mdt, B, ch.m, ch.n, c->ns, c->gamma, c->cache_mode, t, s));
-      } else {
-        SM_TRY(ns_core(w.x0, w.d, w.ns, w.scale, c->mdt, B, ch.m, ch.n, c->ns, s));
+        SM_TRY(gram_core(r.w.x0, r.w.d, r.qt, r.cs, M, nullptr, nullptr, dg, 2, r.w.gram,
+                         r.w.scale, c->mdt, r.B, ch.m, ch.n, c->ns, c->gamma, c->cache_mode, t,
+                         s));
+        continue;
       }
-      if (polar) {
-        SM_TRY(launch_polar_update(w.d, c->mdt, nc, count, wt, c->wdt, c->lr, s));
-      } else {
-        SM_TRY(launch_sign_pack(w.d, c->mdt, B, count, w.bits, words, s));
-      }
+      const NsJob job{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.B, ch.m, ch.n};
+      if (ns_grouped_ok(job, c->mdt, c->ns))
+        grouped.push_back(job);
+      else
+        SM_TRY(ns_core(r.w.x0, r.w.d, r.w.ns, r.w.scale, c->mdt, r.B, ch.m, ch.n, c->ns, s));
+    }
+    if (!grouped.empty()) SM_TRY(ns_grouped(grouped, c->ns, s));
+  }
+  // a7-a10: signs, pack, vote and update (or the polar update)
+  for (size_t ci = 0; ci < chunks.size(); ++ci) {
+    ChunkRun& r = runs[ci];
+    if (muon_step) {
+      if (polar)
+        SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));
+      else
+        SM_TRY(launch_sign_pack(r.w.d, c->mdt, r.B, r.count, r.w.bits, r.words, s));
     }
     if (!polar)
-      SM_TRY(launch_vote_update(w.bits, M, words, (int64_t)M * words, nc, count, wt, c->wdt,
-                                c->lr, nullptr, s));
+      SM_TRY(launch_vote_update(r.w.bits, M, r.words, (int64_t)M * r.words, r.nc, r.count, r.wt,
+                                c->wdt, c->lr, nullptr, s));
   }
   return SM_OK;
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <algorithm>
+#include <cstring>
 
 #include "../../include/sm.h"
 
@@ -143,10 +145,6 @@ sm_status launch_vote_update(const uint64_t* bits, int M, int64_t words_stride,
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
                               int wdt, float lr, hipStream_t s);
 
-// xt[b] = x[b]^T for batch problems of m x n (row-major, contiguous).
-sm_status launch_transpose(const void* x, void* xt, int dt, int batch, int m, int n,
-                           hipStream_t s);
-
 // has_cache flags of nprob problems: hc[b] = cache_state(b)[0], where problem
 // b's {has_cache, a_t} pair is at tbl_addr(cs, b, per, 8).
 sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t* hc,
@@ -209,31 +207,34 @@ int gemm_tiles(int mfma_dt, int M, int N);
 // Launch with MFMA operand type mfma_dt (BF16 -> bf16 MFMA, F32 -> fp32 MFMA).
 sm_status launch_gemm(const GemmArgs& g, int mfma_dt, int kind, hipStream_t s);
 
-// ---------------------------------------------------------------- NT bf16 GEMM (NS hot path)
+// ---------------------------------------------------------------- grouped NS GEMM
 
-// C[b] = alpha_b * A[b] B[b]^T + beta_b * Cin[b]; A: M x K, B: N x K, both
-// row-major bf16 with k contiguous; C (M x N) and optional C^T (N x M) bf16.
-// sym: A == B (C symmetric): only the lower tile triangle is computed and
-// mirrored.  alpha_b / beta_b as in GemmArgs.
-struct NtLaunch {
-  const bf16_t* a; int64_t lda, sa;
-  const bf16_t* b; int64_t ldb, sb;
-  const bf16_t* cin; int64_t ldcin, scin;
+// One group of batched problems for the persistent NS GEMM:
+// C[b] = alpha_b * A[b] B[b]^T (+ identity term), A: M x K, B: N x K in the
+// operand sense, bf16, C (M x N) row-major bf16.  An operand with *_kr set is
+// stored k-major (K x rows, row-major, leading dimension ld over rows).
+// sym: A == B (same layout), C symmetric: only tm >= tn tiles are computed,
+// off-diagonal ones are also stored transposed.  ident: 1 adds (a I) times
+// the B part (needs K == M), 2 adds the A part times (a I) (needs K == N);
+// a = hi + lo as bf16 bit patterns (ident_terms 1: hi only).
+// alpha_b = alpha * scale[b]^alpha_pow (scale may be null).
+constexpr int kNsgMaxGroups = 4;
+struct NsgGroup {
+  const bf16_t* a; int64_t lda, sa; int a_kr;
+  const bf16_t* b; int64_t ldb, sb; int b_kr;
   bf16_t* c; int64_t ldc, sc;
-  bf16_t* ct; int64_t ldct, sct;
-  const float* scale; int alpha_pow, beta_pow;
-  float alpha, beta;
+  const float* scale; int alpha_pow; float alpha;
   int M, N, K, batch;
-  bool sym;
-  // Identity fold: 1 adds (a I) * B-operand part (C += a * B^T rows, the wide
-  // apply), 2 adds A-operand * (a I) (the tall apply); ident_bits = bf16(a),
-  // which must equal a exactly.
-  int ident;
-  uint32_t ident_bits;
+  int sym;
+  int ident, ident_terms;
+  uint32_t ident_hi, ident_lo;
 };
 
-// True when the operands satisfy the vector-load alignment of the NT kernel.
-bool gemm_nt_supported(const NtLaunch& L);
-sm_status launch_gemm_nt(const NtLaunch& L, int kind, hipStream_t s);
+bool gemm_ns_supported(const NsgGroup& g);
+// Splits a into bf16 terms hi (+ lo); returns the number of terms whose sum
+// is exactly a (1 or 2), or 0 if two do not suffice.
+int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
+// All groups of one launch must be of the same kind (Gram, apply or r x r).
+sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s);
 
 }  // namespace sm
