@@ -12,11 +12,12 @@
 // tall Gram X^T X reads X as KR on both sides.  KR fragments come out of LDS
 // through the gfx950 transposing read ds_read_b64_tr_b16.
 //
-// Work split.  The grid is one workgroup per CU (or fewer), each walking the
-// flat list of 256 x 256 output tiles with stride gridDim; workgroups of one
-// XCD take consecutive tiles so that they share that XCD's L2.  Groups are
-// ordered by the caller (largest K first) so that concurrent tiles have
-// similar work.
+// Work split.  The grid is one workgroup per CU (or fewer), walking the flat
+// list of 256 x 256 output tiles in rounds of gridDim tiles, in alternating
+// direction (snake); workgroups of one XCD take consecutive tiles so that
+// they share that XCD's L2.  Groups are ordered by the caller (largest K
+// first), so concurrent tiles have similar work and the snake evens out the
+// rest.
 //
 // Pipeline.  256 threads = 4 waves (2 x 2), each wave 128 x 128 of the tile
 // as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Operands go HBM -> LDS with
@@ -90,6 +91,13 @@ struct Args {
 // land in four distinct 64-byte bank ranges).
 
 // ---------------------------------------------------------------- tile decode
+// Tile of round r for workgroup v (of stride): rounds alternate direction, so
+// with the list ordered from long to short K a workgroup that had a long tile
+// in one round tends to get a short one in the next.
+__device__ __forceinline__ int tile_of(int r, int v, int stride) {
+  return r * stride + ((r & 1) ? stride - 1 - v : v);
+}
+
 struct Tile {
   int gi, prob, tm, tn;
 };
@@ -157,12 +165,17 @@ struct LoadPos {
   const char* bbase;
   uint32_t aoff[4], boff[4];
   uint32_t akst, bkst;
-  int t;        // tile
+  int r;        // round of the tile (tile = tile_of(r, workgroup, stride))
   int kg;       // group of 4 stages within the tile
   int nkg;      // groups in the tile
 };
 
-__device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int t) {
+__device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r, int t) {
+  // The tile index is wave-uniform; readfirstlane states it, so that the
+  // decode and the argument reads are scalar (a vector read of the arguments
+  // would wait for every load in flight).
+  t = __builtin_amdgcn_readfirstlane(t);
+  r = __builtin_amdgcn_readfirstlane(r);
   const Tile tl = decode_tile(A, t);
   const Grp& g = A.g[tl.gi];
   L.abase = reinterpret_cast<const char*>(g.a + (int64_t)tl.prob * g.sa);
@@ -171,7 +184,7 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int t
   dma_offsets(L.boff, g.b_kr, g.ldb, tl.tn * 256, g.N);
   L.akst = g.a_kr ? (uint32_t)(2 * g.lda) : 2u;
   L.bkst = g.b_kr ? (uint32_t)(2 * g.ldb) : 2u;
-  L.t = t;
+  L.r = r;
   L.kg = 0;
   L.nkg = g.K / (4 * BK);
 }
@@ -179,11 +192,12 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int t
 // The group after p: the next group of the same tile, else the first group of
 // the workgroup's next tile; past the last tile p itself (its stages are then
 // loaded again into buffers that are never multiplied).
-__device__ __forceinline__ void load_advance(LoadPos& p, const Args& A, int stride) {
+__device__ __forceinline__ void load_advance(LoadPos& p, const Args& A, int vid, int stride) {
   if (p.kg + 1 < p.nkg) {
     ++p.kg;
-  } else if (p.t + stride < A.total_tiles) {
-    load_tile_setup(p, A, p.t + stride);
+  } else {
+    const int nt = tile_of(p.r + 1, vid, stride);
+    if (nt < A.total_tiles) load_tile_setup(p, A, p.r + 1, nt);
   }
 }
 
@@ -260,34 +274,46 @@ struct Frags {
 // this wave's rows rbase.. (128 rows = 4 blocks of 32): KC uses one offset
 // per k16 slice (block i adds 32 rows = i * 32 * BK elements); KR uses one
 // per (block, read) pair (slice s adds 16 k-rows = s * 16 * 256 elements).
-struct FragOffs {
+// Only the layout's own offsets are computed, per tile, so that they are not
+// live across the epilogue.
+template <int KR>
+struct FragOffs;
+
+template <>
+struct FragOffs<0> {
   int kc[2];
-  int kr[4][2];
+  __device__ __forceinline__ explicit FragOffs(int rbase) {
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int R = rbase + lr, c = 2 * s + lk;
+      kc[s] = R * BK + 8 * (c ^ ((R >> 2) & 3));
+    }
+  }
 };
 
-__device__ __forceinline__ void frag_offsets(FragOffs& f, int rbase) {
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lk = lane >> 5;
+template <>
+struct FragOffs<1> {
+  int kr[4][2];
+  __device__ __forceinline__ explicit FragOffs(int rbase) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int R = rbase + lr, c = 2 * s + lk;
-    f.kc[s] = R * BK + 8 * (c ^ ((R >> 2) & 3));
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int krow = 8 * (g >> 1) + 4 * r + (j >> 2);
+        const int col = rbase + 32 * i + 16 * (g & 1) + 4 * (j & 3);
+        const int chunk = (col >> 3) ^ (4 * (krow & 3));
+        kr[i][r] = krow * 256 + 8 * chunk + (col & 7);
+      }
   }
-  const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int krow = 8 * (g >> 1) + 4 * r + (j >> 2);
-      const int col = rbase + 32 * i + 16 * (g & 1) + 4 * (j & 3);
-      const int chunk = (col >> 3) ^ (4 * (krow & 3));
-      f.kr[i][r] = krow * 256 + 8 * chunk + (col & 7);
-    }
-}
+};
 
 // Fragment of block i (32 operand rows), k16 slice s, of an operand half.
 template <int KR>
-__device__ __forceinline__ bf16x8 frag(const bf16_t* H, const FragOffs& f, int i, int s) {
+__device__ __forceinline__ bf16x8 frag(const bf16_t* H, const FragOffs<KR>& f, int i, int s) {
   if constexpr (!KR) {
     return *reinterpret_cast<const bf16x8*>(H + f.kc[s] + i * 32 * BK);
   } else {
@@ -363,7 +389,7 @@ template <int AKR, int BKR, int IDM, int IDT, int IB>
 __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                          const bf16_t* cur, const bf16_t* nxt, uint32_t ld3,
                                          uint32_t wbase, const LoadPos& L, int ls,
-                                         const FragOffs& fa, const FragOffs& fb,
+                                         const FragOffs<AKR>& fa, const FragOffs<BKR>& fb,
                                          const Ident& id) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -397,9 +423,17 @@ template <int AKR, int BKR, int IDM, int IDT>
 __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                          const bf16_t* S0, const bf16_t* S1, const bf16_t* S2,
                                          const bf16_t* S3, const uint32_t (&la)[4],
-                                         uint32_t wbase, LoadPos& LP, const Args& A,
-                                         int stride, int nkg, int id_g, const FragOffs& fa,
-                                         const FragOffs& fb, const Ident& id, bool lenient) {
+                                         uint32_t wbase, LoadPos& LP, const Args& A, int vid,
+                                         int stride, int nkg, int id_g, int wm, int wn,
+                                         const Ident& id, bool lenient) {
+  const FragOffs<AKR> fa(wm * 128);
+  const FragOffs<BKR> fb(wn * 128);
+  // slice 0 of the tile's first stage (in S0; the previous tile's last step
+  // read it with that tile's layouts, so it is read again with this tile's)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f0.a[i] = frag<AKR>(S0, fa, i, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f0.b[i] = frag<BKR>(S0 + HALF, fb, i, 0);
   for (int kg = 0; kg < nkg; ++kg) {
 #define SM_NSG_STEP(S_, CUR, NXT, LD3, LS, IDM_)                                            \
     {                                                                                       \
@@ -409,7 +443,7 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
       /* follow it; in a tile's first step an epilogue's >= 55 stores do as well.  */       \
       if ((S_) == 0 && kg == 0 && lenient) wait_vm<63>(); else wait_vm<8>();                \
       barrier_nofence();                                                                    \
-      if ((S_) == 0) load_advance(LP, A, stride);                                           \
+      if ((S_) == 0) load_advance(LP, A, vid, stride);                                      \
     }
 #define SM_NSG_GROUP(IDM_)                      \
     SM_NSG_STEP(0, S0, S1, la[3], 3, IDM_)      \
@@ -440,10 +474,24 @@ __device__ __forceinline__ uint32_t cvt2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Stores this wave's 128 x 128 sub-tile (origin wr0, wc0) of alpha * acc, and
-// its transpose into the mirror tile when `mirror`.  Returns with every
-// store issued (and, for a tile that is not entirely inside the matrix, the
-// wave's memory operations drained, so that the next steps' waits hold).
+// 8-byte store; STREAM marks it non-temporal (for outputs too large to be
+// read back from the caches).
+template <bool STREAM>
+__device__ __forceinline__ void st8(bf16_t* p, uint2 v) {
+  if constexpr (STREAM) {
+    __builtin_nontemporal_store(v.x, reinterpret_cast<uint32_t*>(p));
+    __builtin_nontemporal_store(v.y, reinterpret_cast<uint32_t*>(p) + 1);
+  } else {
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+}
+
+// Stores this wave's 128 x 128 sub-tile (origin wr0, wc0) of alpha * acc
+// (SCALE false: alpha is 1), and its transpose into the mirror tile when
+// `mirror`.  Returns with every store issued (and, for a tile that is not
+// entirely inside the matrix, the wave's memory operations drained, so that
+// the next steps' waits hold).
+template <bool SCALE, bool STREAM>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc, int M,
                                          int N, int wr0, int wc0, float alpha, bool mirror) {
   const int lane = threadIdx.x & 63;
@@ -459,13 +507,19 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
-        const uint32_t v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
-        const uint32_t v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
+        uint32_t v0, v1;
+        if constexpr (SCALE) {
+          v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
+          v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
+        } else {
+          v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        }
         if (mirror) {   // C^T: the 4 rows are 4 consecutive elements of one row
           const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
           bf16_t* p = C + (int64_t)trow * ldc + tcol;
           if (interior) {
-            *reinterpret_cast<uint2*>(p) = make_uint2(v0, v1);
+            st8<STREAM>(p, make_uint2(v0, v1));
           } else if (trow < N) {
             const uint32_t w[2] = {v0, v1};
 #pragma unroll
@@ -486,10 +540,10 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, i
         const int col = wc0 + j * 32 + colq;
         bf16_t* p = C + (int64_t)row * ldc + col;
         if (interior) {
-          *reinterpret_cast<uint2*>(p) = out;
+          st8<STREAM>(p, out);
         } else if (row < M) {
           if (col + 4 <= N) {
-            *reinterpret_cast<uint2*>(p) = out;
+            st8<STREAM>(p, out);
           } else {
             const uint32_t w[2] = {out.x, out.y};
 #pragma unroll
@@ -518,20 +572,18 @@ void k_gemm_ns(Args args) {
   int vid = blockIdx.x;
   if (A.xcd_chunk > 0) vid = (vid & 7) * A.xcd_chunk + (vid >> 3);
   const int stride = gridDim.x;
-  int t = vid;
+  int round = 0;
+  int t = tile_of(0, vid, stride);
   if (t >= A.total_tiles) return;
 
   const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  FragOffs fa, fb;
-  frag_offsets(fa, wm * 128);
-  frag_offsets(fb, wn * 128);
 
   // LDS byte addresses of the stage buffers and of this wave's load slots
   const uint32_t la[4] = {lds_addr(S0), lds_addr(S1), lds_addr(S2), lds_addr(S3)};
   const uint32_t wbase = 4096u * (uint32_t)__builtin_amdgcn_readfirstlane(wave);
   // prologue: stages 0..2 of the first tile
   LoadPos LP;
-  load_tile_setup(LP, A, t);
+  load_tile_setup(LP, A, 0, t);
 #pragma unroll
   for (int q = 0; q < 8; ++q) dma_load(la[0], wbase, LP, 0, q);
 #pragma unroll
@@ -556,13 +608,6 @@ void k_gemm_ns(Args args) {
     Ident id;
     id.hi = g.id_hi;
     id.lo = g.id_lo;
-    // slice 0 of the tile's first stage (in S0; the previous tile's last step
-    // read it with that tile's layouts, so it is read again with this tile's)
-#define SM_NSG_F0(AKR_, BKR_)                                                 \
-    {                                                                         \
-      for (int i = 0; i < 4; ++i) f0.a[i] = frag<AKR_>(S0, fa, i, 0);         \
-      for (int i = 0; i < 4; ++i) f0.b[i] = frag<BKR_>(S0 + HALF, fb, i, 0);  \
-    }
     f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -572,44 +617,47 @@ void k_gemm_ns(Args args) {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     if constexpr (ROLE == SM_K_GEMM_GRAM) {
       if (g.combo == 0) {
-        SM_NSG_F0(0, 0)
-        run_tile<0, 0, 0, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 0, 0, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else {
-        SM_NSG_F0(1, 1)
-        run_tile<1, 1, 0, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<1, 1, 0, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
     } else if constexpr (ROLE == SM_K_GEMM_APPLY) {
       if (g.combo == 0) {
-        SM_NSG_F0(0, 1)
-        run_tile<0, 1, 1, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 1, 1, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 1) {
-        SM_NSG_F0(0, 0)
-        run_tile<0, 0, 2, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 0, 2, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 2) {
-        SM_NSG_F0(0, 1)
-        run_tile<0, 1, 1, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 1, 1, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else {
-        SM_NSG_F0(0, 0)
-        run_tile<0, 0, 2, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 0, 2, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
     } else {
       if (g.combo == 0) {
-        SM_NSG_F0(0, 0)
-        run_tile<0, 0, 2, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 0, 2, 1>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else {
-        SM_NSG_F0(0, 0)
-        run_tile<0, 0, 2, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, stride, nkg, id_g, fa, fb, id, lenient);
+        run_tile<0, 0, 2, 2>(acc, f0, f1, S0, S1, S2, S3, la, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
     }
-#undef SM_NSG_F0
     float alpha = g.alpha;
     if (g.scale) {
       const float sc = scalar_load(g.scale + tc.prob);
       for (int p = 0; p < g.alpha_pow; ++p) alpha *= sc;
     }
-    epilogue(acc, g.c + (int64_t)tc.prob * g.sc, g.ldc, g.M, g.N, wr0, wc0, alpha,
-             g.sym && tc.tm != tc.tn);
-    t += stride;
+    // Each role compiles only its own epilogues (extra instantiations cost
+    // the whole kernel registers).  Gram and A^2 products are symmetric,
+    // scaled (by b, or c) and read back by the next launch, so they stay
+    // cacheable; the applies are not symmetric, mostly unscaled (alpha is 1
+    // after the first iteration) and their outputs stream out.
+    bf16_t* C = g.c + (int64_t)tc.prob * g.sc;
+    if constexpr (ROLE == SM_K_GEMM_APPLY) {
+      if (alpha == 1.f)
+        epilogue<false, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false);
+      else
+        epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false);
+    } else {
+      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, tc.tm != tc.tn);
+    }
+    t = tile_of(++round, vid, stride);
     if (t >= A.total_tiles) break;
     lenient = true;
   }
@@ -713,6 +761,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
       if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 1 : 0;
     }
     if (combo < 0) return SM_ERR_UNSUPPORTED;
+    // the kernels compile the symmetric epilogue for Gram / r x r products
+    // only, and the plain one for applies only
+    if ((kind == SM_K_GEMM_APPLY) == (g.sym != 0)) return SM_ERR_UNSUPPORTED;
     g.combo = combo;
     g.tiles_m = (G.M + 255) / 256;
     g.tiles_n = (G.N + 255) / 256;
