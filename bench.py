@@ -12,10 +12,19 @@ measured with HIP events on the step's stream over the timed region, and the
 CPU oracle timed on a bounded sample on this host.
 
   python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu]
+  python bench.py --copy-calibration   # plain device copy of known size, for
+                                       # scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
+
+roofline.traffic is the dominant kernel's HBM bytes per launch from the
+rocprofv3 counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each
+scaled by what the counter reads for the plain copy); it is reported only
+while the kernel source still hashes to the value recorded with the
+counters, and is null otherwise.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,7 +47,67 @@ def parse():
     ap.add_argument("--gamma", type=float, default=None, help="CacheMuon threshold override")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (counter scaling)")
     return ap.parse_args()
+
+
+# Kernel source behind each GEMM kind, and the counter summary of the
+# default workload's dominant kernel.
+KERNEL_SOURCES = {"gemm_gram": "k_gemm_ns.hip", "gemm_apply": "k_gemm_ns.hip",
+                  "gemm_rr": "k_gemm_ns.hip"}
+TRAFFIC_SUMMARY = "profiles/{workload}.{kind}.hbm_traffic.md"
+
+
+def source_sha256(kind):
+    name = KERNEL_SOURCES.get(kind)
+    if not name:
+        return None
+    path = os.path.join(ROOT, "matrix_aware_optimizer_momentum_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload, kind):
+    """HBM bytes per launch recorded in the counter summary, if the kernel is unchanged."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY.format(workload=workload, kind=kind))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != source_sha256(kind):
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, timed; its rocprofv3 FETCH_SIZE
+    and WRITE_SIZE give the counters' scale (bytes moved / counter reading)."""
+    import torch
+    nbytes = 1 << 30
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    reps = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "launches": reps + 2, "ms_per_copy": ms,
+                      "copy_gbs": 2 * nbytes / (ms * 1e-3) / 1e9}))
 
 
 def _tdt(dt):
@@ -150,6 +219,9 @@ def main():
     from matrix_aware_optimizer_momentum_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     wl = W.WORKLOADS[args.config]
     mats = build_state(wl)
     cfg = step_config(wl, args.gamma)
@@ -201,7 +273,8 @@ def main():
         peak = PEAK_HBM_GBS
         unit = "GB/s"
     roofline = {"bound": "mfma" if is_mfma else "hbm", "kernel": dom, "achieved": achieved,
-                "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": None,
+                "peak": peak, "unit": unit, "frac": achieved / peak,
+                "traffic": recorded_traffic(wl.name, dom),
                 "avg_launch_ms": dk["avg_launch_ms"], "work_per_launch": dk["work_per_launch"]}
 
     ns_ms = sum(kinds.get(k, {}).get("ms_per_step", 0.0) for k in ("gemm_gram", "gemm_apply",
