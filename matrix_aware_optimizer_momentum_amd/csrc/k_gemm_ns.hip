@@ -75,6 +75,8 @@ struct Grp {
   int alpha_pow;
   float alpha;
   int tiles_m, tiles_n, tiles_per_prob, tile_begin;
+  int a_tbl, b_tbl, tbl_per;   // per-matrix operand addressing (see NsgGroup)
+  PtrTbl tbl;
 };
 
 struct Args {
@@ -178,8 +180,10 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r
   r = __builtin_amdgcn_readfirstlane(r);
   const Tile tl = decode_tile(A, t);
   const Grp& g = A.g[tl.gi];
-  L.abase = reinterpret_cast<const char*>(g.a + (int64_t)tl.prob * g.sa);
-  L.bbase = reinterpret_cast<const char*>(g.b + (int64_t)tl.prob * g.sb);
+  L.abase = g.a_tbl ? tbl_addr(g.tbl, tl.prob, g.tbl_per, 2 * g.sa)
+                    : reinterpret_cast<const char*>(g.a + (int64_t)tl.prob * g.sa);
+  L.bbase = g.b_tbl ? tbl_addr(g.tbl, tl.prob, g.tbl_per, 2 * g.sb)
+                    : reinterpret_cast<const char*>(g.b + (int64_t)tl.prob * g.sb);
   dma_offsets(L.aoff, g.a_kr, g.lda, tl.tm * 256, g.M);
   dma_offsets(L.boff, g.b_kr, g.ldb, tl.tn * 256, g.N);
   L.akst = g.a_kr ? (uint32_t)(2 * g.lda) : 2u;
@@ -686,7 +690,15 @@ int cu_count() {
 
 bool gemm_ns_supported(const NsgGroup& G) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (!al(G.a) || !al(G.b) || !al(G.c)) return false;
+  if ((G.a_tbl || G.b_tbl) && (!G.tbl || G.tbl_per < 1 || G.batch > G.tbl_per * kTbl))
+    return false;
+  auto al_op = [&](const bf16_t* p, int use_tbl) {
+    if (!use_tbl) return p != nullptr && al(p);
+    for (int q = 0; q < (G.batch + G.tbl_per - 1) / G.tbl_per; ++q)
+      if (!G.tbl->p[q] || !al(G.tbl->p[q])) return false;
+    return true;
+  };
+  if (!al_op(G.a, G.a_tbl) || !al_op(G.b, G.b_tbl) || !al(G.c)) return false;
   if (G.lda % 8 || G.ldb % 8 || G.sa % 8 || G.sb % 8 || G.ldc % 4 || G.sc % 4) return false;
   if (G.M < 8 || G.N < 8 || G.K <= 0 || G.K % (4 * nsg::BK)) return false;
   if (G.a_kr && G.M % 8) return false;
@@ -695,7 +707,8 @@ bool gemm_ns_supported(const NsgGroup& G) {
   const int64_t ea = G.a_kr ? (int64_t)G.K * G.lda : (int64_t)G.M * G.lda;
   const int64_t eb = G.b_kr ? (int64_t)G.K * G.ldb : (int64_t)G.N * G.ldb;
   if (2 * ea >= ((int64_t)1 << 32) || 2 * eb >= ((int64_t)1 << 32)) return false;
-  if (G.sym && (G.M != G.N || G.a != G.b || G.a_kr != G.b_kr)) return false;
+  if (G.sym && (G.M != G.N || G.a != G.b || G.a_kr != G.b_kr || G.a_tbl != G.b_tbl))
+    return false;
   if (G.ident && G.ident_terms != 1 && G.ident_terms != 2) return false;
   if (G.ident == 1 && G.K != G.M) return false;
   if (G.ident == 2 && G.K != G.N) return false;
@@ -748,6 +761,10 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.id_lo = G.ident_terms == 2 ? G.ident_lo : 0u;
     g.alpha_pow = G.alpha_pow;
     g.alpha = G.alpha;
+    g.a_tbl = G.a_tbl ? 1 : 0;
+    g.b_tbl = G.b_tbl ? 1 : 0;
+    g.tbl_per = G.tbl_per;
+    if (G.a_tbl || G.b_tbl) g.tbl = *G.tbl;
     // the instantiation for this group's layouts and identity mode
     int combo = -1;
     const bool two = G.ident && G.ident_terms == 2;

@@ -157,13 +157,17 @@ void carve_ns(Carver& cv, int dt, int batch, int m, int n, NsWs& w) {
   w.amat2 = cv.take<void>((size_t)batch * r * r * es);
 }
 
-// One batch of same-shaped direct-NS problems: x[batch][m][n] -> out.
+// One batch of same-shaped direct-NS problems: x[batch][m][n] -> out.  With
+// xtbl set, x is null and problem p is read from worker p % xper of matrix
+// p / xper (the momentum tensors themselves, no contiguous copy).
 struct NsJob {
   const void* x;
   void* out;
   NsWs w;
   const float* scale;
   int batch, m, n;
+  const PtrTbl* xtbl = nullptr;
+  int xper = 1;
 };
 
 // The grouped-kernel descriptors of one NS iteration of job j:
@@ -186,9 +190,11 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, const sm_ns
   auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
   auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
   std::memset(&d, 0, sizeof(d));
+  const int tb = (cur == nullptr && j.xtbl) ? 1 : 0;   // cur is the tabled input
   NsgGroup& g = d.gram;
   g.a = bp(cur); g.lda = n; g.sa = mn; g.a_kr = wide ? 0 : 1;
   g.b = bp(cur); g.ldb = n; g.sb = mn; g.b_kr = wide ? 0 : 1;
+  g.tbl = j.xtbl; g.tbl_per = j.xper; g.a_tbl = tb; g.b_tbl = tb;
   g.c = mp(j.w.amat); g.ldc = r; g.sc = rr;
   g.scale = j.scale; g.alpha_pow = first && j.scale ? 2 : 0;
   g.alpha = (p.c == 0.f) ? p.b : 1.f;
@@ -208,12 +214,13 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, const sm_ns
     bmat = j.w.amat2;
   }
   NsgGroup& a = d.apply;
+  a.tbl = j.xtbl; a.tbl_per = j.xper;
   if (wide) {
     a.a = bp(bmat); a.lda = r; a.sa = rr;
-    a.b = bp(cur); a.ldb = n; a.sb = mn; a.b_kr = 1;
+    a.b = bp(cur); a.ldb = n; a.sb = mn; a.b_kr = 1; a.b_tbl = tb;
     a.ident = 1;
   } else {
-    a.a = bp(cur); a.lda = n; a.sa = mn;
+    a.a = bp(cur); a.lda = n; a.sa = mn; a.a_tbl = tb;
     a.b = bp(bmat); a.ldb = r; a.sb = rr;
     a.ident = 2;
   }
@@ -758,6 +765,8 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     PtrTbl mom, grad, wt, qt, cs;
     int nc, B;
     int64_t count, words;
+    NsJob job;      // direct NS of this chunk
+    bool grouped;   // job runs in the grouped launches
   };
   std::vector<ChunkRun> runs(chunks.size());
   Carver cv(ws);
@@ -782,6 +791,25 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
       r.qt.p[j] = reinterpret_cast<const char*>(a.q_cache);
       r.cs.p[j] = reinterpret_cast<const char*>(a.cache_state);
     }
+    // Direct NS input: Sign-Muon's is the momentum itself (Y = M), read in
+    // place through the pointer table when the grouped kernel takes it, so
+    // a1 writes no copy; LionMuon's is the interpolation Ghat, which only
+    // exists as the copy a1 writes.
+    r.grouped = false;
+    if (muon_step && c->algo != SM_CACHE_MUON) {
+      r.job = NsJob{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.B, ch.m, ch.n};
+      if (c->algo == SM_SIGN_MUON) {
+        NsJob tj = r.job;
+        tj.x = nullptr;
+        tj.xtbl = &r.mom;
+        tj.xper = M;
+        if (ns_grouped_ok(tj, c->mdt, c->ns)) {
+          r.job = tj;
+          r.grouped = true;
+        }
+      }
+      if (!r.grouped) r.grouped = ns_grouped_ok(r.job, c->mdt, c->ns);
+    }
   }
   // a1 (+ a2 partials): momentum, and the NS input or the Lion signs
   for (size_t ci = 0; ci < chunks.size(); ++ci) {
@@ -794,7 +822,8 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
         SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
                            nullptr, c->mdt, nullptr, r.w.bits, r.words, s));
     } else {
-      SM_TRY(launch_ema_single(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, r.w.x0,
+      void* x0 = (r.grouped && r.job.xtbl) ? nullptr : r.w.x0;   // no copy when NS reads M
+      SM_TRY(launch_ema_single(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, x0,
                                c->mdt, r.w.partials, s));
     }
     if (muon_step) SM_TRY(launch_scale_finalize(r.w.partials, r.B, c->ns.eps, r.w.scale, s));
@@ -821,9 +850,8 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
                          s));
         continue;
       }
-      const NsJob job{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.B, ch.m, ch.n};
-      if (ns_grouped_ok(job, c->mdt, c->ns))
-        grouped.push_back(job);
+      if (r.grouped)
+        grouped.push_back(r.job);
       else
         SM_TRY(ns_core(r.w.x0, r.w.d, r.w.ns, r.w.scale, c->mdt, r.B, ch.m, ch.n, c->ns, s));
     }

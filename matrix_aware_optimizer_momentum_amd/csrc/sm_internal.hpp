@@ -222,6 +222,10 @@ constexpr int kNsgMaxGroups = 4;
 struct NsgGroup {
   const bf16_t* a; int64_t lda, sa; int a_kr;
   const bf16_t* b; int64_t ldb, sb; int b_kr;
+  // Optional per-matrix addressing of the operands flagged a_tbl / b_tbl
+  // (then a / b are unused): problem p is worker p % tbl_per of matrix
+  // p / tbl_per, at tbl->p[p / tbl_per] + (p % tbl_per) * s{a,b} elements.
+  const PtrTbl* tbl; int tbl_per; int a_tbl, b_tbl;
   bf16_t* c; int64_t ldc, sc;
   const float* scale; int alpha_pow; float alpha;
   int M, N, K, batch;
