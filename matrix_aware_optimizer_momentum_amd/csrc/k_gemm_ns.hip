@@ -76,6 +76,8 @@ struct Grp {
   float alpha;
   int tiles_m, tiles_n, tiles_per_prob, tile_begin;
   int a_tbl, b_tbl, tbl_per;   // per-matrix operand addressing (see NsgGroup)
+  uint64_t* bits;              // apply: signs instead of C (see NsgGroup)
+  int64_t bits_stride;
   PtrTbl tbl;
 };
 
@@ -220,7 +222,11 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
   const uint32_t sm0 = (uint32_t)__builtin_amdgcn_readfirstlane(m0);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  // The hazard recognizer does not look inside inline asm, so the asm keeps
+  // its own wait states: 5 between a VALU write of an SGPR (the readfirstlane
+  // of the base, which the compiler may place just before) and a memory
+  // instruction reading it, and 1 between writing M0 and the LDS DMA.
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sb), "s"(sm0)
                : "memory", "m0");
@@ -559,6 +565,78 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, i
   if (!interior) wait_vm<0>();
 }
 
+// The writelane intrinsic, which this compiler exposes under no builtin
+// name.  Going through the intrinsic (not inline asm) keeps the instruction
+// visible to the hazard recognizer: v_writelane reads its value from an SGPR
+// that the ballot's compare has just written, and needs wait states after it.
+extern "C" __device__ int sm_llvm_writelane(int val, int lane, int old)
+    __asm("llvm.amdgcn.writelane.i32");
+
+// v[lane] = val (val wave-uniform, lane a constant): v_writelane_b32.
+template <int LANE>
+__device__ __forceinline__ uint32_t writelane(uint32_t v, uint32_t val) {
+  return (uint32_t)sm_llvm_writelane((int)val, LANE, (int)v);
+}
+
+// Writes the signs of this wave's 128 x 128 sub-tile of alpha * acc as packed
+// bits (the sign of each value rounded to bf16 exactly as epilogue() rounds
+// it, so the bits equal the sign packing of the stored direction): bit = 1
+// <=> negative, 64 consecutive columns of a row per 64-bit word (N % 64 ==
+// 0, wpr = N / 64 words per row).  A ballot over one accumulator register
+// gives 32 columns of two rows (lanes 0-31: row r, 32-63: row r + 4); two
+// column blocks make one word per row, placed with writelane into the lane
+// that stores it (lane L: row L % 32 of the block, word L / 32).  Issues 4
+// stores, then drains this wave's memory operations (fewer stores than the
+// lenient wait after a plain epilogue assumes).
+template <bool SCALE>
+__device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_t* bits,
+                                              int64_t wpr, int M, int N, int wr0, int wc0,
+                                              float alpha) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t wlo = 0u, whi = 0u;   // this lane's word
+    // p: word (columns 64p..64p+63 of the sub-tile); q, e: accumulator
+    // register q*4 + e of blocks (i, 2p) and (i, 2p + 1)
+#define SM_BITS_QE(P, Q, E)                                                                \
+    {                                                                                      \
+      float a0 = acc[i][2 * (P)][(Q) * 4 + (E)], a1 = acc[i][2 * (P)][(Q) * 4 + (E) + 1];  \
+      float b0 = acc[i][2 * (P) + 1][(Q) * 4 + (E)];                                       \
+      float b1 = acc[i][2 * (P) + 1][(Q) * 4 + (E) + 1];                                   \
+      if constexpr (SCALE) {                                                               \
+        a0 *= alpha; a1 *= alpha; b0 *= alpha; b1 *= alpha;                                \
+      }                                                                                    \
+      const uint32_t ha = cvt2(a0, a1), hb = cvt2(b0, b1);                                 \
+      SM_BITS_H(P, Q, E, 0, ha << 16, hb << 16)                                            \
+      SM_BITS_H(P, Q, E, 1, ha & 0xFFFF0000u, hb & 0xFFFF0000u)                            \
+    }
+    /* register e + h: rows q*8 + e + h (lanes 0-31) and q*8 + 4 + e + h (lanes 32-63) */
+#define SM_BITS_H(P, Q, E, H, XA, XB)                                                      \
+    {                                                                                      \
+      const uint64_t ma = __builtin_amdgcn_ballot_w64(__uint_as_float(XA) < 0.f);          \
+      const uint64_t mb = __builtin_amdgcn_ballot_w64(__uint_as_float(XB) < 0.f);          \
+      constexpr int L0 = (P) * 32 + (Q) * 8 + (E) + (H);                                   \
+      wlo = writelane<L0>(wlo, (uint32_t)ma);                                              \
+      whi = writelane<L0>(whi, (uint32_t)mb);                                              \
+      wlo = writelane<L0 + 4>(wlo, (uint32_t)(ma >> 32));                                  \
+      whi = writelane<L0 + 4>(whi, (uint32_t)(mb >> 32));                                  \
+    }
+#define SM_BITS_Q(P, Q) SM_BITS_QE(P, Q, 0) SM_BITS_QE(P, Q, 2)
+#define SM_BITS_P(P) SM_BITS_Q(P, 0) SM_BITS_Q(P, 1) SM_BITS_Q(P, 2) SM_BITS_Q(P, 3)
+    SM_BITS_P(0)
+    SM_BITS_P(1)
+#undef SM_BITS_P
+#undef SM_BITS_Q
+#undef SM_BITS_H
+#undef SM_BITS_QE
+    const int row = wr0 + i * 32 + (lane & 31);
+    const int col = wc0 + 64 * (lane >> 5);
+    if (row < M && col < N)
+      *reinterpret_cast<uint2*>(bits + (int64_t)row * wpr + (col >> 6)) = make_uint2(wlo, whi);
+  }
+  wait_vm<0>();
+}
+
 // ---------------------------------------------------------------- kernel
 // Combos per role (index = Grp::combo): operand layouts and identity mode.
 //   GRAM:  0 (KC, KC)        1 (KR, KR)
@@ -654,16 +732,25 @@ void k_gemm_ns(Args args) {
     // after the first iteration) and their outputs stream out.
     bf16_t* C = g.c + (int64_t)tc.prob * g.sc;
     if constexpr (ROLE == SM_K_GEMM_APPLY) {
-      if (alpha == 1.f)
+      if (g.bits) {   // the last iteration of a vote-mode step: signs only
+        uint64_t* bp = g.bits + (int64_t)tc.prob * g.bits_stride;
+        if (alpha == 1.f)
+          epilogue_bits<false>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+        else
+          epilogue_bits<true>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+      } else if (alpha == 1.f) {
         epilogue<false, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false);
-      else
+      } else {
         epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false);
+      }
     } else {
       epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, tc.tm != tc.tn);
     }
     t = tile_of(++round, vid, stride);
     if (t >= A.total_tiles) break;
-    lenient = true;
+    // the next tile's first wait relies on a plain epilogue's >= 55 stores
+    // (a bits epilogue drains instead)
+    lenient = g.bits == nullptr;
   }
   wait_vm<0>();   // the loads past the last stage target this workgroup's LDS
 }
@@ -710,6 +797,9 @@ bool gemm_ns_supported(const NsgGroup& G) {
   if (G.sym && (G.M != G.N || G.a != G.b || G.a_kr != G.b_kr || G.a_tbl != G.b_tbl))
     return false;
   if (G.ident && G.ident_terms != 1 && G.ident_terms != 2) return false;
+  if (G.bits && (G.sym || G.N % 64 != 0 || (reinterpret_cast<uintptr_t>(G.bits) & 7u) ||
+                 G.bits_stride < (int64_t)G.M * (G.N / 64)))
+    return false;
   if (G.ident == 1 && G.K != G.M) return false;
   if (G.ident == 2 && G.K != G.N) return false;
   return true;
@@ -761,6 +851,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.id_lo = G.ident_terms == 2 ? G.ident_lo : 0u;
     g.alpha_pow = G.alpha_pow;
     g.alpha = G.alpha;
+    g.bits = G.bits;
+    g.bits_stride = G.bits_stride;
+    if (G.bits && kind != SM_K_GEMM_APPLY) return SM_ERR_UNSUPPORTED;
     g.a_tbl = G.a_tbl ? 1 : 0;
     g.b_tbl = G.b_tbl ? 1 : 0;
     g.tbl_per = G.tbl_per;

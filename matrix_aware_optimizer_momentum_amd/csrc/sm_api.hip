@@ -168,6 +168,11 @@ struct NsJob {
   int batch, m, n;
   const PtrTbl* xtbl = nullptr;
   int xper = 1;
+  // Vote mode: the last iteration writes the packed signs of X_K here
+  // ([batch][bits_stride] words, the layout of launch_sign_pack) instead of
+  // out (needs n % 64 == 0).
+  uint64_t* bits = nullptr;
+  int64_t bits_stride = 0;
 };
 
 // The grouped-kernel descriptors of one NS iteration of job j:
@@ -182,8 +187,8 @@ struct NsDesc {
   NsgGroup gram, rr, apply;
 };
 
-bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, const sm_ns_params& p,
-             NsDesc& d) {
+bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, bool last,
+             const sm_ns_params& p, NsDesc& d) {
   const bool wide = j.m <= j.n;
   const int m = j.m, n = j.n, r = wide ? m : n;
   const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
@@ -228,6 +233,10 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, const sm_ns
   a.scale = j.scale; a.alpha_pow = first && j.scale ? 1 : 0; a.alpha = 1.f;
   a.M = m; a.N = n; a.K = r; a.batch = j.batch;
   a.ident_terms = ns_ident_split(p.a, &a.ident_hi, &a.ident_lo);
+  if (last && j.bits) {
+    a.bits = j.bits;
+    a.bits_stride = j.bits_stride;
+  }
   return a.ident_terms != 0 && gemm_ns_supported(a);
 }
 
@@ -256,7 +265,7 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
       const NsJob& j = jobs[i];
       const void* cur = k == 0 ? j.x : (((K - k) % 2 == 0) ? j.out : j.w.tmp);
       void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
-      if (!ns_desc(j, cur, dst, k == 0, p, d[i])) return SM_ERR_UNSUPPORTED;
+      if (!ns_desc(j, cur, dst, k == 0, k == K - 1, p, d[i])) return SM_ERR_UNSUPPORTED;
       gram.push_back(d[i].gram);
       if (p.c != 0.f) rr.push_back(d[i].rr);
       apply.push_back(d[i].apply);
@@ -273,7 +282,8 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
 bool ns_grouped_ok(const NsJob& j, int dt, const sm_ns_params& p) {
   if (dt != BF16) return false;
   NsDesc d;
-  return ns_desc(j, j.x, j.out, true, p, d) && ns_desc(j, j.out, j.w.tmp, false, p, d);
+  return ns_desc(j, j.x, j.out, true, p.iters == 1, p, d) &&
+         ns_desc(j, j.out, j.w.tmp, false, true, p, d);
 }
 
 // Products of one direct NS step on problems of shape m x n (x contiguous):
@@ -765,8 +775,9 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     PtrTbl mom, grad, wt, qt, cs;
     int nc, B;
     int64_t count, words;
-    NsJob job;      // direct NS of this chunk
-    bool grouped;   // job runs in the grouped launches
+    NsJob job;          // direct NS of this chunk
+    bool grouped;       // job runs in the grouped launches
+    bool fused_signs;   // its last product writes the packed signs (no a7/a8 launch)
   };
   std::vector<ChunkRun> runs(chunks.size());
   Carver cv(ws);
@@ -796,6 +807,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     // a1 writes no copy; LionMuon's is the interpolation Ghat, which only
     // exists as the copy a1 writes.
     r.grouped = false;
+    r.fused_signs = false;
     if (muon_step && c->algo != SM_CACHE_MUON) {
       r.job = NsJob{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.B, ch.m, ch.n};
       if (c->algo == SM_SIGN_MUON) {
@@ -809,6 +821,18 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
         }
       }
       if (!r.grouped) r.grouped = ns_grouped_ok(r.job, c->mdt, c->ns);
+      // a7 + a8 fused into the last NS product when the signs are all the
+      // step needs from the direction
+      r.fused_signs = false;
+      if (r.grouped && !polar) {
+        NsJob bj = r.job;
+        bj.bits = r.w.bits;
+        bj.bits_stride = r.words;
+        if (ns_grouped_ok(bj, c->mdt, c->ns)) {
+          r.job = bj;
+          r.fused_signs = true;
+        }
+      }
     }
   }
   // a1 (+ a2 partials): momentum, and the NS input or the Lion signs
@@ -863,7 +887,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     if (muon_step) {
       if (polar)
         SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));
-      else
+      else if (!r.fused_signs)
         SM_TRY(launch_sign_pack(r.w.d, c->mdt, r.B, r.count, r.w.bits, r.words, s));
     }
     if (!polar)

@@ -232,6 +232,10 @@ struct NsgGroup {
   int sym;
   int ident, ident_terms;
   uint32_t ident_hi, ident_lo;
+  // Apply only: instead of C, write the 1-bit signs of its bf16 values
+  // (bit = 1 <=> negative, bit j of word w <=> row-major entry 64 w + j) to
+  // bits + problem * bits_stride words; needs N % 64 == 0.
+  uint64_t* bits; int64_t bits_stride;
 };
 
 bool gemm_ns_supported(const NsgGroup& g);
