@@ -34,6 +34,10 @@ Readings taken where the pages are silent (each is repeated at its function):
   * 1-bit layout: uint64 words, bit (i mod 64) of word i//64 is 1 iff entry i
     (row-major, original orientation) is negative; tail bits are 0.
   * Update: W <- rnd_W(fp32(W) - fp32(lr) * V) with one float32 rounding.
+  * int8 encoding (the integer SUM all-reduce variant): one signed byte per
+    entry, s in {-1, +1}; the vote sums them as integers, ties give 0.
+  * Optional polar step on the vote: D = NS(V / (||V||_F + eps)) with the
+    workers' Newton-Schulz settings, then W <- rnd_W(fp32(W) - fp32(lr * D)).
 """
 from __future__ import annotations
 
@@ -428,6 +432,51 @@ def update_polar(w_values, d_values, lr: float, wdtype: str) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# The int8 encoding, and the optional local polar step on the vote
+# --------------------------------------------------------------------------
+
+ENC_BITS = 0
+ENC_INT8 = 1
+
+
+def sign_int8(x) -> np.ndarray:
+    """a7 in the int8 encoding: one signed byte per entry, s in {-1, +1}.
+
+    [SignMuon-ja] section 2, algorithm flow step 3 (the integer SUM all-reduce
+    variant) and "communication efficiency": instead of one packed bit, each
+    entry's sign travels as an int8 (8 bits per entry, 4x fewer bytes than
+    float32).  Same sign convention as the bit path: -1 iff x < 0.
+    """
+    return sign_values(np.asarray(x).reshape(-1))
+
+
+def vote_from_int8(signs_per_worker: Sequence[np.ndarray], count: int) -> np.ndarray:
+    """Majority vote from int8 signs: the integer sum over workers (what the
+    SUM all-reduce hands every worker), then sign() with 0 on ties.
+
+    [SignMuon-ja] section 2, core mechanism item 3 and algorithm flow step 4.
+    """
+    total = np.zeros(count, dtype=np.int64)
+    for sv in signs_per_worker:
+        total += np.asarray(sv, dtype=np.int64).reshape(-1)[:count]
+    return np.sign(total).astype(np.int8)
+
+
+def vote_polar_direction(v, p: NSParams) -> np.ndarray:
+    """Optional local polar step on the aggregated sign matrix V (m x n).
+
+    [SignMuon-ja] section 2, algorithm flow step 5, and [SignMuon-abs]: after
+    the vote a worker may take a local polar step on the voted sign matrix,
+    pushing the update toward orthogonality at no extra communication.
+    Reading (the pages give no formula): the polar factor is approximated by
+    the same Newton-Schulz iteration, coefficients and Frobenius
+    normalisation as the workers' own directions, D = NS(V / (||V||_F + eps)),
+    and the update is the dense one, W <- W - eta * D.  V = 0 gives D = 0.
+    """
+    return ns_polar(np.asarray(v, dtype=np.float64), p, normalize=True)
+
+
+# --------------------------------------------------------------------------
 # Whole steps (trajectory references)
 # --------------------------------------------------------------------------
 
@@ -452,6 +501,8 @@ class StepConfig:
     ns: NSParams = field(default_factory=NSParams)
     gamma: float = 0.0
     cache_mode: int = MODE_TRIGGER
+    encoding: int = ENC_BITS   # how the signs travel: packed bits or int8
+    vote_polar: bool = False   # W <- W - lr * NS(V) instead of W - lr * V
 
 
 @dataclass
@@ -469,7 +520,9 @@ def step_matrix(st: MatrixState, grads: Sequence[np.ndarray], cfg: StepConfig, t
     """One optimizer step of one weight matrix with cfg.workers workers.
 
     Returns a dict with the per-worker directions ('d'), packed bits ('bits'),
-    the vote ('vote') and CacheMuon diagnostics; `st` is updated in place.
+    int8 signs ('signs8'), the vote ('vote'), the polar direction of the vote
+    ('vote_d', with vote_polar) and CacheMuon diagnostics; `st` is updated in
+    place.
     Momentum and directions are rounded to their storage dtype between
     stages, the way a stored tensor is.
     """
@@ -477,7 +530,8 @@ def step_matrix(st: MatrixState, grads: Sequence[np.ndarray], cfg: StepConfig, t
     assert len(grads) == mw and len(st.mom) == mw
     m, n = st.w.shape
     count = m * n
-    out = {"d": [None] * mw, "bits": [None] * mw, "err": [], "refreshed": []}
+    out = {"d": [None] * mw, "bits": [None] * mw, "signs8": [None] * mw, "err": [],
+           "refreshed": [], "vote_d": None}
     if cfg.algo == CACHE_MUON and not st.cache:
         st.cache = [CacheState() for _ in range(mw)]
 
@@ -494,7 +548,9 @@ def step_matrix(st: MatrixState, grads: Sequence[np.ndarray], cfg: StepConfig, t
             if not muon_step:
                 # Lion step: sign of the interpolation, decided in float32.
                 out["d"][k] = y
-                out["bits"][k] = pack_bits(lion_sign_negative(m_prev, g, cfg.beta1).reshape(-1))
+                neg = lion_sign_negative(m_prev, g, cfg.beta1).reshape(-1)
+                out["bits"][k] = pack_bits(neg)
+                out["signs8"][k] = np.where(neg, -1, 1).astype(np.int8)
                 continue
             y = round_storage(y, cfg.mdtype)
         else:
@@ -510,13 +566,22 @@ def step_matrix(st: MatrixState, grads: Sequence[np.ndarray], cfg: StepConfig, t
         d = _direction_storage(d, cfg)
         out["d"][k] = d
         out["bits"][k] = sign_pack(d)
+        out["signs8"][k] = sign_int8(d)
 
     if cfg.update == UPDATE_POLAR and muon_step:
         assert mw == 1
         st.w = update_polar(st.w, out["d"][0], cfg.lr, cfg.wdtype)
         out["vote"] = None
+        return out
+    if cfg.encoding == ENC_INT8:
+        v = vote_from_int8(out["signs8"], count).reshape(m, n)
     else:
         v = vote_from_bits(out["bits"], count).reshape(m, n)
-        out["vote"] = v
+    out["vote"] = v
+    if cfg.vote_polar:
+        dv = round_storage(vote_polar_direction(v, cfg.ns), cfg.mdtype)
+        out["vote_d"] = dv
+        st.w = update_polar(st.w, dv, cfg.lr, cfg.wdtype)
+    else:
         st.w = update_vote(st.w, v, cfg.lr, cfg.wdtype)
     return out

@@ -533,3 +533,115 @@ def test_update_polar_matches_torch_float32_and_bf16():
     want_b = (wbf - tl * torch.from_numpy(d32)).to(torch.bfloat16).view(torch.int16).numpy()
     got_b = O.update_polar(wbf.numpy(), d32, lr, O.BF16).astype(np.float32)
     np.testing.assert_array_equal(O.bf16_bits_from_f32(got_b), want_b.view(np.uint16))
+
+
+# ---------------------------------------------------------------- P-16 int8 encoding
+
+def test_p16_sign_int8_special_values_and_payload():
+    x = np.array([0.0, -0.0, np.nan, -1e-30, 1e-30, -np.inf, np.inf, -2.5, 3.0], np.float32)
+    want = np.array([1, 1, 1, -1, 1, -1, 1, -1, 1], np.int8)   # -1 iff x < 0
+    s = O.sign_int8(x)
+    assert s.dtype == np.int8
+    np.testing.assert_array_equal(s, want)
+    # one byte per entry: the int8 payload of the pages' 4x ratio
+    with open(os.path.join(GOLDEN, "payload_ratios.json")) as f:
+        gold = json.load(f)
+    n = 768 * 2304
+    assert (n * 4) // O.sign_int8(np.ones(n, np.float32)).nbytes == gold["int8_vs_float32"]
+
+
+@pytest.mark.parametrize("mw", [1, 2, 3, 4, 5, 16])
+def test_p16_int8_vote_brute_force_and_equals_bit_vote(mw):
+    rng = np.random.default_rng(100 + mw)
+    n = 300
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(mw)]
+    xs[0][:5] = [0.0, -0.0, np.nan, -1e-30, 1e-30]
+    v8 = O.vote_from_int8([O.sign_int8(x) for x in xs], n)
+    for i in range(n):
+        total = sum(-1 if xs[k][i] < 0 else 1 for k in range(mw))
+        assert v8[i] == (0 if total == 0 else (1 if total > 0 else -1))
+    # M - 2 n_neg (the bit path's popcount form) equals the plain integer sum
+    np.testing.assert_array_equal(v8, O.vote_from_bits([O.sign_pack(x) for x in xs], n))
+
+
+def test_p16_int8_vote_ties_for_even_workers():
+    s = [np.array([1, 1, -1, -1, 1], np.int8), np.array([-1, 1, 1, -1, 1], np.int8)]
+    np.testing.assert_array_equal(O.vote_from_int8(s, 5), [0, 1, 0, -1, 1])
+
+
+# ---------------------------------------------------------------- P-17 polar step on the vote
+
+def _hadamard(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def _scalar_ns(sigma, p):
+    for _ in range(p.iters):
+        sigma = p.a * sigma + p.b * sigma ** 3 + p.c * sigma ** 5
+    return sigma
+
+
+@pytest.mark.parametrize("coef", [(1.5, -0.5, 0.0), (3.4445, -4.775, 2.0315)])
+@pytest.mark.parametrize("n,reps,tall", [(4, 1, False), (8, 1, False), (8, 2, False),
+                                         (8, 3, True), (16, 1, False)])
+def test_p17_vote_polar_on_hadamard_votes_closed_form(coef, n, reps, tall):
+    """V made of Hadamard blocks has all singular values equal, so NS acts as
+    one scalar map: D = phi^K(sigma0) V / s with s = sqrt(n reps), the common
+    singular value, and sigma0 = s / (||V||_F + eps)."""
+    p = O.NSParams(5, *coef, eps=1e-7)
+    v = np.hstack([_hadamard(n)] * reps)
+    if tall:
+        v = v.T
+    s = math.sqrt(n * reps)
+    sigma0 = s / (math.sqrt(v.size) + p.eps)
+    want = _scalar_ns(sigma0, p) * v / s
+    d = O.vote_polar_direction(v.astype(np.int8), p)
+    assert d.shape == v.shape
+    np.testing.assert_allclose(d, want, rtol=1e-12, atol=1e-14)
+
+
+def test_p17_vote_polar_rank_one_and_zero_votes():
+    p = O.NSParams()
+    rng = np.random.default_rng(7)
+    u = rng.choice([-1, 1], size=12)
+    w = rng.choice([-1, 1], size=20)
+    v = np.outer(u, w)
+    s = math.sqrt(v.size)                 # the one nonzero singular value
+    sigma0 = s / (s + p.eps)
+    np.testing.assert_allclose(O.vote_polar_direction(v, p), _scalar_ns(sigma0, p) * v / s,
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(O.vote_polar_direction(np.zeros((6, 9), np.int8), p),
+                                  np.zeros((6, 9)))
+
+
+def test_p17_step_with_unanimous_hadamard_vote():
+    """Whole step: every worker's momentum is a positive multiple of a
+    Hadamard matrix H, so every sign matrix, and the vote, is H; with the
+    polar step the update is W - lr * rnd(phi^K(sigma0) H / sqrt(n)); with
+    either encoding the plain vote update is W - lr * H."""
+    n, mw = 8, 3
+    h = _hadamard(n)
+    w0 = (0.02 * np.random.default_rng(3).standard_normal((n, n))).astype(np.float32)
+    grads = [(k + 1.0) * h for k in range(mw)]
+    p = O.NSParams()
+    base = dict(algo=O.SIGN_MUON, workers=mw, wdtype=O.F32, mdtype=O.F32, lr=1e-3, beta1=0.9,
+                ns=p)
+    # momentum after one step from zero: 0.1 (k+1) H, ||.||_F = 0.1 (k+1) n
+    results = {}
+    for enc in (O.ENC_BITS, O.ENC_INT8):
+        for vp in (False, True):
+            st = O.MatrixState(w=w0.astype(np.float64), mom=[np.zeros((n, n))] * mw)
+            out = O.step_matrix(st, grads, O.StepConfig(encoding=enc, vote_polar=vp, **base), 1)
+            np.testing.assert_array_equal(out["vote"], h.astype(np.int8))
+            results[(enc, vp)] = st.w
+    np.testing.assert_array_equal(results[(O.ENC_BITS, False)],
+                                  O.update_vote(w0, h, 1e-3, O.F32))
+    sigma0 = math.sqrt(n) / (n + p.eps)
+    d = (_scalar_ns(sigma0, p) * h / math.sqrt(n)).astype(np.float32)
+    want = (w0 - (np.float32(1e-3) * d).astype(np.float32)).astype(np.float32)
+    np.testing.assert_array_equal(results[(O.ENC_BITS, True)].astype(np.float32), want)
+    for vp in (False, True):
+        np.testing.assert_array_equal(results[(O.ENC_INT8, vp)], results[(O.ENC_BITS, vp)])
