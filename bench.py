@@ -9,7 +9,10 @@ matrices.  Inputs are synthetic and resident in HBM before timing starts.
 
 Prints one JSON line: steps/s (value), the roofline of the dominant kernel
 measured with HIP events on the step's stream over the timed region, and the
-CPU oracle timed on a bounded sample on this host.
+CPU oracle timed on a bounded sample on this host.  After the main timed
+region, `variants` times the same step with the int8 sign encoding and with
+the optional polar step on the vote (--variant-steps each, default 10; the
+main `value` is always the 1-bit vote step).
 
   python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu]
   python bench.py --copy-calibration   # plain device copy of known size, for
@@ -49,7 +52,101 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter scaling)")
+    ap.add_argument("--variant-steps", type=int, default=10,
+                    help="timed steps of each step variant (int8 encoding, polar step on the "
+                         "vote); 0 skips them")
     return ap.parse_args()
+
+
+KINDS = ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pack",
+         "vote_update", "lion", "polar_update", "misc"]
+
+
+def read_kinds(sm, steps):
+    """Per-kind kernel time and algorithmic work from the library's HIP events."""
+    kinds = {}
+    for kind in KINDS:
+        ms, n, work = sm.profile_read(kind)
+        if n:
+            kinds[kind] = {"ms_per_step": ms / steps, "launches_per_step": n / steps,
+                           "avg_launch_ms": ms / n, "work_per_launch": work / n,
+                           "flops" if kind.startswith(("gemm", "probe")) else "bytes":
+                               work / steps}
+    return kinds
+
+
+def timed_steps(sm, torch, call, t, warmup, steps):
+    """warmup untimed steps, then `steps` timed ones with kernel accounting on."""
+    for _ in range(warmup):
+        call(t)
+        t += 1
+    torch.cuda.synchronize()
+    sm.profile_enable(True)
+    sm.profile_reset()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call(t)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sm.profile_enable(False)
+    return t, wall, read_kinds(sm, steps)
+
+
+def stream_roofline(kinds, names):
+    """HBM roofline of the slowest of the named streaming kernels."""
+    have = [k for k in names if k in kinds]
+    if not have:
+        return None
+    dom = max(have, key=lambda k: kinds[k]["ms_per_step"])
+    dk = kinds[dom]
+    achieved = dk["work_per_launch"] / (dk["avg_launch_ms"] * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+            "avg_launch_ms": dk["avg_launch_ms"], "work_per_launch": dk["work_per_launch"]}
+
+
+def gemm_totals(kinds):
+    ms = sum(kinds.get(k, {}).get("ms_per_step", 0.0) for k in ("gemm_gram", "gemm_apply",
+                                                               "gemm_rr"))
+    fl = sum(kinds.get(k, {}).get("flops", 0.0) for k in ("gemm_gram", "gemm_apply", "gemm_rr"))
+    return ms, fl
+
+
+def measure_variants(sm, torch, wl, cfg, mats, t, args, base_ms, base_kinds):
+    """The step variants the pages describe besides the default 1-bit vote:
+    the int8 sign encoding and the optional polar step on the vote.  Each runs
+    on the same state, warmed up and timed like the main step."""
+    import dataclasses
+    out = {}
+    if wl.update != sm.UPDATE_VOTE or args.variant_steps <= 0:
+        return out, t
+    n = args.variant_steps
+    # int8 encoding: sign kernel (int8 out) and the integer-sum vote
+    c8 = dataclasses.replace(cfg, encoding=sm.ENC_INT8)
+    t, wall, kinds = timed_steps(sm, torch, sm.StepCall(c8, mats), t, 2, n)
+    out["int8_encoding"] = {
+        "value": n / wall, "unit": "steps/s", "ms_per_step": 1000.0 * wall / n,
+        "roofline": stream_roofline(kinds, ["sign_pack", "vote_update"]),
+        "kernels": {k: kinds[k] for k in ("sign_pack", "vote_update") if k in kinds}}
+    # polar step on the vote: vote as a matrix, its NS, the dense update
+    cp = dataclasses.replace(cfg, vote_polar=True)
+    t, wall, kinds = timed_steps(sm, torch, sm.StepCall(cp, mats), t, 2, n)
+    g_ms, g_fl = gemm_totals(kinds)
+    b_ms, b_fl = gemm_totals(base_kinds)
+    extra_ms, extra_fl = g_ms - b_ms, g_fl - b_fl
+    achieved = extra_fl / (extra_ms * 1e-3) / 1e12 if extra_ms > 0 else None
+    peak = PEAK_TFLOPS[wl.mdt]
+    out["vote_polar"] = {
+        "value": n / wall, "unit": "steps/s", "ms_per_step": 1000.0 * wall / n,
+        "extra_ms_per_step": 1000.0 * wall / n - base_ms,
+        "roofline": {"bound": "mfma", "kernel": "ns_of_vote (gemm launches beyond the main "
+                     "step's)", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak if achieved else None, "traffic": None,
+                     "ms_per_step": extra_ms, "flops_per_step": extra_fl},
+        "stream_roofline": stream_roofline(kinds, ["vote_update", "polar_update"]),
+        "kernels": {k: kinds[k] for k in ("vote_update", "polar_update", "norm") if k in kinds}}
+    return out, t
 
 
 # Kernel source behind each GEMM kind, and the counter summary of the
@@ -253,14 +350,7 @@ def main():
     ms_per_step = 1000.0 * wall / args.steps
     value = args.steps / wall
 
-    kinds = {}
-    for kind in ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pack",
-                 "vote_update", "lion", "polar_update", "misc"]:
-        ms, n, work = sm.profile_read(kind)
-        if n:
-            kinds[kind] = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
-                           "avg_launch_ms": ms / n, "work_per_launch": work / n,
-                           "flops" if kind.startswith(("gemm", "probe")) else "bytes": work / args.steps}
+    kinds = read_kinds(sm, args.steps)
     dom = max(kinds, key=lambda k: kinds[k]["ms_per_step"])
     is_mfma = dom.startswith(("gemm", "probe"))
     dk = kinds[dom]
@@ -293,6 +383,9 @@ def main():
     if wl.algo == sm.CACHE_MUON:
         refreshed = sum(int(mb.cache_state[:, 1].eq(t - 1).sum().item()) for mb in mats)
         extra["last_step_refreshed_matrices"] = refreshed
+    variants, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms_per_step, kinds)
+    if variants:
+        extra["variants"] = variants
 
     out = {
         "metric": METRIC,

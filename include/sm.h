@@ -159,6 +159,58 @@ sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int6
                          void* w, int wdt, float lr, int8_t* vote_out, hipStream_t s);
 
 /* ------------------------------------------------------------------------
+ * int8 sign encoding (the integer SUM all-reduce variant).
+ * [SignMuon-ja] section 2, algorithm flow step 3 (all-reduce variant) and
+ * communication efficiency: each entry's sign travels as one int8 (8 bits
+ * per entry, 4x fewer bytes than float32), and the workers' signs are
+ * summed as integers before the threshold.
+ *
+ * sm_sign_int8: s[i] = -1 if x[i] < 0 else +1 (+0, -0, NaN -> +1).
+ *   x : [count] in dt (element-aligned).  s : [count] int8 out (any
+ *   alignment; 8-byte alignment takes the vector path).
+ *   Errors: SM_ERR_ARG (null/misaligned x), SM_ERR_SHAPE (count < 0),
+ *   SM_ERR_DTYPE.  count == 0 is a no-op.
+ * sm_vote_update_int8: sum_i = sum_m s[m][i] (integer), V_i = sign(sum_i)
+ *   in {-1, 0, +1} (0 only on ties), then W <- rnd_W(fp32(W) - fp32(lr)*V)
+ *   as sm_vote_update.  s : [M][stride] int8, worker m's signs at
+ *   s + m*stride (stride >= count, in elements).  The signs must be -1 or
+ *   +1 (as sm_sign_int8 writes them); the vote equals sm_vote_update's on
+ *   the same signs.  vote_out : optional [count] int8.
+ *   Errors: as sm_vote_update (stride < count -> SM_ERR_ARG).
+ * ---------------------------------------------------------------------- */
+typedef enum { SM_ENC_BITS = 0, SM_ENC_INT8 = 1 } sm_encoding;
+
+sm_status sm_sign_int8(const void* x, int dt, int64_t count, int8_t* s, hipStream_t stream);
+sm_status sm_vote_update_int8(const int8_t* s, int M, int64_t stride, int64_t count, void* w,
+                              int wdt, float lr, int8_t* vote_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The vote as a matrix, and the dense update (the optional local polar step
+ * on the vote).
+ * [SignMuon-ja] section 2, algorithm flow step 5, and [SignMuon-abs]: a
+ * worker may apply a local polar step to the aggregated sign matrix, at no
+ * extra communication cost.  The library reads it as D = NS(V / (||V||_F +
+ * eps)) with the step's Newton-Schulz settings, and W <- W - lr*D:
+ * sm_vote -> sm_ns_polar (normalize = 1) -> sm_polar_update.
+ *
+ * sm_vote: V_i = sign(sum_m s_m,i) in {-1, 0, +1} written to v ([count] in
+ *   vdt, 16-byte aligned).  signs: packed bits ([M][stride] uint64, 8-byte
+ *   aligned, stride >= ceil(count/64) words) for encoding SM_ENC_BITS, or
+ *   int8 signs ([M][stride] int8, stride >= count) for SM_ENC_INT8.
+ *   Errors: SM_ERR_ARG (null/misaligned, bad encoding, stride too small),
+ *   SM_ERR_SHAPE (count < 0), SM_ERR_UNSUPPORTED (M outside 1..64),
+ *   SM_ERR_DTYPE.
+ * sm_polar_update: w [count] in wdt updated in place, W <- rnd_W(fp32(W) -
+ *   fp32(fp32(lr) * D)); d [count] in ddt.  Both 16-byte aligned, not
+ *   overlapping.  Errors: SM_ERR_ARG (null/misaligned/overlap, lr not
+ *   finite), SM_ERR_SHAPE, SM_ERR_DTYPE.
+ * ---------------------------------------------------------------------- */
+sm_status sm_vote(const void* signs, int encoding, int M, int64_t stride, int64_t count, void* v,
+                  int vdt, hipStream_t stream);
+sm_status sm_polar_update(void* w, int wdt, const void* d, int ddt, int64_t count, float lr,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Whole optimizer step over a set of weight matrices.
  *
  * algo SM_SIGN_MUON  ([SignMuon-ja] section 2, algorithm flow steps 1-4):
@@ -175,6 +227,13 @@ sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int6
  *   (a Muon step), otherwise sign(G_hat) (a Lion step; period 0 = never
  *   Muon).  Signs are voted over the M workers; with SM_UPDATE_POLAR and
  *   M = 1 a Muon step applies W <- W - lr*D instead.
+ * encoding: how the signs travel between the a7 and a9 stages, SM_ENC_BITS
+ *   (1-bit packing, the all-gather payload) or SM_ENC_INT8 (one int8 per
+ *   entry, the SUM all-reduce payload); the vote, and so W, is identical.
+ * vote_polar: 1 replaces W <- W - lr*V by the optional polar step on the
+ *   vote, W <- W - lr*NS(V/(||V||_F+eps)), with the step's ns settings and
+ *   the Newton-Schulz operand type mdt (vote updates only; ignored on a
+ *   SM_UPDATE_POLAR Muon step).
  *
  * sm_matrix: m, n > 0; w [m][n] in wdt; mom [M][m][n] in mdt (updated in
  *   place); grad [M][m][n] in gdt (read-only); q_cache [M][r][r] float32 and
@@ -184,9 +243,9 @@ sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int6
  * t: 1-based step index.  ws: at least sm_step_ws(...) bytes.
  * diag: optional device float [nmat][M][2] out = {err, refreshed} per
  *   (matrix, worker) for SM_CACHE_MUON (NULL to skip; ignored otherwise).
- * Errors: SM_ERR_ARG, SM_ERR_SHAPE, SM_ERR_DTYPE, SM_ERR_WORKSPACE,
- *   SM_ERR_UNSUPPORTED (M outside 1..64, POLAR with M != 1, SIGN_MUON with
- *   POLAR), SM_ERR_HIP.
+ * Errors: SM_ERR_ARG (also a bad encoding or vote_polar), SM_ERR_SHAPE,
+ *   SM_ERR_DTYPE, SM_ERR_WORKSPACE, SM_ERR_UNSUPPORTED (M outside 1..64,
+ *   POLAR with M != 1, SIGN_MUON with POLAR), SM_ERR_HIP.
  * ---------------------------------------------------------------------- */
 typedef enum { SM_SIGN_MUON = 0, SM_CACHE_MUON = 1, SM_LION_MUON = 2 } sm_algo;
 typedef enum { SM_UPDATE_VOTE = 0, SM_UPDATE_POLAR = 1 } sm_update;
@@ -212,6 +271,8 @@ typedef struct {
   sm_ns_params ns;
   float gamma;         /* CacheMuon residual threshold                     */
   int32_t cache_mode;  /* CacheMuon mode (0 trigger, 1 fresh, 2 reuse)     */
+  int32_t encoding;    /* sm_encoding of the signs                         */
+  int32_t vote_polar;  /* 1: polar step on the vote before the update      */
 } sm_config;
 
 sm_status sm_step_ws(const sm_config* c, const sm_matrix* mats, int nmat, size_t* ws_bytes);

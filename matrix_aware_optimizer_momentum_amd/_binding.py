@@ -20,6 +20,7 @@ F32, BF16 = 0, 1
 SIGN_MUON, CACHE_MUON, LION_MUON = 0, 1, 2
 UPDATE_VOTE, UPDATE_POLAR = 0, 1
 MODE_TRIGGER, MODE_FORCE_FRESH, MODE_FORCE_REUSE = 0, 1, 2
+ENC_BITS, ENC_INT8 = 0, 1
 
 KERNEL_KINDS = ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pack",
                 "vote_update", "lion", "polar_update", "misc"]
@@ -44,7 +45,7 @@ class Config(ctypes.Structure):
     _fields_ = [("algo", c_int32), ("update", c_int32), ("M", c_int32), ("wdt", c_int32),
                 ("mdt", c_int32), ("gdt", c_int32), ("lr", c_float), ("beta1", c_float),
                 ("beta2", c_float), ("period", c_int32), ("ns", NSParams), ("gamma", c_float),
-                ("cache_mode", c_int32)]
+                ("cache_mode", c_int32), ("encoding", c_int32), ("vote_polar", c_int32)]
 
 
 P = ctypes.POINTER
@@ -62,6 +63,11 @@ SIGNATURES = {
     "sm_sign_pack": (c_int, [c_void_p, c_int, c_int64, c_void_p, c_void_p]),
     "sm_vote_update": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_int, c_float,
                                c_void_p, c_void_p]),
+    "sm_sign_int8": (c_int, [c_void_p, c_int, c_int64, c_void_p, c_void_p]),
+    "sm_vote_update_int8": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_int, c_float,
+                                    c_void_p, c_void_p]),
+    "sm_vote": (c_int, [c_void_p, c_int, c_int, c_int64, c_int64, c_void_p, c_int, c_void_p]),
+    "sm_polar_update": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int64, c_float, c_void_p]),
     "sm_step_ws": (c_int, [P(Config), P(Matrix), c_int, P(c_size_t)]),
     "sm_step": (c_int, [P(Config), P(Matrix), c_int, c_int64, c_void_p, c_size_t, c_void_p,
                         c_void_p]),

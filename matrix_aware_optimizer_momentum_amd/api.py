@@ -45,11 +45,14 @@ class StepConfig:
     ns: NSParams = field(default_factory=NSParams)
     gamma: float = 0.0
     cache_mode: int = B.MODE_TRIGGER
+    encoding: int = B.ENC_BITS
+    vote_polar: bool = False
 
     def c_struct(self) -> B.Config:
         return B.Config(self.algo, self.update, self.M, _DT[self.wdt], _DT[self.mdt],
                         _DT[self.gdt], self.lr, self.beta1, self.beta2, self.period,
-                        self.ns.c_struct(), self.gamma, self.cache_mode)
+                        self.ns.c_struct(), self.gamma, self.cache_mode, self.encoding,
+                        int(self.vote_polar))
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -177,6 +180,63 @@ def vote_update(bits: torch.Tensor, w: torch.Tensor, lr: float,
     code = B.lib().sm_vote_update(bits.data_ptr(), M, stride, w.numel(), w.data_ptr(), _dt(w),
                                   lr, vp, _stream())
     B.check(code, "sm_vote_update")
+    return w
+
+
+def sign_int8(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 signs (-1 iff x < 0, else +1) of x's elements, flat [numel]."""
+    _dev(x, "x")
+    out = torch.empty(x.numel(), dtype=torch.int8, device=x.device) if out is None else out
+    if out.dtype != torch.int8 or out.numel() < x.numel():
+        raise ValueError("out must be int8 with at least x.numel() elements")
+    code = B.lib().sm_sign_int8(x.data_ptr(), _dt(x), x.numel(), out.data_ptr(), _stream())
+    B.check(code, "sm_sign_int8")
+    return out
+
+
+def vote_update_int8(signs: torch.Tensor, w: torch.Tensor, lr: float,
+                     vote_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """signs: int8 [M, stride] (stride >= w.numel()); w updated in place; returns w."""
+    _dev(signs, "signs"); _dev(w, "w")
+    if signs.dtype != torch.int8 or signs.dim() != 2:
+        raise ValueError("signs must be int8 [M, stride]")
+    M, stride = signs.shape
+    vp = 0
+    if vote_out is not None:
+        _dev(vote_out, "vote_out")
+        if vote_out.dtype != torch.int8 or vote_out.numel() != w.numel():
+            raise ValueError("vote_out must be int8 with w's element count")
+        vp = vote_out.data_ptr()
+    code = B.lib().sm_vote_update_int8(signs.data_ptr(), M, stride, w.numel(), w.data_ptr(),
+                                       _dt(w), lr, vp, _stream())
+    B.check(code, "sm_vote_update_int8")
+    return w
+
+
+def vote(signs: torch.Tensor, count: int, out: torch.Tensor) -> torch.Tensor:
+    """The vote V in {-1, 0, +1} written to out ([count] float32/bfloat16).
+    signs: int64 [M, words_stride] packed bits, or int8 [M, stride] signs."""
+    _dev(signs, "signs"); _dev(out, "out")
+    if signs.dim() != 2 or signs.dtype not in (torch.int64, torch.int8):
+        raise ValueError("signs must be int64 (packed bits) or int8, shape [M, stride]")
+    enc = B.ENC_BITS if signs.dtype == torch.int64 else B.ENC_INT8
+    M, stride = signs.shape
+    if out.numel() < count:
+        raise ValueError("out is smaller than count")
+    code = B.lib().sm_vote(signs.data_ptr(), enc, M, stride, count, out.data_ptr(), _dt(out),
+                           _stream())
+    B.check(code, "sm_vote")
+    return out
+
+
+def polar_update(w: torch.Tensor, d: torch.Tensor, lr: float) -> torch.Tensor:
+    """w <- rnd(w - lr * d) in place (d has w's element count); returns w."""
+    _dev(w, "w"); _dev(d, "d")
+    if d.numel() != w.numel():
+        raise ValueError("d must have w's element count")
+    code = B.lib().sm_polar_update(w.data_ptr(), _dt(w), d.data_ptr(), _dt(d), w.numel(), lr,
+                                   _stream())
+    B.check(code, "sm_polar_update")
     return w
 
 

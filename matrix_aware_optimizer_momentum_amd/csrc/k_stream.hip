@@ -1,7 +1,7 @@
 // Streaming (HBM-bound) kernels of the optimizer step: momentum EMA with
-// sum-of-squares partials, the fused Lion step, sign + 1-bit pack, majority
-// vote + update, the polar update, and the small per-problem finalize
-// kernels.  Every kernel reads and writes each element once with 16-byte
+// sum-of-squares partials, the fused Lion step, sign + 1-bit pack or int8
+// signs, majority vote + update (or the vote as a matrix), the polar update,
+// and the small per-problem finalize kernels.  Every kernel reads and writes each element once with 16-byte
 // vector accesses where the problem size allows, and reduces in a fixed
 // order so results are run-to-run identical.
 //
@@ -100,6 +100,22 @@ __device__ __forceinline__ void flush_bytes(uint8_t* sbytes, uint64_t* bits, int
   __syncthreads();
 }
 
+// Eight int8 signs (-1 iff v[e] < 0, else +1) of entries e0..e0+7, stored
+// as one 8-byte word when all are inside and the target is aligned.
+__device__ __forceinline__ void store_signs8(int8_t* s, int64_t e0, int64_t count,
+                                             const float* v) {
+  if (e0 + 8 <= count && (reinterpret_cast<uintptr_t>(s + e0) & 7u) == 0) {
+    uint64_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) word |= (uint64_t)(v[e] < 0.f ? 0xFFu : 0x01u) << (8 * e);
+    *reinterpret_cast<uint64_t*>(s + e0) = word;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e0 + e < count) s[e0 + e] = v[e] < 0.f ? (int8_t)-1 : (int8_t)1;
+  }
+}
+
 // ------------------------------------------------------------------ EMA
 
 template <typename TM, typename TG, typename TX>
@@ -139,7 +155,7 @@ template <typename TM, typename TG, typename TX>
 __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int per,
                                                    int64_t count, float b1, float b2, TX* x,
                                                    float* partials, uint64_t* bits,
-                                                   int64_t words, bool vec) {
+                                                   int64_t words, int8_t* s8, bool vec) {
   __shared__ float red[4];
   __shared__ uint8_t sbytes[kThreads];
   const int b = blockIdx.y;
@@ -147,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
   const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
   TX* xo = x ? x + (int64_t)b * count : nullptr;
   uint64_t* bo = bits ? bits + (int64_t)b * words : nullptr;
+  int8_t* so = s8 ? s8 + (int64_t)b * count : nullptr;
   const float omb1 = 1.0f - b1, omb2 = 1.0f - b2;
   float acc = 0.f;
   const int64_t nchunks = (count + kChunk - 1) / kChunk;
@@ -165,6 +182,8 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
       store8_tail<TM>(m, e0, count, vec, mv);
       if (bo) {
         byte = neg_byte(dv, e0, count);
+      } else if (so) {
+        store_signs8(so, e0, count, dv);
       } else if (xo) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) dv[e] = round_to<TX>(dv[e]);
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
       flush_bytes(sbytes, bo, ci * (kChunk / 64), words);
     }
   }
-  if (!bo) {
+  if (!bo && !so) {
     float s = block_sum(acc, red);
     if (threadIdx.x == 0 && partials) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
   }
@@ -232,43 +251,89 @@ __global__ __launch_bounds__(kThreads) void k_sign_pack(const T* x, int64_t coun
   }
 }
 
-// Vote over M <= 64 workers for 8 entries per thread.  Each worker's byte of
-// sign bits is spread to one byte-wide counter per entry (a nibble times
-// 0x00204081 places bit i at bit 8i; the 4 partial products never overlap),
-// so one 32-bit add counts 4 entries at once; counts stay below 256.
-template <typename TW>
-__global__ __launch_bounds__(kThreads) void k_vote_update(const uint64_t* bits, int M,
-                                                          int64_t words_stride,
-                                                          int64_t mat_stride_words,
-                                                          int64_t count, PtrTbl w, float lr,
-                                                          int8_t* vote_out, bool vec) {
-  const int j = blockIdx.y;
-  const uint8_t* bb = reinterpret_cast<const uint8_t*>(bits + (int64_t)j * mat_stride_words);
-  const int64_t stride_bytes = words_stride * 8;
-  TW* wp = (TW*)w.p[j];
-  const int64_t nbytes = (count + 7) / 8;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nbytes;
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_sign_int8(const T* x, int64_t count, int8_t* s,
+                                                        bool vec) {
+  const int b = blockIdx.y;
+  const T* xp = x + (int64_t)b * count;
+  int8_t* sp = s + (int64_t)b * count;
+  const int64_t n8 = (count + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * kThreads) {
-    uint32_t lo = 0, hi = 0;
-    for (int k = 0; k < M; ++k) {
-      const uint32_t byte = bb[(int64_t)k * stride_bytes + i];
-      lo += ((byte & 15u) * 0x00204081u) & 0x01010101u;
-      hi += ((byte >> 4) * 0x00204081u) & 0x01010101u;
-    }
+    float v[8];
+    load8_tail<T>(xp, 8 * i, count, vec, v);
+    store_signs8(sp, 8 * i, count, v);
+  }
+}
+
+// Vote over M <= 64 workers for 8 entries per thread.
+//  ENC 0 (packed bits): each worker's byte of sign bits is spread to one
+//    byte-wide counter per entry (a nibble times 0x00204081 places bit i at
+//    bit 8i; the 4 partial products never overlap), so one 32-bit add counts
+//    4 entries at once; counts stay below 256; sum = M - 2 n_neg.
+//  ENC 1 (int8 signs): the integer sum of the workers' bytes, as the SUM
+//    all-reduce of the int8 variant would deliver it.
+// V = sign(sum), 0 on ties.  UPDATE: W <- rnd_W(fp32(W) - lr V) in place in
+// the table's matrices (and the vote to vote_out); otherwise V itself is
+// written, as TW, to the table's matrices.  Strides count words (ENC 0) or
+// bytes (ENC 1).
+template <int ENC, typename TW, bool UPDATE>
+__global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int64_t stride,
+                                                   int64_t mat_stride, int64_t count, PtrTbl w,
+                                                   float lr, int8_t* vote_out, bool vec) {
+  const int j = blockIdx.y;
+  TW* wp = (TW*)w.p[j];
+  const int64_t n8 = (count + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kThreads) {
     const int64_t e0 = 8 * i;
-    float wv[8];
-    int vv[8];
-    load8_tail<TW>(wp, e0, count, vec, wv);
+    int sum[8];
+    if constexpr (ENC == 0) {
+      const uint8_t* bb =
+          reinterpret_cast<const uint8_t*>(static_cast<const uint64_t*>(signs) + j * mat_stride);
+      const int64_t stride_bytes = stride * 8;
+      uint32_t lo = 0, hi = 0;
+      for (int k = 0; k < M; ++k) {
+        const uint32_t byte = bb[(int64_t)k * stride_bytes + i];
+        lo += ((byte & 15u) * 0x00204081u) & 0x01010101u;
+        hi += ((byte >> 4) * 0x00204081u) & 0x01010101u;
+      }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int nneg = (int)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
-      const int sum = M - 2 * nneg;
-      const int v = (sum > 0) - (sum < 0);
-      vv[e] = v;
-      wv[e] = wv[e] - lr * (float)v;  // lr*v is exact: one rounding
+      for (int e = 0; e < 8; ++e)
+        sum[e] = M - 2 * (int)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+    } else {
+      const int8_t* sb = static_cast<const int8_t*>(signs) + j * mat_stride;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] = 0;
+      const bool full = e0 + 8 <= count && (stride & 7) == 0 &&
+                        (reinterpret_cast<uintptr_t>(sb + e0) & 7u) == 0;
+      for (int k = 0; k < M; ++k) {
+        const int8_t* src = sb + (int64_t)k * stride + e0;
+        if (full) {
+          const uint64_t word = *reinterpret_cast<const uint64_t*>(src);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[e] += (int)(int8_t)(uint8_t)(word >> (8 * e));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e0 + e < count) sum[e] += (int)src[e];
+        }
+      }
+    }
+    int vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vv[e] = (sum[e] > 0) - (sum[e] < 0);
+    float wv[8];
+    if constexpr (UPDATE) {
+      load8_tail<TW>(wp, e0, count, vec, wv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = wv[e] - lr * (float)vv[e];  // lr*v is exact: one rounding
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = (float)vv[e];
     }
     store8_tail<TW>(wp, e0, count, vec, wv);
-    if (vote_out) {
+    if (UPDATE && vote_out) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e0 + e < count) vote_out[e0 + e] = (int8_t)vv[e];
@@ -373,16 +438,19 @@ sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int 
 
 sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob, int64_t count,
                       int mdt, int gdt, float beta1, float beta2, void* x, int xdt,
-                      float* partials, uint64_t* bits, int64_t words, hipStream_t s) {
+                      float* partials, uint64_t* bits, int64_t words, int8_t* s8,
+                      hipStream_t s) {
   if (nprob <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
-  dim3 grid(bits ? stream_blocks(count, nprob) : kNormParts, nprob);
+  const bool signs = bits || s8;
+  dim3 grid(signs ? stream_blocks(count, nprob) : kNormParts, nprob);
   double bytes = (double)nprob * count * (2.0 * dt_size(mdt) + dt_size(gdt)) +
-                 (bits ? (double)nprob * words * 8.0 : (double)nprob * count * dt_size(xdt));
+                 (bits ? (double)nprob * words * 8.0
+                       : (s8 ? (double)nprob * count : (double)nprob * count * dt_size(xdt)));
   prof_begin(SM_K_LION, bytes, s);
   SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG, SM_DISPATCH_DT(xdt, TX,
       hipLaunchKernelGGL((k_lion<TM, TG, TX>), grid, dim3(kThreads), 0, s, mom, grad, per,
-                         count, beta1, beta2, (TX*)x, partials, bits, words, vec))));
+                         count, beta1, beta2, (TX*)x, partials, bits, words, s8, vec))));
   prof_end(s);
   return check_launch();
 }
@@ -423,20 +491,56 @@ sm_status launch_sign_pack(const void* x, int dt, int nprob, int64_t count, uint
   return check_launch();
 }
 
-sm_status launch_vote_update(const uint64_t* bits, int M, int64_t words_stride,
-                             int64_t mat_stride_words, int nmat, int64_t count, const PtrTbl& w,
-                             int wdt, float lr, int8_t* vote_out, hipStream_t s) {
+sm_status launch_sign_int8(const void* x, int dt, int nprob, int64_t count, int8_t* s8,
+                           hipStream_t s) {
+  if (nprob <= 0 || count <= 0) return SM_OK;
+  const bool vec = (count % 8) == 0 && (reinterpret_cast<uintptr_t>(x) % 16) == 0;
+  const int64_t n8 = (count + 7) / 8;
+  int64_t want = (4096 + nprob - 1) / nprob;
+  int64_t need = (n8 + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)(need < want ? need : want), nprob);
+  prof_begin(SM_K_SIGN_PACK, (double)nprob * count * (dt_size(dt) + 1.0), s);
+  SM_DISPATCH_DT(dt, T,
+      hipLaunchKernelGGL((k_sign_int8<T>), grid, dim3(kThreads), 0, s, (const T*)x, count, s8,
+                         vec));
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t mat_stride,
+                      int nmat, int64_t count, const PtrTbl& w, int wdt, float lr,
+                      int8_t* vote_out, bool update, hipStream_t s) {
   if (nmat <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
-  const int64_t nbytes = (count + 7) / 8;
+  const int64_t n8 = (count + 7) / 8;
   int64_t want = (4096 + nmat - 1) / nmat;
-  int64_t need = (nbytes + kThreads - 1) / kThreads;
+  int64_t need = (n8 + kThreads - 1) / kThreads;
   dim3 grid((unsigned)(need < want ? need : want), nmat);
-  double bytes = (double)nmat * count * (M / 8.0 + 2.0 * dt_size(wdt) + (vote_out ? 1.0 : 0.0));
+  const double sign_bytes = enc == SM_ENC_BITS ? M / 8.0 : (double)M;
+  double bytes = (double)nmat * count *
+                 (sign_bytes + (update ? 2.0 : 1.0) * dt_size(wdt) + (vote_out ? 1.0 : 0.0));
   prof_begin(SM_K_VOTE_UPDATE, bytes, s);
-  SM_DISPATCH_DT(wdt, TW,
-      hipLaunchKernelGGL((k_vote_update<TW>), grid, dim3(kThreads), 0, s, bits, M,
-                         words_stride, mat_stride_words, count, w, lr, vote_out, vec));
+  if (enc == SM_ENC_BITS) {
+    if (update) {
+      SM_DISPATCH_DT(wdt, TW,
+          hipLaunchKernelGGL((k_vote<0, TW, true>), grid, dim3(kThreads), 0, s, signs, M,
+                             stride, mat_stride, count, w, lr, vote_out, vec));
+    } else {
+      SM_DISPATCH_DT(wdt, TW,
+          hipLaunchKernelGGL((k_vote<0, TW, false>), grid, dim3(kThreads), 0, s, signs, M,
+                             stride, mat_stride, count, w, lr, nullptr, vec));
+    }
+  } else {
+    if (update) {
+      SM_DISPATCH_DT(wdt, TW,
+          hipLaunchKernelGGL((k_vote<1, TW, true>), grid, dim3(kThreads), 0, s, signs, M,
+                             stride, mat_stride, count, w, lr, vote_out, vec));
+    } else {
+      SM_DISPATCH_DT(wdt, TW,
+          hipLaunchKernelGGL((k_vote<1, TW, false>), grid, dim3(kThreads), 0, s, signs, M,
+                             stride, mat_stride, count, w, lr, nullptr, vec));
+    }
+  }
   prof_end(s);
   return check_launch();
 }

@@ -544,13 +544,14 @@ std::vector<Chunk> plan_chunks(const sm_matrix* mats, int nmat) {
 }
 
 struct ChunkWs {
-  void* x0;
+  void* x0;          // NS input copy (and the vote matrix of the polar step)
   void* d;
   NsWs ns;
   GramWs gram;
   float* partials;
   float* scale;
-  uint64_t* bits;
+  uint64_t* bits;    // packed signs [B][words]   (SM_ENC_BITS)
+  int8_t* s8;        // int8 signs   [B][count]   (SM_ENC_INT8)
 };
 
 void carve_chunk(Carver& cv, const sm_config& c, const Chunk& ch, ChunkWs& w) {
@@ -558,18 +559,19 @@ void carve_chunk(Carver& cv, const sm_config& c, const Chunk& ch, ChunkWs& w) {
   const int64_t count = (int64_t)ch.m * ch.n;
   const size_t es = dt_size(c.mdt);
   const int64_t words = (count + 63) / 64;
-  const bool ns_possible = !(c.algo == SM_LION_MUON && c.period == 0);
+  const bool ns_possible = !(c.algo == SM_LION_MUON && c.period == 0) || c.vote_polar;
   std::memset(&w, 0, sizeof(w));
-  w.bits = cv.take<uint64_t>((size_t)B * words * 8);
+  if (c.encoding == SM_ENC_INT8)
+    w.s8 = cv.take<int8_t>((size_t)B * count);
+  else
+    w.bits = cv.take<uint64_t>((size_t)B * words * 8);
   if (!ns_possible) return;
   w.partials = cv.take<float>((size_t)B * kNormParts * 4);
   w.scale = cv.take<float>((size_t)B * 4);
   w.x0 = cv.take<void>((size_t)B * count * es);
   w.d = cv.take<void>((size_t)B * count * es);
-  if (c.algo == SM_CACHE_MUON)
-    carve_gram(cv, B, ch.m, ch.n, w.gram);
-  else
-    carve_ns(cv, c.mdt, B, ch.m, ch.n, w.ns);
+  if (c.algo == SM_CACHE_MUON) carve_gram(cv, B, ch.m, ch.n, w.gram);
+  if (c.algo != SM_CACHE_MUON || c.vote_polar) carve_ns(cv, c.mdt, B, ch.m, ch.n, w.ns);
 }
 
 sm_status check_config(const sm_config* c) {
@@ -585,6 +587,8 @@ sm_status check_config(const sm_config* c) {
   if (c->M < 1 || c->M > 64) return SM_ERR_UNSUPPORTED;
   if (c->update == SM_UPDATE_POLAR && (c->M != 1 || c->algo == SM_SIGN_MUON))
     return SM_ERR_UNSUPPORTED;
+  if (c->encoding != SM_ENC_BITS && c->encoding != SM_ENC_INT8) return SM_ERR_ARG;
+  if (c->vote_polar != 0 && c->vote_polar != 1) return SM_ERR_ARG;
   return SM_OK;
 }
 
@@ -636,7 +640,7 @@ const char* sm_status_string(int s) {
 
 int sm_last_hip_error(void) { return g_last_hip.load(); }
 
-int sm_version(void) { return 1; }
+int sm_version(void) { return 2; }
 
 sm_status sm_ns_polar_ws(int dt, int batch, int m, int n, size_t* ws_bytes) {
   if (!ws_bytes) return SM_ERR_ARG;
@@ -744,7 +748,57 @@ sm_status sm_vote_update(const uint64_t* bits, int M, int64_t words_stride, int6
   if (!bits || !w || !al16(w) || (reinterpret_cast<uintptr_t>(bits) & 7u)) return SM_ERR_ARG;
   if (words_stride < (count + 63) / 64 || !finite(lr)) return SM_ERR_ARG;
   const PtrTbl wt = tbl_one(w);
-  return launch_vote_update(bits, M, words_stride, 0, 1, count, wt, wdt, lr, vote_out, s);
+  return launch_vote(SM_ENC_BITS, bits, M, words_stride, 0, 1, count, wt, wdt, lr, vote_out,
+                     true, s);
+}
+
+sm_status sm_sign_int8(const void* x, int dt, int64_t count, int8_t* sg, hipStream_t s) {
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  if (count < 0) return SM_ERR_SHAPE;
+  if (count == 0) return SM_OK;
+  if (!x || !sg || (reinterpret_cast<uintptr_t>(x) % dt_size(dt))) return SM_ERR_ARG;
+  if (overlap(x, (size_t)count * dt_size(dt), sg, (size_t)count)) return SM_ERR_ARG;
+  return launch_sign_int8(x, dt, 1, count, sg, s);
+}
+
+sm_status sm_vote_update_int8(const int8_t* sg, int M, int64_t stride, int64_t count, void* w,
+                              int wdt, float lr, int8_t* vote_out, hipStream_t s) {
+  if (!valid_dt(wdt)) return SM_ERR_DTYPE;
+  if (count < 0) return SM_ERR_SHAPE;
+  if (M < 1 || M > 64) return SM_ERR_UNSUPPORTED;
+  if (count == 0) return SM_OK;
+  if (!sg || !w || !al16(w)) return SM_ERR_ARG;
+  if (stride < count || !finite(lr)) return SM_ERR_ARG;
+  const PtrTbl wt = tbl_one(w);
+  return launch_vote(SM_ENC_INT8, sg, M, stride, 0, 1, count, wt, wdt, lr, vote_out, true, s);
+}
+
+sm_status sm_vote(const void* signs, int encoding, int M, int64_t stride, int64_t count, void* v,
+                  int vdt, hipStream_t s) {
+  if (!valid_dt(vdt)) return SM_ERR_DTYPE;
+  if (count < 0) return SM_ERR_SHAPE;
+  if (M < 1 || M > 64) return SM_ERR_UNSUPPORTED;
+  if (encoding != SM_ENC_BITS && encoding != SM_ENC_INT8) return SM_ERR_ARG;
+  if (count == 0) return SM_OK;
+  if (!signs || !v || !al16(v)) return SM_ERR_ARG;
+  if (encoding == SM_ENC_BITS) {
+    if ((reinterpret_cast<uintptr_t>(signs) & 7u) || stride < (count + 63) / 64) return SM_ERR_ARG;
+  } else if (stride < count) {
+    return SM_ERR_ARG;
+  }
+  const PtrTbl vt = tbl_one(v);
+  return launch_vote(encoding, signs, M, stride, 0, 1, count, vt, vdt, 0.f, nullptr, false, s);
+}
+
+sm_status sm_polar_update(void* w, int wdt, const void* d, int ddt, int64_t count, float lr,
+                          hipStream_t s) {
+  if (!valid_dt(wdt) || !valid_dt(ddt)) return SM_ERR_DTYPE;
+  if (count < 0) return SM_ERR_SHAPE;
+  if (count == 0) return SM_OK;
+  if (!w || !d || !al16(w) || !al16(d) || !finite(lr)) return SM_ERR_ARG;
+  if (overlap(w, (size_t)count * dt_size(wdt), d, (size_t)count * dt_size(ddt))) return SM_ERR_ARG;
+  const PtrTbl wt = tbl_one(w);
+  return launch_polar_update(d, ddt, 1, count, wt, wdt, lr, s);
 }
 
 sm_status sm_step_ws(const sm_config* c, const sm_matrix* mats, int nmat, size_t* ws_bytes) {
@@ -824,7 +878,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
       // a7 + a8 fused into the last NS product when the signs are all the
       // step needs from the direction
       r.fused_signs = false;
-      if (r.grouped && !polar) {
+      if (r.grouped && !polar && c->encoding == SM_ENC_BITS) {
         NsJob bj = r.job;
         bj.bits = r.w.bits;
         bj.bits_stride = r.words;
@@ -841,10 +895,10 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     if (c->algo == SM_LION_MUON) {
       if (muon_step)
         SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
-                           r.w.x0, c->mdt, r.w.partials, nullptr, 0, s));
+                           r.w.x0, c->mdt, r.w.partials, nullptr, 0, nullptr, s));
       else
         SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
-                           nullptr, c->mdt, nullptr, r.w.bits, r.words, s));
+                           nullptr, c->mdt, nullptr, r.w.bits, r.words, r.w.s8, s));
     } else {
       void* x0 = (r.grouped && r.job.xtbl) ? nullptr : r.w.x0;   // no copy when NS reads M
       SM_TRY(launch_ema_single(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, x0,
@@ -881,18 +935,63 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     }
     if (!grouped.empty()) SM_TRY(ns_grouped(grouped, c->ns, s));
   }
-  // a7-a10: signs, pack, vote and update (or the polar update)
+  // a7-a10: signs (packed bits or int8), vote and update (or the polar update)
+  const bool int8 = c->encoding == SM_ENC_INT8;
   for (size_t ci = 0; ci < chunks.size(); ++ci) {
     ChunkRun& r = runs[ci];
     if (muon_step) {
       if (polar)
         SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));
+      else if (int8)
+        SM_TRY(launch_sign_int8(r.w.d, c->mdt, r.B, r.count, r.w.s8, s));
       else if (!r.fused_signs)
         SM_TRY(launch_sign_pack(r.w.d, c->mdt, r.B, r.count, r.w.bits, r.words, s));
     }
-    if (!polar)
-      SM_TRY(launch_vote_update(r.w.bits, M, r.words, (int64_t)M * r.words, r.nc, r.count, r.wt,
-                                c->wdt, c->lr, nullptr, s));
+  }
+  if (polar) return SM_OK;
+  std::vector<const void*> sg(chunks.size());
+  for (size_t ci = 0; ci < chunks.size(); ++ci)
+    sg[ci] = int8 ? (const void*)runs[ci].w.s8 : (const void*)runs[ci].w.bits;
+  if (!c->vote_polar) {
+    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+      ChunkRun& r = runs[ci];
+      const int64_t stride = int8 ? r.count : r.words;
+      SM_TRY(launch_vote(c->encoding, sg[ci], M, stride, (int64_t)M * stride, r.nc, r.count,
+                         r.wt, c->wdt, c->lr, nullptr, true, s));
+    }
+    return SM_OK;
+  }
+  // Optional local polar step on the vote: V (exact in mdt) -> its own
+  // normalisation -> NS with the step's settings -> W <- W - lr * D.
+  std::vector<NsJob> vjobs;
+  std::vector<size_t> vgen;   // chunks whose vote NS takes the generic path
+  for (size_t ci = 0; ci < chunks.size(); ++ci) {
+    const Chunk& ch = chunks[ci];
+    ChunkRun& r = runs[ci];
+    const int64_t stride = int8 ? r.count : r.words;
+    PtrTbl vt;
+    std::memset(&vt, 0, sizeof(vt));
+    for (int j = 0; j < r.nc; ++j)
+      vt.p[j] = static_cast<const char*>(r.w.x0) + (int64_t)j * r.count * dt_size(c->mdt);
+    SM_TRY(launch_vote(c->encoding, sg[ci], M, stride, (int64_t)M * stride, r.nc, r.count, vt,
+                       c->mdt, 0.f, nullptr, false, s));
+    SM_TRY(launch_sumsq(r.w.x0, c->mdt, r.nc, r.count, r.w.partials, s));
+    SM_TRY(launch_scale_finalize(r.w.partials, r.nc, c->ns.eps, r.w.scale, s));
+    NsJob j{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.nc, ch.m, ch.n};
+    if (ns_grouped_ok(j, c->mdt, c->ns))
+      vjobs.push_back(j);
+    else
+      vgen.push_back(ci);
+  }
+  if (!vjobs.empty()) SM_TRY(ns_grouped(vjobs, c->ns, s));
+  for (size_t ci : vgen) {
+    const Chunk& ch = chunks[ci];
+    ChunkRun& r = runs[ci];
+    SM_TRY(ns_core(r.w.x0, r.w.d, r.w.ns, r.w.scale, c->mdt, r.nc, ch.m, ch.n, c->ns, s));
+  }
+  for (size_t ci = 0; ci < chunks.size(); ++ci) {
+    ChunkRun& r = runs[ci];
+    SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));
   }
   return SM_OK;
 }

@@ -115,12 +115,14 @@ sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int 
                             float* partials, hipStream_t s);
 
 // LionMuon fused kernel.  ghat = beta1*M + (1-beta1)*G, M <- beta2*M +
-// (1-beta2)*G.  If bits != null (Lion step) the signs of ghat (float32) are
-// packed to bits[nprob][words]; otherwise ghat is stored to x in xdt with
+// (1-beta2)*G.  On a Lion step the signs of ghat (decided in float32) are
+// packed to bits[nprob][words] (bits != null) or written as int8 signs to
+// s8[nprob][count] (s8 != null); otherwise ghat is stored to x in xdt with
 // sum-of-squares partials (Muon step input).
 sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob, int64_t count,
                       int mdt, int gdt, float beta1, float beta2, void* x, int xdt,
-                      float* partials, uint64_t* bits, int64_t words, hipStream_t s);
+                      float* partials, uint64_t* bits, int64_t words, int8_t* s8,
+                      hipStream_t s);
 
 // Sum-of-squares partials of nprob contiguous problems.
 sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* partials,
@@ -135,11 +137,19 @@ sm_status launch_scale_finalize(const float* partials, int nprob, float eps, flo
 sm_status launch_sign_pack(const void* x, int dt, int nprob, int64_t count, uint64_t* bits,
                            int64_t words, hipStream_t s);
 
-// Vote + update of `nmat` matrices; matrix j reads bits + j*mat_stride_words
-// (worker k at + k*words_stride) and updates w.p[j].
-sm_status launch_vote_update(const uint64_t* bits, int M, int64_t words_stride,
-                             int64_t mat_stride_words, int nmat, int64_t count, const PtrTbl& w,
-                             int wdt, float lr, int8_t* vote_out, hipStream_t s);
+// int8 signs (-1 iff x < 0, else +1) of nprob contiguous problems of `count`
+// elements into s8 (problem b at s8 + b*count).
+sm_status launch_sign_int8(const void* x, int dt, int nprob, int64_t count, int8_t* s8,
+                           hipStream_t s);
+
+// Vote of `nmat` matrices from packed bits (enc SM_ENC_BITS; strides in
+// uint64 words) or int8 signs (SM_ENC_INT8; strides in bytes): matrix j reads
+// signs + j*mat_stride, worker k at + k*stride.  update: W <- rnd(W - lr*V)
+// in place at w.p[j] (vote_out optional); otherwise V in {-1, 0, +1} is
+// written as wdt to w.p[j].
+sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t mat_stride,
+                      int nmat, int64_t count, const PtrTbl& w, int wdt, float lr,
+                      int8_t* vote_out, bool update, hipStream_t s);
 
 // W <- rnd(fp32(W) - fp32(lr*D)) for nmat matrices, D contiguous [nmat][count].
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,

@@ -45,9 +45,10 @@ def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "sm.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(sm_ns_params),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(sm_ns_params),"
         " sizeof(sm_matrix), sizeof(sm_config), offsetof(sm_config, ns),"
-        " offsetof(sm_config, gamma), offsetof(sm_matrix, w), offsetof(sm_matrix, cache_state));"
+        " offsetof(sm_config, gamma), offsetof(sm_matrix, w), offsetof(sm_matrix, cache_state),"
+        " offsetof(sm_config, encoding), offsetof(sm_config, vote_polar));"
         "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", "-I/opt/rocm/include",
@@ -56,7 +57,7 @@ def test_struct_layout_matches_c(tmp_path):
                                            check=True).stdout.split()]
     want = [ctypes.sizeof(B.NSParams), ctypes.sizeof(B.Matrix), ctypes.sizeof(B.Config),
             B.Config.ns.offset, B.Config.gamma.offset, B.Matrix.w.offset,
-            B.Matrix.cache_state.offset]
+            B.Matrix.cache_state.offset, B.Config.encoding.offset, B.Config.vote_polar.offset]
     assert vals == want
 
 
@@ -106,7 +107,7 @@ def test_step_ws_and_config_validation():
                       (dict(update=1, M=1), 5),            # Sign-Muon with polar update
                       (dict(algo=1, update=1, M=2), 5),    # polar needs one worker
                       (dict(period=-1), 1), (dict(lr=float("nan")), 1),
-                      (dict(cache_mode=3), 1)):
+                      (dict(cache_mode=3), 1), (dict(encoding=2), 1), (dict(vote_polar=2), 1)):
         c = _cfg(**bad)
         assert _ws(lib.sm_step_ws, ctypes.byref(c), mats, 2)[0] == want, bad
     c = _cfg(wdt=torch.float32)
@@ -138,6 +139,31 @@ def test_host_validation_rejects_before_any_gpu_call():
     # words_stride too small for the count
     assert lib.sm_vote_update(ctypes.c_void_p(0x1000), 3, 1, 65, ctypes.c_void_p(0x2000),
                               B.F32, 1e-3, None, None) == 1
+    # int8 encoding, the vote as a matrix, the dense update
+    assert lib.sm_sign_int8(None, B.F32, 10, None, None) == 1
+    assert lib.sm_sign_int8(None, B.F32, -1, None, None) == 2
+    assert lib.sm_sign_int8(None, B.F32, 0, None, None) == 0
+    assert lib.sm_sign_int8(ctypes.c_void_p(0x1002), B.F32, 10, ctypes.c_void_p(0x2000),
+                            None) == 1
+    assert lib.sm_sign_int8(ctypes.c_void_p(0x1000), B.F32, 10, ctypes.c_void_p(0x1010),
+                            None) == 1                              # overlap
+    assert lib.sm_vote_update_int8(None, 0, 10, 10, None, B.F32, 1e-3, None, None) == 5
+    assert lib.sm_vote_update_int8(ctypes.c_void_p(0x1000), 3, 9, 10, ctypes.c_void_p(0x2000),
+                                   B.F32, 1e-3, None, None) == 1    # stride < count
+    assert lib.sm_vote_update_int8(ctypes.c_void_p(0x1000), 3, 10, 10, ctypes.c_void_p(0x2000),
+                                   B.F32, float("inf"), None, None) == 1
+    assert lib.sm_vote(ctypes.c_void_p(0x1000), 2, 3, 10, 10, ctypes.c_void_p(0x2000), B.F32,
+                       None) == 1                                   # bad encoding
+    assert lib.sm_vote(ctypes.c_void_p(0x1004), 0, 3, 1, 64, ctypes.c_void_p(0x2000), B.F32,
+                       None) == 1                                   # misaligned bits
+    assert lib.sm_vote(ctypes.c_void_p(0x1000), 0, 3, 1, 65, ctypes.c_void_p(0x2000), B.F32,
+                       None) == 1                                   # stride too small
+    assert lib.sm_vote(ctypes.c_void_p(0x1000), 1, 70, 100, 10, ctypes.c_void_p(0x2000), B.F32,
+                       None) == 5
+    assert lib.sm_polar_update(ctypes.c_void_p(0x1000), B.F32, ctypes.c_void_p(0x1000), B.F32,
+                               10, 1e-3, None) == 1                 # aliasing
+    assert lib.sm_polar_update(ctypes.c_void_p(0x1000), B.F32, ctypes.c_void_p(0x2000), 4,
+                               10, 1e-3, None) == 3
     # aliasing input/output of NS
     assert lib.sm_ns_polar(ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10000), B.F32, 1, 4, 4,
                            1, ctypes.byref(p), ctypes.c_void_p(0x100000), 1 << 20, None) == 1

@@ -79,6 +79,112 @@ def test_vote_update_bit_exact(gpu_lib, wdt, M, count):
                                   want_w.astype(np.float32).view(np.uint32))
 
 
+# ------------------------------------------------------------------ int8 encoding
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 2049, 100003, (1 << 20) + 5])
+def test_sign_int8_bit_exact(gpu_lib, dt, n):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(2000 + n)
+    x = _special(rng, n)
+    xt = to_gpu(x, dt)
+    s8 = sm.sign_int8(xt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s8.cpu().numpy(), O.sign_int8(to_np(xt)))
+
+
+def test_sign_int8_unaligned_output(gpu_lib):
+    """An output that is not 8-byte aligned takes the per-byte path."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    x = _special(np.random.default_rng(5), 1001)
+    xt = to_gpu(x, "f32")
+    buf = torch.zeros(1010, dtype=torch.int8, device="cuda")
+    sm.sign_int8(xt, out=buf[3:1004])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    np.testing.assert_array_equal(got[3:1004], O.sign_int8(x))
+    assert not got[:3].any() and not got[1004:].any()
+
+
+def _signs_for_vote(rng, M, count):
+    xs = [rng.standard_normal(count).astype(np.float32) for _ in range(M)]
+    if M >= 4:                               # exact ties on some entries
+        k = min(count, 50)
+        for j in range(M // 2):
+            xs[j][:k] = -1.0
+        for j in range(M // 2, 2 * (M // 2)):
+            xs[j][:k] = 1.0
+    return xs
+
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 16, 64])
+@pytest.mark.parametrize("count", [1, 8, 1000, 4097, 65539])
+def test_vote_update_int8_bit_exact_and_equal_to_bits(gpu_lib, wdt, M, count):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(M * 7919 + count)
+    xs = _signs_for_vote(rng, M, count)
+    stride = count + 5                       # padded, unaligned worker stride
+    s8 = np.full((M, stride), 77, dtype=np.int8)   # padding must be ignored
+    for k in range(M):
+        s8[k, :count] = O.sign_int8(xs[k])
+    w0 = (0.02 * rng.standard_normal(count)).astype(np.float32)
+    wt = to_gpu(w0, wdt)
+    w_before = to_np(wt)
+    vote = torch.empty(count, dtype=torch.int8, device="cuda")
+    sm.vote_update_int8(torch.from_numpy(s8).cuda(), wt, 1e-3, vote_out=vote)
+    # the same signs through the 1-bit path
+    words = (count + 63) // 64
+    packed = np.stack([O.sign_pack(x) for x in xs]).astype(np.uint64)
+    wb = to_gpu(w0, wdt)
+    vote_b = torch.empty(count, dtype=torch.int8, device="cuda")
+    sm.vote_update(torch.from_numpy(packed.view(np.int64)).cuda(), wb, 1e-3, vote_out=vote_b)
+    torch.cuda.synchronize()
+    want_v = O.vote_from_int8([s8[k, :count] for k in range(M)], count)
+    np.testing.assert_array_equal(vote.cpu().numpy(), want_v)
+    np.testing.assert_array_equal(vote_b.cpu().numpy(), want_v)
+    want_w = O.update_vote(w_before, want_v, 1e-3, O.F32 if wdt == "f32" else O.BF16)
+    np.testing.assert_array_equal(to_np(wt).view(np.uint32),
+                                  want_w.astype(np.float32).view(np.uint32))
+    assert torch.equal(wt, wb)
+    assert words == packed.shape[1]
+
+
+@pytest.mark.parametrize("vdt", ["f32", "bf16"])
+@pytest.mark.parametrize("enc", ["bits", "int8"])
+@pytest.mark.parametrize("M,count", [(1, 9), (4, 4097), (5, 65539), (16, 1000)])
+def test_vote_matrix_bit_exact(gpu_lib, vdt, enc, M, count):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(31 * M + count)
+    xs = _signs_for_vote(rng, M, count)
+    if enc == "bits":
+        signs = torch.from_numpy(np.stack([O.sign_pack(x) for x in xs]).view(np.int64)).cuda()
+    else:
+        signs = torch.from_numpy(np.stack([O.sign_int8(x) for x in xs])).cuda()
+    out = torch.full((count,), 5.0, dtype=torch.float32 if vdt == "f32" else torch.bfloat16,
+                     device="cuda")
+    sm.vote(signs, count, out)
+    torch.cuda.synchronize()
+    want = O.vote_from_int8([O.sign_int8(x) for x in xs], count).astype(np.float64)
+    np.testing.assert_array_equal(to_np(out), want)
+
+
+@pytest.mark.parametrize("wdt,ddt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"),
+                                     ("f32", "bf16")])
+@pytest.mark.parametrize("count", [1, 1001, 65536])
+def test_polar_update_bit_exact(gpu_lib, wdt, ddt, count):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(count + 17)
+    wt = to_gpu((0.02 * rng.standard_normal(count)).astype(np.float32), wdt)
+    dt_ = to_gpu((rng.standard_normal(count) / 30).astype(np.float32), ddt)
+    w_before, d = to_np(wt), to_np(dt_)
+    sm.polar_update(wt, dt_, 3e-3)
+    torch.cuda.synchronize()
+    want = O.update_polar(w_before, d, 3e-3, O.F32 if wdt == "f32" else O.BF16)
+    np.testing.assert_array_equal(to_np(wt).view(np.uint32),
+                                  want.astype(np.float32).view(np.uint32))
+
+
 # ------------------------------------------------------------------ direct NS
 
 NS_CASES = [

@@ -9,8 +9,14 @@
 * Composition: sm_step equals, bit for bit, the chain of the individual entry
   points (sm_ns_polar / sm_gram_ns_cached -> sm_sign_pack -> sm_vote_update)
   run on the step's own momentum.
+* Encodings: the int8 sign encoding gives the same momentum and weights, bit
+  for bit, as the 1-bit encoding, for every algorithm.
+* Polar step on the vote: sm_step equals the chain sm_vote -> sm_ns_polar ->
+  sm_polar_update on the step's own signs, and the implied direction matches
+  the oracle's NS of the same vote within the NS tolerance.
 * Full size: one GPT-2-small step (12 layers, M = 5, bf16) in the launch
-  configuration the benchmark times, checked on sampled matrices.
+  configuration the benchmark times, checked on sampled matrices, in both
+  encodings and with the polar step on the vote.
 """
 import numpy as np
 import pytest
@@ -47,7 +53,8 @@ def _ocfg(wl: W.Workload, cfg: sm.StepConfig) -> O.StepConfig:
                         beta2=f32(cfg.beta2), period=cfg.period,
                         ns=O.NSParams(cfg.ns.iters, f32(cfg.ns.a), f32(cfg.ns.b), f32(cfg.ns.c),
                                       f32(cfg.ns.eps)),
-                        gamma=f32(cfg.gamma), cache_mode=cfg.cache_mode)
+                        gamma=f32(cfg.gamma), cache_mode=cfg.cache_mode,
+                        encoding=cfg.encoding, vote_polar=bool(cfg.vote_polar))
 
 
 def _check_mom(wl, cfg, gpu_mom, ms, m_prev, g, what):
@@ -274,6 +281,116 @@ def test_lion_muon_polar_single_worker(gpu_lib):
     assert rel_fro(delta_gpu, out["d"][0]) <= 1e-3
 
 
+# ------------------------------------------------------------------ encodings and the polar step on the vote
+
+def _clone_state(st: "Seeded"):
+    return [sm.MatrixBuffers(w=mb.w.clone(), mom=mb.mom.clone(), grad=mb.grad,
+                             q_cache=None if mb.q_cache is None else mb.q_cache.clone(),
+                             cache_state=None if mb.cache_state is None else mb.cache_state.clone())
+            for mb in st.mats]
+
+
+ENC_CASES = [
+    ("sign", 1, [(256, 256)], {}, 3),
+    ("sign", 3, [(64, 147), (256, 64), (128, 1152)], {}, 3),
+    ("sign", 2, [(768, 2304), (3072, 768)], {}, 3),
+    ("cache", 4, [(128, 384), (512, 128)], dict(M=3, update=sm.UPDATE_VOTE, wdt="bf16",
+                                                mdt="bf16", gdt="bf16"), 1),
+    ("lion-lion", 5, [(64, 200), (300, 70)], dict(M=3, period=2, wdt="f32", mdt="f32",
+                                                  gdt="f32"), 1),
+    ("lion-muon", 5, [(64, 200), (300, 70)], dict(M=4, period=2, wdt="bf16", mdt="bf16",
+                                                  gdt="bf16"), 2),
+]
+
+
+@pytest.mark.parametrize("case", ENC_CASES, ids=[f"{c[0]}-{len(c[2])}" for c in ENC_CASES])
+def test_int8_encoding_step_equals_bit_encoding(gpu_lib, case):
+    _, idx, shapes, kw, t = case
+    wl = W.WORKLOADS[idx].scaled(**kw) if kw else W.WORKLOADS[idx]
+    st = Seeded(wl, shapes, mom_scale=1.0 if wl.algo == sm.LION_MUON else 0.01)
+    if wl.algo == sm.CACHE_MUON:
+        _cache_bufs(st, wl.M)
+    mats_b, mats_8 = _clone_state(st), _clone_state(st)
+    sm.StepCall(_cfg(wl), mats_b)(t)
+    sm.StepCall(_cfg(wl, encoding=sm.ENC_INT8), mats_8)(t)
+    torch.cuda.synchronize()
+    for j, (a, b) in enumerate(zip(mats_b, mats_8)):
+        assert torch.equal(a.mom, b.mom), j
+        assert torch.equal(a.w.view(torch.int16) if a.w.dtype == torch.bfloat16 else a.w,
+                           b.w.view(torch.int16) if b.w.dtype == torch.bfloat16 else b.w), j
+        assert not torch.equal(a.w, st.mats[j].w), j        # the step moved W
+
+
+def _vote_polar_chain(cfg, mb, w_before, enc, signs_fn):
+    """W after the polar step on the vote, through the individual entry points."""
+    m, n = mb.w.shape
+    signs = signs_fn(mb)
+    v = torch.empty(m, n, dtype=cfg.mdt, device="cuda")
+    sm.vote(signs, m * n, v)
+    d = sm.ns_polar(v[None], params=cfg.ns)
+    w2 = w_before.clone()
+    sm.polar_update(w2, d[0], cfg.lr)
+    return w2, v
+
+
+def _ns_signs(cfg, enc):
+    def fn(mb):
+        u = sm.ns_polar(mb.mom, params=cfg.ns)
+        if enc == sm.ENC_BITS:
+            count = u[0].numel()
+            bits = torch.empty(cfg.M, (count + 63) // 64, dtype=torch.int64, device="cuda")
+            for k in range(cfg.M):
+                sm.sign_pack(u[k], bits=bits[k])
+            return bits
+        return torch.stack([sm.sign_int8(u[k]) for k in range(cfg.M)])
+    return fn
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("enc", [0, 1], ids=["bits", "int8"])
+def test_vote_polar_step_equals_chain_and_oracle(gpu_lib, dt, enc):
+    wl = W.WORKLOADS[3].scaled(wdt="f32", mdt=dt, gdt=dt, M=4)
+    shapes = [(64, 147), (256, 64), (128, 384), (384, 1280)]
+    st = Seeded(wl, shapes)
+    cfg = _cfg(wl, encoding=enc, vote_polar=True)
+    w_before = [mb.w.clone() for mb in st.mats]
+    sm.StepCall(cfg, st.mats)(2)
+    torch.cuda.synchronize()
+    ocfg = _ocfg(wl, cfg)
+    for j, (mb, (m, n)) in enumerate(zip(st.mats, shapes)):
+        w2, v = _vote_polar_chain(cfg, mb, w_before[j], enc, _ns_signs(cfg, enc))
+        torch.cuda.synchronize()
+        assert torch.equal(w2, mb.w), f"matrix {j}: step differs from the entry-point chain"
+        ms, out = _oracle_step(wl, cfg, st, j, 2)
+        _check_vote(to_np(v), out["vote"], out["d"], dt, f"matrix {j} {m}x{n}")
+        d_or = O.round_storage(O.vote_polar_direction(to_np(v), ocfg.ns), dt)
+        delta = (to_np(w_before[j]).astype(np.float64) - to_np(mb.w)) / cfg.lr
+        tol = 1e-3 if dt == "f32" else 3e-2
+        assert rel_fro(delta, d_or) <= tol, (j, rel_fro(delta, d_or))
+
+
+def test_vote_polar_on_a_lion_step(gpu_lib):
+    """Lion step (signs of the interpolation, decided in float32) + the polar
+    step on their vote: the oracle's exact signs through the GPU chain."""
+    wl = W.WORKLOADS[5].scaled(wdt="f32", mdt="f32", gdt="f32", M=3, period=4)
+    shapes = [(96, 200), (200, 96)]
+    st = Seeded(wl, shapes, mom_scale=1.0)
+    cfg = _cfg(wl, vote_polar=True, encoding=sm.ENC_INT8)
+    w_before = [mb.w.clone() for mb in st.mats]
+    sm.StepCall(cfg, st.mats)(1)                 # t = 1, P = 4: a Lion step
+    torch.cuda.synchronize()
+    for j, mb in enumerate(st.mats):
+        ms, out = _oracle_step(wl, cfg, st, j, 1)
+        signs8 = torch.from_numpy(np.stack(out["signs8"])).cuda()
+        w2, v = _vote_polar_chain(cfg, mb, w_before[j], sm.ENC_INT8, lambda _: signs8)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(v), out["vote"].astype(np.float64))
+        assert torch.equal(w2, mb.w), j
+        _check_mom(wl, cfg, to_np(mb.mom), ms, st.mom[j], st.grad[j], f"matrix {j}")
+        delta = (to_np(w_before[j]).astype(np.float64) - to_np(mb.w)) / cfg.lr
+        assert rel_fro(delta, out["vote_d"]) <= 1e-3
+
+
 # ------------------------------------------------------------------ full size (benchmark launch)
 
 def test_full_size_gpt2_small_step_sampled(gpu_lib):
@@ -305,3 +422,38 @@ def test_full_size_gpt2_small_step_sampled(gpu_lib):
         _check_mom(wl, cfg, to_np(mats[j].mom), ms, m0, g0, f"full-size matrix {j}")
         v_gpu = _vote_from_w(w0, to_np(mats[j].w), cfg.lr, "bf16")
         _check_vote(v_gpu, out["vote"], out["d"], "bf16", f"full-size matrix {j}")
+
+
+@pytest.mark.parametrize("variant", ["int8", "vote_polar"])
+def test_full_size_gpt2_small_step_variants(gpu_lib, variant):
+    """The full config-2 step with the int8 encoding (identical to the 1-bit
+    step) and with the polar step on the vote (equal to the chain on sampled
+    matrices), as the benchmark runs them."""
+    wl = W.WORKLOADS[2]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 1)
+    mats = []
+    for (m, n) in wl.shapes:
+        w = (0.02 * torch.randn(m, n, generator=gen, device="cuda")).to(torch.bfloat16)
+        mom = (1e-4 * torch.randn(wl.M, m, n, generator=gen, device="cuda")).to(torch.bfloat16)
+        g = (wl.grad_std * torch.randn(wl.M, m, n, generator=gen, device="cuda")).to(torch.bfloat16)
+        mats.append(sm.MatrixBuffers(w=w, mom=mom, grad=g))
+    ref = [sm.MatrixBuffers(w=mb.w.clone(), mom=mb.mom.clone(), grad=mb.grad) for mb in mats]
+    w_before = [mb.w.clone() for mb in mats]
+    if variant == "int8":
+        sm.StepCall(_cfg(wl, encoding=sm.ENC_INT8), mats)(5)
+        sm.StepCall(_cfg(wl), ref)(5)
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(mats, ref)):
+            assert torch.equal(a.mom, b.mom), j
+            assert torch.equal(a.w.view(torch.int16), b.w.view(torch.int16)), j
+        return
+    cfg = _cfg(wl, vote_polar=True)
+    sm.StepCall(cfg, mats)(5)
+    torch.cuda.synchronize()
+    for j in [0, 1, 3, 46]:
+        w2, v = _vote_polar_chain(cfg, mats[j], w_before[j], sm.ENC_BITS,
+                                  _ns_signs(cfg, sm.ENC_BITS))
+        torch.cuda.synchronize()
+        assert torch.equal(w2.view(torch.int16), mats[j].w.view(torch.int16)), j
+        assert v.abs().eq(1).all(), j                 # odd M: no ties
