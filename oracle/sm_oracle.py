@@ -432,6 +432,58 @@ def update_polar(w_values, d_values, lr: float, wdtype: str) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# CacheMuon fidelity diagnostic: spectral distance of the cached direction
+# --------------------------------------------------------------------------
+
+def spectral_norm_power(e, v0, iters: int) -> float:
+    """Power-iteration estimate of ||E||_2 (the largest singular value).
+
+    [CacheMuon-ja] theoretical analysis: the deviation of the cached direction
+    from the exact one is measured in the spectral norm, ||D_hat - D||_sp <=
+    delta_t.  The estimate follows the plain power method on E^T E from the
+    given start vector v0 (length n): v <- v0 / ||v0||; then `iters` times
+    y = E v, z = E^T y, v = z / ||z|| (stopping at v = 0 if z = 0); the
+    result is ||E v||.  It never exceeds ||E||_2 and reaches it as iters
+    grows when v0 is not orthogonal to the top right singular vector.
+    """
+    e = np.asarray(e, dtype=np.float64)
+    v = np.asarray(v0, dtype=np.float64).reshape(-1)
+    nv = math.sqrt(float(v @ v))
+    if nv == 0.0:
+        return 0.0
+    v = v / nv
+    for _ in range(iters):
+        z = e.T @ (e @ v)
+        nz = math.sqrt(float(z @ z))
+        if nz == 0.0:
+            return 0.0
+        v = z / nz
+    y = e @ v
+    return math.sqrt(float(y @ y))
+
+
+def cache_fidelity(y, q, p: NSParams, v0, iters: int):
+    """The diagnostic for one matrix: (err, distance) of a cached Q on Y.
+
+    [CacheMuon-ja] core mechanism items 2-3 and the diagnostic findings of the
+    experiments: the residual err of the cached candidate D_hat = Q X, and the
+    spectral distance of D_hat from the fresh solve's direction on the same
+    X, ||D_hat - D_fresh||_sp (estimated by the power method above), whose
+    relation to err is what the pages report on.  X = Y / (||Y||_F + eps) in
+    the wide orientation; the distance is taken on the difference in Y's own
+    orientation (m x n), so v0 has n entries.
+    """
+    x, tr = orient(y)
+    x = frobenius_normalize(x, p.eps)
+    cand = cache_reuse_oriented(q, x)
+    fresh, _ = gram_ns_fresh_oriented(x, p)
+    diff = cand - fresh
+    if tr:
+        diff = diff.T
+    return orth_residual(cand), spectral_norm_power(diff, v0, iters)
+
+
+# --------------------------------------------------------------------------
 # The int8 encoding, and the optional local polar step on the vote
 # --------------------------------------------------------------------------
 

@@ -645,3 +645,74 @@ def test_p17_step_with_unanimous_hadamard_vote():
     np.testing.assert_array_equal(results[(O.ENC_BITS, True)].astype(np.float32), want)
     for vp in (False, True):
         np.testing.assert_array_equal(results[(O.ENC_INT8, vp)], results[(O.ENC_BITS, vp)])
+
+
+# ---------------------------------------------------------------- P-18 spectral distance
+
+@pytest.mark.parametrize("m,n", [(40, 40), (30, 70), (90, 20)])
+def test_p18_power_method_converges_to_svd(m, n):
+    rng = np.random.default_rng(m * 1000 + n)
+    r = min(m, n)
+    s = np.linspace(3.0, 0.5, r)              # a clear gap at the top
+    u = _orthonormal(rng, m, r)
+    v = _orthonormal(rng, n, r)
+    e = u @ np.diag(s) @ v.T
+    v0 = rng.standard_normal(n)
+    est = O.spectral_norm_power(e, v0, 300)
+    assert abs(est - np.linalg.svd(e, compute_uv=False)[0]) <= 1e-10 * 3.0
+    # a lower bound at every iteration count, increasing
+    prev = 0.0
+    for k in (0, 1, 2, 5, 10):
+        cur = O.spectral_norm_power(e, v0, k)
+        assert cur <= 3.0 + 1e-12 and cur >= prev - 1e-12
+        prev = cur
+
+
+def test_p18_power_method_closed_forms():
+    rng = np.random.default_rng(18)
+    # rank one: one iteration is exact, sigma = |a| |b|
+    a, b = rng.standard_normal(12), rng.standard_normal(9)
+    v0 = rng.standard_normal(9)
+    assert math.isclose(O.spectral_norm_power(np.outer(a, b), v0, 1),
+                        np.linalg.norm(a) * np.linalg.norm(b), rel_tol=1e-13)
+    # diagonal: v_k is proportional to d^(2k) * v0, so the estimate is
+    # ||d^(2k+1) v0|| / ||d^(2k) v0||
+    d = np.array([2.0, -1.5, 1.0, 0.25])
+    v0 = np.array([0.1, 1.0, 1.0, 1.0])
+    for k in (0, 1, 3, 8):
+        w = d ** (2 * k) * v0
+        want = np.linalg.norm(d * w) / np.linalg.norm(w)
+        assert math.isclose(O.spectral_norm_power(np.diag(d), v0, k), want, rel_tol=1e-13)
+    # zero matrix, zero start vector, start vector orthogonal to the row space
+    assert O.spectral_norm_power(np.zeros((5, 7)), np.ones(7), 4) == 0.0
+    assert O.spectral_norm_power(np.eye(3), np.zeros(3), 4) == 0.0
+    e = np.zeros((3, 3)); e[0, 0] = 5.0
+    assert O.spectral_norm_power(e, np.array([0.0, 1.0, 0.0]), 3) == 0.0
+
+
+def test_p18_fidelity_of_a_fresh_cache_is_zero_and_tall_matches_wide():
+    """A Q just produced by the fresh solve on the same input reproduces the
+    fresh direction (distance 0), and a tall input gives the transpose's
+    numbers."""
+    rng = np.random.default_rng(81)
+    p = O.NSParams()
+    y = rng.standard_normal((24, 60))
+    x = O.frobenius_normalize(y, p.eps)
+    _, q = O.gram_ns_fresh_oriented(x, p)
+    v0 = rng.standard_normal(60)
+    err, dist = O.cache_fidelity(y, q, p, v0, 20)
+    assert dist <= 1e-12
+    assert math.isclose(err, O.orth_residual(q @ x), rel_tol=1e-12)
+    # a stale Q (from another input) has a positive distance, and the tall
+    # input's distance equals the wide one with the start vector in the
+    # other dimension
+    q_stale = O.gram_ns_fresh_oriented(O.frobenius_normalize(
+        y + 0.3 * rng.standard_normal(y.shape), p.eps), p)[1]
+    err_w, dist_w = O.cache_fidelity(y, q_stale, p, rng.standard_normal(60), 200)
+    err_t, dist_t = O.cache_fidelity(y.T, q_stale, p, rng.standard_normal(24), 200)
+    assert dist_w > 1e-3
+    assert math.isclose(err_w, err_t, rel_tol=1e-12)
+    assert math.isclose(dist_w, dist_t, rel_tol=1e-8)
+    cand = q_stale @ x
+    fresh = O.gram_ns_fresh_oriented(x, p)[0]
+    assert math.isclose(dist_w, np.linalg.svd(cand - fresh, compute_uv=False)[0], rel_tol=1e-8)
