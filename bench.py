@@ -17,6 +17,7 @@ main `value` is always the 1-bit vote step).
   python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu]
   python bench.py --copy-calibration   # plain device copy of known size, for
                                        # scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
+  python bench.py --fidelity [--gamma G] # CacheMuon fidelity diagnostic (config 4)
 
 roofline.traffic is the dominant kernel's HBM bytes per launch from the
 rocprofv3 counter summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each
@@ -52,6 +53,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter scaling)")
+    ap.add_argument("--fidelity", action="store_true",
+                    help="CacheMuon fidelity diagnostic instead of the benchmark line: per step, "
+                         "the residual and the spectral distance of the cached direction from a "
+                         "fresh solve, and the refresh rate (default config 4)")
+    ap.add_argument("--fidelity-steps", type=int, default=12)
+    ap.add_argument("--fidelity-iters", type=int, default=30,
+                    help="power-method iterations of the spectral distance")
+    ap.add_argument("--fidelity-matrices", type=int, default=0,
+                    help="diagnose only the first N matrices (0 = all)")
     ap.add_argument("--variant-steps", type=int, default=10,
                     help="timed steps of each step variant (int8 encoding, polar step on the "
                          "vote); 0 skips them")
@@ -305,6 +315,118 @@ def cpu_baseline(wl, seconds):
             "seconds_per_step": sec_per_step}
 
 
+def _pearson(xs, ys):
+    import math
+    n = len(xs)
+    if n < 2:
+        return None
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    sxx = sum((x - mx) ** 2 for x in xs)
+    syy = sum((y - my) ** 2 for y in ys)
+    return sxy / math.sqrt(sxx * syy) if sxx > 0 and syy > 0 else None
+
+
+def _ranks(xs):
+    order = sorted(range(len(xs)), key=lambda i: xs[i])
+    r = [0.0] * len(xs)
+    i = 0
+    while i < len(order):
+        j = i
+        while j + 1 < len(order) and xs[order[j + 1]] == xs[order[i]]:
+            j += 1
+        for k in range(i, j + 1):
+            r[order[k]] = (i + j) / 2.0
+        i = j + 1
+    return r
+
+
+def fidelity(args, sm, torch, W):
+    """CacheMuon fidelity diagnostic (the residual trigger against the spectral
+    distance of the cached direction from a fresh solve, and the refresh rate)
+    on an AR(1) gradient stream G_t = rho G_{t-1} + sqrt(1 - rho^2) sigma xi_t.
+    After each step, for every diagnosed matrix: the cache as it was before the
+    step is applied to the step's own momentum (forced reuse: D_hat and err),
+    a fresh solve runs on a copy (D_fresh), and ||D_hat - D_fresh||_sp is
+    estimated by the power method from a seeded start vector."""
+    import math
+    cfg_n = args.config if args.config != 2 else 4
+    wl = W.WORKLOADS[cfg_n]
+    if wl.algo != sm.CACHE_MUON:
+        raise SystemExit("--fidelity needs a CacheMuon configuration")
+    mats = build_state(wl)
+    cfg = step_config(wl, args.gamma)
+    nd = len(mats) if args.fidelity_matrices <= 0 else min(args.fidelity_matrices, len(mats))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 4242)
+    rho = wl.ar1_rho
+    diag = torch.zeros(len(mats), wl.M, 2, device="cuda")
+    call = sm.StepCall(cfg, mats, diag=diag)
+    # the diagnosed matrices, grouped by shape so each diagnostic call is batched
+    groups = {}
+    for j, mb in enumerate(mats[:nd]):
+        groups.setdefault(tuple(mb.w.shape), []).append(j)
+    v0s = {sh: torch.randn(len(js) * wl.M, sh[1], generator=gen, device="cuda")
+           for sh, js in groups.items()}
+    curve, pairs = [], []
+    spec_ms, spec_work, spec_n = 0.0, 0.0, 0
+    for t in range(1, args.fidelity_steps + 1):
+        if t > 1:
+            for mb in mats:
+                xi = torch.randn(mb.grad.shape, generator=gen, device="cuda")
+                g = rho * mb.grad.float() + math.sqrt(1 - rho * rho) * wl.grad_std * xi
+                mb.grad.copy_(g.to(mb.grad.dtype))
+                del xi, g
+        before = [(mb.q_cache.clone(), mb.cache_state.clone()) for mb in mats[:nd]]
+        call(t)
+        torch.cuda.synchronize()
+        refreshed = diag[:, :, 1].float().mean().item()
+        errs, dists = [], []
+        if t > 1:
+            sm.profile_enable(True)
+            sm.profile_reset()
+            for sh, js in groups.items():
+                x = torch.cat([mats[j].mom for j in js])
+                q0 = torch.cat([before[j][0] for j in js])
+                c0 = torch.cat([before[j][1] for j in js])
+                d_hat, err, _ = sm.gram_ns_cached(x, q0.clone(), c0.clone(), t, 0.0,
+                                                  mode=sm.MODE_FORCE_REUSE, params=cfg.ns)
+                d_fr, _, _ = sm.gram_ns_cached(x, q0, c0, t, 0.0,
+                                               mode=sm.MODE_FORCE_FRESH, params=cfg.ns)
+                dist = sm.spectral_norm(d_hat, d_fr, v0s[sh], args.fidelity_iters)
+                errs += err.cpu().tolist()
+                dists += dist.cpu().tolist()
+                del x, q0, c0, d_hat, d_fr
+            ms, n, work = sm.profile_read("spectral")
+            spec_ms, spec_work, spec_n = spec_ms + ms, spec_work + work, spec_n + n
+            sm.profile_enable(False)
+            pairs += list(zip(errs, dists))
+        curve.append({"t": t, "refresh_rate": refreshed,
+                      "err_mean": sum(errs) / len(errs) if errs else None,
+                      "err_max": max(errs) if errs else None,
+                      "dist_mean": sum(dists) / len(dists) if dists else None,
+                      "dist_max": max(dists) if dists else None})
+        print(json.dumps({"fidelity_step": t, **curve[-1]}), file=sys.stderr, flush=True)
+    e = [p[0] for p in pairs]
+    d = [p[1] for p in pairs]
+    achieved = spec_work / (spec_ms * 1e-3) / 1e9 if spec_ms > 0 else None
+    out = {
+        "metric": "CacheMuon fidelity: residual err vs ||D_hat - D_fresh||_sp, refresh rate",
+        "workload": wl.name, "gamma": cfg.gamma, "steps": args.fidelity_steps,
+        "diagnosed_matrices": nd, "power_iters": args.fidelity_iters,
+        "grad": f"AR(1) rho={rho} sigma={wl.grad_std}",
+        "pearson_err_dist": _pearson(e, d),
+        "spearman_err_dist": _pearson(_ranks(e), _ranks(d)) if len(e) > 1 else None,
+        "refresh_rate_mean": sum(c["refresh_rate"] for c in curve) / len(curve),
+        "spectral_roofline": {"bound": "hbm", "kernel": "k_pm_av / k_pm_atv (+ norms)",
+                              "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": achieved / PEAK_HBM_GBS if achieved else None,
+                              "launches": spec_n, "ms": spec_ms},
+        "curve": curve,
+    }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -318,6 +440,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.fidelity:
+        fidelity(args, sm, torch, W)
         return
     wl = W.WORKLOADS[args.config]
     mats = build_state(wl)

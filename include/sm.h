@@ -211,6 +211,34 @@ sm_status sm_polar_update(void* w, int wdt, const void* d, int ddt, int64_t coun
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Spectral norm of a difference (the CacheMuon fidelity diagnostic).
+ * [CacheMuon-ja] theoretical analysis: the cached direction's deviation
+ * from the exact one is bounded in the spectral norm, ||D_hat - D||_sp <=
+ * delta_t; experiments, diagnostic findings: the residual trigger tracks the
+ * agreement between cached and fresh updates.  With the cached candidate
+ * (sm_gram_ns_cached, mode 2) and the fresh direction (mode 1, on a copy of
+ * the cache) of the same momentum, this call measures that distance.
+ *
+ * Per problem b, with E = a_b - b_b (b == NULL: E = a_b), m x n row-major
+ * in dt: v = v0_b / ||v0_b||; `iters` times y = E v, z = E^T y, v = z/||z||
+ * (v = 0 once z = 0); out[b] = ||E v||, a lower bound of ||E||_2 that
+ * reaches it as iters grows (unless v0_b is orthogonal to E's top right
+ * singular vector).  Arithmetic in float32 (norms in double); the sums run
+ * in a fixed order.
+ * a, b : [batch][m][n] in dt (element-aligned; 16-byte alignment and n % 8
+ *        == 0 take the vector path).  v0 : [batch][n] float32, the start
+ *        vectors (the caller's, e.g. seeded random).  out : [batch] float32.
+ * iters: 0..100000.  ws : at least sm_spectral_norm_ws(...) bytes, 256-byte
+ *        aligned.
+ * Errors: SM_ERR_ARG (null/misaligned, bad iters, out overlapping ws),
+ *         SM_ERR_SHAPE, SM_ERR_DTYPE, SM_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+sm_status sm_spectral_norm_ws(int batch, int m, int n, size_t* ws_bytes);
+sm_status sm_spectral_norm(const void* a, const void* b, int dt, int batch, int m, int n,
+                           const float* v0, int iters, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Whole optimizer step over a set of weight matrices.
  *
  * algo SM_SIGN_MUON  ([SignMuon-ja] section 2, algorithm flow steps 1-4):
@@ -300,7 +328,8 @@ enum {
   SM_K_LION = 8,         /* fused Lion interpolation/EMA/sign/pack bytes  */
   SM_K_POLAR_UPDATE = 9, /* W <- W - lr D                          bytes  */
   SM_K_MISC = 10,        /* small finalize / copy kernels          bytes  */
-  SM_K_NUM_KINDS = 11
+  SM_K_SPECTRAL = 11,    /* power-method passes (diagnostic)       bytes  */
+  SM_K_NUM_KINDS = 12
 };
 sm_status sm_profile_enable(int on);
 sm_status sm_profile_reset(void);

@@ -23,7 +23,7 @@ MODE_TRIGGER, MODE_FORCE_FRESH, MODE_FORCE_REUSE = 0, 1, 2
 ENC_BITS, ENC_INT8 = 0, 1
 
 KERNEL_KINDS = ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pack",
-                "vote_update", "lion", "polar_update", "misc"]
+                "vote_update", "lion", "polar_update", "misc", "spectral"]
 
 # Every function the header declares, with its ctypes signature.
 c_int, c_int32, c_int64, c_float, c_double = (ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
@@ -68,6 +68,9 @@ SIGNATURES = {
                                     c_void_p, c_void_p]),
     "sm_vote": (c_int, [c_void_p, c_int, c_int, c_int64, c_int64, c_void_p, c_int, c_void_p]),
     "sm_polar_update": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int64, c_float, c_void_p]),
+    "sm_spectral_norm_ws": (c_int, [c_int, c_int, c_int, P(c_size_t)]),
+    "sm_spectral_norm": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int,
+                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "sm_step_ws": (c_int, [P(Config), P(Matrix), c_int, P(c_size_t)]),
     "sm_step": (c_int, [P(Config), P(Matrix), c_int, c_int64, c_void_p, c_size_t, c_void_p,
                         c_void_p]),

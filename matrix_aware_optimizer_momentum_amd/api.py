@@ -240,6 +240,31 @@ def polar_update(w: torch.Tensor, d: torch.Tensor, lr: float) -> torch.Tensor:
     return w
 
 
+def spectral_norm(a: torch.Tensor, b: Optional[torch.Tensor], v0: torch.Tensor,
+                  iters: int, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Power-method ||a - b||_2 per problem (b None: ||a||_2).
+
+    a, b: [batch, m, n] or [m, n] (same dtype); v0: float32 [batch, n] start
+    vectors.  Returns float32 [batch]."""
+    _dev(a, "a"); _dev(v0, "v0")
+    batch, m, n = _bmn(a)
+    if b is not None:
+        _dev(b, "b")
+        if b.shape != a.shape or b.dtype != a.dtype:
+            raise ValueError("b must match a in shape and dtype")
+    if v0.dtype != torch.float32 or v0.numel() != batch * n:
+        raise ValueError("v0 must be float32 with batch * n entries")
+    out = torch.empty(batch, dtype=torch.float32, device=a.device)
+    need = ctypes.c_size_t(0)
+    B.check(B.lib().sm_spectral_norm_ws(batch, m, n, ctypes.byref(need)), "sm_spectral_norm_ws")
+    ws = _ws(need.value, a.device, ws)
+    code = B.lib().sm_spectral_norm(a.data_ptr(), b.data_ptr() if b is not None else None,
+                                    _dt(a), batch, m, n, v0.data_ptr(), iters, out.data_ptr(),
+                                    ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
+    B.check(code, "sm_spectral_norm")
+    return out
+
+
 # ------------------------------------------------------------------ sm_step
 
 @dataclass

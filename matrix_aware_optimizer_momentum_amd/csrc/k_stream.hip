@@ -369,7 +369,7 @@ __global__ void k_gather_has_cache(PtrTbl cs, int per, int nprob, int32_t* hc) {
 __global__ void k_cache_decide(const float* resid, int parts, int nprob, int r,
                                const int32_t* hc, PtrTbl cs, int per, int mode, float gamma,
                                int32_t t32, int32_t* flags, float* err, int32_t* refreshed,
-                               float* diag, int diag_stride) {
+                               PtrTbl diag, bool has_diag) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nprob) return;
   int refresh;
@@ -385,9 +385,10 @@ __global__ void k_cache_decide(const float* resid, int parts, int nprob, int r,
   flags[b] = refresh;
   if (err) err[b] = e;
   if (refreshed) refreshed[b] = refresh;
-  if (diag) {
-    diag[(int64_t)b * diag_stride] = e;
-    diag[(int64_t)b * diag_stride + 1] = (float)refresh;
+  if (has_diag) {   // problem b's {err, refreshed} row, by the table of matrices
+    float* row = const_cast<float*>(reinterpret_cast<const float*>(tbl_addr(diag, b, per, 8)));
+    row[0] = e;
+    row[1] = (float)refresh;
   }
   if (refresh) {
     int32_t* st = const_cast<int32_t*>(reinterpret_cast<const int32_t*>(tbl_addr(cs, b, per, 8)));
@@ -409,16 +410,6 @@ inline int stream_blocks(int64_t count, int nprob) {
 
 // ------------------------------------------------------------------ launchers
 
-#define SM_DISPATCH_DT(dt, T, ...)                   \
-  do {                                               \
-    if ((dt) == BF16) {                              \
-      typedef bf16_t T;                              \
-      __VA_ARGS__;                                   \
-    } else {                                         \
-      typedef float T;                               \
-      __VA_ARGS__;                                   \
-    }                                                \
-  } while (0)
 
 sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
                             int64_t count, int mdt, int gdt, float beta, void* x, int xdt,
@@ -575,12 +566,14 @@ sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t*
 sm_status launch_cache_decide(const float* resid_partials, int parts, int nprob, int r,
                               const int32_t* hc, const PtrTbl& cs, int per, int mode,
                               float gamma, int64_t t, int32_t* flags, float* err,
-                              int32_t* refreshed, float* diag, int diag_stride, hipStream_t s) {
+                              int32_t* refreshed, const PtrTbl* diag, hipStream_t s) {
   if (nprob <= 0) return SM_OK;
+  PtrTbl dt;
+  if (diag) dt = *diag; else std::memset(&dt, 0, sizeof(dt));
   prof_begin(SM_K_MISC, (double)nprob * (parts * 4.0 + 24.0), s);
   hipLaunchKernelGGL(k_cache_decide, dim3((nprob + 63) / 64), dim3(64), 0, s, resid_partials,
                      parts, nprob, r, hc, cs, per, mode, gamma, (int32_t)t, flags, err,
-                     refreshed, diag, diag_stride);
+                     refreshed, dt, diag != nullptr);
   prof_end(s);
   return check_launch();
 }

@@ -30,11 +30,6 @@ sm_status check_launch() {
   return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 
-#define SM_TRY(expr)                    \
-  do {                                  \
-    sm_status _st = (expr);             \
-    if (_st != SM_OK) return _st;       \
-  } while (0)
 
 // ====================================================================== profiling
 
@@ -393,7 +388,7 @@ void carve_gram(Carver& cv, int batch, int m, int n, GramWs& w) {
 // qtbl[b / qper] + (b % qper) * r*r floats; its {has_cache, a_t} pair at
 // cstbl[b / qper] + (b % qper) * 2 ints.
 sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cstbl, int qper,
-                    float* err_out, int32_t* refr_out, float* diag, int diag_stride,
+                    float* err_out, int32_t* refr_out, const PtrTbl* diag,
                     const GramWs& w, const float* scale, int dt, int batch, int m, int n,
                     const sm_ns_params& p, float gamma, int mode, int64_t t, hipStream_t s) {
   const bool wide = m <= n;
@@ -418,7 +413,7 @@ sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cs
     SM_TRY(launch_gemm(pr, dt, SM_K_PROBE, s));
   }
   SM_TRY(launch_cache_decide(w.resid, gemm_tiles(dt, r, r), batch, r, w.hc, cstbl, qper, mode,
-                             gamma, t, w.flags, err_out, refr_out, diag, diag_stride, s));
+                             gamma, t, w.flags, err_out, refr_out, diag, s));
 
   // Q_k lives in the cache for k == K (mod 2) so that Q_K lands there.
   auto qbuf_is_cache = [&](int k) { return ((K - k) % 2) == 0; };
@@ -640,7 +635,7 @@ const char* sm_status_string(int s) {
 
 int sm_last_hip_error(void) { return g_last_hip.load(); }
 
-int sm_version(void) { return 2; }
+int sm_version(void) { return 3; }
 
 sm_status sm_ns_polar_ws(int dt, int batch, int m, int n, size_t* ws_bytes) {
   if (!ws_bytes) return SM_ERR_ARG;
@@ -725,7 +720,7 @@ sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_sta
     SM_TRY(launch_scale_finalize(partials, batch, p->eps, scale, s));
   }
   const PtrTbl qt = tbl_one(q), cs = tbl_one(cache_state);
-  return gram_core(x, d, qt, cs, batch, err, refreshed, nullptr, 2, w,
+  return gram_core(x, d, qt, cs, batch, err, refreshed, nullptr, w,
                    normalize ? scale : nullptr, dt, batch, m, n, *p, gamma, mode, t, s);
 }
 
@@ -799,6 +794,32 @@ sm_status sm_polar_update(void* w, int wdt, const void* d, int ddt, int64_t coun
   if (overlap(w, (size_t)count * dt_size(wdt), d, (size_t)count * dt_size(ddt))) return SM_ERR_ARG;
   const PtrTbl wt = tbl_one(w);
   return launch_polar_update(d, ddt, 1, count, wt, wdt, lr, s);
+}
+
+sm_status sm_spectral_norm_ws(int batch, int m, int n, size_t* ws_bytes) {
+  if (!ws_bytes) return SM_ERR_ARG;
+  SM_TRY(check_shape(batch, m, n));
+  *ws_bytes = spectral_norm_ws_bytes(batch, m, n);
+  return SM_OK;
+}
+
+sm_status sm_spectral_norm(const void* a, const void* b, int dt, int batch, int m, int n,
+                           const float* v0, int iters, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t s) {
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  SM_TRY(check_shape(batch, m, n));
+  if (!a || !v0 || !out || !ws || iters < 0 || iters > 100000) return SM_ERR_ARG;
+  const uintptr_t es = dt_size(dt);
+  if ((reinterpret_cast<uintptr_t>(a) % es) || (b && (reinterpret_cast<uintptr_t>(b) % es)))
+    return SM_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(v0) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return SM_ERR_ARG;
+  const size_t need = spectral_norm_ws_bytes(batch, m, n);
+  if (ws_bytes < need) return SM_ERR_WORKSPACE;
+  if (overlap(out, (size_t)batch * 4, ws, ws_bytes) || overlap(v0, (size_t)batch * n * 4, ws, ws_bytes))
+    return SM_ERR_ARG;
+  return launch_spectral_norm(a, b, dt, batch, m, n, v0, iters, out, ws, s);
 }
 
 sm_status sm_step_ws(const sm_config* c, const sm_matrix* mats, int nmat, size_t* ws_bytes) {
@@ -914,16 +935,14 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
       const Chunk& ch = chunks[ci];
       ChunkRun& r = runs[ci];
       if (c->algo == SM_CACHE_MUON) {
-        // diag rows follow the matrices' order; a chunk's matrices may not be
-        // consecutive, so write per chunk into the rows of its first matrix
-        // only when they are, else skip diag for that chunk.
-        float* dg = nullptr;
-        if (diag) {
-          bool consecutive = true;
-          for (int j = 1; j < r.nc; ++j) consecutive &= (ch.mats[j] == ch.mats[0] + j);
-          if (consecutive) dg = diag + (int64_t)ch.mats[0] * M * 2;
-        }
-        SM_TRY(gram_core(r.w.x0, r.w.d, r.qt, r.cs, M, nullptr, nullptr, dg, 2, r.w.gram,
+        // diag rows follow the caller's matrix order: the chunk's matrix j
+        // (any position in that order) has its M rows at diag + mats[j]*M*2
+        PtrTbl dt;
+        std::memset(&dt, 0, sizeof(dt));
+        for (int j = 0; diag && j < r.nc; ++j)
+          dt.p[j] = reinterpret_cast<const char*>(diag + (int64_t)ch.mats[j] * M * 2);
+        SM_TRY(gram_core(r.w.x0, r.w.d, r.qt, r.cs, M, nullptr, nullptr, diag ? &dt : nullptr,
+                         r.w.gram,
                          r.w.scale, c->mdt, r.B, ch.m, ch.n, c->ns, c->gamma, c->cache_mode, t,
                          s));
         continue;
@@ -1048,7 +1067,7 @@ sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double*
 const char* sm_kernel_kind_name(int kind) {
   static const char* names[SM_K_NUM_KINDS] = {
       "ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe",
-      "sign_pack", "vote_update", "lion", "polar_update", "misc"};
+      "sign_pack", "vote_update", "lion", "polar_update", "misc", "spectral"};
   if (kind < 0 || kind >= SM_K_NUM_KINDS) return "unknown";
   return names[kind];
 }

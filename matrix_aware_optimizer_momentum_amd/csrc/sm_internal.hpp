@@ -37,6 +37,18 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+// Runs __VA_ARGS__ with T the element type of dt (bf16_t or float).
+#define SM_DISPATCH_DT(dt, T, ...)                   \
+  do {                                               \
+    if ((dt) == BF16) {                              \
+      typedef bf16_t T;                              \
+      __VA_ARGS__;                                   \
+    } else {                                         \
+      typedef float T;                               \
+      __VA_ARGS__;                                   \
+    }                                                \
+  } while (0)
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ __forceinline__ static float load(const float* p) { return *p; }
@@ -101,6 +113,14 @@ void prof_end(hipStream_t s);
 sm_status hip_fail(hipError_t e);
 sm_status check_launch();
 
+// Returns the status of expr from the calling function unless it is SM_OK.
+#define SM_TRY(expr)                    \
+  do {                                  \
+    sm_status _st = (expr);             \
+    if (_st != SM_OK) return _st;       \
+  } while (0)
+
+
 // ---------------------------------------------------------------- streaming kernels
 
 // Number of partial sums per problem used by every sum-of-squares producer.
@@ -151,6 +171,13 @@ sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t
                       int nmat, int64_t count, const PtrTbl& w, int wdt, float lr,
                       int8_t* vote_out, bool update, hipStream_t s);
 
+// Power-method spectral norm of E_b = A_b - B_b (b may be null), batch
+// problems of m x n (k_power.hip); ws of spectral_norm_ws_bytes().
+int spectral_row_chunks(int batch, int m, int n);
+size_t spectral_norm_ws_bytes(int batch, int m, int n);
+sm_status launch_spectral_norm(const void* a, const void* b, int dt, int batch, int m, int n,
+                               const float* v0, int iters, float* out, void* ws, hipStream_t s);
+
 // W <- rnd(fp32(W) - fp32(lr*D)) for nmat matrices, D contiguous [nmat][count].
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
                               int wdt, float lr, hipStream_t s);
@@ -162,12 +189,13 @@ sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t*
 
 // CacheMuon accept/refresh decision per problem (see sm_gram_ns_cached):
 // err from the residual partials, flags[b] = 1 to refresh, outputs err /
-// refreshed / diag (each optional), and {1, t} written to cache_state on a
+// refreshed / diag (each optional; problem b's {err, refreshed} float pair
+// at tbl_addr(*diag, b, per, 8)), and {1, t} written to cache_state on a
 // refresh.
 sm_status launch_cache_decide(const float* resid_partials, int parts, int nprob, int r,
                               const int32_t* hc, const PtrTbl& cs, int per, int mode,
                               float gamma, int64_t t, int32_t* flags, float* err,
-                              int32_t* refreshed, float* diag, int diag_stride, hipStream_t s);
+                              int32_t* refreshed, const PtrTbl* diag, hipStream_t s);
 
 // ---------------------------------------------------------------- batched MFMA GEMM
 

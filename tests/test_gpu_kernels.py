@@ -356,3 +356,80 @@ def test_gram_reuse_on_identical_input_is_stable(gpu_lib):
     assert rel_fro(to_np(d2), to_np(d1)) <= 1e-5
     for k in range(2):
         assert abs(err.cpu().numpy()[k] - O.orth_residual(to_np(d1)[k].astype(np.float64))) < 1e-4
+
+
+# ------------------------------------------------------------------ spectral distance (CacheMuon fidelity)
+
+SPEC_CASES = [
+    # dt, batch, m, n, iters, with_b
+    ("f32", 1, 37, 53, 0, True),
+    ("f32", 2, 37, 53, 5, True),
+    ("f32", 3, 64, 200, 30, False),
+    ("f32", 2, 2100, 9, 12, True),
+    ("bf16", 3, 64, 200, 30, True),
+    ("bf16", 2, 520, 136, 20, True),
+    ("bf16", 2, 768, 2304, 15, True),
+    ("bf16", 1, 5, 4099, 8, True),
+]
+
+
+@pytest.mark.parametrize("case", SPEC_CASES, ids=lambda c: f"{c[0]}-b{c[1]}-{c[2]}x{c[3]}-it{c[4]}")
+def test_spectral_norm_matches_oracle(gpu_lib, case):
+    import matrix_aware_optimizer_momentum_amd as sm
+    dt, batch, m, n, iters, with_b = case
+    rng = np.random.default_rng(batch * 1009 + m + n + iters)
+    a = to_gpu(rng.standard_normal((batch, m, n)).astype(np.float32), dt)
+    b = to_gpu((rng.standard_normal((batch, m, n)) * 0.5).astype(np.float32), dt) if with_b else None
+    v0 = torch.from_numpy(rng.standard_normal((batch, n)).astype(np.float32)).cuda()
+    out = sm.spectral_norm(a, b, v0, iters)
+    torch.cuda.synchronize()
+    an, v0n = to_np(a).astype(np.float64), v0.cpu().numpy().astype(np.float64)
+    bn = to_np(b).astype(np.float64) if with_b else np.zeros_like(an)
+    for k in range(batch):
+        want = O.spectral_norm_power(an[k] - bn[k], v0n[k], iters)
+        got = float(out.cpu().numpy()[k])
+        assert abs(got - want) <= 2e-4 * want, (k, got, want)
+
+
+def test_spectral_norm_zero_difference_and_zero_start(gpu_lib):
+    import matrix_aware_optimizer_momentum_amd as sm
+    rng = np.random.default_rng(3)
+    a = to_gpu(rng.standard_normal((2, 30, 40)).astype(np.float32), "f32")
+    v0 = torch.from_numpy(rng.standard_normal((2, 40)).astype(np.float32)).cuda()
+    assert sm.spectral_norm(a, a.clone(), v0, 6).cpu().tolist() == [0.0, 0.0]
+    assert sm.spectral_norm(a, None, torch.zeros_like(v0), 6).cpu().tolist() == [0.0, 0.0]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(96, 256), (256, 96)])
+def test_cache_fidelity_chain_matches_oracle(gpu_lib, dt, shape):
+    """The diagnostic as a chain of entry points: the cached candidate
+    (forced reuse) and the fresh direction (forced fresh, on a copy of the
+    cache) of the same input, their spectral distance, and the residual,
+    against the oracle's cache_fidelity with the same stale Q and start
+    vector."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    m, n = shape
+    r = min(m, n)
+    rng = np.random.default_rng(m + 7 * n)
+    p = O.NSParams()
+    y = rng.standard_normal((m, n)).astype(np.float32)
+    y_old = y + 0.4 * rng.standard_normal((m, n)).astype(np.float32)
+    xo, _ = O.orient(y_old)
+    q_stale = O.gram_ns_fresh_oriented(O.frobenius_normalize(xo, p.eps), p)[1].astype(np.float32)
+    yt = to_gpu(y, dt)
+    y_used = to_np(yt).astype(np.float64)
+    q = torch.from_numpy(q_stale[None]).cuda()
+    cs = torch.tensor([[1, 1]], dtype=torch.int32, device="cuda")
+    q2, cs2 = q.clone(), cs.clone()
+    d_hat, err, _ = sm.gram_ns_cached(yt[None], q, cs, 2, 0.0, mode=sm.MODE_FORCE_REUSE)
+    d_fresh, _, _ = sm.gram_ns_cached(yt[None], q2, cs2, 2, 0.0, mode=sm.MODE_FORCE_FRESH)
+    v0 = torch.from_numpy(rng.standard_normal((1, n)).astype(np.float32)).cuda()
+    dist = sm.spectral_norm(d_hat, d_fresh, v0, 50)
+    torch.cuda.synchronize()
+    err_or, dist_or = O.cache_fidelity(y_used, q_stale.astype(np.float64), p,
+                                       v0.cpu().numpy()[0].astype(np.float64), 50)
+    tol = 1e-3 if dt == "f32" else 3e-2
+    assert abs(err.item() - err_or) <= tol * max(err_or, 1.0), (err.item(), err_or)
+    assert abs(dist.item() - dist_or) <= tol, (dist.item(), dist_or)
+    assert dist_or > 0.03                           # the stale cache is measurably off

@@ -214,6 +214,33 @@ def test_cache_muon_step_equals_entry_point_chain(gpu_lib, dt):
             assert all(mb.cache_state.cpu().tolist() == [[1, 1]] for mb in st.mats)
 
 
+def test_cache_muon_diag_rows_with_interleaved_shapes(gpu_lib):
+    """diag rows follow the caller's matrix order even when the matrices of
+    one shape are not next to each other (GPT-2 layer sets alternate shapes)."""
+    wl = W.WORKLOADS[4].scaled(wdt="f32", mdt="f32", gdt="f32", M=2, update=sm.UPDATE_VOTE)
+    shapes = [(96, 256), (64, 64), (96, 256), (64, 64), (256, 96)]
+    st = Seeded(wl, shapes)
+    _cache_bufs(st, 2)
+    cfg = _cfg(wl)
+    for t, (gamma, mode) in enumerate([(0.0, 0), (1e9, 0), (-1.0, 0)], 1):
+        cfg.gamma, cfg.cache_mode = gamma, mode
+        q_before = [mb.q_cache.clone() for mb in st.mats]
+        cs_before = [mb.cache_state.clone() for mb in st.mats]
+        diag = torch.full((len(shapes), 2, 2), 7.0, device="cuda")
+        sm.StepCall(cfg, st.mats, diag=diag)(t)
+        for j, mb in enumerate(st.mats):
+            _, err, refr = sm.gram_ns_cached(mb.mom, q_before[j], cs_before[j], t, gamma,
+                                             mode=mode, params=cfg.ns)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(diag[j, :, 0].cpu().numpy(), err.cpu().numpy())
+            np.testing.assert_array_equal(diag[j, :, 1].cpu().numpy(),
+                                          refr.cpu().numpy().astype(np.float32))
+        if t == 2:
+            assert not diag[:, :, 1].any()          # huge gamma: every cache reused
+        else:
+            assert diag[:, :, 1].all()              # first step, and gamma < 0
+
+
 def test_cache_muon_reuse_step_with_oracle_written_cache(gpu_lib):
     """A reuse step whose cached Q comes from the oracle's own fresh solve."""
     wl = W.WORKLOADS[4].scaled(wdt="f32", mdt="f32", gdt="f32")
