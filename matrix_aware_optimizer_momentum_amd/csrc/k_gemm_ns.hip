@@ -372,29 +372,31 @@ struct Ident {
   uint32_t hi, lo;
 };
 
+// Identity fragments of the two k16 slices (a_hi, and a_lo for two terms),
+// built once when a tile reaches its identity group.
+struct IdFrags {
+  bf16x8 h[2], l[2];
+};
+
 #define SM_MFMA(A_, B_, C_) C_ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_, B_, C_, 0, 0, 0)
 
 // Identity MFMAs of slice s for block IB.
 template <int IDM, int IDT, int IB>
-__device__ __forceinline__ void ident_mma(f32x16 (&acc)[4][4], const Frags& f, const Ident& id,
-                                          int s) {
+__device__ __forceinline__ void ident_mma(f32x16 (&acc)[4][4], const Frags& f,
+                                          const IdFrags& idf, int s) {
   if constexpr (IDM == 1) {
-    const bf16x8 h = ident_frag(s, id.hi);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) SM_MFMA(h, f.b[j], acc[IB][j]);
+    for (int j = 0; j < 4; ++j) SM_MFMA(idf.h[s], f.b[j], acc[IB][j]);
     if constexpr (IDT == 2) {
-      const bf16x8 l = ident_frag(s, id.lo);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) SM_MFMA(l, f.b[j], acc[IB][j]);
+      for (int j = 0; j < 4; ++j) SM_MFMA(idf.l[s], f.b[j], acc[IB][j]);
     }
   } else if constexpr (IDM == 2) {
-    const bf16x8 h = ident_frag(s, id.hi);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], h, acc[i][IB]);
+    for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], idf.h[s], acc[i][IB]);
     if constexpr (IDT == 2) {
-      const bf16x8 l = ident_frag(s, id.lo);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], l, acc[i][IB]);
+      for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], idf.l[s], acc[i][IB]);
     }
   }
 }
@@ -417,7 +419,7 @@ __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& 
                                          const bf16_t* cur, const bf16_t* nxt, uint32_t ldb,
                                          uint32_t wbase, const LoadPos& L, int ls,
                                          const FragOffs<AKR>& fa, const FragOffs<BKR>& fb,
-                                         const Ident& id, bool wait_lenient) {
+                                         const IdFrags& idf, bool wait_lenient) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int i = q >> 2, j = q & 3;
@@ -426,7 +428,7 @@ __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& 
     else if (q < 8) f1.b[q - 4] = frag<BKR>(cur + HALF, fb, q - 4, 1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  ident_mma<IDM, IDT, IB>(acc, f0, id, 0);
+  ident_mma<IDM, IDT, IB>(acc, f0, idf, 0);
   __builtin_amdgcn_sched_barrier(0);
   // stage k + 1 must have landed; in steady state the loads of stages k + 2
   // and k + 3 (16) follow it
@@ -441,7 +443,7 @@ __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& 
     else dma_load(ldb, wbase, L, ls, q - 8);
     __builtin_amdgcn_sched_barrier(0);
   }
-  ident_mma<IDM, IDT, IB>(acc, f1, id, 1);
+  ident_mma<IDM, IDT, IB>(acc, f1, idf, 1);
 }
 
 // The k loop of one tile: nk / 4 groups of 4 steps.  Stages live in a ring
@@ -476,7 +478,7 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
       const int lb = cb == 0 ? NBUF - 1 : cb - 1;                                           \
       nsg_step<AKR, BKR, IDM_, IDT, S_>(acc, f0, f1, smem + cb * STG, smem + nb * STG,      \
                                         la0 + (uint32_t)(lb * STG * 2), wbase, LP, S_, fa,  \
-                                        fb, id, lenient && kg == 0 && (S_) < 3);            \
+                                        fb, idf, lenient && kg == 0 && (S_) < 3);           \
       cb = nb;                                                                              \
       if ((S_) == 3) load_advance(LP, A, vid, stride);                                      \
     }
@@ -487,22 +489,33 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
     SM_NSG_STEP(3, IDM_)
     if constexpr (IDM != 0) {
       if (kg == id_g) {
+        IdFrags idf;
+        idf.h[0] = ident_frag(0, id.hi);
+        idf.h[1] = ident_frag(1, id.hi);
+        if constexpr (IDT == 2) {
+          idf.l[0] = ident_frag(0, id.lo);
+          idf.l[1] = ident_frag(1, id.lo);
+        }
         SM_NSG_GROUP(IDM)
         continue;
       }
     }
-    SM_NSG_GROUP(0)
+    {
+      IdFrags idf;   // not read: the group has no identity MFMAs
+      SM_NSG_GROUP(0)
+    }
 #undef SM_NSG_GROUP
 #undef SM_NSG_STEP
   }
 }
 
 // ---------------------------------------------------------------- epilogue
+// Quad permutes (every lane written: no old value needed).
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t cvt2(float x, float y) {
   const f32x2 v = {x, y};
@@ -526,12 +539,13 @@ __device__ __forceinline__ void st8(bf16_t* p, uint2 v) {
 // `mirror`.  Returns with every store issued (and, for a tile that is not
 // entirely inside the matrix, the wave's memory operations drained, so that
 // the next steps' waits hold).
-template <bool SCALE, bool STREAM>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc, int M,
-                                         int N, int wr0, int wc0, float alpha, bool mirror) {
+template <bool SCALE, bool STREAM, bool INTERIOR>
+__device__ __forceinline__ void epilogue_body(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc,
+                                              int M, int N, int wr0, int wc0, float alpha,
+                                              bool mirror) {
   const int lane = fresh_tid() & 63;
   const int lr = lane & 31, lq = (lane >> 5) * 4;
-  const bool interior = wr0 + 128 <= M && wc0 + 128 <= N;
+  constexpr bool interior = INTERIOR;
   const int cm = lane & 3;
   const int rsel = ((cm & 1) << 1) | (cm >> 1);   // which of the 4 rows this lane ends with
   const int colq = lr & ~3;
@@ -587,7 +601,22 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, i
           }
         }
       }
-  if (!interior) wait_vm<0>();
+}
+
+// The wave's sub-tile lies wholly inside C or not; readfirstlane states that
+// this is wave-uniform, so the choice is one scalar branch per tile instead
+// of an exec-mask branch around every store.
+template <bool SCALE, bool STREAM>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc, int M,
+                                         int N, int wr0, int wc0, float alpha, bool mirror) {
+  const int inside =
+      __builtin_amdgcn_readfirstlane((wr0 + 128 <= M && wc0 + 128 <= N) ? 1 : 0);
+  if (inside) {
+    epilogue_body<SCALE, STREAM, true>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror);
+  } else {
+    epilogue_body<SCALE, STREAM, false>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror);
+    wait_vm<0>();
+  }
 }
 
 // The writelane intrinsic, which this compiler exposes under no builtin
