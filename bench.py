@@ -430,8 +430,8 @@ def fidelity(args, sm, torch, W):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "path is not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library "
+              "has no multi-GPU exchange", file=sys.stderr)
         sys.exit(2)
     import torch
     import matrix_aware_optimizer_momentum_amd as sm

@@ -52,7 +52,7 @@ typedef enum {
   SM_ERR_SHAPE = 2,        /* non-positive or too large dimension                */
   SM_ERR_DTYPE = 3,        /* dtype not SM_F32 / SM_BF16                         */
   SM_ERR_WORKSPACE = 4,    /* ws too small (query the *_ws call)                 */
-  SM_ERR_UNSUPPORTED = 5,  /* valid request outside what this build implements   */
+  SM_ERR_UNSUPPORTED = 5,  /* valid request outside what the library implements  */
   SM_ERR_HIP = 6           /* a HIP runtime call or launch failed                */
 } sm_status;
 

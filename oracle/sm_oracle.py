@@ -158,7 +158,7 @@ def frobenius_normalize(y, eps: float) -> np.ndarray:
 
     [CacheMuon-ja] core mechanism item 2 calls X_t the normalised momentum;
     [SignMuon-ja] section 4 (nanoGPT, hyper-parameters) says Frobenius
-    scaling works.  The eps guard is this build's reading (Y = 0 gives X = 0).
+    scaling works.  The eps guard is a reading; the pages give none (Y = 0 gives X = 0).
     """
     y = np.asarray(y, dtype=np.float64)
     norm = math.sqrt(float(np.sum(y * y)))
