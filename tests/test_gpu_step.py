@@ -484,3 +484,35 @@ def test_full_size_gpt2_small_step_variants(gpu_lib, variant):
         torch.cuda.synchronize()
         assert torch.equal(w2.view(torch.int16), mats[j].w.view(torch.int16)), j
         assert v.abs().eq(1).all(), j                 # odd M: no ties
+
+
+# ------------------------------------------------------------------ degenerate shapes and worker counts
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_sign_muon_step_degenerate_shapes(gpu_lib, dt):
+    """1 x 1, row and column vectors and a ragged small matrix in one step
+    (the generic NS path, word tails of the packed signs)."""
+    wl = W.WORKLOADS[3].scaled(wdt=dt, mdt=dt, gdt=dt, M=4)
+    shapes = [(1, 1), (1, 7), (9, 1), (3, 200), (65, 65)]
+    _check_step(wl, _cfg(wl), Seeded(wl, shapes), 2, dt)
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_sign_muon_step_worker_count_limits(gpu_lib, M):
+    wl = W.WORKLOADS[1].scaled(M=M)
+    st = Seeded(wl, [(48, 80), (130, 40)])
+    _check_step(wl, _cfg(wl), st, 1, "f32")
+    # the int8 encoding agrees at the same limits
+    st2 = Seeded(wl, [(48, 80), (130, 40)])
+    mats8 = _clone_state(st2)
+    sm.StepCall(_cfg(wl), st2.mats)(1)
+    sm.StepCall(_cfg(wl, encoding=sm.ENC_INT8), mats8)(1)
+    torch.cuda.synchronize()
+    for a, b in zip(st2.mats, mats8):
+        assert torch.equal(a.w, b.w) and torch.equal(a.mom, b.mom)
+
+
+def test_step_rejects_more_than_64_workers(gpu_lib):
+    wl = W.WORKLOADS[1].scaled(M=65)
+    with pytest.raises(sm.SmError):
+        sm.StepCall(_cfg(wl), Seeded(W.WORKLOADS[1].scaled(M=2), [(8, 8)]).mats)
