@@ -34,9 +34,10 @@
 // Epilogue: value = alpha_b * acc, rounded to bf16 with v_cvt_pk_bf16_f32 and
 // stored straight from registers (no LDS: the ring holds the next tile).
 // Row-major C: two rounds of quad DPP shuffles give each lane 1 row x 4
-// columns (8-byte stores).  A symmetric product (A == B) computes only tiles
-// with tm >= tn and stores each off-diagonal tile a second time, transposed,
-// as the mirror tile (8-byte stores of 4 consecutive rows of one column).
+// columns (8-byte stores).  A symmetric product (A == B, or two commuting
+// symmetric matrices) computes only tiles with tm >= tn and stores each
+// off-diagonal tile a second time, transposed, as the mirror tile (8-byte
+// stores of 4 consecutive rows of one column).
 //
 // Identity fold.  The apply X' = a X + B X gets a X from extra MFMAs in the
 // k-stages that cover the output's own rows (wide: (a I) X) or columns (tall:
@@ -850,7 +851,7 @@ bool gemm_ns_supported(const NsgGroup& G) {
   const int64_t ea = G.a_kr ? (int64_t)G.K * G.lda : (int64_t)G.M * G.lda;
   const int64_t eb = G.b_kr ? (int64_t)G.K * G.ldb : (int64_t)G.N * G.ldb;
   if (2 * ea >= ((int64_t)1 << 32) || 2 * eb >= ((int64_t)1 << 32)) return false;
-  if (G.sym && (G.M != G.N || G.a != G.b || G.a_kr != G.b_kr || G.a_tbl != G.b_tbl))
+  if (G.sym && (G.M != G.N || G.a_kr != G.b_kr || G.a_tbl != G.b_tbl))
     return false;
   if (G.ident && G.ident_terms != 1 && G.ident_terms != 2) return false;
   if (G.bits && (G.sym || G.N % 64 != 0 || (reinterpret_cast<uintptr_t>(G.bits) & 7u) ||

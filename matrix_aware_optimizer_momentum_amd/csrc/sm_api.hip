@@ -248,16 +248,157 @@ sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
   return SM_OK;
 }
 
+// ------------------------------------------------------------------ Gram-form NS
+// The cubic iteration (c = 0) reaches the same X_K through r x r products,
+// which is cheaper when the matrix is far from square.  With S_k = b X_k X_k^T
+// and P_k = S_k + aI one direct step is X_{k+1} = P_k X_k, so X_k = Q_k X_0
+// with Q_k = P_{k-1} ... P_0.  S_k, P_k and Q_k are all polynomials in
+// G = X_0 X_0^T, hence symmetric and commuting, and
+//   S_0 = b s^2 x x^T            (the Gram product over the long side)
+//   Q_1 = S_0 + aI               (identity fill)
+//   T_k = S_k (S_k + aI),  S_{k+1} = T_k (S_k + aI)   (= P_k S_k P_k), k < K-1
+//   Q_{k+1} = Q_k (S_k + aI)     (k >= 1)
+//   X_K = s Q_K x                (one apply over the long side)
+// Every r x r product is a symmetric one (lower-triangle tiles) whose aI
+// part comes from the identity fold, so S_k, T_k and Q_k are rounded to
+// bf16 once per product, like the direct form's B_k and X_k.  Storing P_k
+// instead of S_k would round its O(1) diagonal and costs several times the
+// error.  Same-iteration products run in one launch: L1(k) = {T_k, Q_{k+1}},
+// L2(k) = {S_{k+1}}, 2K - 1 launches in all.
+struct GfSlot {
+  bf16_t* p;
+  int64_t st;   // elements between problems
+};
+
+struct GfPlan {
+  NsgGroup gram, apply;
+  std::vector<std::vector<NsgGroup>> rr;   // [2K - 1] launches
+  GfSlot fill_src, fill_dst;
+  int r, batch;
+  float a;
+};
+
+// Executed MFMA work of one problem in 256 x 256 tile x 128-deep k-group
+// units, for the direct and the Gram form (identity groups included).
+int64_t ns_tile_work(int r, int cols, int K, bool gram_form) {
+  const int64_t tr = (r + 255) / 256, tc = (cols + 255) / 256;
+  const int64_t sym = tr * (tr + 1) / 2;
+  const int64_t kr = (r + 127) / 128, kc = (cols + 127) / 128;
+  if (!gram_form) return K * (sym * kc + tr * tc * (kr + 1));
+  return sym * kc + 3 * (int64_t)(K - 1) * sym * (kr + 1) + tr * tc * (kr + 1);
+}
+
+bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
+  const int K = p.iters;
+  if (p.c != 0.f || K < 2) return false;
+  const bool wide = j.m <= j.n;
+  const int m = j.m, n = j.n, r = wide ? m : n, cols = wide ? n : m;
+  // two of the four r x r slots live in the m x n iterate buffer
+  if ((int64_t)cols < 2 * (int64_t)r) return false;
+  if (ns_tile_work(r, cols, K, true) >= ns_tile_work(r, cols, K, false)) return false;
+  const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
+  auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
+  auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
+  const int tb = (j.x == nullptr && j.xtbl) ? 1 : 0;
+  GfSlot slot[3] = {{mp(j.w.amat), rr}, {mp(j.w.amat2), rr}, {mp(j.w.tmp), mn}};
+  const GfSlot tslot{mp(j.w.tmp) + rr, mn};
+  uint32_t id_hi = 0, id_lo = 0;
+  const int id_terms = ns_ident_split(p.a, &id_hi, &id_lo);
+  if (id_terms == 0) return false;
+
+  std::memset(&g.gram, 0, sizeof(g.gram));
+  NsgGroup& gr = g.gram;
+  gr.a = bp(j.x); gr.lda = n; gr.sa = mn; gr.a_kr = wide ? 0 : 1;
+  gr.b = bp(j.x); gr.ldb = n; gr.sb = mn; gr.b_kr = wide ? 0 : 1;
+  gr.tbl = j.xtbl; gr.tbl_per = j.xper; gr.a_tbl = tb; gr.b_tbl = tb;
+  gr.c = slot[0].p; gr.ldc = r; gr.sc = slot[0].st;
+  gr.scale = j.scale; gr.alpha_pow = j.scale ? 2 : 0; gr.alpha = p.b;
+  gr.M = r; gr.N = r; gr.K = cols; gr.batch = j.batch; gr.sym = 1;
+  if (!gemm_ns_supported(gr)) return false;
+
+  // C = A (B + aI) over r x r slots
+  auto prod = [&](const GfSlot& A, const GfSlot& B, const GfSlot& C) {
+    NsgGroup q;
+    std::memset(&q, 0, sizeof(q));
+    q.a = A.p; q.lda = r; q.sa = A.st;
+    q.b = B.p; q.ldb = r; q.sb = B.st;
+    q.c = C.p; q.ldc = r; q.sc = C.st;
+    q.alpha = 1.f;
+    q.M = r; q.N = r; q.K = r; q.batch = j.batch; q.sym = 1;
+    q.ident = 2; q.ident_terms = id_terms; q.ident_hi = id_hi; q.ident_lo = id_lo;
+    return q;
+  };
+  int si = 0, qi = 1, fi = 2;   // slots of S_k, Q_k and the free one
+  g.fill_src = slot[si];
+  g.fill_dst = slot[qi];
+  g.rr.assign(2 * K - 1, {});
+  for (int k = 0; k < K; ++k) {
+    std::vector<NsgGroup>& l1 = g.rr[2 * k];
+    if (k < K - 1) l1.push_back(prod(slot[si], slot[si], tslot));       // T_k
+    if (k >= 1) {                                                       // Q_{k+1}
+      l1.push_back(prod(slot[qi], slot[si], slot[fi]));
+      std::swap(qi, fi);
+    }
+    if (k < K - 1) {                                                    // S_{k+1}
+      g.rr[2 * k + 1].push_back(prod(tslot, slot[si], slot[fi]));
+      std::swap(si, fi);
+    }
+  }
+  for (const auto& l : g.rr)
+    for (const NsgGroup& q : l)
+      if (!gemm_ns_supported(q)) return false;
+
+  std::memset(&g.apply, 0, sizeof(g.apply));
+  NsgGroup& a = g.apply;
+  const GfSlot& qk = slot[qi];
+  a.tbl = j.xtbl; a.tbl_per = j.xper;
+  if (wide) {   // X_K = (Q_K + 0 I) x
+    a.a = qk.p; a.lda = r; a.sa = qk.st;
+    a.b = bp(j.x); a.ldb = n; a.sb = mn; a.b_kr = 1; a.b_tbl = tb;
+    a.ident = 1;
+  } else {      // X_K = x (Q_K + 0 I)
+    a.a = bp(j.x); a.lda = n; a.sa = mn; a.a_tbl = tb;
+    a.b = qk.p; a.ldb = r; a.sb = qk.st;
+    a.ident = 2;
+  }
+  a.c = mp(j.out); a.ldc = n; a.sc = mn;
+  a.scale = j.scale; a.alpha_pow = j.scale ? 1 : 0; a.alpha = 1.f;
+  a.M = m; a.N = n; a.K = r; a.batch = j.batch;
+  a.ident_terms = ns_ident_split(0.f, &a.ident_hi, &a.ident_lo);
+  if (j.bits) {
+    a.bits = j.bits;
+    a.bits_stride = j.bits_stride;
+  }
+  if (!gemm_ns_supported(a)) return false;
+  g.r = r;
+  g.batch = j.batch;
+  g.a = p.a;
+  auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  return r % 8 == 0 && rr % 8 == 0 && mn % 8 == 0 && al(j.w.amat) && al(j.w.amat2) &&
+         al(j.w.tmp);
+}
+
 // Direct NS on bf16 jobs with the grouped kernel, all jobs' products of one
-// kind and iteration in one launch.  Returns SM_ERR_UNSUPPORTED (nothing
-// launched) if some job does not meet the kernel's requirements.
+// kind and iteration in one launch; jobs that gf_plan takes run the Gram form
+// (their Gram product shares the first launch, their apply the last).
+// Returns SM_ERR_UNSUPPORTED (nothing launched) if some job does not meet the
+// kernel's requirements.
 sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipStream_t s) {
   const int K = p.iters;
-  std::vector<NsDesc> d(jobs.size());
+  std::vector<const NsJob*> dj;
+  std::vector<GfPlan> gf;
+  for (const NsJob& j : jobs) {
+    GfPlan g;
+    if (gf_plan(j, p, g))
+      gf.push_back(std::move(g));
+    else
+      dj.push_back(&j);
+  }
+  std::vector<NsDesc> d(dj.size());
   for (int k = 0; k < K; ++k) {
     std::vector<NsgGroup> gram, rr, apply;
-    for (size_t i = 0; i < jobs.size(); ++i) {
-      const NsJob& j = jobs[i];
+    for (size_t i = 0; i < dj.size(); ++i) {
+      const NsJob& j = *dj[i];
       const void* cur = k == 0 ? j.x : (((K - k) % 2 == 0) ? j.out : j.w.tmp);
       void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
       if (!ns_desc(j, cur, dst, k == 0, k == K - 1, p, d[i])) return SM_ERR_UNSUPPORTED;
@@ -265,7 +406,21 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
       if (p.c != 0.f) rr.push_back(d[i].rr);
       apply.push_back(d[i].apply);
     }
+    if (k == 0)
+      for (const GfPlan& g : gf) gram.push_back(g.gram);
+    if (k == K - 1)
+      for (const GfPlan& g : gf) apply.push_back(g.apply);
     SM_TRY(launch_ns_groups(gram, SM_K_GEMM_GRAM, s));
+    if (k == 0 && !gf.empty()) {
+      for (const GfPlan& g : gf)
+        SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
+                                   g.r, g.batch, g.a, s));
+      for (int l = 0; l < 2 * K - 1; ++l) {
+        std::vector<NsgGroup> v;
+        for (const GfPlan& g : gf) v.insert(v.end(), g.rr[l].begin(), g.rr[l].end());
+        SM_TRY(launch_ns_groups(v, SM_K_GEMM_RR, s));
+      }
+    }
     if (!rr.empty()) SM_TRY(launch_ns_groups(rr, SM_K_GEMM_RR, s));
     SM_TRY(launch_ns_groups(apply, SM_K_GEMM_APPLY, s));
   }
@@ -276,6 +431,8 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
 // pointers; later iterations use buffers of the same shapes and alignment).
 bool ns_grouped_ok(const NsJob& j, int dt, const sm_ns_params& p) {
   if (dt != BF16) return false;
+  GfPlan g;
+  if (gf_plan(j, p, g)) return true;
   NsDesc d;
   return ns_desc(j, j.x, j.out, true, p.iters == 1, p, d) &&
          ns_desc(j, j.out, j.w.tmp, false, true, p, d);

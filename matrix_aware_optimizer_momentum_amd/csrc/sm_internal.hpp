@@ -182,6 +182,11 @@ sm_status launch_spectral_norm(const void* a, const void* b, int dt, int batch, 
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
                               int wdt, float lr, hipStream_t s);
 
+// q_b = s_b + a I for a batch of r x r bf16 matrices (float32 sum, bf16
+// rounding); needs r % 8 == 0, strides % 8 == 0 and 16-byte aligned bases.
+sm_status launch_add_identity(const bf16_t* src, int64_t ss, bf16_t* dst, int64_t sq, int r,
+                              int batch, float a, hipStream_t s);
+
 // has_cache flags of nprob problems: hc[b] = cache_state(b)[0], where problem
 // b's {has_cache, a_t} pair is at tbl_addr(cs, b, per, 8).
 sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t* hc,
@@ -251,8 +256,10 @@ sm_status launch_gemm(const GemmArgs& g, int mfma_dt, int kind, hipStream_t s);
 // C[b] = alpha_b * A[b] B[b]^T (+ identity term), A: M x K, B: N x K in the
 // operand sense, bf16, C (M x N) row-major bf16.  An operand with *_kr set is
 // stored k-major (K x rows, row-major, leading dimension ld over rows).
-// sym: A == B (same layout), C symmetric: only tm >= tn tiles are computed,
-// off-diagonal ones are also stored transposed.  ident: 1 adds (a I) times
+// sym: C is symmetric (A == B, or A and B are commuting symmetric matrices,
+// as all polynomials in one Gram matrix are), same layout on both sides:
+// only tm >= tn tiles are computed, off-diagonal ones are also stored
+// transposed.  ident: 1 adds (a I) times
 // the B part (needs K == M), 2 adds the A part times (a I) (needs K == N);
 // a = hi + lo as bf16 bit patterns (ident_terms 1: hi only).
 // alpha_b = alpha * scale[b]^alpha_pow (scale may be null).

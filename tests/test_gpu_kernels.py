@@ -215,6 +215,15 @@ NS_CASES = [
     ("bf16", 3, 128, 1152, 3, (1.5, -0.5, 0.0)),
     ("bf16", 2, 384, 640, 5, (1.3, -0.3, 0.0)),
     ("bf16", 2, 640, 384, 4, (1.3, -0.3, 0.0)),
+    # cubic on far-from-square shapes: the Gram form (r x r products), one
+    # and several tiles, partial tiles, the two-term identity split (1.3),
+    # the fewest iterations it takes (2), wide and tall
+    ("bf16", 2, 256, 1024, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 1024, 256, 4, (1.5, -0.5, 0.0)),
+    ("bf16", 3, 384, 1152, 2, (1.3, -0.3, 0.0)),
+    ("bf16", 1, 128, 4096, 5, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 640, 1920, 3, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 1920, 640, 6, (1.3, -0.3, 0.0)),
 ]
 
 
@@ -235,6 +244,29 @@ def test_ns_polar_matches_oracle(gpu_lib, case):
         want = O.ns_polar(xin[k], op, normalize=True)
         err = rel_fro(got[k], want)
         assert err <= TOL[dt], (k, err)
+
+
+@pytest.mark.parametrize("m,n,iters,gram_form", [
+    (768, 3072, 5, True), (3072, 768, 5, True), (384, 1152, 2, True),
+    (768, 768, 5, False), (384, 640, 5, False), (768, 3072, 1, False)])
+def test_ns_form_taken(gpu_lib, m, n, iters, gram_form):
+    """Far-from-square cubic problems run as r x r products, others directly."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    x = torch.randn(2, m, n, device="cuda", dtype=torch.bfloat16)
+    sm.profile_enable(True)
+    try:
+        sm.profile_reset()
+        sm.ns_polar(x, params=sm.NSParams(iters=iters))
+        torch.cuda.synchronize()
+        rr_launches = sm.profile_read("gemm_rr")[1]
+        gram_launches = sm.profile_read("gemm_gram")[1]
+        apply_launches = sm.profile_read("gemm_apply")[1]
+    finally:
+        sm.profile_enable(False)
+    if gram_form:
+        assert (gram_launches, apply_launches, rr_launches) == (1, 1, 2 * iters - 1)
+    else:
+        assert (gram_launches, apply_launches, rr_launches) == (iters, iters, 0)
 
 
 def test_ns_polar_without_normalisation(gpu_lib):
