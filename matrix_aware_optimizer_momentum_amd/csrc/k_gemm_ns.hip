@@ -76,15 +76,17 @@ struct Grp {
   float alpha;
   int tiles_m, tiles_n, tiles_per_prob, tile_begin;
   int a_tbl, b_tbl, tbl_per;   // per-matrix operand addressing (see NsgGroup)
+  int tbl;                     // byte offset of the group's table in Args
   uint64_t* bits;              // apply: signs instead of C (see NsgGroup)
   int64_t bits_stride;
-  PtrTbl tbl;
 };
 
 struct Args {
   Grp g[kNsgMaxGroups];
+  PtrTbl tbl[kNsgMaxTables];
   int ngroups, total_tiles, xcd_chunk;
 };
+static_assert(sizeof(Args) <= 4096, "kernel arguments stay within 4 KB");
 
 // ---------------------------------------------------------------- LDS layouts
 // KC half: 256 operand rows x 64 bytes; the 16-byte k chunk c of row R sits
@@ -194,9 +196,12 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r
   r = __builtin_amdgcn_readfirstlane(r);
   const Tile tl = decode_tile(A, t);
   const Grp& g = A.g[tl.gi];
-  L.abase = g.a_tbl ? tbl_addr(g.tbl, tl.prob, g.tbl_per, 2 * g.sa)
+  // the group's table, addressed by its byte offset in the arguments (an
+  // index into Args::tbl makes the compiler copy the arguments to scratch)
+  const PtrTbl* tb = reinterpret_cast<const PtrTbl*>(reinterpret_cast<const char*>(&A) + g.tbl);
+  L.abase = g.a_tbl ? tbl_addr(*tb, tl.prob, g.tbl_per, 2 * g.sa)
                     : reinterpret_cast<const char*>(g.a + (int64_t)tl.prob * g.sa);
-  L.bbase = g.b_tbl ? tbl_addr(g.tbl, tl.prob, g.tbl_per, 2 * g.sb)
+  L.bbase = g.b_tbl ? tbl_addr(*tb, tl.prob, g.tbl_per, 2 * g.sb)
                     : reinterpret_cast<const char*>(g.b + (int64_t)tl.prob * g.sb);
   dma_offsets(L.aoff, g.a_kr, g.lda, tl.tm * 256, g.M);
   dma_offsets(L.boff, g.b_kr, g.ldb, tl.tn * 256, g.N);
@@ -273,8 +278,13 @@ __device__ __forceinline__ void wait_vm() {
 // not vmcnt, so it does not wait for the loads in flight); the wait is in the
 // same statement.
 __device__ __forceinline__ float scalar_load(const float* p) {
+  // the address is wave-uniform; readfirstlane states it for the compiler
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const float* q = reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
   float v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
   return v;
 }
 
@@ -535,6 +545,9 @@ __device__ __forceinline__ void st8(bf16_t* p, uint2 v) {
   }
 }
 
+// 16-byte store (plain: the symmetric products are read back).
+__device__ __forceinline__ void st16(bf16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
 // Stores this wave's 128 x 128 sub-tile (origin wr0, wc0) of alpha * acc
 // (SCALE false: alpha is 1), and its transpose into the mirror tile when
 // `mirror`.  Returns with every store issued (and, for a tile that is not
@@ -543,79 +556,106 @@ __device__ __forceinline__ void st8(bf16_t* p, uint2 v) {
 template <bool SCALE, bool STREAM, bool INTERIOR>
 __device__ __forceinline__ void epilogue_body(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc,
                                               int M, int N, int wr0, int wc0, float alpha,
-                                              bool mirror) {
+                                              bool mirror, bf16_t* stage) {
   const int lane = fresh_tid() & 63;
   const int lr = lane & 31, lq = (lane >> 5) * 4;
   constexpr bool interior = INTERIOR;
   const int cm = lane & 3;
   const int rsel = ((cm & 1) << 1) | (cm >> 1);   // which of the 4 rows this lane ends with
   const int colq = lr & ~3;
+  // 64 x 64 chunks (I, J) of 2 x 2 blocks of 32 x 32
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int I = 0; I < 2; ++I)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int J = 0; J < 2; ++J) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
-        uint32_t v0, v1;
-        if constexpr (SCALE) {
-          v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
-          v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
-        } else {
-          v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        }
-        if (mirror) {   // C^T: the 4 rows are 4 consecutive elements of one row
-          const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
-          bf16_t* p = C + (int64_t)trow * ldc + tcol;
-          if (interior) {
-            st8<STREAM>(p, make_uint2(v0, v1));
-          } else if (trow < N) {
-            const uint32_t w[2] = {v0, v1};
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (tcol + e < M) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 2 * I + ii, j = 2 * J + jj;
+            // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
+            uint32_t v0, v1;
+            if constexpr (SCALE) {
+              v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
+              v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
+            } else {
+              v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+              v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+            }
+            if (mirror) {   // C^T: the 4 rows are 4 consecutive entries of one row
+              if (interior) {
+                // into the chunk's LDS stage: mirror row R (of 64), 16-byte
+                // piece c at position c ^ (R & 7)
+                const int R = jj * 32 + lr, c = ii * 4 + q;
+                *reinterpret_cast<uint2*>(stage + R * 64 + ((c ^ (R & 7)) * 8) + lq) =
+                    make_uint2(v0, v1);
+              } else {
+                const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
+                bf16_t* p = C + (int64_t)trow * ldc + tcol;
+                if (trow < N) {
+                  const uint32_t w[2] = {v0, v1};
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    if (tcol + e < M) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+                }
+              }
+            }
+            const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
+            const uint32_t mine = (cm & 1) ? v1 : v0;
+            const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
+            const uint32_t hi = (cm & 1) ? mine : recv;
+            const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
+            const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
+            const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
+            const uint32_t keep = (cm < 2) ? ra : rb;
+            const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
+            const int row = wr0 + i * 32 + q * 8 + lq + rsel;
+            const int col = wc0 + j * 32 + colq;
+            bf16_t* p = C + (int64_t)row * ldc + col;
+            if (interior) {
+              st8<STREAM>(p, out);
+            } else if (row < M) {
+              if (col + 4 <= N) {
+                st8<STREAM>(p, out);
+              } else {
+                const uint32_t w[2] = {out.x, out.y};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+              }
+            }
           }
-        }
-        const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
-        const uint32_t mine = (cm & 1) ? v1 : v0;
-        const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
-        const uint32_t hi = (cm & 1) ? mine : recv;
-        const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
-        const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
-        const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
-        const uint32_t keep = (cm < 2) ? ra : rb;
-        const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
-        const int row = wr0 + i * 32 + q * 8 + lq + rsel;
-        const int col = wc0 + j * 32 + colq;
-        bf16_t* p = C + (int64_t)row * ldc + col;
-        if (interior) {
-          st8<STREAM>(p, out);
-        } else if (row < M) {
-          if (col + 4 <= N) {
-            st8<STREAM>(p, out);
-          } else {
-            const uint32_t w[2] = {out.x, out.y};
+      if (interior && mirror) {
+        // the chunk back as 16-byte row pieces: whole 128-byte row segments
+        // of the mirror tile (one wave's LDS accesses execute in order, so
+        // these reads see the writes above and the next chunk's writes
+        // follow them)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
-          }
+        for (int t = 0; t < 8; ++t) {
+          const int R = t * 8 + (lane >> 3), c = lane & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + R * 64 + ((c ^ (R & 7)) * 8));
+          st16(C + (int64_t)(wc0 + J * 64 + R) * ldc + (wr0 + I * 64 + c * 8), v);
         }
       }
+    }
 }
 
 // The wave's sub-tile lies wholly inside C or not; readfirstlane states that
 // this is wave-uniform, so the choice is one scalar branch per tile instead
 // of an exec-mask branch around every store.
+// `stage`: this wave's 8 KB of LDS for the mirror copy (mirror only).
 template <bool SCALE, bool STREAM>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc, int M,
-                                         int N, int wr0, int wc0, float alpha, bool mirror) {
+                                         int N, int wr0, int wc0, float alpha, bool mirror,
+                                         bf16_t* stage) {
   const int inside =
       __builtin_amdgcn_readfirstlane((wr0 + 128 <= M && wc0 + 128 <= N) ? 1 : 0);
   if (inside) {
-    epilogue_body<SCALE, STREAM, true>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror);
+    epilogue_body<SCALE, STREAM, true>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror, stage);
   } else {
-    epilogue_body<SCALE, STREAM, false>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror);
+    epilogue_body<SCALE, STREAM, false>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror, stage);
     wait_vm<0>();
   }
 }
@@ -693,11 +733,14 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 }
 
 // ---------------------------------------------------------------- kernel
-// Combos per role (index = Grp::combo): operand layouts and identity mode.
-//   GRAM:  0 (KC, KC)        1 (KR, KR)
+// Two kernels: one for symmetric products (Gram products and the r x r
+// products), one for applies.  Combos per kernel (index = Grp::combo):
+// operand layouts and identity mode.
+//   SYM:   0 (KC, KC)        1 (KR, KR)
+//          2 (KC, KC, B-side id, 1 term)   3 (KC, KC, B-side id, 2 terms)
 //   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
-//   RR:    0 (KC, KC, B-side id, 1 term)   1 (KC, KC, B-side id, 2 terms)
+constexpr int ROLE_SYM = 0, ROLE_APPLY = 1;
 template <int ROLE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_ns(Args args) {
@@ -752,25 +795,23 @@ void k_gemm_ns(Args args) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    if constexpr (ROLE == SM_K_GEMM_GRAM) {
+    if constexpr (ROLE == ROLE_SYM) {
       if (g.combo == 0) {
         run_tile<0, 0, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
+      } else if (g.combo == 1) {
         run_tile<1, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else if (g.combo == 2) {
+        run_tile<0, 0, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else {
+        run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
-    } else if constexpr (ROLE == SM_K_GEMM_APPLY) {
+    } else {
       if (g.combo == 0) {
         run_tile<0, 1, 1, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 1) {
         run_tile<0, 0, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 2) {
         run_tile<0, 1, 1, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
-        run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      }
-    } else {
-      if (g.combo == 0) {
-        run_tile<0, 0, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else {
         run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
@@ -783,13 +824,13 @@ void k_gemm_ns(Args args) {
       const float sc = scalar_load(g.scale + tc.prob);
       for (int p = 0; p < g.alpha_pow; ++p) alpha *= sc;
     }
-    // Each role compiles only its own epilogues (extra instantiations cost
-    // the whole kernel registers).  Gram and A^2 products are symmetric,
-    // scaled (by b, or c) and read back by the next launch, so they stay
-    // cacheable; the applies are not symmetric, mostly unscaled (alpha is 1
-    // after the first iteration) and their outputs stream out.
+    // Each kernel compiles only its own epilogues (extra instantiations cost
+    // the whole kernel registers).  Symmetric products are scaled (by b, c
+    // or 1) and read back by the next launch, so they stay cacheable; the
+    // applies are not symmetric, mostly unscaled (alpha is 1 after the first
+    // iteration) and their outputs stream out.
     bf16_t* C = g.c + (int64_t)tc.prob * g.sc;
-    if constexpr (ROLE == SM_K_GEMM_APPLY) {
+    if constexpr (ROLE == ROLE_APPLY) {
       if (g.bits) {   // the last iteration of a vote-mode step: signs only
         uint64_t* bp = g.bits + (int64_t)tc.prob * g.bits_stride;
         if (alpha == 1.f)
@@ -797,12 +838,21 @@ void k_gemm_ns(Args args) {
         else
           epilogue_bits<true>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
       } else if (alpha == 1.f) {
-        epilogue<false, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false);
+        epilogue<false, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, nullptr);
       } else {
-        epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false);
+        epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, nullptr);
       }
     } else {
-      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, tc.tm != tc.tn);
+      // An off-diagonal tile also stores its mirror, staged through the ring
+      // buffer of the stage just multiplied (the next tile's first loads
+      // target the other four; its stage 4 goes there only after the
+      // barrier of its first step).  Every wave is past its reads of that
+      // stage once all have met here.
+      const bool mirror = tc.tm != tc.tn;
+      if (mirror) barrier_nofence();
+      bf16_t* stage = smem + (cb == 0 ? NBUF - 1 : cb - 1) * STG +
+                      4096 * __builtin_amdgcn_readfirstlane(fresh_tid() >> 6);
+      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, mirror, stage);
     }
     t = tile_of(++round, vid, stride);
     if (t >= A.total_tiles) break;
@@ -887,11 +937,28 @@ int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits) {
   return (fl(h) + fl(l) == a) ? 2 : 0;
 }
 
+int ns_group_tables(const NsgGroup* groups, int ngroups) {
+  const PtrTbl* seen[kNsgMaxGroups];
+  int n = 0;
+  for (int q = 0; q < ngroups && q < kNsgMaxGroups; ++q) {
+    const NsgGroup& G = groups[q];
+    if (!(G.a_tbl || G.b_tbl)) continue;
+    bool found = false;
+    for (int i = 0; i < n; ++i) found |= seen[i] == G.tbl;
+    if (!found) seen[n++] = G.tbl;
+  }
+  return n;
+}
+
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s) {
   using namespace nsg;
   if (ngroups <= 0 || ngroups > kNsgMaxGroups) return SM_ERR_ARG;
+  const bool apply = kind == SM_K_GEMM_APPLY;
+  if (!apply && kind != SM_K_GEMM_GRAM && kind != SM_K_GEMM_RR) return SM_ERR_ARG;
   Args a;
   std::memset(&a, 0, sizeof(a));
+  const PtrTbl* tbls[kNsgMaxTables];
+  int ntbl = 0;
   int tiles = 0;
   double flops = 0.0;
   for (int q = 0; q < ngroups; ++q) {
@@ -910,27 +977,36 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.alpha = G.alpha;
     g.bits = G.bits;
     g.bits_stride = G.bits_stride;
-    if (G.bits && kind != SM_K_GEMM_APPLY) return SM_ERR_UNSUPPORTED;
+    if (G.bits && !apply) return SM_ERR_UNSUPPORTED;
     g.a_tbl = G.a_tbl ? 1 : 0;
     g.b_tbl = G.b_tbl ? 1 : 0;
     g.tbl_per = G.tbl_per;
-    if (G.a_tbl || G.b_tbl) g.tbl = *G.tbl;
+    if (G.a_tbl || G.b_tbl) {
+      int ti = 0;
+      while (ti < ntbl && tbls[ti] != G.tbl) ++ti;
+      if (ti == ntbl) {
+        if (ntbl == kNsgMaxTables) return SM_ERR_UNSUPPORTED;
+        tbls[ntbl] = G.tbl;
+        a.tbl[ntbl] = *G.tbl;
+        ++ntbl;
+      }
+      g.tbl = (int)(offsetof(Args, tbl) + ti * sizeof(PtrTbl));
+    }
     // the instantiation for this group's layouts and identity mode
     int combo = -1;
     const bool two = G.ident && G.ident_terms == 2;
-    if (kind == SM_K_GEMM_GRAM) {
+    if (!apply) {
       if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
       else if (!G.ident && g.a_kr && g.b_kr) combo = 1;
-    } else if (kind == SM_K_GEMM_APPLY) {
+      else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 2;
+    } else {
       if (G.ident == 1 && !g.a_kr && g.b_kr) combo = two ? 2 : 0;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 1;
-    } else if (kind == SM_K_GEMM_RR) {
-      if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 1 : 0;
     }
     if (combo < 0) return SM_ERR_UNSUPPORTED;
-    // the kernels compile the symmetric epilogue for Gram / r x r products
-    // only, and the plain one for applies only
-    if ((kind == SM_K_GEMM_APPLY) == (g.sym != 0)) return SM_ERR_UNSUPPORTED;
+    // the symmetric kernel compiles only the symmetric epilogue, the apply
+    // kernel only the plain one
+    if (apply == (g.sym != 0)) return SM_ERR_UNSUPPORTED;
     g.combo = combo;
     g.tiles_m = (G.M + 255) / 256;
     g.tiles_n = (G.N + 255) / 256;
@@ -948,12 +1024,10 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
   const int grid = std::min(tiles, cu_count());
   a.xcd_chunk = (grid % 8 == 0) ? grid / 8 : 0;
   prof_begin(kind, flops, s);
-  if (kind == SM_K_GEMM_GRAM)
-    hipLaunchKernelGGL((k_gemm_ns<SM_K_GEMM_GRAM>), dim3(grid), dim3(NT), 0, s, a);
-  else if (kind == SM_K_GEMM_APPLY)
-    hipLaunchKernelGGL((k_gemm_ns<SM_K_GEMM_APPLY>), dim3(grid), dim3(NT), 0, s, a);
+  if (apply)
+    hipLaunchKernelGGL((k_gemm_ns<ROLE_APPLY>), dim3(grid), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm_ns<SM_K_GEMM_RR>), dim3(grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_ns<ROLE_SYM>), dim3(grid), dim3(NT), 0, s, a);
   prof_end(s);
   return check_launch();
 }

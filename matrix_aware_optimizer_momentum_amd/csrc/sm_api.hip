@@ -235,15 +235,20 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, bool last,
   return a.ident_terms != 0 && gemm_ns_supported(a);
 }
 
-// Launches one product kind for all jobs, at most kNsgMaxGroups groups per
-// launch, groups ordered by decreasing K so that concurrent tiles carry
-// similar work.
+// Launches one product kind for all jobs, groups ordered by decreasing K so
+// that concurrent tiles carry similar work, as few launches as the group
+// and table limits allow.
 sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
   std::stable_sort(gs.begin(), gs.end(),
                    [](const NsgGroup& x, const NsgGroup& y) { return x.K > y.K; });
-  for (size_t i = 0; i < gs.size(); i += kNsgMaxGroups) {
-    const int ng = (int)std::min<size_t>(kNsgMaxGroups, gs.size() - i);
+  size_t i = 0;
+  while (i < gs.size()) {
+    int ng = 1;
+    while (i + ng < gs.size() && ng < kNsgMaxGroups &&
+           ns_group_tables(gs.data() + i, ng + 1) <= kNsgMaxTables)
+      ++ng;
     SM_TRY(launch_gemm_ns(gs.data() + i, ng, kind, s));
+    i += ng;
   }
   return SM_OK;
 }
@@ -379,8 +384,10 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
 }
 
 // Direct NS on bf16 jobs with the grouped kernel, all jobs' products of one
-// kind and iteration in one launch; jobs that gf_plan takes run the Gram form
-// (their Gram product shares the first launch, their apply the last).
+// kind and iteration in one launch; jobs that gf_plan takes run the Gram form.
+// The Gram-form jobs' Gram product shares the first launch, their r x r
+// launches take the direct jobs' Gram products of iterations 1 .. K-1 along
+// (the kernel is the same), and their apply shares the last launch.
 // Returns SM_ERR_UNSUPPORTED (nothing launched) if some job does not meet the
 // kernel's requirements.
 sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipStream_t s) {
@@ -395,33 +402,43 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
       dj.push_back(&j);
   }
   std::vector<NsDesc> d(dj.size());
+  const int nrr = gf.empty() ? 0 : 2 * K - 1;   // Gram-form r x r launches
+  auto take_rr = [&](int l, std::vector<NsgGroup>& v) {
+    for (const GfPlan& g : gf) v.insert(v.end(), g.rr[l].begin(), g.rr[l].end());
+  };
+  int l = 0;
   for (int k = 0; k < K; ++k) {
-    std::vector<NsgGroup> gram, rr, apply;
+    std::vector<NsgGroup> sym, rr, apply;
     for (size_t i = 0; i < dj.size(); ++i) {
       const NsJob& j = *dj[i];
       const void* cur = k == 0 ? j.x : (((K - k) % 2 == 0) ? j.out : j.w.tmp);
       void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
       if (!ns_desc(j, cur, dst, k == 0, k == K - 1, p, d[i])) return SM_ERR_UNSUPPORTED;
-      gram.push_back(d[i].gram);
+      sym.push_back(d[i].gram);
       if (p.c != 0.f) rr.push_back(d[i].rr);
       apply.push_back(d[i].apply);
     }
+    int kind = SM_K_GEMM_GRAM;
+    if (k == 0) {
+      for (const GfPlan& g : gf) sym.push_back(g.gram);
+    } else if (l < nrr) {
+      take_rr(l++, sym);
+      kind = SM_K_GEMM_RR;
+    }
+    SM_TRY(launch_ns_groups(sym, kind, s));
     if (k == 0)
-      for (const GfPlan& g : gf) gram.push_back(g.gram);
-    if (k == K - 1)
-      for (const GfPlan& g : gf) apply.push_back(g.apply);
-    SM_TRY(launch_ns_groups(gram, SM_K_GEMM_GRAM, s));
-    if (k == 0 && !gf.empty()) {
       for (const GfPlan& g : gf)
         SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
                                    g.r, g.batch, g.a, s));
-      for (int l = 0; l < 2 * K - 1; ++l) {
+    if (!rr.empty()) SM_TRY(launch_ns_groups(rr, SM_K_GEMM_RR, s));
+    if (k == K - 1) {   // the rest of the Gram-form chain, then every last apply
+      for (; l < nrr; ++l) {
         std::vector<NsgGroup> v;
-        for (const GfPlan& g : gf) v.insert(v.end(), g.rr[l].begin(), g.rr[l].end());
+        take_rr(l, v);
         SM_TRY(launch_ns_groups(v, SM_K_GEMM_RR, s));
       }
+      for (const GfPlan& g : gf) apply.push_back(g.apply);
     }
-    if (!rr.empty()) SM_TRY(launch_ns_groups(rr, SM_K_GEMM_RR, s));
     SM_TRY(launch_ns_groups(apply, SM_K_GEMM_APPLY, s));
   }
   return SM_OK;

@@ -259,11 +259,13 @@ sm_status launch_gemm(const GemmArgs& g, int mfma_dt, int kind, hipStream_t s);
 // sym: C is symmetric (A == B, or A and B are commuting symmetric matrices,
 // as all polynomials in one Gram matrix are), same layout on both sides:
 // only tm >= tn tiles are computed, off-diagonal ones are also stored
-// transposed.  ident: 1 adds (a I) times
-// the B part (needs K == M), 2 adds the A part times (a I) (needs K == N);
-// a = hi + lo as bf16 bit patterns (ident_terms 1: hi only).
-// alpha_b = alpha * scale[b]^alpha_pow (scale may be null).
-constexpr int kNsgMaxGroups = 4;
+// transposed.  ident: 1 adds (a I) times the B part (needs K == M), 2 adds
+// the A part times (a I) (needs K == N); a = hi + lo as bf16 bit patterns
+// (ident_terms 1: hi only).  alpha_b = alpha * scale[b]^alpha_pow (scale may
+// be null).  One launch takes up to kNsgMaxGroups groups that use at most
+// kNsgMaxTables distinct pointer tables.
+constexpr int kNsgMaxGroups = 8;
+constexpr int kNsgMaxTables = 4;
 struct NsgGroup {
   const bf16_t* a; int64_t lda, sa; int a_kr;
   const bf16_t* b; int64_t ldb, sb; int b_kr;
@@ -287,7 +289,12 @@ bool gemm_ns_supported(const NsgGroup& g);
 // Splits a into bf16 terms hi (+ lo); returns the number of terms whose sum
 // is exactly a (1 or 2), or 0 if two do not suffice.
 int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
-// All groups of one launch must be of the same kind (Gram, apply or r x r).
+// All groups of one launch are symmetric products (kind SM_K_GEMM_GRAM or
+// SM_K_GEMM_RR, which differ only in the kernel-time accounting) or all are
+// applies (SM_K_GEMM_APPLY).  Returns SM_ERR_UNSUPPORTED for more than
+// kNsgMaxTables distinct tables.
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s);
+// Distinct pointer tables among the groups.
+int ns_group_tables(const NsgGroup* groups, int ngroups);
 
 }  // namespace sm
