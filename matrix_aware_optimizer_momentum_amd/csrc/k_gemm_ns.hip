@@ -491,7 +491,6 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
                                         la0 + (uint32_t)(lb * STG * 2), wbase, LP, S_, fa,  \
                                         fb, idf, lenient && kg == 0 && (S_) < 3);           \
       cb = nb;                                                                              \
-      if ((S_) == 3) load_advance(LP, A, vid, stride);                                      \
     }
 #define SM_NSG_GROUP(IDM_) \
     SM_NSG_STEP(0, IDM_)   \
@@ -508,15 +507,20 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
           idf.l[1] = ident_frag(1, id.lo);
         }
         SM_NSG_GROUP(IDM)
-        continue;
+      } else {
+        IdFrags idf;   // not read: the group has no identity MFMAs
+        SM_NSG_GROUP(0)
       }
-    }
-    {
-      IdFrags idf;   // not read: the group has no identity MFMAs
+    } else {
+      IdFrags idf;
       SM_NSG_GROUP(0)
     }
 #undef SM_NSG_GROUP
 #undef SM_NSG_STEP
+    // after step 3 the load position moves on; outside the identity branch,
+    // whose condition the compiler takes for divergent, the next tile's
+    // arguments stay scalar loads
+    load_advance(LP, A, vid, stride);
   }
 }
 
@@ -550,9 +554,10 @@ __device__ __forceinline__ void st16(bf16_t* p, uint4 v) { *reinterpret_cast<uin
 
 // Stores this wave's 128 x 128 sub-tile (origin wr0, wc0) of alpha * acc
 // (SCALE false: alpha is 1), and its transpose into the mirror tile when
-// `mirror`.  Returns with every store issued (and, for a tile that is not
-// entirely inside the matrix, the wave's memory operations drained, so that
-// the next steps' waits hold).
+// `mirror` (symmetric kernel only; through the wave's LDS `stage` when the
+// sub-tile is interior).  Returns with every store issued (and, for a tile
+// that is not entirely inside the matrix, the wave's memory operations
+// drained, so that the next steps' waits hold).
 template <bool SCALE, bool STREAM, bool INTERIOR>
 __device__ __forceinline__ void epilogue_body(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc,
                                               int M, int N, int wr0, int wc0, float alpha,
@@ -563,83 +568,80 @@ __device__ __forceinline__ void epilogue_body(const f32x16 (&acc)[4][4], bf16_t*
   const int cm = lane & 3;
   const int rsel = ((cm & 1) << 1) | (cm >> 1);   // which of the 4 rows this lane ends with
   const int colq = lr & ~3;
-  // 64 x 64 chunks (I, J) of 2 x 2 blocks of 32 x 32
+  // The 4 x 4 blocks of 32 x 32: row-block-major in the apply kernel
+  // (STREAM), in 64 x 64 chunks (I, J) of 2 x 2 blocks in the symmetric one,
+  // whose mirror copy goes through LDS a chunk at a time.
 #pragma unroll
-  for (int I = 0; I < 2; ++I)
+  for (int u = 0; u < 16; ++u) {
+    const int I = u >> 3, J = (u >> 2) & 1;
+    const int ii = STREAM ? 0 : (u >> 1) & 1, jj = STREAM ? 0 : u & 1;
+    const int i = STREAM ? u >> 2 : 2 * I + ii, j = STREAM ? u & 3 : 2 * J + jj;
 #pragma unroll
-    for (int J = 0; J < 2; ++J) {
+    for (int q = 0; q < 4; ++q) {
+      // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
+      uint32_t v0, v1;
+      if constexpr (SCALE) {
+        v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
+        v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
+      } else {
+        v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+        v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+      }
+      if (!STREAM && mirror) {   // C^T: the 4 rows are 4 consecutive entries of one row
+        if (interior) {
+          // into the chunk's LDS stage: mirror row R (of 64), 16-byte
+          // piece c at position c ^ (R & 7)
+          const int R = jj * 32 + lr, c = ii * 4 + q;
+          *reinterpret_cast<uint2*>(stage + R * 64 + ((c ^ (R & 7)) * 8) + lq) =
+              make_uint2(v0, v1);
+        } else {
+          const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
+          bf16_t* p = C + (int64_t)trow * ldc + tcol;
+          if (trow < N) {
+            const uint32_t w[2] = {v0, v1};
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = 2 * I + ii, j = 2 * J + jj;
-            // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
-            uint32_t v0, v1;
-            if constexpr (SCALE) {
-              v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
-              v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
-            } else {
-              v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-              v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-            }
-            if (mirror) {   // C^T: the 4 rows are 4 consecutive entries of one row
-              if (interior) {
-                // into the chunk's LDS stage: mirror row R (of 64), 16-byte
-                // piece c at position c ^ (R & 7)
-                const int R = jj * 32 + lr, c = ii * 4 + q;
-                *reinterpret_cast<uint2*>(stage + R * 64 + ((c ^ (R & 7)) * 8) + lq) =
-                    make_uint2(v0, v1);
-              } else {
-                const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
-                bf16_t* p = C + (int64_t)trow * ldc + tcol;
-                if (trow < N) {
-                  const uint32_t w[2] = {v0, v1};
-#pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    if (tcol + e < M) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
-                }
-              }
-            }
-            const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
-            const uint32_t mine = (cm & 1) ? v1 : v0;
-            const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
-            const uint32_t hi = (cm & 1) ? mine : recv;
-            const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
-            const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
-            const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
-            const uint32_t keep = (cm < 2) ? ra : rb;
-            const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
-            const int row = wr0 + i * 32 + q * 8 + lq + rsel;
-            const int col = wc0 + j * 32 + colq;
-            bf16_t* p = C + (int64_t)row * ldc + col;
-            if (interior) {
-              st8<STREAM>(p, out);
-            } else if (row < M) {
-              if (col + 4 <= N) {
-                st8<STREAM>(p, out);
-              } else {
-                const uint32_t w[2] = {out.x, out.y};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
-              }
-            }
+            for (int e = 0; e < 4; ++e)
+              if (tcol + e < M) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
           }
-      if (interior && mirror) {
-        // the chunk back as 16-byte row pieces: whole 128-byte row segments
-        // of the mirror tile (one wave's LDS accesses execute in order, so
-        // these reads see the writes above and the next chunk's writes
-        // follow them)
+        }
+      }
+      const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
+      const uint32_t mine = (cm & 1) ? v1 : v0;
+      const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
+      const uint32_t hi = (cm & 1) ? mine : recv;
+      const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
+      const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
+      const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
+      const uint32_t keep = (cm < 2) ? ra : rb;
+      const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
+      const int row = wr0 + i * 32 + q * 8 + lq + rsel;
+      const int col = wc0 + j * 32 + colq;
+      bf16_t* p = C + (int64_t)row * ldc + col;
+      if (interior) {
+        st8<STREAM>(p, out);
+      } else if (row < M) {
+        if (col + 4 <= N) {
+          st8<STREAM>(p, out);
+        } else {
+          const uint32_t w[2] = {out.x, out.y};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int R = t * 8 + (lane >> 3), c = lane & 7;
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + R * 64 + ((c ^ (R & 7)) * 8));
-          st16(C + (int64_t)(wc0 + J * 64 + R) * ldc + (wr0 + I * 64 + c * 8), v);
+          for (int e = 0; e < 4; ++e)
+            if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
+    if (!STREAM && interior && mirror && (u & 3) == 3) {
+      // the chunk back as 16-byte row pieces: whole 128-byte row segments of
+      // the mirror tile (one wave's LDS accesses execute in order, so these
+      // reads see the writes above and the next chunk's writes follow them)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int R = t * 8 + (lane >> 3), c = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + R * 64 + ((c ^ (R & 7)) * 8));
+        st16(C + (int64_t)(wc0 + J * 64 + R) * ldc + (wr0 + I * 64 + c * 8), v);
+      }
+    }
+  }
 }
 
 // The wave's sub-tile lies wholly inside C or not; readfirstlane states that
@@ -740,6 +742,7 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 //          2 (KC, KC, B-side id, 1 term)   3 (KC, KC, B-side id, 2 terms)
 //   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
+//          4 (KC, KR)        5 (KC, KC)
 constexpr int ROLE_SYM = 0, ROLE_APPLY = 1;
 template <int ROLE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -812,8 +815,12 @@ void k_gemm_ns(Args args) {
         run_tile<0, 0, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 2) {
         run_tile<0, 1, 1, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
+      } else if (g.combo == 3) {
         run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else if (g.combo == 4) {
+        run_tile<0, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else {
+        run_tile<0, 0, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
     }
     wm = (fresh_tid() >> 6) >> 1;
@@ -1002,6 +1009,8 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     } else {
       if (G.ident == 1 && !g.a_kr && g.b_kr) combo = two ? 2 : 0;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 1;
+      else if (!G.ident && !g.a_kr && g.b_kr) combo = 4;
+      else if (!G.ident && !g.a_kr && !g.b_kr) combo = 5;
     }
     if (combo < 0) return SM_ERR_UNSUPPORTED;
     // the symmetric kernel compiles only the symmetric epilogue, the apply

@@ -139,7 +139,7 @@ GemmArgs gemm_base(int M, int N, int K, int batch) {
 // ------------------------------------------------------------------ direct NS
 
 struct NsWs {
-  void* tmp;    // [batch][m*n] ping-pong iterate
+  void* tmp;    // [batch][m*n] ping-pong iterate, or [batch][2][r*r] Gram-form slots
   void* amat;   // [batch][r*r]
   void* amat2;  // [batch][r*r] (quintic term)
 };
@@ -147,7 +147,7 @@ struct NsWs {
 void carve_ns(Carver& cv, int dt, int batch, int m, int n, NsWs& w) {
   const int64_t r = m < n ? m : n;
   const size_t es = dt_size(dt);
-  w.tmp = cv.take<void>((size_t)batch * m * n * es);
+  w.tmp = cv.take<void>((size_t)batch * std::max<int64_t>((int64_t)m * n, 2 * r * r) * es);
   w.amat = cv.take<void>((size_t)batch * r * r * es);
   w.amat2 = cv.take<void>((size_t)batch * r * r * es);
 }
@@ -290,23 +290,25 @@ int64_t ns_tile_work(int r, int cols, int K, bool gram_form) {
   const int64_t sym = tr * (tr + 1) / 2;
   const int64_t kr = (r + 127) / 128, kc = (cols + 127) / 128;
   if (!gram_form) return K * (sym * kc + tr * tc * (kr + 1));
-  return sym * kc + 3 * (int64_t)(K - 1) * sym * (kr + 1) + tr * tc * (kr + 1);
+  return sym * kc + 3 * (int64_t)(K - 1) * sym * (kr + 1) + tr * tc * kr;
 }
 
+// Takes job j in the Gram form if that form's MFMA work is below the direct
+// form's.  The choice depends on the job alone (not on the other jobs of the
+// call), so a matrix gets the same result from a step as from sm_ns_polar.
 bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   const int K = p.iters;
   if (p.c != 0.f || K < 2) return false;
   const bool wide = j.m <= j.n;
   const int m = j.m, n = j.n, r = wide ? m : n, cols = wide ? n : m;
-  // two of the four r x r slots live in the m x n iterate buffer
-  if ((int64_t)cols < 2 * (int64_t)r) return false;
   if (ns_tile_work(r, cols, K, true) >= ns_tile_work(r, cols, K, false)) return false;
   const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
   auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
   auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
   const int tb = (j.x == nullptr && j.xtbl) ? 1 : 0;
-  GfSlot slot[3] = {{mp(j.w.amat), rr}, {mp(j.w.amat2), rr}, {mp(j.w.tmp), mn}};
-  const GfSlot tslot{mp(j.w.tmp) + rr, mn};
+  // two of the four r x r slots live in the iterate buffer
+  GfSlot slot[3] = {{mp(j.w.amat), rr}, {mp(j.w.amat2), rr}, {mp(j.w.tmp), 2 * rr}};
+  const GfSlot tslot{mp(j.w.tmp) + rr, 2 * rr};
   uint32_t id_hi = 0, id_lo = 0;
   const int id_terms = ns_ident_split(p.a, &id_hi, &id_lo);
   if (id_terms == 0) return false;
@@ -357,19 +359,16 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   NsgGroup& a = g.apply;
   const GfSlot& qk = slot[qi];
   a.tbl = j.xtbl; a.tbl_per = j.xper;
-  if (wide) {   // X_K = (Q_K + 0 I) x
+  if (wide) {   // X_K = Q_K x
     a.a = qk.p; a.lda = r; a.sa = qk.st;
     a.b = bp(j.x); a.ldb = n; a.sb = mn; a.b_kr = 1; a.b_tbl = tb;
-    a.ident = 1;
-  } else {      // X_K = x (Q_K + 0 I)
+  } else {      // X_K = x Q_K
     a.a = bp(j.x); a.lda = n; a.sa = mn; a.a_tbl = tb;
     a.b = qk.p; a.ldb = r; a.sb = qk.st;
-    a.ident = 2;
   }
   a.c = mp(j.out); a.ldc = n; a.sc = mn;
   a.scale = j.scale; a.alpha_pow = j.scale ? 1 : 0; a.alpha = 1.f;
   a.M = m; a.N = n; a.K = r; a.batch = j.batch;
-  a.ident_terms = ns_ident_split(0.f, &a.ident_hi, &a.ident_lo);
   if (j.bits) {
     a.bits = j.bits;
     a.bits_stride = j.bits_stride;
@@ -379,7 +378,7 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   g.batch = j.batch;
   g.a = p.a;
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  return r % 8 == 0 && rr % 8 == 0 && mn % 8 == 0 && al(j.w.amat) && al(j.w.amat2) &&
+  return r % 8 == 0 && al(j.w.amat) && al(j.w.amat2) &&
          al(j.w.tmp);
 }
 

@@ -248,7 +248,7 @@ def test_ns_polar_matches_oracle(gpu_lib, case):
 
 @pytest.mark.parametrize("m,n,iters,gram_form", [
     (768, 3072, 5, True), (3072, 768, 5, True), (384, 1152, 2, True),
-    (768, 768, 5, False), (384, 640, 5, False), (768, 3072, 1, False)])
+    (384, 640, 5, True), (768, 768, 5, False), (640, 768, 5, False), (768, 3072, 1, False)])
 def test_ns_form_taken(gpu_lib, m, n, iters, gram_form):
     """Far-from-square cubic problems run as r x r products, others directly."""
     import matrix_aware_optimizer_momentum_amd as sm
