@@ -73,7 +73,8 @@ KINDS = ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pac
 
 
 def read_kinds(sm, steps):
-    """Per-kind kernel time and algorithmic work from the library's HIP events."""
+    """Per-kind kernel time, algorithmic work and algorithmic HBM bytes from the
+    library's HIP events."""
     kinds = {}
     for kind in KINDS:
         ms, n, work = sm.profile_read(kind)
@@ -82,7 +83,39 @@ def read_kinds(sm, steps):
                            "avg_launch_ms": ms / n, "work_per_launch": work / n,
                            "flops" if kind.startswith(("gemm", "probe")) else "bytes":
                                work / steps}
+            if kind.startswith(("gemm", "probe")):
+                hb = sm.profile_read_bytes(kind)
+                kinds[kind]["hbm_bytes"] = hb / steps
+                kinds[kind]["bytes_per_launch"] = hb / n
     return kinds
+
+
+def kind_roofline(kinds, kind, mdt):
+    """Roofline of one kernel kind.  A GEMM kind sits under the MFMA roof when
+    its arithmetic intensity (algorithmic flops / algorithmic HBM bytes) is at
+    least the ridge point peak_flops / peak_bandwidth, else under the HBM roof;
+    `achieved` is then algorithmic bytes per launch / average launch time."""
+    dk = kinds[kind]
+    out = {"kernel": kind, "avg_launch_ms": dk["avg_launch_ms"],
+           "work_per_launch": dk["work_per_launch"]}
+    secs = dk["avg_launch_ms"] * 1e-3
+    if kind.startswith(("gemm", "probe")):
+        peak_f = PEAK_TFLOPS[mdt]
+        ai = dk["flops"] / dk["hbm_bytes"] if dk.get("hbm_bytes") else float("inf")
+        ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+        out.update(arith_intensity=ai, ridge=ridge, bytes_per_launch=dk.get("bytes_per_launch"))
+        if ai >= ridge:
+            achieved = dk["work_per_launch"] / secs / 1e12
+            out.update(bound="mfma", achieved=achieved, peak=peak_f, unit="TFLOP/s")
+        else:
+            achieved = dk["bytes_per_launch"] / secs / 1e9
+            out.update(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                       tflops=dk["work_per_launch"] / secs / 1e12)
+    else:
+        achieved = dk["work_per_launch"] / secs / 1e9
+        out.update(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s")
+    out["frac"] = out["achieved"] / out["peak"]
+    return out
 
 
 def timed_steps(sm, torch, call, t, warmup, steps):
@@ -477,20 +510,12 @@ def main():
 
     kinds = read_kinds(sm, args.steps)
     dom = max(kinds, key=lambda k: kinds[k]["ms_per_step"])
-    is_mfma = dom.startswith(("gemm", "probe"))
-    dk = kinds[dom]
-    if is_mfma:
-        achieved = dk["work_per_launch"] / (dk["avg_launch_ms"] * 1e-3) / 1e12
-        peak = PEAK_TFLOPS[wl.mdt]
-        unit = "TFLOP/s"
-    else:
-        achieved = dk["work_per_launch"] / (dk["avg_launch_ms"] * 1e-3) / 1e9
-        peak = PEAK_HBM_GBS
-        unit = "GB/s"
-    roofline = {"bound": "mfma" if is_mfma else "hbm", "kernel": dom, "achieved": achieved,
-                "peak": peak, "unit": unit, "frac": achieved / peak,
-                "traffic": recorded_traffic(wl.name, dom),
-                "avg_launch_ms": dk["avg_launch_ms"], "work_per_launch": dk["work_per_launch"]}
+    rl = kind_roofline(kinds, dom, wl.mdt)
+    roofline = {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline["traffic"] = recorded_traffic(wl.name, dom)
+    roofline.update({k: v for k, v in rl.items() if k not in roofline})
+    others = {k: kind_roofline(kinds, k, wl.mdt) for k in kinds
+              if k != dom and kinds[k]["ms_per_step"] > 0.05 * ms_per_step}
 
     ns_ms = sum(kinds.get(k, {}).get("ms_per_step", 0.0) for k in ("gemm_gram", "gemm_apply",
                                                                    "gemm_rr"))
@@ -500,7 +525,12 @@ def main():
     if ns_ms > 0:
         extra["ns_tflops"] = ns_flops / (ns_ms * 1e-3) / 1e12
         extra["ns_mfma_frac"] = extra["ns_tflops"] / PEAK_TFLOPS[wl.mdt]
-        extra["ns_tflops_step"] = wl.ns_flops_per_step() / (ms_per_step * 1e-3) / 1e12
+        # the direct iteration's flop count over the whole step time: the
+        # rate the pages' form of the iteration would need to match this step
+        extra["ns_direct_form_equivalent_tflops"] = (wl.ns_flops_per_step() /
+                                                     (ms_per_step * 1e-3) / 1e12)
+    if others:
+        extra["other_rooflines"] = others
     if "vote_update" in kinds:
         vu = kinds["vote_update"]
         extra["vote_update_gbs"] = vu["bytes"] / (vu["ms_per_step"] * 1e-3) / 1e9

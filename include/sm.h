@@ -312,7 +312,10 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
  * While enabled, every kernel the library launches is bracketed by a pair of
  * HIP events on its stream, tagged with its kind and its algorithmic work
  * (flops for GEMMs, bytes for streaming kernels).  sm_profile_read waits for
- * the recorded events and returns the totals for one kind.  Enabling
+ * the recorded events and returns the totals for one kind;
+ * sm_profile_read_bytes returns the kind's algorithmic HBM bytes (every
+ * operand read once, every output written once; for streaming kinds the
+ * same as the work), from which a GEMM's arithmetic intensity follows.  Enabling
  * creates an event pool (up to 65536 launches); reading or disabling never
  * allocates.  Not thread-safe; meant for one benchmarking thread.
  * ---------------------------------------------------------------------- */
@@ -334,6 +337,7 @@ enum {
 sm_status sm_profile_enable(int on);
 sm_status sm_profile_reset(void);
 sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double* work);
+sm_status sm_profile_read_bytes(int kind, double* bytes);
 const char* sm_kernel_kind_name(int kind);
 
 #ifdef __cplusplus

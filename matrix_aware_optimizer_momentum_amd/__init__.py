@@ -9,7 +9,7 @@ from ._binding import (BF16, CACHE_MUON, ENC_BITS, ENC_INT8, F32, LION_MUON, MOD
                        SmError, lib)
 from .api import (MatrixBuffers, NSParams, StepCall, StepConfig, gram_ns_cached,
                   gram_ns_cached_ws, ns_polar, ns_polar_ws, polar_update, profile_enable,
-                  profile_read, profile_reset, sign_int8, sign_pack, spectral_norm, step, step_ws,
+                  profile_read, profile_read_bytes, profile_reset, sign_int8, sign_pack, spectral_norm, step, step_ws,
                   vote, vote_update, vote_update_int8)
 
 __all__ = [
@@ -17,7 +17,7 @@ __all__ = [
     "MODE_FORCE_REUSE", "MODE_TRIGGER", "SIGN_MUON", "UPDATE_POLAR", "UPDATE_VOTE", "SmError",
     "lib", "MatrixBuffers", "NSParams", "StepCall", "StepConfig", "gram_ns_cached",
     "gram_ns_cached_ws", "ns_polar", "ns_polar_ws", "polar_update", "profile_enable",
-    "profile_read", "profile_reset", "sign_int8", "sign_pack", "spectral_norm", "step",
+    "profile_read", "profile_read_bytes", "profile_reset", "sign_int8", "sign_pack", "spectral_norm", "step",
     "step_ws", "vote",
     "vote_update", "vote_update_int8",
 ]

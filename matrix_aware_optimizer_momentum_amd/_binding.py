@@ -77,6 +77,7 @@ SIGNATURES = {
     "sm_profile_enable": (c_int, [c_int]),
     "sm_profile_reset": (c_int, []),
     "sm_profile_read": (c_int, [c_int, P(c_double), P(c_int64), P(c_double)]),
+    "sm_profile_read_bytes": (c_int, [c_int, P(c_double)]),
     "sm_kernel_kind_name": (c_char_p, [c_int]),
 }
 

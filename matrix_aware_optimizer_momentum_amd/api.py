@@ -344,3 +344,11 @@ def profile_read(kind: str):
     B.check(B.lib().sm_profile_read(k, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work)),
             "sm_profile_read")
     return ms.value, n.value, work.value
+
+
+def profile_read_bytes(kind: str) -> float:
+    """Algorithmic HBM bytes of one kernel kind (operands read once, outputs written once)."""
+    k = B.KERNEL_KINDS.index(kind)
+    b = ctypes.c_double(0)
+    B.check(B.lib().sm_profile_read_bytes(k, ctypes.byref(b)), "sm_profile_read_bytes")
+    return b.value

@@ -362,7 +362,9 @@ sm_status launch_t(const GemmArgs& g, int kind, hipStream_t s) {
   ka.tiles_n = (g.N + BN - 1) / BN;
   ka.tiles = tiles_m * ka.tiles_n;
   dim3 grid(ka.tiles, g.batch);
-  prof_begin(kind, 2.0 * g.M * (double)g.N * g.K * g.batch, s);
+  const double bytes = ((double)g.M * g.K * dt_size(g.a.dt) + (double)g.N * g.K * dt_size(g.b.dt) +
+                        (double)g.M * g.N * (g.c ? dt_size(g.c_dt) : 0)) * g.batch;
+  prof_begin(kind, 2.0 * g.M * (double)g.N * g.K * g.batch, s, bytes);
   switch (kind) {
     case SM_K_GEMM_GRAM:
       hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_GRAM>), grid, dim3(NT), 0, s, ka);

@@ -967,7 +967,7 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
   const PtrTbl* tbls[kNsgMaxTables];
   int ntbl = 0;
   int tiles = 0;
-  double flops = 0.0;
+  double flops = 0.0, bytes = 0.0;
   for (int q = 0; q < ngroups; ++q) {
     const NsgGroup& G = groups[q];
     Grp& g = a.g[q];
@@ -1027,12 +1027,17 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     tiles += (int)gt;
     // a symmetric product is credited with the half it needs (M N K)
     flops += (g.sym ? 1.0 : 2.0) * G.M * (double)G.N * G.K * G.batch;
+    // operands read once (one operand when A and B are the same matrix),
+    // C written once (the 1-bit signs in its place)
+    const bool same = G.a == G.b && G.a_kr == G.b_kr && G.a_tbl == G.b_tbl && G.sa == G.sb;
+    bytes += ((same ? 0.0 : 2.0 * G.N * (double)G.K) + 2.0 * G.M * (double)G.K +
+              (G.bits ? G.M * (double)G.N / 8.0 : 2.0 * G.M * (double)G.N)) * G.batch;
   }
   a.ngroups = ngroups;
   a.total_tiles = tiles;
   const int grid = std::min(tiles, cu_count());
   a.xcd_chunk = (grid % 8 == 0) ? grid / 8 : 0;
-  prof_begin(kind, flops, s);
+  prof_begin(kind, flops, s, bytes);
   if (apply)
     hipLaunchKernelGGL((k_gemm_ns<ROLE_APPLY>), dim3(grid), dim3(NT), 0, s, a);
   else

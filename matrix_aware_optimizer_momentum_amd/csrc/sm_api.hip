@@ -36,7 +36,7 @@ sm_status check_launch() {
 namespace {
 struct ProfRec {
   int kind;
-  double work;
+  double work, bytes;
   hipEvent_t a, b;
 };
 constexpr size_t kProfMax = 65536;
@@ -46,12 +46,12 @@ std::vector<ProfRec> g_prof_recs;
 bool g_prof_open = false;
 }  // namespace
 
-void prof_begin(int kind, double work, hipStream_t s) {
+void prof_begin(int kind, double work, hipStream_t s, double bytes) {
   g_prof_open = false;
   if (!g_prof_on) return;
   const size_t i = g_prof_recs.size();
   if (2 * i + 1 >= g_prof_pool.size()) return;
-  ProfRec r{kind, work, g_prof_pool[2 * i], g_prof_pool[2 * i + 1]};
+  ProfRec r{kind, work, bytes < 0.0 ? work : bytes, g_prof_pool[2 * i], g_prof_pool[2 * i + 1]};
   if (hipEventRecord(r.a, s) != hipSuccess) return;
   g_prof_recs.push_back(r);
   g_prof_open = true;
@@ -1234,6 +1234,15 @@ sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double*
   *ms_total = ms;
   *launches = n;
   *work = wk;
+  return SM_OK;
+}
+
+sm_status sm_profile_read_bytes(int kind, double* bytes) {
+  if (kind < 0 || kind >= SM_K_NUM_KINDS || !bytes) return SM_ERR_ARG;
+  double b = 0.0;
+  for (const ProfRec& r : g_prof_recs)
+    if (r.kind == kind) b += r.bytes;
+  *bytes = b;
   return SM_OK;
 }
 

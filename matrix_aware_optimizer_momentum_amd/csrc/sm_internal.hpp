@@ -106,7 +106,10 @@ __device__ __forceinline__ const char* tbl_addr(const PtrTbl& t, int b, int per,
 // ---------------------------------------------------------------- launch accounting
 
 // Brackets every launch with events while profiling is enabled.
-void prof_begin(int kind, double work, hipStream_t s);
+// work: flops (GEMMs) or bytes (streaming kernels); bytes: the launch's
+// algorithmic HBM bytes (each operand read once, each output written once);
+// negative means "same as work".
+void prof_begin(int kind, double work, hipStream_t s, double bytes = -1.0);
 void prof_end(hipStream_t s);
 
 // Records a failed HIP call and maps it to SM_ERR_HIP.

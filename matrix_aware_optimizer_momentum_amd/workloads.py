@@ -82,12 +82,15 @@ class Workload:
         return sum(m * n for m, n in self.shapes)
 
     def ns_flops_per_step(self, muon_step: bool = True) -> float:
-        """Direct NS flops per step, counted as the kernels count them.
+        """NS flops per step of the direct iteration, counted as the kernels count them.
 
         Per cubic iteration and problem the two products are 2 r^2 c each
         (+2 r^3 for the quintic term).  The bf16 path computes the symmetric
         Gram product X X^T (and A^2) as one triangle, so it is credited with
         half of it: 3 r^2 c (+ r^3).  The f32 path computes full products.
+        The library runs far-from-square cubic problems in the Gram form,
+        which reaches the same X_K with fewer flops; this is the direct
+        form's count, a reference figure, not the work done.
         """
         if not muon_step or self.algo == CACHE_MUON:
             return 0.0

@@ -269,6 +269,26 @@ def test_ns_form_taken(gpu_lib, m, n, iters, gram_form):
         assert (gram_launches, apply_launches, rr_launches) == (iters, iters, 0)
 
 
+def test_profile_counts_algorithmic_bytes(gpu_lib):
+    """Each GEMM launch is credited with its operands read once and its output written once."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    b, m, n = 3, 256, 1024
+    x = torch.randn(b, m, n, device="cuda", dtype=torch.bfloat16)
+    sm.profile_enable(True)
+    try:
+        sm.profile_reset()
+        sm.ns_polar(x, params=sm.NSParams(iters=1))
+        torch.cuda.synchronize()
+        gram = sm.profile_read_bytes("gemm_gram")
+        apply_ = sm.profile_read_bytes("gemm_apply")
+        ema = sm.profile_read("norm")[2], sm.profile_read_bytes("norm")
+    finally:
+        sm.profile_enable(False)
+    assert gram == b * (2 * m * n + 2 * m * m)          # X once (A == B), B_0 written
+    assert apply_ == b * (2 * m * m + 2 * m * n + 2 * m * n)   # B_0, X read; X_1 written
+    assert ema[0] == ema[1]                              # streaming kinds: bytes = work
+
+
 def test_ns_polar_without_normalisation(gpu_lib):
     import matrix_aware_optimizer_momentum_amd as sm
     rng = np.random.default_rng(5)
