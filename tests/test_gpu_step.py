@@ -142,6 +142,26 @@ def test_sign_muon_step_matches_oracle(gpu_lib, idx, shapes):
     _check_step(wl, _cfg(wl), st, 3, wl.mdt)
 
 
+def test_sign_muon_step_mixed_forms_launches_and_parity(gpu_lib):
+    """A step whose square matrices run the direct NS and whose far-from-square
+    ones run the Gram form: parity with the oracle, and the launch schedule
+    (one Gram launch, 2K - 1 r x r launches carrying the square problems'
+    later Gram products, the square problems' applies, one final apply)."""
+    wl = W.WORKLOADS[2]
+    shapes = [(256, 256), (256, 1024), (1024, 256), (256, 256)]
+    st = Seeded(wl, shapes)
+    cfg = _cfg(wl)
+    K = cfg.ns.iters
+    sm.profile_enable(True)
+    try:
+        sm.profile_reset()
+        _check_step(wl, cfg, st, 2, wl.mdt)
+        launches = {k: sm.profile_read(k)[1] for k in ("gemm_gram", "gemm_rr", "gemm_apply")}
+    finally:
+        sm.profile_enable(False)
+    assert launches == {"gemm_gram": 1, "gemm_rr": 2 * K - 1, "gemm_apply": K}, launches
+
+
 def _composition_sign_muon(cfg, st, t):
     before_w = [mb.w.clone() for mb in st.mats]
     call = sm.StepCall(cfg, st.mats)
