@@ -86,6 +86,14 @@ int sm_version(void);
  * x, u : [batch][m][n] in dt.  u receives X_K.  x is read-only and must not
  *        overlap u.  A tall problem (m > n) is iterated on its transpose
  *        (Gram matrix n x n); x and u keep the original orientation.
+ *        With bf16 operands, cubic coefficients (c = 0), K >= 2 and a shape
+ *        far enough from square, X_K is computed in the Gram form: with
+ *        S_k = b X_k X_k^T, X_{k+1} = (S_k + aI) X_k, so X_K = Q_K X_0 with
+ *        Q_K the product of the (S_k + aI), all polynomials in X_0 X_0^T
+ *        (r x r products instead of r x max(m,n) ones).  It is the same X_K
+ *        up to rounding; the choice depends on the problem alone (shape,
+ *        dtype, K, coefficients), so sm_step gives a matrix the same bits
+ *        as this call.
  * normalize : 1 -> iterate from x / (||x||_F + eps) per problem; 0 -> from x.
  * ws   : scratch of at least sm_ns_polar_ws(...) bytes, 256-byte aligned.
  * Errors: SM_ERR_ARG (null, misaligned, overlap, bad params), SM_ERR_SHAPE
