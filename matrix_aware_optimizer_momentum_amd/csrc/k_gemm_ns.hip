@@ -442,8 +442,8 @@ __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& 
   ident_mma<IDM, IDT, IB>(acc, f0, idf, 0);
   __builtin_amdgcn_sched_barrier(0);
   // stage k + 1 must have landed; in steady state the loads of stages k + 2
-  // and k + 3 (16) follow it
-  if (wait_lenient) wait_vm<63>(); else wait_vm<16>();
+  // and k + 3 (16) follow it, after an epilogue also its >= 32 stores
+  if (wait_lenient) wait_vm<48>(); else wait_vm<16>();
   barrier_nofence();
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -462,9 +462,10 @@ __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& 
 // stage.  Step s of group kg loads stage s of the group after it (the load
 // position LP is one group ahead: group kg + 1, or the first group of the
 // workgroup's next tile), so LP moves on after step 3.  `lenient`: the tile
-// follows an epilogue, which issued at least 47 stores after the loads of
+// follows an epilogue, which issued at least 32 stores after the loads of
 // the tile's first stages (or drained them all), so in the tile's first
-// three steps vmcnt <= 63 implies the stage being waited for has landed.
+// three steps at least 48 operations follow the stage being waited for
+// (16 stage loads and 32 stores) and vmcnt <= 48 implies it has landed.
 template <int AKR, int BKR, int IDM, int IDT>
 __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                          const bf16_t* smem, uint32_t la0, int& cb,
@@ -549,52 +550,128 @@ __device__ __forceinline__ void st8(bf16_t* p, uint2 v) {
   }
 }
 
-// 16-byte store (plain: the symmetric products are read back).
-__device__ __forceinline__ void st16(bf16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// 16-byte store; STREAM marks it non-temporal.
+template <bool STREAM>
+__device__ __forceinline__ void st16(bf16_t* p, uint4 v) {
+  if constexpr (STREAM) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    __builtin_nontemporal_store(v.x, q);
+    __builtin_nontemporal_store(v.y, q + 1);
+    __builtin_nontemporal_store(v.z, q + 2);
+    __builtin_nontemporal_store(v.w, q + 3);
+  } else {
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+}
 
-// Stores this wave's 128 x 128 sub-tile (origin wr0, wc0) of alpha * acc
-// (SCALE false: alpha is 1), and its transpose into the mirror tile when
-// `mirror` (symmetric kernel only; through the wave's LDS `stage` when the
-// sub-tile is interior).  Returns with every store issued (and, for a tile
-// that is not entirely inside the matrix, the wave's memory operations
-// drained, so that the next steps' waits hold).
-template <bool SCALE, bool STREAM, bool INTERIOR>
-__device__ __forceinline__ void epilogue_body(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc,
-                                              int M, int N, int wr0, int wc0, float alpha,
-                                              bool mirror, bf16_t* stage) {
+// Stores this wave's interior 128 x 128 sub-tile (origin wr0, wc0) of
+// alpha * acc (SCALE false: alpha is 1), or with TRANSPOSED its mirror copy
+// (the sub-tile transposed, at (wc0, wr0)), through LDS: four 64 x 64 chunks
+// pass through the wave's 8 KB `stage`, written as 8-byte pieces and read
+// back as 16-byte row pieces, so that every global store instruction writes
+// 8 whole 128-byte row segments.  Straight from registers a store covered
+// 64 bytes of 8 rows (normal) or 16 bytes of 32 rows (mirror).  Chunk
+// layout: 64 rows of 128 bytes, the 16-byte piece c of row R at position
+// c ^ (R & 7).  One wave's LDS accesses execute in order, so the read-back
+// sees the chunk's writes and the next chunk's writes follow the reads.
+// Issues 32 global stores.
+template <bool SCALE, bool STREAM, bool TRANSPOSED>
+__device__ __forceinline__ void store_staged(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc,
+                                             int wr0, int wc0, float alpha, bf16_t* stage) {
   const int lane = fresh_tid() & 63;
   const int lr = lane & 31, lq = (lane >> 5) * 4;
-  constexpr bool interior = INTERIOR;
   const int cm = lane & 3;
   const int rsel = ((cm & 1) << 1) | (cm >> 1);   // which of the 4 rows this lane ends with
   const int colq = lr & ~3;
-  // The 4 x 4 blocks of 32 x 32: row-block-major in the apply kernel
-  // (STREAM), in 64 x 64 chunks (I, J) of 2 x 2 blocks in the symmetric one,
-  // whose mirror copy goes through LDS a chunk at a time.
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int I = u >> 3, J = (u >> 2) & 1;
-    const int ii = STREAM ? 0 : (u >> 1) & 1, jj = STREAM ? 0 : u & 1;
-    const int i = STREAM ? u >> 2 : 2 * I + ii, j = STREAM ? u & 3 : 2 * J + jj;
+  for (int I = 0; I < 2; ++I)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
-      uint32_t v0, v1;
-      if constexpr (SCALE) {
-        v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
-        v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
-      } else {
-        v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-        v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+    for (int J = 0; J < 2; ++J) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // rows i*32 + q*8 + lq + {0,1} (v0) and {2,3} (v1) of column j*32 + lr
+            const f32x16& a = acc[2 * I + ii][2 * J + jj];
+            uint32_t v0, v1;
+            if constexpr (SCALE) {
+              v0 = cvt2(alpha * a[q * 4 + 0], alpha * a[q * 4 + 1]);
+              v1 = cvt2(alpha * a[q * 4 + 2], alpha * a[q * 4 + 3]);
+            } else {
+              v0 = cvt2(a[q * 4 + 0], a[q * 4 + 1]);
+              v1 = cvt2(a[q * 4 + 2], a[q * 4 + 3]);
+            }
+            int R, c, off;
+            uint2 piece;
+            if constexpr (TRANSPOSED) {
+              // the 4 rows are 4 consecutive entries of mirror row jj*32 + lr
+              R = jj * 32 + lr;
+              c = ii * 4 + q;
+              off = lq;
+              piece = make_uint2(v0, v1);
+            } else {
+              // two rounds of quad shuffles: 1 row x 4 columns per lane
+              const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
+              const uint32_t mine = (cm & 1) ? v1 : v0;
+              const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
+              const uint32_t hi = (cm & 1) ? mine : recv;
+              const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
+              const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
+              const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
+              const uint32_t keep = (cm < 2) ? ra : rb;
+              piece = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
+              R = ii * 32 + q * 8 + lq + rsel;
+              const int col = jj * 32 + colq;
+              c = col >> 3;
+              off = col & 4;
+            }
+            *reinterpret_cast<uint2*>(stage + R * 64 + ((c ^ (R & 7)) * 8) + off) = piece;
+            // one piece at a time keeps few values live (the k loop's
+            // registers are all taken)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int R = t * 8 + (lane >> 3), c = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + R * 64 + ((c ^ (R & 7)) * 8));
+        bf16_t* p = TRANSPOSED ? C + (int64_t)(wc0 + J * 64 + R) * ldc + (wr0 + I * 64 + c * 8)
+                               : C + (int64_t)(wr0 + I * 64 + R) * ldc + (wc0 + J * 64 + c * 8);
+        st16<STREAM>(p, v);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (!STREAM && mirror) {   // C^T: the 4 rows are 4 consecutive entries of one row
-        if (interior) {
-          // into the chunk's LDS stage: mirror row R (of 64), 16-byte
-          // piece c at position c ^ (R & 7)
-          const int R = jj * 32 + lr, c = ii * 4 + q;
-          *reinterpret_cast<uint2*>(stage + R * 64 + ((c ^ (R & 7)) * 8) + lq) =
-              make_uint2(v0, v1);
+    }
+}
+
+// Stores a sub-tile that is not wholly inside C, element-checked (and its
+// mirror copy when `mirror`), straight from registers: two rounds of quad
+// DPP shuffles give each lane 1 row x 4 columns; the mirror's 4 rows are 4
+// consecutive entries of one row.
+template <bool SCALE, bool STREAM>
+__device__ __forceinline__ void epilogue_edge(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc,
+                                              int M, int N, int wr0, int wc0, float alpha,
+                                              bool mirror) {
+  const int lane = fresh_tid() & 63;
+  const int lr = lane & 31, lq = (lane >> 5) * 4;
+  const int cm = lane & 3;
+  const int rsel = ((cm & 1) << 1) | (cm >> 1);
+  const int colq = lr & ~3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v0, v1;
+        if constexpr (SCALE) {
+          v0 = cvt2(alpha * acc[i][j][q * 4 + 0], alpha * acc[i][j][q * 4 + 1]);
+          v1 = cvt2(alpha * acc[i][j][q * 4 + 2], alpha * acc[i][j][q * 4 + 3]);
         } else {
+          v0 = cvt2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          v1 = cvt2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        }
+        if (!STREAM && mirror) {
           const int trow = wc0 + j * 32 + lr, tcol = wr0 + i * 32 + q * 8 + lq;
           bf16_t* p = C + (int64_t)trow * ldc + tcol;
           if (trow < N) {
@@ -604,50 +681,39 @@ __device__ __forceinline__ void epilogue_body(const f32x16 (&acc)[4][4], bf16_t*
               if (tcol + e < M) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
           }
         }
-      }
-      const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
-      const uint32_t mine = (cm & 1) ? v1 : v0;
-      const uint32_t lo = (cm & 1) ? recv : mine;              // lower column
-      const uint32_t hi = (cm & 1) ? mine : recv;
-      const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);          // first row, 2 columns
-      const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);      // second row, 2 columns
-      const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
-      const uint32_t keep = (cm < 2) ? ra : rb;
-      const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
-      const int row = wr0 + i * 32 + q * 8 + lq + rsel;
-      const int col = wc0 + j * 32 + colq;
-      bf16_t* p = C + (int64_t)row * ldc + col;
-      if (interior) {
-        st8<STREAM>(p, out);
-      } else if (row < M) {
-        if (col + 4 <= N) {
-          st8<STREAM>(p, out);
-        } else {
-          const uint32_t w[2] = {out.x, out.y};
+        const uint32_t recv = dpp_xor1((cm & 1) ? v0 : v1);
+        const uint32_t mine = (cm & 1) ? v1 : v0;
+        const uint32_t lo = (cm & 1) ? recv : mine;
+        const uint32_t hi = (cm & 1) ? mine : recv;
+        const uint32_t ra = (lo & 0xFFFFu) | (hi << 16);
+        const uint32_t rb = (lo >> 16) | (hi & 0xFFFF0000u);
+        const uint32_t r2 = dpp_xor2((cm < 2) ? rb : ra);
+        const uint32_t keep = (cm < 2) ? ra : rb;
+        const uint2 out = (cm < 2) ? make_uint2(keep, r2) : make_uint2(r2, keep);
+        const int row = wr0 + i * 32 + q * 8 + lq + rsel;
+        const int col = wc0 + j * 32 + colq;
+        bf16_t* p = C + (int64_t)row * ldc + col;
+        if (row < M) {
+          if (col + 4 <= N) {
+            st8<STREAM>(p, out);
+          } else {
+            const uint32_t w[2] = {out.x, out.y};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < 4; ++e)
+              if (col + e < N) p[e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
-    }
-    if (!STREAM && interior && mirror && (u & 3) == 3) {
-      // the chunk back as 16-byte row pieces: whole 128-byte row segments of
-      // the mirror tile (one wave's LDS accesses execute in order, so these
-      // reads see the writes above and the next chunk's writes follow them)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int R = t * 8 + (lane >> 3), c = lane & 7;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + R * 64 + ((c ^ (R & 7)) * 8));
-        st16(C + (int64_t)(wc0 + J * 64 + R) * ldc + (wr0 + I * 64 + c * 8), v);
-      }
-    }
-  }
 }
 
 // The wave's sub-tile lies wholly inside C or not; readfirstlane states that
-// this is wave-uniform, so the choice is one scalar branch per tile instead
-// of an exec-mask branch around every store.
-// `stage`: this wave's 8 KB of LDS for the mirror copy (mirror only).
+// this is wave-uniform, so the choice is one scalar branch per tile.  An
+// interior sub-tile goes out through LDS (`stage`: this wave's 8 KB of the
+// free ring buffer; the caller has met the workgroup at a barrier, so every
+// wave is past its reads of it), 32 stores, 64 with the mirror copy (the
+// symmetric kernel's off-diagonal tiles); an edge sub-tile is stored element
+// by element and the wave's memory operations drained, so that the next
+// tile's first waits hold (see run_tile).
 template <bool SCALE, bool STREAM>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, int64_t ldc, int M,
                                          int N, int wr0, int wc0, float alpha, bool mirror,
@@ -655,9 +721,12 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, i
   const int inside =
       __builtin_amdgcn_readfirstlane((wr0 + 128 <= M && wc0 + 128 <= N) ? 1 : 0);
   if (inside) {
-    epilogue_body<SCALE, STREAM, true>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror, stage);
+    store_staged<SCALE, STREAM, false>(acc, C, ldc, wr0, wc0, alpha, stage);
+    if constexpr (!STREAM) {
+      if (mirror) store_staged<SCALE, false, true>(acc, C, ldc, wr0, wc0, alpha, stage);
+    }
   } else {
-    epilogue_body<SCALE, STREAM, false>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror, stage);
+    epilogue_edge<SCALE, STREAM>(acc, C, ldc, M, N, wr0, wc0, alpha, mirror);
     wait_vm<0>();
   }
 }
@@ -837,6 +906,12 @@ void k_gemm_ns(Args args) {
     // applies are not symmetric, mostly unscaled (alpha is 1 after the first
     // iteration) and their outputs stream out.
     bf16_t* C = g.c + (int64_t)tc.prob * g.sc;
+    // The stores go through the ring buffer of the stage just multiplied:
+    // the next tile's first loads target the other four, and its stage 4
+    // goes there only after the barrier of its first step.  Every wave is
+    // past its reads of that stage once all have met here.
+    bf16_t* stage = smem + (cb == 0 ? NBUF - 1 : cb - 1) * STG +
+                    4096 * __builtin_amdgcn_readfirstlane(fresh_tid() >> 6);
     if constexpr (ROLE == ROLE_APPLY) {
       if (g.bits) {   // the last iteration of a vote-mode step: signs only
         uint64_t* bp = g.bits + (int64_t)tc.prob * g.bits_stride;
@@ -844,26 +919,21 @@ void k_gemm_ns(Args args) {
           epilogue_bits<false>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
         else
           epilogue_bits<true>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
-      } else if (alpha == 1.f) {
-        epilogue<false, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, nullptr);
       } else {
-        epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, nullptr);
+        barrier_nofence();
+        if (alpha == 1.f)
+          epilogue<false, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, stage);
+        else
+          epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, stage);
       }
     } else {
-      // An off-diagonal tile also stores its mirror, staged through the ring
-      // buffer of the stage just multiplied (the next tile's first loads
-      // target the other four; its stage 4 goes there only after the
-      // barrier of its first step).  Every wave is past its reads of that
-      // stage once all have met here.
-      const bool mirror = tc.tm != tc.tn;
-      if (mirror) barrier_nofence();
-      bf16_t* stage = smem + (cb == 0 ? NBUF - 1 : cb - 1) * STG +
-                      4096 * __builtin_amdgcn_readfirstlane(fresh_tid() >> 6);
-      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, mirror, stage);
+      // an off-diagonal tile also stores its mirror copy
+      barrier_nofence();
+      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, tc.tm != tc.tn, stage);
     }
     t = tile_of(++round, vid, stride);
     if (t >= A.total_tiles) break;
-    // every epilogue issues >= 64 stores or drains (see run_tile)
+    // every epilogue issues >= 32 stores or drains (see run_tile)
     lenient = true;
   }
   wait_vm<0>();   // the loads past the last stage target this workgroup's LDS
