@@ -1,9 +1,12 @@
-// Persistent grouped bf16 GEMM for the direct Newton-Schulz products.
+// Persistent grouped bf16 GEMMs for the Newton-Schulz products.
 //
-// One launch computes every product of one kind (all Gram products X X^T,
-// or all applies B X, of one NS iteration) over several groups of batched
-// problems of different shapes: C = alpha_b * A B^T per problem, A M x K and
-// B N x K in the "operand" sense, fp32 accumulation, bf16 output.
+// Two kernels: one for symmetric products (the Gram products X X^T, and the
+// r x r products of the Gram form, whose operands are commuting symmetric
+// matrices) and one for applies ((B + aI) X, X (B + aI), Q X).  One launch
+// computes every product of one kind and step of the iteration over up to
+// eight groups of batched problems of different shapes: C = alpha_b * A B^T
+// per problem, A M x K and B N x K in the "operand" sense, fp32
+// accumulation, bf16 output.
 //
 // Operand storage.  An operand is either k-contiguous (KC: stored rows x K,
 // row-major) or k-major (KR: stored K x rows, row-major, i.e. its transpose
@@ -31,18 +34,21 @@
 // next tile's first stages load during the current tile's last steps and its
 // epilogue.
 //
-// Epilogue: value = alpha_b * acc, rounded to bf16 with v_cvt_pk_bf16_f32 and
-// stored straight from registers (no LDS: the ring holds the next tile).
-// Row-major C: two rounds of quad DPP shuffles give each lane 1 row x 4
-// columns (8-byte stores).  A symmetric product (A == B, or two commuting
-// symmetric matrices) computes only tiles with tm >= tn and stores each
-// off-diagonal tile a second time, transposed, as the mirror tile (8-byte
-// stores of 4 consecutive rows of one column).
+// Epilogue: value = alpha_b * acc, rounded to bf16 with v_cvt_pk_bf16_f32.
+// An interior sub-tile goes out through the ring buffer of the stage just
+// multiplied (free until the next tile's first barrier) in 64 x 64 chunks,
+// so that every store writes whole 128-byte row segments; edge sub-tiles are
+// stored element by element straight from registers.  A symmetric product
+// (A == B, or two commuting symmetric matrices) computes only tiles with
+// tm >= tn and stores each off-diagonal tile a second time, transposed, as
+// the mirror tile.  In a vote step the last apply stores the packed signs of
+// the values instead (wave ballots).
 //
 // Identity fold.  The apply X' = a X + B X gets a X from extra MFMAs in the
 // k-stages that cover the output's own rows (wide: (a I) X) or columns (tall:
 // X (a I)), against an a I fragment; a is split into up to two bf16 terms
-// a_hi + a_lo, whose products with bf16 data are exact in fp32.
+// a_hi + a_lo, whose products with bf16 data are exact in fp32.  The Gram
+// form's products A (B + aI) use the same fold.
 #include "sm_internal.hpp"
 
 namespace sm {
