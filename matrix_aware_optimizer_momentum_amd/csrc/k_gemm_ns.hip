@@ -1020,6 +1020,8 @@ int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits) {
   return (fl(h) + fl(l) == a) ? 2 : 0;
 }
 
+int gemm_ns_cus() { return cu_count(); }
+
 int ns_group_tables(const NsgGroup* groups, int ngroups) {
   const PtrTbl* seen[kNsgMaxGroups];
   int n = 0;

@@ -139,7 +139,7 @@ GemmArgs gemm_base(int M, int N, int K, int batch) {
 // ------------------------------------------------------------------ direct NS
 
 struct NsWs {
-  void* tmp;    // [batch][m*n] ping-pong iterate, or [batch][2][r*r] Gram-form slots
+  void* tmp;    // [batch][m*n] ping-pong iterate, or [batch][3][r*r] Gram-form slots
   void* amat;   // [batch][r*r]
   void* amat2;  // [batch][r*r] (quintic term)
 };
@@ -147,7 +147,7 @@ struct NsWs {
 void carve_ns(Carver& cv, int dt, int batch, int m, int n, NsWs& w) {
   const int64_t r = m < n ? m : n;
   const size_t es = dt_size(dt);
-  w.tmp = cv.take<void>((size_t)batch * std::max<int64_t>((int64_t)m * n, 2 * r * r) * es);
+  w.tmp = cv.take<void>((size_t)batch * std::max<int64_t>((int64_t)m * n, 3 * r * r) * es);
   w.amat = cv.take<void>((size_t)batch * r * r * es);
   w.amat2 = cv.take<void>((size_t)batch * r * r * es);
 }
@@ -268,8 +268,10 @@ sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
 // part comes from the identity fold, so S_k, T_k and Q_k are rounded to
 // bf16 once per product, like the direct form's B_k and X_k.  Storing P_k
 // instead of S_k would round its O(1) diagonal and costs several times the
-// error.  Same-iteration products run in one launch: L1(k) = {T_k, Q_{k+1}},
-// L2(k) = {S_{k+1}}, 2K - 1 launches in all.
+// error.  Launches L1(k) = {T_k, Q_{k+1}} and L2(k) = {S_{k+1}}, 2K - 1 in
+// all; Q_{k+1} (k = 1 .. K-2) may be split by problems between L1(k) and
+// L2(k) to fill L1(k)'s last round of tiles (ns_grouped).  Five r x r slots
+// per problem: S_k, Q_k, two free ones rotating, and T.
 struct GfSlot {
   bf16_t* p;
   int64_t st;   // elements between problems
@@ -277,11 +279,23 @@ struct GfSlot {
 
 struct GfPlan {
   NsgGroup gram, apply;
-  std::vector<std::vector<NsgGroup>> rr;   // [2K - 1] launches
+  // products per iteration k: T[k] = T_k, S[k] = S_{k+1} (k < K-1),
+  // Q[k] = Q_{k+1} (k >= 1); unused entries have batch 0
+  std::vector<NsgGroup> T, S, Q;
   GfSlot fill_src, fill_dst;
-  int r, batch;
+  int r, batch, tiles;   // tiles: 256 x 256 tiles of one r x r product
   float a;
 };
+
+// Problems [p0, p0 + n) of group g (no pointer tables).
+NsgGroup ns_subrange(const NsgGroup& g, int p0, int n) {
+  NsgGroup h = g;
+  h.a = g.a + (int64_t)p0 * g.sa;
+  h.b = g.b + (int64_t)p0 * g.sb;
+  h.c = g.c + (int64_t)p0 * g.sc;
+  h.batch = n;
+  return h;
+}
 
 // Executed MFMA work of one problem in 256 x 256 tile x 128-deep k-group
 // units, for the direct and the Gram form (identity groups included).
@@ -306,9 +320,10 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
   auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
   const int tb = (j.x == nullptr && j.xtbl) ? 1 : 0;
-  // two of the four r x r slots live in the iterate buffer
-  GfSlot slot[3] = {{mp(j.w.amat), rr}, {mp(j.w.amat2), rr}, {mp(j.w.tmp), 2 * rr}};
-  const GfSlot tslot{mp(j.w.tmp) + rr, 2 * rr};
+  // three of the five r x r slots live in the iterate buffer
+  GfSlot slot[4] = {{mp(j.w.amat), rr}, {mp(j.w.amat2), rr}, {mp(j.w.tmp), 3 * rr},
+                    {mp(j.w.tmp) + rr, 3 * rr}};
+  const GfSlot tslot{mp(j.w.tmp) + 2 * rr, 3 * rr};
   uint32_t id_hi = 0, id_lo = 0;
   const int id_terms = ns_ident_split(p.a, &id_hi, &id_lo);
   if (id_terms == 0) return false;
@@ -335,25 +350,26 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
     q.ident = 2; q.ident_terms = id_terms; q.ident_hi = id_hi; q.ident_lo = id_lo;
     return q;
   };
-  int si = 0, qi = 1, fi = 2;   // slots of S_k, Q_k and the free one
+  // slots of S_k and Q_k, and the two free ones (Q_{k+1}, S_{k+1} go there)
+  int si = 0, qi = 1, f1 = 2, f2 = 3;
   g.fill_src = slot[si];
   g.fill_dst = slot[qi];
-  g.rr.assign(2 * K - 1, {});
+  NsgGroup none;
+  std::memset(&none, 0, sizeof(none));
+  g.T.assign(K, none);
+  g.S.assign(K, none);
+  g.Q.assign(K, none);
   for (int k = 0; k < K; ++k) {
-    std::vector<NsgGroup>& l1 = g.rr[2 * k];
-    if (k < K - 1) l1.push_back(prod(slot[si], slot[si], tslot));       // T_k
-    if (k >= 1) {                                                       // Q_{k+1}
-      l1.push_back(prod(slot[qi], slot[si], slot[fi]));
-      std::swap(qi, fi);
-    }
-    if (k < K - 1) {                                                    // S_{k+1}
-      g.rr[2 * k + 1].push_back(prod(tslot, slot[si], slot[fi]));
-      std::swap(si, fi);
-    }
+    if (k < K - 1) g.T[k] = prod(slot[si], slot[si], tslot);         // T_k
+    if (k >= 1) g.Q[k] = prod(slot[qi], slot[si], slot[f1]);        // Q_{k+1}
+    if (k < K - 1) g.S[k] = prod(tslot, slot[si], slot[f2]);         // S_{k+1}
+    const int os = si, oq = qi;
+    if (k >= 1) { qi = f1; f1 = oq; }
+    if (k < K - 1) { si = f2; f2 = os; }
   }
-  for (const auto& l : g.rr)
-    for (const NsgGroup& q : l)
-      if (!gemm_ns_supported(q)) return false;
+  for (int k = 0; k < K; ++k)
+    for (const NsgGroup* q : {&g.T[k], &g.S[k], &g.Q[k]})
+      if (q->batch && !gemm_ns_supported(*q)) return false;
 
   std::memset(&g.apply, 0, sizeof(g.apply));
   NsgGroup& a = g.apply;
@@ -376,6 +392,7 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   if (!gemm_ns_supported(a)) return false;
   g.r = r;
   g.batch = j.batch;
+  g.tiles = (int)(((r + 255) / 256) * ((r + 255) / 256 + 1) / 2);
   g.a = p.a;
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   return r % 8 == 0 && al(j.w.amat) && al(j.w.amat2) &&
@@ -402,8 +419,54 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
   }
   std::vector<NsDesc> d(dj.size());
   const int nrr = gf.empty() ? 0 : 2 * K - 1;   // Gram-form r x r launches
+  // Tiles of the direct jobs' Gram products that ride along with Gram-form
+  // launch l (the one issued in direct iteration l + 1).
+  int64_t dtiles = 0;
+  for (const NsJob* j : dj) {
+    const int64_t tr = ((j->m < j->n ? j->m : j->n) + 255) / 256;
+    dtiles += tr * (tr + 1) / 2 * j->batch;
+  }
+  auto riders = [&](int l) { return (l + 1 <= K - 1) ? dtiles : (int64_t)0; };
+  // Q_{k+1} (k = 1 .. K-2) goes to L1(k) whole, or its first problems fill
+  // L1(k)'s last round of tiles and the rest joins L2(k), whichever needs
+  // fewer rounds of the grid (qa[k][job]: problems in L1(k)).
+  const int64_t cus = gemm_ns_cus();
+  auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
+  std::vector<std::vector<int>> qa(K, std::vector<int>(gf.size(), 0));
+  for (int k = 1; k < K; ++k) {
+    int64_t tt = 0, qt = 0, st = 0;
+    for (size_t i = 0; i < gf.size(); ++i) {
+      tt += (int64_t)gf[i].tiles * gf[i].T[k].batch;
+      qt += (int64_t)gf[i].tiles * gf[i].Q[k].batch;
+      st += (int64_t)gf[i].tiles * gf[i].S[k].batch;
+      qa[k][i] = gf[i].Q[k].batch;   // whole, unless split below
+    }
+    if (k > K - 2) continue;
+    const int64_t b1 = tt + riders(2 * k), b2 = st + riders(2 * k + 1);
+    int64_t room = rounds(b1) * cus - b1, moved = 0;
+    std::vector<int> split(gf.size(), 0);
+    for (size_t i = 0; i < gf.size(); ++i) {
+      const int n = (int)std::min<int64_t>(gf[i].Q[k].batch, room / gf[i].tiles);
+      split[i] = n;
+      room -= (int64_t)n * gf[i].tiles;
+      moved += (int64_t)n * gf[i].tiles;
+    }
+    if (rounds(b1) + rounds(b2 + qt - moved) < rounds(b1 + qt) + rounds(b2)) qa[k] = split;
+  }
   auto take_rr = [&](int l, std::vector<NsgGroup>& v) {
-    for (const GfPlan& g : gf) v.insert(v.end(), g.rr[l].begin(), g.rr[l].end());
+    const int k = l / 2;
+    for (size_t i = 0; i < gf.size(); ++i) {
+      const GfPlan& g = gf[i];
+      const NsgGroup& q = g.Q[k];
+      if (l % 2 == 0) {   // L1(k): T_k and the first qa problems of Q_{k+1}
+        if (g.T[k].batch) v.push_back(g.T[k]);
+        if (q.batch && qa[k][i]) v.push_back(ns_subrange(q, 0, qa[k][i]));
+      } else {            // L2(k): S_{k+1} and the rest of Q_{k+1}
+        if (g.S[k].batch) v.push_back(g.S[k]);
+        if (q.batch && qa[k][i] < q.batch)
+          v.push_back(ns_subrange(q, qa[k][i], q.batch - qa[k][i]));
+      }
+    }
   };
   int l = 0;
   for (int k = 0; k < K; ++k) {

@@ -299,5 +299,7 @@ int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s);
 // Distinct pointer tables among the groups.
 int ns_group_tables(const NsgGroup* groups, int ngroups);
+// Workgroups one NS GEMM launch runs at most (one per CU of the device).
+int gemm_ns_cus();
 
 }  // namespace sm

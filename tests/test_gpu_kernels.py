@@ -269,6 +269,30 @@ def test_ns_form_taken(gpu_lib, m, n, iters, gram_form):
         assert (gram_launches, apply_launches, rr_launches) == (iters, iters, 0)
 
 
+def test_ns_gram_form_split_launches(gpu_lib):
+    """300 one-tile problems: Q_{k+1} of the middle iterations is split between
+    two launches by problems (the first ones fill a launch's last round of
+    tiles); problems on both sides of the split match the oracle."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    b, m, n = 300, 256, 512
+    rng = np.random.default_rng(4242)
+    x = (0.01 * rng.standard_normal((b, m, n))).astype(np.float32)
+    xt = to_gpu(x, "bf16")
+    sm.profile_enable(True)
+    try:
+        sm.profile_reset()
+        u = sm.ns_polar(xt, params=sm.NSParams(iters=5))
+        torch.cuda.synchronize()
+        rr_launches = sm.profile_read("gemm_rr")[1]
+    finally:
+        sm.profile_enable(False)
+    assert rr_launches >= 9
+    xin, got = to_np(xt), to_np(u)
+    for k in (0, 100, 211, 212, 213, 299):
+        want = O.ns_polar(xin[k], O.NSParams(iters=5), normalize=True)
+        assert rel_fro(got[k], want) <= TOL["bf16"], k
+
+
 def test_profile_counts_algorithmic_bytes(gpu_lib):
     """Each GEMM launch is credited with its operands read once and its output written once."""
     import matrix_aware_optimizer_momentum_amd as sm
