@@ -277,43 +277,59 @@ __global__ __launch_bounds__(kThreads) void k_sign_int8(const T* x, int64_t coun
 // the table's matrices (and the vote to vote_out); otherwise V itself is
 // written, as TW, to the table's matrices.  Strides count words (ENC 0) or
 // bytes (ENC 1).
+// Vote (+ update) of one matrix's entries 8 at a time, threads bx .. of nbx:
+// sg is the matrix's first worker's signs (packed words, or int8), the M
+// workers stride entries (words / bytes) apart.
 template <int ENC, typename TW, bool UPDATE>
-__global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int64_t stride,
-                                                   int64_t mat_stride, int64_t count, PtrTbl w,
-                                                   float lr, int8_t* vote_out, bool vec) {
-  const int j = blockIdx.y;
-  TW* wp = (TW*)w.p[j];
+__device__ __forceinline__ void vote_body(const void* sg, int M, int64_t stride, int64_t count,
+                                          TW* wp, float lr, int8_t* vote_out, bool vec,
+                                          int64_t first, int64_t step) {
   const int64_t n8 = (count + 7) / 8;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8;
-       i += (int64_t)gridDim.x * kThreads) {
+  for (int64_t i = first; i < n8; i += step) {
     const int64_t e0 = 8 * i;
     int sum[8];
+    // workers 8 at a time, all 8 loads issued before their sums (a plain
+    // loop over M would wait for each worker's load in turn)
     if constexpr (ENC == 0) {
-      const uint8_t* bb =
-          reinterpret_cast<const uint8_t*>(static_cast<const uint64_t*>(signs) + j * mat_stride);
+      const uint8_t* bb = reinterpret_cast<const uint8_t*>(sg);
       const int64_t stride_bytes = stride * 8;
       uint32_t lo = 0, hi = 0;
-      for (int k = 0; k < M; ++k) {
-        const uint32_t byte = bb[(int64_t)k * stride_bytes + i];
-        lo += ((byte & 15u) * 0x00204081u) & 0x01010101u;
-        hi += ((byte >> 4) * 0x00204081u) & 0x01010101u;
+      for (int k0 = 0; k0 < M; k0 += 8) {
+        uint32_t by[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          by[q] = k0 + q < M ? (uint32_t)bb[(int64_t)(k0 + q) * stride_bytes + i] : 0u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          lo += ((by[q] & 15u) * 0x00204081u) & 0x01010101u;
+          hi += ((by[q] >> 4) * 0x00204081u) & 0x01010101u;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         sum[e] = M - 2 * (int)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
     } else {
-      const int8_t* sb = static_cast<const int8_t*>(signs) + j * mat_stride;
+      const int8_t* sb = static_cast<const int8_t*>(sg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum[e] = 0;
       const bool full = e0 + 8 <= count && (stride & 7) == 0 &&
                         (reinterpret_cast<uintptr_t>(sb + e0) & 7u) == 0;
-      for (int k = 0; k < M; ++k) {
-        const int8_t* src = sb + (int64_t)k * stride + e0;
-        if (full) {
-          const uint64_t word = *reinterpret_cast<const uint64_t*>(src);
+      if (full) {
+        for (int k0 = 0; k0 < M; k0 += 8) {
+          uint64_t wd[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sum[e] += (int)(int8_t)(uint8_t)(word >> (8 * e));
-        } else {
+          for (int q = 0; q < 8; ++q)
+            wd[q] = k0 + q < M
+                ? *reinterpret_cast<const uint64_t*>(sb + (int64_t)(k0 + q) * stride + e0)
+                : 0ull;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum[e] += (int)(int8_t)(uint8_t)(wd[q] >> (8 * e));
+        }
+      } else {
+        for (int k = 0; k < M; ++k) {
+          const int8_t* src = sb + (int64_t)k * stride + e0;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             if (e0 + e < count) sum[e] += (int)src[e];
@@ -339,6 +355,29 @@ __global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int
         if (e0 + e < count) vote_out[e0 + e] = (int8_t)vv[e];
     }
   }
+}
+
+template <int ENC, typename TW, bool UPDATE>
+__global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int64_t stride,
+                                                   int64_t mat_stride, int64_t count, PtrTbl w,
+                                                   float lr, int8_t* vote_out, bool vec) {
+  const int j = blockIdx.y;
+  const void* sg = ENC == 0
+      ? static_cast<const void*>(static_cast<const uint64_t*>(signs) + j * mat_stride)
+      : static_cast<const void*>(static_cast<const int8_t*>(signs) + j * mat_stride);
+  vote_body<ENC, TW, UPDATE>(sg, M, stride, count, (TW*)w.p[j], lr, vote_out, vec,
+                             (int64_t)blockIdx.x * kThreads + threadIdx.x,
+                             (int64_t)gridDim.x * kThreads);
+}
+
+// The vote + update of matrices of different shapes in one launch (one
+// matrix per blockIdx.y, described by the table).
+template <int ENC, typename TW>
+__global__ __launch_bounds__(kThreads) void k_vote_tbl(VoteTbl t, int M, float lr) {
+  const VoteMat& v = t.m[blockIdx.y];
+  vote_body<ENC, TW, true>(v.signs, M, v.stride, v.count, static_cast<TW*>(v.w), lr, nullptr,
+                           (v.count % 8) == 0, (int64_t)blockIdx.x * kThreads + threadIdx.x,
+                           (int64_t)gridDim.x * kThreads);
 }
 
 template <typename TD, typename TW>
@@ -556,6 +595,37 @@ sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t
   }
   prof_end(s);
   return check_launch();
+}
+
+sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt, float lr,
+                          hipStream_t s) {
+  for (int q0 = 0; q0 < nmat; q0 += kVoteMax) {
+    const int n = std::min(kVoteMax, nmat - q0);
+    VoteTbl t;
+    std::memset(&t, 0, sizeof(t));
+    int64_t need = 1;
+    double bytes = 0.0;
+    const double sign_bytes = enc == SM_ENC_BITS ? M / 8.0 : (double)M;
+    for (int q = 0; q < n; ++q) {
+      t.m[q] = mats[q0 + q];
+      const int64_t n8 = (t.m[q].count + 7) / 8;
+      need = std::max<int64_t>(need, (n8 + kThreads - 1) / kThreads);
+      bytes += (double)t.m[q].count * (sign_bytes + 2.0 * dt_size(wdt));
+    }
+    const int64_t want = (4096 + n - 1) / n;
+    const dim3 grid((unsigned)(need < want ? need : want), n);
+    prof_begin(SM_K_VOTE_UPDATE, bytes, s);
+    if (enc == SM_ENC_BITS) {
+      SM_DISPATCH_DT(wdt, TW,
+          hipLaunchKernelGGL((k_vote_tbl<0, TW>), grid, dim3(kThreads), 0, s, t, M, lr));
+    } else {
+      SM_DISPATCH_DT(wdt, TW,
+          hipLaunchKernelGGL((k_vote_tbl<1, TW>), grid, dim3(kThreads), 0, s, t, M, lr));
+    }
+    prof_end(s);
+    SM_TRY(check_launch());
+  }
+  return SM_OK;
 }
 
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,

@@ -1207,14 +1207,22 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
   std::vector<const void*> sg(chunks.size());
   for (size_t ci = 0; ci < chunks.size(); ++ci)
     sg[ci] = int8 ? (const void*)runs[ci].w.s8 : (const void*)runs[ci].w.bits;
-  if (!c->vote_polar) {
+  if (!c->vote_polar) {   // every matrix of every chunk in one launch
+    std::vector<VoteMat> vm;
     for (size_t ci = 0; ci < chunks.size(); ++ci) {
       ChunkRun& r = runs[ci];
       const int64_t stride = int8 ? r.count : r.words;
-      SM_TRY(launch_vote(c->encoding, sg[ci], M, stride, (int64_t)M * stride, r.nc, r.count,
-                         r.wt, c->wdt, c->lr, nullptr, true, s));
+      for (int j = 0; j < r.nc; ++j) {
+        VoteMat v;
+        v.signs = int8 ? static_cast<const void*>(runs[ci].w.s8 + (int64_t)j * M * stride)
+                       : static_cast<const void*>(runs[ci].w.bits + (int64_t)j * M * stride);
+        v.w = const_cast<char*>(r.wt.p[j]);
+        v.stride = stride;
+        v.count = r.count;
+        vm.push_back(v);
+      }
     }
-    return SM_OK;
+    return launch_vote_tbl(c->encoding, M, vm.data(), (int)vm.size(), c->wdt, c->lr, s);
   }
   // Optional local polar step on the vote: V (exact in mdt) -> its own
   // normalisation -> NS with the step's settings -> W <- W - lr * D.

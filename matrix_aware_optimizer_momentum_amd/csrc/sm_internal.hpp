@@ -181,6 +181,23 @@ size_t spectral_norm_ws_bytes(int batch, int m, int n);
 sm_status launch_spectral_norm(const void* a, const void* b, int dt, int batch, int m, int n,
                                const float* v0, int iters, float* out, void* ws, hipStream_t s);
 
+// One matrix of a multi-shape vote + update: its first worker's signs
+// (packed words or int8), the workers `stride` words / bytes apart, its
+// entry count and weights.
+struct VoteMat {
+  const void* signs;
+  void* w;
+  int64_t stride, count;
+};
+constexpr int kVoteMax = 96;   // matrices per launch (the table rides in the arguments)
+struct VoteTbl {
+  VoteMat m[kVoteMax];
+};
+// Vote + update (W <- rnd(fp32(W) - fp32(lr) * v)) of nmat matrices of any
+// shapes, kVoteMax per launch.
+sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt, float lr,
+                          hipStream_t s);
+
 // W <- rnd(fp32(W) - fp32(lr*D)) for nmat matrices, D contiguous [nmat][count].
 sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, const PtrTbl& w,
                               int wdt, float lr, hipStream_t s);
