@@ -38,6 +38,34 @@ __device__ __forceinline__ void load8_tail(const T* p, int64_t e0, int64_t count
   }
 }
 
+// load8_tail for data read once (the gradients): non-temporal 16-byte loads
+// keep the streams from evicting what the next kernels read back (the
+// momentum, which the Newton-Schulz launches read in place).
+template <typename T>
+__device__ __forceinline__ void load8_once(const T* p, int64_t e0, int64_t count, bool vec,
+                                           float* v) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  if (vec && e0 + 8 <= count) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + e0));
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    } else {
+      const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + e0));
+      const u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + e0 + 4));
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = __uint_as_float(w[q]);
+    }
+  } else {
+    load8_tail<T>(p, e0, count, vec, v);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store8_tail(T* p, int64_t e0, int64_t count, bool vec,
                                             const float* v) {
@@ -135,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad
     if (e0 >= count) continue;
     float mv[8], gv[8];
     load8_tail<TM>(m, e0, count, vec, mv);
-    load8_tail<TG>(g, e0, count, vec, gv);
+    load8_once<TG>(g, e0, count, vec, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = round_to<TM>(ema32(beta, mv[e], omb, gv[e]));
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
     if (e0 < count) {
       float mv[8], gv[8], dv[8];
       load8_tail<TM>(m, e0, count, vec, mv);
-      load8_tail<TG>(g, e0, count, vec, gv);
+      load8_once<TG>(g, e0, count, vec, gv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         dv[e] = ema32(b1, mv[e], omb1, gv[e]);
