@@ -815,6 +815,7 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 // operand layouts and identity mode.
 //   SYM:   0 (KC, KC)        1 (KR, KR)
 //          2 (KC, KC, B-side id, 1 term)   3 (KC, KC, B-side id, 2 terms)
+//          4 (KC, KR, A-side id, 1 term): a plain apply riding along
 //   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
 //          4 (KC, KR)        5 (KC, KC)
@@ -880,8 +881,10 @@ void k_gemm_ns(Args args) {
         run_tile<1, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 2) {
         run_tile<0, 0, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
+      } else if (g.combo == 3) {
         run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else {
+        run_tile<0, 1, 1, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
     } else {
       if (g.combo == 0) {
@@ -933,9 +936,10 @@ void k_gemm_ns(Args args) {
           epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, stage);
       }
     } else {
-      // an off-diagonal tile also stores its mirror copy
+      // an off-diagonal tile of a symmetric product also stores its mirror copy
       barrier_nofence();
-      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, tc.tm != tc.tn, stage);
+      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, g.sym && tc.tm != tc.tn,
+                            stage);
     }
     t = tile_of(++round, vid, stride);
     if (t >= A.total_tiles) break;
@@ -1080,10 +1084,12 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     // the instantiation for this group's layouts and identity mode
     int combo = -1;
     const bool two = G.ident && G.ident_terms == 2;
-    if (!apply) {
+    if (!apply && g.sym) {
       if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
       else if (!G.ident && g.a_kr && g.b_kr) combo = 1;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 2;
+    } else if (!apply) {   // an apply riding along with symmetric products
+      if (G.ident == 1 && !g.a_kr && g.b_kr && !two && !G.bits) combo = 4;
     } else {
       if (G.ident == 1 && !g.a_kr && g.b_kr) combo = two ? 2 : 0;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 1;
@@ -1091,9 +1097,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
       else if (!G.ident && !g.a_kr && !g.b_kr) combo = 5;
     }
     if (combo < 0) return SM_ERR_UNSUPPORTED;
-    // the symmetric kernel compiles only the symmetric epilogue, the apply
-    // kernel only the plain one
-    if (apply == (g.sym != 0)) return SM_ERR_UNSUPPORTED;
+    // the apply kernel compiles only the plain epilogue (the symmetric one
+    // stores a plain tile when its group is not symmetric)
+    if (apply && g.sym) return SM_ERR_UNSUPPORTED;
     g.combo = combo;
     g.tiles_m = (G.M + 255) / 256;
     g.tiles_n = (G.N + 255) / 256;

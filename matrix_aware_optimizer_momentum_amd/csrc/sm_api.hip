@@ -399,13 +399,29 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
          al(j.w.tmp);
 }
 
-// Direct NS on bf16 jobs with the grouped kernel, all jobs' products of one
-// kind and iteration in one launch; jobs that gf_plan takes run the Gram form.
-// The Gram-form jobs' Gram product shares the first launch, their r x r
-// launches take the direct jobs' Gram products of iterations 1 .. K-1 along
-// (the kernel is the same), and their apply shares the last launch.
-// Returns SM_ERR_UNSUPPORTED (nothing launched) if some job does not meet the
-// kernel's requirements.
+// Tiles of one launch of group g (256 x 256; lower triangle when symmetric).
+int64_t ns_group_tiles(const NsgGroup& g) {
+  const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
+  return (g.sym ? tm * (tm + 1) / 2 : tm * tn) * g.batch;
+}
+
+// Whether the symmetric kernel runs apply g (its one apply combo: wide,
+// one-term identity, no signs).
+bool ns_rides_sym(const NsgGroup& g) {
+  return g.ident == 1 && !g.a_kr && g.b_kr && g.ident_terms == 1 && !g.bits && !g.sym;
+}
+
+// NS on bf16 jobs with the grouped kernels.  Jobs that gf_plan takes run the
+// Gram form, the others the direct form.  Direct only: per iteration one
+// Gram launch and one apply launch for all jobs.  With Gram-form jobs: their
+// Gram products share the first launch with the direct jobs' first Gram
+// products; their 2K - 1 r x r launches carry the direct jobs' next
+// products along (the direct chain a_0, g_1, a_1, ..., g_{K-1}, one per
+// launch, when the symmetric kernel runs their applies; else only the
+// Gram products g_1 .. g_{K-1}, with the applies in launches of their own);
+// and their applies share the last launch with the direct jobs' last
+// apply.  Returns SM_ERR_UNSUPPORTED (nothing launched) if some job does not
+// meet the kernels' requirements.
 sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipStream_t s) {
   const int K = p.iters;
   std::vector<const NsJob*> dj;
@@ -417,16 +433,37 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
     else
       dj.push_back(&j);
   }
-  std::vector<NsDesc> d(dj.size());
+  // the direct jobs' products of every iteration
+  std::vector<std::vector<NsDesc>> D(K, std::vector<NsDesc>(dj.size()));
+  for (int k = 0; k < K; ++k)
+    for (size_t i = 0; i < dj.size(); ++i) {
+      const NsJob& j = *dj[i];
+      const void* cur = k == 0 ? j.x : (((K - k) % 2 == 0) ? j.out : j.w.tmp);
+      void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
+      if (!ns_desc(j, cur, dst, k == 0, k == K - 1, p, D[k][i])) return SM_ERR_UNSUPPORTED;
+    }
   const int nrr = gf.empty() ? 0 : 2 * K - 1;   // Gram-form r x r launches
-  // Tiles of the direct jobs' Gram products that ride along with Gram-form
-  // launch l (the one issued in direct iteration l + 1).
-  int64_t dtiles = 0;
-  for (const NsJob* j : dj) {
-    const int64_t tr = ((j->m < j->n ? j->m : j->n) + 255) / 256;
-    dtiles += tr * (tr + 1) / 2 * j->batch;
-  }
-  auto riders = [&](int l) { return (l + 1 <= K - 1) ? dtiles : (int64_t)0; };
+  // ride: the direct chain's applies travel in the r x r launches too
+  bool ride = nrr > 0 && !dj.empty() && p.c == 0.f;
+  for (int k = 0; ride && k < K - 1; ++k)
+    for (size_t i = 0; i < dj.size(); ++i) ride = ride && ns_rides_sym(D[k][i].apply);
+  // the direct products that travel with r x r launch l
+  auto riders_of = [&](int l, std::vector<NsgGroup>& v) {
+    for (size_t i = 0; i < dj.size(); ++i) {
+      if (ride) {
+        if (l <= 2 * K - 3) v.push_back(l % 2 == 0 ? D[l / 2][i].apply : D[(l + 1) / 2][i].gram);
+      } else if (l + 1 <= K - 1) {
+        v.push_back(D[l + 1][i].gram);
+      }
+    }
+  };
+  auto riders = [&](int l) {
+    std::vector<NsgGroup> v;
+    riders_of(l, v);
+    int64_t t = 0;
+    for (const NsgGroup& g : v) t += ns_group_tiles(g);
+    return t;
+  };
   // Q_{k+1} (k = 1 .. K-2) goes to L1(k) whole, or its first problems fill
   // L1(k)'s last round of tiles and the rest joins L2(k), whichever needs
   // fewer rounds of the grid (qa[k][job]: problems in L1(k)).
@@ -468,17 +505,36 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
       }
     }
   };
+  auto fills = [&]() -> sm_status {
+    for (const GfPlan& g : gf)
+      SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
+                                 g.r, g.batch, g.a, s));
+    return SM_OK;
+  };
+
+  if (ride) {
+    std::vector<NsgGroup> first, last;
+    for (size_t i = 0; i < dj.size(); ++i) first.push_back(D[0][i].gram);
+    for (const GfPlan& g : gf) first.push_back(g.gram);
+    SM_TRY(launch_ns_groups(first, SM_K_GEMM_GRAM, s));
+    SM_TRY(fills());
+    for (int l = 0; l < nrr; ++l) {
+      std::vector<NsgGroup> v;
+      take_rr(l, v);
+      riders_of(l, v);
+      SM_TRY(launch_ns_groups(v, SM_K_GEMM_RR, s));
+    }
+    for (size_t i = 0; i < dj.size(); ++i) last.push_back(D[K - 1][i].apply);
+    for (const GfPlan& g : gf) last.push_back(g.apply);
+    return launch_ns_groups(last, SM_K_GEMM_APPLY, s);
+  }
   int l = 0;
   for (int k = 0; k < K; ++k) {
     std::vector<NsgGroup> sym, rr, apply;
     for (size_t i = 0; i < dj.size(); ++i) {
-      const NsJob& j = *dj[i];
-      const void* cur = k == 0 ? j.x : (((K - k) % 2 == 0) ? j.out : j.w.tmp);
-      void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
-      if (!ns_desc(j, cur, dst, k == 0, k == K - 1, p, d[i])) return SM_ERR_UNSUPPORTED;
-      sym.push_back(d[i].gram);
-      if (p.c != 0.f) rr.push_back(d[i].rr);
-      apply.push_back(d[i].apply);
+      sym.push_back(D[k][i].gram);
+      if (p.c != 0.f) rr.push_back(D[k][i].rr);
+      apply.push_back(D[k][i].apply);
     }
     int kind = SM_K_GEMM_GRAM;
     if (k == 0) {
@@ -488,10 +544,7 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
       kind = SM_K_GEMM_RR;
     }
     SM_TRY(launch_ns_groups(sym, kind, s));
-    if (k == 0)
-      for (const GfPlan& g : gf)
-        SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
-                                   g.r, g.batch, g.a, s));
+    if (k == 0) SM_TRY(fills());
     if (!rr.empty()) SM_TRY(launch_ns_groups(rr, SM_K_GEMM_RR, s));
     if (k == K - 1) {   // the rest of the Gram-form chain, then every last apply
       for (; l < nrr; ++l) {

@@ -309,10 +309,12 @@ bool gemm_ns_supported(const NsgGroup& g);
 // Splits a into bf16 terms hi (+ lo); returns the number of terms whose sum
 // is exactly a (1 or 2), or 0 if two do not suffice.
 int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
-// All groups of one launch are symmetric products (kind SM_K_GEMM_GRAM or
-// SM_K_GEMM_RR, which differ only in the kernel-time accounting) or all are
-// applies (SM_K_GEMM_APPLY).  Returns SM_ERR_UNSUPPORTED for more than
-// kNsgMaxTables distinct tables.
+// Kinds SM_K_GEMM_GRAM and SM_K_GEMM_RR (which differ only in the kernel-time
+// accounting) run the symmetric-product kernel: symmetric groups, plus wide
+// applies with a one-term identity and no signs riding along; kind
+// SM_K_GEMM_APPLY runs the apply kernel (applies only).  Returns
+// SM_ERR_UNSUPPORTED for other groups or more than kNsgMaxTables distinct
+// tables.
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s);
 // Distinct pointer tables among the groups.
 int ns_group_tables(const NsgGroup* groups, int ngroups);
