@@ -815,7 +815,8 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 // operand layouts and identity mode.
 //   SYM:   0 (KC, KC)        1 (KR, KR)
 //          2 (KC, KC, B-side id, 1 term)   3 (KC, KC, B-side id, 2 terms)
-//          4 (KC, KR, A-side id, 1 term): a plain apply riding along
+//          4 (KC, KR, A-side id, 1 term)
+//          (2 to 4 also take plain applies riding along: tall 2/3, wide 4)
 //   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
 //          4 (KC, KR)        5 (KC, KC)
@@ -1088,8 +1089,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
       if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
       else if (!G.ident && g.a_kr && g.b_kr) combo = 1;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 2;
-    } else if (!apply) {   // an apply riding along with symmetric products
-      if (G.ident == 1 && !g.a_kr && g.b_kr && !two && !G.bits) combo = 4;
+    } else if (!apply && !G.bits) {   // an apply riding along with symmetric products
+      if (G.ident == 1 && !g.a_kr && g.b_kr && !two) combo = 4;
+      else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 2;
     } else {
       if (G.ident == 1 && !g.a_kr && g.b_kr) combo = two ? 2 : 0;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 1;

@@ -405,10 +405,12 @@ int64_t ns_group_tiles(const NsgGroup& g) {
   return (g.sym ? tm * (tm + 1) / 2 : tm * tn) * g.batch;
 }
 
-// Whether the symmetric kernel runs apply g (its one apply combo: wide,
-// one-term identity, no signs).
+// Whether the symmetric kernel runs apply g: its combos take the tall apply
+// X (B + aI) and the wide (B + aI) X with a one-term identity, not signs.
 bool ns_rides_sym(const NsgGroup& g) {
-  return g.ident == 1 && !g.a_kr && g.b_kr && g.ident_terms == 1 && !g.bits && !g.sym;
+  if (g.sym || g.bits) return false;
+  if (g.ident == 2) return !g.a_kr && !g.b_kr;
+  return g.ident == 1 && !g.a_kr && g.b_kr && g.ident_terms == 1;
 }
 
 // NS on bf16 jobs with the grouped kernels.  Jobs that gf_plan takes run the

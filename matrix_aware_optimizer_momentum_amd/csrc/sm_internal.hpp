@@ -310,8 +310,8 @@ bool gemm_ns_supported(const NsgGroup& g);
 // is exactly a (1 or 2), or 0 if two do not suffice.
 int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
 // Kinds SM_K_GEMM_GRAM and SM_K_GEMM_RR (which differ only in the kernel-time
-// accounting) run the symmetric-product kernel: symmetric groups, plus wide
-// applies with a one-term identity and no signs riding along; kind
+// accounting) run the symmetric-product kernel: symmetric groups, plus tall
+// applies and wide ones with a one-term identity (no signs) riding along; kind
 // SM_K_GEMM_APPLY runs the apply kernel (applies only).  Returns
 // SM_ERR_UNSUPPORTED for other groups or more than kNsgMaxTables distinct
 // tables.

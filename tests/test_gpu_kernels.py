@@ -17,6 +17,9 @@ from tests.helpers import rel_fro, to_gpu, to_np, words_np
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# an identity coefficient that is exactly the sum of two bf16 values
+# (1.296875 + 0.0031280517578125), unlike 1.3, which has no such split
+A2 = 1.3000030517578125
 
 
 def _special(rng, n):
@@ -209,21 +212,25 @@ NS_CASES = [
     ("bf16", 2, 256, 1024, 5, (1.8, -0.6, 0.04)),
     ("bf16", 1, 1280, 1280, 5, (1.5, -0.5, 0.0)),
     # 256-tile NT kernel with partial tiles (dimensions multiples of 128):
-    # identity fold (a = 1.5 exact in bf16) and the general a path (1.3)
+    # identity fold with a = 1.5 (one bf16 term), A2 (two terms), and 1.3
+    # (no exact split: the general path of separate products)
     ("bf16", 2, 384, 640, 5, (1.5, -0.5, 0.0)),
     ("bf16", 2, 640, 384, 5, (1.5, -0.5, 0.0)),
     ("bf16", 3, 128, 1152, 3, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 640, 768, 5, (A2, 1.0 - A2, 0.0)),
+    ("bf16", 2, 768, 640, 4, (A2, 1.0 - A2, 0.0)),
     ("bf16", 2, 384, 640, 5, (1.3, -0.3, 0.0)),
     ("bf16", 2, 640, 384, 4, (1.3, -0.3, 0.0)),
     # cubic on far-from-square shapes: the Gram form (r x r products), one
-    # and several tiles, partial tiles, the two-term identity split (1.3),
+    # and several tiles, partial tiles, the two-term identity split (A2),
     # the fewest iterations it takes (2), wide and tall
     ("bf16", 2, 256, 1024, 5, (1.5, -0.5, 0.0)),
     ("bf16", 2, 1024, 256, 4, (1.5, -0.5, 0.0)),
-    ("bf16", 3, 384, 1152, 2, (1.3, -0.3, 0.0)),
+    ("bf16", 3, 384, 1152, 2, (A2, 1.0 - A2, 0.0)),
     ("bf16", 1, 128, 4096, 5, (1.5, -0.5, 0.0)),
     ("bf16", 2, 640, 1920, 3, (1.5, -0.5, 0.0)),
-    ("bf16", 2, 1920, 640, 6, (1.3, -0.3, 0.0)),
+    ("bf16", 2, 1920, 640, 6, (A2, 1.0 - A2, 0.0)),
+    ("bf16", 2, 1920, 640, 3, (1.3, -0.3, 0.0)),
 ]
 
 
@@ -246,17 +253,19 @@ def test_ns_polar_matches_oracle(gpu_lib, case):
         assert err <= TOL[dt], (k, err)
 
 
-@pytest.mark.parametrize("m,n,iters,gram_form", [
-    (768, 3072, 5, True), (3072, 768, 5, True), (384, 1152, 2, True),
-    (384, 640, 5, True), (768, 768, 5, False), (640, 768, 5, False), (768, 3072, 1, False)])
-def test_ns_form_taken(gpu_lib, m, n, iters, gram_form):
-    """Far-from-square cubic problems run as r x r products, others directly."""
+@pytest.mark.parametrize("m,n,iters,a,gram_form", [
+    (768, 3072, 5, 1.5, True), (3072, 768, 5, 1.5, True), (384, 1152, 2, 1.5, True),
+    (384, 640, 5, 1.5, True), (1920, 640, 6, A2, True), (768, 768, 5, 1.5, False),
+    (640, 768, 5, 1.5, False), (768, 3072, 1, 1.5, False), (1920, 640, 6, 1.3, False)])
+def test_ns_form_taken(gpu_lib, m, n, iters, a, gram_form):
+    """Far-from-square cubic problems run as r x r products, others directly
+    (and so does every problem whose a has no exact two-term bf16 split)."""
     import matrix_aware_optimizer_momentum_amd as sm
     x = torch.randn(2, m, n, device="cuda", dtype=torch.bfloat16)
     sm.profile_enable(True)
     try:
         sm.profile_reset()
-        sm.ns_polar(x, params=sm.NSParams(iters=iters))
+        sm.ns_polar(x, params=sm.NSParams(iters=iters, a=a, b=1.0 - a, c=0.0))
         torch.cuda.synchronize()
         rr_launches = sm.profile_read("gemm_rr")[1]
         gram_launches = sm.profile_read("gemm_gram")[1]

@@ -142,12 +142,16 @@ def test_sign_muon_step_matches_oracle(gpu_lib, idx, shapes):
     _check_step(wl, _cfg(wl), st, 3, wl.mdt)
 
 
-@pytest.mark.parametrize("shapes,applies", [
+@pytest.mark.parametrize("shapes,a,applies", [
     # square (direct, wide): its applies ride in the r x r launches
-    ([(256, 256), (256, 1024), (1024, 256), (256, 256)], 1),
-    # tall direct (768 x 640): its applies keep launches of their own
-    ([(768, 640), (256, 1024)], 5)], ids=["square-rides", "tall-own-launches"])
-def test_sign_muon_step_mixed_forms_launches_and_parity(gpu_lib, shapes, applies):
+    ([(256, 256), (256, 1024), (1024, 256), (256, 256)], 1.5, 1),
+    # tall direct (768 x 640): rides as well
+    ([(768, 640), (256, 1024)], 1.5, 1),
+    # wide direct with a two-term identity (1.296875 + 0.0031280517578125):
+    # launches of its own
+    ([(256, 256), (256, 1024)], 1.3000030517578125, 5)],
+    ids=["square-rides", "tall-rides", "two-term-own-launches"])
+def test_sign_muon_step_mixed_forms_launches_and_parity(gpu_lib, shapes, a, applies):
     """A step whose square-ish matrices run the direct NS and whose
     far-from-square ones run the Gram form: parity with the oracle, and the
     launch schedule (one Gram launch, 2K - 1 r x r launches carrying the
@@ -155,7 +159,7 @@ def test_sign_muon_step_mixed_forms_launches_and_parity(gpu_lib, shapes, applies
     symmetric kernel does not run get launches of their own)."""
     wl = W.WORKLOADS[2]
     st = Seeded(wl, shapes)
-    cfg = _cfg(wl)
+    cfg = _cfg(wl, ns=sm.NSParams(wl.ns_iters, a, 1.0 - a, 0.0, wl.ns_eps))
     K = cfg.ns.iters
     sm.profile_enable(True)
     try:
