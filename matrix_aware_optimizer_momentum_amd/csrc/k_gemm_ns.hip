@@ -82,6 +82,8 @@ struct Grp {
   float alpha;
   int tiles_m, tiles_n, tiles_per_prob, tile_begin;
   int a_tbl, b_tbl, tbl_per;   // per-matrix operand addressing (see NsgGroup)
+  int a_low, b_low;            // operand stored as its lower triangle of tiles
+  int c_low;                   // symmetric C: store the lower triangle only
   int tbl;                     // byte offset of the group's table in Args
   uint64_t* bits;              // apply: signs instead of C (see NsgGroup)
   int64_t bits_stride;
@@ -192,14 +194,26 @@ struct LoadPos {
   int r;        // round of the tile (tile = tile_of(r, workgroup, stride))
   int kg;       // group of 4 stages within the tile
   int nkg;      // groups in the tile
+  int sw;       // next group where a lower-stored operand turns to KR reads
 };
 
-__device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r, int t) {
+// The first group past the diagonal block of panel p (256 operand rows, two
+// groups of 128 k): from there on a lower-stored operand's panel entries
+// (p, k) live in the stored tiles (k, p) and are read transposed (KR).
+__device__ __forceinline__ int low_switch(int p, int nkg) {
+  return 2 * (p + 1) < nkg ? 2 * (p + 1) : nkg;
+}
+
+// Load position: group kg of tile t (round r), with the per-lane offsets of
+// the operand layouts that group reads.
+__device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r, int t,
+                                                int kg = 0) {
   // The tile index is wave-uniform; readfirstlane states it, so that the
   // decode and the argument reads are scalar (a vector read of the arguments
   // would wait for every load in flight).
   t = __builtin_amdgcn_readfirstlane(t);
   r = __builtin_amdgcn_readfirstlane(r);
+  kg = __builtin_amdgcn_readfirstlane(kg);
   const Tile tl = decode_tile(A, t);
   const Grp& g = A.g[tl.gi];
   // the group's table, addressed by its byte offset in the arguments (an
@@ -209,24 +223,33 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r
                     : reinterpret_cast<const char*>(g.a + (int64_t)tl.prob * g.sa);
   L.bbase = g.b_tbl ? tbl_addr(*tb, tl.prob, g.tbl_per, 2 * g.sb)
                     : reinterpret_cast<const char*>(g.b + (int64_t)tl.prob * g.sb);
-  dma_offsets(L.aoff, g.a_kr, g.lda, tl.tm * 256, g.M);
-  dma_offsets(L.boff, g.b_kr, g.ldb, tl.tn * 256, g.N);
-  L.akst = g.a_kr ? (uint32_t)(2 * g.lda) : 2u;
-  L.bkst = g.b_kr ? (uint32_t)(2 * g.ldb) : 2u;
+  const int nkg = g.K / (4 * BK);
+  const int asw = g.a_low ? low_switch(tl.tm, nkg) : nkg;
+  const int bsw = g.b_low ? low_switch(tl.tn, nkg) : nkg;
+  const int akr = g.a_kr || kg >= asw, bkr = g.b_kr || kg >= bsw;
+  dma_offsets(L.aoff, akr, g.lda, tl.tm * 256, g.M);
+  dma_offsets(L.boff, bkr, g.ldb, tl.tn * 256, g.N);
+  L.akst = akr ? (uint32_t)(2 * g.lda) : 2u;
+  L.bkst = bkr ? (uint32_t)(2 * g.ldb) : 2u;
   L.r = r;
-  L.kg = 0;
-  L.nkg = g.K / (4 * BK);
+  L.kg = kg;
+  L.nkg = nkg;
+  L.sw = kg < asw ? (kg < bsw && bsw < asw ? bsw : asw) : (kg < bsw ? bsw : nkg);
 }
 
 // The group after p: the next group of the same tile, else the first group of
 // the workgroup's next tile; past the last tile p itself (its stages are then
 // loaded again into buffers that are never multiplied).
 __device__ __forceinline__ void load_advance(LoadPos& p, const Args& A, int vid, int stride) {
-  if (p.kg + 1 < p.nkg) {
+  if (p.kg + 1 < p.nkg && p.kg + 1 != p.sw) {
     ++p.kg;
   } else {
-    const int nt = tile_of(p.r + 1, vid, stride);
-    if (nt < A.total_tiles) load_tile_setup(p, A, p.r + 1, nt);
+    // the next tile, or the same tile where an operand turns to KR reads
+    // (one setup for both, so that it is inlined once)
+    const bool next = p.kg + 1 >= p.nkg;
+    const int r = next ? p.r + 1 : p.r;
+    const int nt = tile_of(r, vid, stride);
+    if (nt < A.total_tiles) load_tile_setup(p, A, r, nt, next ? 0 : p.kg + 1);
   }
 }
 
@@ -472,16 +495,18 @@ __device__ __forceinline__ void nsg_step(f32x16 (&acc)[4][4], Frags& f0, Frags& 
 // the tile's first stages (or drained them all), so in the tile's first
 // three steps at least 48 operations follow the stage being waited for
 // (16 stage loads and 32 stores) and vmcnt <= 48 implies it has landed.
+// Groups kg0 .. kg1 - 1 of a tile, all read with layouts (AKR, BKR).
 template <int AKR, int BKR, int IDM, int IDT>
-__device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
-                                         const bf16_t* smem, uint32_t la0, int& cb,
-                                         uint32_t wbase, LoadPos& LP, const Args& A, int vid,
-                                         int stride, int nkg, int id_g, int wm, int wn,
-                                         const Ident& id, bool lenient) {
+__device__ __forceinline__ void run_groups(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                           const bf16_t* smem, uint32_t la0, int& cb,
+                                           uint32_t wbase, LoadPos& LP, const Args& A, int vid,
+                                           int stride, int kg0, int kg1, int id_g, int wm,
+                                           int wn, const Ident& id, bool lenient) {
+  if (kg0 >= kg1) return;
   const FragOffs<AKR> fa(wm * 128);
   const FragOffs<BKR> fb(wn * 128);
-  // slice 0 of the tile's first stage (the previous tile's last step read it
-  // with that tile's layouts, so it is read again with this tile's)
+  // slice 0 of the first stage (the step before read it with the layouts of
+  // the previous tile or segment, so it is read again with these)
   {
     const bf16_t* c0 = smem + cb * STG;
 #pragma unroll
@@ -489,7 +514,7 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
 #pragma unroll
     for (int i = 0; i < 4; ++i) f0.b[i] = frag<BKR>(c0 + HALF, fb, i, 0);
   }
-  for (int kg = 0; kg < nkg; ++kg) {
+  for (int kg = kg0; kg < kg1; ++kg) {
 #define SM_NSG_STEP(S_, IDM_)                                                               \
     {                                                                                       \
       const int nb = cb == NBUF - 1 ? 0 : cb + 1;                                           \
@@ -528,6 +553,50 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
     // whose condition the compiler takes for divergent, the next tile's
     // arguments stay scalar loads
     load_advance(LP, A, vid, stride);
+  }
+}
+
+template <int AKR, int BKR, int IDM, int IDT>
+__device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                         const bf16_t* smem, uint32_t la0, int& cb,
+                                         uint32_t wbase, LoadPos& LP, const Args& A, int vid,
+                                         int stride, int nkg, int id_g, int wm, int wn,
+                                         const Ident& id, bool lenient) {
+  run_groups<AKR, BKR, IDM, IDT>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, 0, nkg,
+                                 id_g, wm, wn, id, lenient);
+}
+
+// A tile with lower-stored operands: k segments of fixed layouts, split where
+// an operand's panel passes its diagonal block (asw for A, bsw for B; see
+// low_switch).  LOW 3: both operands (symmetric tile, tn <= tm, so B turns
+// first); 1: A only, B KR; 2: B only, A KC.  The identity group of a panel
+// lies in its diagonal block, before the switch, so only the first segment
+// carries the identity MFMAs.
+template <int LOW, int IDM, int IDT>
+__device__ __forceinline__ void run_tile_low(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                             const bf16_t* smem, uint32_t la0, int& cb,
+                                             uint32_t wbase, LoadPos& LP, const Args& A,
+                                             int vid, int stride, int nkg, int asw, int bsw,
+                                             int id_g, int wm, int wn, const Ident& id,
+                                             bool lenient) {
+  static_assert(LOW != 3 || IDM != 1, "an A-side identity group may follow B's switch");
+  if constexpr (LOW == 3) {
+    run_groups<0, 0, IDM, IDT>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, 0, bsw,
+                               id_g, wm, wn, id, lenient);
+    run_groups<0, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, bsw, asw,
+                           id_g, wm, wn, id, false);
+    run_groups<1, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, asw, nkg,
+                           id_g, wm, wn, id, false);
+  } else if constexpr (LOW == 1) {
+    run_groups<0, 1, IDM, IDT>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, 0, asw,
+                               id_g, wm, wn, id, lenient);
+    run_groups<1, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, asw, nkg,
+                           id_g, wm, wn, id, false);
+  } else {
+    run_groups<0, 0, IDM, IDT>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, 0, bsw,
+                               id_g, wm, wn, id, lenient);
+    run_groups<0, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, bsw, nkg,
+                           id_g, wm, wn, id, false);
   }
 }
 
@@ -816,16 +885,22 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 //   SYM:   0 (KC, KC)        1 (KR, KR)
 //          2 (KC, KC, B-side id, 1 term)   3 (KC, KC, B-side id, 2 terms)
 //          4 (KC, KR, A-side id, 1 term)
+//          5 (both lower-stored, B-side id, 1 term)
 //          (2 to 4 also take plain applies riding along: tall 2/3, wide 4)
 //   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
 //          4 (KC, KR)        5 (KC, KC)
+//          6 (A lower-stored, KR)          7 (KC, B lower-stored)
 constexpr int ROLE_SYM = 0, ROLE_APPLY = 1;
 template <int ROLE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_ns(Args args) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[NBUF * STG];
-  const Args& A = args;   // read in place from the kernel argument segment
+  // Read in place from the kernel argument segment, where args is the only
+  // explicit argument (offset 0).  Through the parameter itself the compiler
+  // copied all of Args to scratch once the kernel had grown past some size.
+  (void)args;
+  const Args& A = *(const Args*)(__builtin_amdgcn_kernarg_segment_ptr());
   int vid = blockIdx.x;
   if (A.xcd_chunk > 0) vid = (vid & 7) * A.xcd_chunk + (vid >> 3);
   const int stride = gridDim.x;
@@ -884,8 +959,12 @@ void k_gemm_ns(Args args) {
         run_tile<0, 0, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 3) {
         run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
+      } else if (g.combo == 4) {
         run_tile<0, 1, 1, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else {
+        run_tile_low<3, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg,
+                              low_switch(tc.tm, nkg), low_switch(tc.tn, nkg), id_g, wm, wn, id,
+                              lenient);
       }
     } else {
       if (g.combo == 0) {
@@ -898,8 +977,14 @@ void k_gemm_ns(Args args) {
         run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 4) {
         run_tile<0, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
+      } else if (g.combo == 5) {
         run_tile<0, 0, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else if (g.combo == 6) {
+        run_tile_low<1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg,
+                              low_switch(tc.tm, nkg), nkg, id_g, wm, wn, id, lenient);
+      } else {
+        run_tile_low<2, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, nkg,
+                              low_switch(tc.tn, nkg), id_g, wm, wn, id, lenient);
       }
     }
     wm = (fresh_tid() >> 6) >> 1;
@@ -937,10 +1022,11 @@ void k_gemm_ns(Args args) {
           epilogue<true, true>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, false, stage);
       }
     } else {
-      // an off-diagonal tile of a symmetric product also stores its mirror copy
+      // an off-diagonal tile of a symmetric product also stores its mirror
+      // copy, unless C is kept as its lower triangle
       barrier_nofence();
-      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha, g.sym && tc.tm != tc.tn,
-                            stage);
+      epilogue<true, false>(acc, C, g.ldc, g.M, g.N, wr0, wc0, alpha,
+                            g.sym && !g.c_low && tc.tm != tc.tn, stage);
     }
     t = tile_of(++round, vid, stride);
     if (t >= A.total_tiles) break;
@@ -997,6 +1083,10 @@ bool gemm_ns_supported(const NsgGroup& G) {
     return false;
   if (G.ident == 1 && G.K != G.M) return false;
   if (G.ident == 2 && G.K != G.N) return false;
+  // lower-stored operands: square KC matrices; C kept lower only when symmetric
+  if (G.a_low && (G.a_kr || G.a_tbl || G.M != G.K || G.M % 8)) return false;
+  if (G.b_low && (G.b_kr || G.b_tbl || G.N != G.K || G.N % 8)) return false;
+  if (G.c_low && !G.sym) return false;
   return true;
 }
 
@@ -1071,6 +1161,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.a_tbl = G.a_tbl ? 1 : 0;
     g.b_tbl = G.b_tbl ? 1 : 0;
     g.tbl_per = G.tbl_per;
+    g.a_low = G.a_low ? 1 : 0;
+    g.b_low = G.b_low ? 1 : 0;
+    g.c_low = G.c_low ? 1 : 0;
     if (G.a_tbl || G.b_tbl) {
       int ti = 0;
       while (ti < ntbl && tbls[ti] != G.tbl) ++ti;
@@ -1085,13 +1178,21 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     // the instantiation for this group's layouts and identity mode
     int combo = -1;
     const bool two = G.ident && G.ident_terms == 2;
+    const int low = (g.a_low ? 1 : 0) | (g.b_low ? 2 : 0);
     if (!apply && g.sym) {
-      if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
+      if (low == 3) {
+        if (G.ident == 2 && !two) combo = 5;
+      } else if (low) {
+      } else if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
       else if (!G.ident && g.a_kr && g.b_kr) combo = 1;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 2;
     } else if (!apply && !G.bits) {   // an apply riding along with symmetric products
-      if (G.ident == 1 && !g.a_kr && g.b_kr && !two) combo = 4;
+      if (low) {
+      } else if (G.ident == 1 && !g.a_kr && g.b_kr && !two) combo = 4;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 2;
+    } else if (low) {
+      if (!G.ident && low == 1 && g.b_kr) combo = 6;
+      else if (!G.ident && low == 2 && !g.a_kr) combo = 7;
     } else {
       if (G.ident == 1 && !g.a_kr && g.b_kr) combo = two ? 2 : 0;
       else if (G.ident == 2 && !g.a_kr && !g.b_kr) combo = two ? 3 : 1;
@@ -1113,11 +1214,16 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     tiles += (int)gt;
     // a symmetric product is credited with the half it needs (M N K)
     flops += (g.sym ? 1.0 : 2.0) * G.M * (double)G.N * G.K * G.batch;
-    // operands read once (one operand when A and B are the same matrix),
-    // C written once (the 1-bit signs in its place)
-    const bool same = G.a == G.b && G.a_kr == G.b_kr && G.a_tbl == G.b_tbl && G.sa == G.sb;
-    bytes += ((same ? 0.0 : 2.0 * G.N * (double)G.K) + 2.0 * G.M * (double)G.K +
-              (G.bits ? G.M * (double)G.N / 8.0 : 2.0 * G.M * (double)G.N)) * G.batch;
+    // stored entries of each operand read once (one operand when A and B
+    // are the same matrix), C written once (the 1-bit signs in its place);
+    // a lower-stored matrix holds only its tiles on and below the diagonal
+    const bool same = G.a == G.b && G.a_kr == G.b_kr && G.a_tbl == G.b_tbl && G.sa == G.sb &&
+                      G.a_low == G.b_low;
+    const double ea = G.a_low ? lower_tile_entries(G.M) : G.M * (double)G.K;
+    const double eb = G.b_low ? lower_tile_entries(G.N) : G.N * (double)G.K;
+    const double ec = G.bits ? G.M * (double)G.N / 16.0
+                             : (G.c_low ? lower_tile_entries(G.M) : G.M * (double)G.N);
+    bytes += 2.0 * ((same ? 0.0 : eb) + ea + ec) * G.batch;
   }
   a.ngroups = ngroups;
   a.total_tiles = tiles;

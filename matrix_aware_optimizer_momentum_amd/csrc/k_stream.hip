@@ -429,10 +429,11 @@ __global__ __launch_bounds__(kThreads) void k_polar_update(const TD* d, int64_t 
 
 // q = s + a I for a batch of r x r bf16 matrices (problem p at s + p ss and
 // q + p sq), summed in float32 and rounded to bf16.  Eight consecutive
-// entries of one row per thread (r % 8 == 0, 16-byte aligned rows).
+// entries of one row per thread (r % 8 == 0, 16-byte aligned rows); with
+// `lower`, entries of 256 x 256 tiles above the diagonal are skipped.
 __global__ __launch_bounds__(kThreads) void k_add_identity(const bf16_t* s, int64_t ss,
                                                            bf16_t* q, int64_t sq, int r,
-                                                           float a) {
+                                                           float a, int lower) {
   const int64_t rr = (int64_t)r * r;
   const bf16_t* sp = s + (int64_t)blockIdx.y * ss;
   bf16_t* qp = q + (int64_t)blockIdx.y * sq;
@@ -442,6 +443,7 @@ __global__ __launch_bounds__(kThreads) void k_add_identity(const bf16_t* s, int6
     load8<bf16_t>(sp + e0, v);
     const int64_t row = e0 / r;
     const int64_t d = row - (e0 - row * r);   // diagonal entry's offset in the eight
+    if (lower && ((e0 - row * r) >> 8) > (row >> 8)) continue;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (d == e) v[e] = __fadd_rn(v[e], a);
@@ -674,7 +676,7 @@ sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, c
 
 
 sm_status launch_add_identity(const bf16_t* src, int64_t ss, bf16_t* dst, int64_t sq, int r,
-                              int batch, float a, hipStream_t s) {
+                              int batch, float a, bool lower, hipStream_t s) {
   if (batch <= 0 || r <= 0) return SM_OK;
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (r % 8 || ss % 8 || sq % 8 || !al(src) || !al(dst)) return SM_ERR_UNSUPPORTED;
@@ -682,8 +684,10 @@ sm_status launch_add_identity(const bf16_t* src, int64_t ss, bf16_t* dst, int64_
   int64_t want = (2048 + batch - 1) / batch;
   const int64_t need = (n8 + kThreads - 1) / kThreads;
   dim3 grid((unsigned)(need < want ? need : want), batch);
-  prof_begin(SM_K_MISC, (double)batch * r * r * 4.0, s);
-  hipLaunchKernelGGL(k_add_identity, grid, dim3(kThreads), 0, s, src, ss, dst, sq, r, a);
+  prof_begin(SM_K_MISC, (double)batch * (lower ? lower_tile_entries(r) : (double)r * r) * 4.0,
+             s);
+  hipLaunchKernelGGL(k_add_identity, grid, dim3(kThreads), 0, s, src, ss, dst, sq, r, a,
+                     lower ? 1 : 0);
   prof_end(s);
   return check_launch();
 }

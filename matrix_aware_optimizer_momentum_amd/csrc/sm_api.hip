@@ -327,6 +327,10 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   uint32_t id_hi = 0, id_lo = 0;
   const int id_terms = ns_ident_split(p.a, &id_hi, &id_lo);
   if (id_terms == 0) return false;
+  // S_k, T_k, Q_k are symmetric: with a one-term identity the products keep
+  // only their tiles on and below the diagonal, and read the rest of a panel
+  // from the mirror tiles (no mirror stores)
+  const int low = id_terms == 1 ? 1 : 0;
 
   std::memset(&g.gram, 0, sizeof(g.gram));
   NsgGroup& gr = g.gram;
@@ -335,7 +339,7 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   gr.tbl = j.xtbl; gr.tbl_per = j.xper; gr.a_tbl = tb; gr.b_tbl = tb;
   gr.c = slot[0].p; gr.ldc = r; gr.sc = slot[0].st;
   gr.scale = j.scale; gr.alpha_pow = j.scale ? 2 : 0; gr.alpha = p.b;
-  gr.M = r; gr.N = r; gr.K = cols; gr.batch = j.batch; gr.sym = 1;
+  gr.M = r; gr.N = r; gr.K = cols; gr.batch = j.batch; gr.sym = 1; gr.c_low = low;
   if (!gemm_ns_supported(gr)) return false;
 
   // C = A (B + aI) over r x r slots
@@ -348,6 +352,7 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
     q.alpha = 1.f;
     q.M = r; q.N = r; q.K = r; q.batch = j.batch; q.sym = 1;
     q.ident = 2; q.ident_terms = id_terms; q.ident_hi = id_hi; q.ident_lo = id_lo;
+    q.a_low = q.b_low = q.c_low = low;
     return q;
   };
   // slots of S_k and Q_k, and the two free ones (Q_{k+1}, S_{k+1} go there)
@@ -376,11 +381,11 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   const GfSlot& qk = slot[qi];
   a.tbl = j.xtbl; a.tbl_per = j.xper;
   if (wide) {   // X_K = Q_K x
-    a.a = qk.p; a.lda = r; a.sa = qk.st;
+    a.a = qk.p; a.lda = r; a.sa = qk.st; a.a_low = low;
     a.b = bp(j.x); a.ldb = n; a.sb = mn; a.b_kr = 1; a.b_tbl = tb;
   } else {      // X_K = x Q_K
     a.a = bp(j.x); a.lda = n; a.sa = mn; a.a_tbl = tb;
-    a.b = qk.p; a.ldb = r; a.sb = qk.st;
+    a.b = qk.p; a.ldb = r; a.sb = qk.st; a.b_low = low;
   }
   a.c = mp(j.out); a.ldc = n; a.sc = mn;
   a.scale = j.scale; a.alpha_pow = j.scale ? 1 : 0; a.alpha = 1.f;
@@ -510,7 +515,7 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
   auto fills = [&]() -> sm_status {
     for (const GfPlan& g : gf)
       SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
-                                 g.r, g.batch, g.a, s));
+                                 g.r, g.batch, g.a, g.gram.c_low != 0, s));
     return SM_OK;
   };
 

@@ -204,8 +204,19 @@ sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, c
 
 // q_b = s_b + a I for a batch of r x r bf16 matrices (float32 sum, bf16
 // rounding); needs r % 8 == 0, strides % 8 == 0 and 16-byte aligned bases.
+// lower: only the 256 x 256 tiles on and below the diagonal (matrices kept
+// as their lower triangle of tiles).
 sm_status launch_add_identity(const bf16_t* src, int64_t ss, bf16_t* dst, int64_t sq, int r,
-                              int batch, float a, hipStream_t s);
+                              int batch, float a, bool lower, hipStream_t s);
+
+// Entries of an n x n matrix kept as its 256 x 256 tiles on and below the
+// diagonal (row block i holds rows x min(256 (i + 1), n) entries).
+inline double lower_tile_entries(int n) {
+  double e = 0.0;
+  for (int r0 = 0; r0 < n; r0 += 256)
+    e += (double)(n - r0 < 256 ? n - r0 : 256) * (r0 + 256 < n ? r0 + 256 : n);
+  return e;
+}
 
 // has_cache flags of nprob problems: hc[b] = cache_state(b)[0], where problem
 // b's {has_cache, a_t} pair is at tbl_addr(cs, b, per, 8).
@@ -299,6 +310,12 @@ struct NsgGroup {
   int sym;
   int ident, ident_terms;
   uint32_t ident_hi, ident_lo;
+  // Lower-triangle storage of symmetric square matrices (Gram-form chain):
+  // a_low / b_low mark an operand (KC, K x K) whose 256 x 256 tiles above the
+  // diagonal were never written; the kernel reads a panel's entries past its
+  // diagonal block from the mirror tiles, transposed.  c_low (symmetric
+  // products) stores the tiles on and below the diagonal only.
+  int a_low, b_low, c_low;
   // Apply only: instead of C, write the 1-bit signs of its bf16 values
   // (bit = 1 <=> negative, bit j of word w <=> row-major entry 64 w + j) to
   // bits + problem * bits_stride words; needs N % 64 == 0.

@@ -231,6 +231,11 @@ NS_CASES = [
     ("bf16", 2, 640, 1920, 3, (1.5, -0.5, 0.0)),
     ("bf16", 2, 1920, 640, 6, (A2, 1.0 - A2, 0.0)),
     ("bf16", 2, 1920, 640, 3, (1.3, -0.3, 0.0)),
+    # lower-triangle storage of S_k, T_k, Q_k over several row blocks: each
+    # panel read partly as stored rows, partly from the mirror tiles
+    ("bf16", 1, 1280, 3840, 3, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 896, 2688, 3, (1.5, -0.5, 0.0)),
+    ("bf16", 2, 2688, 896, 2, (1.5, -0.5, 0.0)),
 ]
 
 
@@ -320,6 +325,30 @@ def test_profile_counts_algorithmic_bytes(gpu_lib):
     assert gram == b * (2 * m * n + 2 * m * m)          # X once (A == B), B_0 written
     assert apply_ == b * (2 * m * m + 2 * m * n + 2 * m * n)   # B_0, X read; X_1 written
     assert ema[0] == ema[1]                              # streaming kinds: bytes = work
+
+
+def test_profile_counts_lower_stored_gram_form(gpu_lib):
+    """Gram form with a one-term identity: S_k, T_k, Q_k are kept as their
+    256 x 256 tiles on and below the diagonal, and each launch is credited
+    with those stored entries (read once, written once)."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    b, m, n, K = 2, 640, 1920, 3
+    x = torch.randn(b, m, n, device="cuda", dtype=torch.bfloat16)
+    sm.profile_enable(True)
+    try:
+        sm.profile_reset()
+        sm.ns_polar(x, params=sm.NSParams(iters=K))
+        torch.cuda.synchronize()
+        gram = sm.profile_read_bytes("gemm_gram")
+        rr = sm.profile_read_bytes("gemm_rr")
+        apply_ = sm.profile_read_bytes("gemm_apply")
+    finally:
+        sm.profile_enable(False)
+    low = 256 * 256 + 256 * 512 + 128 * 640          # row blocks of 256, 256, 128
+    assert gram == b * (2 * m * n + 2 * low)
+    # T_0 = S_0 (S_0 + aI) and T_1 read one matrix; S_1, Q_2, S_2, Q_3 two
+    assert rr == b * 2 * (2 * 2 + 4 * 3) * low
+    assert apply_ == b * (2 * low + 2 * m * n + 2 * m * n)
 
 
 def test_ns_polar_without_normalisation(gpu_lib):
