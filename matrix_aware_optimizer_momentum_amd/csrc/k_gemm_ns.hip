@@ -41,8 +41,11 @@
 // stored element by element straight from registers.  A symmetric product
 // (A == B, or two commuting symmetric matrices) computes only tiles with
 // tm >= tn and stores each off-diagonal tile a second time, transposed, as
-// the mirror tile.  In a vote step the last apply stores the packed signs of
-// the values instead (wave ballots).
+// the mirror tile, unless C is kept as its lower triangle of tiles (the
+// Gram form's chain): its consumers then read a panel's entries past the
+// diagonal block from the stored tiles, transposed, in k segments of fixed
+// operand layouts.  In a vote step the last apply stores the packed signs
+// of the values instead (wave ballots).
 //
 // Identity fold.  The apply X' = a X + B X gets a X from extra MFMAs in the
 // k-stages that cover the output's own rows (wide: (a I) X) or columns (tall:
