@@ -12,6 +12,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <vector>
 
 namespace sm {
@@ -293,6 +295,8 @@ NsgGroup ns_subrange(const NsgGroup& g, int p0, int n) {
   h.a = g.a + (int64_t)p0 * g.sa;
   h.b = g.b + (int64_t)p0 * g.sb;
   h.c = g.c + (int64_t)p0 * g.sc;
+  if (g.scale) h.scale = g.scale + p0;
+  if (g.bits) h.bits = g.bits + (int64_t)p0 * g.bits_stride;
   h.batch = n;
   return h;
 }
@@ -454,21 +458,70 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
   bool ride = nrr > 0 && !dj.empty() && p.c == 0.f;
   for (int k = 0; ride && k < K - 1; ++k)
     for (size_t i = 0; i < dj.size(); ++i) ride = ride && ns_rides_sym(D[k][i].apply);
+  // Riding, a direct job's chain a_0, g_1, a_1, ..., g_{K-1} (2K - 2
+  // products, each needing the one before) takes one product per r x r
+  // launch, so it skips one of the 2K - 1 launches.  The job's problems may
+  // form two cohorts that skip different launches (chosen below to save
+  // rounds of the grid); a_0 reads the input through its table and scale, so
+  // both cohorts run it in launch 0 (skip >= 1) and it is never split.
+  struct Cohort {
+    int p0, n, skip;
+  };
+  std::vector<std::vector<Cohort>> coh(dj.size());
+  for (size_t i = 0; i < dj.size(); ++i)
+    coh[i] = {{0, D[0][i].apply.batch, std::max(nrr - 1, 1)}};
   // the direct products that travel with r x r launch l
   auto riders_of = [&](int l, std::vector<NsgGroup>& v) {
     for (size_t i = 0; i < dj.size(); ++i) {
-      if (ride) {
-        if (l <= 2 * K - 3) v.push_back(l % 2 == 0 ? D[l / 2][i].apply : D[(l + 1) / 2][i].gram);
-      } else if (l + 1 <= K - 1) {
-        v.push_back(D[l + 1][i].gram);
+      if (!ride) {
+        if (l + 1 <= K - 1) v.push_back(D[l + 1][i].gram);
+        continue;
       }
+      // chain element of each cohort in launch l; equal elements of
+      // adjacent cohorts go out as one group
+      int c0 = -1, p0 = 0, n = 0;
+      auto flush = [&]() {
+        if (c0 < 0) return;
+        const NsgGroup& g = c0 % 2 == 0 ? D[c0 / 2][i].apply : D[(c0 + 1) / 2][i].gram;
+        v.push_back(p0 == 0 && n == g.batch ? g : ns_subrange(g, p0, n));
+        c0 = -1;
+      };
+      for (const Cohort& h : coh[i]) {
+        const int c = l == h.skip ? -1 : (l < h.skip ? l : l - 1);
+        if (c < 0 || c > 2 * K - 3) { flush(); continue; }
+        if (c == c0 && p0 + n == h.p0) { n += h.n; continue; }
+        flush();
+        c0 = c; p0 = h.p0; n = h.n;
+      }
+      flush();
     }
   };
-  auto riders = [&](int l) {
-    std::vector<NsgGroup> v;
-    riders_of(l, v);
+  // tiles per problem of a direct job's applies and Gram products
+  std::vector<int64_t> tpp_apply(dj.size()), tpp_gram(dj.size());
+  for (size_t i = 0; i < dj.size(); ++i) {
+    tpp_apply[i] = ns_group_tiles(D[0][i].apply) / D[0][i].apply.batch;
+    tpp_gram[i] = ns_group_tiles(D[0][i].gram) / D[0][i].gram.batch;
+  }
+  // tiles and groups of the direct products in r x r launch l (as riders_of
+  // issues them, counted without building them)
+  auto riders = [&](int l, int* groups = nullptr) {
     int64_t t = 0;
-    for (const NsgGroup& g : v) t += ns_group_tiles(g);
+    int ng = 0;
+    for (size_t i = 0; i < dj.size(); ++i) {
+      if (!ride) {
+        if (l + 1 <= K - 1) { t += tpp_gram[i] * D[l + 1][i].gram.batch; ++ng; }
+        continue;
+      }
+      int c0 = -1;
+      for (const Cohort& h : coh[i]) {
+        const int c = l == h.skip ? -1 : (l < h.skip ? l : l - 1);
+        if (c < 0 || c > 2 * K - 3) { c0 = -1; continue; }
+        t += (c % 2 == 0 ? tpp_apply[i] : tpp_gram[i]) * h.n;
+        if (c != c0) ++ng;
+        c0 = c;
+      }
+    }
+    if (groups) *groups = ng;
     return t;
   };
   // Q_{k+1} (k = 1 .. K-2) goes to L1(k) whole, or its first problems fill
@@ -477,26 +530,29 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
   const int64_t cus = gemm_ns_cus();
   auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
   std::vector<std::vector<int>> qa(K, std::vector<int>(gf.size(), 0));
-  for (int k = 1; k < K; ++k) {
-    int64_t tt = 0, qt = 0, st = 0;
-    for (size_t i = 0; i < gf.size(); ++i) {
-      tt += (int64_t)gf[i].tiles * gf[i].T[k].batch;
-      qt += (int64_t)gf[i].tiles * gf[i].Q[k].batch;
-      st += (int64_t)gf[i].tiles * gf[i].S[k].batch;
-      qa[k][i] = gf[i].Q[k].batch;   // whole, unless split below
+  auto plan_q = [&]() {
+    for (int k = 1; k < K; ++k) {
+      int64_t tt = 0, qt = 0, st = 0;
+      for (size_t i = 0; i < gf.size(); ++i) {
+        tt += (int64_t)gf[i].tiles * gf[i].T[k].batch;
+        qt += (int64_t)gf[i].tiles * gf[i].Q[k].batch;
+        st += (int64_t)gf[i].tiles * gf[i].S[k].batch;
+        qa[k][i] = gf[i].Q[k].batch;   // whole, unless split below
+      }
+      if (k > K - 2) continue;
+      const int64_t b1 = tt + riders(2 * k), b2 = st + riders(2 * k + 1);
+      int64_t room = rounds(b1) * cus - b1, moved = 0;
+      std::vector<int> split(gf.size(), 0);
+      for (size_t i = 0; i < gf.size(); ++i) {
+        const int n = (int)std::min<int64_t>(gf[i].Q[k].batch, room / gf[i].tiles);
+        split[i] = n;
+        room -= (int64_t)n * gf[i].tiles;
+        moved += (int64_t)n * gf[i].tiles;
+      }
+      if (rounds(b1) + rounds(b2 + qt - moved) < rounds(b1 + qt) + rounds(b2)) qa[k] = split;
     }
-    if (k > K - 2) continue;
-    const int64_t b1 = tt + riders(2 * k), b2 = st + riders(2 * k + 1);
-    int64_t room = rounds(b1) * cus - b1, moved = 0;
-    std::vector<int> split(gf.size(), 0);
-    for (size_t i = 0; i < gf.size(); ++i) {
-      const int n = (int)std::min<int64_t>(gf[i].Q[k].batch, room / gf[i].tiles);
-      split[i] = n;
-      room -= (int64_t)n * gf[i].tiles;
-      moved += (int64_t)n * gf[i].tiles;
-    }
-    if (rounds(b1) + rounds(b2 + qt - moved) < rounds(b1 + qt) + rounds(b2)) qa[k] = split;
-  }
+  };
+  plan_q();
   auto take_rr = [&](int l, std::vector<NsgGroup>& v) {
     const int k = l / 2;
     for (size_t i = 0; i < gf.size(); ++i) {
@@ -512,6 +568,63 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
       }
     }
   };
+  // rounds of the grid over the r x r launches; a launch that would need
+  // more than kNsgMaxGroups groups rules the configuration out
+  auto rr_rounds = [&]() -> int64_t {
+    plan_q();
+    int64_t total = 0;
+    for (int l = 0; l < nrr; ++l) {
+      const int k = l / 2;
+      int ng = 0;
+      int64_t t = riders(l, &ng);
+      for (size_t i = 0; i < gf.size(); ++i) {
+        const GfPlan& g = gf[i];
+        const int qb = g.Q[k].batch, q1 = qa[k][i];
+        const int a = l % 2 == 0 ? g.T[k].batch : g.S[k].batch;
+        const int q = l % 2 == 0 ? q1 : qb - q1;
+        t += (int64_t)g.tiles * (a + q);
+        ng += (a > 0) + (q > 0);
+      }
+      if (ng > kNsgMaxGroups) return INT64_MAX;
+      total += rounds(t);
+    }
+    return total;
+  };
+  if (ride && nrr >= 3) {
+    // per direct job, the cohorts that need fewest rounds (greedy over the
+    // jobs); the choice depends only on the launch shapes, so it is cached
+    std::vector<int64_t> key = {K, cus};
+    for (const GfPlan& g : gf) key.insert(key.end(), {g.tiles, g.batch});
+    for (size_t i = 0; i < dj.size(); ++i)
+      key.insert(key.end(), {tpp_apply[i], tpp_gram[i], D[0][i].apply.batch});
+    static std::mutex mu;
+    static std::map<std::vector<int64_t>, std::vector<std::vector<Cohort>>> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      coh = it->second;
+    } else {
+      for (size_t i = 0; i < dj.size(); ++i) {
+        const int b = D[0][i].apply.batch;
+        std::vector<Cohort> best = coh[i];
+        int64_t best_r = rr_rounds();
+        auto consider = [&](std::vector<Cohort> c) {
+          coh[i] = std::move(c);
+          const int64_t r = rr_rounds();
+          if (r < best_r) { best_r = r; best = coh[i]; }
+        };
+        for (int s1 = 1; s1 < nrr; ++s1) consider({{0, b, s1}});
+        const int step = std::max(1, b / 64);
+        for (int n1 = step; n1 < b; n1 += step)
+          for (int s1 = 1; s1 < nrr; ++s1)
+            for (int s2 = 1; s2 < nrr; ++s2)
+              if (s1 != s2) consider({{0, n1, s1}, {n1, b - n1, s2}});
+        coh[i] = best;
+      }
+      if (cache.size() < 256) cache[key] = coh;
+    }
+    plan_q();
+  }
   auto fills = [&]() -> sm_status {
     for (const GfPlan& g : gf)
       SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,

@@ -460,7 +460,10 @@ def test_full_size_gpt2_small_step_sampled(gpu_lib):
         mom = (1e-4 * torch.randn(wl.M, m, n, generator=gen, device="cuda")).to(torch.bfloat16)
         g = (wl.grad_std * torch.randn(wl.M, m, n, generator=gen, device="cuda")).to(torch.bfloat16)
         mats.append(sm.MatrixBuffers(w=w, mom=mom, grad=g))
-    sample = [0, 2, 3, 46]                    # qkv, fc, fc_out (tall), a last-layer fc
+    # qkv, the square proj of the first and the last layer (the direct form,
+    # in different cohorts of riding problems), fc, fc_out (tall), a
+    # last-layer fc
+    sample = [0, 1, 45, 2, 3, 46]
     before = {j: (to_np(mats[j].w), to_np(mats[j].mom), to_np(mats[j].grad)) for j in sample}
     w_all_before = [mb.w.clone() for mb in mats]
     cfg = _cfg(wl)
