@@ -79,7 +79,7 @@ struct Grp {
   int combo;          // instantiation index within the kernel's role
   int a_kr, b_kr;
   int sym;
-  int ident;          // 0 none, 1 A side (wide apply), 2 B side (tall apply)
+  int ident;          // 0 none, 1 A side (wide apply), 2 B side (tall apply), 3 both
   uint32_t id_hi, id_lo;   // bf16 bits of the identity terms
   int alpha_pow;
   float alpha;
@@ -416,7 +416,9 @@ struct Ident {
 };
 
 // Identity fragments of the two k16 slices (a_hi, and a_lo for two terms),
-// built once when a tile reaches its identity group.
+// built once when a tile reaches its identity group.  With the identity on
+// both sides (one term), h is the A side's fragment and l the B side's,
+// each zero when the group does not carry that side.
 struct IdFrags {
   bf16x8 h[2], l[2];
 };
@@ -441,6 +443,19 @@ __device__ __forceinline__ void ident_mma(f32x16 (&acc)[4][4], const Frags& f,
 #pragma unroll
       for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], idf.l[s], acc[i][IB]);
     }
+  } else if constexpr (IDM == 3) {
+    // (A + aI)(B + aI) = AB + aB + aA + a^2 I, one term: the A side's
+    // group covers the wave's rows, the B side's its columns, and where
+    // both coincide the a^2 term lands on the diagonal of block (IB, IB).
+    // All nine MFMAs run, against zero fragments for a side the group does
+    // not carry: under a lane-mask branch the compiler may leave out the
+    // skip, and an MFMA issued with no active lanes still accumulates.
+    static_assert(IDT == 1, "both-sided identity takes one term");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) SM_MFMA(idf.h[s], f.b[j], acc[IB][j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) SM_MFMA(f.a[i], idf.l[s], acc[i][IB]);
+    SM_MFMA(idf.h[s], idf.l[s], acc[IB][IB]);
   }
 }
 
@@ -532,7 +547,21 @@ __device__ __forceinline__ void run_groups(f32x16 (&acc)[4][4], Frags& f0, Frags
     SM_NSG_STEP(1, IDM_)   \
     SM_NSG_STEP(2, IDM_)   \
     SM_NSG_STEP(3, IDM_)
-    if constexpr (IDM != 0) {
+    if constexpr (IDM == 3) {   // id_g: the A side's group | the B side's << 16
+      const bool ia = kg == (id_g & 0xffff), ib = kg == (id_g >> 16);
+      if (ia || ib) {
+        IdFrags idf;
+        const bf16x8 z{};
+        idf.h[0] = ia ? ident_frag(0, id.hi) : z;
+        idf.h[1] = ia ? ident_frag(1, id.hi) : z;
+        idf.l[0] = ib ? ident_frag(0, id.hi) : z;
+        idf.l[1] = ib ? ident_frag(1, id.hi) : z;
+        SM_NSG_GROUP(3)
+      } else {
+        IdFrags idf;   // not read: the group has no identity MFMAs
+        SM_NSG_GROUP(0)
+      }
+    } else if constexpr (IDM != 0) {
       if (kg == id_g) {
         IdFrags idf;
         idf.h[0] = ident_frag(0, id.hi);
@@ -573,8 +602,9 @@ __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], Frags& f0, Frags& 
 // an operand's panel passes its diagonal block (asw for A, bsw for B; see
 // low_switch).  LOW 3: both operands (symmetric tile, tn <= tm, so B turns
 // first); 1: A only, B KR; 2: B only, A KC.  The identity group of a panel
-// lies in its diagonal block, before the switch, so only the first segment
-// carries the identity MFMAs.
+// lies in its diagonal block, before that panel's switch: a B-side (or a
+// one-operand) identity falls in the first segment; with the identity on
+// both sides (IDM 3) the A side's group may fall in the second.
 template <int LOW, int IDM, int IDT>
 __device__ __forceinline__ void run_tile_low(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                              const bf16_t* smem, uint32_t la0, int& cb,
@@ -586,8 +616,8 @@ __device__ __forceinline__ void run_tile_low(f32x16 (&acc)[4][4], Frags& f0, Fra
   if constexpr (LOW == 3) {
     run_groups<0, 0, IDM, IDT>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, 0, bsw,
                                id_g, wm, wn, id, lenient);
-    run_groups<0, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, bsw, asw,
-                           id_g, wm, wn, id, false);
+    run_groups<0, 1, IDM == 3 ? 3 : 0, IDT>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid,
+                                            stride, bsw, asw, id_g, wm, wn, id, false);
     run_groups<1, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, asw, nkg,
                            id_g, wm, wn, id, false);
   } else if constexpr (LOW == 1) {
@@ -889,6 +919,7 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 //          2 (KC, KC, B-side id, 1 term)   3 (KC, KC, B-side id, 2 terms)
 //          4 (KC, KR, A-side id, 1 term)
 //          5 (both lower-stored, B-side id, 1 term)
+//          6 (both lower-stored, id on both sides, 1 term)
 //          (2 to 4 also take plain applies riding along: tall 2/3, wide 4)
 //   APPLY: 0 (KC, KR, A-side id, 1 term)   1 (KC, KC, B-side id, 1 term)
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
@@ -942,7 +973,9 @@ void k_gemm_ns(Args args) {
     // the k loop rather than kept live across it
     int wm = (fresh_tid() >> 6) >> 1, wn = (fresh_tid() >> 6) & 1;
     // identity group of this wave: the 128 k-indices equal to its rows / columns
-    const int id_g = g.ident == 1 ? 2 * tc.tm + wm : 2 * tc.tn + wn;
+    const int id_g = g.ident == 1   ? 2 * tc.tm + wm
+                     : g.ident == 2 ? 2 * tc.tn + wn
+                                    : (2 * tc.tm + wm) | ((2 * tc.tn + wn) << 16);
     Ident id;
     id.hi = g.id_hi;
     id.lo = g.id_lo;
@@ -964,8 +997,12 @@ void k_gemm_ns(Args args) {
         run_tile<0, 0, 2, 2>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       } else if (g.combo == 4) {
         run_tile<0, 1, 1, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
-      } else {
+      } else if (g.combo == 5) {
         run_tile_low<3, 2, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg,
+                              low_switch(tc.tm, nkg), low_switch(tc.tn, nkg), id_g, wm, wn, id,
+                              lenient);
+      } else {
+        run_tile_low<3, 3, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg,
                               low_switch(tc.tm, nkg), low_switch(tc.tn, nkg), id_g, wm, wn, id,
                               lenient);
       }
@@ -1086,6 +1123,10 @@ bool gemm_ns_supported(const NsgGroup& G) {
     return false;
   if (G.ident == 1 && G.K != G.M) return false;
   if (G.ident == 2 && G.K != G.N) return false;
+  // both sides: symmetric lower-stored products of square matrices, one term
+  if (G.ident == 3 &&
+      (G.K != G.M || G.K != G.N || !G.sym || !G.a_low || !G.b_low || G.ident_terms != 1))
+    return false;
   // lower-stored operands: square KC matrices; C kept lower only when symmetric
   if (G.a_low && (G.a_kr || G.a_tbl || G.M != G.K || G.M % 8)) return false;
   if (G.b_low && (G.b_kr || G.b_tbl || G.N != G.K || G.N % 8)) return false;
@@ -1185,6 +1226,7 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     if (!apply && g.sym) {
       if (low == 3) {
         if (G.ident == 2 && !two) combo = 5;
+        else if (G.ident == 3 && !two) combo = 6;
       } else if (low) {
       } else if (!G.ident && !g.a_kr && !g.b_kr) combo = 0;
       else if (!G.ident && g.a_kr && g.b_kr) combo = 1;

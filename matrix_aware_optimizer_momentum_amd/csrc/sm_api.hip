@@ -268,7 +268,9 @@ sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
 //   X_K = s Q_K x                (one apply over the long side)
 // Every r x r product is a symmetric one (lower-triangle tiles) whose aI
 // part comes from the identity fold, so S_k, T_k and Q_k are rounded to
-// bf16 once per product, like the direct form's B_k and X_k.  Storing P_k
+// bf16 once per product, like the direct form's B_k and X_k.  With a
+// one-term identity there is no fill: Q_2 = (S_0 + aI)(S_1 + aI) takes the
+// identity on both sides, straight from S_0.  Storing P_k
 // instead of S_k would round its O(1) diagonal and costs several times the
 // error.  Launches L1(k) = {T_k, Q_{k+1}} and L2(k) = {S_{k+1}}, 2K - 1 in
 // all; Q_{k+1} (k = 1 .. K-2) may be split by problems between L1(k) and
@@ -341,7 +343,10 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   gr.a = bp(j.x); gr.lda = n; gr.sa = mn; gr.a_kr = wide ? 0 : 1;
   gr.b = bp(j.x); gr.ldb = n; gr.sb = mn; gr.b_kr = wide ? 0 : 1;
   gr.tbl = j.xtbl; gr.tbl_per = j.xper; gr.a_tbl = tb; gr.b_tbl = tb;
-  gr.c = slot[0].p; gr.ldc = r; gr.sc = slot[0].st;
+  // lower-stored: S_0 goes to Q_1's slot and serves as Q_1 too (Q_2 takes
+  // the identity on both sides); else Q_1 = S_0 + aI is filled in
+  const GfSlot& s0 = low ? slot[1] : slot[0];
+  gr.c = s0.p; gr.ldc = r; gr.sc = s0.st;
   gr.scale = j.scale; gr.alpha_pow = j.scale ? 2 : 0; gr.alpha = p.b;
   gr.M = r; gr.N = r; gr.K = cols; gr.batch = j.batch; gr.sym = 1; gr.c_low = low;
   if (!gemm_ns_supported(gr)) return false;
@@ -359,9 +364,11 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
     q.a_low = q.b_low = q.c_low = low;
     return q;
   };
-  // slots of S_k and Q_k, and the two free ones (Q_{k+1}, S_{k+1} go there)
-  int si = 0, qi = 1, f1 = 2, f2 = 3;
-  g.fill_src = slot[si];
+  // slots of S_k and Q_k, and the two free ones (Q_{k+1}, S_{k+1} go there);
+  // lower-stored, S_0 and Q_1 share slot 1 until Q_2 is made, and slot 0
+  // stands by as S_2's
+  int si = low ? 1 : 0, qi = 1, f1 = 2, f2 = 3;
+  g.fill_src = low ? GfSlot{nullptr, 0} : slot[si];
   g.fill_dst = slot[qi];
   NsgGroup none;
   std::memset(&none, 0, sizeof(none));
@@ -371,10 +378,11 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   for (int k = 0; k < K; ++k) {
     if (k < K - 1) g.T[k] = prod(slot[si], slot[si], tslot);         // T_k
     if (k >= 1) g.Q[k] = prod(slot[qi], slot[si], slot[f1]);        // Q_{k+1}
+    if (k == 1 && low) g.Q[k].ident = 3;   // Q_2 = (S_0 + aI)(S_1 + aI)
     if (k < K - 1) g.S[k] = prod(tslot, slot[si], slot[f2]);         // S_{k+1}
     const int os = si, oq = qi;
     if (k >= 1) { qi = f1; f1 = oq; }
-    if (k < K - 1) { si = f2; f2 = os; }
+    if (k < K - 1) { si = f2; f2 = (k == 0 && low) ? 0 : os; }
   }
   for (int k = 0; k < K; ++k)
     for (const NsgGroup* q : {&g.T[k], &g.S[k], &g.Q[k]})
@@ -627,8 +635,9 @@ sm_status ns_grouped(const std::vector<NsJob>& jobs, const sm_ns_params& p, hipS
   }
   auto fills = [&]() -> sm_status {
     for (const GfPlan& g : gf)
-      SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
-                                 g.r, g.batch, g.a, g.gram.c_low != 0, s));
+      if (g.fill_src.p)
+        SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st,
+                                   g.r, g.batch, g.a, g.gram.c_low != 0, s));
     return SM_OK;
   };
 
