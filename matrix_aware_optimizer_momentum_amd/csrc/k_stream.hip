@@ -249,12 +249,18 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(const T* x, int64_t count, f
   if (threadIdx.x == 0) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
 }
 
-__global__ void k_scale_finalize(const float* partials, int nprob, float eps, float* scale) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nprob) return;
+// One wave per problem: lane l sums partials l, l + 64, ... in order (fp64),
+// then the lanes combine in a fixed butterfly, so the result is the same on
+// every run.
+__global__ __launch_bounds__(64) void k_scale_finalize(const float* partials, int parts,
+                                                       float eps, float* scale) {
+  const int b = blockIdx.x;
+  const float* p = partials + (int64_t)b * kNormParts;
   double s = 0.0;
-  for (int i = 0; i < kNormParts; ++i) s += (double)partials[(int64_t)b * kNormParts + i];
-  scale[b] = (float)(1.0 / (sqrt(s) + (double)eps));
+  for (int i = threadIdx.x; i < parts; i += 64) s += (double)p[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (threadIdx.x == 0) scale[b] = (float)(1.0 / (sqrt(s) + (double)eps));
 }
 
 template <typename T>
@@ -507,7 +513,7 @@ sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int 
                             float* partials, hipStream_t s) {
   if (nprob <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
-  dim3 grid(kNormParts, nprob);
+  dim3 grid(norm_parts(count), nprob);
   double bytes = (double)nprob * count *
                  (2.0 * dt_size(mdt) + dt_size(gdt) + (x ? dt_size(xdt) : 0.0));
   prof_begin(SM_K_EMA, bytes, s);
@@ -525,7 +531,7 @@ sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
   if (nprob <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
   const bool signs = bits || s8;
-  dim3 grid(signs ? stream_blocks(count, nprob) : kNormParts, nprob);
+  dim3 grid(signs ? stream_blocks(count, nprob) : norm_parts(count), nprob);
   double bytes = (double)nprob * count * (2.0 * dt_size(mdt) + dt_size(gdt)) +
                  (bits ? (double)nprob * words * 8.0
                        : (s8 ? (double)nprob * count : (double)nprob * count * dt_size(xdt)));
@@ -537,11 +543,16 @@ sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
   return check_launch();
 }
 
+int norm_parts(int64_t count) {
+  const int64_t n = (count + kChunk - 1) / kChunk;
+  return (int)(n < 1 ? 1 : (n > kNormParts ? kNormParts : n));
+}
+
 sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* partials,
                        hipStream_t s) {
   if (nprob <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
-  dim3 grid(kNormParts, nprob);
+  dim3 grid(norm_parts(count), nprob);
   prof_begin(SM_K_NORM, (double)nprob * count * dt_size(dt), s);
   SM_DISPATCH_DT(dt, T,
       hipLaunchKernelGGL((k_sumsq<T>), grid, dim3(kThreads), 0, s, (const T*)x, count,
@@ -550,12 +561,13 @@ sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* p
   return check_launch();
 }
 
-sm_status launch_scale_finalize(const float* partials, int nprob, float eps, float* scale,
-                                hipStream_t s) {
+sm_status launch_scale_finalize(const float* partials, int nprob, int64_t count, float eps,
+                                float* scale, hipStream_t s) {
   if (nprob <= 0) return SM_OK;
-  prof_begin(SM_K_MISC, (double)nprob * (kNormParts + 1) * 4.0, s);
-  hipLaunchKernelGGL(k_scale_finalize, dim3((nprob + 63) / 64), dim3(64), 0, s, partials,
-                     nprob, eps, scale);
+  const int parts = norm_parts(count);
+  prof_begin(SM_K_MISC, (double)nprob * (parts + 1) * 4.0, s);
+  hipLaunchKernelGGL(k_scale_finalize, dim3(nprob), dim3(64), 0, s, partials, parts, eps,
+                     scale);
   prof_end(s);
   return check_launch();
 }

@@ -1091,7 +1091,7 @@ sm_status sm_ns_polar(const void* x, void* u, int dt, int batch, int m, int n, i
   const int64_t count = (int64_t)m * n;
   if (normalize) {
     SM_TRY(launch_sumsq(x, dt, batch, count, partials, s));
-    SM_TRY(launch_scale_finalize(partials, batch, p->eps, scale, s));
+    SM_TRY(launch_scale_finalize(partials, batch, count, p->eps, scale, s));
   }
   return ns_core(x, u, w, normalize ? scale : nullptr, dt, batch, m, n, *p, s);
 }
@@ -1135,7 +1135,7 @@ sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_sta
   float* scale = cv.take<float>((size_t)batch * 4);
   if (normalize) {
     SM_TRY(launch_sumsq(x, dt, batch, (int64_t)m * n, partials, s));
-    SM_TRY(launch_scale_finalize(partials, batch, p->eps, scale, s));
+    SM_TRY(launch_scale_finalize(partials, batch, (int64_t)m * n, p->eps, scale, s));
   }
   const PtrTbl qt = tbl_one(q), cs = tbl_one(cache_state);
   return gram_core(x, d, qt, cs, batch, err, refreshed, nullptr, w,
@@ -1343,7 +1343,8 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
       SM_TRY(launch_ema_single(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, x0,
                                c->mdt, r.w.partials, s));
     }
-    if (muon_step) SM_TRY(launch_scale_finalize(r.w.partials, r.B, c->ns.eps, r.w.scale, s));
+    if (muon_step)
+      SM_TRY(launch_scale_finalize(r.w.partials, r.B, r.count, c->ns.eps, r.w.scale, s));
   }
   // a3-a5: the direction.  Direct NS runs all chunks the grouped kernel takes
   // together (one launch per product kind and iteration).
@@ -1421,7 +1422,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     SM_TRY(launch_vote(c->encoding, sg[ci], M, stride, (int64_t)M * stride, r.nc, r.count, vt,
                        c->mdt, 0.f, nullptr, false, s));
     SM_TRY(launch_sumsq(r.w.x0, c->mdt, r.nc, r.count, r.w.partials, s));
-    SM_TRY(launch_scale_finalize(r.w.partials, r.nc, c->ns.eps, r.w.scale, s));
+    SM_TRY(launch_scale_finalize(r.w.partials, r.nc, r.count, c->ns.eps, r.w.scale, s));
     NsJob j{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.nc, ch.m, ch.n};
     if (ns_grouped_ok(j, c->mdt, c->ns))
       vjobs.push_back(j);

@@ -126,8 +126,11 @@ sm_status check_launch();
 
 // ---------------------------------------------------------------- streaming kernels
 
-// Number of partial sums per problem used by every sum-of-squares producer.
-constexpr int kNormParts = 32;
+// Partial sums per problem of every sum-of-squares producer: one per block,
+// norm_parts(count) blocks (up to kNormParts, the stride of the partials
+// array), so that a launch has enough blocks to keep HBM busy.
+constexpr int kNormParts = 512;
+int norm_parts(int64_t count);
 
 // Single EMA  M <- beta*M + (1-beta)*G  over `nprob` problems (= matrices x
 // workers) of `count` elements.  Writes M, the NS input copy x (contiguous
@@ -151,9 +154,10 @@ sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
 sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* partials,
                        hipStream_t s);
 
-// scale[b] = 1 / (sqrt(sum_i partials[b][i]) + eps)
-sm_status launch_scale_finalize(const float* partials, int nprob, float eps, float* scale,
-                                hipStream_t s);
+// scale[b] = 1 / (sqrt(sum_i partials[b][i]) + eps) over the norm_parts(count)
+// partials of problems of `count` elements
+sm_status launch_scale_finalize(const float* partials, int nprob, int64_t count, float eps,
+                                float* scale, hipStream_t s);
 
 // Sign + 1-bit pack of nprob contiguous problems of `count` elements into
 // bits (problem b at bits + b*words).
