@@ -654,7 +654,9 @@ sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt
       need = std::max<int64_t>(need, (n8 + kThreads - 1) / kThreads);
       bytes += (double)t.m[q].count * (sign_bytes + 2.0 * dt_size(wdt));
     }
-    const int64_t want = (4096 + n - 1) / n;
+    // about 64 blocks per CU in all: the matrices' sizes differ, and short
+    // blocks even out the launch's tail
+    const int64_t want = (16384 + n - 1) / n;
     const dim3 grid((unsigned)(need < want ? need : want), n);
     prof_begin(SM_K_VOTE_UPDATE, bytes, s);
     if (enc == SM_ENC_BITS) {
