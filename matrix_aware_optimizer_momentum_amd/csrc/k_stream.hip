@@ -16,6 +16,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = kThreads * 8;  // elements per block iteration
+static_assert(kChunk == kNormChunk, "the norm partials count chunks of kChunk");
 
 template <typename T>
 __device__ __forceinline__ float round_to(float v) {
@@ -146,19 +147,15 @@ __device__ __forceinline__ void store_signs8(int8_t* s, int64_t e0, int64_t coun
 
 // ------------------------------------------------------------------ EMA
 
+// The EMA of one problem's chunks part, part + nparts, ...; returns this
+// thread's sum of squares of the stored x values.
 template <typename TM, typename TG, typename TX>
-__global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad, int per,
-                                                         int64_t count, float beta, TX* x,
-                                                         float* partials, bool vec) {
-  __shared__ float red[4];
-  const int b = blockIdx.y;
-  TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
-  const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
-  TX* xo = x ? x + (int64_t)b * count : nullptr;
+__device__ __forceinline__ float ema_run(TM* m, const TG* g, TX* xo, int64_t count, float beta,
+                                         bool vec, int64_t part, int64_t nparts) {
   const float omb = 1.0f - beta;
   float acc = 0.f;
   const int64_t nchunks = (count + kChunk - 1) / kChunk;
-  for (int64_t ci = blockIdx.x; ci < nchunks; ci += gridDim.x) {
+  for (int64_t ci = part; ci < nchunks; ci += nparts) {
     const int64_t e0 = ci * kChunk + (int64_t)threadIdx.x * 8;
     if (e0 >= count) continue;
     float mv[8], gv[8];
@@ -174,8 +171,39 @@ __global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad
     store8_tail<TM>(m, e0, count, vec, mv);
     if (xo) store8_tail<TX>(xo, e0, count, vec, gv);
   }
+  return acc;
+}
+
+template <typename TM, typename TG, typename TX>
+__global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad, int per,
+                                                         int64_t count, float beta, TX* x,
+                                                         float* partials, bool vec) {
+  __shared__ float red[4];
+  const int b = blockIdx.y;
+  TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
+  const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
+  TX* xo = x ? x + (int64_t)b * count : nullptr;
+  const float acc = ema_run<TM, TG, TX>(m, g, xo, count, beta, vec, blockIdx.x, gridDim.x);
   float s = block_sum(acc, red);
   if (threadIdx.x == 0 && partials) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
+}
+
+// Problem b = matrix b / per, worker b % per; blocks past the problem's
+// norm_parts have nothing to do.
+template <typename TM, typename TG>
+__global__ __launch_bounds__(kThreads) void k_ema_tbl(EmaTbl t, int per, float beta) {
+  __shared__ float red[4];
+  const int b = blockIdx.y, q = b / per, w = b - q * per;
+  const EmaMat& e = t.m[q];
+  const int parts = norm_parts(e.count);
+  if ((int)blockIdx.x >= parts) return;
+  TM* m = static_cast<TM*>(e.mom) + (int64_t)w * e.count;
+  const TG* g = static_cast<const TG*>(e.grad) + (int64_t)w * e.count;
+  TM* xo = e.x ? static_cast<TM*>(e.x) + (int64_t)w * e.count : nullptr;
+  const float acc = ema_run<TM, TG, TM>(m, g, xo, e.count, beta, (e.count % 8) == 0,
+                                        blockIdx.x, parts);
+  float s = block_sum(acc, red);
+  if (threadIdx.x == 0) e.partials[(int64_t)w * kNormParts + blockIdx.x] = s;
 }
 
 // LionMuon: ghat = b1*M + (1-b1)*G (direction), M <- b2*M + (1-b2)*G.
@@ -252,15 +280,24 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(const T* x, int64_t count, f
 // One wave per problem: lane l sums partials l, l + 64, ... in order (fp64),
 // then the lanes combine in a fixed butterfly, so the result is the same on
 // every run.
-__global__ __launch_bounds__(64) void k_scale_finalize(const float* partials, int parts,
-                                                       float eps, float* scale) {
-  const int b = blockIdx.x;
-  const float* p = partials + (int64_t)b * kNormParts;
+__device__ __forceinline__ void finalize_one(const float* p, int parts, float eps, float* out) {
   double s = 0.0;
   for (int i = threadIdx.x; i < parts; i += 64) s += (double)p[i];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (threadIdx.x == 0) scale[b] = (float)(1.0 / (sqrt(s) + (double)eps));
+  if (threadIdx.x == 0) *out = (float)(1.0 / (sqrt(s) + (double)eps));
+}
+
+__global__ __launch_bounds__(64) void k_scale_finalize(const float* partials, int parts,
+                                                       float eps, float* scale) {
+  const int b = blockIdx.x;
+  finalize_one(partials + (int64_t)b * kNormParts, parts, eps, scale + b);
+}
+
+__global__ __launch_bounds__(64) void k_scale_finalize_tbl(EmaTbl t, int per, float eps) {
+  const int b = blockIdx.x, q = b / per, w = b - q * per;
+  const EmaMat& e = t.m[q];
+  finalize_one(e.partials + (int64_t)w * kNormParts, norm_parts(e.count), eps, e.scale + w);
 }
 
 template <typename T>
@@ -524,6 +561,38 @@ sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int 
   return check_launch();
 }
 
+sm_status launch_ema_tbl(const EmaMat* mats, int nmat, int per, int mdt, int gdt, float beta,
+                         bool finalize, float eps, hipStream_t s) {
+  for (int q0 = 0; q0 < nmat; q0 += kEmaMax) {
+    const int n = std::min(kEmaMax, nmat - q0);
+    EmaTbl t;
+    std::memset(&t, 0, sizeof(t));
+    int parts = 1;
+    double bytes = 0.0;
+    for (int q = 0; q < n; ++q) {
+      t.m[q] = mats[q0 + q];
+      parts = std::max(parts, norm_parts(t.m[q].count));
+      bytes += (double)per * t.m[q].count *
+               (2.0 * dt_size(mdt) + dt_size(gdt) + (t.m[q].x ? dt_size(mdt) : 0.0));
+    }
+    prof_begin(SM_K_EMA, bytes, s);
+    SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG,
+        hipLaunchKernelGGL((k_ema_tbl<TM, TG>), dim3(parts, n * per), dim3(kThreads), 0, s, t,
+                           per, beta)));
+    prof_end(s);
+    SM_TRY(check_launch());
+    if (finalize) {
+      double fb = 0.0;
+      for (int q = 0; q < n; ++q) fb += (double)per * (norm_parts(t.m[q].count) + 1) * 4.0;
+      prof_begin(SM_K_MISC, fb, s);
+      hipLaunchKernelGGL(k_scale_finalize_tbl, dim3(n * per), dim3(64), 0, s, t, per, eps);
+      prof_end(s);
+      SM_TRY(check_launch());
+    }
+  }
+  return SM_OK;
+}
+
 sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob, int64_t count,
                       int mdt, int gdt, float beta1, float beta2, void* x, int xdt,
                       float* partials, uint64_t* bits, int64_t words, int8_t* s8,
@@ -541,11 +610,6 @@ sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
                          count, beta1, beta2, (TX*)x, partials, bits, words, s8, vec))));
   prof_end(s);
   return check_launch();
-}
-
-int norm_parts(int64_t count) {
-  const int64_t n = (count + kChunk - 1) / kChunk;
-  return (int)(n < 1 ? 1 : (n > kNormParts ? kNormParts : n));
 }
 
 sm_status launch_sumsq(const void* x, int dt, int nprob, int64_t count, float* partials,

@@ -1328,23 +1328,40 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
       }
     }
   }
-  // a1 (+ a2 partials): momentum, and the NS input or the Lion signs
-  for (size_t ci = 0; ci < chunks.size(); ++ci) {
-    ChunkRun& r = runs[ci];
-    if (c->algo == SM_LION_MUON) {
+  // a1 (+ a2 partials): momentum, and the NS input or the Lion signs.  The
+  // single EMA of every chunk goes out as one launch over a table of
+  // matrices (and one norm finalize).
+  if (c->algo == SM_LION_MUON) {
+    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+      ChunkRun& r = runs[ci];
       if (muon_step)
         SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
                            r.w.x0, c->mdt, r.w.partials, nullptr, 0, nullptr, s));
       else
         SM_TRY(launch_lion(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, c->beta2,
                            nullptr, c->mdt, nullptr, r.w.bits, r.words, r.w.s8, s));
-    } else {
-      void* x0 = (r.grouped && r.job.xtbl) ? nullptr : r.w.x0;   // no copy when NS reads M
-      SM_TRY(launch_ema_single(r.mom, r.grad, M, r.B, r.count, c->mdt, c->gdt, c->beta1, x0,
-                               c->mdt, r.w.partials, s));
+      if (muon_step)
+        SM_TRY(launch_scale_finalize(r.w.partials, r.B, r.count, c->ns.eps, r.w.scale, s));
     }
-    if (muon_step)
-      SM_TRY(launch_scale_finalize(r.w.partials, r.B, r.count, c->ns.eps, r.w.scale, s));
+  } else {
+    std::vector<EmaMat> ema;
+    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+      ChunkRun& r = runs[ci];
+      void* x0 = (r.grouped && r.job.xtbl) ? nullptr : r.w.x0;   // no copy when NS reads M
+      for (int j = 0; j < r.nc; ++j) {
+        EmaMat e;
+        e.mom = const_cast<char*>(r.mom.p[j]);
+        e.grad = r.grad.p[j];
+        e.x = x0 ? static_cast<char*>(x0) + (int64_t)j * M * r.count * dt_size(c->mdt)
+                 : nullptr;
+        e.partials = r.w.partials + (int64_t)j * M * kNormParts;
+        e.scale = r.w.scale + (int64_t)j * M;
+        e.count = r.count;
+        ema.push_back(e);
+      }
+    }
+    SM_TRY(launch_ema_tbl(ema.data(), (int)ema.size(), M, c->mdt, c->gdt, c->beta1, muon_step,
+                          c->ns.eps, s));
   }
   // a3-a5: the direction.  Direct NS runs all chunks the grouped kernel takes
   // together (one launch per product kind and iteration).

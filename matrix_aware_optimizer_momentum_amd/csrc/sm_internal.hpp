@@ -130,7 +130,11 @@ sm_status check_launch();
 // norm_parts(count) blocks (up to kNormParts, the stride of the partials
 // array), so that a launch has enough blocks to keep HBM busy.
 constexpr int kNormParts = 512;
-int norm_parts(int64_t count);
+constexpr int kNormChunk = 2048;   // entries per block iteration
+__host__ __device__ inline int norm_parts(int64_t count) {
+  const int64_t n = (count + kNormChunk - 1) / kNormChunk;
+  return (int)(n < 1 ? 1 : (n > kNormParts ? kNormParts : n));
+}
 
 // Single EMA  M <- beta*M + (1-beta)*G  over `nprob` problems (= matrices x
 // workers) of `count` elements.  Writes M, the NS input copy x (contiguous
@@ -139,6 +143,26 @@ int norm_parts(int64_t count);
 sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
                             int64_t count, int mdt, int gdt, float beta, void* x, int xdt,
                             float* partials, hipStream_t s);
+
+// The same EMA over a table of matrices of any shapes (the momentum and the
+// gradients of matrix q: `per` workers, count entries apart), kEmaMax per
+// launch; with `finalize`, also scale = 1 / (||x|| + eps) per problem, as
+// launch_scale_finalize.  Partials and scales per matrix: [per][kNormParts]
+// and [per].
+struct EmaMat {
+  void* mom;
+  const void* grad;
+  void* x;            // NS input copy [per][count] in the momentum type, or null
+  float* partials;
+  float* scale;
+  int64_t count;
+};
+constexpr int kEmaMax = 64;
+struct EmaTbl {
+  EmaMat m[kEmaMax];
+};
+sm_status launch_ema_tbl(const EmaMat* mats, int nmat, int per, int mdt, int gdt, float beta,
+                         bool finalize, float eps, hipStream_t s);
 
 // LionMuon fused kernel.  ghat = beta1*M + (1-beta1)*G, M <- beta2*M +
 // (1-beta2)*G.  On a Lion step the signs of ghat (decided in float32) are
