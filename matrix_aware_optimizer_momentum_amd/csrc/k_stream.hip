@@ -174,20 +174,6 @@ __device__ __forceinline__ float ema_run(TM* m, const TG* g, TX* xo, int64_t cou
   return acc;
 }
 
-template <typename TM, typename TG, typename TX>
-__global__ __launch_bounds__(kThreads) void k_ema_single(PtrTbl mom, PtrTbl grad, int per,
-                                                         int64_t count, float beta, TX* x,
-                                                         float* partials, bool vec) {
-  __shared__ float red[4];
-  const int b = blockIdx.y;
-  TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
-  const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
-  TX* xo = x ? x + (int64_t)b * count : nullptr;
-  const float acc = ema_run<TM, TG, TX>(m, g, xo, count, beta, vec, blockIdx.x, gridDim.x);
-  float s = block_sum(acc, red);
-  if (threadIdx.x == 0 && partials) partials[(int64_t)b * kNormParts + blockIdx.x] = s;
-}
-
 // Problem b = matrix b / per, worker b % per; blocks past the problem's
 // norm_parts have nothing to do.
 template <typename TM, typename TG>
@@ -544,22 +530,6 @@ inline int stream_blocks(int64_t count, int nprob) {
 
 // ------------------------------------------------------------------ launchers
 
-
-sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
-                            int64_t count, int mdt, int gdt, float beta, void* x, int xdt,
-                            float* partials, hipStream_t s) {
-  if (nprob <= 0 || count <= 0) return SM_OK;
-  const bool vec = (count % 8) == 0;
-  dim3 grid(norm_parts(count), nprob);
-  double bytes = (double)nprob * count *
-                 (2.0 * dt_size(mdt) + dt_size(gdt) + (x ? dt_size(xdt) : 0.0));
-  prof_begin(SM_K_EMA, bytes, s);
-  SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG, SM_DISPATCH_DT(xdt, TX,
-      hipLaunchKernelGGL((k_ema_single<TM, TG, TX>), grid, dim3(kThreads), 0, s, mom, grad,
-                         per, count, beta, (TX*)x, partials, vec))));
-  prof_end(s);
-  return check_launch();
-}
 
 sm_status launch_ema_tbl(const EmaMat* mats, int nmat, int per, int mdt, int gdt, float beta,
                          bool finalize, float eps, hipStream_t s) {

@@ -136,19 +136,13 @@ __host__ __device__ inline int norm_parts(int64_t count) {
   return (int)(n < 1 ? 1 : (n > kNormParts ? kNormParts : n));
 }
 
-// Single EMA  M <- beta*M + (1-beta)*G  over `nprob` problems (= matrices x
-// workers) of `count` elements.  Writes M, the NS input copy x (contiguous
-// [nprob][count] in xdt, may be null) and the per-problem sum-of-squares
-// partials of the stored x values ([nprob][kNormParts]).
-sm_status launch_ema_single(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
-                            int64_t count, int mdt, int gdt, float beta, void* x, int xdt,
-                            float* partials, hipStream_t s);
-
-// The same EMA over a table of matrices of any shapes (the momentum and the
-// gradients of matrix q: `per` workers, count entries apart), kEmaMax per
-// launch; with `finalize`, also scale = 1 / (||x|| + eps) per problem, as
-// launch_scale_finalize.  Partials and scales per matrix: [per][kNormParts]
-// and [per].
+// Single EMA  M <- beta*M + (1-beta)*G over a table of matrices of any
+// shapes (the momentum and the gradients of matrix q: `per` workers, count
+// entries apart), kEmaMax per launch.  Writes M, the NS input copy x
+// ([per][count] in the momentum type, may be null) and the sum-of-squares
+// partials of the stored x values ([per][kNormParts], norm_parts(count) of
+// them); with `finalize`, also scale = 1 / (||x|| + eps) per problem, as
+// launch_scale_finalize.
 struct EmaMat {
   void* mom;
   const void* grad;
