@@ -142,6 +142,15 @@ def test_sign_muon_step_matches_oracle(gpu_lib, idx, shapes):
     _check_step(wl, _cfg(wl), st, 3, wl.mdt)
 
 
+def test_sign_muon_step_more_matrices_than_one_ema_launch_takes(gpu_lib):
+    """70 matrices in three shape chunks: the EMA's matrix table (64 per
+    launch) splits across a chunk, and every matrix still matches the oracle."""
+    wl = W.WORKLOADS[2]
+    shapes = [(64, 128)] * 40 + [(128, 64)] * 20 + [(96, 96)] * 10
+    st = Seeded(wl, shapes)
+    _check_step(wl, _cfg(wl), st, 2, wl.mdt)
+
+
 @pytest.mark.parametrize("shapes,a,applies", [
     # square (direct, wide): its applies ride in the r x r launches
     ([(256, 256), (256, 1024), (1024, 256), (256, 256)], 1.5, 1),
