@@ -51,7 +51,8 @@
 // k-stages that cover the output's own rows (wide: (a I) X) or columns (tall:
 // X (a I)), against an a I fragment; a is split into up to two bf16 terms
 // a_hi + a_lo, whose products with bf16 data are exact in fp32.  The Gram
-// form's products A (B + aI) use the same fold.
+// form's products A (B + aI) use the same fold, and (A + aI)(B + aI) folds
+// the identity on both sides (plus a^2 where the two groups meet).
 #include "sm_internal.hpp"
 
 namespace sm {
