@@ -286,7 +286,7 @@ struct GfPlan {
   // products per iteration k: T[k] = T_k, S[k] = S_{k+1} (k < K-1),
   // Q[k] = Q_{k+1} (k >= 1); unused entries have batch 0
   std::vector<NsgGroup> T, S, Q;
-  GfSlot fill_src, fill_dst;
+  GfSlot fill_src, fill_dst;   // Q_1 = S_0 + aI (fill_src.p null: no fill)
   int r, batch, tiles;   // tiles: 256 x 256 tiles of one r x r product
   float a;
 };
