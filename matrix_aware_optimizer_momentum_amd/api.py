@@ -68,6 +68,20 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _expect(t: torch.Tensor, name: str, shape=None, dtype=None, min_numel=None, dev=True):
+    """Shape / dtype / size check of a caller tensor before its pointer
+    crosses the C ABI (which sees only raw pointers and cannot check sizes);
+    then (dev) that it is a contiguous GPU tensor."""
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, has {t.numel()}")
+    if dev:
+        _dev(t, name)
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -102,7 +116,7 @@ def ns_polar(x: torch.Tensor, out: Optional[torch.Tensor] = None, normalize: boo
     batch, m, n = _bmn(x)
     p = params or NSParams()
     out = torch.empty_like(x) if out is None else out
-    _dev(out, "out")
+    _expect(out, "out", x.shape, x.dtype)
     ws = _ws(ns_polar_ws(x.dtype, batch, m, n), x.device, ws)
     cp = p.c_struct()
     code = B.lib().sm_ns_polar(x.data_ptr(), out.data_ptr(), _dt(x), batch, m, n,
@@ -140,6 +154,9 @@ def gram_ns_cached(x: torch.Tensor, q: torch.Tensor, cache_state: torch.Tensor, 
     err = torch.empty(batch, dtype=torch.float32, device=x.device) if err is None else err
     refreshed = (torch.empty(batch, dtype=torch.int32, device=x.device)
                  if refreshed is None else refreshed)
+    _expect(d, "d", x.shape, x.dtype)
+    _expect(err, "err", dtype=torch.float32, min_numel=batch)
+    _expect(refreshed, "refreshed", dtype=torch.int32, min_numel=batch)
     ws = _ws(gram_ns_cached_ws(x.dtype, batch, m, n), x.device, ws)
     cp = p.c_struct()
     code = B.lib().sm_gram_ns_cached(x.data_ptr(), d.data_ptr(), q.data_ptr(),
@@ -159,6 +176,7 @@ def sign_pack(x: torch.Tensor, bits: Optional[torch.Tensor] = None) -> torch.Ten
     count = x.numel()
     words = (count + 63) // 64
     bits = torch.empty(max(words, 1), dtype=torch.int64, device=x.device) if bits is None else bits
+    _expect(bits, "bits", dtype=torch.int64, min_numel=words)
     code = B.lib().sm_sign_pack(x.data_ptr(), _dt(x), count, bits.data_ptr(), _stream())
     B.check(code, "sm_sign_pack")
     return bits
@@ -171,6 +189,8 @@ def vote_update(bits: torch.Tensor, w: torch.Tensor, lr: float,
     if bits.dtype != torch.int64 or bits.dim() != 2:
         raise ValueError("bits must be int64 [M, words_stride]")
     M, stride = bits.shape
+    if stride * 64 < w.numel():
+        raise ValueError("bits rows hold fewer than w.numel() signs")
     vp = 0
     if vote_out is not None:
         _dev(vote_out, "vote_out")
@@ -201,6 +221,8 @@ def vote_update_int8(signs: torch.Tensor, w: torch.Tensor, lr: float,
     if signs.dtype != torch.int8 or signs.dim() != 2:
         raise ValueError("signs must be int8 [M, stride]")
     M, stride = signs.shape
+    if stride < w.numel():
+        raise ValueError("signs rows hold fewer than w.numel() signs")
     vp = 0
     if vote_out is not None:
         _dev(vote_out, "vote_out")
@@ -223,6 +245,8 @@ def vote(signs: torch.Tensor, count: int, out: torch.Tensor) -> torch.Tensor:
     M, stride = signs.shape
     if out.numel() < count:
         raise ValueError("out is smaller than count")
+    if stride * (64 if enc == B.ENC_BITS else 1) < count:
+        raise ValueError("signs rows hold fewer than count signs")
     code = B.lib().sm_vote(signs.data_ptr(), enc, M, stride, count, out.data_ptr(), _dt(out),
                            _stream())
     B.check(code, "sm_vote")
@@ -283,6 +307,35 @@ class MatrixBuffers:
                         self.cache_state.data_ptr() if self.cache_state is not None else None)
 
 
+def _check_mats(cfg: StepConfig, mats: Sequence[MatrixBuffers], diag: Optional[torch.Tensor]):
+    """Every tensor of every matrix has the shape and dtype the configuration
+    implies (the library reads and writes them through raw pointers), and
+    is a contiguous GPU tensor."""
+    if len(mats) == 0:
+        raise ValueError("a step needs at least one matrix")
+    tensors = []
+    for j, mb in enumerate(mats):
+        if mb.w.dim() != 2:
+            raise ValueError(f"matrix {j}: w must be [m, n]")
+        m, n = mb.w.shape
+        r = min(m, n)
+        want = [(mb.w, "w", None, cfg.wdt), (mb.mom, "mom", (cfg.M, m, n), cfg.mdt),
+                (mb.grad, "grad", (cfg.M, m, n), cfg.gdt)]
+        if cfg.algo == B.CACHE_MUON:
+            if mb.q_cache is None or mb.cache_state is None:
+                raise ValueError(f"matrix {j}: CacheMuon needs q_cache and cache_state")
+            want += [(mb.q_cache, "q_cache", (cfg.M, r, r), torch.float32),
+                     (mb.cache_state, "cache_state", (cfg.M, 2), torch.int32)]
+        for t, name, shape, dtype in want:
+            _expect(t, f"matrix {j} {name}", shape, dtype, dev=False)
+            tensors.append((t, f"matrix {j} {name}"))
+    if diag is not None:
+        _expect(diag, "diag", dtype=torch.float32, min_numel=len(mats) * cfg.M * 2, dev=False)
+        tensors.append((diag, "diag"))
+    for t, name in tensors:
+        _dev(t, name)
+
+
 def _mats_array(mats: Sequence[MatrixBuffers]):
     arr = (B.Matrix * len(mats))()
     for i, mb in enumerate(mats):
@@ -303,9 +356,7 @@ class StepCall:
 
     def __init__(self, cfg: StepConfig, mats: Sequence[MatrixBuffers],
                  ws: Optional[torch.Tensor] = None, diag: Optional[torch.Tensor] = None):
-        for mb in mats:
-            for name in ("w", "mom", "grad"):
-                _dev(getattr(mb, name), name)
+        _check_mats(cfg, mats, diag)
         self.cfg = cfg
         self.mats = list(mats)
         self._c = cfg.c_struct()

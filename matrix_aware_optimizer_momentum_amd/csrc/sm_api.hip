@@ -1127,6 +1127,16 @@ sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_sta
   size_t need = 0;
   SM_TRY(sm_gram_ns_cached_ws(dt, batch, m, n, &need));
   if (ws_bytes < need) return SM_ERR_WORKSPACE;
+  // the workspace must not alias any caller buffer the call reads or writes
+  const int r = m < n ? m : n;
+  const size_t qbytes = (size_t)batch * r * r * sizeof(float);
+  const size_t sbytes = (size_t)batch * 2 * sizeof(int32_t);
+  if (overlap(ws, ws_bytes, x, bytes) || overlap(ws, ws_bytes, d, bytes) ||
+      overlap(ws, ws_bytes, q, qbytes) || overlap(ws, ws_bytes, cache_state, sbytes) ||
+      (err && overlap(ws, ws_bytes, err, (size_t)batch * 4)) ||
+      (refreshed && overlap(ws, ws_bytes, refreshed, (size_t)batch * 4)))
+    return SM_ERR_ARG;
+  if (overlap(q, qbytes, x, bytes) || overlap(q, qbytes, d, bytes)) return SM_ERR_ARG;
 
   Carver cv(ws);
   GramWs w;

@@ -133,20 +133,17 @@ def lion_momentum(m_prev, g, beta2: float) -> np.ndarray:
 
 
 def lion_sign_negative(m_prev, g, beta1: float) -> np.ndarray:
-    """Sign decision of the Lion direction, taken in float32 as the kernel takes it.
+    """'Entry is negative' for the Lion direction sign(G_hat), G_hat exact.
 
-    The sign is an integer decided by floating point, so it is decided in the
-    kernel's precision: with b = fp32(beta1) and c = fp32(1 - b), the kernel
-    evaluates b*m + rnd32(c*g) with one final rounding, whose sign is the
-    sign of the exact value computed here (b*m is exact in float64).  Entries
-    that are exactly 0 count as +1.
+    [LionMuon-pt] Methodology, core algorithm item 2: a Lion step moves by
+    the sign of the interpolation G_hat = beta1*M_{t-1} + (1-beta1)*G_t.
+    The sign is that of the exact value: with M_{t-1} and G_t the stored
+    (float32 or bfloat16) values and beta1 a float32 hyper-parameter, both
+    products and 1 - beta1 are exact in float64, and the one rounding of
+    their float64 sum cannot change its sign (it is 0 only when the exact
+    sum is 0, which counts as +1).
     """
-    b = np.float32(beta1)
-    c = np.float32(np.float32(1.0) - b)
-    m32 = np.asarray(m_prev, dtype=np.float64).astype(np.float32)
-    g32 = np.asarray(g, dtype=np.float64).astype(np.float32)
-    cg = (c * g32).astype(np.float32).astype(np.float64)
-    return (np.float64(b) * m32.astype(np.float64) + cg) < 0
+    return sign_negative(lion_interp(m_prev, g, beta1))
 
 
 # --------------------------------------------------------------------------
@@ -598,7 +595,7 @@ def step_matrix(st: MatrixState, grads: Sequence[np.ndarray], cfg: StepConfig, t
             y = lion_interp(m_prev, g, cfg.beta1)
             st.mom[k] = round_storage(lion_momentum(st.mom[k], g, cfg.beta2), cfg.mdtype)
             if not muon_step:
-                # Lion step: sign of the interpolation, decided in float32.
+                # Lion step: the exact sign of the interpolation.
                 out["d"][k] = y
                 neg = lion_sign_negative(m_prev, g, cfg.beta1).reshape(-1)
                 out["bits"][k] = pack_bits(neg)

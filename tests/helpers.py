@@ -72,3 +72,31 @@ def assert_ema_close(gpu, want, m_prev, g, beta, dt, what=""):
 def f32(v: float) -> float:
     """A hyper-parameter as the float32 the C ABI receives."""
     return float(np.float32(v))
+
+
+def lion_band(m_prev, g, beta1: float) -> np.ndarray:
+    """Entries whose Lion sign a float32 evaluation may decide either way.
+
+    G_hat = b*m + (1-b)*g evaluated in float32 (b = fp32(beta1)) carries at
+    most a few roundings of the size of its terms, so its sign can differ
+    from the exact sign only where |G_hat| <= 2^-22 (|b m| + |(1-b) g|).
+    """
+    b = np.float64(np.float32(beta1))
+    m = np.asarray(m_prev, np.float64)
+    g = np.asarray(g, np.float64)
+    exact = b * m + (1.0 - b) * g
+    return np.abs(exact) <= 2.0 ** -22 * (np.abs(b * m) + np.abs((1.0 - b) * g))
+
+
+def check_vote_within(v_gpu, v_or, ambiguous, what, max_frac):
+    """The vote may differ from the oracle's only where some worker's sign is
+    ambiguous (decided by rounding); the fraction of such entries is bounded.
+    v_gpu may hold 9 where the update does not tell the vote apart."""
+    v_gpu = np.asarray(v_gpu)
+    amb = np.any(np.stack([np.asarray(a, bool).reshape(v_gpu.shape) for a in ambiguous]), axis=0)
+    known = v_gpu != 9
+    mism = known & (v_gpu != np.asarray(v_or).reshape(v_gpu.shape))
+    bad = mism & ~amb
+    assert not np.any(bad), f"{what}: {int(bad.sum())} vote mismatches outside the rounding band"
+    assert mism.mean() <= max_frac, f"{what}: mismatch fraction {mism.mean():.2e}"
+    return int(mism.sum())

@@ -206,3 +206,75 @@ def test_python_front_end_needs_gpu_tensors():
     import matrix_aware_optimizer_momentum_amd as sm
     with pytest.raises(ValueError):
         sm.sign_pack(torch.zeros(10))
+
+
+def test_gram_ns_cached_rejects_workspace_aliasing():
+    """The workspace may not overlap x, d, Q, the cache state, err or the
+    refresh flags (checked on the host; nothing is launched)."""
+    lib = B.lib()
+    p = B.NSParams(5, 1.5, -0.5, 0.0, 1e-7)
+    need = ctypes.c_size_t(0)
+    assert lib.sm_gram_ns_cached_ws(B.F32, 2, 64, 96, ctypes.byref(need)) == 0
+    x, d, q, cs = 0x100000, 0x200000, 0x300000, 0x400000
+    err, rf = 0x500000, 0x600000
+    big = 1 << 24
+    for ws in (x, d, q, cs, err, rf, q - 256 * 16):
+        args = [ctypes.c_void_p(v) for v in (x, d, q, cs, err, rf)]
+        assert lib.sm_gram_ns_cached(*args, B.F32, 2, 64, 96, 1, ctypes.byref(p), 1.0, 0, 1,
+                                     ctypes.c_void_p(ws), max(need.value, big), None) == 1, hex(ws)
+    # Q aliasing the input
+    assert lib.sm_gram_ns_cached(ctypes.c_void_p(x), ctypes.c_void_p(d), ctypes.c_void_p(x),
+                                 ctypes.c_void_p(cs), None, None, B.F32, 2, 64, 96, 1,
+                                 ctypes.byref(p), 1.0, 0, 1, ctypes.c_void_p(0x10000000),
+                                 need.value, None) == 1
+    assert lib.sm_last_hip_error() == 0
+
+
+def _cpu_mats(M=3, m=8, n=12, wdt=None, mdt=None, gdt=None, mom_shape=None):
+    import torch
+    from matrix_aware_optimizer_momentum_amd.api import MatrixBuffers
+    f = torch.float32
+    return [MatrixBuffers(w=torch.zeros(m, n, dtype=wdt or f),
+                          mom=torch.zeros(*(mom_shape or (M, m, n)), dtype=mdt or f),
+                          grad=torch.zeros(M, m, n, dtype=gdt or f))]
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(mdt="bf16"), "mom must be torch.float32"),
+    (dict(gdt="bf16"), "grad must be torch.float32"),
+    (dict(wdt="bf16"), "w must be torch.float32"),
+    (dict(mom_shape=(2, 8, 12)), "mom must have shape"),
+    (dict(mom_shape=(3, 12, 8)), "mom must have shape"),
+])
+def test_step_front_end_checks_shapes_and_dtypes(kw, msg):
+    """A bf16 momentum with a float32 configuration (and the like) is refused
+    before any pointer reaches the library."""
+    import torch
+    from matrix_aware_optimizer_momentum_amd.api import StepCall, StepConfig
+    kw = {k: (torch.bfloat16 if v == "bf16" else v) for k, v in kw.items()}
+    with pytest.raises(ValueError, match=msg):
+        StepCall(StepConfig(M=3), _cpu_mats(**kw))
+
+
+def test_step_front_end_checks_cache_buffers_and_diag():
+    import torch
+    from matrix_aware_optimizer_momentum_amd.api import StepCall, StepConfig
+    mats = _cpu_mats(M=1)
+    cfg = StepConfig(algo=B.CACHE_MUON, update=B.UPDATE_POLAR, M=1)
+    with pytest.raises(ValueError, match="needs q_cache"):
+        StepCall(cfg, mats)
+    mats[0].q_cache = torch.zeros(1, 8, 8, dtype=torch.float64)
+    mats[0].cache_state = torch.zeros(1, 2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="q_cache must be torch.float32"):
+        StepCall(cfg, mats)
+    mats[0].q_cache = torch.zeros(1, 12, 12)
+    with pytest.raises(ValueError, match="q_cache must have shape"):
+        StepCall(cfg, mats)
+    mats[0].q_cache = torch.zeros(1, 8, 8)
+    mats[0].cache_state = torch.zeros(1, 2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="cache_state must be torch.int32"):
+        StepCall(cfg, mats)
+    with pytest.raises(ValueError, match="diag must hold at least 6"):
+        StepCall(StepConfig(M=3), _cpu_mats(), diag=torch.zeros(5))
+    with pytest.raises(ValueError, match="at least one matrix"):
+        StepCall(StepConfig(M=3), [])

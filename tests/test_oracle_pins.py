@@ -499,24 +499,50 @@ def test_cache_muon_trajectory_polar_mode():
 
 # ---------------------------------------------------------------- Lion sign decision
 
-def test_lion_sign_decision_in_float32():
+def _exact_lion_negative(m, g, beta1):
+    """Brute force with exact rationals: beta1 as the float32 the ABI
+    receives, m and g as the stored values."""
+    from fractions import Fraction
+    b = Fraction(float(np.float32(beta1)))
+    return np.array([b * Fraction(float(mi)) + (1 - b) * Fraction(float(gi)) < 0
+                     for mi, gi in zip(m, g)])
+
+
+def test_lion_sign_is_the_exact_sign_of_the_interpolation():
     rng = np.random.default_rng(22)
-    m = rng.standard_normal(20000)
-    g = rng.standard_normal(20000)
-    b = float(np.float32(0.9))
-    exact = b * m.astype(np.float32).astype(np.float64) + \
-        (1 - b) * g.astype(np.float32).astype(np.float64)
-    clear = np.abs(exact) > 1e-5
-    got = O.lion_sign_negative(m, g, 0.9)
-    np.testing.assert_array_equal(got[clear], exact[clear] < 0)
-    # exact cancellation g = -9 m: with fp32(0.9) = 0.89999998 and
-    # fp32(1 - 0.89999998) = 0.10000002 the float32 value is
-    # 0.89999998 - rnd32(0.90000021) = -2.4e-7 < 0, while beta = 0.9 exactly
-    # would give 0 (sign +1).
-    assert O.lion_sign_negative(np.array([1.0]), np.array([-9.0]), 0.9)[0]
-    assert not O.lion_sign_negative(np.array([-1.0]), np.array([9.0]), 0.9)[0]
-    # beta = 0.5 is exact in float32: m = 1, g = -1 cancels to +0 -> +1
+    b = np.float32(0.9)
+    b9 = float(b)     # the hyper-parameter as the float32 the C ABI receives
+    c = np.float32(1) - b
+    m = rng.standard_normal(3000).astype(np.float32)
+    g = rng.standard_normal(3000).astype(np.float32)
+    # near-cancellations: g ~ -(b/c) m rounded to float32, nudged by 0..3 ulp
+    # either way, where the float32 rounding of c*g decides a float32 sign
+    k = 1500
+    g_c = (-(np.float64(b) / np.float64(c)) * m[:k].astype(np.float64)).astype(np.float32)
+    nudge = rng.integers(-3, 4, size=k)
+    g[:k] = np.array([np.nextafter(x, np.float32(np.inf) if s > 0 else np.float32(-np.inf))
+                      if s else x for x, s in zip(g_c, nudge)], dtype=np.float32)
+    for _ in range(2):
+        g[:k] = np.where(np.abs(nudge) > 1,
+                         np.nextafter(g[:k], np.where(nudge > 0, np.inf, -np.inf).astype(np.float32)),
+                         g[:k])
+        nudge = np.where(np.abs(nudge) > 1, nudge - np.sign(nudge), nudge)
+    got = O.lion_sign_negative(m, g, b9)
+    np.testing.assert_array_equal(got, _exact_lion_negative(m, g, 0.9))
+    # bf16-valued state: same rule
+    mb = torch.from_numpy(m).to(torch.bfloat16).float().numpy()
+    gb = torch.from_numpy(g).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(O.lion_sign_negative(mb, gb, b9),
+                                  _exact_lion_negative(mb, gb, 0.9))
+    # exact cancellation g = -9 m: fp32(0.9) = 0.89999998 and 1 - fp32(0.9) =
+    # 0.10000002, so G_hat = 0.89999998 - 0.90000021 < 0 for m = 1
+    assert O.lion_sign_negative(np.array([1.0]), np.array([-9.0]), b9)[0]
+    assert not O.lion_sign_negative(np.array([-1.0]), np.array([9.0]), b9)[0]
+    # beta1 = 0.5 is exact: m = 1, g = -1 cancels to 0 -> +1
     assert not O.lion_sign_negative(np.array([1.0]), np.array([-1.0]), 0.5)[0]
+    # beta1 = 0 is signSGD on the gradient, beta1 = 1 the sign of the buffer
+    np.testing.assert_array_equal(O.lion_sign_negative(m, g, 0.0), g < 0)
+    np.testing.assert_array_equal(O.lion_sign_negative(m, g, 1.0), m < 0)
 
 
 def test_update_polar_matches_torch_float32_and_bf16():
