@@ -1,20 +1,25 @@
 """Benchmark of the Muon-family optimizer step on one MI355X.
 
-Default workload: the GPT-2-small layer set (12 layers x {768x2304, 768x768,
-768x3072, 3072x768}, 84,934,656 parameters), Sign-Muon with M = 5 simulated
-workers, bf16 momentum / Newton-Schulz operands with float32 accumulation,
-5 cubic NS iterations, 1-bit packed majority vote.  A step is one sm_step
-call: momentum EMA + norm, NS, sign + pack, vote + update for all 48
-matrices.  Inputs are synthetic and resident in HBM before timing starts.
+Default workload (the largest configuration): LionMuon on 8 x 4096x4096 +
+8 x 4096x11008 bf16 matrices (494,927,872 parameters), M = 16 simulated
+workers with Student-t(3) gradients, dual EMA (beta1 0.9, beta2 0.99), a
+Muon step (5 cubic Newton-Schulz iterations on G_hat) every P = 4 steps and
+Lion sign steps otherwise, 1-bit packed majority vote.  A step is one
+sm_step call over all 16 matrices; the timed region starts on a P-cycle
+boundary and holds whole cycles by default, so `value` is the P-averaged
+steps/s.  Inputs are synthetic and resident in HBM before timing starts.
 
-Prints one JSON line: steps/s (value), the roofline of the dominant kernel
-measured with HIP events on the step's stream over the timed region, and the
-CPU oracle timed on a bounded sample on this host.  After the main timed
-region, `variants` times the same step with the int8 sign encoding and with
-the optional polar step on the vote (--variant-steps each, default 10; the
-main `value` is always the 1-bit vote step).
+Prints one JSON line: steps/s (value), per-step-type times and rooflines
+(Muon step: NS GEMMs against the bf16 MFMA peak; Lion step: the fused Lion
+kernel against HBM), the roofline of the dominant kernel measured with HIP
+events on the step's stream over the timed region, the CPU oracle timed on a
+bounded sample on this host, and sub-objects for two more configurations:
+`gpt2_small` (Sign-Muon, M = 5; with the int8 encoding and the polar step on
+the vote as variants) and `gpt2_large_cache_muon` (CacheMuon at gamma 2, 15,
+a mixed-rate gamma and always-fresh, with refresh rates and executed
+orthogonalisation FLOPs).
 
-  python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu] [--no-sub]
   python bench.py --copy-calibration   # plain device copy of known size, for
                                        # scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
   python bench.py --fidelity [--gamma G] # CacheMuon fidelity diagnostic (config 4)
@@ -30,6 +35,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -40,17 +46,25 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 METRIC = "optimizer steps/s per layer set; NS TFLOP/s (MFMA %); vote+update GB/s (HBM %)"
+DEFAULT_CONFIG = 5
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 for LionMuon = 5 P-cycles, 30 otherwise)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: one P-cycle for LionMuon, else 3)")
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
     ap.add_argument("--gamma", type=float, default=None, help="CacheMuon threshold override")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="budget of the CPU oracle sample")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the GPT-2-small and GPT-2-large sub-objects")
+    ap.add_argument("--sub-steps", type=int, default=20,
+                    help="timed steps of each sub-object run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter scaling)")
     ap.add_argument("--fidelity", action="store_true",
@@ -64,7 +78,7 @@ def parse():
                     help="diagnose only the first N matrices (0 = all)")
     ap.add_argument("--variant-steps", type=int, default=10,
                     help="timed steps of each step variant (int8 encoding, polar step on the "
-                         "vote); 0 skips them")
+                         "vote) of the Sign-Muon runs; 0 skips them")
     return ap.parse_args()
 
 
@@ -91,10 +105,12 @@ def read_kinds(sm, steps):
 
 
 def kind_roofline(kinds, kind, mdt):
-    """Roofline of one kernel kind.  A GEMM kind sits under the MFMA roof when
-    its arithmetic intensity (algorithmic flops / algorithmic HBM bytes) is at
-    least the ridge point peak_flops / peak_bandwidth, else under the HBM roof;
-    `achieved` is then algorithmic bytes per launch / average launch time."""
+    """Roofline of one kernel kind.  The NS / Gram GEMMs are dense
+    contractions and sit under the MFMA roof of their operand type:
+    `achieved` = algorithmic flops per launch / average launch time.  Their
+    arithmetic intensity (algorithmic flops / algorithmic HBM bytes) and the
+    HBM view (algorithmic bytes per launch / launch time against 8 TB/s) are
+    reported beside it.  Streaming kinds sit under the HBM roof."""
     dk = kinds[kind]
     out = {"kernel": kind, "avg_launch_ms": dk["avg_launch_ms"],
            "work_per_launch": dk["work_per_launch"]}
@@ -103,14 +119,13 @@ def kind_roofline(kinds, kind, mdt):
         peak_f = PEAK_TFLOPS[mdt]
         ai = dk["flops"] / dk["hbm_bytes"] if dk.get("hbm_bytes") else float("inf")
         ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
-        out.update(arith_intensity=ai, ridge=ridge, bytes_per_launch=dk.get("bytes_per_launch"))
-        if ai >= ridge:
-            achieved = dk["work_per_launch"] / secs / 1e12
-            out.update(bound="mfma", achieved=achieved, peak=peak_f, unit="TFLOP/s")
-        else:
-            achieved = dk["bytes_per_launch"] / secs / 1e9
-            out.update(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                       tflops=dk["work_per_launch"] / secs / 1e12)
+        achieved = dk["work_per_launch"] / secs / 1e12
+        out.update(bound="mfma", achieved=achieved, peak=peak_f, unit="TFLOP/s",
+                   arith_intensity=ai, ridge=ridge, bytes_per_launch=dk.get("bytes_per_launch"))
+        if dk.get("bytes_per_launch"):
+            gbs = dk["bytes_per_launch"] / secs / 1e9
+            out["hbm_view"] = {"achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": gbs / PEAK_HBM_GBS}
     else:
         achieved = dk["work_per_launch"] / secs / 1e9
         out.update(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s")
@@ -227,6 +242,7 @@ def recorded_traffic(workload, kind):
         return None
 
 
+
 def copy_calibration():
     """A plain device-to-device copy of known size, timed; its rocprofv3 FETCH_SIZE
     and WRITE_SIZE give the counters' scale (bytes moved / counter reading)."""
@@ -248,6 +264,7 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
                       "launches": reps + 2, "ms_per_copy": ms,
                       "copy_gbs": 2 * nbytes / (ms * 1e-3) / 1e9}))
+
 
 
 def _tdt(dt):
@@ -292,60 +309,6 @@ def step_config(wl, gamma=None):
                          ns=sm.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c, wl.ns_eps),
                          gamma=wl.gamma if gamma is None else gamma, cache_mode=wl.cache_mode)
 
-
-def stream_bytes(wl, kind):
-    """Algorithmic bytes per step of one streaming kernel kind (whole layer set)."""
-    es = {"bf16": 2, "f32": 4}
-    n = wl.params
-    if kind == "ema":        # read G and M, write M and the NS input copy
-        return n * wl.M * (es[wl.gdt] + 2 * es[wl.mdt] + es[wl.mdt])
-    if kind == "sign_pack":  # read D, write 1 bit
-        return n * wl.M * (es[wl.mdt] + 1 / 8)
-    if kind == "vote_update":
-        return n * (wl.M / 8 + 2 * es[wl.wdt])
-    return 0.0
-
-
-def cpu_baseline(wl, seconds):
-    """The oracle's step on a bounded sample of the layer set, on this host's cores."""
-    import numpy as np
-    from matrix_aware_optimizer_momentum_amd import workloads as W
-    from oracle import sm_oracle as O
-    try:
-        import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
-                      default=os.cpu_count())
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    ocfg = O.StepConfig(algo=wl.algo, update=wl.update, workers=wl.M, wdtype=wl.wdt,
-                        mdtype=wl.mdt, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
-                        period=wl.period, ns=O.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c,
-                                                        wl.ns_eps),
-                        gamma=wl.gamma, cache_mode=wl.cache_mode)
-    done_params = 0
-    elapsed = 0.0
-    nmat = 0
-    rng = np.random.default_rng(wl.seed)
-    for (m, n) in wl.shapes:
-        w = W.as_storage((0.02 * rng.standard_normal((m, n))).astype(np.float32), wl.wdt)
-        g = [W.as_storage((wl.grad_std * rng.standard_normal((m, n))).astype(np.float32), wl.gdt)
-             for _ in range(wl.M)]
-        st = O.MatrixState(w=w.astype(np.float64), mom=[np.zeros((m, n)) for _ in range(wl.M)])
-        t0 = time.perf_counter()
-        O.step_matrix(st, g, ocfg, 1)
-        elapsed += time.perf_counter() - t0
-        done_params += m * n
-        nmat += 1
-        if elapsed >= seconds:
-            break
-    scale = wl.params / done_params
-    sec_per_step = elapsed * scale
-    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"{nmat} of {len(wl.shapes)} matrices ({done_params} of {wl.params} "
-                       f"parameters) x {wl.M} workers, one step, {elapsed:.1f} s; "
-                       f"{'extrapolated x%.2f to the whole layer set' % scale if scale > 1 else 'whole layer set'}"),
-            "seconds_per_step": sec_per_step}
 
 
 def _pearson(xs, ys):
@@ -460,6 +423,273 @@ def fidelity(args, sm, torch, W):
     print(json.dumps(out))
 
 
+def host_info():
+    """CPU model, BLAS library and the BLAS threads NumPy uses on this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas, threads = None, os.cpu_count()
+    try:
+        import threadpoolctl
+        libs = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            threads = max(int(i.get("num_threads", 1)) for i in libs)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas, threads
+
+
+def _oracle_inputs(wl, m, n, rng):
+    import numpy as np
+    from matrix_aware_optimizer_momentum_amd import workloads as W
+    w = W.as_storage((0.02 * rng.standard_normal((m, n))).astype(np.float32), wl.wdt)
+    if wl.grad_kind == "student_t":
+        g = rng.standard_t(3, size=(m, n))
+    else:
+        g = rng.standard_normal((m, n))
+    g = W.as_storage((wl.grad_std * g).astype(np.float32), wl.gdt)
+    return w, g
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle timed on this host on a bounded sample of the workload.
+
+    One worker on one matrix of each distinct shape, per step type (LionMuon:
+    a Muon step and a Lion step; CacheMuon: a fresh step, then a reuse step
+    with the workload's gamma; Sign-Muon: one step); each time is scaled by
+    the shape's matrix count times the worker count, and the step types are
+    combined as the step schedule mixes them (LionMuon: (Muon + (P-1) Lion)
+    / P).  Shapes not reached within the budget are extrapolated from the
+    measured seconds per parameter."""
+    import numpy as np
+    from oracle import sm_oracle as O
+    model, blas, threads = host_info()
+    counts = {}
+    for sh in wl.shapes:
+        counts[sh] = counts.get(sh, 0) + 1
+    order = sorted(counts, key=lambda sh: sh[0] * sh[1])
+    ocfg = O.StepConfig(algo=wl.algo, update=wl.update, workers=1, wdtype=wl.wdt,
+                        mdtype=wl.mdt, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
+                        period=wl.period, ns=O.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c,
+                                                        wl.ns_eps),
+                        gamma=wl.gamma, cache_mode=wl.cache_mode)
+    if wl.algo == O.LION_MUON:
+        types = ([("muon", wl.period)] if wl.period > 0 else []) + [("lion", 1)]
+    elif wl.algo == O.CACHE_MUON:
+        types = [("fresh", 1), ("reuse", 2)]
+    else:
+        types = [("step", 1)]
+    rng = np.random.default_rng(wl.seed)
+    spent = 0.0
+    per_type = {}
+    covered = {typ: {} for typ, _ in types}
+    for sh in order:
+        m, n = sh
+        w, g = _oracle_inputs(wl, m, n, rng)
+        st = O.MatrixState(w=w.astype(np.float64), mom=[np.zeros((m, n))])
+        for typ, t in types:
+            if spent >= budget_s:
+                break
+            if typ == "reuse":        # continues from the fresh step's cache
+                pass
+            elif typ == "fresh":
+                st = O.MatrixState(w=w.astype(np.float64), mom=[np.zeros((m, n))])
+            t0 = time.perf_counter()
+            O.step_matrix(st, [g], ocfg, t)
+            dt = time.perf_counter() - t0
+            spent += dt
+            covered[typ][sh] = dt
+    for typ, _ in types:
+        done = covered[typ]
+        if not done:
+            continue
+        secs = sum(counts[sh] * wl.M * done[sh] for sh in done)
+        done_params = sum(counts[sh] * sh[0] * sh[1] for sh in done)
+        per_param = secs / done_params
+        missing = sum(counts[sh] * sh[0] * sh[1] for sh in counts if sh not in done)
+        per_type[typ] = {"seconds_per_step": secs + per_param * missing,
+                         "measured_shapes": [f"{a}x{b}" for a, b in done],
+                         "seconds_measured": sum(done.values())}
+    if wl.algo == O.LION_MUON and "muon" in per_type and "lion" in per_type:
+        P = wl.period
+        sec = (per_type["muon"]["seconds_per_step"] +
+               (P - 1) * per_type["lion"]["seconds_per_step"]) / P
+        how = f"P-averaged over P = {P} (one Muon step, {P - 1} Lion steps)"
+    elif wl.algo == O.CACHE_MUON and "reuse" in per_type:
+        sec = per_type["reuse"]["seconds_per_step"]
+        how = "reuse step (gamma %g), fresh step reported beside it" % wl.gamma
+    else:
+        sec = next(iter(per_type.values()))["seconds_per_step"]
+        how = "one step"
+    total = sum(len(v) for v in covered.values())
+    return {"value": 1.0 / sec, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one worker on one matrix of each of {len(counts)} distinct shapes "
+                       f"({total} oracle steps, {spent:.1f} s on the host), scaled by matrix "
+                       f"count x {wl.M} workers; {how}; extrapolated"),
+            "extrapolated": True, "seconds_per_step": sec, "cpu_model": model, "blas": blas,
+            "per_step_type": per_type}
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def headline_roofline(kinds, mdt, wl_name, ms_per_step):
+    dom = max(kinds, key=lambda k: kinds[k]["ms_per_step"])
+    rl = kind_roofline(kinds, dom, mdt)
+    roofline = {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline["traffic"] = recorded_traffic(wl_name, dom)
+    roofline.update({k: v for k, v in rl.items() if k not in roofline})
+    others = {k: kind_roofline(kinds, k, mdt) for k in kinds
+              if k != dom and kinds[k]["ms_per_step"] > 0.05 * ms_per_step}
+    return roofline, others
+
+
+def ns_summary(kinds, mdt, wl, ms_per_step, muon_fraction=1.0):
+    out = {}
+    ms, fl = gemm_totals(kinds)
+    if ms > 0:
+        out["ns_tflops"] = fl / (ms * 1e-3) / 1e12
+        out["ns_mfma_frac"] = out["ns_tflops"] / PEAK_TFLOPS[mdt]
+        # the direct iteration's flop count over the whole step time: the
+        # rate the pages' form of the iteration would need to match this step
+        out["ns_direct_form_equivalent_tflops"] = (wl.ns_flops_per_step() * muon_fraction /
+                                                   (ms_per_step * 1e-3) / 1e12)
+    if "vote_update" in kinds:
+        vu = kinds["vote_update"]
+        out["vote_update_gbs"] = vu["bytes"] / (vu["ms_per_step"] * 1e-3) / 1e9
+        out["vote_update_hbm_frac"] = out["vote_update_gbs"] / PEAK_HBM_GBS
+    return out
+
+
+def sign_muon_sub(sm, torch, W, args, index=2):
+    """A Sign-Muon configuration timed like the headline (wall clock over the
+    timed steps), with its dominant-kernel roofline and the step variants."""
+    wl = W.WORKLOADS[index]
+    mats = build_state(wl)
+    cfg = step_config(wl)
+    call = sm.StepCall(cfg, mats)
+    t, wall, kinds = timed_steps(sm, torch, call, 1, 3, args.sub_steps)
+    ms = 1000.0 * wall / args.sub_steps
+    roofline, others = headline_roofline(kinds, wl.mdt, wl.name, ms)
+    out = {"workload": wl.name, "value": args.sub_steps / wall, "unit": "steps/s",
+           "ms_per_step": ms, "steps": args.sub_steps, "roofline": roofline,
+           **ns_summary(kinds, wl.mdt, wl, ms), "other_rooflines": others, "kernels": kinds}
+    variants, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms, kinds)
+    if variants:
+        out["variants"] = variants
+    del mats, call
+    torch.cuda.empty_cache()
+    return out
+
+
+def _cache_flops(shapes, K):
+    """Algorithmic orthogonalisation flops per problem: fresh Gram-NS solve
+    2r^2c + 6Kr^3 + 2r^2c; cached candidate + residual probe 4r^2c."""
+    fresh, probe = [], []
+    for m, n in shapes:
+        r, c = min(m, n), max(m, n)
+        fresh.append(4.0 * r * r * c + 6.0 * K * r ** 3)
+        probe.append(4.0 * r * r * c)
+    return fresh, probe
+
+
+def cache_muon_run(sm, torch, wl, gamma, mode, steps, warmup, label):
+    """CacheMuon on an AR(1) gradient stream advanced before every step
+    (outside the timed interval): per-step HIP events around sm_step, the
+    refresh decisions and residuals read back after each step."""
+    mats = build_state(wl)
+    cfg = step_config(wl, gamma)
+    cfg.cache_mode = mode
+    M = wl.M
+    diag = torch.zeros(len(mats), M, 2, device="cuda")
+    call = sm.StepCall(cfg, mats, diag=diag)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 99)
+    rho = wl.ar1_rho
+    fresh_f, probe_f = _cache_flops(wl.shapes, wl.ns_iters)
+    always_fresh = M * sum(fresh_f)
+    rec = {"ms": [], "refreshed": [], "executed_flops": [], "errs": []}
+    for t in range(1, warmup + steps + 1):
+        if t > 1:
+            for mb in mats:
+                xi = torch.randn(mb.grad.shape, generator=gen, device="cuda")
+                g = rho * mb.grad.float() + math.sqrt(1 - rho * rho) * wl.grad_std * xi
+                mb.grad.copy_(g.to(mb.grad.dtype))
+                del xi, g
+        timed = t > warmup
+        if timed and t == warmup + 1:
+            torch.cuda.synchronize()
+            sm.profile_enable(True)
+            sm.profile_reset()
+        e0, e1 = _events(torch)
+        e0.record()
+        call(t)
+        e1.record()
+        torch.cuda.synchronize()
+        d = diag.cpu()
+        refreshed = d[:, :, 1]
+        probed = (d[:, :, 0] >= 0)
+        if timed:
+            rec["ms"].append(e0.elapsed_time(e1))
+            rec["refreshed"].append(float(refreshed.mean()))
+            ex = 0.0
+            for j in range(len(mats)):
+                ex += float(probed[j].sum()) * probe_f[j] + float(refreshed[j].sum()) * fresh_f[j]
+            rec["executed_flops"].append(ex)
+        rec["errs"] += [float(e) for e in d[:, :, 0].flatten() if e >= 0]
+    kinds = read_kinds(sm, steps)
+    sm.profile_enable(False)
+    ms = sum(rec["ms"]) / steps
+    ex = sum(rec["executed_flops"]) / steps
+    gms, gfl = gemm_totals(kinds)
+    gms += kinds.get("probe", {}).get("ms_per_step", 0.0)
+    gfl += kinds.get("probe", {}).get("flops", 0.0)
+    out = {"label": label, "gamma": gamma, "mode": ["trigger", "force_fresh", "force_reuse"][mode],
+           "value": 1000.0 / ms, "unit": "steps/s (sum of per-step HIP event intervals)",
+           "ms_per_step": ms, "steps": steps, "warmup": warmup,
+           "refresh_rate": sum(rec["refreshed"]) / steps,
+           "orth_flops_per_step": ex,
+           "always_fresh_orth_flops_per_step": always_fresh,
+           "orth_flop_reduction_vs_always_fresh": 1.0 - ex / always_fresh,
+           "gemm_executed_tflops": gfl / (gms * 1e-3) / 1e12 if gms > 0 else None,
+           "gemm_mfma_frac": (gfl / (gms * 1e-3) / 1e12 / PEAK_TFLOPS[wl.mdt]) if gms > 0 else None,
+           "kernels": {k: {"ms_per_step": v["ms_per_step"], "launches_per_step":
+                           v["launches_per_step"]} for k, v in kinds.items()}}
+    errs = rec["errs"]
+    del mats, call, diag
+    torch.cuda.empty_cache()
+    return out, errs
+
+
+def cache_muon_sub(sm, torch, W, args):
+    """CacheMuon (GPT-2 large, M = 1) at the pages' gamma = 2 and 15, at a
+    mixed-rate gamma (the median residual of a calibration run, so that both
+    branches run in the timed steps), and always-fresh (GramMuon)."""
+    wl = W.WORKLOADS[4]
+    steps, warmup = args.sub_steps, 2
+    runs = {}
+    for g in (2.0, 15.0):
+        runs[f"gamma_{g:g}"], _ = cache_muon_run(sm, torch, wl, g, 0, steps, warmup, f"gamma {g:g}")
+    # calibration: forced reuse, residuals of every cached candidate
+    _, errs = cache_muon_run(sm, torch, wl, 0.0, 2, 3, 1, "calibration")
+    errs.sort()
+    g_mixed = errs[len(errs) // 2] if errs else 1.0
+    runs["gamma_mixed"], _ = cache_muon_run(sm, torch, wl, g_mixed, 0, steps, warmup,
+                                            "mixed-rate gamma (median residual)")
+    runs["always_fresh"], _ = cache_muon_run(sm, torch, wl, 0.0, 1, steps, warmup,
+                                             "always fresh (GramMuon)")
+    return {"workload": wl.name, "grad": f"AR(1) rho={wl.ar1_rho} sigma={wl.grad_std}",
+            "mixed_gamma": g_mixed, "runs": runs}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -478,79 +708,101 @@ def main():
         fidelity(args, sm, torch, W)
         return
     wl = W.WORKLOADS[args.config]
+    P = wl.period if wl.algo == sm.LION_MUON else 0
+    warmup = args.warmup if args.warmup is not None else (P if P else 3)
+    steps = args.steps if args.steps is not None else (5 * P if P else 30)
+    is_muon = (lambda t: P > 0 and t % P == 0) if wl.algo == sm.LION_MUON else (lambda t: True)
+
     mats = build_state(wl)
     cfg = step_config(wl, args.gamma)
     call = sm.StepCall(cfg, mats)
     torch.cuda.synchronize()
+    print(f"bench: {wl.name}, warmup {warmup}, timed {steps}", file=sys.stderr, flush=True)
 
     t = 1
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         call(t)
         t += 1
     torch.cuda.synchronize()
 
     sm.profile_enable(True)
     sm.profile_reset()
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [_events(torch) for _ in range(steps)]
+    types = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(steps):
+        evs[i][0].record()
         call(t)
+        evs[i][1].record()
+        types.append("muon" if is_muon(t) else "lion")
         t += 1
-    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sm.profile_enable(False)
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = 1000.0 * wall / args.steps
-    value = args.steps / wall
-
-    kinds = read_kinds(sm, args.steps)
-    dom = max(kinds, key=lambda k: kinds[k]["ms_per_step"])
-    rl = kind_roofline(kinds, dom, wl.mdt)
-    roofline = {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roofline["traffic"] = recorded_traffic(wl.name, dom)
-    roofline.update({k: v for k, v in rl.items() if k not in roofline})
-    others = {k: kind_roofline(kinds, k, wl.mdt) for k in kinds
-              if k != dom and kinds[k]["ms_per_step"] > 0.05 * ms_per_step}
-
-    ns_ms = sum(kinds.get(k, {}).get("ms_per_step", 0.0) for k in ("gemm_gram", "gemm_apply",
-                                                                   "gemm_rr"))
-    ns_flops = sum(kinds.get(k, {}).get("flops", 0.0) for k in ("gemm_gram", "gemm_apply",
-                                                               "gemm_rr"))
-    extra = {}
-    if ns_ms > 0:
-        extra["ns_tflops"] = ns_flops / (ns_ms * 1e-3) / 1e12
-        extra["ns_mfma_frac"] = extra["ns_tflops"] / PEAK_TFLOPS[wl.mdt]
-        # the direct iteration's flop count over the whole step time: the
-        # rate the pages' form of the iteration would need to match this step
-        extra["ns_direct_form_equivalent_tflops"] = (wl.ns_flops_per_step() /
-                                                     (ms_per_step * 1e-3) / 1e12)
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = 1000.0 * wall / steps
+    value = steps / wall
+    kinds = read_kinds(sm, steps)
+    roofline, others = headline_roofline(kinds, wl.mdt, wl.name, ms_per_step)
+    n_muon = types.count("muon")
+    extra = ns_summary(kinds, wl.mdt, wl, ms_per_step, n_muon / steps)
     if others:
         extra["other_rooflines"] = others
-    if "vote_update" in kinds:
-        vu = kinds["vote_update"]
-        extra["vote_update_gbs"] = vu["bytes"] / (vu["ms_per_step"] * 1e-3) / 1e9
-        extra["vote_update_hbm_frac"] = extra["vote_update_gbs"] / PEAK_HBM_GBS
+
+    if wl.algo == sm.LION_MUON:
+        # per step type: its mean time over the timed region, and a kernel
+        # attribution of one more step of that type
+        per = {}
+        for typ in ("muon", "lion"):
+            ms_t = [m for m, ty in zip(step_ms, types) if ty == typ]
+            if not ms_t:
+                continue
+            while ("muon" if is_muon(t) else "lion") != typ:
+                call(t)
+                t += 1
+            torch.cuda.synchronize()
+            sm.profile_enable(True)
+            sm.profile_reset()
+            call(t)
+            t += 1
+            k1 = read_kinds(sm, 1)
+            sm.profile_enable(False)
+            ms1 = sum(ms_t) / len(ms_t)
+            if typ == "muon":
+                rl, oth = headline_roofline(k1, wl.mdt, wl.name, ms1)
+                summ = ns_summary(k1, wl.mdt, wl, ms1)
+            else:
+                rl = stream_roofline(k1, ["lion"])
+                oth = {k: kind_roofline(k1, k, wl.mdt) for k in k1 if k != "lion"
+                       and k1[k]["ms_per_step"] > 0.05 * ms1}
+                summ = ns_summary(k1, wl.mdt, wl, ms1, 0.0)
+            per[typ] = {"steps_timed": len(ms_t), "ms_per_step": ms1,
+                        "steps_per_s": 1000.0 / ms1, "roofline": rl, "other_rooflines": oth,
+                        **summ, "kernels": k1}
+        extra["per_step_type"] = per
+        if "muon" in per and "lion" in per and P > 0:
+            extra["p_averaged_steps_per_s"] = 1000.0 * P / (per["muon"]["ms_per_step"] +
+                                                            (P - 1) * per["lion"]["ms_per_step"])
     if wl.algo == sm.CACHE_MUON:
         refreshed = sum(int(mb.cache_state[:, 1].eq(t - 1).sum().item()) for mb in mats)
         extra["last_step_refreshed_matrices"] = refreshed
-    variants, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms_per_step, kinds)
-    if variants:
-        extra["variants"] = variants
+    if wl.algo == sm.SIGN_MUON:
+        variants, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms_per_step, kinds)
+        if variants:
+            extra["variants"] = variants
+    del mats, call
+    torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC,
         "value": value,
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
-        "gpu_ms_per_step": gpu_ms / args.steps,
+        "gpu_ms_per_step": sum(step_ms) / steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -559,12 +811,19 @@ def main():
         "config": {"workload": wl.name, "matrices": len(wl.shapes), "params": wl.params,
                    "workers": wl.M, "ns_iters": wl.ns_iters, "algo": ["sign_muon", "cache_muon",
                                                                        "lion_muon"][wl.algo],
+                   "period": wl.period, "muon_steps_timed": n_muon,
                    "weights": wl.wdt, "momentum": wl.mdt, "grads": wl.gdt},
         "roofline": roofline,
         **extra,
         "kernels": kinds,
     }
+    if not args.no_sub and args.config == DEFAULT_CONFIG:
+        print("bench: sub-object gpt2_small", file=sys.stderr, flush=True)
+        out["gpt2_small"] = sign_muon_sub(sm, torch, W, args, 2)
+        print("bench: sub-object gpt2_large_cache_muon", file=sys.stderr, flush=True)
+        out["gpt2_large_cache_muon"] = cache_muon_sub(sm, torch, W, args)
     if not args.no_cpu:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out))
 

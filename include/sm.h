@@ -323,9 +323,14 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
  * the recorded events and returns the totals for one kind;
  * sm_profile_read_bytes returns the kind's algorithmic HBM bytes (every
  * operand read once, every output written once; for streaming kinds the
- * same as the work), from which a GEMM's arithmetic intensity follows.  Enabling
- * creates an event pool (up to 65536 launches); reading or disabling never
- * allocates.  Not thread-safe; meant for one benchmarking thread.
+ * same as the work), from which a GEMM's arithmetic intensity follows.
+ * Launches whose problems run only if a device flag says so (CacheMuon's
+ * fresh solve and cached candidate) are credited with the work of the
+ * problems that actually ran: those kernels add it to a small device-side
+ * accumulator, which reading and resetting synchronise the device to copy.
+ * Enabling creates an event pool (up to 65536 launches); reading or
+ * disabling never allocates.  Not thread-safe; meant for one benchmarking
+ * thread, outside timed regions for reads and resets.
  * ---------------------------------------------------------------------- */
 enum {
   SM_K_EMA = 0,          /* momentum EMA (+ norm partials)         bytes  */

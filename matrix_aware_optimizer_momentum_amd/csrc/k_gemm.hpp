@@ -244,6 +244,10 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   const GemmArgs& g = ka.g;
   const int b = blockIdx.y;
   if (g.pred && g.pred[(int64_t)b * g.pred_stride] != g.pred_val) return;
+  if (g.prof_exec && blockIdx.x == 0 && threadIdx.x == 0) {
+    atomicAdd(g.prof_exec, g.prof_flops);
+    atomicAdd(g.prof_exec + 1, g.prof_bytes);
+  }
 
   const int tile = blockIdx.x;
   const int tm = tile / ka.tiles_n, tn = tile % ka.tiles_n;
@@ -364,7 +368,16 @@ sm_status launch_t(const GemmArgs& g, int kind, hipStream_t s) {
   dim3 grid(ka.tiles, g.batch);
   const double bytes = ((double)g.M * g.K * dt_size(g.a.dt) + (double)g.N * g.K * dt_size(g.b.dt) +
                         (double)g.M * g.N * (g.c ? dt_size(g.c_dt) : 0)) * g.batch;
-  prof_begin(kind, 2.0 * g.M * (double)g.N * g.K * g.batch, s, bytes);
+  double* exec = g.pred ? prof_exec_slot(kind) : nullptr;
+  if (exec) {  // the problems that run report their own work
+    ka.g.prof_exec = exec;
+    ka.g.prof_flops = 2.0 * g.M * (double)g.N * g.K;
+    ka.g.prof_bytes = bytes / g.batch;
+    prof_begin(kind, 0.0, s, 0.0);
+  } else {
+    ka.g.prof_exec = nullptr;
+    prof_begin(kind, 2.0 * g.M * (double)g.N * g.K * g.batch, s, bytes);
+  }
   switch (kind) {
     case SM_K_GEMM_GRAM:
       hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_GRAM>), grid, dim3(NT), 0, s, ka);

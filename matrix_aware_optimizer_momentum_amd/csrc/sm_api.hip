@@ -65,6 +65,19 @@ void prof_end(hipStream_t s) {
   (void)hipEventRecord(g_prof_recs.back().b, s);
 }
 
+// Executed work of predicated launches, accumulated on the device:
+// {flops, bytes} per kernel kind.  Written only by kernels (vector atomics);
+// the host reads and clears it with copies while profiling.
+__device__ __align__(256) double g_prof_exec[2 * SM_K_NUM_KINDS];
+namespace {
+double* g_prof_exec_ptr = nullptr;  // device address of g_prof_exec (current device)
+}
+
+double* prof_exec_slot(int kind) {
+  if (!g_prof_on || !g_prof_exec_ptr || kind < 0 || kind >= SM_K_NUM_KINDS) return nullptr;
+  return g_prof_exec_ptr + 2 * kind;
+}
+
 // ====================================================================== helpers
 
 namespace {
@@ -1484,6 +1497,15 @@ sm_status sm_profile_enable(int on) {
       }
       g_prof_recs.reserve(kProfMax);
     }
+    if (!g_prof_exec_ptr) {
+      void* p = nullptr;
+      hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_prof_exec));
+      if (e != hipSuccess) return hip_fail(e);
+      g_prof_exec_ptr = static_cast<double*>(p);
+      const double zero[2 * SM_K_NUM_KINDS] = {};
+      e = hipMemcpy(g_prof_exec_ptr, zero, sizeof(zero), hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_fail(e);
+    }
     g_prof_on = true;
   } else {
     g_prof_on = false;
@@ -1494,7 +1516,24 @@ sm_status sm_profile_enable(int on) {
 sm_status sm_profile_reset(void) {
   g_prof_recs.clear();
   g_prof_open = false;
+  if (g_prof_exec_ptr) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e);
+    const double zero[2 * SM_K_NUM_KINDS] = {};
+    e = hipMemcpy(g_prof_exec_ptr, zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return SM_OK;
+}
+
+// Executed {flops, bytes} of a kind's predicated launches so far.
+static sm_status read_exec(int kind, double* out2) {
+  out2[0] = out2[1] = 0.0;
+  if (!g_prof_exec_ptr) return SM_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipMemcpy(out2, g_prof_exec_ptr + 2 * kind, 2 * sizeof(double), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 
 sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double* work) {
@@ -1512,9 +1551,11 @@ sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double*
     wk += r.work;
     ++n;
   }
+  double ex[2];
+  SM_TRY(read_exec(kind, ex));
   *ms_total = ms;
   *launches = n;
-  *work = wk;
+  *work = wk + ex[0];
   return SM_OK;
 }
 
@@ -1523,7 +1564,9 @@ sm_status sm_profile_read_bytes(int kind, double* bytes) {
   double b = 0.0;
   for (const ProfRec& r : g_prof_recs)
     if (r.kind == kind) b += r.bytes;
-  *bytes = b;
+  double ex[2];
+  SM_TRY(read_exec(kind, ex));
+  *bytes = b + ex[1];
   return SM_OK;
 }
 

@@ -111,6 +111,11 @@ __device__ __forceinline__ const char* tbl_addr(const PtrTbl& t, int b, int per,
 // negative means "same as work".
 void prof_begin(int kind, double work, hipStream_t s, double bytes = -1.0);
 void prof_end(hipStream_t s);
+// Device address of a kind's {executed flops, executed bytes} accumulator
+// while profiling is enabled, else null.  Launches whose problems are
+// predicated on a device flag record no work on the host; their kernels add
+// the work of the problems that ran here.
+double* prof_exec_slot(int kind);
 
 // Records a failed HIP call and maps it to SM_ERR_HIP.
 sm_status hip_fail(hipError_t e);
@@ -295,6 +300,9 @@ struct GemmArgs {
   // (CacheMuon's per-matrix Q caches); tbl_per problems per entry.
   PtrTbl tbl;
   int tbl_per;
+  // Kernel-time accounting of predicated launches (set by the launcher):
+  // each problem that runs adds prof_flops / prof_bytes to prof_exec[0 / 1].
+  double* prof_exec; double prof_flops, prof_bytes;
 };
 
 // Tiles per problem that the GEMM launch uses for (M, N) (resid partials).
