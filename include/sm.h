@@ -105,6 +105,24 @@ sm_status sm_ns_polar(const void* x, void* u, int dt, int batch, int m, int n,
                       hipStream_t s);
 
 /* ------------------------------------------------------------------------
+ * sm_ns_polar without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same inputs, outputs, kernels
+ * and results (bit for bit) as sm_ns_polar; the scratch is a fixed device
+ * array inside the library of SM_NS_NOALLOC_MAX_WS bytes (64 MiB), one per
+ * GPU, held until the process ends.  The call allocates nothing and uses
+ * no zero-initialised scratch.  Limit: sm_ns_polar_ws(dt, batch, m, n) must
+ * not exceed SM_NS_NOALLOC_MAX_WS (about a 2048 x 8192 bf16 problem, or
+ * eight 768 x 3072 ones), else SM_ERR_WORKSPACE and nothing is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or host threads) race and must be ordered by
+ * the caller.  Errors as for sm_ns_polar.
+ * ---------------------------------------------------------------------- */
+#define SM_NS_NOALLOC_MAX_WS (64u << 20)
+sm_status sm_ns_polar_noalloc(const void* x, void* u, int dt, int batch, int m, int n,
+                              int normalize, const sm_ns_params* p, hipStream_t s);
+
+/* ------------------------------------------------------------------------
  * CacheMuon orthogonalisation: Gram Newton-Schulz with a cached left
  * transform Q and a residual-based reuse trigger.
  * [CacheMuon-ja] method, core mechanism items 1-3: a refresh runs the fresh

@@ -21,6 +21,7 @@ SIGN_MUON, CACHE_MUON, LION_MUON = 0, 1, 2
 UPDATE_VOTE, UPDATE_POLAR = 0, 1
 MODE_TRIGGER, MODE_FORCE_FRESH, MODE_FORCE_REUSE = 0, 1, 2
 ENC_BITS, ENC_INT8 = 0, 1
+NS_NOALLOC_MAX_WS = 64 << 20   # SM_NS_NOALLOC_MAX_WS
 
 KERNEL_KINDS = ["ema", "norm", "gemm_gram", "gemm_apply", "gemm_rr", "probe", "sign_pack",
                 "vote_update", "lion", "polar_update", "misc", "spectral"]
@@ -56,6 +57,8 @@ SIGNATURES = {
     "sm_ns_polar_ws": (c_int, [c_int, c_int, c_int, c_int, P(c_size_t)]),
     "sm_ns_polar": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, P(NSParams),
                             c_void_p, c_size_t, c_void_p]),
+    "sm_ns_polar_noalloc": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                    P(NSParams), c_void_p]),
     "sm_gram_ns_cached_ws": (c_int, [c_int, c_int, c_int, c_int, P(c_size_t)]),
     "sm_gram_ns_cached": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int, c_int, c_int, c_int, c_int, P(NSParams), c_float,

@@ -126,6 +126,22 @@ def ns_polar(x: torch.Tensor, out: Optional[torch.Tensor] = None, normalize: boo
     return out
 
 
+def ns_polar_noalloc(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     normalize: bool = True, params: Optional[NSParams] = None) -> torch.Tensor:
+    """sm_ns_polar on the library's fixed scratch (no workspace argument).
+    With out given, nothing is allocated here either."""
+    _dev(x, "x")
+    batch, m, n = _bmn(x)
+    p = params or NSParams()
+    out = torch.empty_like(x) if out is None else out
+    _expect(out, "out", x.shape, x.dtype)
+    cp = p.c_struct()
+    code = B.lib().sm_ns_polar_noalloc(x.data_ptr(), out.data_ptr(), _dt(x), batch, m, n,
+                                       int(normalize), ctypes.byref(cp), _stream())
+    B.check(code, "sm_ns_polar_noalloc")
+    return out
+
+
 # ------------------------------------------------------------------ sm_gram_ns_cached
 
 def gram_ns_cached_ws(dtype: torch.dtype, batch: int, m: int, n: int) -> int:

@@ -1109,6 +1109,55 @@ sm_status sm_ns_polar(const void* x, void* u, int dt, int batch, int m, int n, i
   return ns_core(x, u, w, normalize ? scale : nullptr, dt, batch, m, n, *p, s);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ static scratch
+
+// Scratch of sm_ns_polar_noalloc: a file-scope device array (each device the
+// library runs on holds its own copy until the process ends).  In host code
+// `scratch` names a host-side stand-in, never a device address: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// pointer is passed to kernels.
+__device__ __align__(256) unsigned char scratch[SM_NS_NOALLOC_MAX_WS];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device ordinal -> device address of `scratch`
+
+sm_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return SM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+sm_status sm_ns_polar_noalloc(const void* x, void* u, int dt, int batch, int m, int n,
+                              int normalize, const sm_ns_params* p, hipStream_t s) {
+  if (!valid_dt(dt)) return SM_ERR_DTYPE;
+  SM_TRY(check_shape(batch, m, n));
+  SM_TRY(check_ns_params(p));
+  if (!x || !u || !al16(x) || !al16(u)) return SM_ERR_ARG;
+  if (normalize != 0 && normalize != 1) return SM_ERR_ARG;
+  size_t need = 0;
+  SM_TRY(sm_ns_polar_ws(dt, batch, m, n, &need));
+  if (need > (size_t)SM_NS_NOALLOC_MAX_WS) return SM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  SM_TRY(scratch_address(&ws));
+  return sm_ns_polar(x, u, dt, batch, m, n, normalize, p, ws, (size_t)SM_NS_NOALLOC_MAX_WS, s);
+}
+
 sm_status sm_gram_ns_cached_ws(int dt, int batch, int m, int n, size_t* ws_bytes) {
   if (!ws_bytes) return SM_ERR_ARG;
   if (!valid_dt(dt)) return SM_ERR_DTYPE;

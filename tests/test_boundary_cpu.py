@@ -278,3 +278,16 @@ def test_step_front_end_checks_cache_buffers_and_diag():
         StepCall(StepConfig(M=3), _cpu_mats(), diag=torch.zeros(5))
     with pytest.raises(ValueError, match="at least one matrix"):
         StepCall(StepConfig(M=3), [])
+
+
+def test_noalloc_entry_point_rejects_oversized_problems_on_the_host():
+    """The scratch limit is checked before any HIP call."""
+    lib = B.lib()
+    p = B.NSParams(5, 1.5, -0.5, 0.0, 1e-7)
+    need = ctypes.c_size_t(0)
+    assert lib.sm_ns_polar_ws(B.BF16, 4, 4096, 4096, ctypes.byref(need)) == 0
+    assert need.value > B.NS_NOALLOC_MAX_WS
+    assert lib.sm_ns_polar_noalloc(ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000000),
+                                   B.BF16, 4, 4096, 4096, 1, ctypes.byref(p), None) == 4
+    assert lib.sm_ns_polar_noalloc(None, None, B.BF16, 1, 8, 8, 1, ctypes.byref(p), None) == 1
+    assert lib.sm_last_hip_error() == 0
