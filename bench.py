@@ -13,11 +13,12 @@ Prints one JSON line: steps/s (value), per-step-type times and rooflines
 (Muon step: NS GEMMs against the bf16 MFMA peak; Lion step: the fused Lion
 kernel against HBM), the roofline of the dominant kernel measured with HIP
 events on the step's stream over the timed region, the CPU oracle timed on a
-bounded sample on this host, and sub-objects for two more configurations:
+bounded sample on this host, and sub-objects for the other configurations:
 `gpt2_small` (Sign-Muon, M = 5; with the int8 encoding and the polar step on
-the vote as variants) and `gpt2_large_cache_muon` (CacheMuon at gamma 2, 15,
-a mixed-rate gamma and always-fresh, with refresh rates and executed
-orthogonalisation FLOPs).
+the vote as variants), `gpt2_large_cache_muon` (CacheMuon at gamma 2, 15, a
+mixed-rate gamma and always-fresh, with refresh rates and executed
+orthogonalisation FLOPs), `resnet50` (53 float32 convolution matrices, M =
+4, one NS iteration) and `single_256` (one float32 256 x 256 matrix, M = 3).
 
   python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu] [--no-sub]
   python bench.py --copy-calibration   # plain device copy of known size, for
@@ -62,7 +63,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--no-sub", action="store_true",
-                    help="skip the GPT-2-small and GPT-2-large sub-objects")
+                    help="skip the sub-objects of the other configurations")
     ap.add_argument("--sub-steps", type=int, default=20,
                     help="timed steps of each sub-object run")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -569,22 +570,24 @@ def ns_summary(kinds, mdt, wl, ms_per_step, muon_fraction=1.0):
     return out
 
 
-def sign_muon_sub(sm, torch, W, args, index=2):
+def sign_muon_sub(sm, torch, W, args, index=2, steps=None, variants=True):
     """A Sign-Muon configuration timed like the headline (wall clock over the
     timed steps), with its dominant-kernel roofline and the step variants."""
     wl = W.WORKLOADS[index]
+    steps = steps or args.sub_steps
     mats = build_state(wl)
     cfg = step_config(wl)
     call = sm.StepCall(cfg, mats)
-    t, wall, kinds = timed_steps(sm, torch, call, 1, 3, args.sub_steps)
-    ms = 1000.0 * wall / args.sub_steps
+    t, wall, kinds = timed_steps(sm, torch, call, 1, 3, steps)
+    ms = 1000.0 * wall / steps
     roofline, others = headline_roofline(kinds, wl.mdt, wl.name, ms)
-    out = {"workload": wl.name, "value": args.sub_steps / wall, "unit": "steps/s",
-           "ms_per_step": ms, "steps": args.sub_steps, "roofline": roofline,
+    out = {"workload": wl.name, "value": steps / wall, "unit": "steps/s",
+           "ms_per_step": ms, "steps": steps, "roofline": roofline,
            **ns_summary(kinds, wl.mdt, wl, ms), "other_rooflines": others, "kernels": kinds}
-    variants, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms, kinds)
     if variants:
-        out["variants"] = variants
+        v, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms, kinds)
+        if v:
+            out["variants"] = v
     del mats, call
     torch.cuda.empty_cache()
     return out
@@ -822,6 +825,9 @@ def main():
         out["gpt2_small"] = sign_muon_sub(sm, torch, W, args, 2)
         print("bench: sub-object gpt2_large_cache_muon", file=sys.stderr, flush=True)
         out["gpt2_large_cache_muon"] = cache_muon_sub(sm, torch, W, args)
+        print("bench: sub-objects resnet50, single_256", file=sys.stderr, flush=True)
+        out["resnet50"] = sign_muon_sub(sm, torch, W, args, 3, variants=False)
+        out["single_256"] = sign_muon_sub(sm, torch, W, args, 1, steps=100, variants=False)
     if not args.no_cpu:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -85,18 +85,29 @@ struct Grp {
   int alpha_pow;
   float alpha;
   int tiles_m, tiles_n, tiles_per_prob, tile_begin;
+  int tpp_begin;               // tiles per problem of the groups before this one
   int a_tbl, b_tbl, tbl_per;   // per-matrix operand addressing (see NsgGroup)
   int a_low, b_low;            // operand stored as its lower triangle of tiles
   int c_low;                   // symmetric C: store the lower triangle only
   int tbl;                     // byte offset of the group's table in Args
   uint64_t* bits;              // apply: signs instead of C (see NsgGroup)
   int64_t bits_stride;
+  const int32_t* pred;         // per-problem store predicate (see NsgGroup), or null
+  float* resid;                // probe: residual partials (see NsgGroup)
 };
 
 struct Args {
   Grp g[kNsgMaxGroups];
   PtrTbl tbl[kNsgMaxTables];
+  const int32_t* gate;         // launch-wide: nothing to do while *gate == 0
+  // Problem list on the device, or null: dyn[0] problems run, the indices
+  // dyn[1 ..] (every group has the same problems); tiles are then laid out
+  // group by group over those problems only.
+  const int32_t* dyn;
+  double* prof_exec;           // gated launch while profiling: work added here when it runs
+  double prof_flops, prof_bytes;   // per launch, or per listed problem with dyn
   int ngroups, total_tiles, xcd_chunk;
+  int tpp_total;               // tiles per problem over all groups
 };
 static_assert(sizeof(Args) <= 4096, "kernel arguments stay within 4 KB");
 
@@ -132,17 +143,33 @@ struct Tile {
   int gi, prob, tm, tn;
 };
 
-__device__ __forceinline__ Tile decode_tile(const Args& A, int t) {
+// A wave-uniform int32 loaded through the scalar unit (counted by lgkmcnt,
+// not vmcnt, so it does not wait for the loads in flight); the wait is in the
+// same statement.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const int32_t* q = reinterpret_cast<const int32_t*>(((uint64_t)hi << 32) | lo);
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
+  return v;
+}
+
+// Tile t of the launch; cnt < 0: the static layout, else the device problem
+// list with cnt problems (see Args::dyn).
+__device__ __forceinline__ Tile decode_tile(const Args& A, int t, int cnt) {
   Tile r;
   int gi = 0;
 #pragma unroll
   for (int q = 1; q < kNsgMaxGroups; ++q)
-    if (q < A.ngroups && t >= A.g[q].tile_begin) gi = q;
+    if (q < A.ngroups && t >= (cnt < 0 ? A.g[q].tile_begin : cnt * A.g[q].tpp_begin)) gi = q;
   const Grp& g = A.g[gi];
-  const int local = t - g.tile_begin;
+  const int local = t - (cnt < 0 ? g.tile_begin : cnt * g.tpp_begin);
   r.gi = gi;
-  r.prob = local / g.tiles_per_prob;
-  const int u = local - r.prob * g.tiles_per_prob;
+  const int pc = local / g.tiles_per_prob;
+  r.prob = cnt < 0 ? pc : sload_i32(A.dyn + 1 + pc);
+  const int u = local - pc * g.tiles_per_prob;
   if (g.sym) {  // lower triangle, row-major: u = tm (tm + 1) / 2 + tn
     int tm = (int)((sqrtf(8.f * u + 1.f) - 1.f) * 0.5f);
     while ((tm + 1) * (tm + 2) / 2 <= u) ++tm;
@@ -199,6 +226,8 @@ struct LoadPos {
   int kg;       // group of 4 stages within the tile
   int nkg;      // groups in the tile
   int sw;       // next group where a lower-stored operand turns to KR reads
+  int cnt;      // problems of a device problem list (-1: static layout)
+  int total;    // tiles of the launch
 };
 
 // The first group past the diagonal block of panel p (256 operand rows, two
@@ -218,7 +247,7 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r
   t = __builtin_amdgcn_readfirstlane(t);
   r = __builtin_amdgcn_readfirstlane(r);
   kg = __builtin_amdgcn_readfirstlane(kg);
-  const Tile tl = decode_tile(A, t);
+  const Tile tl = decode_tile(A, t, L.cnt);
   const Grp& g = A.g[tl.gi];
   // the group's table, addressed by its byte offset in the arguments (an
   // index into Args::tbl makes the compiler copy the arguments to scratch)
@@ -253,7 +282,7 @@ __device__ __forceinline__ void load_advance(LoadPos& p, const Args& A, int vid,
     const bool next = p.kg + 1 >= p.nkg;
     const int r = next ? p.r + 1 : p.r;
     const int nt = tile_of(r, vid, stride);
-    if (nt < A.total_tiles) load_tile_setup(p, A, r, nt, next ? 0 : p.kg + 1);
+    if (nt < p.total) load_tile_setup(p, A, r, nt, next ? 0 : p.kg + 1);
   }
 }
 
@@ -319,6 +348,11 @@ __device__ __forceinline__ float scalar_load(const float* p) {
   float v;
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
   return v;
+}
+
+// A wave-uniform int32 loaded through the scalar unit (see scalar_load).
+__device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
+  return __builtin_bit_cast(int, scalar_load(reinterpret_cast<const float*>(p)));
 }
 
 // Workgroup barrier without a memory fence (no wait for outstanding direct-
@@ -840,6 +874,35 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], bf16_t* C, i
   }
 }
 
+// The probe's epilogue: this wave's part of sum (alpha * acc - [row == col])^2
+// over the entries inside M x N, times `weight`, as one float at *out (a
+// vector store from lane 0); the wave's memory operations are drained, so
+// that the next tile's first waits hold (see run_tile).
+__device__ __forceinline__ void epilogue_resid(const f32x16 (&acc)[4][4], float* out, int M,
+                                               int N, int wr0, int wc0, float alpha,
+                                               float weight) {
+  const int lane = fresh_tid() & 63;
+  const int lr = lane & 31, lq = (lane >> 5) * 4;
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wr0 + 32 * i + 8 * (v >> 2) + lq + (v & 3);
+        const int col = wc0 + 32 * j + lr;
+        if (row < M && col < N) {
+          const float d = __fsub_rn(__fmul_rn(alpha, acc[i][j][v]), row == col ? 1.f : 0.f);
+          part = __fmaf_rn(d, d, part);
+        }
+      }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part = __fadd_rn(part, __shfl_xor(part, o, 64));
+  if (lane == 0) *out = __fmul_rn(weight, part);
+  wait_vm<0>();
+}
+
 // The writelane intrinsic, which this compiler exposes under no builtin
 // name.  Going through the intrinsic (not inline asm) keeps the instruction
 // visible to the hazard recognizer: v_writelane reads its value from an SGPR
@@ -926,7 +989,8 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 //          2 (KC, KR, A-side id, 2 terms)  3 (KC, KC, B-side id, 2 terms)
 //          4 (KC, KR)        5 (KC, KC)
 //          6 (A lower-stored, KR)          7 (KC, B lower-stored)
-constexpr int ROLE_SYM = 0, ROLE_APPLY = 1;
+//   PROBE: 0 (KC, KC)       1 (KR, KR)    (symmetric, residual epilogue)
+constexpr int ROLE_SYM = 0, ROLE_APPLY = 1, ROLE_PROBE = 2;
 template <int ROLE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_ns(Args args) {
@@ -942,6 +1006,18 @@ void k_gemm_ns(Args args) {
   int round = 0;
   int t = tile_of(0, vid, stride);
   if (t >= A.total_tiles) return;
+  if (A.gate && scalar_load_i32(A.gate) == 0) return;   // uniform over the launch
+  int cnt = -1, total = A.total_tiles;
+  if (A.dyn) {
+    cnt = sload_i32(A.dyn);
+    total = cnt * A.tpp_total;
+    if (t >= total) return;
+  }
+  if (A.prof_exec && blockIdx.x == 0 && threadIdx.x == 0) {
+    const double mult = A.dyn ? (double)cnt : 1.0;
+    atomicAdd(A.prof_exec, mult * A.prof_flops);
+    atomicAdd(A.prof_exec + 1, mult * A.prof_bytes);
+  }
 
   const int wave = threadIdx.x >> 6;
 
@@ -951,6 +1027,8 @@ void k_gemm_ns(Args args) {
   // prologue: the first tile's stages 0..3 into buffers 0..3; the load
   // position then moves one group ahead
   LoadPos LP;
+  LP.cnt = cnt;
+  LP.total = total;
   load_tile_setup(LP, A, 0, t);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -967,7 +1045,7 @@ void k_gemm_ns(Args args) {
 
   bool lenient = false;
   for (;;) {
-    const Tile tc = decode_tile(A, t);
+    const Tile tc = decode_tile(A, t, cnt);
     const Grp& g = A.g[tc.gi];
     const int nkg = g.K / (4 * BK);
     // this wave's 128 x 128 quarter (wm, wn) of the tile, derived again after
@@ -1006,6 +1084,12 @@ void k_gemm_ns(Args args) {
         run_tile_low<3, 3, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg,
                               low_switch(tc.tm, nkg), low_switch(tc.tn, nkg), id_g, wm, wn, id,
                               lenient);
+      }
+    } else if constexpr (ROLE == ROLE_PROBE) {
+      if (g.combo == 0) {
+        run_tile<0, 0, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
+      } else {
+        run_tile<1, 1, 0, 1>(acc, f0, f1, smem, la0, cb, wbase, LP, A, vid, stride, nkg, id_g, wm, wn, id, lenient);
       }
     } else {
       if (g.combo == 0) {
@@ -1048,7 +1132,16 @@ void k_gemm_ns(Args args) {
     // past its reads of that stage once all have met here.
     bf16_t* stage = smem + (cb == 0 ? NBUF - 1 : cb - 1) * STG +
                     4096 * __builtin_amdgcn_readfirstlane(fresh_tid() >> 6);
-    if constexpr (ROLE == ROLE_APPLY) {
+    if (g.pred && scalar_load_i32(g.pred + tc.prob) != 1) {
+      // a problem that keeps its output: nothing stored; drained like an edge
+      // epilogue, so that the next tile's first waits hold (see run_tile)
+      wait_vm<0>();
+    } else if constexpr (ROLE == ROLE_PROBE) {
+      const int u = tc.tm * (tc.tm + 1) / 2 + tc.tn;
+      float* out = g.resid + (int64_t)tc.prob * 4 * g.tiles_per_prob + 4 * u +
+                   __builtin_amdgcn_readfirstlane(fresh_tid() >> 6);
+      epilogue_resid(acc, out, g.M, g.N, wr0, wc0, alpha, tc.tm != tc.tn ? 2.f : 1.f);
+    } else if constexpr (ROLE == ROLE_APPLY) {
       if (g.bits) {   // the last iteration of a vote-mode step: signs only
         uint64_t* bp = g.bits + (int64_t)tc.prob * g.bits_stride;
         if (alpha == 1.f)
@@ -1070,7 +1163,7 @@ void k_gemm_ns(Args args) {
                             g.sym && !g.c_low && tc.tm != tc.tn, stage);
     }
     t = tile_of(++round, vid, stride);
-    if (t >= A.total_tiles) break;
+    if (t >= total) break;
     // every epilogue issues >= 32 stores or drains (see run_tile)
     lenient = true;
   }
@@ -1175,11 +1268,13 @@ int ns_group_tables(const NsgGroup* groups, int ngroups) {
   return n;
 }
 
-sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s) {
+sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s,
+                         const int32_t* gate, const int32_t* dyn) {
   using namespace nsg;
   if (ngroups <= 0 || ngroups > kNsgMaxGroups) return SM_ERR_ARG;
   const bool apply = kind == SM_K_GEMM_APPLY;
-  if (!apply && kind != SM_K_GEMM_GRAM && kind != SM_K_GEMM_RR) return SM_ERR_ARG;
+  const bool probe = kind == SM_K_PROBE;
+  if (!apply && !probe && kind != SM_K_GEMM_GRAM && kind != SM_K_GEMM_RR) return SM_ERR_ARG;
   Args a;
   std::memset(&a, 0, sizeof(a));
   const PtrTbl* tbls[kNsgMaxTables];
@@ -1202,7 +1297,11 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.alpha = G.alpha;
     g.bits = G.bits;
     g.bits_stride = G.bits_stride;
+    g.pred = G.pred;
+    g.resid = G.resid;
+    if (probe != (G.resid != nullptr)) return SM_ERR_UNSUPPORTED;
     if (G.bits && !apply) return SM_ERR_UNSUPPORTED;
+    if (G.pred && G.bits) return SM_ERR_UNSUPPORTED;
     g.a_tbl = G.a_tbl ? 1 : 0;
     g.b_tbl = G.b_tbl ? 1 : 0;
     g.tbl_per = G.tbl_per;
@@ -1224,7 +1323,10 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     int combo = -1;
     const bool two = G.ident && G.ident_terms == 2;
     const int low = (g.a_low ? 1 : 0) | (g.b_low ? 2 : 0);
-    if (!apply && g.sym) {
+    if (probe) {
+      if (g.sym && !G.ident && !low && !G.c_low && !G.pred && g.a_kr == g.b_kr)
+        combo = g.a_kr ? 1 : 0;
+    } else if (!apply && g.sym) {
       if (low == 3) {
         if (G.ident == 2 && !two) combo = 5;
         else if (G.ident == 3 && !two) combo = 6;
@@ -1254,6 +1356,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.tiles_n = (G.N + 255) / 256;
     g.tiles_per_prob = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
     g.tile_begin = tiles;
+    g.tpp_begin = a.tpp_total;
+    a.tpp_total += g.tiles_per_prob;
+    if (dyn && (G.batch != groups[0].batch || G.a_tbl || G.b_tbl)) return SM_ERR_UNSUPPORTED;
     const int64_t gt = (int64_t)g.tiles_per_prob * G.batch;
     if (gt <= 0) return SM_ERR_ARG;
     if ((int64_t)tiles + gt > (int64_t)1 << 30) return SM_ERR_UNSUPPORTED;
@@ -1267,17 +1372,30 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
                       G.a_low == G.b_low;
     const double ea = G.a_low ? lower_tile_entries(G.M) : G.M * (double)G.K;
     const double eb = G.b_low ? lower_tile_entries(G.N) : G.N * (double)G.K;
-    const double ec = G.bits ? G.M * (double)G.N / 16.0
+    const double ec = probe ? 2.0 * ns_probe_parts(G.M)   // the float partials
+                      : G.bits ? G.M * (double)G.N / 16.0
                              : (G.c_low ? lower_tile_entries(G.M) : G.M * (double)G.N);
     bytes += 2.0 * ((same ? 0.0 : eb) + ea + ec) * G.batch;
   }
   a.ngroups = ngroups;
   a.total_tiles = tiles;
+  a.gate = gate;
+  a.dyn = dyn;
   const int grid = std::min(tiles, cu_count());
   a.xcd_chunk = (grid % 8 == 0) ? grid / 8 : 0;
-  prof_begin(kind, flops, s, bytes);
+  double* exec = (gate || dyn) ? prof_exec_slot(kind) : nullptr;
+  if (exec) {   // a gated launch reports its work only if it runs (per listed problem)
+    a.prof_exec = exec;
+    a.prof_flops = dyn ? flops / groups[0].batch : flops;
+    a.prof_bytes = dyn ? bytes / groups[0].batch : bytes;
+    prof_begin(kind, 0.0, s, 0.0);
+  } else {
+    prof_begin(kind, flops, s, bytes);
+  }
   if (apply)
     hipLaunchKernelGGL((k_gemm_ns<ROLE_APPLY>), dim3(grid), dim3(NT), 0, s, a);
+  else if (probe)
+    hipLaunchKernelGGL((k_gemm_ns<ROLE_PROBE>), dim3(grid), dim3(NT), 0, s, a);
   else
     hipLaunchKernelGGL((k_gemm_ns<ROLE_SYM>), dim3(grid), dim3(NT), 0, s, a);
   prof_end(s);

@@ -117,16 +117,29 @@ __device__ __forceinline__ uint32_t neg_byte(const float* v, int64_t e0, int64_t
   return byte;
 }
 
-// Each thread leaves one byte (8 entries) in sbytes[tid]; threads 0..31 then
-// store the block's 2048 entries as 32 uint64 words (LSB-first).
-__device__ __forceinline__ void flush_bytes(uint8_t* sbytes, uint64_t* bits, int64_t word0,
-                                            int64_t words) {
-  __syncthreads();
-  if (threadIdx.x < kChunk / 64) {
-    int64_t wi = word0 + threadIdx.x;
-    if (wi < words) bits[wi] = reinterpret_cast<const uint64_t*>(sbytes)[threadIdx.x];
+// The sign word of 64 consecutive entries, assembled across the 8 lanes that
+// hold them: lane 8q + i of a wave holds the byte of entries 8i..8i+7 of the
+// group's word (bit e of the byte = entry 8i + e); every lane of the group
+// gets the word.  All lanes of the wave must call it.
+__device__ __forceinline__ uint64_t group8_word(uint32_t byte) {
+  const int sh = 8 * (threadIdx.x & 7);
+  uint32_t lo = sh < 32 ? byte << sh : 0u;
+  uint32_t hi = sh >= 32 ? byte << (sh - 32) : 0u;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    lo |= (uint32_t)__shfl_xor((int)lo, o, 64);
+    hi |= (uint32_t)__shfl_xor((int)hi, o, 64);
   }
-  __syncthreads();
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Stores the sign word of the thread's 8-lane group: the thread's entries
+// start at e0 = 8 * (thread index in a 64-entry-aligned run), so word e0/64.
+__device__ __forceinline__ void store_group_word(uint64_t* bits, int64_t e0, int64_t words,
+                                                 uint32_t byte) {
+  const uint64_t w = group8_word(byte);
+  const int64_t wi = e0 >> 6;
+  if ((threadIdx.x & 7) == 0 && wi < words) bits[wi] = w;
 }
 
 // Eight int8 signs (-1 iff v[e] < 0, else +1) of entries e0..e0+7, stored
@@ -199,7 +212,6 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
                                                    float* partials, uint64_t* bits,
                                                    int64_t words, int8_t* s8, bool vec) {
   __shared__ float red[4];
-  __shared__ uint8_t sbytes[kThreads];
   const int b = blockIdx.y;
   TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
   const TG* g = (const TG*)tbl_addr(grad, b, per, count * (int64_t)sizeof(TG));
@@ -233,10 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
         store8_tail<TX>(xo, e0, count, vec, dv);
       }
     }
-    if (bo) {
-      sbytes[threadIdx.x] = (uint8_t)byte;
-      flush_bytes(sbytes, bo, ci * (kChunk / 64), words);
-    }
+    if (bo) store_group_word(bo, e0, words, byte);
   }
   if (!bo && !so) {
     float s = block_sum(acc, red);
@@ -290,7 +299,6 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_sign_pack(const T* x, int64_t count,
                                                         uint64_t* bits, int64_t words,
                                                         bool vec) {
-  __shared__ uint8_t sbytes[kThreads];
   const int b = blockIdx.y;
   const T* xp = x + (int64_t)b * count;
   uint64_t* bo = bits + (int64_t)b * words;
@@ -303,8 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_sign_pack(const T* x, int64_t coun
       load8_tail<T>(xp, e0, count, vec, v);
       byte = neg_byte(v, e0, count);
     }
-    sbytes[threadIdx.x] = (uint8_t)byte;
-    flush_bytes(sbytes, bo, ci * (kChunk / 64), words);
+    store_group_word(bo, e0, words, byte);
   }
 }
 
@@ -323,20 +330,116 @@ __global__ __launch_bounds__(kThreads) void k_sign_int8(const T* x, int64_t coun
   }
 }
 
-// Vote over M <= 64 workers for 8 entries per thread.
-//  ENC 0 (packed bits): each worker's byte of sign bits is spread to one
-//    byte-wide counter per entry (a nibble times 0x00204081 places bit i at
-//    bit 8i; the 4 partial products never overlap), so one 32-bit add counts
-//    4 entries at once; counts stay below 256; sum = M - 2 n_neg.
-//  ENC 1 (int8 signs): the integer sum of the workers' bytes, as the SUM
-//    all-reduce of the int8 variant would deliver it.
-// V = sign(sum), 0 on ties.  UPDATE: W <- rnd_W(fp32(W) - lr V) in place in
-// the table's matrices (and the vote to vote_out); otherwise V itself is
-// written, as TW, to the table's matrices.  Strides count words (ENC 0) or
-// bytes (ENC 1).
-// Vote (+ update) of one matrix's entries 8 at a time, threads bx .. of nbx:
-// sg is the matrix's first worker's signs (packed words, or int8), the M
-// workers stride entries (words / bytes) apart.
+// ------------------------------------------------------------------ 1-bit vote
+
+// Per block iteration a tile of 256 sign words (16384 entries).  Phase 1:
+// thread t reads word t of every worker (8-byte loads, each worker's 2 KB of
+// the tile contiguous) and counts the negatives of its 64 entries in
+// bit-sliced form: plane p of the count of entry j is bit j of c[p], and a
+// worker's word is added with a ripple of carries through the 7 planes
+// (counts up to 64).  The vote of entry j is +1 iff 2 n_neg < M and -1 iff
+// 2 n_neg > M (0 on a tie), i.e. n_neg < ceil(M/2) and n_neg > floor(M/2),
+// compared plane by plane from the top.  The two 64-bit masks go to LDS.
+// Phase 2: thread t takes the tile's 8-entry groups t, t + 256, ...: their
+// vote bytes come from LDS, and the weights are read and written with
+// 16-byte accesses that are contiguous across the block.
+constexpr int kVotePlanes = 7;
+
+__device__ __forceinline__ void bits_less_greater(const uint64_t* c, int k, uint64_t* lt,
+                                                  uint64_t* gt) {
+  uint64_t l = 0, g = 0, eq = ~0ull;
+#pragma unroll
+  for (int p = kVotePlanes - 1; p >= 0; --p) {
+    if ((k >> p) & 1) {
+      l |= eq & ~c[p];
+      eq &= c[p];
+    } else {
+      g |= eq & c[p];
+      eq &= ~c[p];
+    }
+  }
+  *lt = l;
+  *gt = g;
+}
+
+template <typename TW, bool UPDATE>
+__device__ __forceinline__ void vote_bits_tiles(const uint64_t* sg, int M, int64_t stride,
+                                                int64_t count, TW* wp, float lr,
+                                                int8_t* vote_out, bool vec, int64_t tile0,
+                                                int64_t tstep, uint64_t* pos_s,
+                                                uint64_t* neg_s) {
+  const int64_t words = (count + 63) / 64;
+  const int64_t ntiles = (words + kThreads - 1) / kThreads;
+  const int k_pos = (M + 1) / 2, k_neg = M / 2;
+  for (int64_t tile = tile0; tile < ntiles; tile += tstep) {
+    const int64_t wi = tile * kThreads + threadIdx.x;
+    uint64_t c[kVotePlanes];
+#pragma unroll
+    for (int p = 0; p < kVotePlanes; ++p) c[p] = 0;
+    if (wi < words) {
+      for (int k0 = 0; k0 < M; k0 += 8) {
+        uint64_t wd[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)       // all eight loads issued before the adds
+          wd[q] = k0 + q < M ? sg[(int64_t)(k0 + q) * stride + wi] : 0ull;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          uint64_t carry = wd[q];
+#pragma unroll
+          for (int p = 0; p < kVotePlanes; ++p) {
+            const uint64_t t = c[p] & carry;
+            c[p] ^= carry;
+            carry = t;
+          }
+        }
+      }
+    }
+    uint64_t pos, neg, unused;
+    bits_less_greater(c, k_pos, &pos, &unused);   // n_neg < ceil(M/2): +1
+    bits_less_greater(c, k_neg, &unused, &neg);   // n_neg > floor(M/2): -1
+    pos_s[threadIdx.x] = pos;
+    neg_s[threadIdx.x] = neg;
+    __syncthreads();
+    const uint8_t* pb = reinterpret_cast<const uint8_t*>(pos_s);
+    const uint8_t* nb = reinterpret_cast<const uint8_t*>(neg_s);
+    const int64_t et = tile * (int64_t)kThreads * 64;
+#pragma unroll
+    for (int g8 = 0; g8 < 8; ++g8) {
+      const int q = g8 * kThreads + threadIdx.x;   // 8-entry group within the tile
+      const int64_t e0 = et + (int64_t)q * 8;
+      if (e0 < count) {
+        const uint32_t pbyte = pb[q], nbyte = nb[q];
+        float wv[8];
+        int vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = (int)((pbyte >> e) & 1u) - (int)((nbyte >> e) & 1u);
+        if constexpr (UPDATE) {
+          load8_tail<TW>(wp, e0, count, vec, wv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wv[e] = wv[e] - lr * (float)vv[e];  // lr*v exact: one rounding
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wv[e] = (float)vv[e];
+        }
+        store8_tail<TW>(wp, e0, count, vec, wv);
+        if (UPDATE && vote_out) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e0 + e < count) vote_out[e0 + e] = (int8_t)vv[e];
+        }
+      }
+    }
+    __syncthreads();   // the masks are rewritten by the next tile
+  }
+}
+
+// Vote over M <= 64 workers from int8 signs, 8 entries per thread: the
+// integer sum of the workers' bytes, as the SUM all-reduce of the int8
+// variant would deliver it; V = sign(sum), 0 on ties.  UPDATE: W <- rnd_W(
+// fp32(W) - lr V) in place (and the vote to vote_out); otherwise V itself is
+// written as TW.  sg is the matrix's first worker's signs, the M workers
+// `stride` bytes apart; threads first, first + step, ... of the matrix's
+// 8-entry groups.
 template <int ENC, typename TW, bool UPDATE>
 __device__ __forceinline__ void vote_body(const void* sg, int M, int64_t stride, int64_t count,
                                           TW* wp, float lr, int8_t* vote_out, bool vec,
@@ -345,33 +448,15 @@ __device__ __forceinline__ void vote_body(const void* sg, int M, int64_t stride,
   for (int64_t i = first; i < n8; i += step) {
     const int64_t e0 = 8 * i;
     int sum[8];
-    // workers 8 at a time, all 8 loads issued before their sums (a plain
-    // loop over M would wait for each worker's load in turn)
-    if constexpr (ENC == 0) {
-      const uint8_t* bb = reinterpret_cast<const uint8_t*>(sg);
-      const int64_t stride_bytes = stride * 8;
-      uint32_t lo = 0, hi = 0;
-      for (int k0 = 0; k0 < M; k0 += 8) {
-        uint32_t by[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          by[q] = k0 + q < M ? (uint32_t)bb[(int64_t)(k0 + q) * stride_bytes + i] : 0u;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          lo += ((by[q] & 15u) * 0x00204081u) & 0x01010101u;
-          hi += ((by[q] >> 4) * 0x00204081u) & 0x01010101u;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sum[e] = M - 2 * (int)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
-    } else {
+    static_assert(ENC == 1, "the packed-bit vote runs in vote_bits_tiles");
+    {
       const int8_t* sb = static_cast<const int8_t*>(sg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum[e] = 0;
       const bool full = e0 + 8 <= count && (stride & 7) == 0 &&
                         (reinterpret_cast<uintptr_t>(sb + e0) & 7u) == 0;
       if (full) {
+        // workers 8 at a time, all 8 loads issued before their sums
         for (int k0 = 0; k0 < M; k0 += 8) {
           uint64_t wd[8];
 #pragma unroll
@@ -422,9 +507,16 @@ __global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int
   const void* sg = ENC == 0
       ? static_cast<const void*>(static_cast<const uint64_t*>(signs) + j * mat_stride)
       : static_cast<const void*>(static_cast<const int8_t*>(signs) + j * mat_stride);
-  vote_body<ENC, TW, UPDATE>(sg, M, stride, count, (TW*)w.p[j], lr, vote_out, vec,
-                             (int64_t)blockIdx.x * kThreads + threadIdx.x,
-                             (int64_t)gridDim.x * kThreads);
+  if constexpr (ENC == 0) {
+    __shared__ uint64_t pos_s[kThreads], neg_s[kThreads];
+    vote_bits_tiles<TW, UPDATE>(static_cast<const uint64_t*>(sg), M, stride, count,
+                                (TW*)w.p[j], lr, vote_out, vec, blockIdx.x, gridDim.x, pos_s,
+                                neg_s);
+  } else {
+    vote_body<ENC, TW, UPDATE>(sg, M, stride, count, (TW*)w.p[j], lr, vote_out, vec,
+                               (int64_t)blockIdx.x * kThreads + threadIdx.x,
+                               (int64_t)gridDim.x * kThreads);
+  }
 }
 
 // The vote + update of matrices of different shapes in one launch (one
@@ -432,9 +524,16 @@ __global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int
 template <int ENC, typename TW>
 __global__ __launch_bounds__(kThreads) void k_vote_tbl(VoteTbl t, int M, float lr) {
   const VoteMat& v = t.m[blockIdx.y];
-  vote_body<ENC, TW, true>(v.signs, M, v.stride, v.count, static_cast<TW*>(v.w), lr, nullptr,
-                           (v.count % 8) == 0, (int64_t)blockIdx.x * kThreads + threadIdx.x,
-                           (int64_t)gridDim.x * kThreads);
+  if constexpr (ENC == 0) {
+    __shared__ uint64_t pos_s[kThreads], neg_s[kThreads];
+    vote_bits_tiles<TW, true>(static_cast<const uint64_t*>(v.signs), M, v.stride, v.count,
+                              static_cast<TW*>(v.w), lr, nullptr, (v.count % 8) == 0, blockIdx.x,
+                              gridDim.x, pos_s, neg_s);
+  } else {
+    vote_body<ENC, TW, true>(v.signs, M, v.stride, v.count, static_cast<TW*>(v.w), lr, nullptr,
+                             (v.count % 8) == 0, (int64_t)blockIdx.x * kThreads + threadIdx.x,
+                             (int64_t)gridDim.x * kThreads);
+  }
 }
 
 template <typename TD, typename TW>
@@ -518,6 +617,87 @@ __global__ void k_cache_decide(const float* resid, int parts, int nprob, int r,
 }
 
 
+// *out = 1 iff some flag of the sets is 1 (one block; __syncthreads_or
+// combines the threads).
+__global__ __launch_bounds__(kThreads) void k_any_flags(FlagSets fs, int32_t* out) {
+  int v = 0;
+  for (int a = 0; a < fs.count; ++a)
+    for (int i = threadIdx.x; i < fs.n[a]; i += kThreads) v |= fs.f[a][i] == 1;
+  v = __syncthreads_or(v);
+  if (threadIdx.x == 0) *out = v ? 1 : 0;
+}
+
+// The cached Q of every refreshed problem as a whole float32 r x r matrix,
+// from the bf16 matrix stored as its 256 x 256 tiles on and below the
+// diagonal (entries above come from the mirror tiles).  One 64 x 64 block of
+// the output per workgroup, staged through LDS so that a mirror block is
+// read along its stored rows and written transposed.
+__global__ __launch_bounds__(kThreads) void k_q_store(const bf16_t* src, int64_t sst, int r,
+                                                      PtrTbl q, int per, const int32_t* flags) {
+  const int b = blockIdx.y;
+  if (flags[b] != 1) return;
+  __shared__ float tile[64][65];
+  const int nb = (r + 63) / 64;
+  const int i0 = (blockIdx.x / nb) * 64, j0 = (blockIdx.x % nb) * 64;
+  const bool lower = (i0 >> 8) >= (j0 >> 8);
+  const bf16_t* sp = src + (int64_t)b * sst;
+  // source block: rows (lower ? i0 : j0) .., columns (lower ? j0 : i0) ..
+  const int sr0 = lower ? i0 : j0, sc0 = lower ? j0 : i0;
+  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+    const int a = e >> 6, c = e & 63;
+    const int row = sr0 + a, col = sc0 + c;
+    const float v = (row < r && col < r) ? bf2f(sp[(int64_t)row * r + col]) : 0.f;
+    if (lower) tile[a][c] = v; else tile[c][a] = v;
+  }
+  __syncthreads();
+  float* qp = reinterpret_cast<float*>(const_cast<char*>(
+      tbl_addr(q, b, per, (int64_t)r * r * (int64_t)sizeof(float))));
+  for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+    const int a = e >> 6, c = e & 63;
+    if (i0 + a < r && j0 + c < r) qp[(int64_t)(i0 + a) * r + (j0 + c)] = tile[a][c];
+  }
+}
+
+// Float32 cache -> bf16 matrix (round to nearest even), 8 entries per thread.
+__global__ __launch_bounds__(kThreads) void k_q_load(PtrTbl q, int per, int r, bf16_t* dst,
+                                                     int64_t dst_stride, const int32_t* flags) {
+  const int b = blockIdx.y;
+  if (flags[b] != 1) return;
+  const int64_t rr = (int64_t)r * r;
+  const float* src = reinterpret_cast<const float*>(tbl_addr(q, b, per, rr * 4));
+  bf16_t* d = dst + (int64_t)b * dst_stride;
+  for (int64_t e0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; e0 < rr;
+       e0 += (int64_t)gridDim.x * kThreads * 8) {
+    float v[8];
+    load8<float>(src + e0, v);
+    store8<bf16_t>(d + e0, v);
+  }
+}
+
+// Compacts the indices of the set flags, in increasing order: a block-wide
+// inclusive scan per 256 flags.
+__global__ __launch_bounds__(kThreads) void k_compact_flags(const int32_t* flags, int n,
+                                                            int32_t* dyn) {
+  __shared__ int scan[kThreads];
+  int base = 0;
+  for (int i0 = 0; i0 < n; i0 += kThreads) {
+    const int i = i0 + (int)threadIdx.x;
+    const int f = (i < n && flags[i] == 1) ? 1 : 0;
+    scan[threadIdx.x] = f;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = (int)threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (f) dyn[1 + base + scan[threadIdx.x] - 1] = i;
+    base += scan[kThreads - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dyn[0] = base;
+}
+
 inline int stream_blocks(int64_t count, int nprob) {
   // enough blocks in flight to fill 256 CUs several times over
   int64_t per = (count + kChunk - 1) / kChunk;
@@ -569,8 +749,7 @@ sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
                       hipStream_t s) {
   if (nprob <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
-  const bool signs = bits || s8;
-  dim3 grid(signs ? stream_blocks(count, nprob) : norm_parts(count), nprob);
+  dim3 grid(norm_parts(count), nprob);
   double bytes = (double)nprob * count * (2.0 * dt_size(mdt) + dt_size(gdt)) +
                  (bits ? (double)nprob * words * 8.0
                        : (s8 ? (double)nprob * count : (double)nprob * count * dt_size(xdt)));
@@ -642,7 +821,9 @@ sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t
   const bool vec = (count % 8) == 0;
   const int64_t n8 = (count + 7) / 8;
   int64_t want = (4096 + nmat - 1) / nmat;
-  int64_t need = (n8 + kThreads - 1) / kThreads;
+  // bits: one block iteration per tile of kThreads words; int8: of kThreads 8-entry groups
+  int64_t need = enc == SM_ENC_BITS ? ((count + 63) / 64 + kThreads - 1) / kThreads
+                                    : (n8 + kThreads - 1) / kThreads;
   dim3 grid((unsigned)(need < want ? need : want), nmat);
   const double sign_bytes = enc == SM_ENC_BITS ? M / 8.0 : (double)M;
   double bytes = (double)nmat * count *
@@ -685,7 +866,8 @@ sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt
     for (int q = 0; q < n; ++q) {
       t.m[q] = mats[q0 + q];
       const int64_t n8 = (t.m[q].count + 7) / 8;
-      need = std::max<int64_t>(need, (n8 + kThreads - 1) / kThreads);
+      const int64_t units = enc == SM_ENC_BITS ? (t.m[q].count + 63) / 64 : n8;
+      need = std::max<int64_t>(need, (units + kThreads - 1) / kThreads);
       bytes += (double)t.m[q].count * (sign_bytes + 2.0 * dt_size(wdt));
     }
     // about 64 blocks per CU in all: the matrices' sizes differ, and short
@@ -747,6 +929,50 @@ sm_status launch_gather_has_cache(const PtrTbl& cs, int per, int nprob, int32_t*
   prof_begin(SM_K_MISC, (double)nprob * 12.0, s);
   hipLaunchKernelGGL(k_gather_has_cache, dim3((nprob + 63) / 64), dim3(64), 0, s, cs, per,
                      nprob, hc);
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_any_flags(const FlagSets& fs, int32_t* out, hipStream_t s) {
+  if (fs.count <= 0) return SM_ERR_ARG;
+  double bytes = 4.0;
+  for (int a = 0; a < fs.count; ++a) bytes += 4.0 * fs.n[a];
+  prof_begin(SM_K_MISC, bytes, s);
+  hipLaunchKernelGGL(k_any_flags, dim3(1), dim3(kThreads), 0, s, fs, out);
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_q_store(const bf16_t* src, int64_t sst, int r, const PtrTbl& q, int per,
+                         const int32_t* flags, int batch, hipStream_t s) {
+  if (batch <= 0 || r <= 0) return SM_OK;
+  const int nb = (r + 63) / 64;
+  // read up to the lower-tile entries, write r^2 floats, per refreshed problem
+  prof_begin(SM_K_MISC, (double)batch * ((double)r * r * 2.0 + (double)r * r * 4.0), s);
+  hipLaunchKernelGGL(k_q_store, dim3(nb * nb, batch), dim3(kThreads), 0, s, src, sst, r, q, per,
+                     flags);
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_compact_flags(const int32_t* flags, int n, int32_t* dyn, hipStream_t s) {
+  if (n <= 0) return SM_ERR_ARG;
+  prof_begin(SM_K_MISC, 8.0 * n + 4.0, s);
+  hipLaunchKernelGGL(k_compact_flags, dim3(1), dim3(kThreads), 0, s, flags, n, dyn);
+  prof_end(s);
+  return check_launch();
+}
+
+sm_status launch_q_load(const PtrTbl& q, int per, int r, bf16_t* dst, int64_t dst_stride,
+                        const int32_t* flags, int batch, hipStream_t s) {
+  if (batch <= 0 || r <= 0) return SM_OK;
+  if (r % 8 || dst_stride % 8) return SM_ERR_UNSUPPORTED;
+  const int64_t n8 = (int64_t)r * r / 8;
+  int64_t want = (2048 + batch - 1) / batch;
+  const int64_t need = (n8 + kThreads - 1) / kThreads;
+  dim3 grid((unsigned)(need < want ? need : want), batch);
+  prof_begin(SM_K_MISC, (double)batch * (double)r * r * 6.0, s);
+  hipLaunchKernelGGL(k_q_load, grid, dim3(kThreads), 0, s, q, per, r, dst, dst_stride, flags);
   prof_end(s);
   return check_launch();
 }

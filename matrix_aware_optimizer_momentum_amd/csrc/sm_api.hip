@@ -253,7 +253,8 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, bool last,
 // Launches one product kind for all jobs, groups ordered by decreasing K so
 // that concurrent tiles carry similar work, as few launches as the group
 // and table limits allow.
-sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
+sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s,
+                           const int32_t* gate = nullptr, const int32_t* dyn = nullptr) {
   std::stable_sort(gs.begin(), gs.end(),
                    [](const NsgGroup& x, const NsgGroup& y) { return x.K > y.K; });
   size_t i = 0;
@@ -262,7 +263,7 @@ sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s) {
     while (i + ng < gs.size() && ng < kNsgMaxGroups &&
            ns_group_tables(gs.data() + i, ng + 1) <= kNsgMaxTables)
       ++ng;
-    SM_TRY(launch_gemm_ns(gs.data() + i, ng, kind, s));
+    SM_TRY(launch_gemm_ns(gs.data() + i, ng, kind, s, gate, dyn));
     i += ng;
   }
   return SM_OK;
@@ -300,6 +301,7 @@ struct GfPlan {
   // Q[k] = Q_{k+1} (k >= 1); unused entries have batch 0
   std::vector<NsgGroup> T, S, Q;
   GfSlot fill_src, fill_dst;   // Q_1 = S_0 + aI (fill_src.p null: no fill)
+  GfSlot qk;                   // where Q_K ends up (lower-stored when gram.c_low)
   int r, batch, tiles;   // tiles: 256 x 256 tiles of one r x r product
   float a;
 };
@@ -312,6 +314,7 @@ NsgGroup ns_subrange(const NsgGroup& g, int p0, int n) {
   h.c = g.c + (int64_t)p0 * g.sc;
   if (g.scale) h.scale = g.scale + p0;
   if (g.bits) h.bits = g.bits + (int64_t)p0 * g.bits_stride;
+  if (g.pred) h.pred = g.pred + p0;
   h.batch = n;
   return h;
 }
@@ -327,14 +330,15 @@ int64_t ns_tile_work(int r, int cols, int K, bool gram_form) {
 }
 
 // Takes job j in the Gram form if that form's MFMA work is below the direct
-// form's.  The choice depends on the job alone (not on the other jobs of the
-// call), so a matrix gets the same result from a step as from sm_ns_polar.
-bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
+// form's (always with `force`: CacheMuon needs Q_K).  The choice depends on
+// the job alone (not on the other jobs of the call), so a matrix gets the
+// same result from a step as from sm_ns_polar.
+bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g, bool force = false) {
   const int K = p.iters;
   if (p.c != 0.f || K < 2) return false;
   const bool wide = j.m <= j.n;
   const int m = j.m, n = j.n, r = wide ? m : n, cols = wide ? n : m;
-  if (ns_tile_work(r, cols, K, true) >= ns_tile_work(r, cols, K, false)) return false;
+  if (!force && ns_tile_work(r, cols, K, true) >= ns_tile_work(r, cols, K, false)) return false;
   const int64_t mn = (int64_t)m * n, rr = (int64_t)r * r;
   auto bp = [](const void* q) { return static_cast<const bf16_t*>(q); };
   auto mp = [](void* q) { return static_cast<bf16_t*>(q); };
@@ -404,6 +408,7 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g) {
   std::memset(&g.apply, 0, sizeof(g.apply));
   NsgGroup& a = g.apply;
   const GfSlot& qk = slot[qi];
+  g.qk = qk;
   a.tbl = j.xtbl; a.tbl_per = j.xper;
   if (wide) {   // X_K = Q_K x
     a.a = qk.p; a.lda = r; a.sa = qk.st; a.a_low = low;
@@ -790,22 +795,66 @@ struct GramWs {
   float* t;       // [batch][r*r]  P_k G_k
   float* bq;      // [batch][r*r]  b G + c G^2 (quintic)
   float* qt;      // [batch][r*r]  Q ping-pong partner of the cache
+  NsWs ns;        // bf16 Gram-form slots over the same bytes as ga .. qt
   float* resid;   // [batch][tiles]
   int32_t* hc;    // [batch] has_cache snapshot
   int32_t* flags; // [batch] refresh decision
+  int32_t* any;   // 1 iff some problem refreshes
+  int32_t* any_hc;  // 1 iff some problem has a cache
+  int32_t* dyn;   // [1 + batch] the refreshed problems: count, then indices
 };
 
+// The five float32 r x r buffers of the generic solve are one region; the
+// bf16 Gram-form solve (five r x r bf16 slots per problem: NsWs amat, amat2
+// and the three-slot tmp) uses its first half.
 void carve_gram(Carver& cv, int batch, int m, int n, GramWs& w) {
   const int64_t r = m < n ? m : n;
   const size_t rr = (size_t)batch * r * r * 4;
-  w.ga = cv.take<float>(rr);
-  w.gb = cv.take<float>(rr);
-  w.t = cv.take<float>(rr);
-  w.bq = cv.take<float>(rr);
-  w.qt = cv.take<float>(rr);
+  char* region = cv.take<char>(5 * rr);
+  w.ga = reinterpret_cast<float*>(region);
+  w.gb = reinterpret_cast<float*>(region + rr);
+  w.t = reinterpret_cast<float*>(region + 2 * rr);
+  w.bq = reinterpret_cast<float*>(region + 3 * rr);
+  w.qt = reinterpret_cast<float*>(region + 4 * rr);
+  w.ns.amat = region;                 // [batch][r*r] bf16
+  w.ns.amat2 = region + rr / 2;       // [batch][r*r] bf16
+  w.ns.tmp = region + rr;             // [batch][3 r*r] bf16
   w.resid = cv.take<float>((size_t)batch * gemm_tiles(0, (int)r, (int)r) * 4);
   w.hc = cv.take<int32_t>((size_t)batch * 4);
   w.flags = cv.take<int32_t>((size_t)batch * 4);
+  w.any = cv.take<int32_t>(4);
+  w.any_hc = cv.take<int32_t>(4);
+  w.dyn = cv.take<int32_t>((size_t)(batch + 1) * 4);
+}
+
+// The fresh solve of CacheMuon in the Gram form on the persistent MFMA
+// kernels (bf16 operands, cubic coefficients): the same chain as the
+// Newton-Schulz Gram form (S_k = b G_k, P_k = S_k + aI, so G_{k+1} = P_k G_k
+// P_k and Q_{k+1} = P_k Q_k are the products T_k = S_k P_k, S_{k+1} = T_k P_k,
+// Q_{k+1} = Q_k P_k).  Every launch runs only the refreshed problems, listed
+// on the device (dyn, from the decision flags), and nothing when there are
+// none (gate `any`); Q_K goes to their caches as whole float32 matrices.
+sm_status gram_fresh_gf(const GfPlan& g, const int32_t* flags, const int32_t* any,
+                        int32_t* dyn, const PtrTbl& qtbl, int qper, hipStream_t s) {
+  const int K = (int)g.T.size();
+  SM_TRY(launch_compact_flags(flags, g.batch, dyn, s));
+  std::vector<NsgGroup> v{g.gram};
+  SM_TRY(launch_ns_groups(v, SM_K_GEMM_GRAM, s, any, dyn));
+  if (g.fill_src.p)
+    SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st, g.r,
+                               g.batch, g.a, g.gram.c_low != 0, s));
+  for (int k = 0; k < K; ++k) {
+    std::vector<NsgGroup> l1, l2;             // {T_k, Q_{k+1}}, then {S_{k+1}}
+    if (g.T[k].batch) l1.push_back(g.T[k]);
+    if (g.Q[k].batch) l1.push_back(g.Q[k]);
+    if (g.S[k].batch) l2.push_back(g.S[k]);
+    if (!l1.empty()) SM_TRY(launch_ns_groups(l1, SM_K_GEMM_RR, s, any, dyn));
+    if (!l2.empty()) SM_TRY(launch_ns_groups(l2, SM_K_GEMM_RR, s, any, dyn));
+  }
+  v = {g.apply};
+  SM_TRY(launch_ns_groups(v, SM_K_GEMM_APPLY, s, any, dyn));
+  if (!g.gram.c_low) return SM_ERR_UNSUPPORTED;   // q_store reads the lower-stored Q_K
+  return launch_q_store(g.qk.p, g.qk.st, g.r, qtbl, qper, flags, g.batch, s);
 }
 
 // One CacheMuon orthogonalisation per problem, [CacheMuon-ja] core mechanism:
@@ -829,7 +878,64 @@ sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cs
   const bool quintic = p.c != 0.f;
 
   SM_TRY(launch_gather_has_cache(cstbl, qper, batch, w.hc, s));
-  if (mode != 1) {
+  // bf16 and cubic with a one-term identity: the candidate, its probe and
+  // the fresh solve run on the persistent MFMA kernels when they take the
+  // shapes (the fresh solve as the lower-stored Gram-form chain)
+  GfPlan gf;
+  bool fast = false;
+  if (dt == BF16 && !quintic && K >= 2) {
+    uint32_t hi = 0, lo = 0;
+    const NsJob job{x, d, w.ns, scale, batch, m, n};
+    fast = ns_ident_split(p.a, &hi, &lo) == 1 && gf_plan(job, p, gf, true) && gf.gram.c_low;
+  }
+  auto any_of = [&](const int32_t* flags, int32_t* out) {
+    FlagSets fs;
+    std::memset(&fs, 0, sizeof(fs));
+    fs.f[0] = flags;
+    fs.n[0] = batch;
+    fs.count = 1;
+    return launch_any_flags(fs, out, s);
+  };
+  int parts = gemm_tiles(dt, r, r);
+  if (fast && mode != 1) {
+    // candidate D_hat = s Q x (x Q^T when tall) with Q rounded to bf16 (the
+    // operand type the generic kernel would round it to), then the residual
+    // partials of D_hat D_hat^T - I; problems without a cache skip both
+    SM_TRY(any_of(w.hc, w.any_hc));
+    bf16_t* qb = static_cast<bf16_t*>(w.ns.amat);
+    SM_TRY(launch_q_load(qtbl, qper, r, qb, rr, w.hc, batch, s));
+    const int64_t mn = (int64_t)m * n;
+    NsgGroup ap;
+    std::memset(&ap, 0, sizeof(ap));
+    if (wide) {
+      ap.a = qb; ap.lda = r; ap.sa = rr;
+      ap.b = static_cast<const bf16_t*>(x); ap.ldb = n; ap.sb = mn; ap.b_kr = 1;
+    } else {
+      ap.a = static_cast<const bf16_t*>(x); ap.lda = n; ap.sa = mn;
+      ap.b = qb; ap.ldb = r; ap.sb = rr;
+    }
+    ap.c = static_cast<bf16_t*>(d); ap.ldc = n; ap.sc = mn;
+    ap.scale = scale; ap.alpha_pow = scale ? 1 : 0; ap.alpha = 1.f;
+    ap.M = m; ap.N = n; ap.K = r; ap.batch = batch;
+    ap.pred = w.hc;
+    NsgGroup pr;
+    std::memset(&pr, 0, sizeof(pr));
+    pr.a = static_cast<const bf16_t*>(d); pr.lda = n; pr.sa = mn; pr.a_kr = wide ? 0 : 1;
+    pr.b = static_cast<const bf16_t*>(d); pr.ldb = n; pr.sb = mn; pr.b_kr = wide ? 0 : 1;
+    pr.alpha = 1.f;
+    pr.M = r; pr.N = r; pr.K = wide ? n : m; pr.batch = batch; pr.sym = 1;
+    pr.resid = w.resid;
+    if (gemm_ns_supported(ap) && gemm_ns_supported(pr)) {
+      std::vector<NsgGroup> v{ap};
+      SM_TRY(launch_ns_groups(v, SM_K_GEMM_APPLY, s, w.any_hc));
+      v = {pr};
+      SM_TRY(launch_ns_groups(v, SM_K_PROBE, s, w.any_hc));
+      parts = ns_probe_parts(r);
+    } else {
+      fast = false;
+    }
+  }
+  if (!fast && mode != 1) {
     // candidate D_hat = s * Q x  (x^T oriented: s * x Q^T for a tall x)
     GemmArgs g = apply_args(qtbl.p[0], F32, 1, x, dt, batch, m, n);
     g.tbl = qtbl; g.tbl_per = qper;
@@ -843,8 +949,12 @@ sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cs
     pr.pred = w.hc; pr.pred_stride = 1; pr.pred_val = 1;
     SM_TRY(launch_gemm(pr, dt, SM_K_PROBE, s));
   }
-  SM_TRY(launch_cache_decide(w.resid, gemm_tiles(dt, r, r), batch, r, w.hc, cstbl, qper, mode,
-                             gamma, t, w.flags, err_out, refr_out, diag, s));
+  SM_TRY(launch_cache_decide(w.resid, parts, batch, r, w.hc, cstbl, qper, mode, gamma, t,
+                             w.flags, err_out, refr_out, diag, s));
+  if (fast) {
+    SM_TRY(any_of(w.flags, w.any));
+    return gram_fresh_gf(gf, w.flags, w.any, w.dyn, qtbl, qper, s);
+  }
 
   // Q_k lives in the cache for k == K (mod 2) so that Q_K lands there.
   auto qbuf_is_cache = [&](int k) { return ((K - k) % 2) == 0; };

@@ -260,6 +260,26 @@ sm_status launch_cache_decide(const float* resid_partials, int parts, int nprob,
                               float gamma, int64_t t, int32_t* flags, float* err,
                               int32_t* refreshed, const PtrTbl* diag, hipStream_t s);
 
+// Flag arrays of up to kTbl sets of problems (f[a] holds n[a] int32 flags).
+struct FlagSets {
+  const int32_t* f[kTbl];
+  int n[kTbl];
+  int count;
+};
+// *out = 1 iff some flag is 1, else 0 (device int32).
+sm_status launch_any_flags(const FlagSets& fs, int32_t* out, hipStream_t s);
+
+// Writes the cache of each problem b with flags[b] == 1: the r x r bf16
+// matrix src + b*sst, stored as its 256 x 256 tiles on and below the
+// diagonal, as a whole float32 matrix at tbl_addr(q, b, per, 4 r^2).
+sm_status launch_q_store(const bf16_t* src, int64_t sst, int r, const PtrTbl& q, int per,
+                         const int32_t* flags, int batch, hipStream_t s);
+// The cache of each problem b with flags[b] == 1 (float32 r x r at
+// tbl_addr(q, b, per, 4 r^2)) rounded to bf16 into dst + b*dst_stride;
+// needs r % 8 == 0.
+sm_status launch_q_load(const PtrTbl& q, int per, int r, bf16_t* dst, int64_t dst_stride,
+                        const int32_t* flags, int batch, hipStream_t s);
+
 // ---------------------------------------------------------------- batched MFMA GEMM
 
 enum Layout : int {
@@ -350,7 +370,22 @@ struct NsgGroup {
   // (bit = 1 <=> negative, bit j of word w <=> row-major entry 64 w + j) to
   // bits + problem * bits_stride words; needs N % 64 == 0.
   uint64_t* bits; int64_t bits_stride;
+  // Optional per-problem store predicate (device int32 per problem): a
+  // problem whose flag is not 1 computes its tiles but stores nothing.
+  const int32_t* pred;
+  // Probe (kind SM_K_PROBE, symmetric, no identity): instead of C, each
+  // wave writes the residual partial sum over its 128 x 128 part of the
+  // tile of (alpha * value - [row == col])^2 (doubled below the diagonal,
+  // whose mirror is not computed) to resid + problem * 4 * lower tiles +
+  // 4 * (tm (tm + 1) / 2 + tn) + wave.
+  float* resid;
 };
+
+// Residual partials per problem that a probe launch writes (4 per lower tile).
+inline int ns_probe_parts(int r) {
+  const int t = (r + 255) / 256;
+  return 4 * (t * (t + 1) / 2);
+}
 
 bool gemm_ns_supported(const NsgGroup& g);
 // Splits a into bf16 terms hi (+ lo); returns the number of terms whose sum
@@ -362,7 +397,16 @@ int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
 // SM_K_GEMM_APPLY runs the apply kernel (applies only).  Returns
 // SM_ERR_UNSUPPORTED for other groups or more than kNsgMaxTables distinct
 // tables.
-sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s);
+// gate (optional device int32): when it holds 0 at launch time the whole
+// launch does nothing (the fresh solve of a CacheMuon step that refreshes
+// no problem).  dyn (optional device int32 [1 + batch]): only the dyn[0]
+// problems dyn[1 ..] run (every group must have the same batch and no
+// pointer tables); the others are neither computed nor stored.
+sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s,
+                         const int32_t* gate = nullptr, const int32_t* dyn = nullptr);
+// dyn[0] = the number of problems b < n with flags[b] == 1, dyn[1 ..] = those
+// b in increasing order (one workgroup).
+sm_status launch_compact_flags(const int32_t* flags, int n, int32_t* dyn, hipStream_t s);
 // Distinct pointer tables among the groups.
 int ns_group_tables(const NsgGroup* groups, int ngroups);
 // Workgroups one NS GEMM launch runs at most (one per CU of the device).

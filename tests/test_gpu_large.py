@@ -99,12 +99,16 @@ def test_cache_muon_gpt2_large_shapes(gpu_lib, shape):
     assert rel_fro(d4, d4_or.T if tr else d4_or) <= TOL_BF16
 
 
-def test_predicated_fresh_solve_credits_no_work(gpu_lib):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_predicated_fresh_solve_credits_no_work(gpu_lib, dt):
     """Kernel-time accounting: a fresh solve skipped on the device (forced
-    reuse) is credited with no GEMM work; a forced fresh solve with all of it."""
+    reuse) is credited with no GEMM work; a forced fresh solve with all of
+    it.  bf16 runs the Gram-form chain on the persistent kernels (gated
+    launches; a symmetric product is credited with the half it computes),
+    float32 the generic kernel (per-problem predicates, full products)."""
     m, n, batch = 256, 768, 3
     rng = np.random.default_rng(5)
-    x = to_gpu((1e-2 * rng.standard_normal((batch, m, n))).astype(np.float32), "bf16")
+    x = to_gpu((1e-2 * rng.standard_normal((batch, m, n))).astype(np.float32), dt)
     q = torch.zeros(batch, m, m, dtype=torch.float32, device="cuda")
     cs = torch.zeros(batch, 2, dtype=torch.int32, device="cuda")
     sm.gram_ns_cached(x, q, cs, 1, 2.0, mode=sm.MODE_FORCE_FRESH)
@@ -121,15 +125,16 @@ def test_predicated_fresh_solve_credits_no_work(gpu_lib):
         finally:
             sm.profile_enable(False)
     K = 5
+    sym = 1.0 if dt == "bf16" else 2.0
     reuse, fresh = work[sm.MODE_FORCE_REUSE], work[sm.MODE_FORCE_FRESH]
     # forced reuse: the candidate (apply) and its probe ran, nothing of the solve
     assert reuse["gemm_gram"][2] == 0.0 and reuse["gemm_rr"][2] == 0.0
     assert reuse["gemm_apply"][2] == batch * 2.0 * m * m * n
-    assert reuse["probe"][2] == batch * 2.0 * m * m * n
+    assert reuse["probe"][2] == batch * sym * m * m * n
     # forced fresh: no candidate, the whole solve
     assert fresh["probe"][2] == 0.0
-    assert fresh["gemm_gram"][2] == batch * 2.0 * m * m * n
-    assert fresh["gemm_rr"][2] == batch * 3 * (K - 1) * 2.0 * m ** 3
+    assert fresh["gemm_gram"][2] == batch * sym * m * m * n
+    assert fresh["gemm_rr"][2] == batch * 3 * (K - 1) * sym * m ** 3
     assert fresh["gemm_apply"][2] == batch * 2.0 * m * m * n
 
 
