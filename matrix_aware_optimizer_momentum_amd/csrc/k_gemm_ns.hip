@@ -18,7 +18,9 @@
 // Work split.  The grid is one workgroup per CU (or fewer), walking the flat
 // list of 256 x 256 output tiles in rounds of gridDim tiles, in alternating
 // direction (snake); workgroups of one XCD take consecutive tiles so that
-// they share that XCD's L2.  Groups are ordered by the caller (largest K
+// they share that XCD's L2, and within a problem the tiles go in bands of
+// four tile rows, column by column (ns_tiles.hpp), so that those tiles share
+// few operand panels.  Groups are ordered by the caller (largest K
 // first), so concurrent tiles have similar work and the snake evens out the
 // rest.
 //
@@ -54,6 +56,9 @@
 // form's products A (B + aI) use the same fold, and (A + aI)(B + aI) folds
 // the identity on both sides (plus a^2 where the two groups meet).
 #include "sm_internal.hpp"
+
+#define SM_HD __host__ __device__
+#include "ns_tiles.hpp"
 
 namespace sm {
 namespace nsg {
@@ -170,19 +175,7 @@ __device__ __forceinline__ Tile decode_tile(const Args& A, int t, int cnt) {
   const int pc = local / g.tiles_per_prob;
   r.prob = cnt < 0 ? pc : sload_i32(A.dyn + 1 + pc);
   const int u = local - pc * g.tiles_per_prob;
-  if (g.sym) {  // lower triangle, row-major: u = tm (tm + 1) / 2 + tn
-    int tm = (int)((sqrtf(8.f * u + 1.f) - 1.f) * 0.5f);
-    while ((tm + 1) * (tm + 2) / 2 <= u) ++tm;
-    while (tm * (tm + 1) / 2 > u) --tm;
-    r.tm = tm;
-    r.tn = u - tm * (tm + 1) / 2;
-  } else if (g.tiles_m <= 4) {  // few row tiles: consecutive tiles share B's rows
-    r.tn = u / g.tiles_m;
-    r.tm = u - r.tn * g.tiles_m;
-  } else {
-    r.tm = u / g.tiles_n;
-    r.tn = u - r.tm * g.tiles_n;
-  }
+  ns_tile_coords(u, g.tiles_m, g.tiles_n, g.sym, &r.tm, &r.tn);   // banded walk
   return r;
 }
 
@@ -897,8 +890,13 @@ __device__ __forceinline__ void epilogue_resid(const f32x16 (&acc)[4][4], float*
           part = __fmaf_rn(d, d, part);
         }
       }
+  // butterfly over the wave; the lane id comes from fresh_tid (a shuffle
+  // builtin would derive its own, which the compiler hoists and spills)
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) part = __fadd_rn(part, __shfl_xor(part, o, 64));
+  for (int o = 32; o > 0; o >>= 1) {
+    const int other = __builtin_amdgcn_ds_bpermute((lane ^ o) << 2, __float_as_int(part));
+    part = __fadd_rn(part, __int_as_float(other));
+  }
   if (lane == 0) *out = __fmul_rn(weight, part);
   wait_vm<0>();
 }

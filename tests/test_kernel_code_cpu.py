@@ -38,14 +38,14 @@ def gemm_ns_asm(tmp_path_factory):
     for m in re.finditer(r"^(_ZN2sm3nsg9k_gemm_nsILi(\d)EEEvNS0_4ArgsE):[^\n]*\n(.*?)^\s*s_endpgm",
                          text, re.S | re.M):
         kernels[int(m.group(2))] = m.group(3)
-    assert set(kernels) == {0, 1}, sorted(kernels)
+    assert set(kernels) == {0, 1, 2}, sorted(kernels)
     return text, kernels
 
 
 def test_gemm_ns_kernels_use_no_scratch(gemm_ns_asm):
     text, _ = gemm_ns_asm
     sizes = re.findall(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)
-    assert len(sizes) >= 2
+    assert len(sizes) >= 3
     assert all(int(v) == 0 for v in sizes), sizes
 
 
@@ -65,7 +65,7 @@ def masked_mfmas_without_skip(body: str):
     return bad
 
 
-@pytest.mark.parametrize("role", [0, 1], ids=["symmetric", "apply"])
+@pytest.mark.parametrize("role", [0, 1, 2], ids=["symmetric", "apply", "probe"])
 def test_no_mfma_under_a_lane_mask_without_skip(gemm_ns_asm, role):
     _, kernels = gemm_ns_asm
     bad = masked_mfmas_without_skip(kernels[role])
@@ -85,3 +85,39 @@ def test_scan_finds_a_masked_mfma():
     ])
     bad = masked_mfmas_without_skip(body)
     assert [n for n, _ in bad] == [1]
+
+
+def test_tile_walk_is_a_bijection(tmp_path):
+    """The banded walk of a problem's 256 x 256 tiles (ns_tiles.hpp) visits
+    every tile of the rectangle, or of the lower triangle, exactly once."""
+    src = tmp_path / "walk.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include <set>
+#include <utility>
+#include "ns_tiles.hpp"
+int main() {
+  int bad = 0;
+  for (int sym = 0; sym < 2; ++sym)
+    for (int tm = 1; tm <= 45; ++tm)
+      for (int tn = 1; tn <= 45; ++tn) {
+        if (sym && tn != tm) continue;
+        const int total = sym ? tm * (tm + 1) / 2 : tm * tn;
+        std::set<std::pair<int, int>> seen;
+        for (int u = 0; u < total; ++u) {
+          int a = -1, b = -1;
+          sm::ns_tile_coords(u, tm, tn, sym, &a, &b);
+          if (a < 0 || a >= tm || b < 0 || b >= tn || (sym && b > a)) ++bad;
+          seen.insert({a, b});
+        }
+        if ((int)seen.size() != total) ++bad;
+      }
+  std::printf("%d\n", bad);
+  return bad != 0;
+}
+''')
+    exe = tmp_path / "walk"
+    subprocess.run(["g++", "-std=c++17", f"-I{build_lib.CSRC}", str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "0", out.stdout
