@@ -1,7 +1,13 @@
-// Batched MFMA GEMM for gfx950 (CDNA4), shared by the Newton-Schulz and
-// Gram Newton-Schulz products.
+// Batched, grouped MFMA GEMM for gfx950 (CDNA4), shared by the Newton-Schulz
+// and Gram Newton-Schulz products that the persistent bf16 NS kernel does not
+// take (float32 NS, CacheMuon's generic solve, edge layouts).
 //
 //   C[b] = alpha_b * A[b] * B[b] + beta_b * Cin[b] + diag * I     (M x N, K)
+//
+// One launch runs up to kGemmMaxGroups product sets of possibly different
+// shapes (one block per 128 x 128 output tile per problem, the sets' blocks
+// laid end to end in a 1-D grid), so the products of every matrix shape of a
+// step share a launch and fill the chip together.
 //
 // Block tile 128 x 128, 256 threads = 4 waves in a 2 x 2 arrangement, each
 // wave owning a 64 x 64 sub-tile as 2 x 2 blocks of 32 x 32 MFMA outputs.
@@ -12,6 +18,10 @@
 // way into LDS.  Interior tiles with aligned leading dimensions take the
 // vector path, edge tiles load element by element with zero fill, so any
 // M, N, K >= 1 is handled.
+//
+// Pipelining: two LDS stages.  The global loads of k-slab t+1 are issued into
+// registers before the MFMAs of slab t, and written to the other LDS stage
+// after them, so their latency hides behind the MFMAs; one barrier per slab.
 //
 // MFMA lane layout relied on (32 x 32 output blocks): for the A operand lane
 // l supplies row l % 32, for the B operand column l % 32, each with a group
@@ -31,6 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BM = 128;
 constexpr int BN = 128;
 constexpr int NT = 256;
+constexpr int kGemmMaxGroups = 8;
 
 template <typename TM> struct Cfg;
 template <> struct Cfg<bf16_t> {
@@ -56,207 +67,270 @@ template <> struct Conv<bf16_t, float> {
   __device__ __forceinline__ static float cv(bf16_t v) { return bf2f(v); }
 };
 
-__device__ __forceinline__ uint32_t pack_bf2(bf16_t lo, bf16_t hi) {
-  return (uint32_t)lo | ((uint32_t)hi << 16);
-}
+// ------------------------------------------------------------ staging
+// A stage is split in two: load() issues the global loads of one k-slab of
+// the tile into registers (raw HBM type), store() converts them to the MFMA
+// type and writes them to an LDS stage.  Between the two the loads are in
+// flight.
 
-// ------------------------------------------------------------ staging: KC operand
-// Tile rows [r0, r0+128), k in [k0, k0+BK) of an operand stored row-major with
-// k contiguous: element (r, k) at base[r*ld + k].
-template <typename TG, typename TM>
-__device__ __forceinline__ void stage_kc(const TG* __restrict__ base, int64_t ld, int r0,
-                                         int rows, int k0, int K, bool fast, TM* S) {
-  constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
-  constexpr int VEC = 16 / sizeof(TM);          // elements per 16-byte LDS write
-  constexpr int VPR = BK / VEC;                 // vectors per row (4)
-  constexpr int NV = (BM * VPR) / NT;           // vectors per thread (2)
+template <typename TG, typename TM, int LAY> struct Stage;
+
+// KC operand: tile rows [r0, r0+128), k in [k0, k0+BK), element (r, k) at
+// base[r*ld + k].  Each thread moves NV vectors of VEC consecutive k.
+template <typename TG, typename TM> struct Stage<TG, TM, KC> {
+  static constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
+  static constexpr int VEC = 16 / sizeof(TM);   // elements per 16-byte LDS write
+  static constexpr int VPR = BK / VEC;          // vectors per row (4)
+  static constexpr int NV = (BM * VPR) / NT;    // vectors per thread (2)
+  static_assert((VEC * sizeof(TG)) % 16 == 0, "whole 16-byte global loads");
+  __attribute__((aligned(16))) TG raw[NV][VEC];
+
+  __device__ __forceinline__ void load(const TG* __restrict__ base, int64_t ld, int r0,
+                                       int rows, int k0, int K, bool fast) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = threadIdx.x + NT * i;
-    const int row = v / VPR;
-    const int kv = (v % VPR) * VEC;
-    TM* dst = S + row * LDK + kv;
+    for (int i = 0; i < NV; ++i) {
+      const int v = threadIdx.x + NT * i;
+      const int row = v / VPR;
+      const int kv = (v % VPR) * VEC;
+      if (fast) {
+        const uint4* src =
+            reinterpret_cast<const uint4*>(base + (int64_t)(r0 + row) * ld + (k0 + kv));
+        uint4* dst = reinterpret_cast<uint4*>(raw[i]);
+#pragma unroll
+        for (int q = 0; q < (int)(VEC * sizeof(TG) / 16); ++q) dst[q] = src[q];
+      } else {
+        const int r = r0 + row;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int k = k0 + kv + e;
+          raw[i][e] = (r < rows && k < K) ? base[(int64_t)r * ld + k] : (TG)0;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(TM* S) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = threadIdx.x + NT * i;
+      const int row = v / VPR;
+      const int kv = (v % VPR) * VEC;
+      __attribute__((aligned(16))) TM o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = Conv<TG, TM>::cv(raw[i][e]);
+      *reinterpret_cast<uint4*>(S + row * LDK + kv) = *reinterpret_cast<const uint4*>(o);
+    }
+  }
+};
+
+// RC operand: tile rows [r0, r0+128), k in [k0, k0+BK), element (r, k) at
+// base[k*ld + r].  Each thread loads KV consecutive k for 2 adjacent rows and
+// writes them as two [row][k] vectors.
+template <typename TG, typename TM> struct Stage<TG, TM, RC> {
+  static constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
+  static constexpr int KV = 16 / sizeof(TM);  // k per LDS vector: 8 (bf16) or 4 (f32)
+  static_assert((BK / KV) * (BM / 2) == NT, "one chunk per thread");
+  TG v0[KV], v1[KV];
+
+  __device__ __forceinline__ void load(const TG* __restrict__ base, int64_t ld, int r0,
+                                       int rows, int k0, int K, bool fast) {
+    const int rc = (threadIdx.x % (BM / 2)) * 2;
+    const int kc = (threadIdx.x / (BM / 2)) * KV;
     if (fast) {
-      const TG* src = base + (int64_t)(r0 + row) * ld + (k0 + kv);
-      if constexpr (sizeof(TG) == sizeof(TM)) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-      } else {  // float32 in HBM, bf16 in LDS: 8 floats -> 8 bf16
-        static_assert(sizeof(TG) == 4 && sizeof(TM) == 2, "f32 -> bf16 staging only");
-        float4 x0 = *reinterpret_cast<const float4*>(src);
-        float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-        uint4 o;
-        o.x = pack_bf2(f2bf(x0.x), f2bf(x0.y));
-        o.y = pack_bf2(f2bf(x0.z), f2bf(x0.w));
-        o.z = pack_bf2(f2bf(x1.x), f2bf(x1.y));
-        o.w = pack_bf2(f2bf(x1.z), f2bf(x1.w));
-        *reinterpret_cast<uint4*>(dst) = o;
+      const TG* src = base + (int64_t)(k0 + kc) * ld + (r0 + rc);
+#pragma unroll
+      for (int kk = 0; kk < KV; ++kk) {
+        const TG* p = src + (int64_t)kk * ld;
+        if constexpr (sizeof(TG) == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+          v0[kk] = (TG)(w & 0xFFFFu);
+          v1[kk] = (TG)(w >> 16);
+        } else {
+          const float2 w = *reinterpret_cast<const float2*>(p);
+          v0[kk] = w.x;
+          v1[kk] = w.y;
+        }
       }
     } else {
-      const int r = r0 + row;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int k = k0 + kv + e;
-        TG val = (TG)0;
-        if (r < rows && k < K) val = base[(int64_t)r * ld + k];
-        dst[e] = Conv<TG, TM>::cv(val);
+      for (int kk = 0; kk < KV; ++kk) {
+        const int k = k0 + kc + kk;
+        const int r = r0 + rc;
+        TG a = (TG)0, b = (TG)0;
+        if (k < K) {
+          if (r < rows) a = base[(int64_t)k * ld + r];
+          if (r + 1 < rows) b = base[(int64_t)k * ld + r + 1];
+        }
+        v0[kk] = a;
+        v1[kk] = b;
       }
     }
   }
-}
-
-// ------------------------------------------------------------ staging: RC operand
-// Tile rows [r0, r0+128), k in [k0, k0+BK) of an operand whose row index is
-// contiguous: element (r, k) at base[k*ld + r].  Each thread loads KV
-// consecutive k for 2 adjacent rows and writes them as two [row][k] vectors.
-template <typename TG, typename TM>
-__device__ __forceinline__ void stage_rc(const TG* __restrict__ base, int64_t ld, int r0,
-                                         int rows, int k0, int K, bool fast, TM* S) {
-  constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
-  constexpr int KV = 16 / sizeof(TM);  // k per LDS vector: 8 (bf16) or 4 (f32)
-  static_assert((BK / KV) * (BM / 2) == NT, "one chunk per thread");
-  const int rc = (threadIdx.x % (BM / 2)) * 2;
-  const int kc = (threadIdx.x / (BM / 2)) * KV;
-  __attribute__((aligned(16))) TM v0[KV];
-  __attribute__((aligned(16))) TM v1[KV];
-  if (fast) {
-    const TG* src = base + (int64_t)(k0 + kc) * ld + (r0 + rc);
+  __device__ __forceinline__ void store(TM* S) const {
+    const int rc = (threadIdx.x % (BM / 2)) * 2;
+    const int kc = (threadIdx.x / (BM / 2)) * KV;
+    __attribute__((aligned(16))) TM o0[KV];
+    __attribute__((aligned(16))) TM o1[KV];
 #pragma unroll
     for (int kk = 0; kk < KV; ++kk) {
-      const TG* p = src + (int64_t)kk * ld;
-      if constexpr (sizeof(TG) == 2) {
-        uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-        v0[kk] = Conv<TG, TM>::cv((TG)(w & 0xFFFFu));
-        v1[kk] = Conv<TG, TM>::cv((TG)(w >> 16));
-      } else {
-        float2 w = *reinterpret_cast<const float2*>(p);
-        v0[kk] = Conv<TG, TM>::cv(w.x);
-        v1[kk] = Conv<TG, TM>::cv(w.y);
-      }
+      o0[kk] = Conv<TG, TM>::cv(v0[kk]);
+      o1[kk] = Conv<TG, TM>::cv(v1[kk]);
     }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KV; ++kk) {
-      const int k = k0 + kc + kk;
-      const int r = r0 + rc;
-      TG a = (TG)0, b = (TG)0;
-      if (k < K) {
-        if (r < rows) a = base[(int64_t)k * ld + r];
-        if (r + 1 < rows) b = base[(int64_t)k * ld + r + 1];
-      }
-      v0[kk] = Conv<TG, TM>::cv(a);
-      v1[kk] = Conv<TG, TM>::cv(b);
-    }
+    TM* d0 = S + rc * LDK + kc;  // 16-byte aligned: LDK*sizeof(TM) and kc*sizeof(TM) are
+    TM* d1 = d0 + LDK;            // multiples of 16
+    *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<const uint4*>(o0);
+    *reinterpret_cast<uint4*>(d1) = *reinterpret_cast<const uint4*>(o1);
   }
-  TM* d0 = S + rc * LDK + kc;  // 16-byte aligned: LDK*sizeof(TM) and kc*sizeof(TM) are
-  TM* d1 = d0 + LDK;            // multiples of 16
-  *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<const uint4*>(v0);
-  *reinterpret_cast<uint4*>(d1) = *reinterpret_cast<const uint4*>(v1);
-}
-
-template <typename TG, typename TM, int LAY>
-__device__ __forceinline__ void stage(const TG* base, int64_t ld, int r0, int rows, int k0,
-                                      int K, bool fast, TM* S) {
-  if constexpr (LAY == KC)
-    stage_kc<TG, TM>(base, ld, r0, rows, k0, K, fast, S);
-  else
-    stage_rc<TG, TM>(base, ld, r0, rows, k0, K, fast, S);
-}
+};
 
 // ------------------------------------------------------------ MFMA step
 
 template <typename TM> struct Mma;
 
 template <> struct Mma<bf16_t> {
-  // one k-group of 16: fragments are 8 consecutive k at offset 8*(lane/32)
+  // k-groups of 16: fragments are 8 consecutive k at offset 8*(lane/32).  The
+  // next group's fragments are read before this group's MFMAs go out.
   __device__ __forceinline__ static void step(const bf16_t* As, const bf16_t* Bs, int wm,
                                               int wn, f32x16 (&acc)[2][2]) {
     constexpr int LDK = Cfg<bf16_t>::LDK, BK = Cfg<bf16_t>::BK;
+    constexpr int NG = BK / 16;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
+    const bf16_t* pa = As + (wm * 64 + lr) * LDK + lk * 8;
+    const bf16_t* pb = Bs + (wn * 64 + lr) * LDK + lk * 8;
+    bf16x8 af[2][2], bfg[2][2];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bfg[2];
+    for (int i = 0; i < 2; ++i) {
+      af[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * LDK);
+      bfg[0][i] = *reinterpret_cast<const bf16x8*>(pb + i * 32 * LDK);
+    }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 32 + lr) * LDK + kk + lk * 8);
+    for (int g = 0; g < NG; ++g) {
+      const int c = g & 1, n = c ^ 1;
+      if (g + 1 < NG) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfg[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 32 + lr) * LDK + kk + lk * 8);
+        for (int i = 0; i < 2; ++i) {
+          af[n][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * LDK + (g + 1) * 16);
+          bfg[n][i] = *reinterpret_cast<const bf16x8*>(pb + i * 32 * LDK + (g + 1) * 16);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the reads go out ahead of the MFMAs
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfg[c][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
 
 template <> struct Mma<float> {
-  // pairs of 32x32x2 MFMAs over 4 k: lane supplies k = kk + 2*(lane/32) + {0,1}
+  // k-groups of 4, each two 32x32x2 MFMAs per output block: lane supplies
+  // k = 4 g + 2*(lane/32) + {0,1}.  The next group's fragments are read
+  // before this group's MFMAs go out.
   __device__ __forceinline__ static void step(const float* As, const float* Bs, int wm, int wn,
                                               f32x16 (&acc)[2][2]) {
     constexpr int LDK = Cfg<float>::LDK, BK = Cfg<float>::BK;
+    constexpr int NG = BK / 4;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
+    const float* pa = As + (wm * 64 + lr) * LDK + lk * 2;
+    const float* pb = Bs + (wn * 64 + lr) * LDK + lk * 2;
+    float2 af[2][2], bfg[2][2];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 4) {
-      float2 af[2], bfg[2];
+    for (int i = 0; i < 2; ++i) {
+      af[0][i] = *reinterpret_cast<const float2*>(pa + i * 32 * LDK);
+      bfg[0][i] = *reinterpret_cast<const float2*>(pb + i * 32 * LDK);
+    }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const float2*>(As + (wm * 64 + i * 32 + lr) * LDK + kk + lk * 2);
+    for (int g = 0; g < NG; ++g) {
+      const int c = g & 1, n = c ^ 1;
+      if (g + 1 < NG) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfg[j] = *reinterpret_cast<const float2*>(Bs + (wn * 64 + j * 32 + lr) * LDK + kk + lk * 2);
+        for (int i = 0; i < 2; ++i) {
+          af[n][i] = *reinterpret_cast<const float2*>(pa + i * 32 * LDK + (g + 1) * 4);
+          bfg[n][i] = *reinterpret_cast<const float2*>(pb + i * 32 * LDK + (g + 1) * 4);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the reads go out ahead of the MFMAs
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i].x, bfg[j].x, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i].y, bfg[j].y, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[c][i].x, bfg[c][j].x, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[c][i].y, bfg[c][j].y, acc[i][j], 0, 0, 0);
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
 
 // ------------------------------------------------------------ kernel
 
-// Base address of problem b of an operand or output.
-__device__ __forceinline__ const char* prob_base(const GemmArgs& g, const void* p, int tbl,
-                                                 int64_t stride, size_t es, int b) {
-  if (tbl) return tbl_addr(g.tbl, b, g.tbl_per, stride * (int64_t)es);
-  return reinterpret_cast<const char*>(p) + (int64_t)b * stride * (int64_t)es;
-}
+// One product set of a launch as the kernel sees it.
+struct KGroup {
+  GemmCore g;
+  int tiles_n, tiles;   // tiles per problem
+  int blk_begin;        // first block of the set in the launch grid
+  int a_aligned, b_aligned;
+};
 
 struct KArgs {
-  GemmArgs g;
-  bool a_aligned, b_aligned;
-  int tiles_n, tiles;
+  KGroup grp[kGemmMaxGroups];
+  PtrTbl tbl;
+  int ngroups;
 };
+
+// Base address of problem b of an operand or output.
+__device__ __forceinline__ const char* prob_base(const KArgs& ka, const GemmCore& g, const void* p,
+                                                 int tbl, int64_t stride, size_t es, int b) {
+  if (tbl) {
+    const int e = g.tbl_off + b / g.tbl_per;
+    return ka.tbl.p[e] + (int64_t)(b % g.tbl_per) * stride * (int64_t)es;
+  }
+  return reinterpret_cast<const char*>(p) + (int64_t)b * stride * (int64_t)es;
+}
 
 // ROLE (the SM_K_GEMM_* / SM_K_PROBE kind) changes no code; it gives each
 // role its own kernel symbol so per-kernel profiles attribute time by role.
 template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE>
 __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
-  __shared__ __attribute__((aligned(16))) TM As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) TM Bs[BN * LDK];
+  __shared__ __attribute__((aligned(16))) TM As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) TM Bs[2][BN * LDK];
   __shared__ float red[4];
-  const GemmArgs& g = ka.g;
-  const int b = blockIdx.y;
+  int gi = 0;
+  while (gi + 1 < ka.ngroups && (int)blockIdx.x >= ka.grp[gi + 1].blk_begin) ++gi;
+  const KGroup& kg = ka.grp[gi];
+  const GemmCore& g = kg.g;
+  const int local = (int)blockIdx.x - kg.blk_begin;
+  const int b = local / kg.tiles;
+  const int tile = local - b * kg.tiles;
   if (g.pred && g.pred[(int64_t)b * g.pred_stride] != g.pred_val) return;
-  if (g.prof_exec && blockIdx.x == 0 && threadIdx.x == 0) {
+  if (g.prof_exec && tile == 0 && threadIdx.x == 0) {
     atomicAdd(g.prof_exec, g.prof_flops);
     atomicAdd(g.prof_exec + 1, g.prof_bytes);
   }
 
-  const int tile = blockIdx.x;
-  const int tm = tile / ka.tiles_n, tn = tile % ka.tiles_n;
+  int tm, tn;
+  if (g.sym) {   // lower-triangle tile u = tm (tm + 1) / 2 + tn, tn <= tm
+    tm = (int)((sqrtf(8.f * (float)tile + 1.f) - 1.f) * 0.5f);
+    while (tm * (tm + 1) / 2 > tile) --tm;
+    while ((tm + 1) * (tm + 2) / 2 <= tile) ++tm;
+    tn = tile - tm * (tm + 1) / 2;
+  } else {
+    tm = tile / kg.tiles_n;
+    tn = tile % kg.tiles_n;
+  }
+  const bool mirror = g.sym && tm != tn;
   const int m0 = tm * BM, n0 = tn * BN;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const TA* A = reinterpret_cast<const TA*>(prob_base(g, g.a.p, g.a.tbl, g.a.stride, sizeof(TA), b));
-  const TB* B = reinterpret_cast<const TB*>(prob_base(g, g.b.p, g.b.tbl, g.b.stride, sizeof(TB), b));
+  const TA* A =
+      reinterpret_cast<const TA*>(prob_base(ka, g, g.a.p, g.a.tbl, g.a.stride, sizeof(TA), b));
+  const TB* B =
+      reinterpret_cast<const TB*>(prob_base(ka, g, g.b.p, g.b.tbl, g.b.stride, sizeof(TB), b));
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -266,15 +340,32 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const bool a_rows_in = (m0 + BM) <= g.M;
-  const bool b_rows_in = (n0 + BN) <= g.N;
-  for (int k0 = 0; k0 < g.K; k0 += BK) {
-    const bool k_in = (k0 + BK) <= g.K;
+  const bool a_fast_rows = kg.a_aligned && (m0 + BM) <= g.M;
+  const bool b_fast_rows = kg.b_aligned && (n0 + BN) <= g.N;
+  const int nk = (g.K + BK - 1) / BK;
+  Stage<TA, TM, LA> sa;
+  Stage<TB, TM, LB> sb;
+  sa.load(A, g.a.ld, m0, g.M, 0, g.K, a_fast_rows && BK <= g.K);
+  sb.load(B, g.b.ld, n0, g.N, 0, g.K, b_fast_rows && BK <= g.K);
+  sa.store(As[0]);
+  sb.store(Bs[0]);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k0 = (kt + 1) * BK;
+      const bool k_in = (k0 + BK) <= g.K;
+      sa.load(A, g.a.ld, m0, g.M, k0, g.K, a_fast_rows && k_in);
+      sb.load(B, g.b.ld, n0, g.N, k0, g.K, b_fast_rows && k_in);
+    }
+    Mma<TM>::step(As[cur], Bs[cur], wm, wn, acc);
+    if (more) {
+      // stage cur ^ 1 was last read by slab kt - 1, before the previous barrier
+      sa.store(As[cur ^ 1]);
+      sb.store(Bs[cur ^ 1]);
+    }
     __syncthreads();
-    stage<TA, TM, LA>(A, g.a.ld, m0, g.M, k0, g.K, ka.a_aligned && a_rows_in && k_in, As);
-    stage<TB, TM, LB>(B, g.b.ld, n0, g.N, k0, g.K, ka.b_aligned && b_rows_in && k_in, Bs);
-    __syncthreads();
-    Mma<TM>::step(As, Bs, wm, wn, acc);
   }
 
   // ---------------- epilogue
@@ -287,11 +378,14 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lk = lane >> 5;
   const size_t ces = (g.c_dt == BF16) ? 2 : 4;
-  const char* cin_b = g.cin ? prob_base(g, g.cin, g.cin_tbl, g.scin, ces, b) : nullptr;
-  char* c_b = g.c ? const_cast<char*>(prob_base(g, g.c, g.c_tbl, g.sc, ces, b)) : nullptr;
-  float* c2_b =
-      g.c2 ? reinterpret_cast<float*>(const_cast<char*>(prob_base(g, g.c2, g.c2_tbl, g.sc2, 4, b)))
-           : nullptr;
+  // an input / output is present when its pointer or its table flag is set
+  const char* cin_b =
+      (g.cin || g.cin_tbl) ? prob_base(ka, g, g.cin, g.cin_tbl, g.scin, ces, b) : nullptr;
+  char* c_b = (g.c || g.c_tbl) ? const_cast<char*>(prob_base(ka, g, g.c, g.c_tbl, g.sc, ces, b))
+                               : nullptr;
+  float* c2_b = (g.c2 || g.c2_tbl) ? reinterpret_cast<float*>(const_cast<char*>(
+                                         prob_base(ka, g, g.c2, g.c2_tbl, g.sc2, 4, b)))
+                                   : nullptr;
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -301,6 +395,7 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
         const int col = n0 + wn * 64 + j * 32 + lr;
+        float stored = 0.f;
         if (row < g.M && col < g.N) {
           float val = alpha * acc[i][j][v];
           if (cin_b) {
@@ -311,12 +406,17 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
             val += beta * ci;
           }
           if (row == col) val += g.diag;
+          stored = (g.c_dt == BF16) ? bf2f(f2bf(val)) : val;
           if (c_b) {
             const int64_t off = (int64_t)row * g.ldc + col;
-            if (g.c_dt == BF16)
+            const int64_t offt = (int64_t)col * g.ldc + row;
+            if (g.c_dt == BF16) {
               reinterpret_cast<bf16_t*>(c_b)[off] = f2bf(val);
-            else
+              if (mirror) reinterpret_cast<bf16_t*>(c_b)[offt] = f2bf(val);
+            } else {
               reinterpret_cast<float*>(c_b)[off] = val;
+              if (mirror) reinterpret_cast<float*>(c_b)[offt] = val;
+            }
           }
           if (c2_b) {
             c2_b[(int64_t)row * g.ldc2 + col] = g.c2_scale * val + (row == col ? g.c2_diag : 0.f);
@@ -326,19 +426,41 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
             rs += d * d;
           }
         }
+        acc[i][j][v] = stored;
       }
+  if (g.bits) {
+    // Signs of the stored values, packed: for fixed (i, v) the ballot over
+    // the wave of block j holds row R (lanes 0-31) and row R + 4 (lanes
+    // 32-63), columns c0 + 32 j + lane % 32, with c0 = n0 + 64 wn a multiple
+    // of 64; N % 64 == 0 makes each (row, c0) span exactly one sign word.
+    uint64_t* bits_b = g.bits + (int64_t)b * g.bits_stride;
+    const int c0 = n0 + wn * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint64_t b0 = __ballot(acc[i][0][v] < 0.f);
+        const uint64_t b1 = __ballot(acc[i][1][v] < 0.f);
+        const int row = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
+        if (lr == 0 && row < g.M && c0 < g.N) {
+          const uint64_t w = lk == 0 ? ((b0 & 0xFFFFFFFFull) | (b1 << 32))
+                                     : ((b0 >> 32) | (b1 & 0xFFFFFFFF00000000ull));
+          bits_b[((int64_t)row * g.N + c0) >> 6] = w;
+        }
+      }
+  }
   if (g.resid) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) rs += __shfl_xor(rs, o, 64);
     if (lane == 0) red[wave] = rs;
     __syncthreads();
     if (threadIdx.x == 0)
-      g.resid[(int64_t)b * ka.tiles + tile] = (red[0] + red[1]) + (red[2] + red[3]);
+      g.resid[(int64_t)b * kg.tiles + tile] = (red[0] + red[1]) + (red[2] + red[3]);
   }
 }
 
 // Host-side alignment test for the vector staging path of an operand.
-inline bool operand_aligned(const GemmArgs& g, const GemmOperand& o, int mfma_dt) {
+inline bool operand_aligned(const GemmArgs& g, const GemmOperand& o) {
   const size_t es = dt_size(o.dt);
   uintptr_t p = reinterpret_cast<uintptr_t>(o.p);
   if (o.tbl) {  // every table entry must satisfy the same alignment
@@ -352,32 +474,71 @@ inline bool operand_aligned(const GemmArgs& g, const GemmOperand& o, int mfma_dt
     return (p % 16 == 0) && (o.ld % vec == 0) && (o.stride % vec == 0);
   }
   // pairs of adjacent rows: 4-byte (bf16) or 8-byte (f32) loads
-  (void)mfma_dt;
   return (p % (2 * es) == 0) && (o.ld % 2 == 0) && (o.stride % 2 == 0);
 }
 
+inline bool uses_tbl(const GemmArgs& g) {
+  return g.a.tbl || g.b.tbl || g.cin_tbl || g.c_tbl || g.c2_tbl;
+}
+
+// Launches n (<= kGemmMaxGroups) product sets of one operand-type / layout
+// combination; their tables must fit one launch table together (the caller,
+// launch_gemm_groups, packs them).
 template <typename TA, typename TB, typename TM, int LA, int LB>
-sm_status launch_t(const GemmArgs& g, int kind, hipStream_t s) {
+sm_status launch_t(const GemmArgs* gs, int n, int kind, hipStream_t s) {
   KArgs ka;
-  ka.g = g;
-  ka.a_aligned = operand_aligned(g, g.a, 0);
-  ka.b_aligned = operand_aligned(g, g.b, 0);
-  const int tiles_m = (g.M + BM - 1) / BM;
-  ka.tiles_n = (g.N + BN - 1) / BN;
-  ka.tiles = tiles_m * ka.tiles_n;
-  dim3 grid(ka.tiles, g.batch);
-  const double bytes = ((double)g.M * g.K * dt_size(g.a.dt) + (double)g.N * g.K * dt_size(g.b.dt) +
-                        (double)g.M * g.N * (g.c ? dt_size(g.c_dt) : 0)) * g.batch;
-  double* exec = g.pred ? prof_exec_slot(kind) : nullptr;
-  if (exec) {  // the problems that run report their own work
-    ka.g.prof_exec = exec;
-    ka.g.prof_flops = 2.0 * g.M * (double)g.N * g.K;
-    ka.g.prof_bytes = bytes / g.batch;
-    prof_begin(kind, 0.0, s, 0.0);
-  } else {
-    ka.g.prof_exec = nullptr;
-    prof_begin(kind, 2.0 * g.M * (double)g.N * g.K * g.batch, s, bytes);
+  std::memset(&ka, 0, sizeof(ka));
+  int nt = 0;        // launch table entries used
+  int64_t blk = 0;
+  double flops = 0.0, bytes = 0.0;
+  bool any_pred = false;
+  ka.ngroups = n;
+  for (int i = 0; i < n; ++i) {
+    const GemmArgs& g = gs[i];
+    KGroup& k = ka.grp[i];
+    k.g = static_cast<const GemmCore&>(g);
+    if (uses_tbl(g)) {
+      const int ne = (g.batch + g.tbl_per - 1) / g.tbl_per;
+      int off = -1;
+      for (int o = 0; o + ne <= nt && off < 0; ++o)   // a set of the launch with the same table
+        if (std::memcmp(&ka.tbl.p[o], &g.tbl.p[0], ne * sizeof(const char*)) == 0) off = o;
+      if (off < 0) {
+        if (nt + ne > kTbl) return SM_ERR_UNSUPPORTED;
+        std::memcpy(&ka.tbl.p[nt], &g.tbl.p[0], ne * sizeof(const char*));
+        off = nt;
+        nt += ne;
+      }
+      k.g.tbl_off = off;
+    } else {
+      k.g.tbl_off = 0;
+    }
+    k.a_aligned = operand_aligned(g, g.a);
+    k.b_aligned = operand_aligned(g, g.b);
+    const int tiles_m = (g.M + BM - 1) / BM;
+    k.tiles_n = (g.N + BN - 1) / BN;
+    k.tiles = g.sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * k.tiles_n;
+    k.blk_begin = (int)blk;
+    blk += (int64_t)k.tiles * g.batch;
+    // a symmetric product is credited the half it needs
+    const double fl = (g.sym ? 1.0 : 2.0) * g.M * (double)g.N * g.K;
+    const double by = (double)g.M * g.K * dt_size(g.a.dt) + (double)g.N * g.K * dt_size(g.b.dt) +
+                      (double)g.M * g.N * ((g.c || g.c_tbl) ? dt_size(g.c_dt) : 0);
+    if (g.pred) {  // the problems that run report their own work
+      k.g.prof_exec = prof_exec_slot(kind);
+      k.g.prof_flops = fl;
+      k.g.prof_bytes = by;
+      any_pred = any_pred || k.g.prof_exec;
+    } else {
+      k.g.prof_exec = nullptr;
+      flops += fl * g.batch;
+      bytes += by * g.batch;
+    }
   }
+  if (blk == 0) return SM_OK;
+  if (blk > 0x7FFFFFFF) return SM_ERR_SHAPE;
+  (void)any_pred;
+  prof_begin(kind, flops, s, bytes);
+  const dim3 grid((unsigned)blk);
   switch (kind) {
     case SM_K_GEMM_GRAM:
       hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_GRAM>), grid, dim3(NT), 0, s, ka);

@@ -148,6 +148,7 @@ GemmArgs gemm_base(int M, int N, int K, int batch) {
   g.alpha = 1.f;
   g.beta = 0.f;
   g.tbl_per = 1;
+  g.tbl_off = 0;
   return g;
 }
 
@@ -749,42 +750,86 @@ GemmArgs apply_args(const void* bm, int bm_dt, int bm_tbl, const void* x, int dt
 // X_{k+1} = a X_k + (b A_k + c A_k^2) X_k,  A_k = X_k X_k^T, starting from
 // X_0 = s x (s = scale[b], or 1 without normalisation).  The scale enters
 // the first step's GEMMs: A_0 = s^2 x x^T, X_1 = s (a x + B_0 x).
+// This is the path of the jobs that the persistent bf16 kernel does not
+// take (float32 above all): per iteration the Gram products of every job go
+// out as grouped launches, then the quintic terms, then the applies.
+sm_status ns_generic(const std::vector<NsJob>& jobs, int dt, const sm_ns_params& p,
+                     hipStream_t s) {
+  const int K = p.iters;
+  const size_t nj = jobs.size();
+  std::vector<const void*> cur(nj);
+  for (size_t i = 0; i < nj; ++i) cur[i] = jobs[i].x;
+  // the iterate of job i read through its pointer table (k == 0 with xtbl)
+  auto via_tbl = [&](size_t i, int k) { return k == 0 && jobs[i].xtbl != nullptr; };
+  std::vector<GemmArgs> gr, qr, ap;
+  for (int k = 0; k < K; ++k) {
+    gr.clear();
+    qr.clear();
+    ap.clear();
+    for (size_t i = 0; i < nj; ++i) {
+      const NsJob& j = jobs[i];
+      const int m = j.m, n = j.n, r = m < n ? m : n;
+      const int64_t rr = (int64_t)r * r, mn = (int64_t)m * n;
+      const bool first = (k == 0) && j.scale;
+      const bool last = k == K - 1;
+      const bool tb = via_tbl(i, k);
+      void* dst = ((K - 1 - k) % 2 == 0) ? j.out : j.w.tmp;
+      // A_k (times b when the quintic term is absent)
+      GemmArgs g = gram_args(cur[i], dt, j.batch, m, n);
+      if (tb) {
+        g.a.tbl = g.b.tbl = 1;
+        g.tbl = *j.xtbl;
+        g.tbl_per = j.xper;
+      }
+      g.c = j.w.amat; g.ldc = r; g.sc = rr; g.c_dt = dt;
+      g.scale = j.scale; g.alpha_pow = first ? 2 : 0;
+      g.alpha = (p.c == 0.f) ? p.b : 1.f;
+      g.sym = 1;
+      gr.push_back(g);
+      const void* bmat = j.w.amat;
+      if (p.c != 0.f) {  // B = c A A + b A
+        GemmArgs q = gemm_base(r, r, r, j.batch);
+        q.a = opnd(j.w.amat, r, rr, dt, KC);
+        q.b = opnd(j.w.amat, r, rr, dt, RC);
+        q.cin = j.w.amat; q.ldcin = r; q.scin = rr;
+        q.c = j.w.amat2; q.ldc = r; q.sc = rr; q.c_dt = dt;
+        q.alpha = p.c; q.beta = p.b;
+        q.sym = 1;   // c A^2 + b A of a symmetric A
+        qr.push_back(q);
+        bmat = j.w.amat2;
+      }
+      GemmArgs a = apply_args(bmat, dt, 0, cur[i], dt, j.batch, m, n);
+      a.cin = cur[i]; a.ldcin = n; a.scin = mn;
+      if (tb) {
+        (m <= n ? a.b : a.a).tbl = 1;
+        a.cin_tbl = 1;
+        a.tbl = *j.xtbl;
+        a.tbl_per = j.xper;
+      }
+      a.c_dt = dt;   // also the type of Cin, and the rounding the signs are taken after
+      if (last && j.bits) {   // signs only: X_K itself is not stored
+        a.bits = j.bits;
+        a.bits_stride = j.bits_stride;
+      } else {
+        a.c = dst; a.ldc = n; a.sc = mn;
+      }
+      a.scale = j.scale; a.alpha_pow = first ? 1 : 0; a.beta_pow = first ? 1 : 0;
+      a.alpha = 1.f; a.beta = p.a;
+      ap.push_back(a);
+      cur[i] = dst;
+    }
+    SM_TRY(launch_gemm_groups(gr, dt, SM_K_GEMM_GRAM, s));
+    if (!qr.empty()) SM_TRY(launch_gemm_groups(qr, dt, SM_K_GEMM_RR, s));
+    SM_TRY(launch_gemm_groups(ap, dt, SM_K_GEMM_APPLY, s));
+  }
+  return SM_OK;
+}
+
 sm_status ns_core(const void* x, void* out, const NsWs& w, const float* scale, int dt, int batch,
                   int m, int n, const sm_ns_params& p, hipStream_t s) {
   const NsJob job{x, out, w, scale, batch, m, n};
   if (ns_grouped_ok(job, dt, p)) return ns_grouped(std::vector<NsJob>{job}, p, s);
-  const int r = m < n ? m : n;
-  const int K = p.iters;
-  const void* cur = x;
-  for (int k = 0; k < K; ++k) {
-    void* dst = ((K - 1 - k) % 2 == 0) ? out : w.tmp;
-    const bool first = (k == 0) && scale;
-    // A_k (times b when the quintic term is absent)
-    GemmArgs g = gram_args(cur, dt, batch, m, n);
-    g.c = w.amat; g.ldc = r; g.sc = (int64_t)r * r; g.c_dt = dt;
-    g.scale = scale; g.alpha_pow = first ? 2 : 0;
-    g.alpha = (p.c == 0.f) ? p.b : 1.f;
-    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_GRAM, s));
-    const void* bmat = w.amat;
-    if (p.c != 0.f) {  // B = c A A + b A
-      GemmArgs q = gemm_base(r, r, r, batch);
-      q.a = opnd(w.amat, r, (int64_t)r * r, dt, KC);
-      q.b = opnd(w.amat, r, (int64_t)r * r, dt, RC);
-      q.cin = w.amat; q.ldcin = r; q.scin = (int64_t)r * r;
-      q.c = w.amat2; q.ldc = r; q.sc = (int64_t)r * r; q.c_dt = dt;
-      q.alpha = p.c; q.beta = p.b;
-      SM_TRY(launch_gemm(q, dt, SM_K_GEMM_RR, s));
-      bmat = w.amat2;
-    }
-    GemmArgs a = apply_args(bmat, dt, 0, cur, dt, batch, m, n);
-    a.cin = cur; a.ldcin = n; a.scin = (int64_t)m * n;
-    a.c = dst; a.ldc = n; a.sc = (int64_t)m * n; a.c_dt = dt;
-    a.scale = scale; a.alpha_pow = first ? 1 : 0; a.beta_pow = first ? 1 : 0;
-    a.alpha = 1.f; a.beta = p.a;
-    SM_TRY(launch_gemm(a, dt, SM_K_GEMM_APPLY, s));
-    cur = dst;
-  }
-  return SM_OK;
+  return ns_generic(std::vector<NsJob>{job}, dt, p, s);
 }
 
 // ------------------------------------------------------------------ Gram NS with cache
@@ -1496,14 +1541,19 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
         }
       }
       if (!r.grouped) r.grouped = ns_grouped_ok(r.job, c->mdt, c->ns);
+      if (!r.grouped && c->algo == SM_SIGN_MUON) {  // the generic path reads M in place too
+        r.job.x = nullptr;
+        r.job.xtbl = &r.mom;
+        r.job.xper = M;
+      }
       // a7 + a8 fused into the last NS product when the signs are all the
       // step needs from the direction
       r.fused_signs = false;
-      if (r.grouped && !polar && c->encoding == SM_ENC_BITS) {
+      if (!polar && c->encoding == SM_ENC_BITS) {
         NsJob bj = r.job;
         bj.bits = r.w.bits;
         bj.bits_stride = r.words;
-        if (ns_grouped_ok(bj, c->mdt, c->ns)) {
+        if (r.grouped ? ns_grouped_ok(bj, c->mdt, c->ns) : (ch.n % 64) == 0) {
           r.job = bj;
           r.fused_signs = true;
         }
@@ -1529,7 +1579,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     std::vector<EmaMat> ema;
     for (size_t ci = 0; ci < chunks.size(); ++ci) {
       ChunkRun& r = runs[ci];
-      void* x0 = (r.grouped && r.job.xtbl) ? nullptr : r.w.x0;   // no copy when NS reads M
+      void* x0 = r.job.xtbl ? nullptr : r.w.x0;   // no copy when NS reads M
       for (int j = 0; j < r.nc; ++j) {
         EmaMat e;
         e.mom = const_cast<char*>(r.mom.p[j]);
@@ -1548,7 +1598,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
   // a3-a5: the direction.  Direct NS runs all chunks the grouped kernel takes
   // together (one launch per product kind and iteration).
   if (muon_step) {
-    std::vector<NsJob> grouped;
+    std::vector<NsJob> grouped, generic;
     for (size_t ci = 0; ci < chunks.size(); ++ci) {
       const Chunk& ch = chunks[ci];
       ChunkRun& r = runs[ci];
@@ -1565,12 +1615,10 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
                          s));
         continue;
       }
-      if (r.grouped)
-        grouped.push_back(r.job);
-      else
-        SM_TRY(ns_core(r.w.x0, r.w.d, r.w.ns, r.w.scale, c->mdt, r.B, ch.m, ch.n, c->ns, s));
+      (r.grouped ? grouped : generic).push_back(r.job);
     }
     if (!grouped.empty()) SM_TRY(ns_grouped(grouped, c->ns, s));
+    if (!generic.empty()) SM_TRY(ns_generic(generic, c->mdt, c->ns, s));
   }
   // a7-a10: signs (packed bits or int8), vote and update (or the polar update)
   const bool int8 = c->encoding == SM_ENC_INT8;
@@ -1608,8 +1656,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
   }
   // Optional local polar step on the vote: V (exact in mdt) -> its own
   // normalisation -> NS with the step's settings -> W <- W - lr * D.
-  std::vector<NsJob> vjobs;
-  std::vector<size_t> vgen;   // chunks whose vote NS takes the generic path
+  std::vector<NsJob> vjobs, vgen;   // vote NS jobs: persistent kernel / generic path
   for (size_t ci = 0; ci < chunks.size(); ++ci) {
     const Chunk& ch = chunks[ci];
     ChunkRun& r = runs[ci];
@@ -1623,17 +1670,10 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     SM_TRY(launch_sumsq(r.w.x0, c->mdt, r.nc, r.count, r.w.partials, s));
     SM_TRY(launch_scale_finalize(r.w.partials, r.nc, r.count, c->ns.eps, r.w.scale, s));
     NsJob j{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.nc, ch.m, ch.n};
-    if (ns_grouped_ok(j, c->mdt, c->ns))
-      vjobs.push_back(j);
-    else
-      vgen.push_back(ci);
+    (ns_grouped_ok(j, c->mdt, c->ns) ? vjobs : vgen).push_back(j);
   }
   if (!vjobs.empty()) SM_TRY(ns_grouped(vjobs, c->ns, s));
-  for (size_t ci : vgen) {
-    const Chunk& ch = chunks[ci];
-    ChunkRun& r = runs[ci];
-    SM_TRY(ns_core(r.w.x0, r.w.d, r.w.ns, r.w.scale, c->mdt, r.nc, ch.m, ch.n, c->ns, s));
-  }
+  if (!vgen.empty()) SM_TRY(ns_generic(vgen, c->mdt, c->ns, s));
   for (size_t ci = 0; ci < chunks.size(); ++ci) {
     ChunkRun& r = runs[ci];
     SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));

@@ -8,6 +8,7 @@
 #include <stddef.h>
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "../../include/sm.h"
 
@@ -301,14 +302,24 @@ struct GemmOperand {
 //   alpha_b = alpha * scale[b]^alpha_pow, beta_b = beta * scale[b]^beta_pow.
 // Cin has C's dtype.  Optional outputs: C (c_dt), C2 (float32) =
 // c2_diag*I + c2_scale*value,
-// resid partials ([batch][tiles]) = sum over the tile of (value - I)^2.
+// resid partials ([batch][tiles]) = sum over the tile of (value - I)^2,
+// bits ([batch][bits_stride] words): the packed signs of C as stored (bit e
+// of word w set iff entry 64 w + e of the row-major M x N result is
+// negative; needs N % 64 == 0).
 // Problems with pred && pred[b*pred_stride] != pred_val are skipped.
-struct GemmArgs {
+// sym: the result is symmetric (A B with A = B^T, or commuting symmetric
+// factors, and a symmetric Cin): only tiles on and below the diagonal are
+// computed, each off-diagonal one stored a second time, transposed (C only;
+// no C2, resid or bits).
+// Operands / outputs flagged `tbl` address problem b through the launch's
+// pointer table: entry tbl_off + b / tbl_per, plus (b % tbl_per) * stride.
+struct GemmCore {
   GemmOperand a, b;
   const void* cin; int64_t ldcin, scin; int cin_tbl;
   void* c; int64_t ldc, sc; int c_dt; int c_tbl;
   float* c2; int64_t ldc2, sc2; int c2_tbl;
   float* resid;
+  uint64_t* bits; int64_t bits_stride;
   const float* scale;
   const int32_t* pred; int pred_stride; int32_t pred_val;
   int M, N, K, batch;
@@ -316,13 +327,17 @@ struct GemmArgs {
   float beta; int beta_pow;
   float diag;
   float c2_diag, c2_scale;
-  // Optional per-matrix base pointers for operands / outputs flagged `tbl`
-  // (CacheMuon's per-matrix Q caches); tbl_per problems per entry.
-  PtrTbl tbl;
-  int tbl_per;
+  int sym;
+  int tbl_per, tbl_off;
   // Kernel-time accounting of predicated launches (set by the launcher):
   // each problem that runs adds prof_flops / prof_bytes to prof_exec[0 / 1].
   double* prof_exec; double prof_flops, prof_bytes;
+};
+// One product set as the host builds it: the per-matrix base pointers
+// (CacheMuon's Q caches, Sign-Muon's momenta) ride along in tbl; the launcher
+// packs the tables of the sets it groups into one launch table.
+struct GemmArgs : GemmCore {
+  PtrTbl tbl;
 };
 
 // Tiles per problem that the GEMM launch uses for (M, N) (resid partials).
@@ -330,6 +345,10 @@ int gemm_tiles(int mfma_dt, int M, int N);
 
 // Launch with MFMA operand type mfma_dt (BF16 -> bf16 MFMA, F32 -> fp32 MFMA).
 sm_status launch_gemm(const GemmArgs& g, int mfma_dt, int kind, hipStream_t s);
+// Launches the product sets gs (one kind, one MFMA type) in as few launches
+// as their operand types / layouts, the table capacity and the group limit
+// allow; within a launch the sets run in order of decreasing K.
+sm_status launch_gemm_groups(std::vector<GemmArgs>& gs, int mfma_dt, int kind, hipStream_t s);
 
 // ---------------------------------------------------------------- grouped NS GEMM
 
