@@ -11,6 +11,11 @@ the CPU from hipcc's assembly output (no GPU needed).
   that way).  The scan follows the straight-line order of the assembly: a
   region opened by a mask instruction counts as guarded once a conditional
   branch on the mask follows it.
+* Wait states of the direct-to-LDS loads: their inline assembly sits outside
+  the compiler's hazard recognizer, so the code must keep the distances that
+  the hardware does not check itself: five instructions between a VALU
+  write of an SGPR (v_readfirstlane, v_readlane, v_cmp ...) and a load that
+  reads it as its base, and one between writing M0 and the load.
 """
 import os
 import re
@@ -121,3 +126,73 @@ int main() {
                    check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "0", out.stdout
+
+
+def _sgprs(spec: str):
+    """SGPR numbers named by an operand such as s7 or s[40:41]."""
+    m = re.fullmatch(r"s(\d+)", spec)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", spec)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    return set()
+
+
+def lds_dma_hazards(body: str):
+    """Direct-to-LDS loads that read an SGPR a VALU instruction wrote within
+    the five instructions before (wait states counted as s_nop's argument +
+    1), or that follow an M0 write with no wait state between."""
+    insts = []
+    for line in body.splitlines():
+        t = line.split(";")[0].strip()
+        if not t or t.endswith(":") or t.startswith("."):
+            continue
+        insts.append(t)
+    bad = []
+    for n, t in enumerate(insts):
+        if not t.startswith("global_load_lds"):
+            continue
+        ops = [o.strip() for o in t.split(None, 1)[1].split(",")]
+        base = _sgprs(ops[1]) if len(ops) > 1 else set()
+        dist = 0
+        for back in range(n - 1, -1, -1):
+            u = insts[back]
+            if u.startswith("s_nop"):
+                dist += int(u.split()[1], 0) + 1
+                continue
+            if back == n - 1 and re.match(r"s_mov_b32 m0,", u):
+                bad.append((n, "M0 written just before", t))
+            if u.startswith("v_"):
+                dst = u.split(None, 1)[1].split(",")[0].strip() if " " in u else ""
+                if _sgprs(dst) & base and dist < 5:
+                    bad.append((n, u, t))
+            dist += 1
+            if dist >= 5:
+                break
+    return bad
+
+
+@pytest.mark.parametrize("role", [0, 1, 2], ids=["symmetric", "apply", "probe"])
+def test_lds_dma_wait_states(gemm_ns_asm, role):
+    _, kernels = gemm_ns_asm
+    assert "global_load_lds_dwordx4" in kernels[role]
+    bad = lds_dma_hazards(kernels[role])
+    assert not bad, bad[:5]
+
+
+def test_lds_dma_scan_finds_the_hazards():
+    """The scan itself, on hand-written fragments: a base written by a VALU
+    instruction two instructions ahead, and M0 written with no wait state."""
+    body = "\n".join([
+        "\tv_readfirstlane_b32 s41, v7",
+        "\ts_mov_b32 m0, s42",
+        "\ts_nop 0",
+        "\tglobal_load_lds_dwordx4 v62, s[40:41]",
+        "\tv_readfirstlane_b32 s40, v7",
+        "\ts_nop 4",
+        "\ts_mov_b32 m0, s42",
+        "\tglobal_load_lds_dwordx4 v61, s[40:41]",
+    ])
+    bad = lds_dma_hazards(body)
+    assert [b[0] for b in bad] == [3, 7], bad
