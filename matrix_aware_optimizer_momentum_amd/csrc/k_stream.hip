@@ -16,6 +16,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = kThreads * 8;  // elements per block iteration
+// A launch whose read-modify-write data exceeds the 256 MB Infinity Cache
+// streams it with non-temporal accesses (nothing of it would still be cached
+// when the next step reads it back); smaller data stays cacheable.
+constexpr double kStreamBytes = 256.0 * 1024 * 1024;
 static_assert(kChunk == kNormChunk, "the norm partials count chunks of kChunk");
 
 template <typename T>
@@ -76,6 +80,34 @@ __device__ __forceinline__ void store8_tail(T* p, int64_t e0, int64_t count, boo
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (e0 + e < count) Elem<T>::store(p + e0 + e, v[e]);
+  }
+}
+
+// store8_tail for data not read back soon (a Lion step's momentum, the
+// weights): non-temporal 16-byte stores.
+template <typename T>
+__device__ __forceinline__ void store8_once(T* p, int64_t e0, int64_t count, bool vec,
+                                            const float* v) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  if (vec && e0 + 8 <= count) {
+    if constexpr (sizeof(T) == 2) {
+      u32x4_t o;
+      o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+      o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(p + e0));
+    } else {
+      u32x4_t a, b;
+      a.x = __float_as_uint(v[0]); a.y = __float_as_uint(v[1]);
+      a.z = __float_as_uint(v[2]); a.w = __float_as_uint(v[3]);
+      b.x = __float_as_uint(v[4]); b.y = __float_as_uint(v[5]);
+      b.z = __float_as_uint(v[6]); b.w = __float_as_uint(v[7]);
+      __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(p + e0));
+      __builtin_nontemporal_store(b, reinterpret_cast<u32x4_t*>(p + e0 + 4));
+    }
+  } else {
+    store8_tail<T>(p, e0, count, vec, v);
   }
 }
 
@@ -210,7 +242,8 @@ template <typename TM, typename TG, typename TX>
 __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int per,
                                                    int64_t count, float b1, float b2, TX* x,
                                                    float* partials, uint64_t* bits,
-                                                   int64_t words, int8_t* s8, bool vec) {
+                                                   int64_t words, int8_t* s8, bool vec,
+                                                   bool stream) {
   __shared__ float red[4];
   const int b = blockIdx.y;
   TM* m = (TM*)tbl_addr(mom, b, per, count * (int64_t)sizeof(TM));
@@ -226,14 +259,18 @@ __global__ __launch_bounds__(kThreads) void k_lion(PtrTbl mom, PtrTbl grad, int 
     uint32_t byte = 0;
     if (e0 < count) {
       float mv[8], gv[8], dv[8];
-      load8_tail<TM>(m, e0, count, vec, mv);
+      // a large Lion step's momentum streams (see kStreamBytes); a Muon
+      // step's stays cacheable, like the G_hat its NS reads next
+      if (!stream) load8_tail<TM>(m, e0, count, vec, mv);
+      else load8_once<TM>(m, e0, count, vec, mv);
       load8_once<TG>(g, e0, count, vec, gv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         dv[e] = ema32(b1, mv[e], omb1, gv[e]);
         mv[e] = round_to<TM>(ema32(b2, mv[e], omb2, gv[e]));
       }
-      store8_tail<TM>(m, e0, count, vec, mv);
+      if (!stream) store8_tail<TM>(m, e0, count, vec, mv);
+      else store8_once<TM>(m, e0, count, vec, mv);
       if (bo) {
         byte = neg_byte(dv, e0, count);
       } else if (so) {
@@ -362,7 +399,7 @@ __device__ __forceinline__ void bits_less_greater(const uint64_t* c, int k, uint
   *gt = g;
 }
 
-template <typename TW, bool UPDATE>
+template <typename TW, bool UPDATE, bool STREAM>
 __device__ __forceinline__ void vote_bits_tiles(const uint64_t* sg, int M, int64_t stride,
                                                 int64_t count, TW* wp, float lr,
                                                 int8_t* vote_out, bool vec, int64_t tile0,
@@ -381,7 +418,11 @@ __device__ __forceinline__ void vote_bits_tiles(const uint64_t* sg, int M, int64
         uint64_t wd[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)       // all eight loads issued before the adds
-          wd[q] = k0 + q < M ? sg[(int64_t)(k0 + q) * stride + wi] : 0ull;
+          if constexpr (STREAM)
+            wd[q] = k0 + q < M ? __builtin_nontemporal_load(sg + (int64_t)(k0 + q) * stride + wi)
+                               : 0ull;
+          else
+            wd[q] = k0 + q < M ? sg[(int64_t)(k0 + q) * stride + wi] : 0ull;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           uint64_t carry = wd[q];
@@ -413,15 +454,21 @@ __device__ __forceinline__ void vote_bits_tiles(const uint64_t* sg, int M, int64
         int vv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vv[e] = (int)((pbyte >> e) & 1u) - (int)((nbyte >> e) & 1u);
+        // large weights stream past the caches (see kStreamBytes), like the
+        // signs above; the vote matrix of a polar step stays cacheable for its
+        // norm pass
         if constexpr (UPDATE) {
-          load8_tail<TW>(wp, e0, count, vec, wv);
+          if constexpr (STREAM) load8_once<TW>(wp, e0, count, vec, wv);
+          else load8_tail<TW>(wp, e0, count, vec, wv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) wv[e] = wv[e] - lr * (float)vv[e];  // lr*v exact: one rounding
+          if constexpr (STREAM) store8_once<TW>(wp, e0, count, vec, wv);
+          else store8_tail<TW>(wp, e0, count, vec, wv);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) wv[e] = (float)vv[e];
+          store8_tail<TW>(wp, e0, count, vec, wv);
         }
-        store8_tail<TW>(wp, e0, count, vec, wv);
         if (UPDATE && vote_out) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -502,16 +549,22 @@ __device__ __forceinline__ void vote_body(const void* sg, int M, int64_t stride,
 template <int ENC, typename TW, bool UPDATE>
 __global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int64_t stride,
                                                    int64_t mat_stride, int64_t count, PtrTbl w,
-                                                   float lr, int8_t* vote_out, bool vec) {
+                                                   float lr, int8_t* vote_out, bool vec,
+                                                   bool stream) {
   const int j = blockIdx.y;
   const void* sg = ENC == 0
       ? static_cast<const void*>(static_cast<const uint64_t*>(signs) + j * mat_stride)
       : static_cast<const void*>(static_cast<const int8_t*>(signs) + j * mat_stride);
   if constexpr (ENC == 0) {
     __shared__ uint64_t pos_s[kThreads], neg_s[kThreads];
-    vote_bits_tiles<TW, UPDATE>(static_cast<const uint64_t*>(sg), M, stride, count,
-                                (TW*)w.p[j], lr, vote_out, vec, blockIdx.x, gridDim.x, pos_s,
-                                neg_s);
+    if (stream)
+      vote_bits_tiles<TW, UPDATE, true>(static_cast<const uint64_t*>(sg), M, stride, count,
+                                        (TW*)w.p[j], lr, vote_out, vec, blockIdx.x, gridDim.x,
+                                        pos_s, neg_s);
+    else
+      vote_bits_tiles<TW, UPDATE, false>(static_cast<const uint64_t*>(sg), M, stride, count,
+                                         (TW*)w.p[j], lr, vote_out, vec, blockIdx.x, gridDim.x,
+                                         pos_s, neg_s);
   } else {
     vote_body<ENC, TW, UPDATE>(sg, M, stride, count, (TW*)w.p[j], lr, vote_out, vec,
                                (int64_t)blockIdx.x * kThreads + threadIdx.x,
@@ -522,13 +575,18 @@ __global__ __launch_bounds__(kThreads) void k_vote(const void* signs, int M, int
 // The vote + update of matrices of different shapes in one launch (one
 // matrix per blockIdx.y, described by the table).
 template <int ENC, typename TW>
-__global__ __launch_bounds__(kThreads) void k_vote_tbl(VoteTbl t, int M, float lr) {
+__global__ __launch_bounds__(kThreads) void k_vote_tbl(VoteTbl t, int M, float lr, bool stream) {
   const VoteMat& v = t.m[blockIdx.y];
   if constexpr (ENC == 0) {
     __shared__ uint64_t pos_s[kThreads], neg_s[kThreads];
-    vote_bits_tiles<TW, true>(static_cast<const uint64_t*>(v.signs), M, v.stride, v.count,
-                              static_cast<TW*>(v.w), lr, nullptr, (v.count % 8) == 0, blockIdx.x,
-                              gridDim.x, pos_s, neg_s);
+    if (stream)
+      vote_bits_tiles<TW, true, true>(static_cast<const uint64_t*>(v.signs), M, v.stride,
+                                      v.count, static_cast<TW*>(v.w), lr, nullptr,
+                                      (v.count % 8) == 0, blockIdx.x, gridDim.x, pos_s, neg_s);
+    else
+      vote_bits_tiles<TW, true, false>(static_cast<const uint64_t*>(v.signs), M, v.stride,
+                                       v.count, static_cast<TW*>(v.w), lr, nullptr,
+                                       (v.count % 8) == 0, blockIdx.x, gridDim.x, pos_s, neg_s);
   } else {
     vote_body<ENC, TW, true>(v.signs, M, v.stride, v.count, static_cast<TW*>(v.w), lr, nullptr,
                              (v.count % 8) == 0, (int64_t)blockIdx.x * kThreads + threadIdx.x,
@@ -753,10 +811,12 @@ sm_status launch_lion(const PtrTbl& mom, const PtrTbl& grad, int per, int nprob,
   double bytes = (double)nprob * count * (2.0 * dt_size(mdt) + dt_size(gdt)) +
                  (bits ? (double)nprob * words * 8.0
                        : (s8 ? (double)nprob * count : (double)nprob * count * dt_size(xdt)));
+  const bool stream = x == nullptr && (double)nprob * count * dt_size(mdt) > kStreamBytes;
   prof_begin(SM_K_LION, bytes, s);
   SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG, SM_DISPATCH_DT(xdt, TX,
       hipLaunchKernelGGL((k_lion<TM, TG, TX>), grid, dim3(kThreads), 0, s, mom, grad, per,
-                         count, beta1, beta2, (TX*)x, partials, bits, words, s8, vec))));
+                         count, beta1, beta2, (TX*)x, partials, bits, words, s8, vec,
+                         stream))));
   prof_end(s);
   return check_launch();
 }
@@ -828,26 +888,27 @@ sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t
   const double sign_bytes = enc == SM_ENC_BITS ? M / 8.0 : (double)M;
   double bytes = (double)nmat * count *
                  (sign_bytes + (update ? 2.0 : 1.0) * dt_size(wdt) + (vote_out ? 1.0 : 0.0));
+  const bool stream = (double)nmat * count * dt_size(wdt) > kStreamBytes;
   prof_begin(SM_K_VOTE_UPDATE, bytes, s);
   if (enc == SM_ENC_BITS) {
     if (update) {
       SM_DISPATCH_DT(wdt, TW,
           hipLaunchKernelGGL((k_vote<0, TW, true>), grid, dim3(kThreads), 0, s, signs, M,
-                             stride, mat_stride, count, w, lr, vote_out, vec));
+                             stride, mat_stride, count, w, lr, vote_out, vec, stream));
     } else {
       SM_DISPATCH_DT(wdt, TW,
           hipLaunchKernelGGL((k_vote<0, TW, false>), grid, dim3(kThreads), 0, s, signs, M,
-                             stride, mat_stride, count, w, lr, nullptr, vec));
+                             stride, mat_stride, count, w, lr, nullptr, vec, stream));
     }
   } else {
     if (update) {
       SM_DISPATCH_DT(wdt, TW,
           hipLaunchKernelGGL((k_vote<1, TW, true>), grid, dim3(kThreads), 0, s, signs, M,
-                             stride, mat_stride, count, w, lr, vote_out, vec));
+                             stride, mat_stride, count, w, lr, vote_out, vec, stream));
     } else {
       SM_DISPATCH_DT(wdt, TW,
           hipLaunchKernelGGL((k_vote<1, TW, false>), grid, dim3(kThreads), 0, s, signs, M,
-                             stride, mat_stride, count, w, lr, nullptr, vec));
+                             stride, mat_stride, count, w, lr, nullptr, vec, stream));
     }
   }
   prof_end(s);
@@ -861,7 +922,7 @@ sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt
     VoteTbl t;
     std::memset(&t, 0, sizeof(t));
     int64_t need = 1;
-    double bytes = 0.0;
+    double bytes = 0.0, wbytes = 0.0;
     const double sign_bytes = enc == SM_ENC_BITS ? M / 8.0 : (double)M;
     for (int q = 0; q < n; ++q) {
       t.m[q] = mats[q0 + q];
@@ -869,7 +930,9 @@ sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt
       const int64_t units = enc == SM_ENC_BITS ? (t.m[q].count + 63) / 64 : n8;
       need = std::max<int64_t>(need, (units + kThreads - 1) / kThreads);
       bytes += (double)t.m[q].count * (sign_bytes + 2.0 * dt_size(wdt));
+      wbytes += (double)t.m[q].count * dt_size(wdt);
     }
+    const bool stream = wbytes > kStreamBytes;
     // about 64 blocks per CU in all: the matrices' sizes differ, and short
     // blocks even out the launch's tail
     const int64_t want = (16384 + n - 1) / n;
@@ -877,10 +940,10 @@ sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt
     prof_begin(SM_K_VOTE_UPDATE, bytes, s);
     if (enc == SM_ENC_BITS) {
       SM_DISPATCH_DT(wdt, TW,
-          hipLaunchKernelGGL((k_vote_tbl<0, TW>), grid, dim3(kThreads), 0, s, t, M, lr));
+          hipLaunchKernelGGL((k_vote_tbl<0, TW>), grid, dim3(kThreads), 0, s, t, M, lr, stream));
     } else {
       SM_DISPATCH_DT(wdt, TW,
-          hipLaunchKernelGGL((k_vote_tbl<1, TW>), grid, dim3(kThreads), 0, s, t, M, lr));
+          hipLaunchKernelGGL((k_vote_tbl<1, TW>), grid, dim3(kThreads), 0, s, t, M, lr, stream));
     }
     prof_end(s);
     SM_TRY(check_launch());
