@@ -1356,7 +1356,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.tile_begin = tiles;
     g.tpp_begin = a.tpp_total;
     a.tpp_total += g.tiles_per_prob;
-    if (dyn && (G.batch != groups[0].batch || G.a_tbl || G.b_tbl)) return SM_ERR_UNSUPPORTED;
+    // a device problem list names the same problems in every group (pointer
+    // tables are addressed by the listed problem)
+    if (dyn && G.batch != groups[0].batch) return SM_ERR_UNSUPPORTED;
     const int64_t gt = (int64_t)g.tiles_per_prob * G.batch;
     if (gt <= 0) return SM_ERR_ARG;
     if ((int64_t)tiles + gt > (int64_t)1 << 30) return SM_ERR_UNSUPPORTED;

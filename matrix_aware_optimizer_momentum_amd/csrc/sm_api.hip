@@ -902,105 +902,106 @@ sm_status gram_fresh_gf(const GfPlan& g, const int32_t* flags, const int32_t* an
   return launch_q_store(g.qk.p, g.qk.st, g.r, qtbl, qper, flags, g.batch, s);
 }
 
-// One CacheMuon orthogonalisation per problem, [CacheMuon-ja] core mechanism:
-//   candidate (if cached): D_hat = Q X, err = ||D_hat D_hat^T - I||_F / sqrt(r)
-//   refresh iff no cache / forced / err > gamma, decided on the device;
-//   fresh Gram-NS (predicated on the decision): G_0 = X X^T, P_k = aI + B_k
-//   with B_k = b G_k + c G_k^2, Q_{k+1} = a Q_k + B_k Q_k,
-//   G_{k+1} = a T_k + T_k B_k with T_k = a G_k + B_k G_k, D = Q_K X.
-// The identity parts are added in float32 in the GEMM epilogues.  Q_K is
-// written straight into the cache.  Problem b's Q lives at
-// qtbl[b / qper] + (b % qper) * r*r floats; its {has_cache, a_t} pair at
-// cstbl[b / qper] + (b % qper) * 2 ints.
-sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cstbl, int qper,
-                    float* err_out, int32_t* refr_out, const PtrTbl* diag,
-                    const GramWs& w, const float* scale, int dt, int batch, int m, int n,
-                    const sm_ns_params& p, float gamma, int mode, int64_t t, hipStream_t s) {
-  const bool wide = m <= n;
-  const int r = wide ? m : n;
+// One batch of same-shaped CacheMuon problems.  Problem b's Q lives at
+// qtbl[b / qper] + (b % qper) * r*r floats, its {has_cache, a_t} pair at
+// cstbl[b / qper] + (b % qper) * 2 ints, its diagnostic row (err, refreshed)
+// at diag[b / qper] + (b % qper) * 2 floats when has_diag.  The NS input is x
+// ([batch][m][n]) or, with xtbl, worker b % xper of matrix b / xper read in
+// place (the persistent kernels only: see gram_fast_plan).
+struct GramJob {
+  const void* x;
+  const PtrTbl* xtbl;
+  int xper;
+  void* d;
+  PtrTbl qtbl, cstbl;
+  int qper;
+  float* err_out;
+  int32_t* refr_out;
+  PtrTbl diag;
+  bool has_diag;
+  GramWs w;
+  const float* scale;
+  int batch, m, n;
+};
+
+// The persistent-kernel route of a job (bf16, cubic, one-term identity, and
+// shapes the kernels take): the fresh solve's Gram-form chain, the candidate
+// D_hat = s Q x (x Q^T when tall) with Q rounded to bf16 (the operand type
+// the generic kernel would round it to), and the probe's residual partials
+// of D_hat D_hat^T - I.
+struct GramFast {
+  GfPlan gf;
+  NsgGroup ap, pr;
+};
+
+bool gram_fast_plan(const GramJob& j, int dt, const sm_ns_params& p, GramFast& f) {
+  if (dt != BF16 || p.c != 0.f || p.iters < 2) return false;
+  uint32_t hi = 0, lo = 0;
+  if (ns_ident_split(p.a, &hi, &lo) != 1) return false;
+  NsJob job{j.x, j.d, j.w.ns, j.scale, j.batch, j.m, j.n};
+  job.xtbl = j.xtbl;
+  job.xper = j.xper;
+  if (!gf_plan(job, p, f.gf, true) || !f.gf.gram.c_low) return false;
+  const bool wide = j.m <= j.n;
+  const int r = wide ? j.m : j.n;
+  const int64_t rr = (int64_t)r * r, mn = (int64_t)j.m * j.n;
+  const bf16_t* qb = static_cast<const bf16_t*>(j.w.ns.amat);
+  const bf16_t* xb = static_cast<const bf16_t*>(j.x);
+  const int tb = j.xtbl ? 1 : 0;
+  NsgGroup& ap = f.ap;
+  std::memset(&ap, 0, sizeof(ap));
+  if (wide) {
+    ap.a = qb; ap.lda = r; ap.sa = rr;
+    ap.b = xb; ap.ldb = j.n; ap.sb = mn; ap.b_kr = 1; ap.b_tbl = tb;
+  } else {
+    ap.a = xb; ap.lda = j.n; ap.sa = mn; ap.a_tbl = tb;
+    ap.b = qb; ap.ldb = r; ap.sb = rr;
+  }
+  ap.tbl = j.xtbl; ap.tbl_per = j.xper;
+  ap.c = static_cast<bf16_t*>(j.d); ap.ldc = j.n; ap.sc = mn;
+  ap.scale = j.scale; ap.alpha_pow = j.scale ? 1 : 0; ap.alpha = 1.f;
+  ap.M = j.m; ap.N = j.n; ap.K = r; ap.batch = j.batch;
+  ap.pred = j.w.hc;
+  NsgGroup& pr = f.pr;
+  std::memset(&pr, 0, sizeof(pr));
+  const bf16_t* db = static_cast<const bf16_t*>(j.d);
+  pr.a = db; pr.lda = j.n; pr.sa = mn; pr.a_kr = wide ? 0 : 1;
+  pr.b = db; pr.ldb = j.n; pr.sb = mn; pr.b_kr = wide ? 0 : 1;
+  pr.alpha = 1.f;
+  pr.M = r; pr.N = r; pr.K = wide ? j.n : j.m; pr.batch = j.batch; pr.sym = 1;
+  pr.resid = j.w.resid;
+  return gemm_ns_supported(ap) && gemm_ns_supported(pr);
+}
+
+// The generic route's candidate: D_hat = s * Q x (s * x Q^T for a tall x) and
+// the residual partials of D_hat D_hat^T - I, for the problems with a cache.
+sm_status gram_generic_candidate(const GramJob& j, int dt, hipStream_t s) {
+  GemmArgs g = apply_args(j.qtbl.p[0], F32, 1, j.x, dt, j.batch, j.m, j.n);
+  g.tbl = j.qtbl; g.tbl_per = j.qper;
+  g.c = j.d; g.ldc = j.n; g.sc = (int64_t)j.m * j.n; g.c_dt = dt;
+  g.scale = j.scale; g.alpha_pow = 1;
+  g.pred = j.w.hc; g.pred_stride = 1; g.pred_val = 1;
+  SM_TRY(launch_gemm(g, dt, SM_K_GEMM_APPLY, s));
+  GemmArgs pr = gram_args(j.d, dt, j.batch, j.m, j.n);
+  pr.resid = j.w.resid;
+  pr.pred = j.w.hc; pr.pred_stride = 1; pr.pred_val = 1;
+  return launch_gemm(pr, dt, SM_K_PROBE, s);
+}
+
+// The generic route's fresh Gram-NS, predicated on the decision flags:
+// G_0 = X X^T, P_k = aI + B_k with B_k = b G_k + c G_k^2, Q_{k+1} = a Q_k +
+// B_k Q_k, G_{k+1} = a T_k + T_k B_k with T_k = a G_k + B_k G_k, D = Q_K X.
+// The identity parts are added in float32 in the GEMM epilogues; Q_K is
+// written straight into the cache.
+sm_status gram_generic_fresh(const GramJob& j, int dt, const sm_ns_params& p, hipStream_t s) {
+  const GramWs& w = j.w;
+  const PtrTbl& qtbl = j.qtbl;
+  const int qper = j.qper, batch = j.batch, m = j.m, n = j.n;
+  const void* x = j.x;
+  const int r = m <= n ? m : n;
   const int64_t rr = (int64_t)r * r;
   const int K = p.iters;
   const bool quintic = p.c != 0.f;
-
-  SM_TRY(launch_gather_has_cache(cstbl, qper, batch, w.hc, s));
-  // bf16 and cubic with a one-term identity: the candidate, its probe and
-  // the fresh solve run on the persistent MFMA kernels when they take the
-  // shapes (the fresh solve as the lower-stored Gram-form chain)
-  GfPlan gf;
-  bool fast = false;
-  if (dt == BF16 && !quintic && K >= 2) {
-    uint32_t hi = 0, lo = 0;
-    const NsJob job{x, d, w.ns, scale, batch, m, n};
-    fast = ns_ident_split(p.a, &hi, &lo) == 1 && gf_plan(job, p, gf, true) && gf.gram.c_low;
-  }
-  auto any_of = [&](const int32_t* flags, int32_t* out) {
-    FlagSets fs;
-    std::memset(&fs, 0, sizeof(fs));
-    fs.f[0] = flags;
-    fs.n[0] = batch;
-    fs.count = 1;
-    return launch_any_flags(fs, out, s);
-  };
-  int parts = gemm_tiles(dt, r, r);
-  if (fast && mode != 1) {
-    // candidate D_hat = s Q x (x Q^T when tall) with Q rounded to bf16 (the
-    // operand type the generic kernel would round it to), then the residual
-    // partials of D_hat D_hat^T - I; problems without a cache skip both
-    SM_TRY(any_of(w.hc, w.any_hc));
-    bf16_t* qb = static_cast<bf16_t*>(w.ns.amat);
-    SM_TRY(launch_q_load(qtbl, qper, r, qb, rr, w.hc, batch, s));
-    const int64_t mn = (int64_t)m * n;
-    NsgGroup ap;
-    std::memset(&ap, 0, sizeof(ap));
-    if (wide) {
-      ap.a = qb; ap.lda = r; ap.sa = rr;
-      ap.b = static_cast<const bf16_t*>(x); ap.ldb = n; ap.sb = mn; ap.b_kr = 1;
-    } else {
-      ap.a = static_cast<const bf16_t*>(x); ap.lda = n; ap.sa = mn;
-      ap.b = qb; ap.ldb = r; ap.sb = rr;
-    }
-    ap.c = static_cast<bf16_t*>(d); ap.ldc = n; ap.sc = mn;
-    ap.scale = scale; ap.alpha_pow = scale ? 1 : 0; ap.alpha = 1.f;
-    ap.M = m; ap.N = n; ap.K = r; ap.batch = batch;
-    ap.pred = w.hc;
-    NsgGroup pr;
-    std::memset(&pr, 0, sizeof(pr));
-    pr.a = static_cast<const bf16_t*>(d); pr.lda = n; pr.sa = mn; pr.a_kr = wide ? 0 : 1;
-    pr.b = static_cast<const bf16_t*>(d); pr.ldb = n; pr.sb = mn; pr.b_kr = wide ? 0 : 1;
-    pr.alpha = 1.f;
-    pr.M = r; pr.N = r; pr.K = wide ? n : m; pr.batch = batch; pr.sym = 1;
-    pr.resid = w.resid;
-    if (gemm_ns_supported(ap) && gemm_ns_supported(pr)) {
-      std::vector<NsgGroup> v{ap};
-      SM_TRY(launch_ns_groups(v, SM_K_GEMM_APPLY, s, w.any_hc));
-      v = {pr};
-      SM_TRY(launch_ns_groups(v, SM_K_PROBE, s, w.any_hc));
-      parts = ns_probe_parts(r);
-    } else {
-      fast = false;
-    }
-  }
-  if (!fast && mode != 1) {
-    // candidate D_hat = s * Q x  (x^T oriented: s * x Q^T for a tall x)
-    GemmArgs g = apply_args(qtbl.p[0], F32, 1, x, dt, batch, m, n);
-    g.tbl = qtbl; g.tbl_per = qper;
-    g.c = d; g.ldc = n; g.sc = (int64_t)m * n; g.c_dt = dt;
-    g.scale = scale; g.alpha_pow = 1;
-    g.pred = w.hc; g.pred_stride = 1; g.pred_val = 1;
-    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_APPLY, s));
-    // residual partials of D_hat D_hat^T - I
-    GemmArgs pr = gram_args(d, dt, batch, m, n);
-    pr.resid = w.resid;
-    pr.pred = w.hc; pr.pred_stride = 1; pr.pred_val = 1;
-    SM_TRY(launch_gemm(pr, dt, SM_K_PROBE, s));
-  }
-  SM_TRY(launch_cache_decide(w.resid, parts, batch, r, w.hc, cstbl, qper, mode, gamma, t,
-                             w.flags, err_out, refr_out, diag, s));
-  if (fast) {
-    SM_TRY(any_of(w.flags, w.any));
-    return gram_fresh_gf(gf, w.flags, w.any, w.dyn, qtbl, qper, s);
-  }
-
   // Q_k lives in the cache for k == K (mod 2) so that Q_K lands there.
   auto qbuf_is_cache = [&](int k) { return ((K - k) % 2) == 0; };
   auto set_q_out = [&](GemmArgs& g, int k) {  // write Q_k as output c
@@ -1018,7 +1019,7 @@ sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cs
     GemmArgs g = gram_args(x, dt, batch, m, n);
     pred_fresh(g);
     g.c = w.ga; g.ldc = r; g.sc = rr; g.c_dt = F32;
-    g.scale = scale; g.alpha_pow = 2;
+    g.scale = j.scale; g.alpha_pow = 2;
     if (!quintic) {
       if (qbuf_is_cache(1)) { g.c2 = reinterpret_cast<float*>(const_cast<char*>(qtbl.p[0])); g.c2_tbl = 1; }
       else { g.c2 = w.qt; g.c2_tbl = 0; }
@@ -1085,14 +1086,92 @@ sm_status gram_core(const void* x, void* d, const PtrTbl& qtbl, const PtrTbl& cs
     float* tmp = gprev; gprev = gnew; gnew = tmp;
   }
   // D = s * Q_K x
-  {
-    GemmArgs g = apply_args(qtbl.p[0], F32, 1, x, dt, batch, m, n);
-    pred_fresh(g);
-    g.c = d; g.ldc = n; g.sc = (int64_t)m * n; g.c_dt = dt;
-    g.scale = scale; g.alpha_pow = 1;
-    SM_TRY(launch_gemm(g, dt, SM_K_GEMM_APPLY, s));
+  GemmArgs g = apply_args(qtbl.p[0], F32, 1, x, dt, batch, m, n);
+  pred_fresh(g);
+  g.c = j.d; g.ldc = n; g.sc = (int64_t)m * n; g.c_dt = dt;
+  g.scale = j.scale; g.alpha_pow = 1;
+  return launch_gemm(g, dt, SM_K_GEMM_APPLY, s);
+}
+
+// CacheMuon's orthogonalisation of every problem of the jobs,
+// [CacheMuon-ja] core mechanism:
+//   candidate (if cached): D_hat = Q X, err = ||D_hat D_hat^T - I||_F / sqrt(r)
+//   refresh iff no cache / forced / err > gamma, decided on the device;
+//   fresh Gram-NS for the refreshed problems only.
+// Jobs on the persistent kernels share their candidate launches (one apply
+// and one probe launch for all of them, gated by one device flag: some
+// problem has a cache); each job's decision and fresh solve are its own.
+sm_status gram_jobs(const std::vector<GramJob>& jobs, int dt, const sm_ns_params& p, float gamma,
+                    int mode, int64_t t, hipStream_t s) {
+  const size_t nj = jobs.size();
+  std::vector<GramFast> fp(nj);
+  std::vector<char> fast(nj, 0);
+  for (size_t i = 0; i < nj; ++i) {
+    fast[i] = gram_fast_plan(jobs[i], dt, p, fp[i]);
+    if (!fast[i] && (jobs[i].xtbl || !jobs[i].x)) return SM_ERR_UNSUPPORTED;
+  }
+  for (const GramJob& j : jobs)
+    SM_TRY(launch_gather_has_cache(j.cstbl, j.qper, j.batch, j.w.hc, s));
+  if (mode != 1) {
+    FlagSets fs;
+    std::memset(&fs, 0, sizeof(fs));
+    std::vector<NsgGroup> ap, pr;
+    int32_t* any_hc = nullptr;
+    for (size_t i = 0; i < nj; ++i) {
+      if (!fast[i]) continue;
+      if (fs.count == kTbl) return SM_ERR_UNSUPPORTED;
+      fs.f[fs.count] = jobs[i].w.hc;
+      fs.n[fs.count] = jobs[i].batch;
+      ++fs.count;
+      if (!any_hc) any_hc = jobs[i].w.any_hc;
+      ap.push_back(fp[i].ap);
+      pr.push_back(fp[i].pr);
+    }
+    if (any_hc) {
+      SM_TRY(launch_any_flags(fs, any_hc, s));
+      for (size_t i = 0; i < nj; ++i) {
+        if (!fast[i]) continue;
+        const GramJob& j = jobs[i];
+        const int r = j.m <= j.n ? j.m : j.n;
+        SM_TRY(launch_q_load(j.qtbl, j.qper, r, static_cast<bf16_t*>(j.w.ns.amat),
+                             (int64_t)r * r, j.w.hc, j.batch, s));
+      }
+      SM_TRY(launch_ns_groups(ap, SM_K_GEMM_APPLY, s, any_hc));
+      SM_TRY(launch_ns_groups(pr, SM_K_PROBE, s, any_hc));
+    }
+    for (size_t i = 0; i < nj; ++i)
+      if (!fast[i]) SM_TRY(gram_generic_candidate(jobs[i], dt, s));
+  }
+  for (size_t i = 0; i < nj; ++i) {
+    const GramJob& j = jobs[i];
+    const int r = j.m <= j.n ? j.m : j.n;
+    const int parts = fast[i] ? ns_probe_parts(r) : gemm_tiles(dt, r, r);
+    SM_TRY(launch_cache_decide(j.w.resid, parts, j.batch, r, j.w.hc, j.cstbl, j.qper, mode,
+                               gamma, t, j.w.flags, j.err_out, j.refr_out,
+                               j.has_diag ? &j.diag : nullptr, s));
+  }
+  for (size_t i = 0; i < nj; ++i) {
+    const GramJob& j = jobs[i];
+    if (fast[i]) {
+      FlagSets fs;
+      std::memset(&fs, 0, sizeof(fs));
+      fs.f[0] = j.w.flags;
+      fs.n[0] = j.batch;
+      fs.count = 1;
+      SM_TRY(launch_any_flags(fs, j.w.any, s));
+      SM_TRY(gram_fresh_gf(fp[i].gf, j.w.flags, j.w.any, j.w.dyn, j.qtbl, j.qper, s));
+    } else {
+      SM_TRY(gram_generic_fresh(j, dt, p, s));
+    }
   }
   return SM_OK;
+}
+
+// Whether a step's CacheMuon chunk can read its momenta in place (the
+// persistent-kernel route takes it with the pointer table).
+bool gram_in_place_ok(const GramJob& j, int dt, const sm_ns_params& p) {
+  GramFast f;
+  return gram_fast_plan(j, dt, p, f);
 }
 
 // ------------------------------------------------------------------ step planning
@@ -1364,9 +1443,22 @@ sm_status sm_gram_ns_cached(const void* x, void* d, float* q, int32_t* cache_sta
     SM_TRY(launch_sumsq(x, dt, batch, (int64_t)m * n, partials, s));
     SM_TRY(launch_scale_finalize(partials, batch, (int64_t)m * n, p->eps, scale, s));
   }
-  const PtrTbl qt = tbl_one(q), cs = tbl_one(cache_state);
-  return gram_core(x, d, qt, cs, batch, err, refreshed, nullptr, w,
-                   normalize ? scale : nullptr, dt, batch, m, n, *p, gamma, mode, t, s);
+  GramJob j;
+  std::memset(&j, 0, sizeof(j));
+  j.x = x;
+  j.xper = 1;
+  j.d = d;
+  j.qtbl = tbl_one(q);
+  j.cstbl = tbl_one(cache_state);
+  j.qper = batch;
+  j.err_out = err;
+  j.refr_out = refreshed;
+  j.w = w;
+  j.scale = normalize ? scale : nullptr;
+  j.batch = batch;
+  j.m = m;
+  j.n = n;
+  return gram_jobs(std::vector<GramJob>{j}, dt, *p, gamma, mode, t, s);
 }
 
 sm_status sm_sign_pack(const void* x, int dt, int64_t count, uint64_t* bits, hipStream_t s) {
@@ -1496,6 +1588,7 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     int nc, B;
     int64_t count, words;
     NsJob job;          // direct NS of this chunk
+    GramJob gjob;       // CacheMuon: the chunk's orthogonalisation
     bool grouped;       // job runs in the grouped launches
     bool fused_signs;   // its last product writes the packed signs (no a7/a8 launch)
   };
@@ -1528,6 +1621,32 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     // exists as the copy a1 writes.
     r.grouped = false;
     r.fused_signs = false;
+    if (c->algo == SM_CACHE_MUON) {
+      // diag rows follow the caller's matrix order: the chunk's matrix j
+      // (any position in that order) has its M rows at diag + mats[j]*M*2
+      GramJob& g = r.gjob;
+      std::memset(&g, 0, sizeof(g));
+      g.d = r.w.d;
+      g.qtbl = r.qt;
+      g.cstbl = r.cs;
+      g.qper = M;
+      g.has_diag = diag != nullptr;
+      for (int j = 0; diag && j < r.nc; ++j)
+        g.diag.p[j] = reinterpret_cast<const char*>(diag + (int64_t)ch.mats[j] * M * 2);
+      g.w = r.w.gram;
+      g.scale = r.w.scale;
+      g.batch = r.B;
+      g.m = ch.m;
+      g.n = ch.n;
+      // the momenta read in place where the persistent kernels take the chunk
+      g.xtbl = &r.mom;
+      g.xper = M;
+      if (!gram_in_place_ok(g, c->mdt, c->ns)) {
+        g.xtbl = nullptr;
+        g.xper = 1;
+        g.x = r.w.x0;
+      }
+    }
     if (muon_step && c->algo != SM_CACHE_MUON) {
       r.job = NsJob{r.w.x0, r.w.d, r.w.ns, r.w.scale, r.B, ch.m, ch.n};
       if (c->algo == SM_SIGN_MUON) {
@@ -1579,7 +1698,8 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     std::vector<EmaMat> ema;
     for (size_t ci = 0; ci < chunks.size(); ++ci) {
       ChunkRun& r = runs[ci];
-      void* x0 = r.job.xtbl ? nullptr : r.w.x0;   // no copy when NS reads M
+      // no copy when the NS reads M in place
+      void* x0 = (r.job.xtbl || (c->algo == SM_CACHE_MUON && r.gjob.xtbl)) ? nullptr : r.w.x0;
       for (int j = 0; j < r.nc; ++j) {
         EmaMat e;
         e.mom = const_cast<char*>(r.mom.p[j]);
@@ -1599,24 +1719,16 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
   // together (one launch per product kind and iteration).
   if (muon_step) {
     std::vector<NsJob> grouped, generic;
+    std::vector<GramJob> gjobs;
     for (size_t ci = 0; ci < chunks.size(); ++ci) {
-      const Chunk& ch = chunks[ci];
       ChunkRun& r = runs[ci];
-      if (c->algo == SM_CACHE_MUON) {
-        // diag rows follow the caller's matrix order: the chunk's matrix j
-        // (any position in that order) has its M rows at diag + mats[j]*M*2
-        PtrTbl dt;
-        std::memset(&dt, 0, sizeof(dt));
-        for (int j = 0; diag && j < r.nc; ++j)
-          dt.p[j] = reinterpret_cast<const char*>(diag + (int64_t)ch.mats[j] * M * 2);
-        SM_TRY(gram_core(r.w.x0, r.w.d, r.qt, r.cs, M, nullptr, nullptr, diag ? &dt : nullptr,
-                         r.w.gram,
-                         r.w.scale, c->mdt, r.B, ch.m, ch.n, c->ns, c->gamma, c->cache_mode, t,
-                         s));
-        continue;
-      }
-      (r.grouped ? grouped : generic).push_back(r.job);
+      if (c->algo == SM_CACHE_MUON)
+        gjobs.push_back(r.gjob);
+      else
+        (r.grouped ? grouped : generic).push_back(r.job);
     }
+    if (!gjobs.empty())
+      SM_TRY(gram_jobs(gjobs, c->mdt, c->ns, c->gamma, c->cache_mode, t, s));
     if (!grouped.empty()) SM_TRY(ns_grouped(grouped, c->ns, s));
     if (!generic.empty()) SM_TRY(ns_generic(generic, c->mdt, c->ns, s));
   }

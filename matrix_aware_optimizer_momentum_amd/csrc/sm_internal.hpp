@@ -419,8 +419,9 @@ int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
 // gate (optional device int32): when it holds 0 at launch time the whole
 // launch does nothing (the fresh solve of a CacheMuon step that refreshes
 // no problem).  dyn (optional device int32 [1 + batch]): only the dyn[0]
-// problems dyn[1 ..] run (every group must have the same batch and no
-// pointer tables); the others are neither computed nor stored.
+// problems dyn[1 ..] run (every group must have the same batch; pointer
+// tables are addressed by the listed problem); the others are neither
+// computed nor stored.
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s,
                          const int32_t* gate = nullptr, const int32_t* dyn = nullptr);
 // dyn[0] = the number of problems b < n with flags[b] == 1, dyn[1 ..] = those
