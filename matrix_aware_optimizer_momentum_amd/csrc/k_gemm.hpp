@@ -10,7 +10,9 @@
 // step share a launch and fill the chip together.
 //
 // Block tile 128 x 128, 256 threads = 4 waves in a 2 x 2 arrangement, each
-// wave owning a 64 x 64 sub-tile as 2 x 2 blocks of 32 x 32 MFMA outputs.
+// wave owning a 64 x 64 sub-tile as 2 x 2 blocks of 32 x 32 MFMA outputs; a
+// float32 launch too small to fill the chip with such tiles takes 64 x 64
+// tiles (one 32 x 32 block per wave) instead.
 // Operands are staged through LDS as [row][k] (k contiguous) in the MFMA
 // input type, so every fragment is one 16-byte (bf16) or 8-byte (f32) LDS
 // read.  A KC operand (k contiguous in HBM) is copied with 16-byte loads; an
@@ -38,7 +40,7 @@ namespace gemm {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;
+constexpr int BM = 128;      // block tile (the small-problem float32 variant uses 64)
 constexpr int BN = 128;
 constexpr int NT = 256;
 constexpr int kGemmMaxGroups = 8;
@@ -73,15 +75,16 @@ template <> struct Conv<bf16_t, float> {
 // type and writes them to an LDS stage.  Between the two the loads are in
 // flight.
 
-template <typename TG, typename TM, int LAY> struct Stage;
+template <typename TG, typename TM, int LAY, int T> struct Stage;
 
-// KC operand: tile rows [r0, r0+128), k in [k0, k0+BK), element (r, k) at
+// KC operand: tile rows [r0, r0+T), k in [k0, k0+BK), element (r, k) at
 // base[r*ld + k].  Each thread moves NV vectors of VEC consecutive k.
-template <typename TG, typename TM> struct Stage<TG, TM, KC> {
+template <typename TG, typename TM, int T> struct Stage<TG, TM, KC, T> {
   static constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
   static constexpr int VEC = 16 / sizeof(TM);   // elements per 16-byte LDS write
   static constexpr int VPR = BK / VEC;          // vectors per row (4)
-  static constexpr int NV = (BM * VPR) / NT;    // vectors per thread (2)
+  static constexpr int NV = (T * VPR) / NT;     // vectors per thread (2 for T = 128)
+  static_assert(NV >= 1, "every thread moves a vector");
   static_assert((VEC * sizeof(TG)) % 16 == 0, "whole 16-byte global loads");
   __attribute__((aligned(16))) TG raw[NV][VEC];
 
@@ -122,19 +125,22 @@ template <typename TG, typename TM> struct Stage<TG, TM, KC> {
   }
 };
 
-// RC operand: tile rows [r0, r0+128), k in [k0, k0+BK), element (r, k) at
+// RC operand: tile rows [r0, r0+T), k in [k0, k0+BK), element (r, k) at
 // base[k*ld + r].  Each thread loads KV consecutive k for 2 adjacent rows and
-// writes them as two [row][k] vectors.
-template <typename TG, typename TM> struct Stage<TG, TM, RC> {
+// writes them as two [row][k] vectors (for T = 64 half the threads have a
+// chunk).
+template <typename TG, typename TM, int T> struct Stage<TG, TM, RC, T> {
   static constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
   static constexpr int KV = 16 / sizeof(TM);  // k per LDS vector: 8 (bf16) or 4 (f32)
-  static_assert((BK / KV) * (BM / 2) == NT, "one chunk per thread");
+  static constexpr int CHUNKS = (BK / KV) * (T / 2);
+  static_assert(CHUNKS == NT || CHUNKS == NT / 2, "at most one chunk per thread");
   TG v0[KV], v1[KV];
 
   __device__ __forceinline__ void load(const TG* __restrict__ base, int64_t ld, int r0,
                                        int rows, int k0, int K, bool fast) {
-    const int rc = (threadIdx.x % (BM / 2)) * 2;
-    const int kc = (threadIdx.x / (BM / 2)) * KV;
+    if (CHUNKS < NT && (int)threadIdx.x >= CHUNKS) return;
+    const int rc = (threadIdx.x % (T / 2)) * 2;
+    const int kc = (threadIdx.x / (T / 2)) * KV;
     if (fast) {
       const TG* src = base + (int64_t)(k0 + kc) * ld + (r0 + rc);
 #pragma unroll
@@ -166,8 +172,9 @@ template <typename TG, typename TM> struct Stage<TG, TM, RC> {
     }
   }
   __device__ __forceinline__ void store(TM* S) const {
-    const int rc = (threadIdx.x % (BM / 2)) * 2;
-    const int kc = (threadIdx.x / (BM / 2)) * KV;
+    if (CHUNKS < NT && (int)threadIdx.x >= CHUNKS) return;
+    const int rc = (threadIdx.x % (T / 2)) * 2;
+    const int kc = (threadIdx.x / (T / 2)) * KV;
     __attribute__((aligned(16))) TM o0[KV];
     __attribute__((aligned(16))) TM o1[KV];
 #pragma unroll
@@ -186,20 +193,23 @@ template <typename TG, typename TM> struct Stage<TG, TM, RC> {
 
 template <typename TM> struct Mma;
 
+// A wave owns WB x WB output blocks of 32 x 32 (WB = 2 for the 128 tile, 1
+// for the 64 tile).
 template <> struct Mma<bf16_t> {
   // k-groups of 16: fragments are 8 consecutive k at offset 8*(lane/32).  The
   // next group's fragments are read before this group's MFMAs go out.
+  template <int WB>
   __device__ __forceinline__ static void step(const bf16_t* As, const bf16_t* Bs, int wm,
-                                              int wn, f32x16 (&acc)[2][2]) {
+                                              int wn, f32x16 (&acc)[WB][WB]) {
     constexpr int LDK = Cfg<bf16_t>::LDK, BK = Cfg<bf16_t>::BK;
     constexpr int NG = BK / 16;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
-    const bf16_t* pa = As + (wm * 64 + lr) * LDK + lk * 8;
-    const bf16_t* pb = Bs + (wn * 64 + lr) * LDK + lk * 8;
-    bf16x8 af[2][2], bfg[2][2];
+    const bf16_t* pa = As + (wm * 32 * WB + lr) * LDK + lk * 8;
+    const bf16_t* pb = Bs + (wn * 32 * WB + lr) * LDK + lk * 8;
+    bf16x8 af[2][WB], bfg[2][WB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WB; ++i) {
       af[0][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * LDK);
       bfg[0][i] = *reinterpret_cast<const bf16x8*>(pb + i * 32 * LDK);
     }
@@ -208,16 +218,16 @@ template <> struct Mma<bf16_t> {
       const int c = g & 1, n = c ^ 1;
       if (g + 1 < NG) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < WB; ++i) {
           af[n][i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * LDK + (g + 1) * 16);
           bfg[n][i] = *reinterpret_cast<const bf16x8*>(pb + i * 32 * LDK + (g + 1) * 16);
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // the reads go out ahead of the MFMAs
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < WB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfg[c][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -228,17 +238,18 @@ template <> struct Mma<float> {
   // k-groups of 4, each two 32x32x2 MFMAs per output block: lane supplies
   // k = 4 g + 2*(lane/32) + {0,1}.  The next group's fragments are read
   // before this group's MFMAs go out.
+  template <int WB>
   __device__ __forceinline__ static void step(const float* As, const float* Bs, int wm, int wn,
-                                              f32x16 (&acc)[2][2]) {
+                                              f32x16 (&acc)[WB][WB]) {
     constexpr int LDK = Cfg<float>::LDK, BK = Cfg<float>::BK;
     constexpr int NG = BK / 4;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
-    const float* pa = As + (wm * 64 + lr) * LDK + lk * 2;
-    const float* pb = Bs + (wn * 64 + lr) * LDK + lk * 2;
-    float2 af[2][2], bfg[2][2];
+    const float* pa = As + (wm * 32 * WB + lr) * LDK + lk * 2;
+    const float* pb = Bs + (wn * 32 * WB + lr) * LDK + lk * 2;
+    float2 af[2][WB], bfg[2][WB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WB; ++i) {
       af[0][i] = *reinterpret_cast<const float2*>(pa + i * 32 * LDK);
       bfg[0][i] = *reinterpret_cast<const float2*>(pb + i * 32 * LDK);
     }
@@ -247,16 +258,16 @@ template <> struct Mma<float> {
       const int c = g & 1, n = c ^ 1;
       if (g + 1 < NG) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < WB; ++i) {
           af[n][i] = *reinterpret_cast<const float2*>(pa + i * 32 * LDK + (g + 1) * 4);
           bfg[n][i] = *reinterpret_cast<const float2*>(pb + i * 32 * LDK + (g + 1) * 4);
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // the reads go out ahead of the MFMAs
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < WB; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[c][i].x, bfg[c][j].x, acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[c][i].y, bfg[c][j].y, acc[i][j], 0, 0, 0);
         }
@@ -293,11 +304,15 @@ __device__ __forceinline__ const char* prob_base(const KArgs& ka, const GemmCore
 
 // ROLE (the SM_K_GEMM_* / SM_K_PROBE kind) changes no code; it gives each
 // role its own kernel symbol so per-kernel profiles attribute time by role.
-template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE>
+// T: the square block tile (128, or 64 for launches too small to fill the
+// chip with 128 tiles), a wave owning (T / 2)^2 of it.
+template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE, int T>
 __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
-  __shared__ __attribute__((aligned(16))) TM As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) TM Bs[2][BN * LDK];
+  constexpr int WB = T / 64;   // 32 x 32 blocks per wave and dimension
+  constexpr int WT = T / 2;    // wave sub-tile
+  __shared__ __attribute__((aligned(16))) TM As[2][T * LDK];
+  __shared__ __attribute__((aligned(16))) TM Bs[2][T * LDK];
   __shared__ float red[4];
   int gi = 0;
   while (gi + 1 < ka.ngroups && (int)blockIdx.x >= ka.grp[gi + 1].blk_begin) ++gi;
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
     tn = tile % kg.tiles_n;
   }
   const bool mirror = g.sym && tm != tn;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * T, n0 = tn * T;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -332,19 +347,19 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   const TB* B =
       reinterpret_cast<const TB*>(prob_base(ka, g, g.b.p, g.b.tbl, g.b.stride, sizeof(TB), b));
 
-  f32x16 acc[2][2];
+  f32x16 acc[WB][WB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const bool a_fast_rows = kg.a_aligned && (m0 + BM) <= g.M;
-  const bool b_fast_rows = kg.b_aligned && (n0 + BN) <= g.N;
+  const bool a_fast_rows = kg.a_aligned && (m0 + T) <= g.M;
+  const bool b_fast_rows = kg.b_aligned && (n0 + T) <= g.N;
   const int nk = (g.K + BK - 1) / BK;
-  Stage<TA, TM, LA> sa;
-  Stage<TB, TM, LB> sb;
+  Stage<TA, TM, LA, T> sa;
+  Stage<TB, TM, LB, T> sb;
   sa.load(A, g.a.ld, m0, g.M, 0, g.K, a_fast_rows && BK <= g.K);
   sb.load(B, g.b.ld, n0, g.N, 0, g.K, b_fast_rows && BK <= g.K);
   sa.store(As[0]);
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
       sa.load(A, g.a.ld, m0, g.M, k0, g.K, a_fast_rows && k_in);
       sb.load(B, g.b.ld, n0, g.N, k0, g.K, b_fast_rows && k_in);
     }
-    Mma<TM>::step(As[cur], Bs[cur], wm, wn, acc);
+    Mma<TM>::template step<WB>(As[cur], Bs[cur], wm, wn, acc);
     if (more) {
       // stage cur ^ 1 was last read by slab kt - 1, before the previous barrier
       sa.store(As[cur ^ 1]);
@@ -388,13 +403,13 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
                                    : nullptr;
   float rs = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
-        const int col = n0 + wn * 64 + j * 32 + lr;
+        const int row = m0 + wm * WT + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
+        const int col = n0 + wn * WT + j * 32 + lr;
         float stored = 0.f;
         if (row < g.M && col < g.N) {
           float val = alpha * acc[i][j][v];
@@ -431,23 +446,37 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   if (g.bits) {
     // Signs of the stored values, packed: for fixed (i, v) the ballot over
     // the wave of block j holds row R (lanes 0-31) and row R + 4 (lanes
-    // 32-63), columns c0 + 32 j + lane % 32, with c0 = n0 + 64 wn a multiple
-    // of 64; N % 64 == 0 makes each (row, c0) span exactly one sign word.
-    uint64_t* bits_b = g.bits + (int64_t)b * g.bits_stride;
-    const int c0 = n0 + wn * 64;
+    // 32-63), columns c0 + 32 j + lane % 32, with c0 = n0 + WT wn.
+    // N % 64 == 0 makes each row's 64 columns from a multiple of 64 one sign
+    // word: with the 128 tile a wave covers a whole word (blocks j = 0, 1),
+    // with the 64 tile each wave its 32-bit half.
+    const int c0 = n0 + wn * WT;
+    if constexpr (WB == 2) {
+      uint64_t* bits_b = g.bits + (int64_t)b * g.bits_stride;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WB; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint64_t b0 = __ballot(acc[i][0][v] < 0.f);
+          const uint64_t b1 = __ballot(acc[i][1][v] < 0.f);
+          const int row = m0 + wm * WT + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
+          if (lr == 0 && row < g.M && c0 < g.N) {
+            const uint64_t w = lk == 0 ? ((b0 & 0xFFFFFFFFull) | (b1 << 32))
+                                       : ((b0 >> 32) | (b1 & 0xFFFFFFFF00000000ull));
+            bits_b[((int64_t)row * g.N + c0) >> 6] = w;
+          }
+        }
+    } else {
+      uint32_t* half_b = reinterpret_cast<uint32_t*>(g.bits + (int64_t)b * g.bits_stride);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const uint64_t b0 = __ballot(acc[i][0][v] < 0.f);
-        const uint64_t b1 = __ballot(acc[i][1][v] < 0.f);
-        const int row = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
-        if (lr == 0 && row < g.M && c0 < g.N) {
-          const uint64_t w = lk == 0 ? ((b0 & 0xFFFFFFFFull) | (b1 << 32))
-                                     : ((b0 >> 32) | (b1 & 0xFFFFFFFF00000000ull));
-          bits_b[((int64_t)row * g.N + c0) >> 6] = w;
-        }
+        const uint64_t b0 = __ballot(acc[0][0][v] < 0.f);
+        const int row = m0 + wm * WT + (v >> 2) * 8 + lk * 4 + (v & 3);
+        if (lr == 0 && row < g.M && n0 < g.N)
+          half_b[(((int64_t)row * g.N + n0) >> 6) * 2 + wn] =
+              lk == 0 ? (uint32_t)b0 : (uint32_t)(b0 >> 32);
       }
+    }
   }
   if (g.resid) {
 #pragma unroll
@@ -482,16 +511,15 @@ inline bool uses_tbl(const GemmArgs& g) {
 }
 
 // Launches n (<= kGemmMaxGroups) product sets of one operand-type / layout
-// combination; their tables must fit one launch table together (the caller,
-// launch_gemm_groups, packs them).
-template <typename TA, typename TB, typename TM, int LA, int LB>
-sm_status launch_t(const GemmArgs* gs, int n, int kind, hipStream_t s) {
+// combination with block tile T; their tables must fit one launch table
+// together (the caller, launch_gemm_groups, packs them).
+template <typename TA, typename TB, typename TM, int LA, int LB, int T>
+sm_status launch_tile(const GemmArgs* gs, int n, int kind, hipStream_t s) {
   KArgs ka;
   std::memset(&ka, 0, sizeof(ka));
   int nt = 0;        // launch table entries used
   int64_t blk = 0;
   double flops = 0.0, bytes = 0.0;
-  bool any_pred = false;
   ka.ngroups = n;
   for (int i = 0; i < n; ++i) {
     const GemmArgs& g = gs[i];
@@ -514,8 +542,8 @@ sm_status launch_t(const GemmArgs* gs, int n, int kind, hipStream_t s) {
     }
     k.a_aligned = operand_aligned(g, g.a);
     k.b_aligned = operand_aligned(g, g.b);
-    const int tiles_m = (g.M + BM - 1) / BM;
-    k.tiles_n = (g.N + BN - 1) / BN;
+    const int tiles_m = (g.M + T - 1) / T;
+    k.tiles_n = (g.N + T - 1) / T;
     k.tiles = g.sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * k.tiles_n;
     k.blk_begin = (int)blk;
     blk += (int64_t)k.tiles * g.batch;
@@ -527,7 +555,6 @@ sm_status launch_t(const GemmArgs* gs, int n, int kind, hipStream_t s) {
       k.g.prof_exec = prof_exec_slot(kind);
       k.g.prof_flops = fl;
       k.g.prof_bytes = by;
-      any_pred = any_pred || k.g.prof_exec;
     } else {
       k.g.prof_exec = nullptr;
       flops += fl * g.batch;
@@ -536,25 +563,43 @@ sm_status launch_t(const GemmArgs* gs, int n, int kind, hipStream_t s) {
   }
   if (blk == 0) return SM_OK;
   if (blk > 0x7FFFFFFF) return SM_ERR_SHAPE;
-  (void)any_pred;
   prof_begin(kind, flops, s, bytes);
   const dim3 grid((unsigned)blk);
   switch (kind) {
     case SM_K_GEMM_GRAM:
-      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_GRAM>), grid, dim3(NT), 0, s, ka);
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_GRAM, T>), grid, dim3(NT), 0, s, ka);
       break;
     case SM_K_GEMM_APPLY:
-      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_APPLY>), grid, dim3(NT), 0, s, ka);
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_APPLY, T>), grid, dim3(NT), 0, s, ka);
       break;
     case SM_K_PROBE:
-      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_PROBE>), grid, dim3(NT), 0, s, ka);
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_PROBE, T>), grid, dim3(NT), 0, s, ka);
       break;
     default:
-      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_RR>), grid, dim3(NT), 0, s, ka);
+      hipLaunchKernelGGL((k_gemm<TA, TB, TM, LA, LB, SM_K_GEMM_RR, T>), grid, dim3(NT), 0, s, ka);
       break;
   }
   prof_end(s);
   return check_launch();
+}
+
+// Float32 launches with fewer 128 x 128 tiles than two per CU take the 64
+// tile (four times the blocks, a quarter of the k-loop work each), unless a
+// set writes residual partials (they are laid out per 128 tile).
+template <typename TA, typename TB, typename TM, int LA, int LB>
+sm_status launch_t(const GemmArgs* gs, int n, int kind, hipStream_t s) {
+  if constexpr (sizeof(TM) == 4) {
+    int64_t blk = 0;
+    bool need128 = false;
+    for (int i = 0; i < n; ++i) {
+      const GemmArgs& g = gs[i];
+      const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
+      blk += (g.sym ? tm * (tm + 1) / 2 : tm * tn) * g.batch;
+      need128 = need128 || g.resid;
+    }
+    if (!need128 && blk < 2 * 256) return launch_tile<TA, TB, TM, LA, LB, 64>(gs, n, kind, s);
+  }
+  return launch_tile<TA, TB, TM, LA, LB, 128>(gs, n, kind, s);
 }
 
 }  // namespace gemm
