@@ -213,6 +213,21 @@ def test_sign_muon_step_more_matrices_than_one_ema_launch_takes(gpu_lib):
     _check_step(wl, _cfg(wl), st, 2, wl.mdt)
 
 
+def test_float32_step_more_shape_sets_than_one_gemm_launch_takes(gpu_lib):
+    """Ten wide float32 shapes of seven matrices each: the generic GEMM's
+    grouped launches split by their eight-set limit and by the 64-entry
+    pointer table the momenta are read through (70 matrices); signs are
+    fused into the apply for the shapes with n % 64 == 0 and packed by
+    their own launch otherwise.  Every matrix matches the oracle and its
+    entry-point chain."""
+    wl = W.WORKLOADS[3].scaled(M=2)
+    base = [(16, 64), (24, 72), (32, 96), (40, 128), (48, 64), (56, 120), (64, 64), (8, 200),
+            (72, 136), (80, 192)]
+    shapes = [sh for sh in base for _ in range(7)]
+    st = Seeded(wl, shapes)
+    _check_step(wl, _cfg(wl), st, 1, wl.mdt)
+
+
 @pytest.mark.parametrize("shapes,a,applies", [
     # square (direct, wide): its applies ride in the r x r launches
     ([(256, 256), (256, 1024), (1024, 256), (256, 256)], 1.5, 1),
