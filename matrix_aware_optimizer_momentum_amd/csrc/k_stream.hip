@@ -196,7 +196,7 @@ __device__ __forceinline__ void store_signs8(int8_t* s, int64_t e0, int64_t coun
 // thread's sum of squares of the stored x values.
 template <typename TM, typename TG, typename TX>
 __device__ __forceinline__ float ema_run(TM* m, const TG* g, TX* xo, int64_t count, float beta,
-                                         bool vec, int64_t part, int64_t nparts) {
+                                         bool vec, int64_t part, int64_t nparts, bool stream) {
   const float omb = 1.0f - beta;
   float acc = 0.f;
   const int64_t nchunks = (count + kChunk - 1) / kChunk;
@@ -204,7 +204,8 @@ __device__ __forceinline__ float ema_run(TM* m, const TG* g, TX* xo, int64_t cou
     const int64_t e0 = ci * kChunk + (int64_t)threadIdx.x * 8;
     if (e0 >= count) continue;
     float mv[8], gv[8];
-    load8_tail<TM>(m, e0, count, vec, mv);
+    if (stream) load8_once<TM>(m, e0, count, vec, mv);
+    else load8_tail<TM>(m, e0, count, vec, mv);
     load8_once<TG>(g, e0, count, vec, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -213,7 +214,8 @@ __device__ __forceinline__ float ema_run(TM* m, const TG* g, TX* xo, int64_t cou
       gv[e] = round_to<TX>(v);  // 0 beyond the end: both inputs load as 0
     }
     acc = sumsq8(acc, gv);
-    store8_tail<TM>(m, e0, count, vec, mv);
+    if (stream) store8_once<TM>(m, e0, count, vec, mv);
+    else store8_tail<TM>(m, e0, count, vec, mv);
     if (xo) store8_tail<TX>(xo, e0, count, vec, gv);
   }
   return acc;
@@ -222,7 +224,7 @@ __device__ __forceinline__ float ema_run(TM* m, const TG* g, TX* xo, int64_t cou
 // Problem b = matrix b / per, worker b % per; blocks past the problem's
 // norm_parts have nothing to do.
 template <typename TM, typename TG>
-__global__ __launch_bounds__(kThreads) void k_ema_tbl(EmaTbl t, int per, float beta) {
+__global__ __launch_bounds__(kThreads) void k_ema_tbl(EmaTbl t, int per, float beta, bool stream) {
   __shared__ float red[4];
   const int b = blockIdx.y, q = b / per, w = b - q * per;
   const EmaMat& e = t.m[q];
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_ema_tbl(EmaTbl t, int per, float b
   const TG* g = static_cast<const TG*>(e.grad) + (int64_t)w * e.count;
   TM* xo = e.x ? static_cast<TM*>(e.x) + (int64_t)w * e.count : nullptr;
   const float acc = ema_run<TM, TG, TM>(m, g, xo, e.count, beta, (e.count % 8) == 0,
-                                        blockIdx.x, parts);
+                                        blockIdx.x, parts, stream);
   float s = block_sum(acc, red);
   if (threadIdx.x == 0) e.partials[(int64_t)w * kNormParts + blockIdx.x] = s;
 }
@@ -596,7 +598,8 @@ __global__ __launch_bounds__(kThreads) void k_vote_tbl(VoteTbl t, int M, float l
 
 template <typename TD, typename TW>
 __global__ __launch_bounds__(kThreads) void k_polar_update(const TD* d, int64_t count,
-                                                           PtrTbl w, float lr, bool vec) {
+                                                           PtrTbl w, float lr, bool vec,
+                                                           bool stream) {
   const int j = blockIdx.y;
   const TD* dp = d + (int64_t)j * count;
   TW* wp = (TW*)w.p[j];
@@ -605,11 +608,17 @@ __global__ __launch_bounds__(kThreads) void k_polar_update(const TD* d, int64_t 
        i += (int64_t)gridDim.x * kThreads) {
     const int64_t e0 = 8 * i;
     float wv[8], dv[8];
-    load8_tail<TW>(wp, e0, count, vec, wv);
-    load8_tail<TD>(dp, e0, count, vec, dv);
+    if (stream) {   // large: past the caches (see kStreamBytes)
+      load8_once<TW>(wp, e0, count, vec, wv);
+      load8_once<TD>(dp, e0, count, vec, dv);
+    } else {
+      load8_tail<TW>(wp, e0, count, vec, wv);
+      load8_tail<TD>(dp, e0, count, vec, dv);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) wv[e] = __fsub_rn(wv[e], __fmul_rn(lr, dv[e]));
-    store8_tail<TW>(wp, e0, count, vec, wv);
+    if (stream) store8_once<TW>(wp, e0, count, vec, wv);
+    else store8_tail<TW>(wp, e0, count, vec, wv);
   }
 }
 
@@ -783,10 +792,13 @@ sm_status launch_ema_tbl(const EmaMat* mats, int nmat, int per, int mdt, int gdt
       bytes += (double)per * t.m[q].count *
                (2.0 * dt_size(mdt) + dt_size(gdt) + (t.m[q].x ? dt_size(mdt) : 0.0));
     }
+    double mbytes = 0.0;
+    for (int q = 0; q < n; ++q) mbytes += (double)per * t.m[q].count * dt_size(mdt);
+    const bool stream = mbytes > kStreamBytes;
     prof_begin(SM_K_EMA, bytes, s);
     SM_DISPATCH_DT(mdt, TM, SM_DISPATCH_DT(gdt, TG,
         hipLaunchKernelGGL((k_ema_tbl<TM, TG>), dim3(parts, n * per), dim3(kThreads), 0, s, t,
-                           per, beta)));
+                           per, beta, stream)));
     prof_end(s);
     SM_TRY(check_launch());
     if (finalize) {
@@ -959,10 +971,11 @@ sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, c
   int64_t want = (4096 + nmat - 1) / nmat;
   int64_t need = (n8 + kThreads - 1) / kThreads;
   dim3 grid((unsigned)(need < want ? need : want), nmat);
+  const bool stream = (double)nmat * count * dt_size(wdt) > kStreamBytes;
   prof_begin(SM_K_POLAR_UPDATE, (double)nmat * count * (dt_size(ddt) + 2.0 * dt_size(wdt)), s);
   SM_DISPATCH_DT(ddt, TD, SM_DISPATCH_DT(wdt, TW,
       hipLaunchKernelGGL((k_polar_update<TD, TW>), grid, dim3(kThreads), 0, s, (const TD*)d,
-                         count, w, lr, vec)));
+                         count, w, lr, vec, stream)));
   prof_end(s);
   return check_launch();
 }
