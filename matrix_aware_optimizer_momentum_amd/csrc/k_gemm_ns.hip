@@ -99,18 +99,20 @@ struct Grp {
   int64_t bits_stride;
   const int32_t* pred;         // per-problem store predicate (see NsgGroup), or null
   float* resid;                // probe: residual partials (see NsgGroup)
+  const int32_t* dyn;          // device problem list (see NsgGroup), or null
 };
 
 struct Args {
   Grp g[kNsgMaxGroups];
   PtrTbl tbl[kNsgMaxTables];
   const int32_t* gate;         // launch-wide: nothing to do while *gate == 0
-  // Problem list on the device, or null: dyn[0] problems run, the indices
-  // dyn[1 ..] (every group has the same problems); tiles are then laid out
-  // group by group over those problems only.
-  const int32_t* dyn;
+  // With device problem lists (Grp::dyn): the first tile of each group's
+  // listed problems and, at [kNsgMaxGroups], the launch's total, written by
+  // k_dyn_prefix before the launch; tiles are laid out group by group over
+  // the listed problems only.  Null: the static layout.
+  const int32_t* dyn_tiles;
   double* prof_exec;           // gated launch while profiling: work added here when it runs
-  double prof_flops, prof_bytes;   // per launch, or per listed problem with dyn
+  double prof_flops, prof_bytes;   // per launch
   int ngroups, total_tiles, xcd_chunk;
   int tpp_total;               // tiles per problem over all groups
 };
@@ -161,19 +163,43 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
   return v;
 }
 
-// Tile t of the launch; cnt < 0: the static layout, else the device problem
-// list with cnt problems (see Args::dyn).
-__device__ __forceinline__ Tile decode_tile(const Args& A, int t, int cnt) {
+// Eight wave-uniform int32 (32-byte aligned) through the scalar unit, as
+// sload_i32.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 sload_i32x8(const int32_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const int32_t* q = reinterpret_cast<const int32_t*>(((uint64_t)hi << 32) | lo);
+  i32x8 v;
+  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
+  return v;
+}
+
+// Tile t of the launch; dyn: the layout over the groups' device problem
+// lists (see Args::dyn_tiles), else the static one.
+__device__ __forceinline__ Tile decode_tile(const Args& A, int t, bool dyn) {
   Tile r;
-  int gi = 0;
+  int gi = 0, begin = 0;
+  if (dyn) {
+    const i32x8 first = sload_i32x8(A.dyn_tiles);
 #pragma unroll
-  for (int q = 1; q < kNsgMaxGroups; ++q)
-    if (q < A.ngroups && t >= (cnt < 0 ? A.g[q].tile_begin : cnt * A.g[q].tpp_begin)) gi = q;
+    for (int q = 1; q < kNsgMaxGroups; ++q)
+      if (q < A.ngroups && t >= first[q]) gi = q;
+#pragma unroll
+    for (int q = 0; q < kNsgMaxGroups; ++q)
+      if (q == gi) begin = first[q];
+  } else {
+#pragma unroll
+    for (int q = 1; q < kNsgMaxGroups; ++q)
+      if (q < A.ngroups && t >= A.g[q].tile_begin) gi = q;
+    begin = A.g[gi].tile_begin;
+  }
   const Grp& g = A.g[gi];
-  const int local = t - (cnt < 0 ? g.tile_begin : cnt * g.tpp_begin);
+  const int local = t - begin;
   r.gi = gi;
   const int pc = local / g.tiles_per_prob;
-  r.prob = cnt < 0 ? pc : sload_i32(A.dyn + 1 + pc);
+  r.prob = dyn ? sload_i32(g.dyn + 1 + pc) : pc;
   const int u = local - pc * g.tiles_per_prob;
   ns_tile_coords(u, g.tiles_m, g.tiles_n, g.sym, &r.tm, &r.tn);   // banded walk
   return r;
@@ -219,7 +245,7 @@ struct LoadPos {
   int kg;       // group of 4 stages within the tile
   int nkg;      // groups in the tile
   int sw;       // next group where a lower-stored operand turns to KR reads
-  int cnt;      // problems of a device problem list (-1: static layout)
+  int dyn;      // the layout over device problem lists (Args::dyn_tiles)
   int total;    // tiles of the launch
 };
 
@@ -240,7 +266,7 @@ __device__ __forceinline__ void load_tile_setup(LoadPos& L, const Args& A, int r
   t = __builtin_amdgcn_readfirstlane(t);
   r = __builtin_amdgcn_readfirstlane(r);
   kg = __builtin_amdgcn_readfirstlane(kg);
-  const Tile tl = decode_tile(A, t, L.cnt);
+  const Tile tl = decode_tile(A, t, L.dyn != 0);
   const Grp& g = A.g[tl.gi];
   // the group's table, addressed by its byte offset in the arguments (an
   // index into Args::tbl makes the compiler copy the arguments to scratch)
@@ -1005,16 +1031,16 @@ void k_gemm_ns(Args args) {
   int t = tile_of(0, vid, stride);
   if (t >= A.total_tiles) return;
   if (A.gate && scalar_load_i32(A.gate) == 0) return;   // uniform over the launch
-  int cnt = -1, total = A.total_tiles;
-  if (A.dyn) {
-    cnt = sload_i32(A.dyn);
-    total = cnt * A.tpp_total;
+  const bool dyn = A.dyn_tiles != nullptr;
+  int total = A.total_tiles;
+  if (dyn) {
+    total = sload_i32(A.dyn_tiles + kNsgMaxGroups);
     if (t >= total) return;
   }
-  if (A.prof_exec && blockIdx.x == 0 && threadIdx.x == 0) {
-    const double mult = A.dyn ? (double)cnt : 1.0;
-    atomicAdd(A.prof_exec, mult * A.prof_flops);
-    atomicAdd(A.prof_exec + 1, mult * A.prof_bytes);
+  // (with problem lists k_dyn_prefix credits the work of the listed problems)
+  if (A.prof_exec && !dyn && blockIdx.x == 0 && threadIdx.x == 0) {
+    atomicAdd(A.prof_exec, A.prof_flops);
+    atomicAdd(A.prof_exec + 1, A.prof_bytes);
   }
 
   const int wave = threadIdx.x >> 6;
@@ -1025,7 +1051,7 @@ void k_gemm_ns(Args args) {
   // prologue: the first tile's stages 0..3 into buffers 0..3; the load
   // position then moves one group ahead
   LoadPos LP;
-  LP.cnt = cnt;
+  LP.dyn = dyn ? 1 : 0;
   LP.total = total;
   load_tile_setup(LP, A, 0, t);
 #pragma unroll
@@ -1043,7 +1069,7 @@ void k_gemm_ns(Args args) {
 
   bool lenient = false;
   for (;;) {
-    const Tile tc = decode_tile(A, t, cnt);
+    const Tile tc = decode_tile(A, t, dyn);
     const Grp& g = A.g[tc.gi];
     const int nkg = g.K / (4 * BK);
     // this wave's 128 x 128 quarter (wm, wn) of the tile, derived again after
@@ -1168,6 +1194,41 @@ void k_gemm_ns(Args args) {
   wait_vm<0>();   // the loads past the last stage target this workgroup's LDS
 }
 
+// The tile layout of a launch over its groups' device problem lists: group
+// q's listed problems take tiles [out[q], out[q + 1]) (out[kNsgMaxGroups]:
+// the total; nothing when the gate holds 0), and the work of the listed
+// problems is credited to prof_exec while profiling.  One thread.
+struct DynPrefixArgs {
+  const int32_t* lists[kNsgMaxGroups];
+  int tpp[kNsgMaxGroups];
+  double flops[kNsgMaxGroups], bytes[kNsgMaxGroups];   // per listed problem
+  int ngroups;
+  const int32_t* gate;
+  int32_t* out;
+  double* prof_exec;
+};
+
+__global__ __launch_bounds__(64) void k_dyn_prefix(DynPrefixArgs a) {
+  if (threadIdx.x != 0) return;
+  const bool run = !a.gate || *a.gate != 0;
+  int off = 0;
+  double fl = 0.0, by = 0.0;
+  for (int q = 0; q < kNsgMaxGroups; ++q) {
+    a.out[q] = off;
+    if (q < a.ngroups && run) {
+      const int c = a.lists[q][0];
+      off += c * a.tpp[q];
+      fl += c * a.flops[q];
+      by += c * a.bytes[q];
+    }
+  }
+  a.out[kNsgMaxGroups] = off;
+  if (a.prof_exec && off > 0) {
+    atomicAdd(a.prof_exec, fl);
+    atomicAdd(a.prof_exec + 1, by);
+  }
+}
+
 }  // namespace nsg
 
 // ------------------------------------------------------------------ launcher
@@ -1267,9 +1328,13 @@ int ns_group_tables(const NsgGroup* groups, int ngroups) {
 }
 
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s,
-                         const int32_t* gate, const int32_t* dyn) {
+                         const int32_t* gate, int32_t* dyn_tiles) {
   using namespace nsg;
   if (ngroups <= 0 || ngroups > kNsgMaxGroups) return SM_ERR_ARG;
+  const bool dyn = groups[0].dyn != nullptr;
+  if (dyn && (!dyn_tiles || (reinterpret_cast<uintptr_t>(dyn_tiles) & 31u))) return SM_ERR_ARG;
+  DynPrefixArgs dp;
+  std::memset(&dp, 0, sizeof(dp));
   const bool apply = kind == SM_K_GEMM_APPLY;
   const bool probe = kind == SM_K_PROBE;
   if (!apply && !probe && kind != SM_K_GEMM_GRAM && kind != SM_K_GEMM_RR) return SM_ERR_ARG;
@@ -1356,9 +1421,9 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.tile_begin = tiles;
     g.tpp_begin = a.tpp_total;
     a.tpp_total += g.tiles_per_prob;
-    // a device problem list names the same problems in every group (pointer
-    // tables are addressed by the listed problem)
-    if (dyn && G.batch != groups[0].batch) return SM_ERR_UNSUPPORTED;
+    // device problem lists: in every group of the launch or in none
+    if ((G.dyn != nullptr) != dyn) return SM_ERR_ARG;
+    g.dyn = G.dyn;
     const int64_t gt = (int64_t)g.tiles_per_prob * G.batch;
     if (gt <= 0) return SM_ERR_ARG;
     if ((int64_t)tiles + gt > (int64_t)1 << 30) return SM_ERR_UNSUPPORTED;
@@ -1375,19 +1440,34 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     const double ec = probe ? 2.0 * ns_probe_parts(G.M)   // the float partials
                       : G.bits ? G.M * (double)G.N / 16.0
                              : (G.c_low ? lower_tile_entries(G.M) : G.M * (double)G.N);
-    bytes += 2.0 * ((same ? 0.0 : eb) + ea + ec) * G.batch;
+    const double gbytes = 2.0 * ((same ? 0.0 : eb) + ea + ec);
+    bytes += gbytes * G.batch;
+    dp.lists[q] = G.dyn;
+    dp.tpp[q] = g.tiles_per_prob;
+    dp.flops[q] = (g.sym ? 1.0 : 2.0) * G.M * (double)G.N * G.K;
+    dp.bytes[q] = gbytes;
   }
   a.ngroups = ngroups;
   a.total_tiles = tiles;
   a.gate = gate;
-  a.dyn = dyn;
+  a.dyn_tiles = dyn ? dyn_tiles : nullptr;
   const int grid = std::min(tiles, cu_count());
   a.xcd_chunk = (grid % 8 == 0) ? grid / 8 : 0;
   double* exec = (gate || dyn) ? prof_exec_slot(kind) : nullptr;
-  if (exec) {   // a gated launch reports its work only if it runs (per listed problem)
-    a.prof_exec = exec;
-    a.prof_flops = dyn ? flops / groups[0].batch : flops;
-    a.prof_bytes = dyn ? bytes / groups[0].batch : bytes;
+  if (dyn) {   // the tile layout over the lists (and the work they get credited)
+    dp.ngroups = ngroups;
+    dp.gate = gate;
+    dp.out = dyn_tiles;
+    dp.prof_exec = exec;
+    prof_begin(SM_K_MISC, (kNsgMaxGroups + 1) * 4.0, s);
+    hipLaunchKernelGGL(k_dyn_prefix, dim3(1), dim3(64), 0, s, dp);
+    prof_end(s);
+    SM_TRY(check_launch());
+  }
+  if (exec) {   // a gated launch reports its work only if it runs
+    a.prof_exec = dyn ? nullptr : exec;
+    a.prof_flops = flops;
+    a.prof_bytes = bytes;
     prof_begin(kind, 0.0, s, 0.0);
   } else {
     prof_begin(kind, flops, s, bytes);

@@ -255,7 +255,7 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, bool last,
 // that concurrent tiles carry similar work, as few launches as the group
 // and table limits allow.
 sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s,
-                           const int32_t* gate = nullptr, const int32_t* dyn = nullptr) {
+                           const int32_t* gate = nullptr, int32_t* dyn_tiles = nullptr) {
   std::stable_sort(gs.begin(), gs.end(),
                    [](const NsgGroup& x, const NsgGroup& y) { return x.K > y.K; });
   size_t i = 0;
@@ -264,7 +264,7 @@ sm_status launch_ns_groups(std::vector<NsgGroup>& gs, int kind, hipStream_t s,
     while (i + ng < gs.size() && ng < kNsgMaxGroups &&
            ns_group_tables(gs.data() + i, ng + 1) <= kNsgMaxTables)
       ++ng;
-    SM_TRY(launch_gemm_ns(gs.data() + i, ng, kind, s, gate, dyn));
+    SM_TRY(launch_gemm_ns(gs.data() + i, ng, kind, s, gate, dyn_tiles));
     i += ng;
   }
   return SM_OK;
@@ -847,6 +847,7 @@ struct GramWs {
   int32_t* any;   // 1 iff some problem refreshes
   int32_t* any_hc;  // 1 iff some problem has a cache
   int32_t* dyn;   // [1 + batch] the refreshed problems: count, then indices
+  int32_t* dyn_tiles;   // [kNsgMaxGroups + 1] tile layout of a launch over such lists
 };
 
 // The five float32 r x r buffers of the generic solve are one region; the
@@ -870,6 +871,7 @@ void carve_gram(Carver& cv, int batch, int m, int n, GramWs& w) {
   w.any = cv.take<int32_t>(4);
   w.any_hc = cv.take<int32_t>(4);
   w.dyn = cv.take<int32_t>((size_t)(batch + 1) * 4);
+  w.dyn_tiles = cv.take<int32_t>((size_t)(kNsgMaxGroups + 1) * 4);
 }
 
 // The fresh solve of CacheMuon in the Gram form on the persistent MFMA
@@ -877,29 +879,51 @@ void carve_gram(Carver& cv, int batch, int m, int n, GramWs& w) {
 // Newton-Schulz Gram form (S_k = b G_k, P_k = S_k + aI, so G_{k+1} = P_k G_k
 // P_k and Q_{k+1} = P_k Q_k are the products T_k = S_k P_k, S_{k+1} = T_k P_k,
 // Q_{k+1} = Q_k P_k).  Every launch runs only the refreshed problems, listed
-// on the device (dyn, from the decision flags), and nothing when there are
-// none (gate `any`); Q_K goes to their caches as whole float32 matrices.
-sm_status gram_fresh_gf(const GfPlan& g, const int32_t* flags, const int32_t* any,
-                        int32_t* dyn, const PtrTbl& qtbl, int qper, hipStream_t s) {
-  const int K = (int)g.T.size();
-  SM_TRY(launch_compact_flags(flags, g.batch, dyn, s));
-  std::vector<NsgGroup> v{g.gram};
-  SM_TRY(launch_ns_groups(v, SM_K_GEMM_GRAM, s, any, dyn));
-  if (g.fill_src.p)
-    SM_TRY(launch_add_identity(g.fill_src.p, g.fill_src.st, g.fill_dst.p, g.fill_dst.st, g.r,
-                               g.batch, g.a, g.gram.c_low != 0, s));
+// on the device per plan (from the decision flags), and nothing when there
+// are none (gate `any`); the plans (shape chunks) share each launch.  Q_K
+// goes to the caches as whole float32 matrices.
+struct GfFresh {
+  const GfPlan* plan;
+  const int32_t* flags;
+  int32_t* dyn;
+  const PtrTbl* qtbl;
+  int qper;
+};
+
+sm_status gram_fresh_gf(const std::vector<GfFresh>& fr, const int32_t* any, int32_t* dyn_tiles,
+                        hipStream_t s) {
+  if (fr.empty()) return SM_OK;
+  const int K = (int)fr[0].plan->T.size();
+  auto listed = [](NsgGroup g, int32_t* dyn) {
+    g.dyn = dyn;
+    return g;
+  };
+  std::vector<NsgGroup> v;
+  for (const GfFresh& f : fr) {
+    if ((int)f.plan->T.size() != K || !f.plan->gram.c_low) return SM_ERR_UNSUPPORTED;
+    SM_TRY(launch_compact_flags(f.flags, f.plan->batch, f.dyn, s));
+    v.push_back(listed(f.plan->gram, f.dyn));
+  }
+  SM_TRY(launch_ns_groups(v, SM_K_GEMM_GRAM, s, any, dyn_tiles));
   for (int k = 0; k < K; ++k) {
     std::vector<NsgGroup> l1, l2;             // {T_k, Q_{k+1}}, then {S_{k+1}}
-    if (g.T[k].batch) l1.push_back(g.T[k]);
-    if (g.Q[k].batch) l1.push_back(g.Q[k]);
-    if (g.S[k].batch) l2.push_back(g.S[k]);
-    if (!l1.empty()) SM_TRY(launch_ns_groups(l1, SM_K_GEMM_RR, s, any, dyn));
-    if (!l2.empty()) SM_TRY(launch_ns_groups(l2, SM_K_GEMM_RR, s, any, dyn));
+    for (const GfFresh& f : fr) {
+      const GfPlan& g = *f.plan;
+      if (g.T[k].batch) l1.push_back(listed(g.T[k], f.dyn));
+      if (g.Q[k].batch) l1.push_back(listed(g.Q[k], f.dyn));
+      if (g.S[k].batch) l2.push_back(listed(g.S[k], f.dyn));
+    }
+    if (!l1.empty()) SM_TRY(launch_ns_groups(l1, SM_K_GEMM_RR, s, any, dyn_tiles));
+    if (!l2.empty()) SM_TRY(launch_ns_groups(l2, SM_K_GEMM_RR, s, any, dyn_tiles));
   }
-  v = {g.apply};
-  SM_TRY(launch_ns_groups(v, SM_K_GEMM_APPLY, s, any, dyn));
-  if (!g.gram.c_low) return SM_ERR_UNSUPPORTED;   // q_store reads the lower-stored Q_K
-  return launch_q_store(g.qk.p, g.qk.st, g.r, qtbl, qper, flags, g.batch, s);
+  v.clear();
+  for (const GfFresh& f : fr) v.push_back(listed(f.plan->apply, f.dyn));
+  SM_TRY(launch_ns_groups(v, SM_K_GEMM_APPLY, s, any, dyn_tiles));
+  for (const GfFresh& f : fr) {   // q_store reads the lower-stored Q_K
+    const GfPlan& g = *f.plan;
+    SM_TRY(launch_q_store(g.qk.p, g.qk.st, g.r, *f.qtbl, f.qper, f.flags, g.batch, s));
+  }
+  return SM_OK;
 }
 
 // One batch of same-shaped CacheMuon problems.  Problem b's Q lives at
@@ -1150,20 +1174,33 @@ sm_status gram_jobs(const std::vector<GramJob>& jobs, int dt, const sm_ns_params
                                gamma, t, j.w.flags, j.err_out, j.refr_out,
                                j.has_diag ? &j.diag : nullptr, s));
   }
-  for (size_t i = 0; i < nj; ++i) {
-    const GramJob& j = jobs[i];
-    if (fast[i]) {
-      FlagSets fs;
-      std::memset(&fs, 0, sizeof(fs));
-      fs.f[0] = j.w.flags;
-      fs.n[0] = j.batch;
-      fs.count = 1;
-      SM_TRY(launch_any_flags(fs, j.w.any, s));
-      SM_TRY(gram_fresh_gf(fp[i].gf, j.w.flags, j.w.any, j.w.dyn, j.qtbl, j.qper, s));
-    } else {
-      SM_TRY(gram_generic_fresh(j, dt, p, s));
+  // fresh solves: the persistent-kernel jobs share their launches, gated by
+  // one device flag (some problem of some job refreshes)
+  {
+    FlagSets fs;
+    std::memset(&fs, 0, sizeof(fs));
+    std::vector<GfFresh> fr;
+    int32_t* any = nullptr;
+    int32_t* dyn_tiles = nullptr;
+    for (size_t i = 0; i < nj; ++i) {
+      if (!fast[i]) continue;
+      const GramJob& j = jobs[i];
+      fs.f[fs.count] = j.w.flags;
+      fs.n[fs.count] = j.batch;
+      ++fs.count;
+      if (!any) {
+        any = j.w.any;
+        dyn_tiles = j.w.dyn_tiles;
+      }
+      fr.push_back(GfFresh{&fp[i].gf, j.w.flags, j.w.dyn, &j.qtbl, j.qper});
+    }
+    if (any) {
+      SM_TRY(launch_any_flags(fs, any, s));
+      SM_TRY(gram_fresh_gf(fr, any, dyn_tiles, s));
     }
   }
+  for (size_t i = 0; i < nj; ++i)
+    if (!fast[i]) SM_TRY(gram_generic_fresh(jobs[i], dt, p, s));
   return SM_OK;
 }
 

@@ -398,6 +398,10 @@ struct NsgGroup {
   // whose mirror is not computed) to resid + problem * 4 * lower tiles +
   // 4 * (tm (tm + 1) / 2 + tn) + wave.
   float* resid;
+  // Optional device problem list (int32 [1 + batch]: the count, then the
+  // indices of the problems to run); the other problems are neither
+  // computed nor stored.  In a launch either every group has one or none.
+  const int32_t* dyn;
 };
 
 // Residual partials per problem that a probe launch writes (4 per lower tile).
@@ -418,12 +422,13 @@ int ns_ident_split(float a, uint32_t* hi_bits, uint32_t* lo_bits);
 // tables.
 // gate (optional device int32): when it holds 0 at launch time the whole
 // launch does nothing (the fresh solve of a CacheMuon step that refreshes
-// no problem).  dyn (optional device int32 [1 + batch]): only the dyn[0]
-// problems dyn[1 ..] run (every group must have the same batch; pointer
-// tables are addressed by the listed problem); the others are neither
-// computed nor stored.
+// no problem).  Groups with device problem lists (NsgGroup::dyn) need
+// dyn_tiles, a device int32 [kNsgMaxGroups + 1] scratch that a small kernel
+// ahead of the launch fills with each group's first tile and the total (so
+// that groups of different shapes and lists share a launch); pointer tables
+// are addressed by the listed problem.
 sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStream_t s,
-                         const int32_t* gate = nullptr, const int32_t* dyn = nullptr);
+                         const int32_t* gate = nullptr, int32_t* dyn_tiles = nullptr);
 // dyn[0] = the number of problems b < n with flags[b] == 1, dyn[1 ..] = those
 // b in increasing order (one workgroup).
 sm_status launch_compact_flags(const int32_t* flags, int n, int32_t* dyn, hipStream_t s);

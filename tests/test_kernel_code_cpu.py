@@ -40,9 +40,12 @@ def gemm_ns_asm(tmp_path_factory):
     assert proc.returncode == 0, proc.stdout[-2000:]
     text = out.read_text()
     kernels = {}
-    for m in re.finditer(r"^(_ZN2sm3nsg9k_gemm_nsILi(\d)EEEvNS0_4ArgsE):[^\n]*\n(.*?)^\s*s_endpgm",
+    # a kernel's whole body, up to its end label (an early exit puts an
+    # s_endpgm ahead of the main loop)
+    for m in re.finditer(r"^(_ZN2sm3nsg9k_gemm_nsILi(\d)EEEvNS0_4ArgsE):[^\n]*\n(.*?)^\.Lfunc_end",
                          text, re.S | re.M):
         kernels[int(m.group(2))] = m.group(3)
+    assert all("v_mfma" in body for body in kernels.values())
     assert set(kernels) == {0, 1, 2}, sorted(kernels)
     return text, kernels
 
