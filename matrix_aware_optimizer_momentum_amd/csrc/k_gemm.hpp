@@ -45,14 +45,19 @@ constexpr int BN = 128;
 constexpr int NT = 256;
 constexpr int kGemmMaxGroups = 8;
 
-template <typename TM> struct Cfg;
-template <> struct Cfg<bf16_t> {
+// k-slab depth and LDS row pitch per MFMA type and block tile T.
+template <typename TM, int T> struct Cfg;
+template <int T> struct Cfg<bf16_t, T> {
   static constexpr int BK = 32;
   static constexpr int LDK = 32 + 8;  // LDS row pitch in elements (80 bytes)
 };
-template <> struct Cfg<float> {
-  static constexpr int BK = 16;
-  static constexpr int LDK = 16 + 4;  // 80 bytes
+template <int T> struct Cfg<float, T> {
+  // The 64 tile takes 32 k per slab, so that a wave's 16 MFMAs of a slab
+  // outlast the global latency of the next slab's register prefetch; the 128
+  // tile keeps 16 (its wave issues 16 MFMAs per slab already, and a deeper
+  // slab would halve the blocks an LDS-bound CU holds).
+  static constexpr int BK = T == 64 ? 32 : 16;
+  static constexpr int LDK = BK + 4;  // 144 or 80 bytes
 };
 
 template <typename TG, typename TM> struct Conv;
@@ -80,7 +85,7 @@ template <typename TG, typename TM, int LAY, int T> struct Stage;
 // KC operand: tile rows [r0, r0+T), k in [k0, k0+BK), element (r, k) at
 // base[r*ld + k].  Each thread moves NV vectors of VEC consecutive k.
 template <typename TG, typename TM, int T> struct Stage<TG, TM, KC, T> {
-  static constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
+  static constexpr int BK = Cfg<TM, T>::BK, LDK = Cfg<TM, T>::LDK;
   static constexpr int VEC = 16 / sizeof(TM);   // elements per 16-byte LDS write
   static constexpr int VPR = BK / VEC;          // vectors per row (4)
   static constexpr int NV = (T * VPR) / NT;     // vectors per thread (2 for T = 128)
@@ -126,66 +131,75 @@ template <typename TG, typename TM, int T> struct Stage<TG, TM, KC, T> {
 };
 
 // RC operand: tile rows [r0, r0+T), k in [k0, k0+BK), element (r, k) at
-// base[k*ld + r].  Each thread loads KV consecutive k for 2 adjacent rows and
-// writes them as two [row][k] vectors (for T = 64 half the threads have a
-// chunk).
+// base[k*ld + r].  A chunk is KV consecutive k of 2 adjacent rows, written as
+// two [row][k] vectors; a thread moves NC chunks (for T = 64 with bf16 half
+// the threads have none).
 template <typename TG, typename TM, int T> struct Stage<TG, TM, RC, T> {
-  static constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
+  static constexpr int BK = Cfg<TM, T>::BK, LDK = Cfg<TM, T>::LDK;
   static constexpr int KV = 16 / sizeof(TM);  // k per LDS vector: 8 (bf16) or 4 (f32)
   static constexpr int CHUNKS = (BK / KV) * (T / 2);
-  static_assert(CHUNKS == NT || CHUNKS == NT / 2, "at most one chunk per thread");
-  TG v0[KV], v1[KV];
+  static constexpr int NC = CHUNKS >= NT ? CHUNKS / NT : 1;
+  static_assert(CHUNKS == NT / 2 || CHUNKS % NT == 0, "chunks spread evenly over the threads");
+  TG v0[NC][KV], v1[NC][KV];
 
   __device__ __forceinline__ void load(const TG* __restrict__ base, int64_t ld, int r0,
                                        int rows, int k0, int K, bool fast) {
     if (CHUNKS < NT && (int)threadIdx.x >= CHUNKS) return;
-    const int rc = (threadIdx.x % (T / 2)) * 2;
-    const int kc = (threadIdx.x / (T / 2)) * KV;
-    if (fast) {
-      const TG* src = base + (int64_t)(k0 + kc) * ld + (r0 + rc);
 #pragma unroll
-      for (int kk = 0; kk < KV; ++kk) {
-        const TG* p = src + (int64_t)kk * ld;
-        if constexpr (sizeof(TG) == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-          v0[kk] = (TG)(w & 0xFFFFu);
-          v1[kk] = (TG)(w >> 16);
-        } else {
-          const float2 w = *reinterpret_cast<const float2*>(p);
-          v0[kk] = w.x;
-          v1[kk] = w.y;
-        }
-      }
-    } else {
+    for (int c = 0; c < NC; ++c) {
+      const int id = threadIdx.x + NT * c;
+      const int rc = (id % (T / 2)) * 2;
+      const int kc = (id / (T / 2)) * KV;
+      if (fast) {
+        const TG* src = base + (int64_t)(k0 + kc) * ld + (r0 + rc);
 #pragma unroll
-      for (int kk = 0; kk < KV; ++kk) {
-        const int k = k0 + kc + kk;
-        const int r = r0 + rc;
-        TG a = (TG)0, b = (TG)0;
-        if (k < K) {
-          if (r < rows) a = base[(int64_t)k * ld + r];
-          if (r + 1 < rows) b = base[(int64_t)k * ld + r + 1];
+        for (int kk = 0; kk < KV; ++kk) {
+          const TG* p = src + (int64_t)kk * ld;
+          if constexpr (sizeof(TG) == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+            v0[c][kk] = (TG)(w & 0xFFFFu);
+            v1[c][kk] = (TG)(w >> 16);
+          } else {
+            const float2 w = *reinterpret_cast<const float2*>(p);
+            v0[c][kk] = w.x;
+            v1[c][kk] = w.y;
+          }
         }
-        v0[kk] = a;
-        v1[kk] = b;
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) {
+          const int k = k0 + kc + kk;
+          const int r = r0 + rc;
+          TG a = (TG)0, b = (TG)0;
+          if (k < K) {
+            if (r < rows) a = base[(int64_t)k * ld + r];
+            if (r + 1 < rows) b = base[(int64_t)k * ld + r + 1];
+          }
+          v0[c][kk] = a;
+          v1[c][kk] = b;
+        }
       }
     }
   }
   __device__ __forceinline__ void store(TM* S) const {
     if (CHUNKS < NT && (int)threadIdx.x >= CHUNKS) return;
-    const int rc = (threadIdx.x % (T / 2)) * 2;
-    const int kc = (threadIdx.x / (T / 2)) * KV;
-    __attribute__((aligned(16))) TM o0[KV];
-    __attribute__((aligned(16))) TM o1[KV];
 #pragma unroll
-    for (int kk = 0; kk < KV; ++kk) {
-      o0[kk] = Conv<TG, TM>::cv(v0[kk]);
-      o1[kk] = Conv<TG, TM>::cv(v1[kk]);
+    for (int c = 0; c < NC; ++c) {
+      const int id = threadIdx.x + NT * c;
+      const int rc = (id % (T / 2)) * 2;
+      const int kc = (id / (T / 2)) * KV;
+      __attribute__((aligned(16))) TM o0[KV];
+      __attribute__((aligned(16))) TM o1[KV];
+#pragma unroll
+      for (int kk = 0; kk < KV; ++kk) {
+        o0[kk] = Conv<TG, TM>::cv(v0[c][kk]);
+        o1[kk] = Conv<TG, TM>::cv(v1[c][kk]);
+      }
+      TM* d0 = S + rc * LDK + kc;  // 16-byte aligned: LDK*sizeof(TM) and kc*sizeof(TM) are
+      TM* d1 = d0 + LDK;            // multiples of 16
+      *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<const uint4*>(o0);
+      *reinterpret_cast<uint4*>(d1) = *reinterpret_cast<const uint4*>(o1);
     }
-    TM* d0 = S + rc * LDK + kc;  // 16-byte aligned: LDK*sizeof(TM) and kc*sizeof(TM) are
-    TM* d1 = d0 + LDK;            // multiples of 16
-    *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<const uint4*>(o0);
-    *reinterpret_cast<uint4*>(d1) = *reinterpret_cast<const uint4*>(o1);
   }
 };
 
@@ -201,7 +215,7 @@ template <> struct Mma<bf16_t> {
   template <int WB>
   __device__ __forceinline__ static void step(const bf16_t* As, const bf16_t* Bs, int wm,
                                               int wn, f32x16 (&acc)[WB][WB]) {
-    constexpr int LDK = Cfg<bf16_t>::LDK, BK = Cfg<bf16_t>::BK;
+    constexpr int LDK = Cfg<bf16_t, 64 * WB>::LDK, BK = Cfg<bf16_t, 64 * WB>::BK;
     constexpr int NG = BK / 16;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
@@ -241,7 +255,7 @@ template <> struct Mma<float> {
   template <int WB>
   __device__ __forceinline__ static void step(const float* As, const float* Bs, int wm, int wn,
                                               f32x16 (&acc)[WB][WB]) {
-    constexpr int LDK = Cfg<float>::LDK, BK = Cfg<float>::BK;
+    constexpr int LDK = Cfg<float, 64 * WB>::LDK, BK = Cfg<float, 64 * WB>::BK;
     constexpr int NG = BK / 4;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
@@ -308,7 +322,7 @@ __device__ __forceinline__ const char* prob_base(const KArgs& ka, const GemmCore
 // chip with 128 tiles), a wave owning (T / 2)^2 of it.
 template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE, int T>
 __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
-  constexpr int BK = Cfg<TM>::BK, LDK = Cfg<TM>::LDK;
+  constexpr int BK = Cfg<TM, T>::BK, LDK = Cfg<TM, T>::LDK;
   constexpr int WB = T / 64;   // 32 x 32 blocks per wave and dimension
   constexpr int WT = T / 2;    // wave sub-tile
   __shared__ __attribute__((aligned(16))) TM As[2][T * LDK];
