@@ -17,7 +17,9 @@
 // input type, so every fragment is one 16-byte (bf16) or 8-byte (f32) LDS
 // read.  A KC operand (k contiguous in HBM) is copied with 16-byte loads; an
 // RC operand (row index contiguous in HBM) is transposed in registers on its
-// way into LDS.  Interior tiles with aligned leading dimensions take the
+// way into LDS, except with float32 MFMA input: there it is copied as it
+// lies, [k][row], and a fragment is two dword reads (the float32 MFMA takes
+// one k per register, so no transpose is needed at all).  Interior tiles with aligned leading dimensions take the
 // vector path, edge tiles load element by element with zero fill, so any
 // M, N, K >= 1 is handled.
 //
@@ -58,6 +60,9 @@ template <int T> struct Cfg<float, T> {
   // slab would halve the blocks an LDS-bound CU holds).
   static constexpr int BK = T == 64 ? 32 : 16;
   static constexpr int LDK = BK + 4;  // 144 or 80 bytes
+  // pitch of a [k][row] stage (RC operands): the two k rows that the halves
+  // of a wave read in one fragment load lie 2 * LDR = 32 (mod 64) banks apart
+  static constexpr int LDR = T + 16;
 };
 
 template <typename TG, typename TM> struct Conv;
@@ -89,6 +94,7 @@ template <typename TG, typename TM, int T> struct Stage<TG, TM, KC, T> {
   static constexpr int VEC = 16 / sizeof(TM);   // elements per 16-byte LDS write
   static constexpr int VPR = BK / VEC;          // vectors per row (4)
   static constexpr int NV = (T * VPR) / NT;     // vectors per thread (2 for T = 128)
+  static constexpr int ELEMS = T * LDK;         // LDS elements of one stage, as [row][k]
   static_assert(NV >= 1, "every thread moves a vector");
   static_assert((VEC * sizeof(TG)) % 16 == 0, "whole 16-byte global loads");
   __attribute__((aligned(16))) TG raw[NV][VEC];
@@ -139,6 +145,7 @@ template <typename TG, typename TM, int T> struct Stage<TG, TM, RC, T> {
   static constexpr int KV = 16 / sizeof(TM);  // k per LDS vector: 8 (bf16) or 4 (f32)
   static constexpr int CHUNKS = (BK / KV) * (T / 2);
   static constexpr int NC = CHUNKS >= NT ? CHUNKS / NT : 1;
+  static constexpr int ELEMS = T * LDK;   // LDS elements of one stage, as [row][k]
   static_assert(CHUNKS == NT / 2 || CHUNKS % NT == 0, "chunks spread evenly over the threads");
   TG v0[NC][KV], v1[NC][KV];
 
@@ -203,6 +210,46 @@ template <typename TG, typename TM, int T> struct Stage<TG, TM, RC, T> {
   }
 };
 
+// RC float32 operand with float32 MFMA input: staged without a transpose.
+// The LDS stage holds it as [k][row] (rows contiguous, pitch LDR), and each
+// thread moves NV 16-byte vectors of 4 consecutive rows at one k; the MFMA
+// step reads a lane's two k of a group as two dwords LDR apart.
+template <int T> struct Stage<float, float, RC, T> {
+  static constexpr int BK = Cfg<float, T>::BK, LDR = Cfg<float, T>::LDR;
+  static constexpr int VPK = T / 4;              // vectors per k
+  static constexpr int NV = BK * VPK / NT;       // vectors per thread (2)
+  static constexpr int ELEMS = BK * LDR;         // LDS elements of one stage, as [k][row]
+  static_assert(NV >= 1 && (BK * VPK) % NT == 0, "vectors spread evenly over the threads");
+  float4 raw[NV];
+
+  __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld, int r0,
+                                       int rows, int k0, int K, bool fast) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = threadIdx.x + NT * i;
+      const int k = k0 + v / VPK;
+      const int r = r0 + (v % VPK) * 4;
+      if (fast) {
+        raw[i] = *reinterpret_cast<const float4*>(base + (int64_t)k * ld + r);
+      } else {
+        const float* src = base + (int64_t)k * ld;
+        const bool kin = k < K;
+        raw[i].x = (kin && r < rows) ? src[r] : 0.f;
+        raw[i].y = (kin && r + 1 < rows) ? src[r + 1] : 0.f;
+        raw[i].z = (kin && r + 2 < rows) ? src[r + 2] : 0.f;
+        raw[i].w = (kin && r + 3 < rows) ? src[r + 3] : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* S) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = threadIdx.x + NT * i;
+      *reinterpret_cast<float4*>(S + (v / VPK) * LDR + (v % VPK) * 4) = raw[i];
+    }
+  }
+};
+
 // ------------------------------------------------------------ MFMA step
 
 template <typename TM> struct Mma;
@@ -212,7 +259,7 @@ template <typename TM> struct Mma;
 template <> struct Mma<bf16_t> {
   // k-groups of 16: fragments are 8 consecutive k at offset 8*(lane/32).  The
   // next group's fragments are read before this group's MFMAs go out.
-  template <int WB>
+  template <int WB, int LA, int LB>   // both layouts are staged as [row][k]
   __device__ __forceinline__ static void step(const bf16_t* As, const bf16_t* Bs, int wm,
                                               int wn, f32x16 (&acc)[WB][WB]) {
     constexpr int LDK = Cfg<bf16_t, 64 * WB>::LDK, BK = Cfg<bf16_t, 64 * WB>::BK;
@@ -248,24 +295,35 @@ template <> struct Mma<bf16_t> {
   }
 };
 
+// Float32 fragment of output block i of wave row / column w, k-group g: the
+// lane's k = 4 g + 2 (lane / 32) + {0, 1} of row 32 (WB w + i) + lane % 32,
+// from a [row][k] stage (one 8-byte read) or a [k][row] stage (two dwords).
+template <int LAY, int WB>
+__device__ __forceinline__ float2 frag_f32(const float* S, int w, int i, int g) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+  if constexpr (LAY == RC) {
+    constexpr int LDR = Cfg<float, 64 * WB>::LDR;
+    const float* p = S + (g * 4 + lk * 2) * LDR + (w * WB + i) * 32 + lr;
+    return make_float2(p[0], p[LDR]);
+  } else {
+    constexpr int LDK = Cfg<float, 64 * WB>::LDK;
+    return *reinterpret_cast<const float2*>(S + ((w * WB + i) * 32 + lr) * LDK + g * 4 + lk * 2);
+  }
+}
+
 template <> struct Mma<float> {
-  // k-groups of 4, each two 32x32x2 MFMAs per output block: lane supplies
-  // k = 4 g + 2*(lane/32) + {0,1}.  The next group's fragments are read
-  // before this group's MFMAs go out.
-  template <int WB>
+  // k-groups of 4, each two 32x32x2 MFMAs per output block.  The next
+  // group's fragments are read before this group's MFMAs go out.
+  template <int WB, int LA, int LB>
   __device__ __forceinline__ static void step(const float* As, const float* Bs, int wm, int wn,
                                               f32x16 (&acc)[WB][WB]) {
-    constexpr int LDK = Cfg<float, 64 * WB>::LDK, BK = Cfg<float, 64 * WB>::BK;
-    constexpr int NG = BK / 4;
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 31, lk = lane >> 5;
-    const float* pa = As + (wm * 32 * WB + lr) * LDK + lk * 2;
-    const float* pb = Bs + (wn * 32 * WB + lr) * LDK + lk * 2;
+    constexpr int NG = Cfg<float, 64 * WB>::BK / 4;
     float2 af[2][WB], bfg[2][WB];
 #pragma unroll
     for (int i = 0; i < WB; ++i) {
-      af[0][i] = *reinterpret_cast<const float2*>(pa + i * 32 * LDK);
-      bfg[0][i] = *reinterpret_cast<const float2*>(pb + i * 32 * LDK);
+      af[0][i] = frag_f32<LA, WB>(As, wm, i, 0);
+      bfg[0][i] = frag_f32<LB, WB>(Bs, wn, i, 0);
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -273,8 +331,8 @@ template <> struct Mma<float> {
       if (g + 1 < NG) {
 #pragma unroll
         for (int i = 0; i < WB; ++i) {
-          af[n][i] = *reinterpret_cast<const float2*>(pa + i * 32 * LDK + (g + 1) * 4);
-          bfg[n][i] = *reinterpret_cast<const float2*>(pb + i * 32 * LDK + (g + 1) * 4);
+          af[n][i] = frag_f32<LA, WB>(As, wm, i, g + 1);
+          bfg[n][i] = frag_f32<LB, WB>(Bs, wn, i, g + 1);
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // the reads go out ahead of the MFMAs
@@ -322,11 +380,13 @@ __device__ __forceinline__ const char* prob_base(const KArgs& ka, const GemmCore
 // chip with 128 tiles), a wave owning (T / 2)^2 of it.
 template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE, int T>
 __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
-  constexpr int BK = Cfg<TM, T>::BK, LDK = Cfg<TM, T>::LDK;
+  constexpr int BK = Cfg<TM, T>::BK;
   constexpr int WB = T / 64;   // 32 x 32 blocks per wave and dimension
   constexpr int WT = T / 2;    // wave sub-tile
-  __shared__ __attribute__((aligned(16))) TM As[2][T * LDK];
-  __shared__ __attribute__((aligned(16))) TM Bs[2][T * LDK];
+  using SA = Stage<TA, TM, LA, T>;
+  using SB = Stage<TB, TM, LB, T>;
+  __shared__ __attribute__((aligned(16))) TM As[2][SA::ELEMS];
+  __shared__ __attribute__((aligned(16))) TM Bs[2][SB::ELEMS];
   __shared__ float red[4];
   int gi = 0;
   while (gi + 1 < ka.ngroups && (int)blockIdx.x >= ka.grp[gi + 1].blk_begin) ++gi;
@@ -372,8 +432,8 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   const bool a_fast_rows = kg.a_aligned && (m0 + T) <= g.M;
   const bool b_fast_rows = kg.b_aligned && (n0 + T) <= g.N;
   const int nk = (g.K + BK - 1) / BK;
-  Stage<TA, TM, LA, T> sa;
-  Stage<TB, TM, LB, T> sb;
+  SA sa;
+  SB sb;
   sa.load(A, g.a.ld, m0, g.M, 0, g.K, a_fast_rows && BK <= g.K);
   sb.load(B, g.b.ld, n0, g.N, 0, g.K, b_fast_rows && BK <= g.K);
   sa.store(As[0]);
@@ -388,7 +448,7 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
       sa.load(A, g.a.ld, m0, g.M, k0, g.K, a_fast_rows && k_in);
       sb.load(B, g.b.ld, n0, g.N, k0, g.K, b_fast_rows && k_in);
     }
-    Mma<TM>::template step<WB>(As[cur], Bs[cur], wm, wn, acc);
+    Mma<TM>::template step<WB, LA, LB>(As[cur], Bs[cur], wm, wn, acc);
     if (more) {
       // stage cur ^ 1 was last read by slab kt - 1, before the previous barrier
       sa.store(As[cur ^ 1]);
@@ -503,7 +563,9 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
 }
 
 // Host-side alignment test for the vector staging path of an operand.
-inline bool operand_aligned(const GemmArgs& g, const GemmOperand& o) {
+// vec4_rc: an RC operand staged by 16-byte loads of 4 rows (float32 into a
+// float32 MFMA) rather than by pairs of rows.
+inline bool operand_aligned(const GemmArgs& g, const GemmOperand& o, bool vec4_rc) {
   const size_t es = dt_size(o.dt);
   uintptr_t p = reinterpret_cast<uintptr_t>(o.p);
   if (o.tbl) {  // every table entry must satisfy the same alignment
@@ -516,6 +578,7 @@ inline bool operand_aligned(const GemmArgs& g, const GemmOperand& o) {
     const int64_t vec = 16 / (int64_t)es;
     return (p % 16 == 0) && (o.ld % vec == 0) && (o.stride % vec == 0);
   }
+  if (vec4_rc) return (p % 16 == 0) && (o.ld % 4 == 0) && (o.stride % 4 == 0);
   // pairs of adjacent rows: 4-byte (bf16) or 8-byte (f32) loads
   return (p % (2 * es) == 0) && (o.ld % 2 == 0) && (o.stride % 2 == 0);
 }
@@ -554,8 +617,8 @@ sm_status launch_tile(const GemmArgs* gs, int n, int kind, hipStream_t s) {
     } else {
       k.g.tbl_off = 0;
     }
-    k.a_aligned = operand_aligned(g, g.a);
-    k.b_aligned = operand_aligned(g, g.b);
+    k.a_aligned = operand_aligned(g, g.a, sizeof(TA) == 4 && sizeof(TM) == 4);
+    k.b_aligned = operand_aligned(g, g.b, sizeof(TB) == 4 && sizeof(TM) == 4);
     const int tiles_m = (g.M + T - 1) / T;
     k.tiles_n = (g.N + T - 1) / T;
     k.tiles = g.sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * k.tiles_n;
