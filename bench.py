@@ -19,6 +19,8 @@ the vote as variants), `gpt2_large_cache_muon` (CacheMuon at gamma 2, 15, a
 mixed-rate gamma and always-fresh, with refresh rates and executed
 orthogonalisation FLOPs), `resnet50` (53 float32 convolution matrices, M =
 4, one NS iteration) and `single_256` (one float32 256 x 256 matrix, M = 3).
+Each Sign-Muon sub-object also times the same step replayed from one HIP
+graph (`graph`: sm_step_graph, then sm_graph_launch per step).
 
   python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu] [--no-sub]
   python bench.py --copy-calibration   # plain device copy of known size, for
@@ -570,6 +572,23 @@ def ns_summary(kinds, mdt, wl, ms_per_step, muon_fraction=1.0):
     return out
 
 
+def graph_steps(sm, torch, cfg, mats, ws, t, steps):
+    """The same Sign-Muon step recorded once as a HIP graph (sm_step_graph)
+    and replayed `steps` times, timed by the wall clock like the direct calls:
+    what a step costs once its kernel launches are not issued one by one."""
+    g = sm.StepGraph(cfg, mats, t, ws=ws)
+    for _ in range(3):
+        g()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g.close()
+    return {"steps_per_s": steps / wall, "ms_per_step": 1000.0 * wall / steps, "steps": steps}
+
+
 def sign_muon_sub(sm, torch, W, args, index=2, steps=None, variants=True):
     """A Sign-Muon configuration timed like the headline (wall clock over the
     timed steps), with its dominant-kernel roofline and the step variants."""
@@ -584,6 +603,7 @@ def sign_muon_sub(sm, torch, W, args, index=2, steps=None, variants=True):
     out = {"workload": wl.name, "value": steps / wall, "unit": "steps/s",
            "ms_per_step": ms, "steps": steps, "roofline": roofline,
            **ns_summary(kinds, wl.mdt, wl, ms), "other_rooflines": others, "kernels": kinds}
+    out["graph"] = graph_steps(sm, torch, cfg, mats, call.ws, t, steps)
     if variants:
         v, t = measure_variants(sm, torch, wl, cfg, mats, t, args, ms, kinds)
         if v:

@@ -334,6 +334,35 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
                   void* ws, size_t ws_bytes, float* diag, hipStream_t s);
 
 /* ------------------------------------------------------------------------
+ * One optimizer step recorded as a HIP graph and replayed.
+ * [SignMuon-ja] section 2, algorithm flow steps 1-4 and [LionMuon-pt]
+ * methodology item 1: the same step, with the same matrices, runs at every
+ * iteration t -> t+1; a step of many small matrices is bound by its kernel
+ * launches, which one graph launch replaces.
+ *
+ * sm_step_graph records sm_step(c, mats, nmat, t, ws, ws_bytes, diag) on a
+ * private stream, without running it, and returns an instantiated graph in
+ * *out.  Arguments as for sm_step; the config and matrix arrays are read
+ * during the call only, while the device buffers they name (w, mom, grad,
+ * ws, diag) must stay allocated, in place, until sm_graph_destroy: every
+ * replay reads and writes them as one sm_step call does.  sm_graph_launch
+ * enqueues one replay on s (results bit-identical to sm_step at the
+ * recorded t); replays must not overlap one another or other calls that
+ * use the same buffers (two graphs may share a workspace).  For SM_LION_MUON the
+ * step type follows t (a Muon step iff t % period == 0): record one graph
+ * per type.  The recorded kernels do not read t otherwise.
+ * Errors: as sm_step; SM_ERR_UNSUPPORTED for SM_CACHE_MUON (its kernels store
+ * t with each refresh) or while kernel-time accounting is enabled;
+ * SM_ERR_HIP if capture or instantiation fails.  *out is NULL on error.
+ * sm_graph_destroy(NULL) is a no-op.
+ * ---------------------------------------------------------------------- */
+typedef struct sm_graph_s* sm_graph;
+sm_status sm_step_graph(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t,
+                        void* ws, size_t ws_bytes, float* diag, sm_graph* out);
+sm_status sm_graph_launch(sm_graph g, hipStream_t s);
+sm_status sm_graph_destroy(sm_graph g);
+
+/* ------------------------------------------------------------------------
  * Kernel-time accounting (for benchmarks; not part of the method).
  * While enabled, every kernel the library launches is bracketed by a pair of
  * HIP events on its stream, tagged with its kind and its algorithmic work

@@ -77,6 +77,10 @@ SIGNATURES = {
     "sm_step_ws": (c_int, [P(Config), P(Matrix), c_int, P(c_size_t)]),
     "sm_step": (c_int, [P(Config), P(Matrix), c_int, c_int64, c_void_p, c_size_t, c_void_p,
                         c_void_p]),
+    "sm_step_graph": (c_int, [P(Config), P(Matrix), c_int, c_int64, c_void_p, c_size_t,
+                              c_void_p, P(c_void_p)]),
+    "sm_graph_launch": (c_int, [c_void_p, c_void_p]),
+    "sm_graph_destroy": (c_int, [c_void_p]),
     "sm_profile_enable": (c_int, [c_int]),
     "sm_profile_reset": (c_int, []),
     "sm_profile_read": (c_int, [c_int, P(c_double), P(c_int64), P(c_double)]),

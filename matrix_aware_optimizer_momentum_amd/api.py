@@ -394,6 +394,51 @@ def step(cfg: StepConfig, mats: Sequence[MatrixBuffers], t: int,
     StepCall(cfg, mats, ws, diag)(t)
 
 
+class StepGraph:
+    """sm_step at step index t, recorded once as a HIP graph (sm_step_graph)
+    and replayed on the current stream by each call (sm_graph_launch).
+
+    The matrices' buffers, the workspace and diag are bound at recording and
+    must stay in place while the graph lives.  A LionMuon step's type follows
+    t: record one graph at a Muon step and one at a Lion step (they may share
+    a workspace).  CacheMuon is not recordable (SmError SM_ERR_UNSUPPORTED).
+    """
+
+    def __init__(self, cfg: StepConfig, mats: Sequence[MatrixBuffers], t: int,
+                 ws: Optional[torch.Tensor] = None, diag: Optional[torch.Tensor] = None):
+        self._h = None
+        self._call = StepCall(cfg, mats, ws, diag)   # holds the buffers and the workspace
+        c = self._call
+        h = ctypes.c_void_p()
+        code = B.lib().sm_step_graph(ctypes.byref(c._c), c._arr, len(c.mats), t,
+                                     c.ws.data_ptr(), c.ws.numel() * c.ws.element_size(),
+                                     c.diag.data_ptr() if c.diag is not None else None,
+                                     ctypes.byref(h))
+        B.check(code, "sm_step_graph")
+        self._h = h
+        self.t = t
+
+    @property
+    def ws(self) -> torch.Tensor:
+        return self._call.ws
+
+    def __call__(self):
+        if self._h is None:
+            raise RuntimeError("StepGraph: replay after close()")
+        B.check(B.lib().sm_graph_launch(self._h, _stream()), "sm_graph_launch")
+
+    def close(self):
+        if self._h is not None:
+            h, self._h = self._h, None
+            B.check(B.lib().sm_graph_destroy(h), "sm_graph_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 # ------------------------------------------------------------------ kernel accounting
 
 def profile_enable(on: bool = True):

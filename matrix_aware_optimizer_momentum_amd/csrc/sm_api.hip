@@ -14,7 +14,14 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <new>
 #include <vector>
+
+// A captured and instantiated step (sm_step_graph).
+struct sm_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
 
 namespace sm {
 
@@ -1337,7 +1344,7 @@ const char* sm_status_string(int s) {
 
 int sm_last_hip_error(void) { return g_last_hip.load(); }
 
-int sm_version(void) { return 3; }
+int sm_version(void) { return 4; }
 
 sm_status sm_ns_polar_ws(int dt, int batch, int m, int n, size_t* ws_bytes) {
   if (!ws_bytes) return SM_ERR_ARG;
@@ -1828,6 +1835,70 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));
   }
   return SM_OK;
+}
+
+// ------------------------------------------------------------------ HIP graphs of a step
+
+// The step's launches are recorded on a private non-blocking stream (so the
+// caller's stream, possibly the null stream, is never in capture), then
+// instantiated once.  sm_step only launches kernels (no copies, memsets or
+// allocations), so the graph holds kernel nodes alone and their arguments
+// (pointers, sizes, hyper-parameters) by value.
+sm_status sm_step_graph(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t, void* ws,
+                        size_t ws_bytes, float* diag, sm_graph* out) {
+  if (!out) return SM_ERR_ARG;
+  *out = nullptr;
+  SM_TRY(check_config(c));
+  SM_TRY(check_mats(*c, mats, nmat));
+  if (t < 1 || !ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SM_ERR_ARG;
+  // CacheMuon's kernels record t with each refresh; event pairs of the
+  // kernel-time accounting are host-side records, not graph nodes
+  if (c->algo == SM_CACHE_MUON || g_prof_on) return SM_ERR_UNSUPPORTED;
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return hip_fail(e);
+  }
+  const sm_status st = sm_step(c, mats, nmat, t, ws, ws_bytes, diag, cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (st != SM_OK || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return st != SM_OK ? st : hip_fail(e);
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e);
+  }
+  sm_graph h = new (std::nothrow) sm_graph_s{g, x};
+  if (!h) {
+    (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    return hip_fail(hipErrorOutOfMemory);
+  }
+  *out = h;
+  return SM_OK;
+}
+
+sm_status sm_graph_launch(sm_graph g, hipStream_t s) {
+  if (!g) return SM_ERR_ARG;
+  const hipError_t e = hipGraphLaunch(g->exec, s);
+  return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+sm_status sm_graph_destroy(sm_graph g) {
+  if (!g) return SM_OK;
+  const hipError_t e1 = hipGraphExecDestroy(g->exec);
+  const hipError_t e2 = hipGraphDestroy(g->graph);
+  delete g;
+  if (e1 != hipSuccess) return hip_fail(e1);
+  return e2 == hipSuccess ? SM_OK : hip_fail(e2);
 }
 
 // ------------------------------------------------------------------ profiling ABI

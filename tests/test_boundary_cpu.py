@@ -201,6 +201,28 @@ def test_step_rejects_bad_matrices():
                        None) == 4
 
 
+def test_step_graph_rejects_on_the_host():
+    lib = B.lib()
+    c = _cfg(M=2)
+    ws = ctypes.c_void_p(0x100000)
+    mats = (B.Matrix * 1)()
+    mats[0] = B.Matrix(8, 8, 0x1000, 0x2000, 0x3000, None, None)
+    h = ctypes.c_void_p(0x1234)
+    assert lib.sm_step_graph(ctypes.byref(c), mats, 1, 1, ws, 1 << 20, None, None) == 1
+    assert lib.sm_step_graph(ctypes.byref(c), mats, 1, 0, ws, 1 << 20, None,
+                             ctypes.byref(h)) == 1      # t must be >= 1
+    assert h.value is None                              # *out cleared on error
+    cc = _cfg(algo=1, M=2)                              # CacheMuon records t in its state
+    mc = (B.Matrix * 1)()
+    mc[0] = B.Matrix(8, 8, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000)
+    assert lib.sm_step_graph(ctypes.byref(cc), mc, 1, 1, ws, 1 << 20, None,
+                             ctypes.byref(h)) == 5
+    assert h.value is None
+    assert lib.sm_graph_launch(None, None) == 1
+    assert lib.sm_graph_destroy(None) == 0
+    assert lib.sm_last_hip_error() == 0
+
+
 def test_python_front_end_needs_gpu_tensors():
     import torch
     import matrix_aware_optimizer_momentum_amd as sm
