@@ -350,6 +350,55 @@ template <> struct Mma<float> {
 
 // ------------------------------------------------------------ kernel
 
+// Epilogue of an interior tile with a float32 output and none of the rarer
+// outputs (second output, residual partials): per 32 x 32 block the Cin
+// values are loaded first (all in flight together), then
+// value = alpha acc + beta Cin (+ diag on the diagonal), kept in acc (for the
+// sign packing) and stored, and stored transposed too for a mirrored tile
+// (16-byte aligned output rows: ldc % 4 == 0).
+// The same arithmetic, in the same order, as the general epilogue; no
+// bounds checks and no per-element branches on launch parameters.
+template <bool CIN, int WB>
+__device__ __forceinline__ void epilogue_f32_interior(f32x16 (&acc)[WB][WB], float alpha,
+                                                      float beta, float diag, const float* cin,
+                                                      int64_t ldcin, float* c, int64_t ldc,
+                                                      bool mirror, int r0, int c0) {
+#pragma unroll
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int j = 0; j < WB; ++j) {
+      const int rb = r0 + i * 32;   // row of v = rb + e(v), e(v) = 8 (v / 4) + v % 4
+      const int col = c0 + j * 32;
+      float ci[16];
+      if constexpr (CIN) {
+        const float* p = cin + (int64_t)rb * ldcin + col;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ci[v] = p[((v >> 2) * 8 + (v & 3)) * ldcin];
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = rb + (v >> 2) * 8 + (v & 3);
+        float val = alpha * acc[i][j][v];
+        if constexpr (CIN) val += beta * ci[v];
+        if (row == col) val += diag;
+        acc[i][j][v] = val;
+      }
+      if (c) {
+        float* p = c + (int64_t)rb * ldc + col;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[((v >> 2) * 8 + (v & 3)) * ldc] = acc[i][j][v];
+        if (mirror) {   // rows e(v) of column col: four runs of four consecutive entries
+          float* q = c + (int64_t)col * ldc + rb;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<float4*>(q + 8 * u) =
+                make_float4(acc[i][j][4 * u], acc[i][j][4 * u + 1], acc[i][j][4 * u + 2],
+                            acc[i][j][4 * u + 3]);
+        }
+      }
+    }
+}
+
 // One product set of a launch as the kernel sees it.
 struct KGroup {
   GemmCore g;
@@ -379,7 +428,7 @@ __device__ __forceinline__ const char* prob_base(const KArgs& ka, const GemmCore
 // T: the square block tile (128, or 64 for launches too small to fill the
 // chip with 128 tiles), a wave owning (T / 2)^2 of it.
 template <typename TA, typename TB, typename TM, int LA, int LB, int ROLE, int T>
-__global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
+__global__ __launch_bounds__(NT, (T == 128 && sizeof(TM) == 4) ? 3 : 1) void k_gemm(KArgs ka) {
   constexpr int BK = Cfg<TM, T>::BK;
   constexpr int WB = T / 64;   // 32 x 32 blocks per wave and dimension
   constexpr int WT = T / 2;    // wave sub-tile
@@ -475,48 +524,71 @@ __global__ __launch_bounds__(NT) void k_gemm(KArgs ka) {
   float* c2_b = (g.c2 || g.c2_tbl) ? reinterpret_cast<float*>(const_cast<char*>(
                                          prob_base(ka, g, g.c2, g.c2_tbl, g.sc2, 4, b)))
                                    : nullptr;
+  // uniform parameters, read once (every store below may alias the kernel
+  // arguments as far as the compiler knows)
+  const bool cbf = g.c_dt == BF16;
+  const int Mg = g.M, Ng = g.N;
+  const int64_t ldcin = g.ldcin, ldc = g.ldc, ldc2 = g.ldc2;
+  const float diag = g.diag, c2_scale = g.c2_scale, c2_diag = g.c2_diag;
+  const bool resid = g.resid != nullptr;
   float rs = 0.f;
+  const bool interior = (m0 + T) <= Mg && (n0 + T) <= Ng;
+  // (a mirrored tile's transposed stores go out as 16-byte vectors)
+  const bool vec_ok = !mirror || ((ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c_b) & 15) == 0);
+  // (float32 MFMA kernels only: on the bf16 ones it would cost occupancy)
+  if (sizeof(TM) == 4 && !cbf && interior && !c2_b && !resid && vec_ok) {
+    const int r0 = m0 + wm * WT + lk * 4, c0 = n0 + wn * WT + lr;
+    float* cf = reinterpret_cast<float*>(c_b);
+    if constexpr (sizeof(TM) == 4) {
+      if (cin_b)
+        epilogue_f32_interior<true, WB>(acc, alpha, beta, diag,
+                                        reinterpret_cast<const float*>(cin_b), ldcin, cf, ldc,
+                                        mirror, r0, c0);
+      else
+        epilogue_f32_interior<false, WB>(acc, alpha, beta, diag, nullptr, 0, cf, ldc, mirror,
+                                         r0, c0);
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < WB; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < WB; ++j)
+      for (int j = 0; j < WB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WT + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
-        const int col = n0 + wn * WT + j * 32 + lr;
-        float stored = 0.f;
-        if (row < g.M && col < g.N) {
-          float val = alpha * acc[i][j][v];
-          if (cin_b) {
-            const int64_t off = (int64_t)row * g.ldcin + col;
-            const float ci = (g.c_dt == BF16)
-                                 ? bf2f(reinterpret_cast<const bf16_t*>(cin_b)[off])
-                                 : reinterpret_cast<const float*>(cin_b)[off];
-            val += beta * ci;
-          }
-          if (row == col) val += g.diag;
-          stored = (g.c_dt == BF16) ? bf2f(f2bf(val)) : val;
-          if (c_b) {
-            const int64_t off = (int64_t)row * g.ldc + col;
-            const int64_t offt = (int64_t)col * g.ldc + row;
-            if (g.c_dt == BF16) {
-              reinterpret_cast<bf16_t*>(c_b)[off] = f2bf(val);
-              if (mirror) reinterpret_cast<bf16_t*>(c_b)[offt] = f2bf(val);
-            } else {
-              reinterpret_cast<float*>(c_b)[off] = val;
-              if (mirror) reinterpret_cast<float*>(c_b)[offt] = val;
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WT + i * 32 + (v >> 2) * 8 + lk * 4 + (v & 3);
+          const int col = n0 + wn * WT + j * 32 + lr;
+          float stored = 0.f;
+          if (row < Mg && col < Ng) {
+            float val = alpha * acc[i][j][v];
+            if (cin_b) {
+              const int64_t off = (int64_t)row * ldcin + col;
+              const float ci = cbf ? bf2f(reinterpret_cast<const bf16_t*>(cin_b)[off])
+                                   : reinterpret_cast<const float*>(cin_b)[off];
+              val += beta * ci;
+            }
+            if (row == col) val += diag;
+            stored = cbf ? bf2f(f2bf(val)) : val;
+            if (c_b) {
+              const int64_t off = (int64_t)row * ldc + col;
+              const int64_t offt = (int64_t)col * ldc + row;
+              if (cbf) {
+                reinterpret_cast<bf16_t*>(c_b)[off] = f2bf(val);
+                if (mirror) reinterpret_cast<bf16_t*>(c_b)[offt] = f2bf(val);
+              } else {
+                reinterpret_cast<float*>(c_b)[off] = val;
+                if (mirror) reinterpret_cast<float*>(c_b)[offt] = val;
+              }
+            }
+            if (c2_b)
+              c2_b[(int64_t)row * ldc2 + col] = c2_scale * val + (row == col ? c2_diag : 0.f);
+            if (resid) {
+              const float d = val - (row == col ? 1.f : 0.f);
+              rs += d * d;
             }
           }
-          if (c2_b) {
-            c2_b[(int64_t)row * g.ldc2 + col] = g.c2_scale * val + (row == col ? g.c2_diag : 0.f);
-          }
-          if (g.resid) {
-            const float d = val - (row == col ? 1.f : 0.f);
-            rs += d * d;
-          }
+          acc[i][j][v] = stored;
         }
-        acc[i][j][v] = stored;
-      }
+  }
   if (g.bits) {
     // Signs of the stored values, packed: for fixed (i, v) the ballot over
     // the wave of block j holds row R (lanes 0-31) and row R + 4 (lanes
