@@ -481,29 +481,61 @@ __global__ __launch_bounds__(NT, (T == 128 && sizeof(TM) == 4) ? 3 : 1) void k_g
   const bool a_fast_rows = kg.a_aligned && (m0 + T) <= g.M;
   const bool b_fast_rows = kg.b_aligned && (n0 + T) <= g.N;
   const int nk = (g.K + BK - 1) / BK;
-  SA sa;
-  SB sb;
-  sa.load(A, g.a.ld, m0, g.M, 0, g.K, a_fast_rows && BK <= g.K);
-  sb.load(B, g.b.ld, n0, g.N, 0, g.K, b_fast_rows && BK <= g.K);
-  sa.store(As[0]);
-  sb.store(Bs[0]);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * BK;
-      const bool k_in = (k0 + BK) <= g.K;
-      sa.load(A, g.a.ld, m0, g.M, k0, g.K, a_fast_rows && k_in);
-      sb.load(B, g.b.ld, n0, g.N, k0, g.K, b_fast_rows && k_in);
-    }
-    Mma<TM>::template step<WB, LA, LB>(As[cur], Bs[cur], wm, wn, acc);
-    if (more) {
-      // stage cur ^ 1 was last read by slab kt - 1, before the previous barrier
-      sa.store(As[cur ^ 1]);
-      sb.store(Bs[cur ^ 1]);
-    }
+  auto load = [&](SA& sa, SB& sb, int kt) {
+    const int k0 = kt * BK;
+    const bool k_in = (k0 + BK) <= g.K;
+    sa.load(A, g.a.ld, m0, g.M, k0, g.K, a_fast_rows && k_in);
+    sb.load(B, g.b.ld, n0, g.N, k0, g.K, b_fast_rows && k_in);
+  };
+  if constexpr (sizeof(TM) == 4 && T == 64) {
+    // Two slabs in flight: slab t + 2's loads are issued before slab t's
+    // MFMAs, slab t + 1 (loaded one step earlier) goes to LDS after them.
+    // One slab's MFMAs (16 per wave) are shorter than a load's latency, so
+    // with one slab in flight the loop waited on every load.  The two
+    // register sets alternate, hence the loop by pairs.
+    SA sa0, sa1;
+    SB sb0, sb1;
+    load(sa0, sb0, 0);
+    if (nk > 1) load(sa1, sb1, 1);
+    sa0.store(As[0]);
+    sb0.store(Bs[0]);
     __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      if (kt + 2 < nk) load(sa0, sb0, kt + 2);
+      Mma<TM>::template step<WB, LA, LB>(As[0], Bs[0], wm, wn, acc);
+      if (kt + 1 < nk) {   // stage 1 was last read by slab kt - 1, before the last barrier
+        sa1.store(As[1]);
+        sb1.store(Bs[1]);
+      }
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      if (kt + 3 < nk) load(sa1, sb1, kt + 3);
+      Mma<TM>::template step<WB, LA, LB>(As[1], Bs[1], wm, wn, acc);
+      if (kt + 2 < nk) {
+        sa0.store(As[0]);
+        sb0.store(Bs[0]);
+      }
+      __syncthreads();
+    }
+  } else {
+    SA sa;
+    SB sb;
+    load(sa, sb, 0);
+    sa.store(As[0]);
+    sb.store(Bs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) load(sa, sb, kt + 1);
+      Mma<TM>::template step<WB, LA, LB>(As[cur], Bs[cur], wm, wn, acc);
+      if (more) {
+        // stage cur ^ 1 was last read by slab kt - 1, before the previous barrier
+        sa.store(As[cur ^ 1]);
+        sb.store(Bs[cur ^ 1]);
+      }
+      __syncthreads();
+    }
   }
 
   // ---------------- epilogue
