@@ -19,13 +19,14 @@
 // RC operand (row index contiguous in HBM) is transposed in registers on its
 // way into LDS, except with float32 MFMA input: there it is copied as it
 // lies, [k][row], and a fragment is two dword reads (the float32 MFMA takes
-// one k per register, so no transpose is needed at all).  Interior tiles with aligned leading dimensions take the
-// vector path, edge tiles load element by element with zero fill, so any
-// M, N, K >= 1 is handled.
+// one k per register, so no transpose is needed at all).  Interior tiles
+// with aligned leading dimensions take the vector path, edge tiles load
+// element by element with zero fill, so any M, N, K >= 1 is handled.
 //
 // Pipelining: two LDS stages.  The global loads of k-slab t+1 are issued into
 // registers before the MFMAs of slab t, and written to the other LDS stage
 // after them, so their latency hides behind the MFMAs; one barrier per slab.
+// The float32 64 tile keeps two slabs in flight in two register sets.
 //
 // MFMA lane layout relied on (32 x 32 output blocks): for the A operand lane
 // l supplies row l % 32, for the B operand column l % 32, each with a group
@@ -54,10 +55,9 @@ template <int T> struct Cfg<bf16_t, T> {
   static constexpr int LDK = 32 + 8;  // LDS row pitch in elements (80 bytes)
 };
 template <int T> struct Cfg<float, T> {
-  // The 64 tile takes 32 k per slab, so that a wave's 16 MFMAs of a slab
-  // outlast the global latency of the next slab's register prefetch; the 128
-  // tile keeps 16 (its wave issues 16 MFMAs per slab already, and a deeper
-  // slab would halve the blocks an LDS-bound CU holds).
+  // The 64 tile takes 32 k per slab (a wave's one 32 x 32 block then gets 16
+  // MFMAs per slab); the 128 tile keeps 16 (its wave issues 32 MFMAs per slab
+  // over four blocks already, and a deeper slab would cost the CU blocks).
   static constexpr int BK = T == 64 ? 32 : 16;
   static constexpr int LDK = BK + 4;  // 144 or 80 bytes
   // pitch of a [k][row] stage (RC operands): the two k rows that the halves
