@@ -258,6 +258,28 @@ def test_ns_polar_matches_oracle(gpu_lib, case):
         assert err <= TOL[dt], (k, err)
 
 
+def test_float32_ns_large_tiles_equal_small_tiles(gpu_lib):
+    """Float32 NS on 16 problems of 1024 x 2048 runs its Gram, quintic and
+    apply launches on 128 x 128 tiles (enough tiles to fill the chip: the
+    lean interior epilogue with Cin, mirrored 16-byte stores and four blocks
+    per wave); one of the problems alone takes 64 x 64 tiles.  Both tile
+    sizes sum every product over k in the same order, so the results must be
+    bit-identical; one problem is also checked against the oracle."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    b, m, n = 16, 1024, 2048
+    rng = np.random.default_rng(1128)
+    x = torch.from_numpy((0.01 * rng.standard_normal((b, m, n))).astype(np.float32)).cuda()
+    p = sm.NSParams(iters=2, a=1.8, b=-0.6, c=0.04)
+    u = sm.ns_polar(x, params=p)
+    torch.cuda.synchronize()
+    for k in (0, 11):
+        one = sm.ns_polar(x[k:k + 1].contiguous(), params=p)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0].view(torch.int32), u[k].view(torch.int32)), k
+    want = O.ns_polar(to_np(x[11]), O.NSParams(iters=2, a=1.8, b=-0.6, c=0.04), normalize=True)
+    assert rel_fro(to_np(u[11]), want) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("m,n,iters,a,gram_form", [
     (768, 3072, 5, 1.5, True), (3072, 768, 5, 1.5, True), (384, 1152, 2, 1.5, True),
     (384, 640, 5, 1.5, True), (1920, 640, 6, A2, True), (768, 768, 5, 1.5, False),
