@@ -354,7 +354,8 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
  * Errors: as sm_step; SM_ERR_UNSUPPORTED for SM_CACHE_MUON (its kernels store
  * t with each refresh) or while kernel-time accounting is enabled;
  * SM_ERR_HIP if capture or instantiation fails.  *out is NULL on error.
- * sm_graph_destroy(NULL) is a no-op.
+ * sm_graph_destroy releases the graph and does not wait: call it once the
+ * replays enqueued so far have finished.  sm_graph_destroy(NULL) is a no-op.
  * ---------------------------------------------------------------------- */
 typedef struct sm_graph_s* sm_graph;
 sm_status sm_step_graph(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t,

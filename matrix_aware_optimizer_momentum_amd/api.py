@@ -428,8 +428,10 @@ class StepGraph:
         B.check(B.lib().sm_graph_launch(self._h, _stream()), "sm_graph_launch")
 
     def close(self):
+        """Destroys the graph once every replay enqueued so far has finished."""
         if self._h is not None:
             h, self._h = self._h, None
+            torch.cuda.synchronize(self._call.ws.device)
             B.check(B.lib().sm_graph_destroy(h), "sm_graph_destroy")
 
     def __del__(self):
