@@ -276,6 +276,58 @@ def copy_calibration():
 
 
 
+def attainable_rates(sm, torch):
+    """What the chip reaches at all on this machine, beside its nominal peaks: the
+    MFMA ceiling probe (a bf16 GEMM k loop of the NS kernels' tile shape with no
+    global memory traffic; fragments from LDS, and rotated in registers) and a
+    plain 1 GiB device copy.  Medians of three timed runs after one warm-up."""
+    out = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for lds, key in ((True, "lds_operands"), (False, "register_operands")):
+        rates = []
+        for rep in range(4):
+            e0, e1 = _events(torch)
+            e0.record()
+            flops = sm.mfma_ceiling(out, 256, 100000, lds)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep:
+                rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[key] = sorted(rates)[1]
+    nbytes = 1 << 30
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    y.copy_(x)
+    rates = []
+    for _ in range(3):
+        e0, e1 = _events(torch)
+        e0.record()
+        y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x, y, out
+    return {"mfma_loop_tflops": res, "copy_gbs": sorted(rates)[1],
+            "probe": "sm_mfma_ceiling: 256 workgroups x 4 waves, each 100000 k16 slices of "
+                     "16 v_mfma_f32_32x32x16_bf16 on a 128x128 float32 block; device copy 1 GiB"}
+
+
+def add_attainable(rl, att):
+    """Attach the measured ceiling to a roofline object (its `peak` and `frac`
+    stay the nominal ones)."""
+    if not rl or att is None:
+        return rl
+    if rl.get("bound") == "mfma" and rl.get("unit") == "TFLOP/s" and rl.get("peak") == 2500.0:
+        ceil = att["mfma_loop_tflops"]["lds_operands"]
+        rl["attainable"] = {"peak": ceil, "frac": rl["achieved"] / ceil,
+                            "source": "MFMA ceiling probe, LDS operands"}
+    elif rl.get("bound") == "hbm":
+        ceil = att["copy_gbs"]
+        rl["attainable"] = {"peak": ceil, "frac": rl["achieved"] / ceil,
+                            "source": "plain 1 GiB device copy"}
+    return rl
+
+
 def _tdt(dt):
     import torch
     return torch.bfloat16 if dt == "bf16" else torch.float32
@@ -830,6 +882,12 @@ def main():
             extra["variants"] = variants
     del mats, call
     torch.cuda.empty_cache()
+    att = attainable_rates(sm, torch)
+    add_attainable(roofline, att)
+    if "ns_tflops" in extra and wl.mdt == "bf16":
+        extra["ns_attainable_frac"] = extra["ns_tflops"] / att["mfma_loop_tflops"]["lds_operands"]
+    for typ, rec in extra.get("per_step_type", {}).items():
+        add_attainable(rec.get("roofline"), att)
 
     out = {
         "metric": METRIC,
@@ -851,6 +909,7 @@ def main():
                    "period": wl.period, "muon_steps_timed": n_muon,
                    "weights": wl.wdt, "momentum": wl.mdt, "grads": wl.gdt},
         "roofline": roofline,
+        "attainable": att,
         **extra,
         "kernels": kinds,
     }
@@ -862,6 +921,8 @@ def main():
         print("bench: sub-objects resnet50, single_256", file=sys.stderr, flush=True)
         out["resnet50"] = sign_muon_sub(sm, torch, W, args, 3, variants=False)
         out["single_256"] = sign_muon_sub(sm, torch, W, args, 1, steps=100, variants=False)
+        for key in ("gpt2_small", "resnet50", "single_256"):
+            add_attainable(out[key].get("roofline"), att)
     if not args.no_cpu:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -401,6 +401,23 @@ sm_status sm_profile_read(int kind, double* ms_total, int64_t* launches, double*
 sm_status sm_profile_read_bytes(int kind, double* bytes);
 const char* sm_kernel_kind_name(int kind);
 
+/* ------------------------------------------------------------------------
+ * MFMA ceiling probe (for benchmarks; not part of the method).
+ * The NS GEMMs are priced against the chip's nominal bf16 dense peak, which
+ * assumes every matrix pipe busy at the top shader clock; under a sustained
+ * matrix load the clock drops.  This call measures the rate a bf16 GEMM k
+ * loop of the NS kernels' tile shape can reach at all: `blocks` workgroups of
+ * four waves, each wave running `iters` k16 slices of sixteen
+ * v_mfma_f32_32x32x16_bf16 on a 128x128 float32 accumulator block, with the
+ * fragments read from LDS every slice (lds_operands = 1) or rotated in
+ * registers (0).  It executes blocks * 4 * iters * 16 * 32768 flops and
+ * touches no global memory except `out`: blocks * 256 floats of device
+ * memory (caller-owned, 4-byte aligned), which receives per-thread sums of
+ * the accumulators.  blocks: 1..65536, iters: 1..10^7; SM_ERR_ARG for a null
+ * or misaligned out, SM_ERR_SHAPE otherwise.  Time it with events on `s`.
+ * ---------------------------------------------------------------------- */
+sm_status sm_mfma_ceiling(int lds_operands, int blocks, int iters, float* out, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -443,6 +443,17 @@ class StepGraph:
 
 # ------------------------------------------------------------------ kernel accounting
 
+def mfma_ceiling(out: torch.Tensor, blocks: int, iters: int, lds_operands: bool = True) -> int:
+    """Enqueue the MFMA ceiling probe (sm_mfma_ceiling) on the current stream;
+    returns the flops it executes.  `out` is a float32 device tensor of at
+    least blocks * 256 entries."""
+    _expect(out, "out", dtype=torch.float32, min_numel=blocks * 256)
+    B.check(B.lib().sm_mfma_ceiling(int(bool(lds_operands)), blocks, iters,
+                                    ctypes.c_void_p(out.data_ptr()), _stream()),
+            "sm_mfma_ceiling")
+    return blocks * 4 * iters * 16 * 32768
+
+
 def profile_enable(on: bool = True):
     B.check(B.lib().sm_profile_enable(int(on)), "sm_profile_enable")
 

@@ -313,3 +313,13 @@ def test_noalloc_entry_point_rejects_oversized_problems_on_the_host():
                                    B.BF16, 4, 4096, 4096, 1, ctypes.byref(p), None) == 4
     assert lib.sm_ns_polar_noalloc(None, None, B.BF16, 1, 8, 8, 1, ctypes.byref(p), None) == 1
     assert lib.sm_last_hip_error() == 0
+
+
+def test_mfma_ceiling_probe_rejects_on_the_host():
+    lib = B.lib()
+    assert lib.sm_mfma_ceiling(1, 256, 100, None, None) == 1                    # null out
+    assert lib.sm_mfma_ceiling(1, 256, 100, ctypes.c_void_p(0x1002), None) == 1  # misaligned
+    assert lib.sm_mfma_ceiling(1, 0, 100, ctypes.c_void_p(0x1000), None) == 2
+    assert lib.sm_mfma_ceiling(0, 65537, 100, ctypes.c_void_p(0x1000), None) == 2
+    assert lib.sm_mfma_ceiling(0, 256, 0, ctypes.c_void_p(0x1000), None) == 2
+    assert lib.sm_mfma_ceiling(0, 256, 10000001, ctypes.c_void_p(0x1000), None) == 2

@@ -571,3 +571,26 @@ def test_cache_fidelity_chain_matches_oracle(gpu_lib, dt, shape):
     assert abs(err.item() - err_or) <= tol * max(err_or, 1.0), (err.item(), err_or)
     assert abs(dist.item() - dist_or) <= tol, (dist.item(), dist_or)
     assert dist_or > 0.03                           # the stale cache is measurably off
+
+
+# ------------------------------------------------------------------ measurement probe
+
+@pytest.mark.parametrize("lds", [True, False])
+def test_mfma_ceiling_probe_runs_and_is_deterministic(gpu_lib, lds):
+    """The benchmark's MFMA ceiling probe (not a step of the method): it
+    writes finite per-thread sums of its accumulators for every workgroup,
+    the same bits on a second run, and reports the flops it executes."""
+    import matrix_aware_optimizer_momentum_amd as sm
+    blocks, iters = 8, 64
+    out = torch.full((blocks * 256 + 5,), -7.0, dtype=torch.float32, device="cuda")
+    flops = sm.mfma_ceiling(out, blocks, iters, lds)
+    first = out.clone()
+    sm.mfma_ceiling(out, blocks, iters, lds)
+    torch.cuda.synchronize()
+    assert flops == blocks * 4 * iters * 16 * 32768
+    body = first[: blocks * 256]
+    assert torch.isfinite(body).all() and (body != 0).any()
+    assert torch.equal(out, first)
+    assert (out[blocks * 256:] == -7.0).all()          # nothing written past the end
+    with pytest.raises(ValueError):
+        sm.mfma_ceiling(out[:100], blocks, iters, lds)
