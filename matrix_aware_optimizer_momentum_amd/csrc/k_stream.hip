@@ -354,18 +354,32 @@ __global__ __launch_bounds__(kThreads) void k_sign_pack(const T* x, int64_t coun
   }
 }
 
+// int8 signs: a thread keeps kSignUnroll chunks' loads in flight before it
+// writes any signs (with one 16-byte load per thread at a time the int8
+// signs ran at 4.8-5.3 TB/s on large inputs, with four 5.6-5.9).  Block
+// iteration c takes chunks c * kSignUnroll .. + kSignUnroll - 1.
+constexpr int kSignUnroll = 4;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_sign_int8(const T* x, int64_t count, int8_t* s,
                                                         bool vec) {
   const int b = blockIdx.y;
   const T* xp = x + (int64_t)b * count;
   int8_t* sp = s + (int64_t)b * count;
-  const int64_t n8 = (count + 7) / 8;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8;
-       i += (int64_t)gridDim.x * kThreads) {
-    float v[8];
-    load8_tail<T>(xp, 8 * i, count, vec, v);
-    store_signs8(sp, 8 * i, count, v);
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  for (int64_t c0 = (int64_t)blockIdx.x * kSignUnroll; c0 < nchunks;
+       c0 += (int64_t)gridDim.x * kSignUnroll) {
+    float v[kSignUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kSignUnroll; ++u) {
+      const int64_t e0 = (c0 + u) * kChunk + (int64_t)threadIdx.x * 8;
+      if (c0 + u < nchunks && e0 < count) load8_tail<T>(xp, e0, count, vec, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kSignUnroll; ++u) {
+      const int64_t e0 = (c0 + u) * kChunk + (int64_t)threadIdx.x * 8;
+      if (c0 + u < nchunks && e0 < count) store_signs8(sp, e0, count, v[u]);
+    }
   }
 }
 
@@ -765,12 +779,20 @@ __global__ __launch_bounds__(kThreads) void k_compact_flags(const int32_t* flags
   if (threadIdx.x == 0) dyn[0] = base;
 }
 
+// Blocks per problem of a grid-stride streaming launch (blockIdx.y = the
+// problem) whose problems need at most `need` block iterations each, and
+// about `total` blocks in all, never more: blocks run in rounds of what the
+// CUs hold at once, and a total just above a whole number of rounds of long
+// grid-stride blocks leaves a lone last round.
+inline unsigned blocks_per_problem(int64_t need, int nprob, int64_t total) {
+  int64_t want = total / (nprob > 0 ? nprob : 1);
+  if (want < 1) want = 1;
+  return (unsigned)(need < want ? need : want);
+}
+
 inline int stream_blocks(int64_t count, int nprob) {
   // enough blocks in flight to fill 256 CUs several times over
-  int64_t per = (count + kChunk - 1) / kChunk;
-  int64_t want = (4096 + nprob - 1) / nprob;
-  if (want < 1) want = 1;
-  return (int)(per < want ? per : want);
+  return (int)blocks_per_problem((count + kChunk - 1) / kChunk, nprob, 4096);
 }
 
 }  // namespace
@@ -874,10 +896,11 @@ sm_status launch_sign_int8(const void* x, int dt, int nprob, int64_t count, int8
                            hipStream_t s) {
   if (nprob <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0 && (reinterpret_cast<uintptr_t>(x) % 16) == 0;
-  const int64_t n8 = (count + 7) / 8;
-  int64_t want = (4096 + nprob - 1) / nprob;
-  int64_t need = (n8 + kThreads - 1) / kThreads;
-  dim3 grid((unsigned)(need < want ? need : want), nprob);
+  // one block iteration per block (up to about a million blocks): short
+  // blocks leave a tail of one iteration
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  dim3 grid(blocks_per_problem((nchunks + kSignUnroll - 1) / kSignUnroll, nprob, 1 << 20),
+            nprob);
   prof_begin(SM_K_SIGN_PACK, (double)nprob * count * (dt_size(dt) + 1.0), s);
   SM_DISPATCH_DT(dt, T,
       hipLaunchKernelGGL((k_sign_int8<T>), grid, dim3(kThreads), 0, s, (const T*)x, count, s8,
@@ -892,11 +915,10 @@ sm_status launch_vote(int enc, const void* signs, int M, int64_t stride, int64_t
   if (nmat <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
   const int64_t n8 = (count + 7) / 8;
-  int64_t want = (4096 + nmat - 1) / nmat;
   // bits: one block iteration per tile of kThreads words; int8: of kThreads 8-entry groups
   int64_t need = enc == SM_ENC_BITS ? ((count + 63) / 64 + kThreads - 1) / kThreads
                                     : (n8 + kThreads - 1) / kThreads;
-  dim3 grid((unsigned)(need < want ? need : want), nmat);
+  dim3 grid(blocks_per_problem(need, nmat, 4096), nmat);
   const double sign_bytes = enc == SM_ENC_BITS ? M / 8.0 : (double)M;
   double bytes = (double)nmat * count *
                  (sign_bytes + (update ? 2.0 : 1.0) * dt_size(wdt) + (vote_out ? 1.0 : 0.0));
@@ -947,8 +969,7 @@ sm_status launch_vote_tbl(int enc, int M, const VoteMat* mats, int nmat, int wdt
     const bool stream = wbytes > kStreamBytes;
     // about 64 blocks per CU in all: the matrices' sizes differ, and short
     // blocks even out the launch's tail
-    const int64_t want = (16384 + n - 1) / n;
-    const dim3 grid((unsigned)(need < want ? need : want), n);
+    const dim3 grid(blocks_per_problem(need, n, 16384), n);
     prof_begin(SM_K_VOTE_UPDATE, bytes, s);
     if (enc == SM_ENC_BITS) {
       SM_DISPATCH_DT(wdt, TW,
@@ -968,9 +989,7 @@ sm_status launch_polar_update(const void* d, int ddt, int nmat, int64_t count, c
   if (nmat <= 0 || count <= 0) return SM_OK;
   const bool vec = (count % 8) == 0;
   const int64_t n8 = (count + 7) / 8;
-  int64_t want = (4096 + nmat - 1) / nmat;
-  int64_t need = (n8 + kThreads - 1) / kThreads;
-  dim3 grid((unsigned)(need < want ? need : want), nmat);
+  dim3 grid(blocks_per_problem((n8 + kThreads - 1) / kThreads, nmat, 4096), nmat);
   const bool stream = (double)nmat * count * dt_size(wdt) > kStreamBytes;
   prof_begin(SM_K_POLAR_UPDATE, (double)nmat * count * (dt_size(ddt) + 2.0 * dt_size(wdt)), s);
   SM_DISPATCH_DT(ddt, TD, SM_DISPATCH_DT(wdt, TW,
