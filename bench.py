@@ -278,17 +278,21 @@ def copy_calibration():
 
 def attainable_rates(sm, torch):
     """What the chip reaches at all on this machine, beside its nominal peaks: the
-    MFMA ceiling probe (a bf16 GEMM k loop of the NS kernels' tile shape with no
-    global memory traffic; fragments from LDS, and rotated in registers) and a
-    plain 1 GiB device copy.  Medians of three timed runs after one warm-up."""
+    MFMA ceiling probe (a bf16 GEMM k loop of the NS kernels' tile shape with
+    its fragments read from LDS, or rotated in registers, and no global
+    memory; and the same loop with the NS kernels' operand staging from an
+    L2-sized buffer) and a plain 1 GiB device copy.  Medians of three timed
+    runs after one warm-up."""
     out = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    src = torch.empty(1 << 19, dtype=torch.float32, device="cuda").uniform_()   # 2 MB
     res = {}
-    for lds, key in ((True, "lds_operands"), (False, "register_operands")):
+    for mode, key in ((1, "lds_operands"), (0, "register_operands"),
+                      (2, "lds_operands_with_ns_staging")):
         rates = []
         for rep in range(4):
             e0, e1 = _events(torch)
             e0.record()
-            flops = sm.mfma_ceiling(out, 256, 100000, lds)
+            flops = sm.mfma_ceiling(out, 256, 100000, mode, src)
             e1.record()
             torch.cuda.synchronize()
             if rep:
@@ -306,10 +310,12 @@ def attainable_rates(sm, torch):
         e1.record()
         torch.cuda.synchronize()
         rates.append(2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del x, y, out
+    del x, y, out, src
     return {"mfma_loop_tflops": res, "copy_gbs": sorted(rates)[1],
             "probe": "sm_mfma_ceiling: 256 workgroups x 4 waves, each 100000 k16 slices of "
-                     "16 v_mfma_f32_32x32x16_bf16 on a 128x128 float32 block; device copy 1 GiB"}
+                     "16 v_mfma_f32_32x32x16_bf16 on a 128x128 float32 block (fragments from "
+                     "LDS / registers; with staging: 8 direct-to-LDS loads per wave per k32 "
+                     "step from a 2 MB buffer and one barrier); device copy 1 GiB"}
 
 
 def add_attainable(rl, att):
@@ -319,8 +325,10 @@ def add_attainable(rl, att):
         return rl
     if rl.get("bound") == "mfma" and rl.get("unit") == "TFLOP/s" and rl.get("peak") == 2500.0:
         ceil = att["mfma_loop_tflops"]["lds_operands"]
+        stg = att["mfma_loop_tflops"]["lds_operands_with_ns_staging"]
         rl["attainable"] = {"peak": ceil, "frac": rl["achieved"] / ceil,
-                            "source": "MFMA ceiling probe, LDS operands"}
+                            "source": "MFMA ceiling probe, LDS operands",
+                            "with_ns_staging": {"peak": stg, "frac": rl["achieved"] / stg}}
     elif rl.get("bound") == "hbm":
         ceil = att["copy_gbs"]
         rl["attainable"] = {"peak": ceil, "frac": rl["achieved"] / ceil,

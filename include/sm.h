@@ -406,17 +406,26 @@ const char* sm_kernel_kind_name(int kind);
  * The NS GEMMs are priced against the chip's nominal bf16 dense peak, which
  * assumes every matrix pipe busy at the top shader clock; under a sustained
  * matrix load the clock drops.  This call measures the rate a bf16 GEMM k
- * loop of the NS kernels' tile shape can reach at all: `blocks` workgroups of
- * four waves, each wave running `iters` k16 slices of sixteen
+ * loop of the NS kernels' tile shape can reach: `blocks` workgroups of four
+ * waves, each wave running `iters` k16 slices of sixteen
  * v_mfma_f32_32x32x16_bf16 on a 128x128 float32 accumulator block, with the
- * fragments read from LDS every slice (lds_operands = 1) or rotated in
- * registers (0).  It executes blocks * 4 * iters * 16 * 32768 flops and
- * touches no global memory except `out`: blocks * 256 floats of device
- * memory (caller-owned, 4-byte aligned), which receives per-thread sums of
- * the accumulators.  blocks: 1..65536, iters: 1..10^7; SM_ERR_ARG for a null
- * or misaligned out, SM_ERR_SHAPE otherwise.  Time it with events on `s`.
+ * fragments
+ *   mode 0: rotated in registers;
+ *   mode 1: read from LDS every slice (no global memory in the loop);
+ *   mode 2: as mode 1, plus per two slices the NS kernels' operand staging
+ *           (eight 16-byte direct-to-LDS loads per wave from `src`, a wait
+ *           for the step before last, one workgroup barrier).
+ * It executes blocks * 4 * iters * 16 * 32768 flops.  out: blocks * 256
+ * floats of device memory (caller-owned, 4-byte aligned) that receive
+ * per-thread sums of the accumulators.  src (mode 2 only, else ignored):
+ * src_bytes of device memory, a power of two from 64 KB to 64 MB, 16-byte
+ * aligned, only read (keep it L2-sized to leave out cache misses).
+ * blocks: 1..65536, iters: 1..10^7.  SM_ERR_ARG for a bad mode or a null or
+ * misaligned pointer, SM_ERR_SHAPE for sizes out of range.  Time it with
+ * events on `s`.
  * ---------------------------------------------------------------------- */
-sm_status sm_mfma_ceiling(int lds_operands, int blocks, int iters, float* out, hipStream_t s);
+sm_status sm_mfma_ceiling(int mode, int blocks, int iters, const void* src, size_t src_bytes,
+                          float* out, hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -86,7 +86,7 @@ SIGNATURES = {
     "sm_profile_read": (c_int, [c_int, P(c_double), P(c_int64), P(c_double)]),
     "sm_profile_read_bytes": (c_int, [c_int, P(c_double)]),
     "sm_kernel_kind_name": (c_char_p, [c_int]),
-    "sm_mfma_ceiling": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p]),
+    "sm_mfma_ceiling": (c_int, [c_int, c_int, c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 _lib = None

@@ -443,12 +443,20 @@ class StepGraph:
 
 # ------------------------------------------------------------------ kernel accounting
 
-def mfma_ceiling(out: torch.Tensor, blocks: int, iters: int, lds_operands: bool = True) -> int:
+def mfma_ceiling(out: torch.Tensor, blocks: int, iters: int, mode: int = 1,
+                 src: Optional[torch.Tensor] = None) -> int:
     """Enqueue the MFMA ceiling probe (sm_mfma_ceiling) on the current stream;
     returns the flops it executes.  `out` is a float32 device tensor of at
-    least blocks * 256 entries."""
+    least blocks * 256 entries; mode 2 reads `src` (a device tensor whose
+    byte size is a power of two from 64 KB to 64 MB)."""
     _expect(out, "out", dtype=torch.float32, min_numel=blocks * 256)
-    B.check(B.lib().sm_mfma_ceiling(int(bool(lds_operands)), blocks, iters,
+    sp, sb = None, 0
+    if mode == 2:
+        if src is None:
+            raise ValueError("mode 2 needs a source buffer")
+        _dev(src, "src")
+        sp, sb = ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size()
+    B.check(B.lib().sm_mfma_ceiling(int(mode), blocks, iters, sp, sb,
                                     ctypes.c_void_p(out.data_ptr()), _stream()),
             "sm_mfma_ceiling")
     return blocks * 4 * iters * 16 * 32768

@@ -317,9 +317,18 @@ def test_noalloc_entry_point_rejects_oversized_problems_on_the_host():
 
 def test_mfma_ceiling_probe_rejects_on_the_host():
     lib = B.lib()
-    assert lib.sm_mfma_ceiling(1, 256, 100, None, None) == 1                    # null out
-    assert lib.sm_mfma_ceiling(1, 256, 100, ctypes.c_void_p(0x1002), None) == 1  # misaligned
-    assert lib.sm_mfma_ceiling(1, 0, 100, ctypes.c_void_p(0x1000), None) == 2
-    assert lib.sm_mfma_ceiling(0, 65537, 100, ctypes.c_void_p(0x1000), None) == 2
-    assert lib.sm_mfma_ceiling(0, 256, 0, ctypes.c_void_p(0x1000), None) == 2
-    assert lib.sm_mfma_ceiling(0, 256, 10000001, ctypes.c_void_p(0x1000), None) == 2
+    ok = ctypes.c_void_p(0x1000)
+    assert lib.sm_mfma_ceiling(1, 256, 100, None, 0, None, None) == 1               # null out
+    assert lib.sm_mfma_ceiling(1, 256, 100, None, 0, ctypes.c_void_p(0x1002), None) == 1
+    assert lib.sm_mfma_ceiling(3, 256, 100, None, 0, ok, None) == 1                 # bad mode
+    assert lib.sm_mfma_ceiling(-1, 256, 100, None, 0, ok, None) == 1
+    assert lib.sm_mfma_ceiling(1, 0, 100, None, 0, ok, None) == 2
+    assert lib.sm_mfma_ceiling(0, 65537, 100, None, 0, ok, None) == 2
+    assert lib.sm_mfma_ceiling(0, 256, 0, None, 0, ok, None) == 2
+    assert lib.sm_mfma_ceiling(0, 256, 10000001, None, 0, ok, None) == 2
+    # mode 2: the source buffer is checked too
+    assert lib.sm_mfma_ceiling(2, 256, 100, None, 1 << 21, ok, None) == 1          # null src
+    assert lib.sm_mfma_ceiling(2, 256, 100, ctypes.c_void_p(0x2008), 1 << 21, ok, None) == 1
+    assert lib.sm_mfma_ceiling(2, 256, 100, ctypes.c_void_p(0x2000), 3 << 20, ok, None) == 2
+    assert lib.sm_mfma_ceiling(2, 256, 100, ctypes.c_void_p(0x2000), 1 << 15, ok, None) == 2
+    assert lib.sm_mfma_ceiling(2, 256, 100, ctypes.c_void_p(0x2000), 1 << 27, ok, None) == 2

@@ -575,22 +575,26 @@ def test_cache_fidelity_chain_matches_oracle(gpu_lib, dt, shape):
 
 # ------------------------------------------------------------------ measurement probe
 
-@pytest.mark.parametrize("lds", [True, False])
-def test_mfma_ceiling_probe_runs_and_is_deterministic(gpu_lib, lds):
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_mfma_ceiling_probe_runs_and_is_deterministic(gpu_lib, mode):
     """The benchmark's MFMA ceiling probe (not a step of the method): it
     writes finite per-thread sums of its accumulators for every workgroup,
-    the same bits on a second run, and reports the flops it executes."""
+    the same bits on a second run, reports the flops it executes, and in
+    mode 2 only reads its source buffer."""
     import matrix_aware_optimizer_momentum_amd as sm
     blocks, iters = 8, 64
     out = torch.full((blocks * 256 + 5,), -7.0, dtype=torch.float32, device="cuda")
-    flops = sm.mfma_ceiling(out, blocks, iters, lds)
+    src = torch.arange(1 << 16, dtype=torch.int32, device="cuda")     # 256 KB
+    src0 = src.clone()
+    flops = sm.mfma_ceiling(out, blocks, iters, mode, src)
     first = out.clone()
-    sm.mfma_ceiling(out, blocks, iters, lds)
+    sm.mfma_ceiling(out, blocks, iters, mode, src)
     torch.cuda.synchronize()
     assert flops == blocks * 4 * iters * 16 * 32768
     body = first[: blocks * 256]
     assert torch.isfinite(body).all() and (body != 0).any()
     assert torch.equal(out, first)
     assert (out[blocks * 256:] == -7.0).all()          # nothing written past the end
+    assert torch.equal(src, src0)
     with pytest.raises(ValueError):
-        sm.mfma_ceiling(out[:100], blocks, iters, lds)
+        sm.mfma_ceiling(out[:100], blocks, iters, mode, src)
