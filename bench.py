@@ -25,6 +25,7 @@ graph (`graph`: sm_step_graph, then sm_graph_launch per step).
   python bench.py [--steps K] [--warmup W] [--config {1..5}] [--no-cpu] [--no-sub]
   python bench.py --copy-calibration   # plain device copy of known size, for
                                        # scaling rocprofv3 FETCH_SIZE / WRITE_SIZE
+  python bench.py --attainable         # MFMA ceiling probe and device copy only
   python bench.py --fidelity [--gamma G] # CacheMuon fidelity diagnostic (config 4)
 
 roofline.traffic is the dominant kernel's HBM bytes per launch from the
@@ -70,6 +71,9 @@ def parse():
                     help="timed steps of each sub-object run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter scaling)")
+    ap.add_argument("--attainable", action="store_true",
+                    help="run only the MFMA ceiling probe and the device copy (the `attainable` "
+                         "object of the benchmark line)")
     ap.add_argument("--fidelity", action="store_true",
                     help="CacheMuon fidelity diagnostic instead of the benchmark line: per step, "
                          "the residual and the spectral distance of the cached direction from a "
@@ -315,7 +319,8 @@ def attainable_rates(sm, torch):
             "probe": "sm_mfma_ceiling: 256 workgroups x 4 waves, each 100000 k16 slices of "
                      "16 v_mfma_f32_32x32x16_bf16 on a 128x128 float32 block (fragments from "
                      "LDS / registers; with staging: 8 direct-to-LDS loads per wave per k32 "
-                     "step from a 2 MB buffer and one barrier); device copy 1 GiB"}
+                     "step from a 2 MB buffer, each awaited three steps later, and one "
+                     "barrier); device copy 1 GiB"}
 
 
 def add_attainable(rl, att):
@@ -800,6 +805,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.attainable:
+        print(json.dumps(attainable_rates(sm, torch)))
         return
     if args.fidelity:
         fidelity(args, sm, torch, W)

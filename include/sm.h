@@ -414,7 +414,7 @@ const char* sm_kernel_kind_name(int kind);
  *   mode 1: read from LDS every slice (no global memory in the loop);
  *   mode 2: as mode 1, plus per two slices the NS kernels' operand staging
  *           (eight 16-byte direct-to-LDS loads per wave from `src`, a wait
- *           for the step before last, one workgroup barrier).
+ *           for the loads of three steps before, one workgroup barrier).
  * It executes blocks * 4 * iters * 16 * 32768 flops.  out: blocks * 256
  * floats of device memory (caller-owned, 4-byte aligned) that receive
  * per-thread sums of the accumulators.  src (mode 2 only, else ignored):

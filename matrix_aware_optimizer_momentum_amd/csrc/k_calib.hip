@@ -14,8 +14,9 @@
 //   2  mode 1 plus the NS kernels' operand staging per k32 step (two
 //      slices): eight direct-to-LDS 16-byte loads per wave, in the NS
 //      kernels' issue form, from a caller buffer small enough to stay in L2,
-//      into an LDS area no fragment read touches, a wait for the loads of
-//      the step before last, and one workgroup barrier.
+//      into an LDS area no fragment read touches, a wait for the loads
+//      issued three steps before (the lead the NS kernels' five-stage ring
+//      gives a stage), and one workgroup barrier.
 // Modes 0 and 1 touch no global memory inside the loop: their rate bounds
 // any bf16 GEMM kernel with this tile shape on the same chip.  Mode 2 is
 // the NS kernels' k loop without cache misses, tile changes or epilogues.
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void k_mfma_ceiling(float* out, int iters, con
     }
     if constexpr (MODE == 2) {
       if ((it & 1) == 0) {   // between a step's slices: the stage wait and the barrier
-        wait_vm_probe<16>();
+        wait_vm_probe<24>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
