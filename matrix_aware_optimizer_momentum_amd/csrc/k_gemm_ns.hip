@@ -97,6 +97,7 @@ struct Grp {
   int tbl;                     // byte offset of the group's table in Args
   uint64_t* bits;              // apply: signs instead of C (see NsgGroup)
   int64_t bits_stride;
+  int bits_s8;                 // the signs as int8 (see NsgGroup)
   const int32_t* pred;         // per-problem store predicate (see NsgGroup), or null
   float* resid;                // probe: residual partials (see NsgGroup)
   const int32_t* dyn;          // device problem list (see NsgGroup), or null
@@ -940,6 +941,14 @@ __device__ __forceinline__ uint32_t writelane(uint32_t v, uint32_t val) {
   return (uint32_t)sm_llvm_writelane((int)val, LANE, (int)v);
 }
 
+// Four int8 signs from four sign bits (bit e set <=> byte e is -1, else +1):
+// each bit is moved to the low bit of its byte and scaled by 0xFE, so that
+// 0x01 + 0xFE = 0xFF; no byte carries into the next.
+__device__ __forceinline__ uint32_t s8x4_of_bits(uint32_t b) {
+  const uint32_t spread = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
+  return 0x01010101u + 0xFEu * spread;
+}
+
 // Writes the signs of this wave's 128 x 128 sub-tile of alpha * acc as packed
 // bits (the sign of each value rounded to bf16 exactly as epilogue() rounds
 // it, so the bits equal the sign packing of the stored direction): bit = 1
@@ -949,11 +958,14 @@ __device__ __forceinline__ uint32_t writelane(uint32_t v, uint32_t val) {
 // column blocks make one word per row, placed with writelane into the lane
 // that stores it (lane L: row L % 32 of the block, word L / 32).  Issues 4
 // stores, then drains this wave's memory operations (fewer stores than the
-// lenient wait after a plain epilogue assumes).
-template <bool SCALE>
+// lenient wait after a plain epilogue assumes).  S8: the lane expands its
+// word into the 64 int8 signs of those entries instead (-1 iff negative,
+// else +1; row pitch N bytes from s8) and stores them as four 16-byte
+// vectors, 16 stores per wave.
+template <bool SCALE, bool S8>
 __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_t* bits,
-                                              int64_t wpr, int M, int N, int wr0, int wc0,
-                                              float alpha) {
+                                              int8_t* s8, int64_t wpr, int M, int N, int wr0,
+                                              int wc0, float alpha) {
   const int lane = fresh_tid() & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -993,8 +1005,20 @@ __device__ __forceinline__ void epilogue_bits(const f32x16 (&acc)[4][4], uint64_
 #undef SM_BITS_QE
     const int row = wr0 + i * 32 + (lane & 31);
     const int col = wc0 + 64 * (lane >> 5);
-    if (row < M && col < N)
-      *reinterpret_cast<uint2*>(bits + (int64_t)row * wpr + (col >> 6)) = make_uint2(wlo, whi);
+    if (row < M && col < N) {
+      if constexpr (S8) {
+        // columns col .. col + 63 (N % 64 == 0: all inside the row)
+        uint4* dst = reinterpret_cast<uint4*>(s8 + (int64_t)row * N + col);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t b16 = ((c < 2 ? wlo : whi) >> (16 * (c & 1))) & 0xFFFFu;
+          dst[c] = make_uint4(s8x4_of_bits(b16 & 15u), s8x4_of_bits((b16 >> 4) & 15u),
+                              s8x4_of_bits((b16 >> 8) & 15u), s8x4_of_bits(b16 >> 12));
+        }
+      } else {
+        *reinterpret_cast<uint2*>(bits + (int64_t)row * wpr + (col >> 6)) = make_uint2(wlo, whi);
+      }
+    }
   }
   wait_vm<0>();
 }
@@ -1168,10 +1192,18 @@ void k_gemm_ns(Args args) {
     } else if constexpr (ROLE == ROLE_APPLY) {
       if (g.bits) {   // the last iteration of a vote-mode step: signs only
         uint64_t* bp = g.bits + (int64_t)tc.prob * g.bits_stride;
-        if (alpha == 1.f)
-          epilogue_bits<false>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
-        else
-          epilogue_bits<true>(acc, bp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+        if (g.bits_s8) {
+          int8_t* sp = reinterpret_cast<int8_t*>(bp);
+          if (alpha == 1.f)
+            epilogue_bits<false, true>(acc, bp, sp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+          else
+            epilogue_bits<true, true>(acc, bp, sp, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+        } else {
+          if (alpha == 1.f)
+            epilogue_bits<false, false>(acc, bp, nullptr, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+          else
+            epilogue_bits<true, false>(acc, bp, nullptr, g.N / 64, g.M, g.N, wr0, wc0, alpha);
+        }
       } else {
         barrier_nofence();
         if (alpha == 1.f)
@@ -1274,6 +1306,10 @@ bool gemm_ns_supported(const NsgGroup& G) {
   if (G.bits && (G.sym || G.N % 64 != 0 || (reinterpret_cast<uintptr_t>(G.bits) & 7u) ||
                  G.bits_stride < (int64_t)G.M * (G.N / 64)))
     return false;
+  if (G.bits && G.bits_s8 &&
+      ((reinterpret_cast<uintptr_t>(G.bits) & 15u) || G.bits_stride % 2 ||
+       8 * G.bits_stride < (int64_t)G.M * G.N))
+    return false;
   if (G.ident == 1 && G.K != G.M) return false;
   if (G.ident == 2 && G.K != G.N) return false;
   // both sides: symmetric lower-stored products of square matrices, one term
@@ -1360,6 +1396,7 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     g.alpha = G.alpha;
     g.bits = G.bits;
     g.bits_stride = G.bits_stride;
+    g.bits_s8 = G.bits_s8 ? 1 : 0;
     g.pred = G.pred;
     g.resid = G.resid;
     if (probe != (G.resid != nullptr)) return SM_ERR_UNSUPPORTED;
@@ -1438,7 +1475,7 @@ sm_status launch_gemm_ns(const NsgGroup* groups, int ngroups, int kind, hipStrea
     const double ea = G.a_low ? lower_tile_entries(G.M) : G.M * (double)G.K;
     const double eb = G.b_low ? lower_tile_entries(G.N) : G.N * (double)G.K;
     const double ec = probe ? 2.0 * ns_probe_parts(G.M)   // the float partials
-                      : G.bits ? G.M * (double)G.N / 16.0
+                      : G.bits ? G.M * (double)G.N / (G.bits_s8 ? 2.0 : 16.0)
                              : (G.c_low ? lower_tile_entries(G.M) : G.M * (double)G.N);
     const double gbytes = 2.0 * ((same ? 0.0 : eb) + ea + ec);
     bytes += gbytes * G.batch;

@@ -191,6 +191,9 @@ struct NsJob {
   // out (needs n % 64 == 0).
   uint64_t* bits = nullptr;
   int64_t bits_stride = 0;
+  // bits_s8: the signs as int8 instead ([batch][m n] bytes at bits,
+  // bits_stride = m n / 8 words; the grouped kernels only)
+  bool bits_s8 = false;
 };
 
 // The grouped-kernel descriptors of one NS iteration of job j:
@@ -254,6 +257,7 @@ bool ns_desc(const NsJob& j, const void* cur, void* dst, bool first, bool last,
   if (last && j.bits) {
     a.bits = j.bits;
     a.bits_stride = j.bits_stride;
+    a.bits_s8 = j.bits_s8 ? 1 : 0;
   }
   return a.ident_terms != 0 && gemm_ns_supported(a);
 }
@@ -431,6 +435,7 @@ bool gf_plan(const NsJob& j, const sm_ns_params& p, GfPlan& g, bool force = fals
   if (j.bits) {
     a.bits = j.bits;
     a.bits_stride = j.bits_stride;
+    a.bits_s8 = j.bits_s8 ? 1 : 0;
   }
   if (!gemm_ns_supported(a)) return false;
   g.r = r;
@@ -764,6 +769,8 @@ sm_status ns_generic(const std::vector<NsJob>& jobs, int dt, const sm_ns_params&
                      hipStream_t s) {
   const int K = p.iters;
   const size_t nj = jobs.size();
+  for (const NsJob& j : jobs)
+    if (j.bits_s8) return SM_ERR_UNSUPPORTED;   // int8 signs: the grouped kernels only
   std::vector<const void*> cur(nj);
   for (size_t i = 0; i < nj; ++i) cur[i] = jobs[i].x;
   // the iterate of job i read through its pointer table (k == 0 with xtbl)
@@ -1710,13 +1717,22 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
         r.job.xper = M;
       }
       // a7 + a8 fused into the last NS product when the signs are all the
-      // step needs from the direction
+      // step needs from the direction (int8 signs: the grouped kernels only)
       r.fused_signs = false;
       if (!polar && c->encoding == SM_ENC_BITS) {
         NsJob bj = r.job;
         bj.bits = r.w.bits;
         bj.bits_stride = r.words;
         if (r.grouped ? ns_grouped_ok(bj, c->mdt, c->ns) : (ch.n % 64) == 0) {
+          r.job = bj;
+          r.fused_signs = true;
+        }
+      } else if (!polar && c->encoding == SM_ENC_INT8 && r.grouped && r.count % 16 == 0) {
+        NsJob bj = r.job;
+        bj.bits = reinterpret_cast<uint64_t*>(r.w.s8);
+        bj.bits_stride = r.count / 8;
+        bj.bits_s8 = true;
+        if (ns_grouped_ok(bj, c->mdt, c->ns)) {
           r.job = bj;
           r.fused_signs = true;
         }
@@ -1783,9 +1799,9 @@ sm_status sm_step(const sm_config* c, const sm_matrix* mats, int nmat, int64_t t
     if (muon_step) {
       if (polar)
         SM_TRY(launch_polar_update(r.w.d, c->mdt, r.nc, r.count, r.wt, c->wdt, c->lr, s));
-      else if (int8)
+      else if (int8 && !r.fused_signs)
         SM_TRY(launch_sign_int8(r.w.d, c->mdt, r.B, r.count, r.w.s8, s));
-      else if (!r.fused_signs)
+      else if (!int8 && !r.fused_signs)
         SM_TRY(launch_sign_pack(r.w.d, c->mdt, r.B, r.count, r.w.bits, r.words, s));
     }
   }

@@ -387,8 +387,12 @@ struct NsgGroup {
   int a_low, b_low, c_low;
   // Apply only: instead of C, write the 1-bit signs of its bf16 values
   // (bit = 1 <=> negative, bit j of word w <=> row-major entry 64 w + j) to
-  // bits + problem * bits_stride words; needs N % 64 == 0.
-  uint64_t* bits; int64_t bits_stride;
+  // bits + problem * bits_stride words; needs N % 64 == 0.  With bits_s8
+  // the signs are int8 instead (-1 iff negative, else +1; one byte per
+  // row-major entry, row pitch N bytes) at the same address, bits_stride
+  // still counted in 8-byte words; then bits is 16-byte aligned and
+  // bits_stride even.
+  uint64_t* bits; int64_t bits_stride; int bits_s8;
   // Optional per-problem store predicate (device int32 per problem): a
   // problem whose flag is not 1 computes its tiles but stores nothing.
   const int32_t* pred;
