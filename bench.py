@@ -71,6 +71,9 @@ def parse():
                     help="timed steps of each sub-object run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter scaling)")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the MFMA ceiling probe and device copy of the benchmark line "
+                         "(kernel-statistics runs)")
     ap.add_argument("--attainable", action="store_true",
                     help="run only the MFMA ceiling probe and the device copy (the `attainable` "
                          "object of the benchmark line)")
@@ -898,9 +901,9 @@ def main():
             extra["variants"] = variants
     del mats, call
     torch.cuda.empty_cache()
-    att = attainable_rates(sm, torch)
+    att = None if args.no_attainable else attainable_rates(sm, torch)
     add_attainable(roofline, att)
-    if "ns_tflops" in extra and wl.mdt == "bf16":
+    if att is not None and "ns_tflops" in extra and wl.mdt == "bf16":
         extra["ns_attainable_frac"] = extra["ns_tflops"] / att["mfma_loop_tflops"]["lds_operands"]
     for typ, rec in extra.get("per_step_type", {}).items():
         add_attainable(rec.get("roofline"), att)
