@@ -197,6 +197,19 @@ def test_p8_residual_brute_force_and_special_values():
         assert abs(O.orth_residual(cval * np.eye(6)) - abs(cval ** 2 - 1)) < 1e-14
 
 
+def test_p8_acceptance_is_inclusive():
+    """CacheMuon technical summary, core mechanism item 3: the cached candidate
+    is kept while its residual is at most the threshold (err <= gamma, the
+    boundary included); one ulp above it refreshes, and a NaN residual fails
+    the comparison."""
+    for gamma in (0.0, 0.5, 2.0, 15.0):
+        assert O.accept_cached(gamma, gamma)
+        assert not O.accept_cached(float(np.nextafter(gamma, np.inf)), gamma)
+        assert O.accept_cached(float(np.nextafter(gamma, -np.inf)), gamma)
+    assert not O.accept_cached(float("nan"), 2.0)
+    assert O.accept_cached(0.0, 0.0)     # an exactly orthogonal candidate at gamma = 0
+
+
 # ---------------------------------------------------------------- P-9 trigger
 
 def _ar1_stream(rng, shape, steps, rho=0.99):
