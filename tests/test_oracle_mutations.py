@@ -148,6 +148,44 @@ def lion_sign_of_momentum_only(m_prev, g, beta1):
     return O.sign_negative(np.asarray(m_prev, np.float64))
 
 
+def update_polar_one_rounding(w_values, d_values, lr, wdtype):
+    w = np.asarray(w_values, dtype=np.float64).astype(np.float32).astype(np.float64)
+    d = np.asarray(d_values, dtype=np.float64).astype(np.float32).astype(np.float64)
+    out32 = (w - np.float64(np.float32(lr)) * d).astype(np.float32)   # lr * D not rounded
+    if wdtype == O.F32:
+        return out32.astype(np.float64)
+    return O.f32_from_bf16_bits(O.bf16_bits_from_f32(out32)).astype(np.float64)
+
+
+def power_without_normalising(e, v0, iters):
+    e = np.asarray(e, np.float64)
+    v = np.asarray(v0, np.float64).reshape(-1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for _ in range(iters):
+            v = e.T @ (e @ v)
+        y = e @ v
+        return math.sqrt(float(y @ y))
+
+
+def power_frobenius(e, v0, iters):
+    return float(np.linalg.norm(np.asarray(e, np.float64)))
+
+
+def orient_never_transposes(y):
+    return np.asarray(y, np.float64).copy(), False
+
+
+def vote_polar_unnormalised(v, p):
+    return O.ns_polar(np.asarray(v, dtype=np.float64), p, normalize=False)
+
+
+def unpack_reversed(words, count):
+    words = np.asarray(words, dtype=np.uint64).reshape(-1)
+    shifts = np.arange(63, -1, -1, dtype=np.uint64)
+    bits = (words[:, None] >> shifts[None, :]) & np.uint64(1)
+    return bits.reshape(-1)[:count].astype(bool)
+
+
 # ------------------------------------------------------------------ cases
 
 COEFS = [(1.5, -0.5, 0.0), (1.9, -0.7, 0.05), (1.2, -0.1, -0.08)]
@@ -191,6 +229,19 @@ CASES = [
      [P.test_p14_schedule_phase]),
     ("Lion sign of the momentum alone", "lion_sign_negative", lion_sign_of_momentum_only,
      [P.test_lion_sign_is_the_exact_sign_of_the_interpolation]),
+    ("polar update rounded once", "update_polar", update_polar_one_rounding,
+     [P.test_update_polar_matches_torch_float32_and_bf16]),
+    ("power method never normalised", "spectral_norm_power", power_without_normalising,
+     [lambda: P.test_p18_power_method_converges_to_svd(30, 70), P.test_p18_power_method_closed_forms]),
+    ("Frobenius norm for the spectral norm", "spectral_norm_power", power_frobenius,
+     [lambda: P.test_p18_power_method_converges_to_svd(30, 70), P.test_p18_power_method_closed_forms]),
+    ("tall matrices not transposed", "orient", orient_never_transposes,
+     [P.test_p3_tall_orientation_matches_transpose_map, P.test_p7_gram_tall_orientation]),
+    ("vote not normalised before its polar step", "vote_polar_direction", vote_polar_unnormalised,
+     [lambda: P.test_p17_vote_polar_on_hadamard_votes_closed_form(COEFS[0], 8, 1, False),
+      P.test_p17_vote_polar_rank_one_and_zero_votes]),
+    ("bits unpacked MSB first", "unpack_bits", unpack_reversed,
+     [lambda: P.test_p11_pack_brute_force(65), lambda: P.test_p12_vote_brute_force_and_symmetries(3)]),
 ]
 
 
