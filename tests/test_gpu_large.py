@@ -43,6 +43,69 @@ def _oriented(y):
 
 # ------------------------------------------------------------------ GPT-2 large: CacheMuon
 
+def test_cache_muon_full_size_steps_sampled(gpu_lib):
+    """Two full config-4 steps as the benchmark runs them (144 matrices,
+    707.8M parameters, M = 1, bf16, gamma = 2): the first refreshes every
+    cache, the second reuses every one.  Sampled matrices (one per shape):
+    the cached Q against the oracle's fresh solve on the step's own
+    momentum; the second step's residual against the oracle's residual of
+    the cached candidate on that step's momentum."""
+    wl = W.WORKLOADS[4]
+    say("cache muon full size: 144 matrices")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    mats = []
+    for (m, n) in wl.shapes:
+        r = min(m, n)
+        mats.append(sm.MatrixBuffers(
+            w=(0.02 * torch.randn(m, n, generator=gen, device="cuda")).to(torch.bfloat16),
+            mom=torch.zeros(1, m, n, dtype=torch.bfloat16, device="cuda"),
+            grad=(wl.grad_std * torch.randn(1, m, n, generator=gen, device="cuda")).to(torch.bfloat16),
+            q_cache=torch.zeros(1, r, r, dtype=torch.float32, device="cuda"),
+            cache_state=torch.zeros(1, 2, dtype=torch.int32, device="cuda")))
+    cfg = sm.StepConfig(algo=sm.CACHE_MUON, update=sm.UPDATE_POLAR, M=1, wdt=torch.bfloat16,
+                        mdt=torch.bfloat16, gdt=torch.bfloat16, lr=wl.lr, beta1=wl.beta1,
+                        ns=sm.NSParams(wl.ns_iters, wl.ns_a, wl.ns_b, wl.ns_c, wl.ns_eps),
+                        gamma=wl.gamma, cache_mode=sm.MODE_TRIGGER)
+    diag = torch.full((len(mats), 1, 2), 7.0, device="cuda")
+    call = sm.StepCall(cfg, mats, diag=diag)
+    op = O.NSParams(wl.ns_iters, f32(wl.ns_a), f32(wl.ns_b), f32(wl.ns_c), f32(wl.ns_eps))
+    sample = [0, 1, 2, 3]                         # one matrix of each shape (first layer)
+    w_before = [mb.w.clone() for mb in mats]
+    call(1)
+    torch.cuda.synchronize()
+    assert diag[:, 0, 1].all()                    # no cache yet: every matrix refreshed
+    assert all(mb.cache_state.cpu().tolist() == [[1, 1]] for mb in mats)
+    for j, mb in enumerate(mats):                 # every weight matrix moved
+        assert not torch.equal(mb.w, w_before[j]), j
+    for j in sample:
+        y = to_np(mats[j].mom)[0].astype(np.float64)
+        xo, _ = _oriented(O.frobenius_normalize(y, op.eps))
+        _, q_or = O.gram_ns_fresh_oriented(xo, op)
+        eq = rel_fro(mats[j].q_cache.cpu().numpy()[0].astype(np.float64), q_or)
+        say(f"  step 1 matrix {j} {wl.shapes[j]}: Q {eq:.2e}")
+        assert eq <= TOL_BF16, (j, eq)
+    # second step on a drifted gradient: gamma = 2 reuses every cache
+    q1 = [mats[j].q_cache.clone() for j in sample]
+    for mb in mats:
+        mb.grad.mul_(0.99).add_((0.141 * wl.grad_std * torch.randn(mb.grad.shape, generator=gen,
+                                                                    device="cuda")).to(torch.bfloat16))
+    call(2)
+    torch.cuda.synchronize()
+    assert not diag[:, 0, 1].any()
+    assert all(mb.cache_state.cpu().tolist() == [[1, 1]] for mb in mats)
+    for i, j in enumerate(sample):
+        assert torch.equal(mats[j].q_cache, q1[i])  # the cache is kept as it was
+        y = to_np(mats[j].mom)[0].astype(np.float64)
+        xo, _ = _oriented(O.frobenius_normalize(y, op.eps))
+        cand = O.cache_reuse_oriented(q1[i].cpu().numpy()[0].astype(np.float64), xo)
+        err_or = O.orth_residual(cand)
+        err = float(diag[j, 0, 0].item())
+        say(f"  step 2 matrix {j}: err gpu {err:.6f} oracle {err_or:.6f}")
+        assert 0.0 <= err <= wl.gamma
+        assert abs(err - err_or) <= 1e-3 * err_or, (j, err, err_or)
+
+
 @pytest.mark.parametrize("shape", [(1280, 3840), (1280, 1280), (1280, 5120), (5120, 1280)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_cache_muon_gpt2_large_shapes(gpu_lib, shape):

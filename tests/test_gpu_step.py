@@ -619,6 +619,16 @@ def test_full_size_gpt2_small_step_sampled(gpu_lib):
         _check_directions_and_vote(wl, cfg, view, j, mats[j], 5, out, f"full-size matrix {j}")
 
 
+def test_full_size_resnet50_step(gpu_lib):
+    """One full config-3 step as the benchmark runs it: all 53 ResNet-50
+    convolution matrices (23.5M parameters), M = 4 float32 workers, one NS
+    iteration, ties voted 0; every matrix checked against the oracle."""
+    wl = W.WORKLOADS[3]
+    assert len(wl.shapes) == 53
+    st = Seeded(wl, wl.shapes)
+    _check_step(wl, _cfg(wl), st, 1, wl.mdt)
+
+
 @pytest.mark.parametrize("variant", ["int8", "vote_polar"])
 def test_full_size_gpt2_small_step_variants(gpu_lib, variant):
     """The full config-2 step with the int8 encoding (identical to the 1-bit
