@@ -480,6 +480,9 @@ ENC_CASES = [
     ("sign", 1, [(256, 256)], {}, 3),
     ("sign", 3, [(64, 147), (256, 64), (128, 1152)], {}, 3),
     ("sign", 2, [(768, 2304), (3072, 768)], {}, 3),
+    # bf16 on the grouped kernels: the wide 256 x 1000 (n % 64 != 0) keeps the
+    # separate sign pass, the tall 1000 x 256 has its signs fused
+    ("sign", 2, [(256, 1000), (1000, 256)], {}, 2),
     ("cache", 4, [(128, 384), (512, 128)], dict(M=3, update=sm.UPDATE_VOTE, wdt="bf16",
                                                 mdt="bf16", gdt="bf16"), 1),
     ("lion-lion", 5, [(64, 200), (300, 70)], dict(M=3, period=2, wdt="f32", mdt="f32",
