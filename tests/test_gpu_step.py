@@ -489,6 +489,9 @@ ENC_CASES = [
                                                   gdt="f32"), 1),
     ("lion-muon", 5, [(64, 200), (300, 70)], dict(M=4, period=2, wdt="bf16", mdt="bf16",
                                                   gdt="bf16"), 2),
+    # a LionMuon Muon step on the grouped kernels: signs fused into the last apply
+    ("lion-muon", 5, [(256, 1024), (1024, 256)], dict(M=4, period=2, wdt="bf16", mdt="bf16",
+                                                      gdt="bf16"), 2),
 ]
 
 
